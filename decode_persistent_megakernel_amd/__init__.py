@@ -1,0 +1,188 @@
+"""Batch-1 decode step of a Llama-style decoder on MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/td.h.  It only moves arguments:
+device buffers come from PyTorch tensors (PyTorch is used for device memory and
+streams), and every step of the decode runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import (TD_E_HIP, TD_E_INVALID_ARG, TD_E_NONFINITE, TD_E_PLAN, TD_E_RANGE, TD_E_TIMEOUT,
+                   TD_E_UNSUPPORTED, TD_EXEC_GRAPH, TD_EXEC_MEGAKERNEL, TD_EXEC_PER_OP, TD_OK, TD_WF_BF16,
+                   TD_WF_INT4_G64, TdError)
+
+__all__ = ["DeviceModel", "Decoder", "KVCache", "gemv", "attention", "TdError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(arr: Optional[np.ndarray], device):
+    """A device copy of a host array of stored-format bits (bf16/fp16 bits or bytes)."""
+    if arr is None:
+        return None
+    torch = _torch()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class DeviceModel:
+    """Weights of one model in device memory, in the stored formats of td.h.
+
+    `model` is any object with `cfg` (n_layers, hidden, n_q_heads, n_kv_heads,
+    head_dim, intermediate, vocab, rope_theta, rms_eps, weight_format, qkv_bias,
+    tied), `embed`, `head`, `final_norm` and `layers` (attn_norm, qkv, qkv_bias,
+    o, mlp_norm, gate_up, down; each linear with `.w` and `.s`) as host arrays.
+    """
+
+    def __init__(self, model, device: str = "cuda"):
+        c = model.cfg
+        self.cfg = c
+        self.device = device
+        self.embed = _dev(model.embed, device)
+        self.head = self.embed if c.tied else _dev(model.head, device)
+        self.final_norm = _dev(model.final_norm, device)
+        self.layers = []
+        for L in model.layers:
+            self.layers.append({
+                "attn_norm": _dev(L.attn_norm, device), "mlp_norm": _dev(L.mlp_norm, device),
+                "w_qkv": _dev(L.qkv.w, device), "s_qkv": _dev(L.qkv.s, device),
+                "b_qkv": _dev(L.qkv_bias, device),
+                "w_o": _dev(L.o.w, device), "s_o": _dev(L.o.s, device),
+                "w_gu": _dev(L.gate_up.w, device), "s_gu": _dev(L.gate_up.s, device),
+                "w_d": _dev(L.down.w, device), "s_d": _dev(L.down.s, device),
+            })
+
+    def td_config(self, max_ctx: int) -> _lib.TdConfig:
+        c = self.cfg
+        return _lib.TdConfig(n_layers=c.n_layers, hidden=c.hidden, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
+                             head_dim=c.head_dim, intermediate=c.intermediate, vocab=c.vocab, max_ctx=max_ctx,
+                             rope_theta=c.rope_theta, rms_eps=c.rms_eps, weight_format=c.weight_format,
+                             qkv_bias=int(c.qkv_bias))
+
+    def td_weights(self):
+        n = len(self.layers)
+        arr = (_lib.TdLayerWeights * n)()
+        for i, L in enumerate(self.layers):
+            arr[i] = _lib.TdLayerWeights(**{k: _ptr(v) for k, v in L.items()})
+        w = _lib.TdWeights(embed=_ptr(self.embed), final_norm=_ptr(self.final_norm), head=_ptr(self.head),
+                           layers=arr)
+        return w, arr
+
+
+class KVCache:
+    """K and V caches in device memory: bf16 bits [n_layers][n_kv_heads][max_ctx][head_dim]."""
+
+    def __init__(self, cfg, max_ctx: int, device: str = "cuda", k: Optional[np.ndarray] = None,
+                 v: Optional[np.ndarray] = None):
+        torch = _torch()
+        shape = (cfg.n_layers, cfg.n_kv_heads, max_ctx, cfg.head_dim)
+        self.max_ctx = max_ctx
+        self.k = _dev(k, device) if k is not None else torch.zeros(shape, dtype=torch.int16, device=device)
+        self.v = _dev(v, device) if v is not None else torch.zeros(shape, dtype=torch.int16, device=device)
+        assert tuple(self.k.shape) == shape and tuple(self.v.shape) == shape
+
+    def td_kv(self) -> _lib.TdKV:
+        return _lib.TdKV(k=_ptr(self.k), v=_ptr(self.v), max_ctx=self.max_ctx)
+
+    def host(self):
+        return (self.k.cpu().numpy().view(np.uint16), self.v.cpu().numpy().view(np.uint16))
+
+
+class Decoder:
+    """One td_ctx: td_create at construction, td_decode_step per step."""
+
+    def __init__(self, dm: DeviceModel, max_ctx: int, executor: int = TD_EXEC_MEGAKERNEL):
+        self.dm = dm
+        self.max_ctx = max_ctx
+        self._cfg = dm.td_config(max_ctx)
+        self._w, self._layers = dm.td_weights()
+        h = ctypes.c_void_p()
+        _lib.check(_lib.lib().td_create(ctypes.byref(self._cfg), ctypes.byref(self._w), executor, ctypes.byref(h)),
+                   "td_create")
+        self._h = h
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    def token_ptr(self) -> int:
+        return _lib.lib().td_token_ptr(self._h)
+
+    def step(self, token_ptr: int, pos: int, kv: KVCache, logits, stream=None) -> None:
+        """One decode step; `token_ptr` is a device int32 address, `logits` a float32 device tensor [vocab]."""
+        kvs = kv.td_kv()
+        _lib.check(_lib.lib().td_decode_step(self._h, token_ptr, int(pos), ctypes.byref(kvs), _ptr(logits),
+                                             _stream_handle(stream)), "td_decode_step")
+
+    def status(self) -> int:
+        err = ctypes.c_int32(0)
+        return int(_lib.lib().td_status(self._h, ctypes.byref(err)))
+
+    def set_timing(self, enable: bool) -> None:
+        _lib.check(_lib.lib().td_set_timing(self._h, int(enable)), "td_set_timing")
+
+    def last_step_ms(self) -> float:
+        return float(_lib.lib().td_last_step_ms(self._h))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _lib.lib().td_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gemv(fmt: int, w, s, rows: int, cols: int, x, y, stream=None) -> None:
+    """y = W x on device tensors through the test hook (same chunk arithmetic as the step)."""
+    _lib.check(_lib.lib().td_test_gemv(fmt, _ptr(w), _ptr(s), rows, cols, _ptr(x), _ptr(y), _stream_handle(stream)),
+               "td_test_gemv")
+
+
+def attention(q, k, v, n_pos: int, head_dim: int, out, stream=None) -> None:
+    _lib.check(_lib.lib().td_test_attention(_ptr(q), _ptr(k), _ptr(v), n_pos, head_dim, _ptr(out),
+                                            _stream_handle(stream)), "td_test_attention")
+
+
+_hip = None
+
+
+def _hip_rt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.restype = ctypes.c_int
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    return _hip
+
+
+def read_device_i32(ptr: int) -> int:
+    """Reads one int32 from a device address (synchronous copy on the null stream)."""
+    v = ctypes.c_int32(0)
+    e = _hip_rt().hipMemcpy(ctypes.byref(v), ptr, 4, 2)  # hipMemcpyDeviceToHost
+    if e != 0:
+        raise RuntimeError(f"hipMemcpy failed: {e}")
+    return int(v.value)

@@ -1,0 +1,436 @@
+// td_api.cpp - host side of the C ABI declared in include/td.h.
+//
+// td_create validates the config and the device, builds the static work plan
+// (which CU and wave owns which rows of every stage, how the attention context
+// is split, where everything sits in LDS), validates it, and allocates the
+// context's scratch.  td_decode_step fills the per-step fields and launches the
+// persistent kernel cooperatively (all workgroups resident at once, which the
+// grid barriers need).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "td.h"
+#include "td_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return TD_E_HIP;
+}
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+struct td_ctx {
+  td_config cfg;
+  int executor = TD_EXEC_MEGAKERNEL;
+  int ncu = 0;
+  int ring = 0;
+  td_kparams kp{};
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  td_layer_dev* d_layers = nullptr;
+  float* d_rope = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool launched = false;
+  bool timing = false;
+  bool timed = false;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+};
+
+namespace {
+
+// Enumerates the row ownership of every GEMV stage exactly as the kernel
+// derives it and checks: every unit of every stage is owned by exactly one
+// (CU, wave); every row is produced once; all rows are inside the matrix;
+// per-CU outputs fit the LDS output area.
+int validate_plan(const td_config& c, int ncu, int out_floats, int own_floats) {
+  const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab;
+  const int qd = c.n_q_heads * d, qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * d;
+  struct St {
+    int U, rpu, rows, kind;
+  } st[] = {{qkv_rows / 2, 2, qkv_rows, TD_ST_QKV}, {H, 1, H, TD_ST_O}, {I, 2, 2 * I, TD_ST_GU},
+            {H, 1, H, TD_ST_DOWN}, {V, 1, V, TD_ST_HEAD}};
+  for (const St& s : st) {
+    std::vector<uint8_t> seen_row(s.rows, 0);
+    std::vector<uint8_t> seen_unit(s.U, 0);
+    for (int cu = 0; cu < ncu; ++cu) {
+      int u0 = (int)(((int64_t)s.U * cu) / ncu), u1 = (int)(((int64_t)s.U * (cu + 1)) / ncu);
+      if (u0 < 0 || u1 > s.U || u1 < u0) return fail(TD_E_PLAN, "unit range out of bounds");
+      if ((u1 - u0) * s.rpu > out_floats) return fail(TD_E_PLAN, "per-CU outputs exceed the LDS output area");
+      for (int wave = 0; wave < TD_NW; ++wave) {
+        for (int u = u0 + wave; u < u1; u += TD_NW) {
+          if (seen_unit[u]++) return fail(TD_E_PLAN, "unit owned twice");
+          for (int r = 0; r < s.rpu; ++r) {
+            int row;
+            if (s.kind == TD_ST_QKV) {
+              int half = d / 2, head = u / half, i = u - head * half;
+              row = head * d + i + r * half;
+            } else if (s.kind == TD_ST_GU) {
+              row = u + r * I;
+            } else {
+              row = u;
+            }
+            if (row < 0 || row >= s.rows) return fail(TD_E_PLAN, "row outside the matrix");
+            if (seen_row[row]++) return fail(TD_E_PLAN, "row written twice");
+          }
+        }
+      }
+    }
+    for (int r = 0; r < s.rows; ++r)
+      if (!seen_row[r]) return fail(TD_E_PLAN, "row without a writer");
+  }
+  int own = (int)(((int64_t)H + ncu - 1) / ncu);
+  if (own > own_floats) return fail(TD_E_PLAN, "residual rows exceed the LDS area");
+  (void)qd;
+  return TD_OK;
+}
+
+int check_config(const td_config* c) {
+  if (!c) return fail(TD_E_INVALID_ARG, "null config");
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0 ||
+      c->vocab <= 0 || c->max_ctx <= 0)
+    return fail(TD_E_INVALID_ARG, "non-positive dimension");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(TD_E_INVALID_ARG, "head_dim must be 64 or 128");
+  if (c->n_q_heads % c->n_kv_heads) return fail(TD_E_INVALID_ARG, "n_kv_heads must divide n_q_heads");
+  if (c->n_q_heads / c->n_kv_heads > TD_MAX_GROUP) return fail(TD_E_INVALID_ARG, "more than 8 q heads per kv head");
+  if (c->hidden % 256) return fail(TD_E_INVALID_ARG, "hidden must be a multiple of 256");
+  if (c->intermediate % 64) return fail(TD_E_INVALID_ARG, "intermediate must be a multiple of 64");
+  if (c->weight_format != TD_WF_BF16 && c->weight_format != TD_WF_INT4_G64)
+    return fail(TD_E_INVALID_ARG, "unknown weight format");
+  if (c->weight_format == TD_WF_INT4_G64 &&
+      ((c->hidden % 128) || (c->intermediate % 128) || ((c->n_q_heads * c->head_dim) % 128)))
+    return fail(TD_E_INVALID_ARG, "int4 needs every K to be a multiple of 128");
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(TD_E_INVALID_ARG, "bad rope_theta or rms_eps");
+  return TD_OK;
+}
+
+int check_weights(const td_config* c, const td_weights* w) {
+  if (!w || !w->embed || !w->final_norm || !w->head || !w->layers) return fail(TD_E_INVALID_ARG, "null weight pointer");
+  const bool q4 = c->weight_format == TD_WF_INT4_G64;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const td_layer_weights& L = w->layers[l];
+    if (!L.attn_norm || !L.w_qkv || !L.w_o || !L.mlp_norm || !L.w_gu || !L.w_d)
+      return fail(TD_E_INVALID_ARG, "null layer weight pointer");
+    if (q4 && (!L.s_qkv || !L.s_o || !L.s_gu || !L.s_d)) return fail(TD_E_INVALID_ARG, "int4 layer without scales");
+    if (c->qkv_bias && !L.b_qkv) return fail(TD_E_INVALID_ARG, "qkv_bias set but b_qkv is null");
+  }
+  return TD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* td_strerror(int code) {
+  switch (code) {
+    case TD_OK: return "ok";
+    case TD_E_INVALID_ARG: return "invalid argument";
+    case TD_E_UNSUPPORTED: return "unsupported device or config";
+    case TD_E_PLAN: return "work plan failed validation";
+    case TD_E_RANGE: return "position or token id out of range";
+    case TD_E_HIP: return "HIP runtime error";
+    case TD_E_NONFINITE: return "non-finite logit";
+    case TD_E_NOMEM: return "device allocation failed";
+    case TD_E_TIMEOUT: return "grid-wide wait timed out";
+    default: return "unknown error";
+  }
+}
+
+const char* td_last_error(void) { return g_last_error.c_str(); }
+
+int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ctx** out) {
+  if (!out) return fail(TD_E_INVALID_ARG, "null out pointer");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  rc = check_weights(cfg, w);
+  if (rc) return rc;
+  if (executor != TD_EXEC_MEGAKERNEL) return fail(TD_E_UNSUPPORTED, "executor not available");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(TD_E_UNSUPPORTED, std::string("needs gfx950, found ") + prop.gcnArchName);
+  const int ncu = prop.multiProcessorCount;
+  if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
+  if (!prop.cooperativeLaunch) return fail(TD_E_UNSUPPORTED, "device lacks cooperative launch");
+
+  const td_config& c = *cfg;
+  const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab, L = c.n_layers;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
+  const int qd = nq * d, kvd = nkv * d, qkv_rows = qd + 2 * kvd;
+
+  // attention split: at most one task per CU, chunks a multiple of the tile
+  const int cmax_by_cu = ncu / nkv;
+  int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
+  const int n_chunks_max = (c.max_ctx + chunk_len - 1) / chunk_len;
+  if (n_chunks_max * nkv > ncu) return fail(TD_E_PLAN, "attention split exceeds the CU count");
+
+  // LDS layout
+  const td_attn_lds A = td_attn_layout(d, group);
+  const int64_t kpad = round_up(std::max({H, qd, I}), 2048);
+  const int64_t xin_bytes = std::max<int64_t>(kpad * 4, A.bytes);
+  auto per_cu = [&](int64_t U) { return (int)((U + ncu - 1) / ncu); };
+  const int out_floats = (int)round_up(std::max({per_cu(qkv_rows / 2) * 2, per_cu(H), per_cu(I) * 2, per_cu(V)}), 64);
+  const int own_floats = (int)round_up(per_cu(H), 64);
+  const int64_t lds_cap = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
+  int ring = 0;
+  td_kparams kp{};
+  for (int S : {16, 12, 8}) {
+    int64_t off = 0;
+    kp.off_ring = (int32_t)off;
+    off += (int64_t)TD_NW * S * TD_CHUNK;
+    kp.off_sring = (int32_t)off;
+    if (c.weight_format == TD_WF_INT4_G64) off += (int64_t)TD_NW * S * TD_SCHUNK;
+    kp.off_xin = (int32_t)off;
+    kp.off_attn = (int32_t)off;
+    off += round_up(xin_bytes, 256);
+    kp.off_out = (int32_t)off;
+    off += (int64_t)out_floats * 4;
+    kp.off_own = (int32_t)off;
+    off += (int64_t)own_floats * 4;
+    if (off <= lds_cap && off <= 160 * 1024) {
+      int blocks = 0;
+      int oe = td_megakernel_occupancy(S, (int)off, &blocks);
+      if (oe == 0 && blocks >= 1) {
+        ring = S;
+        kp.lds_bytes = (int32_t)off;
+        break;
+      }
+    }
+  }
+  if (!ring) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
+
+  rc = validate_plan(c, ncu, out_floats, own_floats);
+  if (rc) return rc;
+
+  td_ctx* ctx = new (std::nothrow) td_ctx();
+  if (!ctx) return fail(TD_E_NOMEM, "host allocation failed");
+  ctx->cfg = c;
+  ctx->executor = executor;
+  ctx->ncu = ncu;
+  ctx->ring = ring;
+
+  // scratch: one allocation, 256-byte aligned pieces
+  const int sync_words = (int)round_up(TD_SY_MERGE + L * nkv, 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  const size_t o_x = take((size_t)H * 4), o_q = take((size_t)qd * 4), o_o = take((size_t)qd * 4);
+  const size_t o_act = take((size_t)I * 4);
+  const size_t o_part = take((size_t)nkv * n_chunks_max * group * (d + 2) * 4);
+  const size_t o_cand = take((size_t)ncu * 4 * 4);
+  const size_t o_sync = take((size_t)sync_words * 4);
+  const size_t o_tok = take(4), o_err = take(4);
+  const size_t o_rope = take((size_t)c.max_ctx * (d / 2) * 2 * 4);
+  const size_t o_layers = take(sizeof(td_layer_dev) * L);
+  ctx->scratch_bytes = off;
+  e = hipMalloc(&ctx->scratch, off);
+  if (e != hipSuccess) {
+    delete ctx;
+    return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of scratch failed") : hip_fail(e, "hipMalloc");
+  }
+  uint8_t* base = (uint8_t*)ctx->scratch;
+  e = hipMemset(base, 0, off);
+  if (e != hipSuccess) {
+    (void)hipFree(ctx->scratch);
+    delete ctx;
+    return hip_fail(e, "hipMemset");
+  }
+
+  // RoPE table: angle pos * theta^(-2i/d) and its cos/sin in double, stored as fp32
+  std::vector<float> rope((size_t)c.max_ctx * (d / 2) * 2);
+  for (int p = 0; p < c.max_ctx; ++p)
+    for (int i = 0; i < d / 2; ++i) {
+      double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / d);
+      rope[((size_t)p * (d / 2) + i) * 2 + 0] = (float)std::cos(ang);
+      rope[((size_t)p * (d / 2) + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  std::vector<td_layer_dev> layers(L);
+  for (int l = 0; l < L; ++l) {
+    const td_layer_weights& Lw = w->layers[l];
+    td_layer_dev& Ld = layers[l];
+    Ld.w[0] = (const uint8_t*)Lw.w_qkv;
+    Ld.w[1] = (const uint8_t*)Lw.w_o;
+    Ld.w[2] = (const uint8_t*)Lw.w_gu;
+    Ld.w[3] = (const uint8_t*)Lw.w_d;
+    Ld.s[0] = (const uint16_t*)Lw.s_qkv;
+    Ld.s[1] = (const uint16_t*)Lw.s_o;
+    Ld.s[2] = (const uint16_t*)Lw.s_gu;
+    Ld.s[3] = (const uint16_t*)Lw.s_d;
+    Ld.bias = c.qkv_bias ? (const uint16_t*)Lw.b_qkv : nullptr;
+    Ld.attn_norm = (const uint16_t*)Lw.attn_norm;
+    Ld.mlp_norm = (const uint16_t*)Lw.mlp_norm;
+  }
+  e = hipMemcpy(base + o_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_layers, layers.data(), sizeof(td_layer_dev) * L, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(ctx->scratch);
+    delete ctx;
+    return hip_fail(e, "hipMemcpy");
+  }
+
+  kp.L = L;
+  kp.H = H;
+  kp.nq = nq;
+  kp.nkv = nkv;
+  kp.d = d;
+  kp.I = I;
+  kp.V = V;
+  kp.max_ctx = c.max_ctx;
+  kp.wf = c.weight_format;
+  kp.has_bias = c.qkv_bias ? 1 : 0;
+  kp.qd = qd;
+  kp.kvd = kvd;
+  kp.qkv_rows = qkv_rows;
+  kp.group = group;
+  kp.eps = c.rms_eps;
+  kp.attn_scale = (float)(1.0 / std::sqrt((double)d));
+  kp.chunk_len = chunk_len;
+  kp.n_chunks_max = n_chunks_max;
+  kp.layers = (const td_layer_dev*)(base + o_layers);
+  kp.embed = (const uint16_t*)w->embed;
+  kp.head = (const uint16_t*)w->head;
+  kp.final_norm = (const uint16_t*)w->final_norm;
+  kp.rope_cs = (const float*)(base + o_rope);
+  kp.x = (float*)(base + o_x);
+  kp.q = (float*)(base + o_q);
+  kp.o = (float*)(base + o_o);
+  kp.act = (float*)(base + o_act);
+  kp.part = (float*)(base + o_part);
+  kp.cand = (uint32_t*)(base + o_cand);
+  kp.sync = (uint32_t*)(base + o_sync);
+  kp.token_out = (int32_t*)(base + o_tok);
+  kp.err = (int32_t*)(base + o_err);
+  kp.n_stages = 5 * L + 1;
+  ctx->kp = kp;
+  *out = ctx;
+  return TD_OK;
+}
+
+const int32_t* td_token_ptr(const td_ctx* ctx) { return ctx ? ctx->kp.token_out : nullptr; }
+
+int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv* kv, float* d_logits_out,
+                   void* stream) {
+  if (!ctx || !d_token || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
+  if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (pos < 0 || pos >= ctx->cfg.max_ctx) return fail(TD_E_RANGE, "pos outside [0, max_ctx)");
+  td_kparams p = ctx->kp;
+  p.pos = pos;
+  p.token_in = d_token;
+  p.logits = d_logits_out;
+  p.kc = (uint16_t*)kv->k;
+  p.vc = (uint16_t*)kv->v;
+  hipStream_t s = (hipStream_t)stream;
+  if (ctx->timing) (void)hipEventRecord(ctx->ev0, s);
+  int le = td_launch_megakernel(&p, ctx->ncu, ctx->ring, stream);
+  if (le != 0) return hip_fail((hipError_t)le, "megakernel launch");
+  if (ctx->timing) {
+    (void)hipEventRecord(ctx->ev1, s);
+    ctx->timed = true;
+  }
+  ctx->last_stream = s;
+  ctx->launched = true;
+  return TD_OK;
+}
+
+int td_status(td_ctx* ctx, int32_t* device_error) {
+  if (!ctx) return fail(TD_E_INVALID_ARG, "null ctx");
+  hipError_t e = hipStreamSynchronize(ctx->last_stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int32_t bits = 0;
+  e = hipMemcpy(&bits, ctx->kp.err, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  if (bits) {
+    int32_t zero = 0;
+    e = hipMemcpy(ctx->kp.err, &zero, 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  }
+  int code = TD_OK;
+  if (bits & TD_ERRBIT_NONFINITE) code = TD_E_NONFINITE;
+  if (bits & TD_ERRBIT_RANGE) code = TD_E_RANGE;
+  if (bits & TD_ERRBIT_TIMEOUT) code = TD_E_TIMEOUT;
+  if (device_error) *device_error = code;
+  return code;
+}
+
+void td_destroy(td_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->launched) (void)hipStreamSynchronize(ctx->last_stream);
+  if (ctx->ev0) (void)hipEventDestroy(ctx->ev0);
+  if (ctx->ev1) (void)hipEventDestroy(ctx->ev1);
+  if (ctx->scratch) (void)hipFree(ctx->scratch);
+  delete ctx;
+}
+
+int td_set_timing(td_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(TD_E_INVALID_ARG, "null ctx");
+  if (enable && !ctx->ev0) {
+    hipError_t e = hipEventCreate(&ctx->ev0);
+    if (e == hipSuccess) e = hipEventCreate(&ctx->ev1);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  ctx->timing = enable != 0;
+  ctx->timed = false;
+  return TD_OK;
+}
+
+float td_last_step_ms(td_ctx* ctx) {
+  if (!ctx || !ctx->timed) return -1.f;
+  if (hipEventSynchronize(ctx->ev1) != hipSuccess) return -1.f;
+  float ms = -1.f;
+  if (hipEventElapsedTime(&ms, ctx->ev0, ctx->ev1) != hipSuccess) return -1.f;
+  return ms;
+}
+
+int td_test_gemv(int32_t fmt, const void* w, const void* scales, int32_t rows, int32_t cols, const float* d_x,
+                 float* d_y, void* stream) {
+  if (!w || !d_x || !d_y || rows <= 0 || cols <= 0) return fail(TD_E_INVALID_ARG, "bad gemv arguments");
+  if (fmt == TD_WF_BF16) {
+    if (cols % 8) return fail(TD_E_INVALID_ARG, "bf16 cols must be a multiple of 8");
+  } else if (fmt == TD_WF_INT4_G64) {
+    if (cols % 64 || !scales) return fail(TD_E_INVALID_ARG, "int4 cols must be a multiple of 64, with scales");
+  } else {
+    return fail(TD_E_INVALID_ARG, "unknown format");
+  }
+  int le = td_launch_test_gemv(fmt, w, scales, rows, cols, d_x, d_y, stream);
+  if (le) return hip_fail((hipError_t)le, "gemv launch");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");
+}
+
+int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim, float* d_out,
+                      void* stream) {
+  if (!d_q || !k || !v || !d_out || n_pos <= 0 || (head_dim != 64 && head_dim != 128))
+    return fail(TD_E_INVALID_ARG, "bad attention arguments");
+  int le = td_launch_test_attention(d_q, k, v, n_pos, head_dim, d_out, stream);
+  if (le) return hip_fail((hipError_t)le, "attention launch");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+/*
+ * td.h - C ABI of the batch-1 decode-step library for MI355X (gfx950).
+ *
+ * One call runs one autoregressive decode step of a Llama-style decoder at
+ * batch size one: embedding row, then per layer RMSNorm, the fused QKV
+ * projection (+ optional bias), half-split RoPE and the K/V-cache write,
+ * grouped-query attention over the cache, the output projection and residual,
+ * RMSNorm, the gate/up projections with SiLU(gate)*up, the down projection and
+ * residual; then the final RMSNorm, the vocabulary-wide logits and the greedy
+ * token.  ("Decoding in tiles", sec. 2 lists the chain of steps and sec. 4 how
+ * one layer becomes tiles; "One launch per token", "The oracle, then the
+ * kernels", lists the same fused set; tinyinfer's "speed limit" section defines
+ * the 4-bit format.)
+ *
+ * All pointers named d_* or described as "device" are device memory of the
+ * current HIP device; nothing here allocates host-visible memory for the
+ * caller.  Every function returns TD_OK (0) or a negative TD_E_* code and never
+ * throws.  One context is used from one host thread and one stream at a time.
+ */
+#ifndef TD_H
+#define TD_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ errors */
+enum {
+    TD_OK = 0,
+    TD_E_INVALID_ARG = -1, /* a null pointer, a bad shape or an unknown option */
+    TD_E_UNSUPPORTED = -2, /* the device is not a gfx950 with a CU count the plan handles, or the
+                              config is outside what the kernels handle (see td_create) */
+    TD_E_PLAN = -3,        /* the work plan failed its validation (bounds, single writer, order) */
+    TD_E_RANGE = -4,       /* pos < 0, pos >= max_ctx, or a token id outside [0, vocab) */
+    TD_E_HIP = -5,         /* a HIP runtime call failed; td_last_error() holds its message */
+    TD_E_NONFINITE = -6,   /* a logit was NaN or Inf (reported by td_status) */
+    TD_E_NOMEM = -7,       /* a device allocation failed */
+    TD_E_TIMEOUT = -8      /* a grid-wide wait inside the kernel exceeded its time limit */
+};
+
+/* --------------------------------------------------------------- formats */
+enum {
+    TD_WF_BF16 = 0,     /* layer linears stored as bf16, row-major [rows][cols] */
+    TD_WF_INT4_G64 = 1  /* layer linears stored as 4-bit codes, [rows][cols/2] bytes: element k in
+                           byte k/2, low nibble for even k; code u in 0..15 stands for q = u - 8;
+                           plus fp16 scales [rows][cols/64], one per 64 consecutive elements of a
+                           row; weight = scale * q (tinyinfer: 4 bits plus one fp16 scale per 64
+                           weights). The embedding and the head are bf16 in both formats. */
+};
+
+/* Executors behind the same td_decode_step. */
+enum {
+    TD_EXEC_MEGAKERNEL = 0, /* one persistent kernel over all CUs per step (the default) */
+    TD_EXEC_PER_OP = 1,     /* one kernel launch per fused op (baseline) */
+    TD_EXEC_GRAPH = 2       /* the per-op launches captured once into a hipGraph and replayed */
+};
+
+typedef struct td_config {
+    int32_t n_layers;
+    int32_t hidden;        /* H */
+    int32_t n_q_heads;
+    int32_t n_kv_heads;    /* divides n_q_heads; q head h uses kv head h / (n_q_heads / n_kv_heads) */
+    int32_t head_dim;      /* d: 64 or 128 */
+    int32_t intermediate;  /* I */
+    int32_t vocab;         /* V */
+    int32_t max_ctx;       /* K/V cache positions */
+    float rope_theta;      /* RoPE base: pair (i, i + d/2) turns by pos * theta^(-2i/d) */
+    float rms_eps;         /* RMSNorm: x / sqrt(mean(x^2) + eps) * gain */
+    int32_t weight_format; /* TD_WF_* (layer linears) */
+    int32_t qkv_bias;      /* nonzero: b_qkv is added after the QKV projection, before RoPE */
+} td_config;
+
+/* Device pointers of one layer.  Shapes are [rows][cols], row = output. */
+typedef struct td_layer_weights {
+    const void* attn_norm;  /* bf16 [H] */
+    const void* w_qkv;      /* [(nq + 2 nkv) d][H]: q rows, then k rows, then v rows */
+    const void* s_qkv;      /* fp16 scales (INT4 only, else NULL) */
+    const void* b_qkv;      /* bf16 [(nq + 2 nkv) d] when qkv_bias, else NULL */
+    const void* w_o;        /* [H][nq d] */
+    const void* s_o;
+    const void* mlp_norm;   /* bf16 [H] */
+    const void* w_gu;       /* [2 I][H]: gate rows, then up rows */
+    const void* s_gu;
+    const void* w_d;        /* [H][I] */
+    const void* s_d;
+} td_layer_weights;
+
+typedef struct td_weights {
+    const void* embed;                /* bf16 [V][H] */
+    const void* final_norm;           /* bf16 [H] */
+    const void* head;                 /* bf16 [V][H]; may equal embed (tied) */
+    const td_layer_weights* layers;   /* host array of n_layers entries */
+} td_weights;
+
+/* Caller-owned K/V cache: bf16 [n_layers][n_kv_heads][max_ctx][head_dim] each. */
+typedef struct td_kv {
+    void* k;
+    void* v;
+    int32_t max_ctx;  /* must equal the config's max_ctx */
+} td_kv;
+
+typedef struct td_ctx td_ctx;
+
+/*
+ * td_create: validates the config and the device, builds and validates the
+ * work plan, and allocates the context's device scratch (activations, attention
+ * partials, barrier words, the token and error words, the RoPE table).
+ * `executor` is a TD_EXEC_* value.  The weight buffers are not copied: they
+ * must stay valid and unchanged for the life of the context.
+ * Errors: TD_E_INVALID_ARG (null pointer, shape not positive, n_kv_heads not
+ * dividing n_q_heads, head_dim not 64 or 128, a dimension not a multiple of 64,
+ * more than 8 query heads per kv head, missing scales or bias), TD_E_UNSUPPORTED
+ * (device is not gfx950, or its CU count is not a multiple of 8), TD_E_PLAN,
+ * TD_E_NOMEM, TD_E_HIP.  On error *out is set to NULL.
+ */
+int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ctx** out);
+
+/*
+ * td_decode_step: one decode step at position `pos` for the token id stored at
+ * the device address d_token (an int32 on the device, so greedy steps chain
+ * without a host round trip: pass td_token_ptr(ctx) as the next d_token).
+ * Writes K/V row `pos` of every layer into `kv`, reads rows 0..pos, writes the
+ * fp32 logits [vocab] to d_logits_out (device, caller-owned) and the greedy
+ * token (largest logit, lowest id among ties) to the device int32 at
+ * td_token_ptr(ctx).  Asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream); no host synchronisation and no allocation.
+ * Errors (before launch): TD_E_INVALID_ARG (null ctx/kv/logits/token, kv
+ * max_ctx mismatch), TD_E_RANGE (pos outside [0, max_ctx)), TD_E_HIP.  Errors
+ * found on the device (a non-finite logit, a token id out of range, a timed-out
+ * grid wait) are reported by td_status.
+ */
+int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv* kv, float* d_logits_out,
+                   void* stream);
+
+/* Device address of the context's int32 greedy-token word (valid for the ctx's life). */
+const int32_t* td_token_ptr(const td_ctx* ctx);
+
+/*
+ * td_status: synchronises the stream of the last td_decode_step, then returns
+ * the device error word as a TD_* code (TD_OK, TD_E_NONFINITE, TD_E_RANGE,
+ * TD_E_TIMEOUT) and clears it.  *device_error (optional) receives the same code.
+ * A TD_E_TIMEOUT leaves the context unusable: destroy it.
+ */
+int td_status(td_ctx* ctx, int32_t* device_error);
+
+/* Frees the context's own device memory (never the caller's weights, cache or logits). */
+void td_destroy(td_ctx* ctx);
+
+/* Static description of an error code. */
+const char* td_strerror(int code);
+
+/* The message of the last TD_E_HIP or TD_E_UNSUPPORTED raised in this thread. */
+const char* td_last_error(void);
+
+/* ------------------------------------------------------------ test hooks */
+/* Each runs one device routine on caller device buffers on `stream`, then
+ * synchronises; they exist so that tests can compare one routine with the
+ * oracle.  Same error convention. */
+
+/* y[rows] = W x for a bf16 or int4 linear (the GEMV routine of the step). */
+int td_test_gemv(int32_t weight_format, const void* w, const void* scales, int32_t rows, int32_t cols,
+                 const float* d_x, float* d_y, void* stream);
+
+/* One query head's attention over n_pos bf16 K/V rows ([n_pos][d]), fp32 q and out [d]. */
+int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim,
+                      float* d_out, void* stream);
+
+/* Measured duration of the last megakernel step (HIP events on the step's own
+ * stream), or a negative value when unavailable.  Timing is off unless enabled. */
+int td_set_timing(td_ctx* ctx, int32_t enable);
+float td_last_step_ms(td_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
