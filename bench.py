@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 decode step on one MI355X.
+
+Workload (default): the Llama-3.2-1B-shaped bf16 decoder (16 layers, hidden
+2048, 32 q / 8 kv heads of 64, intermediate 8192, vocab 128256, tied
+embeddings, RoPE theta 500000) with seeded random-init weights ~N(0, 0.02).
+A seeded random 512-token prompt is prefilled into the K/V cache by running it
+through the decode step itself; then greedy decode steps run at positions
+512, 513, ... with the token chained on the device.  A "step" is one decode
+step (one token).  W warmup steps run first (positions 512..), then the K timed
+steps restart at position 512 (each step rewrites its own cache row first).
+
+Printed: one JSON line with tokens/s, ms/token, the roofline of the decode
+kernel (algorithmic HBM bytes per step / measured kernel time, against the
+8 TB/s HBM peak) and the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"megakernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != kernel_hash:
+        return None
+    try:
+        return int(float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(model, cfg, pos0: int, budget_s: float):
+    """The CPU oracle (fp64, all host threads) on decode steps of the same model
+    at the same positions, for about `budget_s` seconds (at least 2 steps)."""
+    import oracle
+    import synth
+
+    nthreads = int(os.environ.get("ORACLE_THREADS", os.cpu_count() or 1))
+    o = oracle.Oracle(model, nthreads=nthreads)
+    k, v = synth.random_kv_prefix(cfg, pos0, seed_tag="cpu_baseline")
+    o.set_kv(k, v)
+    t = synth.first_token(cfg)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r, _ = o.step(t, pos0 + n)
+        t = r if r >= 0 else 0
+        n += 1
+        el = time.perf_counter() - t0
+        if (n >= 2 and el >= budget_s) or pos0 + n >= cfg.max_ctx:
+            break
+    return {"value": round(n / el, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n} decode steps of the same workload at positions {pos0}..{pos0 + n - 1}, "
+                      f"fp64 scalar C oracle, {nthreads} OpenMP threads, K/V prefix random",
+            "ms_per_token": round(el / n * 1e3, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="llama1b")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (a known-size kernel for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_persistent_megakernel_amd as td
+    from decode_persistent_megakernel_amd import accounting
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    model = synth.make_model(cfg)
+    print(f"[bench] generated {model.nbytes() / 1e9:.2f} GB of weights in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+    dm = td.DeviceModel(model, device=dev)
+    dec = td.Decoder(dm, cfg.max_ctx)
+    start = cfg.start_pos
+    if cfg.kv_prefix:
+        k, v = synth.kv_cache(cfg)
+        kv = td.KVCache(cfg, cfg.max_ctx, device=dev, k=k, v=v)
+        first = torch.tensor([synth.first_token(cfg)], dtype=torch.int32, device=dev)
+        del k, v
+    else:
+        kv = td.KVCache(cfg, cfg.max_ctx, device=dev)
+        prompt = synth.prompt(cfg)
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+        scratch_logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+        t_pf = time.perf_counter()
+        for i, t in enumerate(prompt):
+            tok.fill_(int(t))
+            dec.step(tok.data_ptr(), i, kv, scratch_logits)
+        torch.cuda.synchronize()
+        print(f"[bench] prefilled {len(prompt)} tokens through the decode step in "
+              f"{time.perf_counter() - t_pf:.2f}s", file=sys.stderr, flush=True)
+        first = torch.empty(1, dtype=torch.int32, device=dev)
+        first.copy_(torch.tensor([td.read_device_i32(dec.token_ptr())], dtype=torch.int32))
+    st = dec.status()
+    if st != 0:
+        print(f"device status {st} after prefill", file=sys.stderr)
+        return 1
+
+    n_steps = args.steps
+    if start + n_steps > cfg.max_ctx:
+        print(f"--steps {n_steps} exceeds the cache ({cfg.max_ctx - start} positions left)", file=sys.stderr)
+        return 1
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+    tok_ptr = dec.token_ptr()
+    stream = torch.cuda.current_stream()
+
+    def run(n, record):
+        evs = []
+        for i in range(n):
+            src = first.data_ptr() if i == 0 else tok_ptr
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            dec.step(src, start + i, kv, logits, stream=stream)
+            if record:
+                e1.record(stream)
+                evs.append((e0, e1))
+        return evs
+
+    run(min(args.warmup, cfg.max_ctx - start), False)
+    torch.cuda.synchronize()
+    if dec.status() != 0:
+        print("device error during warmup", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = run(n_steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = dec.status()
+    if st != 0:
+        print(f"device status {st} during the timed steps", file=sys.stderr)
+        return 1
+    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    total_ms = float(step_ms.sum())
+    tokens_s = n_steps / (total_ms / 1e3)
+    bytes_mean = accounting.mean_step_bytes(cfg, start, n_steps)
+    kern_ms = float(step_ms.mean())
+    achieved = bytes_mean / (kern_ms / 1e3) / 1e9
+    khash = source_hash()
+    traffic = read_traffic(args.config, khash)
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(model, cfg, start, args.cpu_budget)
+    out = {
+        "metric": "batch-1 decode tokens/s (ms/token) and % of MI355X peak HBM GB/s",
+        "value": round(tokens_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / n_steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: Llama-style decoder, {cfg.n_layers} layers, hidden {cfg.hidden}, "
+                        f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv heads x {cfg.head_dim}, intermediate "
+                        f"{cfg.intermediate}, vocab {cfg.vocab}, "
+                        f"{'int4 g64' if cfg.weight_format else 'bf16'} weights, greedy decode at positions "
+                        f"{start}..{start + n_steps - 1}, batch 1",
+            "weights": "int4-g64+fp16-scales" if cfg.weight_format else "bf16",
+            "arithmetic": "fp32 accumulate, fp32 activations, bf16 K/V cache",
+            "executor": "persistent megakernel (one cooperative launch per token)",
+            "global_batch": 1,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "td_megakernel (the whole step)",
+            "algorithmic_bytes_per_launch": int(round(bytes_mean)),
+            "kernel_ms_mean": round(kern_ms, 4),
+            "kernel_ms_p10": round(float(np.percentile(step_ms, 10)), 4),
+            "kernel_ms_p90": round(float(np.percentile(step_ms, 90)), 4),
+            "source_sha256_16": khash,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+    dec.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
