@@ -91,6 +91,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="llama1b")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--trace", default=None, help="write the in-kernel stage trace summary of one step here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (a known-size kernel for counter calibration)")
     args = ap.parse_args()
@@ -194,6 +195,18 @@ def main() -> int:
     bytes_mean = accounting.mean_step_bytes(cfg, start, n_steps)
     kern_ms = float(step_ms.mean())
     achieved = bytes_mean / (kern_ms / 1e3) / 1e9
+    if args.trace:
+        from decode_persistent_megakernel_amd import trace as tdtrace
+        tr = dec.enable_trace(True)
+        dec.step(first.data_ptr(), start, kv, logits, stream=stream)
+        torch.cuda.synchronize()
+        raw = tr.cpu().numpy()
+        np.save(os.path.splitext(args.trace)[0] + "_raw.npy", raw)
+        summ = tdtrace.summarize(raw, cfg.n_layers)
+        dec.enable_trace(False)
+        with open(args.trace, "w") as f:
+            json.dump(summ, f, indent=1)
+        print(tdtrace.format_summary(summ), file=sys.stderr, flush=True)
     khash = source_hash()
     traffic = read_traffic(args.config, khash)
     cpu = None

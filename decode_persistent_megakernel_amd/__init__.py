@@ -144,6 +144,19 @@ class Decoder:
     def last_step_ms(self) -> float:
         return float(_lib.lib().td_last_step_ms(self._h))
 
+    def enable_trace(self, on: bool = True):
+        """Returns the device trace tensor (uint64 [ncu, n_stages, 32]) that following steps fill."""
+        torch = _torch()
+        if not on:
+            _lib.check(_lib.lib().td_set_trace(self._h, None, 0), "td_set_trace")
+            self._trace = None
+            return None
+        n = int(_lib.lib().td_trace_bytes(self._h))
+        stages = 5 * self.dm.cfg.n_layers + 1
+        self._trace = torch.zeros(n // 8, dtype=torch.int64, device=self.dm.device)
+        _lib.check(_lib.lib().td_set_trace(self._h, self._trace.data_ptr(), n), "td_set_trace")
+        return self._trace.view(-1, stages, 32)
+
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             _lib.lib().td_destroy(self._h)

@@ -26,7 +26,7 @@ TD_EXEC_GRAPH = 2
 
 EXPORTED = [
     "td_create", "td_decode_step", "td_token_ptr", "td_status", "td_destroy", "td_strerror", "td_last_error",
-    "td_test_gemv", "td_test_attention", "td_set_timing", "td_last_step_ms",
+    "td_test_gemv", "td_test_attention", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
 ]
 
 
@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.td_set_timing.argtypes = [vp, i32]
         L.td_last_step_ms.restype = f32
         L.td_last_step_ms.argtypes = [vp]
+        L.td_trace_bytes.restype = ctypes.c_int64
+        L.td_trace_bytes.argtypes = [vp]
+        L.td_set_trace.restype = i32
+        L.td_set_trace.argtypes = [vp, vp, ctypes.c_int64]
         _lib = L
     return _lib
 

@@ -45,6 +45,8 @@ struct td_ctx {
   td_kparams kp{};
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
+  void* wstream = nullptr;      // packed weight streams (code chunks, then int4 scales)
+  size_t wstream_bytes = 0;
   td_layer_dev* d_layers = nullptr;
   float* d_rope = nullptr;
   hipStream_t last_stream = nullptr;
@@ -181,14 +183,19 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
   const int qd = nq * d, kvd = nkv * d, qkv_rows = qd + 2 * kvd;
 
-  // attention split: at most one task per CU, chunks a multiple of the tile
+  // attention split: at most one task per CU, chunks a multiple of the tile,
+  // at most 64 chunks per kv head, and the merge staging within 24 KiB of LDS
   const int cmax_by_cu = ncu / nkv;
   int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
-  const int n_chunks_max = (c.max_ctx + chunk_len - 1) / chunk_len;
+  auto n_chunks_of = [&](int cl) { return (c.max_ctx + cl - 1) / cl; };
+  while (n_chunks_of(chunk_len) > 64 || (int64_t)n_chunks_of(chunk_len) * group * (d + 4) * 4 > 24 * 1024)
+    chunk_len += TD_TILE;
+  const int n_chunks_max = n_chunks_of(chunk_len);
   if (n_chunks_max * nkv > ncu) return fail(TD_E_PLAN, "attention split exceeds the CU count");
+  if ((qkv_rows / 2 + ncu - 1) / ncu > 64) return fail(TD_E_UNSUPPORTED, "more than 64 QKV row pairs per CU");
 
   // LDS layout
-  const td_attn_lds A = td_attn_layout(d, group);
+  const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
   const int64_t kpad = round_up(std::max({H, qd, I}), 2048);
   const int64_t xin_bytes = std::max<int64_t>(kpad * 4, A.bytes);
   auto per_cu = [&](int64_t U) { return (int)((U + ncu - 1) / ncu); };
@@ -197,6 +204,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const int64_t lds_cap = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
   int ring = 0;
   td_kparams kp{};
+  uint64_t stream_code_chunks = 0, stream_scale_blocks = 0;
   for (int S : {16, 12, 8}) {
     int64_t off = 0;
     kp.off_ring = (int32_t)off;
@@ -206,10 +214,18 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     kp.off_xin = (int32_t)off;
     kp.off_attn = (int32_t)off;
     off += round_up(xin_bytes, 256);
+    kp.off_tile = (int32_t)off;
+    off += round_up(td_tile_bytes(d), 256);
     kp.off_out = (int32_t)off;
     off += (int64_t)out_floats * 4;
     kp.off_own = (int32_t)off;
     off += (int64_t)own_floats * 4;
+    kp.off_gain = (int32_t)off;
+    off += round_up((int64_t)H * 2, 256);
+    kp.off_rope = (int32_t)off;
+    off += round_up((int64_t)d * 4, 256);
+    kp.off_wtrace = (int32_t)off;
+    off += (TD_NW + 1) * 4 * 8;
     if (off <= lds_cap && off <= 160 * 1024) {
       int blocks = 0;
       int oe = td_megakernel_occupancy(S, (int)off, &blocks);
@@ -225,6 +241,44 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   rc = validate_plan(c, ncu, out_floats, own_floats);
   if (rc) return rc;
 
+  // every compute wave's packed stream, counted exactly as the kernel walks it:
+  // stages in order (attention has no weights), the wave's units, their rows,
+  // the row's chunks
+  std::vector<td_wstream> ws((size_t)ncu * TD_NW);
+  {
+    struct St {
+      int U, rpu, K, fmt;
+    };
+    std::vector<St> stages;
+    for (int l = 0; l < L; ++l) {
+      stages.push_back({qkv_rows / 2, 2, H, c.weight_format});
+      stages.push_back({H, 1, qd, c.weight_format});
+      stages.push_back({I, 2, H, c.weight_format});
+      stages.push_back({H, 1, I, c.weight_format});
+    }
+    stages.push_back({V, 1, H, TD_WF_BF16});
+    uint64_t code = 0, scal = 0;
+    for (int cu = 0; cu < ncu; ++cu)
+      for (int wave = 0; wave < TD_NW; ++wave) {
+        uint64_t nt = 0, n4 = 0;
+        for (const St& st : stages) {
+          const int u0 = (int)(((int64_t)st.U * cu) / ncu), u1 = (int)(((int64_t)st.U * (cu + 1)) / ncu);
+          const int cnt = u1 - u0;
+          const int n = cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0;
+          const int row_bytes = st.fmt == TD_WF_BF16 ? st.K * 2 : st.K / 2;
+          const uint64_t ch = (uint64_t)n * st.rpu * ((row_bytes + TD_CHUNK - 1) / TD_CHUNK);
+          nt += ch;
+          if (st.fmt == TD_WF_INT4_G64) n4 += ch;
+        }
+        if (code + nt > 0xffffffffull || scal + n4 > 0xffffffffull) return fail(TD_E_UNSUPPORTED, "model too large");
+        ws[(size_t)cu * TD_NW + wave] = {(uint32_t)code, (uint32_t)scal, (uint32_t)nt, (uint32_t)n4};
+        code += nt;
+        scal += n4;
+      }
+    stream_code_chunks = code;
+    stream_scale_blocks = scal;
+  }
+
   td_ctx* ctx = new (std::nothrow) td_ctx();
   if (!ctx) return fail(TD_E_NOMEM, "host allocation failed");
   ctx->cfg = c;
@@ -233,21 +287,24 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   ctx->ring = ring;
 
   // scratch: one allocation, 256-byte aligned pieces
-  const int sync_words = (int)round_up(TD_SY_MERGE + L * nkv, 64);
+  const int sync_words = TD_SY_WORDS;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off += (size_t)round_up((int64_t)bytes, 256);
     return o;
   };
-  const size_t o_x = take((size_t)H * 4), o_q = take((size_t)qd * 4), o_o = take((size_t)qd * 4);
-  const size_t o_act = take((size_t)I * 4);
-  const size_t o_part = take((size_t)nkv * n_chunks_max * group * (d + 2) * 4);
+  const size_t o_xmid = take((size_t)H * 8), o_xout = take((size_t)H * 8);
+  const size_t o_q = take((size_t)(qd + 2 * kvd) * 8), o_o = take((size_t)qd * 8);
+  const size_t o_act = take((size_t)I * 8);
+  const size_t o_part = take((size_t)nkv * n_chunks_max * group * (d + 4) * 8);
   const size_t o_cand = take((size_t)ncu * 4 * 4);
   const size_t o_sync = take((size_t)sync_words * 4);
   const size_t o_tok = take(4), o_err = take(4);
   const size_t o_rope = take((size_t)c.max_ctx * (d / 2) * 2 * 4);
   const size_t o_layers = take(sizeof(td_layer_dev) * L);
+  const size_t o_ws = take(sizeof(td_wstream) * ws.size());
+  const size_t o_bad = take(4);
   ctx->scratch_bytes = off;
   e = hipMalloc(&ctx->scratch, off);
   if (e != hipSuccess) {
@@ -288,6 +345,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   }
   e = hipMemcpy(base + o_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_layers, layers.data(), sizeof(td_layer_dev) * L, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_ws, ws.data(), sizeof(td_wstream) * ws.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(ctx->scratch);
     delete ctx;
@@ -317,16 +375,44 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   kp.head = (const uint16_t*)w->head;
   kp.final_norm = (const uint16_t*)w->final_norm;
   kp.rope_cs = (const float*)(base + o_rope);
-  kp.x = (float*)(base + o_x);
-  kp.q = (float*)(base + o_q);
-  kp.o = (float*)(base + o_o);
-  kp.act = (float*)(base + o_act);
-  kp.part = (float*)(base + o_part);
+  kp.tx_mid = (uint2*)(base + o_xmid);
+  kp.tx_out = (uint2*)(base + o_xout);
+  kp.tq = (uint2*)(base + o_q);
+  kp.to = (uint2*)(base + o_o);
+  kp.tact = (uint2*)(base + o_act);
+  kp.tpart = (uint2*)(base + o_part);
   kp.cand = (uint32_t*)(base + o_cand);
   kp.sync = (uint32_t*)(base + o_sync);
   kp.token_out = (int32_t*)(base + o_tok);
   kp.err = (int32_t*)(base + o_err);
   kp.n_stages = 5 * L + 1;
+  kp.ws = (const td_wstream*)(base + o_ws);
+
+  // pack the weights into the per-wave streams
+  const size_t code_bytes = (size_t)stream_code_chunks * TD_CHUNK;
+  ctx->wstream_bytes = code_bytes + (size_t)stream_scale_blocks * TD_SCHUNK + TD_CHUNK;
+  e = hipMalloc(&ctx->wstream, ctx->wstream_bytes);
+  if (e != hipSuccess) {
+    (void)hipFree(ctx->scratch);
+    delete ctx;
+    return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of the weight streams failed")
+                                    : hip_fail(e, "hipMalloc");
+  }
+  kp.wcode = (const uint8_t*)ctx->wstream;
+  kp.wscale = (const uint8_t*)ctx->wstream + code_bytes;
+  int le = td_launch_repack(&kp, ncu, (uint8_t*)ctx->wstream, (uint8_t*)ctx->wstream + code_bytes, kp.ws,
+                            (int*)(base + o_bad), nullptr);
+  int bad = 0;
+  if (le == 0) e = hipDeviceSynchronize();
+  if (le == 0 && e == hipSuccess) e = hipMemcpy(&bad, base + o_bad, 4, hipMemcpyDeviceToHost);
+  if (le != 0 || e != hipSuccess || bad) {
+    (void)hipFree(ctx->wstream);
+    (void)hipFree(ctx->scratch);
+    delete ctx;
+    if (le) return hip_fail((hipError_t)le, "repack launch");
+    if (e != hipSuccess) return hip_fail(e, "repack");
+    return fail(TD_E_PLAN, "packed weight stream disagrees with the plan");
+  }
   ctx->kp = kp;
   *out = ctx;
   return TD_OK;
@@ -384,6 +470,7 @@ void td_destroy(td_ctx* ctx) {
   if (ctx->ev0) (void)hipEventDestroy(ctx->ev0);
   if (ctx->ev1) (void)hipEventDestroy(ctx->ev1);
   if (ctx->scratch) (void)hipFree(ctx->scratch);
+  if (ctx->wstream) (void)hipFree(ctx->wstream);
   delete ctx;
 }
 
@@ -405,6 +492,18 @@ float td_last_step_ms(td_ctx* ctx) {
   float ms = -1.f;
   if (hipEventElapsedTime(&ms, ctx->ev0, ctx->ev1) != hipSuccess) return -1.f;
   return ms;
+}
+
+int64_t td_trace_bytes(const td_ctx* ctx) {
+  if (!ctx) return -1;
+  return (int64_t)ctx->ncu * ctx->kp.n_stages * TD_TRACE_STAMPS * 8;
+}
+
+int td_set_trace(td_ctx* ctx, void* d_buf, int64_t bytes) {
+  if (!ctx) return fail(TD_E_INVALID_ARG, "null ctx");
+  if (d_buf && bytes < td_trace_bytes(ctx)) return fail(TD_E_INVALID_ARG, "trace buffer too small");
+  ctx->kp.trace = (uint64_t*)d_buf;
+  return TD_OK;
 }
 
 int td_test_gemv(int32_t fmt, const void* w, const void* scales, int32_t rows, int32_t cols, const float* d_x,

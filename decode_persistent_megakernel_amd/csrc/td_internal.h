@@ -8,7 +8,7 @@
 #define TD_THREADS ((TD_NW + 1) * TD_WAVE)  // + one sync wave
 #define TD_TILE 64                    // attention positions per LDS tile
 #define TD_CHUNK 1024                 // bytes per wave-wide weight chunk (64 lanes x 16 B)
-#define TD_SCHUNK 256                 // bytes per int4 scale chunk (64 lanes x 4 B)
+#define TD_SCHUNK 64                  // bytes of fp16 scales per int4 chunk (32 scales)
 #define TD_MAX_GROUP 8                // query heads per kv head handled by one task
 #define TD_SPIN_TICKS 100000000ull    // grid-wait limit in 100 MHz ticks (1 s)
 
@@ -18,15 +18,12 @@ enum { TD_ST_QKV = 0, TD_ST_ATTN = 1, TD_ST_O = 2, TD_ST_GU = 3, TD_ST_DOWN = 4,
 // error bits of the device error word
 enum { TD_ERRBIT_NONFINITE = 1, TD_ERRBIT_RANGE = 2, TD_ERRBIT_TIMEOUT = 4 };
 
-// uint32 word offsets inside the sync area; each group on its own 256 B line(s)
+// uint32 word offsets inside the sync area (each on its own 256-byte line)
 enum {
-  TD_SY_EPOCH = 0,
-  TD_SY_GCTR = 64,
-  TD_SY_XCTR = 128,            // 8 lines: per-XCD arrival counters
-  TD_SY_XREL = 128 + 8 * 64,   // 8 lines: per-XCD release words
-  TD_SY_ABORT = 128 + 16 * 64,
-  TD_SY_FINAL = TD_SY_ABORT + 64,
-  TD_SY_MERGE = TD_SY_FINAL + 64  // n_layers * n_kv_heads attention-merge counters
+  TD_SY_EPOCH = 0,    // launches completed (the tag base of the next launch)
+  TD_SY_ABORT = 64,   // set when a wait timed out
+  TD_SY_FINAL = 128,  // arrivals at the greedy-token reduction
+  TD_SY_WORDS = 192
 };
 
 struct td_layer_dev {
@@ -35,6 +32,13 @@ struct td_layer_dev {
   const uint16_t* bias;    // bf16 QKV bias or null
   const uint16_t* attn_norm;
   const uint16_t* mlp_norm;
+};
+
+// One compute wave's weight stream: its chunks for the whole step, in the
+// order it consumes them, packed contiguously (code_off in 1 KiB chunks), and
+// for the leading n4 int4 chunks their scales (scale_off in 64-byte blocks).
+struct td_wstream {
+  uint32_t code_off, scale_off, n_tot, n4;
 };
 
 struct td_kparams {
@@ -56,44 +60,74 @@ struct td_kparams {
   uint16_t* vc;
   const int32_t* token_in;
   float* logits;
-  // scratch (ctx-owned)
-  float* x;      // [H] residual stream
-  float* q;      // [nq d]
-  float* o;      // [nq d] merged attention output
-  float* act;    // [I]
-  float* part;   // [nkv][n_chunks_max][group][d + 2]
+  // scratch (ctx-owned).  Every value handed from one CU to another is
+  // published as a (value bits, tag) pair written with one 8-byte agent-scope
+  // store; tag = launch epoch * n_stages + stage + 1 names the producing stage,
+  // and readers poll until every pair they need carries the tag they expect.
+  uint2* tx_mid;   // [H] residual after the attention block
+  uint2* tx_out;   // [H] residual after the MLP block
+  uint2* tq;       // [nkv][(group + 2) d]: per kv head its rotated queries, then this
+                   // position's K row (rotated) and V row (bf16 values)
+  uint2* to;       // [nq d] attention output
+  uint2* tact;     // [I] SiLU(gate) * up
+  uint2* tpart;    // [nkv][n_chunks_max][group][d + 4] attention partials: acc[d], m, l, pad
   uint32_t* cand;  // [ncu][4]: value bits, index, nonfinite
   uint32_t* sync;
   int32_t* token_out;
   int32_t* err;
   // LDS layout (byte offsets into dynamic shared memory)
-  int32_t off_ring, off_sring, off_xin, off_out, off_own, off_attn;
+  int32_t off_ring, off_sring, off_xin, off_out, off_own, off_attn, off_tile;
   int32_t lds_bytes;
   int32_t n_stages;   // 5 L + 1
+  uint64_t* trace;    // optional: [ncu][n_stages][TD_TRACE_STAMPS] 100 MHz timestamps, or null
+  // packed weight streams (built at create time)
+  const uint8_t* wcode;
+  const uint8_t* wscale;
+  const td_wstream* ws;   // [ncu][TD_NW]
+  int32_t off_gain, off_rope;  // LDS: next norm's bf16 gains [H]; (cos, sin) of pos for the d/2 pairs
+  int32_t off_wtrace;          // LDS: per compute wave 4 uint64 trace stamps
 };
 
-// LDS offsets inside the attention area (bytes, relative to off_attn)
+// Per (CU, stage) trace record of TD_TRACE_STAMPS uint64 timestamps (100 MHz):
+// [0..4] sync wave: stage start, inputs staged, compute finished, epilogue
+// finished, next stage's prefetches issued; [8 + 3 w + k] compute wave w:
+// stage start, first chunk ready, last chunk done (0 when the wave has no chunk).
+#define TD_TRACE_STAMPS 32
+
+// LDS layout of the attention stage.  The K/V tile area is separate (it is
+// filled while the QKV stage still uses the GEMV input area); the rest aliases
+// the GEMV input area.  K rows are padded by 8 elements so that lanes reading
+// different rows hit different banks.
+#ifdef __HIPCC__
+__host__ __device__
+#endif
+static inline int32_t td_tile_bytes(int d) {
+  return TD_TILE * (d + 8) * 2 + TD_TILE * d * 2;
+}
+
 struct td_attn_lds {
-  int32_t q, k, v, p, part, bytes;
+  int32_t q, p, part, kvp, merge, bytes;
 };
 
 #ifdef __HIPCC__
 __host__ __device__
 #endif
-static inline td_attn_lds td_attn_layout(int d, int group) {
+static inline td_attn_lds td_attn_layout(int d, int group, int n_chunks_max) {
   td_attn_lds a;
-  a.q = 0;
-  a.k = a.q + group * d * 4;
-  a.v = a.k + TD_TILE * (d + 8) * 2;
-  a.p = a.v + TD_TILE * d * 2;
-  a.part = a.p + group * TD_TILE * 4;
-  a.bytes = a.part + group * (d + 2) * 4;
+  a.q = 0;                                          // group x d queries, then this
+  a.kvp = a.q + group * d * 4;                      // position's K and V rows (2 d floats)
+  a.p = a.kvp + 2 * d * 4;                          // group x 64 probabilities
+  a.part = a.p + group * TD_TILE * 4;               // group x (d + 4) own partial
+  a.merge = a.part + group * (d + 4) * 4;           // other chunks' partials
+  a.bytes = a.merge + (n_chunks_max > 1 ? n_chunks_max - 1 : 1) * group * (d + 4) * 4;
   a.bytes = (a.bytes + 255) & ~255;
   return a;
 }
 
 // launch entry points (td_kernels.hip)
 int td_launch_megakernel(const td_kparams* p, int ncu, int ring_slots, void* stream);
+int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
+                     void* stream);
 int td_megakernel_occupancy(int ring_slots, int lds_bytes, int* blocks_per_cu);
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,
                         void* stream);

@@ -67,23 +67,6 @@ DEV void vmcnt_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// 8 agent-scope 16-byte loads, completed before the block ends
-DEV void ld8x4_sc1(const void* const (&a)[8], u32x4 (&r)[8]) {
-  asm volatile(
-      "global_load_dwordx4 %0, %8, off sc1\n\t"
-      "global_load_dwordx4 %1, %9, off sc1\n\t"
-      "global_load_dwordx4 %2, %10, off sc1\n\t"
-      "global_load_dwordx4 %3, %11, off sc1\n\t"
-      "global_load_dwordx4 %4, %12, off sc1\n\t"
-      "global_load_dwordx4 %5, %13, off sc1\n\t"
-      "global_load_dwordx4 %6, %14, off sc1\n\t"
-      "global_load_dwordx4 %7, %15, off sc1\n\t"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-
 // ------------------------------------------------------------ number formats
 DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -261,59 +244,77 @@ DEV void cur_next(Cursor& c, const td_kparams& P, int wave, int cu, int ncu) {
   cur_enter(c, P, wave, cu, ncu, c.seq + 1);
 }
 
-// Start the DMA of the cursor's chunk into one ring slot.  Lanes past the end
-// of the row (K not a multiple of the chunk) fetch the row start instead and
-// are masked out of the arithmetic.
-DEV void issue_chunk(const Cursor& c, const td_kparams& P, uint8_t* slot, uint8_t* sslot, int lane) {
-  int u = c.u_first + c.k * TD_NW;
-  int row = unit_row(P, c.g.kind, u, c.r);
-  int boff = c.j * TD_CHUNK + lane * 16;
-  bool valid = boff < c.g.row_bytes;
-  const uint8_t* src = c.g.w + (size_t)row * c.g.row_bytes + (valid ? boff : 0);
-  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)slot, 16, 0, 0);
-  if (c.g.fmt == 1) {
-    // scale pair (2m, 2m + 1) with m = 16 j + lane / 4 holds this lane's scale
-    int sw = valid ? c.j * 16 + (lane >> 2) : 0;
-    const uint32_t* ss = (const uint32_t*)(c.g.s + (size_t)row * (c.g.K / 64)) + sw;
-    __builtin_amdgcn_global_load_lds((const void*)ss, (__attribute__((address_space(3))) void*)sslot, 4, 0, 0);
-  }
+// ------------------------------------------------------------ hand-off of activations
+// A value handed to other CUs is a (value bits, tag) pair written with one
+// 8-byte agent-scope store; readers poll the pairs with agent-scope loads until
+// every one carries the tag they expect.  The data is its own ready signal, so
+// a stage waits exactly for the values it reads (no grid-wide barrier), and a
+// buffer is only rewritten after every reader of its previous contents has
+// provably moved on (each stage reads the complete output of the one before).
+#define TD_CPOL_SC1 16  // buffer-load cache policy: agent scope
+
+DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-// ------------------------------------------------------------ grid barrier
-DEV int spin_ge(uint32_t* p, uint32_t target, uint32_t* abortf) {
-  uint64_t t0 = wall_clock64();
-  for (uint32_t it = 0;; ++it) {
-    if ((int32_t)(ld_u(p) - target) >= 0) return 1;
-    if ((it & 63u) == 63u) {
-      if (ld_u(abortf)) return 0;
-      if (wall_clock64() - t0 > TD_SPIN_TICKS) {
-        st_u(abortf, 1u);
-        return 0;
+DEV void st_tag(uint2* p, float v, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(w) : "memory");
+}
+
+DEV bool wait_expired(const td_kparams& P, uint64_t t0) {
+  if (ld_u(P.sync + TD_SY_ABORT)) return true;
+  if (wall_clock64() - t0 > TD_SPIN_TICKS) {
+    st_u(P.sync + TD_SY_ABORT, 1u);
+    return true;
+  }
+  return false;
+}
+
+// Waits until the n pairs at src (n even) all carry `tag` and copies their
+// values to dst (LDS).  Each round loads W 16-byte units per lane and re-polls
+// the units still missing.  false: the wait timed out (or another wait did).
+template <int W>
+DEV bool poll_vec_w(const td_kparams& P, const uint2* src, int n, uint32_t tag, float* dst) {
+  const int lane = lane_id();
+  const int nu = n >> 1;  // 16-byte units of two pairs
+  const __amdgpu_buffer_rsrc_t R = rsrc(src, (uint32_t)nu * 16u);
+  const uint64_t t0 = wall_clock64();
+  for (int b0 = 0; b0 < nu; b0 += W * 64) {
+    uint32_t pend = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+      if (b0 + k * 64 + lane < nu) pend |= 1u << k;
+    for (uint32_t it = 0;; ++it) {
+      u32x4 r[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k)
+        r[k] = __builtin_amdgcn_raw_buffer_load_b128(R, (uint32_t)(b0 + k * 64 + lane) * 16u, 0, TD_CPOL_SC1);
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
+          const int u = b0 + k * 64 + lane;
+          dst[2 * u] = __uint_as_float(r[k].x);
+          dst[2 * u + 1] = __uint_as_float(r[k].z);
+          pend &= ~(1u << k);
+        }
       }
+      if (!__any(pend != 0u)) break;
+      if ((it & 3u) == 3u && uni(wait_expired(P, t0) ? 1 : 0)) return false;
     }
   }
+  return true;
 }
 
-// gen: this barrier's global generation number (launch epoch * barriers per launch + index)
-DEV bool grid_barrier(const td_kparams& P, uint32_t gen) {
-  uint32_t* S = P.sync;
-  int ok = 1;
-  if (lane_id() == 0) {
-    uint32_t x = blockIdx.x & 7u;
-    uint32_t per = gridDim.x >> 3;
-    uint32_t old = atomicAdd(S + TD_SY_XCTR + x * 64u, 1u);
-    if (old + 1u == (gen + 1u) * per) {
-      atomicAdd(S + TD_SY_GCTR, 1u);
-      ok = spin_ge(S + TD_SY_GCTR, (gen + 1u) * 8u, S + TD_SY_ABORT);
-      st_u(S + TD_SY_XREL + x * 64u, gen + 1u);
-    } else {
-      ok = spin_ge(S + TD_SY_XREL + x * 64u, gen + 1u, S + TD_SY_ABORT);
-    }
-  }
-  return uni(ok) != 0;
+DEV bool poll_vec(const td_kparams& P, const uint2* src, int n, uint32_t tag, float* dst) {
+  return poll_vec_w<16>(P, src, n, tag, dst);
 }
 
 // ------------------------------------------------------------ attention task
+// Split-K decode attention: kv head g's positions 0..pos are cut into chunks of
+// chunk_len; one CU per (g, chunk) computes a partial (m, l, acc) for the g's
+// query heads; the CU of chunk 0 merges the partials ("One launch per token",
+// "The attention trap").
 struct AttnTask {
   int valid, g, c, t0, t1, ntiles, n_used;
 };
@@ -329,125 +330,148 @@ DEV AttnTask attn_task(const td_kparams& P, int cu) {
   return t;
 }
 
-// compute waves: wave h < group handles query head g * group + h
-DEV void attn_compute(const td_kparams& P, uint8_t* lds, int wave) {
+// compute waves: wave h < group handles query head g * group + h.  Returns
+// the trace stamp taken after the first tile's scores (0 without a trace).
+DEV uint64_t attn_compute(const td_kparams& P, uint8_t* lds, int wave) {
   const AttnTask T = attn_task(P, blockIdx.x);
-  if (!T.valid) return;
+  uint64_t stamp = 0;
+  if (!T.valid) return 0;
   const int lane = lane_id();
   const int d = P.d;
-  const td_attn_lds A = td_attn_layout(d, P.group);
+  const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max);
   uint8_t* base = lds + P.off_attn;
   const float* qs = (const float*)(base + A.q) + wave * d;
-  const uint16_t* kt = (const uint16_t*)(base + A.k);
-  const uint16_t* vt = (const uint16_t*)(base + A.v);
+  const uint16_t* kt = (const uint16_t*)(lds + P.off_tile);
+  const uint16_t* vt = kt + TD_TILE * (d + 8);
   float* ps = (float*)(base + A.p) + wave * TD_TILE;
   float m = -__builtin_inff(), l = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int tile = 0; tile < T.ntiles; ++tile) {
     wg_bar();  // tile in LDS
     if (wave < P.group) {
       const int nv = min(TD_TILE, T.t1 - (T.t0 + tile * TD_TILE));
+      // lane tau: score of position t0 + tau
       float s = -__builtin_inff();
       if (lane < nv) {
         const uint16_t* kr = kt + lane * (d + 8);
         float a = 0.f;
         for (int e = 0; e < d; e += 8) {
-          u32x4 kw = *(const u32x4*)(kr + e);
-          a = fmaf(bf_lo(kw.x), qs[e + 0], a);
-          a = fmaf(bf_hi(kw.x), qs[e + 1], a);
-          a = fmaf(bf_lo(kw.y), qs[e + 2], a);
-          a = fmaf(bf_hi(kw.y), qs[e + 3], a);
-          a = fmaf(bf_lo(kw.z), qs[e + 4], a);
-          a = fmaf(bf_hi(kw.z), qs[e + 5], a);
-          a = fmaf(bf_lo(kw.w), qs[e + 6], a);
-          a = fmaf(bf_hi(kw.w), qs[e + 7], a);
+          const u32x4 kw = *(const u32x4*)(kr + e);
+          const f32x4 q0 = *(const f32x4*)(qs + e), q1 = *(const f32x4*)(qs + e + 4);
+          a = fmaf(bf_lo(kw.x), q0.x, a);
+          a = fmaf(bf_hi(kw.x), q0.y, a);
+          a = fmaf(bf_lo(kw.y), q0.z, a);
+          a = fmaf(bf_hi(kw.y), q0.w, a);
+          a = fmaf(bf_lo(kw.z), q1.x, a);
+          a = fmaf(bf_hi(kw.z), q1.y, a);
+          a = fmaf(bf_lo(kw.w), q1.z, a);
+          a = fmaf(bf_hi(kw.w), q1.w, a);
         }
         s = a;
       }
       const float mt = wave_max(s);
       const float mn = fmaxf(m, mt);
-      const float p = lane < nv ? expf(s - mn) : 0.f;
-      const float corr = expf(m - mn);
+      const float p = lane < nv ? __expf(s - mn) : 0.f;
+      const float corr = __expf(m - mn);
       l = l * corr + wave_sum(p);
       m = mn;
-      ps[lane] = p;
       acc0 *= corr;
       acc1 *= corr;
-      for (int t = 0; t < nv; ++t) {
-        const float pt = ps[t];
-        acc0 = fmaf(pt, bf16f(vt[t * d + lane]), acc0);
-        if (d > 64) acc1 = fmaf(pt, bf16f(vt[t * d + 64 + lane]), acc1);
+      if (P.trace && tile == 0) stamp = wall_clock64();
+      // lane e: sum over tau of p_tau V[tau][e]; p_tau is read from lane tau
+      for (int t0 = 0; t0 < nv; t0 += 16) {
+        float v0[16], v1[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int t = t0 + k < nv ? t0 + k : t0;
+          v0[k] = bf16f(vt[t * d + lane]);
+          v1[k] = d > 64 ? bf16f(vt[t * d + 64 + lane]) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (t0 + k < nv) {
+            const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t0 + k));
+            acc0 = fmaf(pt, v0[k], acc0);
+            if (d > 64) acc1 = fmaf(pt, v1[k], acc1);
+          }
+        }
       }
     }
     wg_bar();  // tile consumed
   }
   if (wave < P.group) {
-    float* pr = (float*)(base + A.part) + wave * (d + 2);
+    float* pr = (float*)(base + A.part) + wave * (d + 4);
     pr[lane] = acc0;
     if (d > 64) pr[64 + lane] = acc1;
     if (lane == 0) {
       pr[d] = m;
       pr[d + 1] = l;
+      pr[d + 2] = 0.f;
+      pr[d + 3] = 0.f;
+    }
+  }
+  return stamp;
+}
+
+// sync wave: K and V rows [tb, tb + nv) of the tile, except row pos (written
+// during this very step; it comes from the published copy), into the LDS tile
+DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask& T, int tile) {
+  const int lane = lane_id();
+  const int d = P.d;
+  const int tb = T.t0 + tile * TD_TILE;
+  const int nv = min(TD_TILE, T.t1 - tb);
+  const size_t head_off = ((size_t)layer * P.nkv + T.g) * P.max_ctx;
+  const __amdgpu_buffer_rsrc_t RK = rsrc(P.kc + (head_off + tb) * d, (uint32_t)(nv * d * 2));
+  const __amdgpu_buffer_rsrc_t RV = rsrc(P.vc + (head_off + tb) * d, (uint32_t)(nv * d * 2));
+  uint16_t* kt = (uint16_t*)(lds + P.off_tile);
+  uint16_t* vt = kt + TD_TILE * (d + 8);
+  const int q16 = d / 8;  // 16-byte pieces per row
+  const int npiece = nv * q16;
+  for (int i0 = 0; i0 < npiece; i0 += 8 * 64) {
+    u32x4 kr[8], vr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t off = (uint32_t)(i0 + k * 64 + lane) * 16u;  // out of range reads 0
+      kr[k] = __builtin_amdgcn_raw_buffer_load_b128(RK, off, 0, 0);
+      vr[k] = __builtin_amdgcn_raw_buffer_load_b128(RV, off, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = i0 + k * 64 + lane;
+      if (i < npiece) {
+        const int row = i / q16, pc = i - row * q16;
+        if (tb + row != P.pos) {
+          *(u32x4*)(kt + row * (d + 8) + pc * 8) = kr[k];
+          *(u32x4*)(vt + row * d + pc * 8) = vr[k];
+        }
+      }
     }
   }
 }
 
-// sync wave: loads the K and V rows of each tile into LDS
-DEV void attn_load_tiles(const td_kparams& P, uint8_t* lds, int layer) {
-  const AttnTask T = attn_task(P, blockIdx.x);
-  if (!T.valid) return;
-  const int lane = lane_id();
-  const int d = P.d;
-  const td_attn_lds A = td_attn_layout(d, P.group);
-  uint8_t* base = lds + P.off_attn;
-  const size_t head_off = ((size_t)layer * P.nkv + T.g) * P.max_ctx;
-  const uint16_t* kg = P.kc + head_off * d;
-  const uint16_t* vg = P.vc + head_off * d;
-  const int q16 = d / 8;  // 16-byte pieces per row
-  for (int tile = 0; tile < T.ntiles; ++tile) {
-    const int tb = T.t0 + tile * TD_TILE;
-    const int nv = min(TD_TILE, T.t1 - tb);
-    const int npiece = nv * q16;
-    for (int i0 = 0; i0 < npiece; i0 += 8 * 64) {
-      const void* ka[8];
-      const void* va[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        int i = i0 + k * 64 + lane;
-        int ii = i < npiece ? i : 0;
-        int row = ii / q16, pc = ii - row * q16;
-        ka[k] = kg + (size_t)(tb + row) * d + pc * 8;
-        va[k] = vg + (size_t)(tb + row) * d + pc * 8;
-      }
-      u32x4 kr[8], vr[8];
-      ld8x4_sc1(ka, kr);
-      ld8x4_sc1(va, vr);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        int i = i0 + k * 64 + lane;
-        if (i < npiece) {
-          int row = i / q16, pc = i - row * q16;
-          *(u32x4*)(base + A.k + (row * (d + 8) + pc * 8) * 2) = kr[k];
-          *(u32x4*)(base + A.v + (row * d + pc * 8) * 2) = vr[k];
-        }
-      }
-    }
-    wg_bar();  // tile in LDS
-    wg_bar();  // tile consumed
+// writes this position's K and V rows (from LDS, fp32 holding bf16 values)
+// into the tile when the tile holds position pos
+DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int tile) {
+  const int tb = T.t0 + tile * TD_TILE;
+  if (P.pos < tb || P.pos >= tb + TD_TILE || P.pos >= T.t1) return;
+  const int d = P.d, row = P.pos - tb;
+  const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max);
+  const float* kvp = (const float*)(lds + P.off_attn + A.kvp);
+  uint16_t* kt = (uint16_t*)(lds + P.off_tile);
+  uint16_t* vt = kt + TD_TILE * (d + 8);
+  for (int e = lane_id(); e < d; e += 64) {
+    kt[row * (d + 8) + e] = (uint16_t)(__float_as_uint(kvp[e]) >> 16);
+    vt[row * d + e] = (uint16_t)(__float_as_uint(kvp[d + e]) >> 16);
   }
 }
 
 // ------------------------------------------------------------ compute waves
-template <int S>
-DEV void compute_transition(const td_kparams& P, uint8_t* lds, int wave, int from, int to) {
-  for (int s = from; s < to; ++s) {
-    wg_bar();  // end of stage s: outputs in LDS
-    if (s + 1 >= P.n_stages) return;
-    wg_bar();  // stage s + 1 inputs in LDS
-    int kind, layer;
-    stage_of(P, s + 1, kind, layer);
-    if (kind == TD_ST_ATTN) attn_compute(P, lds, wave);
-  }
-}
+// A compute wave walks its packed weight stream (one contiguous array per wave,
+// built at create time in exactly the order consumed here): chunk t lands in
+// ring slot t % S, and the DMA of chunk t + S is issued as soon as chunk t has
+// been read out of its slot.  The DMA never waits for a stage boundary, so the
+// next stage's weights stream in while this CU waits at the grid barrier.
+#define TD_DMA_NT 2  // cache policy of the weight stream: non-temporal
+#define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int S>
 DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
@@ -457,100 +481,103 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   uint8_t* sring = lds + P.off_sring + wave * S * TD_SCHUNK;
   const float* xin = (const float*)(lds + P.off_xin);
   float* out = (float*)(lds + P.off_out);
-
-  Cursor use, fe;
-  cur_enter(use, P, wave, cu, ncu, 0);
-  fe = use;
-  int issued = 0;
-  int last_int4 = 0;
+  const td_wstream& W = P.ws[cu * TD_NW + wave];
+  const uint32_t n_tot = W.n_tot, n4 = W.n4;
+  const uint8_t* fptr = P.wcode + (size_t)W.code_off * TD_CHUNK + lane * 16;
+  const uint8_t* sptr = P.wscale + (size_t)W.scale_off * TD_SCHUNK + lane * 4;
+  uint32_t issued = 0;
+  auto issue = [&](int slot) {
+    __builtin_amdgcn_global_load_lds((const void*)fptr, LDSPTR(ring + slot * TD_CHUNK), 16, 0, TD_DMA_NT);
+    fptr += TD_CHUNK;
+    if (issued < n4) {  // the chunk's 32 fp16 scales: 16 lanes x 4 bytes
+      if (lane < 16)
+        __builtin_amdgcn_global_load_lds((const void*)sptr, LDSPTR(sring + slot * TD_SCHUNK), 4, 0, TD_DMA_NT);
+      sptr += TD_SCHUNK;
+    }
+    ++issued;
+  };
 #pragma unroll
-  for (int t = 0; t < S; ++t) {
-    if (fe.seq < P.n_stages) {
-      issue_chunk(fe, P, ring + t * TD_CHUNK, sring + t * TD_SCHUNK, lane);
-      last_int4 = fe.g.fmt;
-      cur_next(fe, P, wave, cu, ncu);
-      ++issued;
-    }
-  }
+  for (int t = 0; t < S; ++t)
+    if (issued < n_tot) issue(t);
 
-  int cur = 0;
-  wg_bar();  // stage 0 inputs in LDS
-  float acc = 0.f;
+  uint32_t t = 0;  // chunks consumed
   int slot = 0;
-  for (int t = 0; use.seq < P.n_stages; ++t) {
-    if (use.seq != cur) {
-      compute_transition<S>(P, lds, wave, cur, use.seq);
-      cur = use.seq;
-    }
-    // chunk t is complete once at most `after` newer DMA operations are pending
-    const int after = issued - 1 - t;
-    if (after >= S - 1) {
-      if (use.g.fmt == 1 && last_int4) vmcnt_wait<2 * S - 2>();
-      else vmcnt_wait<S - 1>();
+  wg_bar();  // stage 0 inputs staged
+  for (int seq = 0; seq < P.n_stages; ++seq) {
+    if (seq) wg_bar();  // stage seq inputs staged
+    int kind, layer;
+    stage_of(P, seq, kind, layer);
+    uint64_t w0 = 0, w1 = 0;
+    if (P.trace) w0 = wall_clock64();
+    if (kind == TD_ST_ATTN) {
+      w1 = attn_compute(P, lds, wave);
     } else {
-      vmcnt_wait<0>();
+      const Gemv g = gemv_of(P, kind, layer);
+      int u0, u1;
+      cu_units(g.U, cu, ncu, u0, u1);
+      const int cnt = u1 - u0;
+      const int n = cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0;
+      const int nrows = n * g.rpu;
+      for (int row = 0; row < nrows; ++row) {
+        float acc = 0.f;
+        for (int j = 0; j < g.J; ++j) {
+          // chunk t is complete once at most the ops issued after it are pending
+          const uint32_t after = issued - 1u - t;
+          if (after >= (uint32_t)(S - 1)) {
+            if (t < n4 && issued - 1u < n4) vmcnt_wait<2 * S - 2>();
+            else vmcnt_wait<S - 1>();
+          } else {
+            vmcnt_wait<0>();
+          }
+          if (P.trace && row == 0 && j == 0) w1 = wall_clock64();
+          const u32x4 w = *(const u32x4*)(ring + slot * TD_CHUNK + lane * 16);
+          if (g.fmt == 0) {
+            acc += dot_bf16(w, xin + j * 512 + lane * 8);
+          } else {
+            const float sc = f16f(*(const uint16_t*)(sring + slot * TD_SCHUNK + (lane >> 1) * 2));
+            acc += dot_int4(w, xin + j * 2048 + lane * 32, sc);
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot read out: refill it
+          if (issued < n_tot) issue(slot);
+          slot = slot + 1 == S ? 0 : slot + 1;
+          ++t;
+        }
+        const float r = wave_sum(acc);
+        const int k = g.rpu == 2 ? row >> 1 : row, rr = g.rpu == 2 ? row & 1 : 0;
+        if (lane == 0) out[(wave + k * TD_NW) * g.rpu + rr] = r;
+      }
     }
-    const uint8_t* sp = ring + slot * TD_CHUNK;
-    const u32x4 w = *(const u32x4*)(sp + lane * 16);
-    const bool valid = use.j * TD_CHUNK + lane * 16 < use.g.row_bytes;
-    float c = 0.f;
-    if (use.g.fmt == 0) {
-      const float* xp = xin + use.j * 512 + lane * 8;
-      c = dot_bf16(w, xp);
-    } else {
-      const uint32_t sw = *(const uint32_t*)(sring + slot * TD_SCHUNK + lane * 4);
-      const float sc = f16f(((lane >> 1) & 1) ? (sw >> 16) : sw);
-      const float* xp = xin + use.j * 2048 + lane * 32;
-      c = dot_int4(w, xp, sc);
+    if (P.trace) {
+      uint64_t* wt = (uint64_t*)(lds + P.off_wtrace) + wave * 4;
+      const uint64_t w2 = wall_clock64();
+      if (lane == 0) {
+        wt[0] = w0;
+        wt[1] = w1;
+        wt[2] = (w1 || kind == TD_ST_ATTN) ? w2 : 0;
+      }
     }
-    acc += valid ? c : 0.f;
-    // the slot's data is in registers: refill it with the chunk S ahead
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (fe.seq < P.n_stages) {
-      issue_chunk(fe, P, ring + slot * TD_CHUNK, sring + slot * TD_SCHUNK, lane);
-      last_int4 = fe.g.fmt;
-      cur_next(fe, P, wave, cu, ncu);
-      ++issued;
-    }
-    if (use.j == use.g.J - 1) {
-      const float r = wave_sum(acc);
-      if (lane == 0) out[(wave + use.k * TD_NW) * use.g.rpu + use.r] = r;
-      acc = 0.f;
-    }
-    cur_next(use, P, wave, cu, ncu);
-    slot = slot + 1 == S ? 0 : slot + 1;
+    wg_bar();  // stage seq outputs in LDS
   }
-  compute_transition<S>(P, lds, wave, cur, P.n_stages);
 }
 
 // ------------------------------------------------------------ sync wave
-// Loads n fp32 values (n % 4 == 0) published by other CUs into LDS.
-DEV void load_vec_sc1(const float* src, int n, float* dst) {
-  const int lane = lane_id();
-  for (int i0 = 0; i0 < n; i0 += 8 * 256) {
-    const void* a[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int i = i0 + (k * 64 + lane) * 4;
-      a[k] = src + (i < n ? i : 0);
-    }
-    u32x4 r[8];
-    ld8x4_sc1(a, r);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int i = i0 + (k * 64 + lane) * 4;
-      if (i < n) *(u32x4*)(dst + i) = r[k];
-    }
-  }
+// zero LDS floats [from, to): the tail of the last chunk of a GEMV input
+DEV void zero_tail(float* x, int from, int to) {
+  for (int i = from + lane_id(); i < to; i += 64) x[i] = 0.f;
 }
 
+DEV int chunk_elems(int fmt) { return fmt ? 2048 : 512; }
+
 // RMSNorm of the residual stream into LDS: xin = x / sqrt(mean(x^2) + eps) * gain.
-// The source is the published fp32 residual, or the bf16 embedding row.
-DEV void norm_input(const td_kparams& P, uint8_t* lds, const float* xsrc, const uint16_t* esrc,
-                    const uint16_t* gain) {
+// The source is the published residual (tagged), or the bf16 embedding row; the
+// bf16 gains were DMA'd into LDS when the previous stage ended.
+DEV bool norm_input(const td_kparams& P, uint8_t* lds, const uint2* xsrc, uint32_t tag, const uint16_t* esrc,
+                    int fmt) {
   const int lane = lane_id();
   float* xin = (float*)(lds + P.off_xin);
+  const uint16_t* gain = (const uint16_t*)(lds + P.off_gain);
   const int H = P.H;  // multiple of 256
+  bool ok = true;
   if (esrc) {
     for (int i = lane * 4; i < H; i += 256) {
       uint2 e = *(const uint2*)(esrc + i);
@@ -558,8 +585,9 @@ DEV void norm_input(const td_kparams& P, uint8_t* lds, const float* xsrc, const 
       *(f32x4*)(xin + i) = v;
     }
   } else {
-    load_vec_sc1(xsrc, H, xin);
+    ok = poll_vec(P, xsrc, H, tag, xin);
   }
+  vm_drain();  // the gains' DMA into LDS
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   float ss = 0.f;
   for (int i = lane * 4; i < H; i += 256) {
@@ -580,119 +608,146 @@ DEV void norm_input(const td_kparams& P, uint8_t* lds, const float* xsrc, const 
     v.w = v.w * inv * bf_hi(g.y);
     *(f32x4*)(xin + i) = v;
   }
+  const int ce = chunk_elems(fmt);
+  zero_tail(xin, H, (H + ce - 1) / ce * ce);
+  return ok;
 }
 
-DEV void sync_prepare(const td_kparams& P, uint8_t* lds, int kind, int layer) {
-  if (kind == TD_ST_QKV) {
-    norm_input(P, lds, P.x, nullptr, P.layers[layer].attn_norm);
-  } else if (kind == TD_ST_GU) {
-    norm_input(P, lds, P.x, nullptr, P.layers[layer].mlp_norm);
-  } else if (kind == TD_ST_HEAD) {
-    norm_input(P, lds, P.x, nullptr, P.final_norm);
-  } else if (kind == TD_ST_O) {
-    load_vec_sc1(P.o, P.qd, (float*)(lds + P.off_xin));
-  } else if (kind == TD_ST_DOWN) {
-    load_vec_sc1(P.act, P.I, (float*)(lds + P.off_xin));
-  } else {  // ATTN: the task's query heads, pre-scaled by 1/sqrt(d)
-    const AttnTask T = attn_task(P, blockIdx.x);
-    if (T.valid) {
-      const td_attn_lds A = td_attn_layout(P.d, P.group);
-      float* qs = (float*)(lds + P.off_attn + A.q);
-      const int n = P.group * P.d;
-      load_vec_sc1(P.q + (size_t)T.g * n, n, qs);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      for (int i = lane_id(); i < n; i += 64) qs[i] *= P.attn_scale;
+// Issued as soon as a stage's epilogue is out: the DMA of the next stage's
+// bf16 norm gains into LDS, and the QKV bias of this CU's units.
+DEV void preload(const td_kparams& P, uint8_t* lds, int kind, int layer, float& ba, float& bb) {
+  const int lane = lane_id();
+  const uint16_t* g = kind == TD_ST_QKV ? P.layers[layer].attn_norm
+                    : kind == TD_ST_GU ? P.layers[layer].mlp_norm
+                    : kind == TD_ST_HEAD ? P.final_norm : nullptr;
+  if (g) {
+    const int bytes = P.H * 2;
+    for (int off = 0; off < bytes; off += TD_CHUNK)
+      if (off + lane * 16 < bytes)
+        __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)g + off + lane * 16),
+                                         LDSPTR(lds + P.off_gain + off), 16, 0, 0);
+  }
+  if (kind == TD_ST_QKV && P.has_bias) {
+    int u0, u1;
+    cu_units(P.qkv_rows / 2, blockIdx.x, gridDim.x, u0, u1);
+    if (lane < u1 - u0) {
+      const int ra = unit_row(P, TD_ST_QKV, u0 + lane, 0);
+      ba = bf16f(P.layers[layer].bias[ra]);
+      bb = bf16f(P.layers[layer].bias[ra + (P.d >> 1)]);
     }
   }
 }
 
-// stage outputs -> epilogue -> published values
-DEV void sync_epilogue(const td_kparams& P, uint8_t* lds, int kind, int layer, uint32_t epoch) {
+// The chunk-0 CU of kv head g: combine every chunk's partial,
+// o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M), and publish o.
+DEV bool attn_merge(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint32_t tag) {
+  const int lane = lane_id();
+  const int d = P.d, G = P.group, st = d + 4;
+  const td_attn_lds A = td_attn_layout(d, G, P.n_chunks_max);
+  const float* own = (const float*)(lds + P.off_attn + A.part);
+  float* mb = (float*)(lds + P.off_attn + A.merge);
+  bool ok = true;
+  if (T.n_used > 1)
+    ok = poll_vec(P, P.tpart + ((size_t)T.g * P.n_chunks_max + 1) * G * st, (T.n_used - 1) * G * st, tag, mb);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (P.trace && lane == 0) ((uint64_t*)(lds + P.off_wtrace))[TD_NW * 4] = wall_clock64();
+  for (int h = 0; h < G; ++h) {
+    // lane c holds chunk c's (m, l)
+    const bool have = lane < T.n_used;
+    const float* pc = (lane == 0 || !have) ? own + h * st : mb + ((lane - 1) * G + h) * st;
+    const float m = have ? pc[d] : -__builtin_inff();
+    const float l = have ? pc[d + 1] : 0.f;
+    const float M = wave_max(m);
+    const float w0 = have ? __expf(m - M) : 0.f;
+    const float w = w0 / wave_sum(l * w0);
+    float o0 = 0.f, o1 = 0.f;
+    for (int c = 0; c < T.n_used; ++c) {
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+      const float* src = c == 0 ? own + h * st : mb + ((c - 1) * G + h) * st;
+      o0 = fmaf(wc, src[lane], o0);
+      if (d > 64) o1 = fmaf(wc, src[64 + lane], o1);
+    }
+    uint2* dst = P.to + ((size_t)T.g * G + h) * d;
+    st_tag(dst + lane, o0, tag);
+    if (d > 64) st_tag(dst + 64 + lane, o1, tag);
+  }
+  return ok;
+}
+
+// stage outputs -> epilogue -> published values (tag: this stage's)
+DEV bool sync_epilogue(const td_kparams& P, uint8_t* lds, int kind, int layer, uint32_t tag, uint32_t epoch,
+                       const AttnTask& T, float ba, float bb) {
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
   const float* out = (const float*)(lds + P.off_out);
   float* own = (float*)(lds + P.off_own);
+  bool ok = true;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (kind == TD_ST_QKV) {
     int u0, u1;
     cu_units(P.qkv_rows / 2, cu, ncu, u0, u1);
     const int half = P.d >> 1;
-    const td_layer_dev& Ld = P.layers[layer];
-    for (int k = lane; k < u1 - u0; k += 64) {
-      const int u = u0 + k;
+    const float* cs = (const float*)(lds + P.off_rope);
+    if (lane < u1 - u0) {  // at most 64 units per CU (checked at create)
+      const int u = u0 + lane;
       const int ra = unit_row(P, TD_ST_QKV, u, 0), rb = ra + half;
-      float a = out[2 * k], b = out[2 * k + 1];
+      float a = out[2 * lane], b = out[2 * lane + 1];
       if (P.has_bias) {
-        a += bf16f(Ld.bias[ra]);
-        b += bf16f(Ld.bias[rb]);
+        a += ba;
+        b += bb;
       }
       const int i = ra % P.d;  // < d/2
-      if (ra < P.qd + P.kvd) {  // q or k: rotate the pair
-        const float* cs = P.rope_cs + ((size_t)P.pos * half + i) * 2;
-        const float c = cs[0], s = cs[1];
-        const float a2 = a * c - b * s;
-        const float b2 = b * c + a * s;
+      if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
+        const float c = cs[2 * i], sn = cs[2 * i + 1];
+        const float a2 = a * c - b * sn;
+        const float b2 = b * c + a * sn;
         a = a2;
         b = b2;
       }
+      const int gw = (P.group + 2) * P.d;  // published block of one kv head
       if (ra < P.qd) {
-        st_f(P.q + ra, a);
-        st_f(P.q + rb, b);
+        const int h = ra / P.d, g = h / P.group;
+        uint2* pub = P.tq + (size_t)g * gw + (h - g * P.group) * P.d;
+        st_tag(pub + i, a, tag);
+        st_tag(pub + i + half, b, tag);
       } else {
         const bool isk = ra < P.qd + P.kvd;
         const int g = (ra - P.qd - (isk ? 0 : P.kvd)) / P.d;
-        uint16_t* cache = isk ? P.kc : P.vc;
-        uint16_t* row = cache + (((size_t)layer * P.nkv + g) * P.max_ctx + P.pos) * P.d;
-        st_u16_sc1(row + i, f2bf(a));
-        st_u16_sc1(row + i + half, f2bf(b));
+        const uint32_t ab = f2bf(a), bbits = f2bf(b);
+        uint16_t* row = (isk ? P.kc : P.vc) + (((size_t)layer * P.nkv + g) * P.max_ctx + P.pos) * P.d;
+        row[i] = (uint16_t)ab;
+        row[i + half] = (uint16_t)bbits;
+        uint2* pub = P.tq + (size_t)g * gw + (P.group + (isk ? 0 : 1)) * P.d;
+        st_tag(pub + i, __uint_as_float(ab << 16), tag);
+        st_tag(pub + i + half, __uint_as_float(bbits << 16), tag);
       }
     }
   } else if (kind == TD_ST_O || kind == TD_ST_DOWN) {
     int r0, r1;
     cu_units(P.H, cu, ncu, r0, r1);
+    uint2* dst = kind == TD_ST_O ? P.tx_mid : P.tx_out;
     for (int k = lane; k < r1 - r0; k += 64) {
-      float v = own[k] + out[k];
+      const float v = own[k] + out[k];
       own[k] = v;
-      st_f(P.x + r0 + k, v);
+      st_tag(dst + r0 + k, v, tag);
     }
   } else if (kind == TD_ST_GU) {
     int u0, u1;
     cu_units(P.I, cu, ncu, u0, u1);
     for (int k = lane; k < u1 - u0; k += 64) {
       const float gt = out[2 * k], up = out[2 * k + 1];
-      st_f(P.act + u0 + k, gt / (1.0f + expf(-gt)) * up);
+      st_tag(P.tact + u0 + k, gt / (1.0f + expf(-gt)) * up, tag);
     }
   } else if (kind == TD_ST_ATTN) {
-    const AttnTask T = attn_task(P, cu);
     if (T.valid) {
-      const int d = P.d, G = P.group;
-      const td_attn_lds A = td_attn_layout(d, G);
-      const float* pr = (const float*)(lds + P.off_attn + A.part);
-      float* gp = P.part + ((size_t)T.g * P.n_chunks_max + T.c) * G * (d + 2);
-      for (int i = lane; i < G * (d + 2); i += 64) st_f(gp + i, pr[i]);
-      vm_drain();
-      uint32_t* ctr = P.sync + TD_SY_MERGE + layer * P.nkv + T.g;
-      int last = 0;
-      if (lane == 0) last = atomicAdd(ctr, 1u) + 1u == (uint32_t)T.n_used;
-      if (uni(last)) {
-        // merge the n_used partials of this kv head: o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
-        const float* base = P.part + (size_t)T.g * P.n_chunks_max * G * (d + 2);
-        for (int h = 0; h < G; ++h) {
-          float M = -__builtin_inff();
-          for (int c = 0; c < T.n_used; ++c) M = fmaxf(M, ld_f(base + ((size_t)c * G + h) * (d + 2) + d));
-          float Lsum = 0.f, o0 = 0.f, o1 = 0.f;
-          for (int c = 0; c < T.n_used; ++c) {
-            const float* pc = base + ((size_t)c * G + h) * (d + 2);
-            const float wgt = expf(ld_f(pc + d) - M);
-            Lsum = fmaf(ld_f(pc + d + 1), wgt, Lsum);
-            o0 = fmaf(ld_f(pc + lane), wgt, o0);
-            if (d > 64) o1 = fmaf(ld_f(pc + 64 + lane), wgt, o1);
-          }
-          float* dst = P.o + ((size_t)T.g * G + h) * d;
-          st_f(dst + lane, o0 / Lsum);
-          if (d > 64) st_f(dst + 64 + lane, o1 / Lsum);
-        }
-        if (lane == 0) st_u(ctr, 0u);
+      if (T.c == 0) {
+        ok = attn_merge(P, lds, T, tag);
+      } else {
+        const int st = P.d + 4;
+        const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
+        const float* pr = (const float*)(lds + P.off_attn + A.part);
+        uint2* gp = P.tpart + ((size_t)T.g * P.n_chunks_max + T.c) * P.group * st;
+        for (int i = lane; i < P.group * st; i += 64) st_tag(gp + i, pr[i], tag);
       }
     }
   } else {  // HEAD: logits, per-CU candidate, last arriver picks the token
@@ -744,44 +799,99 @@ DEV void sync_epilogue(const td_kparams& P, uint8_t* lds, int kind, int layer, u
       }
     }
   }
+  return ok;
 }
 
 DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
   const uint32_t epoch = uni(ld_u(P.sync + TD_SY_EPOCH));
-  const uint32_t nbar = (uint32_t)(P.n_stages - 1);
-  uint32_t gen = epoch * nbar;
-  if (ld_u(P.sync + TD_SY_ABORT) && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
+  const uint32_t tag0 = epoch * (uint32_t)P.n_stages;  // stage seq publishes tag0 + seq + 1
+  bool ok = true;
+  if (ld_u(P.sync + TD_SY_ABORT)) ok = false;
   int tok = uni(*P.token_in);
   if (tok < 0 || tok >= P.V) {
     if (lane == 0 && cu == 0) atomicOr(P.err, TD_ERRBIT_RANGE);
     tok = 0;
   }
   const uint16_t* erow = P.embed + (size_t)tok * P.H;
-  {  // this CU's residual rows start as the embedding row
+  {  // this CU's residual rows start as the embedding row; the RoPE row of pos
     int r0, r1;
     cu_units(P.H, cu, ncu, r0, r1);
     float* own = (float*)(lds + P.off_own);
     for (int k = lane; k < r1 - r0; k += 64) own[k] = bf16f(erow[r0 + k]);
+    float* cs = (float*)(lds + P.off_rope);
+    for (int i = lane; i < P.d; i += 64) cs[i] = P.rope_cs[(size_t)P.pos * P.d + i];
   }
-  bool timed_out = false;
+  const AttnTask T = attn_task(P, cu);
+  const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
+  float ba = 0.f, bb = 0.f;
+  preload(P, lds, TD_ST_QKV, 0, ba, bb);
+  uint64_t* tr = P.trace ? P.trace + (size_t)cu * P.n_stages * TD_TRACE_STAMPS : nullptr;
   for (int seq = 0; seq < P.n_stages; ++seq) {
     int kind, layer;
     stage_of(P, seq, kind, layer);
-    if (kind == TD_ST_QKV && layer == 0) norm_input(P, lds, nullptr, erow, P.layers[0].attn_norm);
-    else sync_prepare(P, lds, kind, layer);
+    const uint32_t tag_in = tag0 + (uint32_t)seq, tag = tag_in + 1u;
+    uint64_t ts[TD_TRACE_STAMPS > 5 ? 5 : TD_TRACE_STAMPS] = {0, 0, 0, 0, 0};
+    if (tr) ts[0] = wall_clock64();
+    if (kind == TD_ST_QKV) {
+      ok &= norm_input(P, lds, P.tx_out, tag_in, layer == 0 ? erow : nullptr, P.wf);
+    } else if (kind == TD_ST_GU) {
+      ok &= norm_input(P, lds, P.tx_mid, tag_in, nullptr, P.wf);
+    } else if (kind == TD_ST_HEAD) {
+      ok &= norm_input(P, lds, P.tx_out, tag_in, nullptr, 0);
+    } else if (kind == TD_ST_O || kind == TD_ST_DOWN) {
+      float* xin = (float*)(lds + P.off_xin);
+      const int K = kind == TD_ST_O ? P.qd : P.I;
+      ok &= poll_vec(P, kind == TD_ST_O ? P.to : P.tact, K, tag_in, xin);
+      const int ce = chunk_elems(P.wf);
+      zero_tail(xin, K, (K + ce - 1) / ce * ce);
+    } else if (T.valid) {  // ATTN: the task's query heads (pre-scaled by 1/sqrt(d)), and row pos
+      // the kv head's block: its query heads, then this position's K and V rows
+      float* qs = (float*)(lds + P.off_attn + A.q);
+      const int n = P.group * P.d;
+      ok &= poll_vec(P, P.tq + (size_t)T.g * (n + 2 * P.d), n + 2 * P.d, tag_in, qs);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      for (int i = lane; i < n; i += 64) qs[i] *= P.attn_scale;
+      if (T.t1 == P.pos + 1) patch_pos_row(P, lds, T, 0);
+    }
     wg_bar();  // inputs ready
-    if (kind == TD_ST_ATTN) attn_load_tiles(P, lds, layer);
+    if (tr) ts[1] = wall_clock64();
+    if (kind == TD_ST_QKV && T.valid) {
+      load_tile(P, lds, layer, T, 0);  // this layer's first attention tile, ahead of time
+    } else if (kind == TD_ST_ATTN && T.valid) {
+      for (int tile = 0; tile < T.ntiles; ++tile) {
+        if (tile) {
+          load_tile(P, lds, layer, T, tile);
+          patch_pos_row(P, lds, T, tile);
+        }
+        wg_bar();  // tile in LDS
+        wg_bar();  // tile consumed
+      }
+    }
     wg_bar();  // outputs ready
-    sync_epilogue(P, lds, kind, layer, epoch);
+    if (tr) ts[2] = wall_clock64();
+    ok &= sync_epilogue(P, lds, kind, layer, tag, epoch, T, ba, bb);
+    if (tr) ts[3] = wall_clock64();
     if (seq + 1 < P.n_stages) {
-      vm_drain();
-      if (!grid_barrier(P, gen)) timed_out = true;
-      ++gen;
+      int nkind, nlayer;
+      stage_of(P, seq + 1, nkind, nlayer);
+      preload(P, lds, nkind, nlayer, ba, bb);
+    }
+    if (tr) {
+      ts[4] = wall_clock64();
+      uint64_t* rec = tr + (size_t)seq * TD_TRACE_STAMPS;
+      if (lane < TD_TRACE_STAMPS) {
+        const uint64_t* wt = (const uint64_t*)(lds + P.off_wtrace);
+        uint64_t v = 0;
+        if (lane < 5) v = ts[lane];
+        else if (lane == 5) v = kind == TD_ST_ATTN && T.valid && T.c == 0 ? wt[TD_NW * 4] : 0;
+        else if (lane >= 8 && lane < 8 + 3 * TD_NW) v = wt[((lane - 8) / 3) * 4 + (lane - 8) % 3];
+        rec[lane] = v;
+      }
     }
   }
-  if (timed_out && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
+  if (!ok && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
 }
 
 template <int S>
@@ -790,6 +900,54 @@ __global__ void __launch_bounds__(TD_THREADS, 1) td_megakernel(td_kparams P) {
   const int wave = uni((int)(threadIdx.x >> 6));
   if (wave < TD_NW) compute_wave<S>(P, lds, wave);
   else sync_wave(P, lds);
+}
+
+// ------------------------------------------------------------ weight packing
+// One wave per (CU, compute wave): walks the same cursor as the plan and copies
+// each chunk of its stream from the caller's row-major weights (zero-padding
+// the tail of a row that is not a whole chunk: bf16 0, or the 4-bit code of 0),
+// plus, for int4 chunks, the chunk's 32 fp16 scales.  A stream whose length
+// disagrees with the host plan raises bit 0 of *bad and is cut short.
+__global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, uint8_t* code, uint8_t* scale,
+                                                        const td_wstream* ws, int* bad) {
+  const int gw = uni((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  if (gw >= ncu * TD_NW) return;
+  const int cu = gw / TD_NW, wave = gw - cu * TD_NW;
+  const int lane = lane_id();
+  const td_wstream W = ws[gw];
+  uint8_t* dst = code + (size_t)W.code_off * TD_CHUNK;
+  uint8_t* sdst = scale + (size_t)W.scale_off * TD_SCHUNK;
+  Cursor c;
+  cur_enter(c, P, wave, cu, ncu, 0);
+  uint32_t n = 0, n4 = 0;
+  while (c.seq < P.n_stages && n < W.n_tot) {
+    const int u = c.u_first + c.k * TD_NW;
+    const int row = unit_row(P, c.g.kind, u, c.r);
+    const int boff = c.j * TD_CHUNK + lane * 16;
+    u32x4 v;
+    if (boff < c.g.row_bytes) {
+      v = *(const u32x4*)(c.g.w + (size_t)row * c.g.row_bytes + boff);
+    } else {
+      const uint32_t z = c.g.fmt ? 0x88888888u : 0u;
+      v = (u32x4){z, z, z, z};
+    }
+    *(u32x4*)(dst + lane * 16) = v;
+    dst += TD_CHUNK;
+    if (c.g.fmt == 1) {
+      if (n4 >= W.n4) break;
+      if (lane < 16) {
+        const int si = c.j * 32 + lane * 2;
+        uint32_t sv = 0;
+        if (si < c.g.K / 64) sv = *(const uint32_t*)(c.g.s + (size_t)row * (c.g.K / 64) + si);
+        *(uint32_t*)(sdst + lane * 4) = sv;
+      }
+      sdst += TD_SCHUNK;
+      ++n4;
+    }
+    cur_next(c, P, wave, cu, ncu);
+    ++n;
+  }
+  if (lane == 0 && (c.seq < P.n_stages || n != W.n_tot || n4 != W.n4)) atomicOr(bad, 1);
 }
 
 // ------------------------------------------------------------ test hooks
@@ -868,6 +1026,13 @@ int td_launch_megakernel(const td_kparams* p, int ncu, int ring_slots, void* str
   TD_RING_CASES(LAUNCH)
 #undef LAUNCH
   return (int)e;
+}
+
+int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
+                     void* stream) {
+  const int waves = ncu * TD_NW;
+  td_repack_kernel<<<(waves + 3) / 4, 256, 0, (hipStream_t)stream>>>(*p, ncu, code, scale, ws, bad);
+  return (int)hipGetLastError();
 }
 
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,

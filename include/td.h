@@ -167,6 +167,17 @@ int td_test_gemv(int32_t weight_format, const void* w, const void* scales, int32
 int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim,
                       float* d_out, void* stream);
 
+/* In-kernel stage trace (the per-worker timeline of one step).  td_trace_bytes
+ * gives the size of the trace: for each CU and each stage of the step (5 per
+ * layer plus the head), a record of 32 uint64 timestamps of the 100 MHz device
+ * clock: [0..4] stage start, inputs staged, compute finished, epilogue finished,
+ * grid barrier passed; [8 + 3w .. 10 + 3w] compute wave w's stage start, first
+ * weight chunk ready and last chunk done (0 if the wave had no chunk).  td_set_trace(ctx, d_buf, bytes) makes every following step write it
+ * to the device buffer d_buf (caller-owned, at least td_trace_bytes bytes);
+ * d_buf = NULL turns it off.  TD_E_INVALID_ARG for a buffer that is too small. */
+int64_t td_trace_bytes(const td_ctx* ctx);
+int td_set_trace(td_ctx* ctx, void* d_buf, int64_t bytes);
+
 /* Measured duration of the last megakernel step (HIP events on the step's own
  * stream), or a negative value when unavailable.  Timing is off unless enabled. */
 int td_set_timing(td_ctx* ctx, int32_t enable);
