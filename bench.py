@@ -29,10 +29,15 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 
 
+KERNEL_SOURCES = ("td_api.cpp", "td_internal.h", "td_kernels.hip")
+
+
 def source_hash() -> str:
+    """sha256 (first 16 hex digits) of the sources that define the decode kernel
+    and its launch plan; a counter summary taken on other sources is stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -256,7 +261,14 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(out), flush=True)
+    # release every device allocation while the runtime is fully up (a profiler
+    # attached to the process then has nothing left to tear down at exit)
     dec.close()
+    del evs, dec, kv, dm, logits, first, model
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return 0
 
 

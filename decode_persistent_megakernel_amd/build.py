@@ -1,4 +1,5 @@
-"""Builds libtd.so (the HIP library behind include/td.h) in-tree for gfx950."""
+"""Builds libtd.so (the HIP library behind include/td.h) in-tree for gfx950, and
+td_bench, the native driver of the decode step (linked to libtd.so and libsynth.so)."""
 from __future__ import annotations
 
 import os
@@ -9,6 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SO = os.path.join(PKG, "libtd.so")
+BENCH = os.path.join(PKG, "td_bench")
+SYNTH_DIR = os.path.join(ROOT, "synth")
 SOURCES = ["td_kernels.hip", "td_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
@@ -28,7 +31,29 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed to build libtd.so")
     os.replace(tmp, SO)
+    build_bench(verbose)
     return SO
+
+
+def build_bench(verbose: bool = False) -> str:
+    """td_bench: host-only C++ against the C ABI; needs synth/libsynth.so built."""
+    synth_so = os.path.join(SYNTH_DIR, "libsynth.so")
+    if not os.path.exists(synth_so):
+        sys.path.insert(0, ROOT)
+        import synth
+        synth.build()
+    tmp = BENCH + ".tmp"
+    cmd = [HIPCC, "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"), "-o", tmp,
+           os.path.join(CSRC, "td_bench.cpp"), "-L", PKG, "-ltd", "-L", SYNTH_DIR, "-lsynth",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,$ORIGIN/../synth"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed to build td_bench")
+    os.replace(tmp, BENCH)
+    return BENCH
 
 
 if __name__ == "__main__":

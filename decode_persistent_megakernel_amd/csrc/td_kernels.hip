@@ -40,6 +40,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define DEV __device__ __forceinline__
@@ -330,86 +331,98 @@ DEV AttnTask attn_task(const td_kparams& P, int cu) {
   return t;
 }
 
-// compute waves: wave h < group handles query head g * group + h.  Returns
-// the trace stamp taken after the first tile's scores (0 without a trace).
-DEV uint64_t attn_compute(const td_kparams& P, uint8_t* lds, int wave) {
-  const AttnTask T = attn_task(P, blockIdx.x);
-  uint64_t stamp = 0;
-  if (!T.valid) return 0;
+// compute waves: wave h < group handles query head g * group + h, one 64-row
+// tile at a time with the online softmax.  Scores: lane tau takes position
+// t0 + tau.  P.V: lane (cg, pg) owns columns 4 cg .. 4 cg + 3 over the rows of
+// position group pg, reading p from LDS (a broadcast) and V as 8-byte pieces;
+// the groups are summed at the end.  Rows past the chunk end are zero in the
+// tile and get p = 0.  Returns the trace stamp taken after the first tile's
+// softmax (0 without a trace).
+template <int D>
+DEV uint64_t attn_compute_d(const td_kparams& P, uint8_t* lds, int wave, const AttnTask& T) {
+  constexpr int LPR = D / 4;           // lanes per V row (4 columns each)
+  constexpr int NG = 64 / LPR;         // position groups
+  constexpr int RPG = TD_TILE / NG;    // rows per group
   const int lane = lane_id();
-  const int d = P.d;
-  const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max);
+  const td_attn_lds A = td_attn_layout(D, P.group, P.n_chunks_max);
   uint8_t* base = lds + P.off_attn;
-  const float* qs = (const float*)(base + A.q) + wave * d;
+  const bool active = wave < P.group;
+  const float* qs = (const float*)(base + A.q) + (active ? wave : 0) * D;
   const uint16_t* kt = (const uint16_t*)(lds + P.off_tile);
-  const uint16_t* vt = kt + TD_TILE * (d + 8);
-  float* ps = (float*)(base + A.p) + wave * TD_TILE;
-  float m = -__builtin_inff(), l = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int tile = 0; tile < T.ntiles; ++tile) {
+  const uint16_t* vt = kt + TD_TILE * (D + 8);
+  float* ps = (float*)(base + A.p) + (active ? wave : 0) * TD_TILE;
+  const int cg = lane % LPR, pg = lane / LPR;
+  const uint16_t* vrow = vt + pg * RPG * D + cg * 4;
+  const float* prow = ps + pg * RPG;
+  const int ntiles = T.ntiles, t0 = T.t0, t1 = T.t1;
+  uint64_t stamp = 0;
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int tile = 0; tile < ntiles; ++tile) {
     wg_bar();  // tile in LDS
-    if (wave < P.group) {
-      const int nv = min(TD_TILE, T.t1 - (T.t0 + tile * TD_TILE));
-      // lane tau: score of position t0 + tau
-      float s = -__builtin_inff();
-      if (lane < nv) {
-        const uint16_t* kr = kt + lane * (d + 8);
-        float a = 0.f;
-        for (int e = 0; e < d; e += 8) {
-          const u32x4 kw = *(const u32x4*)(kr + e);
-          const f32x4 q0 = *(const f32x4*)(qs + e), q1 = *(const f32x4*)(qs + e + 4);
-          a = fmaf(bf_lo(kw.x), q0.x, a);
-          a = fmaf(bf_hi(kw.x), q0.y, a);
-          a = fmaf(bf_lo(kw.y), q0.z, a);
-          a = fmaf(bf_hi(kw.y), q0.w, a);
-          a = fmaf(bf_lo(kw.z), q1.x, a);
-          a = fmaf(bf_hi(kw.z), q1.y, a);
-          a = fmaf(bf_lo(kw.w), q1.z, a);
-          a = fmaf(bf_hi(kw.w), q1.w, a);
-        }
-        s = a;
+    if (active) {
+      const int nv = min(TD_TILE, t1 - (t0 + tile * TD_TILE));
+      const uint16_t* kr = kt + lane * (D + 8);
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; e += 8) {
+        const u32x4 kw = *(const u32x4*)(kr + e);
+        const f32x4 q0 = *(const f32x4*)(qs + e), q1 = *(const f32x4*)(qs + e + 4);
+        a = fmaf(bf_lo(kw.x), q0.x, a);
+        a = fmaf(bf_hi(kw.x), q0.y, a);
+        a = fmaf(bf_lo(kw.y), q0.z, a);
+        a = fmaf(bf_hi(kw.y), q0.w, a);
+        a = fmaf(bf_lo(kw.z), q1.x, a);
+        a = fmaf(bf_hi(kw.z), q1.y, a);
+        a = fmaf(bf_lo(kw.w), q1.z, a);
+        a = fmaf(bf_hi(kw.w), q1.w, a);
       }
-      const float mt = wave_max(s);
-      const float mn = fmaxf(m, mt);
-      const float p = lane < nv ? __expf(s - mn) : 0.f;
+      const float s = lane < nv ? a : -__builtin_inff();
+      const float mn = fmaxf(m, wave_max(s));  // finite: nv >= 1
+      const float p = __expf(s - mn);
       const float corr = __expf(m - mn);
       l = l * corr + wave_sum(p);
       m = mn;
-      acc0 *= corr;
-      acc1 *= corr;
+      acc *= corr;
+      ps[lane] = p;
       if (P.trace && tile == 0) stamp = wall_clock64();
-      // lane e: sum over tau of p_tau V[tau][e]; p_tau is read from lane tau
-      for (int t0 = 0; t0 < nv; t0 += 16) {
-        float v0[16], v1[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int t = t0 + k < nv ? t0 + k : t0;
-          v0[k] = bf16f(vt[t * d + lane]);
-          v1[k] = d > 64 ? bf16f(vt[t * d + 64 + lane]) : 0.f;
-        }
+      for (int t = 0; t < RPG; t += 4) {
+        const f32x4 p4 = *(const f32x4*)(prow + t);
+        u32x2 v[4];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          if (t0 + k < nv) {
-            const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t0 + k));
-            acc0 = fmaf(pt, v0[k], acc0);
-            if (d > 64) acc1 = fmaf(pt, v1[k], acc1);
-          }
+        for (int k = 0; k < 4; ++k) v[k] = *(const u32x2*)(vrow + (t + k) * D);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float pk = k == 0 ? p4.x : k == 1 ? p4.y : k == 2 ? p4.z : p4.w;
+          acc.x = fmaf(pk, bf_lo(v[k].x), acc.x);
+          acc.y = fmaf(pk, bf_hi(v[k].x), acc.y);
+          acc.z = fmaf(pk, bf_lo(v[k].y), acc.z);
+          acc.w = fmaf(pk, bf_hi(v[k].y), acc.w);
         }
       }
     }
     wg_bar();  // tile consumed
   }
-  if (wave < P.group) {
-    float* pr = (float*)(base + A.part) + wave * (d + 4);
-    pr[lane] = acc0;
-    if (d > 64) pr[64 + lane] = acc1;
-    if (lane == 0) {
-      pr[d] = m;
-      pr[d + 1] = l;
-      pr[d + 2] = 0.f;
-      pr[d + 3] = 0.f;
+  if (active) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      acc.x += __shfl_xor(acc.x, off);
+      acc.y += __shfl_xor(acc.y, off);
+      acc.z += __shfl_xor(acc.z, off);
+      acc.w += __shfl_xor(acc.w, off);
     }
+    float* pr = (float*)(base + A.part) + wave * (D + 4);
+    if (pg == 0) *(f32x4*)(pr + 4 * cg) = acc;
+    if (lane == 0) *(f32x4*)(pr + D) = f32x4{m, l, 0.f, 0.f};
   }
   return stamp;
+}
+
+DEV uint64_t attn_compute(const td_kparams& P, uint8_t* lds, int wave) {
+  const AttnTask T = attn_task(P, blockIdx.x);
+  if (!T.valid) return 0;
+  return P.d == 64 ? attn_compute_d<64>(P, lds, wave, T) : attn_compute_d<128>(P, lds, wave, T);
 }
 
 // sync wave: K and V rows [tb, tb + nv) of the tile, except row pos (written
@@ -425,7 +438,7 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
   uint16_t* kt = (uint16_t*)(lds + P.off_tile);
   uint16_t* vt = kt + TD_TILE * (d + 8);
   const int q16 = d / 8;  // 16-byte pieces per row
-  const int npiece = nv * q16;
+  const int npiece = TD_TILE * q16;  // the whole tile: rows >= nv read as zero
   for (int i0 = 0; i0 < npiece; i0 += 8 * 64) {
     u32x4 kr[8], vr[8];
 #pragma unroll
@@ -439,7 +452,7 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
       const int i = i0 + k * 64 + lane;
       if (i < npiece) {
         const int row = i / q16, pc = i - row * q16;
-        if (tb + row != P.pos) {
+        if (row >= nv || tb + row != P.pos) {  // row pos comes from the published copy
           *(u32x4*)(kt + row * (d + 8) + pc * 8) = kr[k];
           *(u32x4*)(vt + row * d + pc * 8) = vr[k];
         }
@@ -639,38 +652,60 @@ DEV void preload(const td_kparams& P, uint8_t* lds, int kind, int layer, float& 
 }
 
 // The chunk-0 CU of kv head g: combine every chunk's partial,
-// o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M), and publish o.
-DEV bool attn_merge(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint32_t tag) {
+// o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M), and publish o.  The
+// weights w[h][c] go to LDS first; then lane i owns 4 consecutive outputs
+// (head i / (D/4)) and sums over the chunks in chunk order.
+template <int D>
+DEV void attn_merge_d(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint32_t tag) {
   const int lane = lane_id();
+  const int G = P.group, n = T.n_used;
+  constexpr int st = D + 4;
+  const td_attn_lds A = td_attn_layout(D, G, P.n_chunks_max);
+  const float* own = (const float*)(lds + P.off_attn + A.part);
+  const float* mb = (const float*)(lds + P.off_attn + A.merge);
+  float* wl = (float*)(lds + P.off_attn + A.p);  // [G][64]: free once the tiles are consumed
+  for (int h = 0; h < G; ++h) {
+    const bool have = lane < n;  // n <= 64
+    const float* pc = lane == 0 ? own + h * st : mb + ((have ? lane - 1 : 0) * G + h) * st;
+    const float m = have ? pc[D] : -__builtin_inff();
+    const float l = have ? pc[D + 1] : 0.f;
+    const float M = wave_max(m);
+    const float w0 = have ? __expf(m - M) : 0.f;
+    wl[h * 64 + lane] = w0 / wave_sum(l * w0);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  for (int i = lane; i < G * (D / 4); i += 64) {
+    const int h = i / (D / 4), e = 4 * (i - h * (D / 4));
+    const float w00 = wl[h * 64];
+    f32x4 o = *(const f32x4*)(own + h * st + e);
+    o.x *= w00; o.y *= w00; o.z *= w00; o.w *= w00;
+    for (int c = 1; c < n; ++c) {
+      const f32x4 v = *(const f32x4*)(mb + ((c - 1) * G + h) * st + e);
+      const float w = wl[h * 64 + c];
+      o.x = fmaf(w, v.x, o.x);
+      o.y = fmaf(w, v.y, o.y);
+      o.z = fmaf(w, v.z, o.z);
+      o.w = fmaf(w, v.w, o.w);
+    }
+    uint2* dst = P.to + ((size_t)T.g * G + h) * D + e;
+    st_tag(dst + 0, o.x, tag);
+    st_tag(dst + 1, o.y, tag);
+    st_tag(dst + 2, o.z, tag);
+    st_tag(dst + 3, o.w, tag);
+  }
+}
+
+DEV bool attn_merge(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint32_t tag) {
   const int d = P.d, G = P.group, st = d + 4;
   const td_attn_lds A = td_attn_layout(d, G, P.n_chunks_max);
-  const float* own = (const float*)(lds + P.off_attn + A.part);
   float* mb = (float*)(lds + P.off_attn + A.merge);
   bool ok = true;
   if (T.n_used > 1)
     ok = poll_vec(P, P.tpart + ((size_t)T.g * P.n_chunks_max + 1) * G * st, (T.n_used - 1) * G * st, tag, mb);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (P.trace && lane == 0) ((uint64_t*)(lds + P.off_wtrace))[TD_NW * 4] = wall_clock64();
-  for (int h = 0; h < G; ++h) {
-    // lane c holds chunk c's (m, l)
-    const bool have = lane < T.n_used;
-    const float* pc = (lane == 0 || !have) ? own + h * st : mb + ((lane - 1) * G + h) * st;
-    const float m = have ? pc[d] : -__builtin_inff();
-    const float l = have ? pc[d + 1] : 0.f;
-    const float M = wave_max(m);
-    const float w0 = have ? __expf(m - M) : 0.f;
-    const float w = w0 / wave_sum(l * w0);
-    float o0 = 0.f, o1 = 0.f;
-    for (int c = 0; c < T.n_used; ++c) {
-      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-      const float* src = c == 0 ? own + h * st : mb + ((c - 1) * G + h) * st;
-      o0 = fmaf(wc, src[lane], o0);
-      if (d > 64) o1 = fmaf(wc, src[64 + lane], o1);
-    }
-    uint2* dst = P.to + ((size_t)T.g * G + h) * d;
-    st_tag(dst + lane, o0, tag);
-    if (d > 64) st_tag(dst + 64 + lane, o1, tag);
-  }
+  if (P.trace && lane_id() == 0) ((uint64_t*)(lds + P.off_wtrace))[TD_NW * 4] = wall_clock64();
+  if (d == 64) attn_merge_d<64>(P, lds, T, tag);
+  else attn_merge_d<128>(P, lds, T, tag);
   return ok;
 }
 
