@@ -1,9 +1,9 @@
 // td_kernels.hip - the persistent decode-step megakernel for MI355X (gfx950)
 // and the single-routine kernels behind the test hooks.
 //
-// One workgroup per CU runs the whole step as a fixed sequence of stages
-// separated by grid barriers ("Decoding in tiles", sec. 4: a static plan of
-// waves; sec. 3: prefetching the next weights while waiting).  Per layer:
+// One workgroup per CU runs the whole step as a fixed sequence of stages from
+// a static plan ("Decoding in tiles", sec. 4; sec. 3: the next weights are
+// fetched while a stage waits for its inputs).  Per layer:
 //   QKV   RMSNorm + fused [Wq;Wk;Wv] GEMV (+bias), RoPE, K/V-cache write
 //   ATTN  split-K grouped-query attention over the cache ("One launch per
 //         token", "The attention trap": heads x chunks, merged with the
@@ -16,21 +16,21 @@
 //
 // Workgroup roles:
 //   8 compute waves stream weight chunks (1 KiB = 64 lanes x 16 B) from HBM
-//     straight into a per-wave LDS ring with global_load_lds_dwordx4.  The
-//     ring runs S chunks ahead of the arithmetic across stage boundaries and
-//     grid barriers: weights never depend on the token, so the loads for the
-//     next stage are in flight while the grid waits.  These waves issue no
-//     other global memory operation, so vmcnt counts only ring loads.
-//   1 sync wave does all activation traffic: it stages the stage inputs in
+//     straight into a per-wave LDS ring with global_load_lds_dwordx4.  Each
+//     wave's chunks are packed at create time in the order it consumes them,
+//     and the ring runs S chunks ahead across stage boundaries: weights never
+//     depend on the token, so the next stage's loads are in flight while the
+//     CU waits for that stage's inputs.  These waves issue no other global
+//     memory operation, so vmcnt counts only ring loads.
+//   1 sync wave does all activation traffic: it stages a stage's inputs in
 //     LDS (with the RMSNorm applied), runs the epilogues (bias, RoPE, K/V
-//     write, SiLU*up, residual), publishes the stage outputs and takes part in
-//     the grid barrier.
-// Cross-CU data: written with agent-scope (sc1) stores, the writer waits for
-// them (vmcnt(0)) before it arrives at the barrier, and readers use sc1 loads.
-// This keeps values coherent across the 8 XCDs without writing back or
-// invalidating whole L2 caches.  The barrier is two-level: 32 arrivals on a
-// per-XCD counter, the last of them arrives on a global counter, then
-// releases its XCD through a per-XCD word.
+//     write, SiLU*up, residual, merge, argmax) and publishes the outputs.
+// Cross-CU hand-off without grid barriers: every value handed to other CUs is
+// a (value, tag) pair written with one 8-byte agent-scope (sc1) store, and a
+// reader polls the pairs with sc1 loads until all carry the tag of the stage
+// that produced them.  The data is its own ready signal, coherent across the 8
+// XCDs without writing back or invalidating whole L2 caches, and a stage waits
+// only for the values it reads.  Every wait is bounded in time.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>

@@ -49,3 +49,62 @@ def test_create_rejects_bad_config_before_touching_the_device():
     cfg.head_dim = 96
     assert L.td_create(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.byref(h)) == _lib.TD_E_INVALID_ARG
     assert not h.value
+
+
+def _valid_config(**over):
+    kw = dict(n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=64, intermediate=512, vocab=1000,
+              max_ctx=64, rope_theta=1e4, rms_eps=1e-5, weight_format=_lib.TD_WF_BF16, qkv_bias=0)
+    kw.update(over)
+    return _lib.TdConfig(**kw)
+
+
+def _fake_weights(n_layers, scales=False, bias=False, drop=None):
+    """Non-null fake device addresses (td_create validates them before any device call)."""
+    p = 0x10000
+    fields = ["attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gu", "w_d"]
+    if scales:
+        fields += ["s_qkv", "s_o", "s_gu", "s_d"]
+    if bias:
+        fields += ["b_qkv"]
+    arr = (_lib.TdLayerWeights * n_layers)()
+    for i in range(n_layers):
+        arr[i] = _lib.TdLayerWeights(**{f: (None if f == drop else p) for f in fields})
+    w = _lib.TdWeights(embed=None if drop == "embed" else p, final_norm=p, head=p, layers=arr)
+    return w, arr
+
+
+@pytest.mark.parametrize("over", [
+    dict(n_layers=0), dict(hidden=-256), dict(vocab=0), dict(max_ctx=0), dict(intermediate=0),
+    dict(head_dim=96), dict(head_dim=32), dict(n_kv_heads=3), dict(n_q_heads=32, n_kv_heads=2),
+    dict(hidden=320), dict(intermediate=520), dict(weight_format=7),
+    dict(weight_format=_lib.TD_WF_INT4_G64, intermediate=576),
+    dict(rope_theta=0.0), dict(rms_eps=-1.0),
+])
+def test_create_rejects_each_bad_config_field(over):
+    L = _lib.lib()
+    cfg = _valid_config(**over)
+    w, keep = _fake_weights(max(1, cfg.n_layers), scales=True, bias=True)
+    h = ctypes.c_void_p(123)
+    assert L.td_create(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.byref(h)) == _lib.TD_E_INVALID_ARG
+    assert h.value is None  # *out is cleared on error
+
+
+@pytest.mark.parametrize("drop,fmt,bias", [
+    ("embed", 0, 0), ("w_qkv", 0, 0), ("w_d", 0, 0), ("mlp_norm", 0, 0),
+    ("s_gu", _lib.TD_WF_INT4_G64, 0), ("b_qkv", 0, 1),
+])
+def test_create_rejects_missing_weights(drop, fmt, bias):
+    L = _lib.lib()
+    cfg = _valid_config(weight_format=fmt, qkv_bias=bias)
+    w, keep = _fake_weights(cfg.n_layers, scales=True, bias=True, drop=drop)
+    h = ctypes.c_void_p()
+    assert L.td_create(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.byref(h)) == _lib.TD_E_INVALID_ARG
+
+
+def test_null_arguments_are_rejected():
+    L = _lib.lib()
+    assert L.td_create(None, None, 0, None) == _lib.TD_E_INVALID_ARG
+    kv = _lib.TdKV(k=None, v=None, max_ctx=64)
+    assert L.td_decode_step(None, None, 0, ctypes.byref(kv), None, None) == _lib.TD_E_INVALID_ARG
+    assert L.td_status(None, None) == _lib.TD_E_INVALID_ARG
+    L.td_destroy(None)  # a no-op

@@ -1,0 +1,104 @@
+"""GPU edge cases of the decode step, each against the CPU oracle or the
+documented error code.
+
+* Split-K chunk boundaries: a shrunk Llama-shaped model with 2 kv heads gives
+  64-position chunks, and decoding from position 60 to 131 crosses the
+  positions 63/64/65 and 127/128/129, where a chunk gains its first or last
+  row (the merge must count every position exactly once).
+* The last cache position (max_ctx - 1), and position max_ctx rejected.
+* Head dim 128 with split-K and a QKV bias.
+* int4 rows whose K is not a whole number of 2048-code chunks (ragged tail).
+* Error words: a token id out of range, a non-finite logit.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.test_gpu_parity import run_compare, td, torch, _say  # noqa: F401  (fixture)
+
+pytestmark = pytest.mark.gpu
+
+BASE = dict(n_layers=2, hidden=256, vocab=1000, prompt_len=0, kv_prefix=0, decode_steps=0)
+SPLITK = synth.shrink(synth.CONFIGS["llama1b"], name="splitk_d64", n_q_heads=8, n_kv_heads=2, head_dim=64,
+                      intermediate=512, max_ctx=256, seed=2001, **BASE)
+SPLITK128 = synth.shrink(synth.CONFIGS["qwen1p5b"], name="splitk_d128", n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=512, max_ctx=256, seed=2002, **BASE)
+RAGGED4 = synth.shrink(synth.CONFIGS["tinyllama_int4"], name="ragged_int4", n_q_heads=4, n_kv_heads=2, head_dim=64,
+                       intermediate=640, max_ctx=128, seed=2003, **BASE)
+
+
+def _case(td, cfg, start, n, tol):
+    m = synth.make_model(cfg)
+    k, v = synth.random_kv_prefix(cfg, start, seed_tag="edges")
+    return run_compare(td, cfg, m, k, v, synth.first_token(cfg), start, n, tol, cfg.name)
+
+
+def test_splitk_chunk_boundaries(td):
+    _say("split-K boundaries, d=64, positions 60..131")
+    _case(td, SPLITK, 60, 72, 2e-2)
+
+
+def test_last_position_and_beyond(td):
+    _say("last cache position, d=64")
+    cfg = SPLITK
+    _case(td, cfg, cfg.max_ctx - 6, 6, 2e-2)
+    from decode_persistent_megakernel_amd import _lib
+    m = synth.make_model(cfg)
+    dec = td.Decoder(td.DeviceModel(m), cfg.max_ctx)
+    kv = td.KVCache(cfg, cfg.max_ctx)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    for bad in (cfg.max_ctx, -1):
+        with pytest.raises(_lib.TdError) as ei:
+            dec.step(tok.data_ptr(), bad, kv, logits)
+        assert ei.value.code == _lib.TD_E_RANGE
+    dec.close()
+
+
+def test_splitk_head_dim_128_with_bias(td):
+    _say("split-K boundaries, d=128 + QKV bias, positions 60..135")
+    _case(td, SPLITK128, 60, 76, 2e-2)
+
+
+def test_int4_ragged_chunks(td):
+    _say("int4, K = 256 and 640 (partial 2048-code chunks)")
+    _case(td, RAGGED4, 40, 24, 5e-2)
+
+
+def test_token_out_of_range_sets_range_error(td):
+    _say("token id out of range")
+    from decode_persistent_megakernel_amd import _lib
+    cfg = SPLITK
+    m = synth.make_model(cfg)
+    dec = td.Decoder(td.DeviceModel(m), cfg.max_ctx)
+    kv = td.KVCache(cfg, cfg.max_ctx)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    for bad in (cfg.vocab, -3):
+        tok = torch.tensor([bad], dtype=torch.int32, device="cuda")
+        dec.step(tok.data_ptr(), 0, kv, logits)
+        torch.cuda.synchronize()
+        assert dec.status() == _lib.TD_E_RANGE
+    tok = torch.tensor([7], dtype=torch.int32, device="cuda")  # the context stays usable
+    dec.step(tok.data_ptr(), 0, kv, logits)
+    torch.cuda.synchronize()
+    assert dec.status() == 0
+    dec.close()
+
+
+def test_nonfinite_logit_sets_error(td):
+    _say("non-finite logit")
+    from decode_persistent_megakernel_amd import _lib
+    cfg = synth.shrink(SPLITK, tied=False)
+    m = synth.make_model(cfg)
+    m.head = m.head.copy()
+    m.head[5, :] = 0x7FC0  # bf16 NaN: logit 5 is NaN
+    dec = td.Decoder(td.DeviceModel(m), cfg.max_ctx)
+    kv = td.KVCache(cfg, cfg.max_ctx)
+    tok = torch.tensor([11], dtype=torch.int32, device="cuda")
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    dec.step(tok.data_ptr(), 0, kv, logits)
+    torch.cuda.synchronize()
+    assert dec.status() == _lib.TD_E_NONFINITE
+    got = logits.cpu().numpy()
+    assert np.isnan(got[5]) and np.isfinite(np.delete(got, 5)).all()  # the logits are still written
+    dec.close()
