@@ -99,6 +99,8 @@ def main() -> int:
     ap.add_argument("--trace", default=None, help="write the in-kernel stage trace summary of one step here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (a known-size kernel for counter calibration)")
+    ap.add_argument("--baseline-steps", type=int, default=32,
+                    help="timed steps of each baseline executor (per-op launches, graph replay); 0 = skip")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -212,6 +214,33 @@ def main() -> int:
         with open(args.trace, "w") as f:
             json.dump(summ, f, indent=1)
         print(tdtrace.format_summary(summ), file=sys.stderr, flush=True)
+    baselines = None
+    if args.baseline_steps > 0:
+        # the same fused ops launched one kernel each, and those launches captured
+        # once into a hipGraph and replayed: timed exactly like the persistent kernel
+        baselines = {}
+        nb = min(args.baseline_steps, n_steps)
+        for name, ex in (("per_op", td.TD_EXEC_PER_OP), ("graph", td.TD_EXEC_GRAPH)):
+            bdec = td.Decoder(dm, cfg.max_ctx, executor=ex)
+            bdec.step(first.data_ptr(), start, kv, logits, stream=stream)  # warm-up (and graph capture)
+            torch.cuda.synchronize()
+            bev = []
+            for i in range(nb):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                bdec.step(first.data_ptr() if i == 0 else bdec.token_ptr(), start + i, kv, logits, stream=stream)
+                e1.record(stream)
+                bev.append((e0, e1))
+            torch.cuda.synchronize()
+            if bdec.status() != 0:
+                print(f"device status error in the {name} baseline", file=sys.stderr)
+                return 1
+            bms = np.array([a.elapsed_time(b) for a, b in bev])
+            baselines[name] = {"tokens_per_s": round(nb / (bms.sum() / 1e3), 2), "ms_per_step": round(float(bms.mean()), 4),
+                               "steps": nb, "launches_per_step": (6 * cfg.n_layers + 3) if name == "per_op" else 2}
+            bdec.close()
+            del bdec
     khash = source_hash()
     traffic = read_traffic(args.config, khash)
     cpu = None
@@ -258,6 +287,7 @@ def main() -> int:
             "source_sha256_16": khash,
         },
         "cpu_baseline": cpu,
+        "baselines": baselines,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(out), flush=True)

@@ -54,6 +54,15 @@ struct td_ctx {
   bool timing = false;
   bool timed = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  // per-op and graph executors
+  td_opparams op{};
+  void* opbuf = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  hipStream_t cap_stream = nullptr;
+  const void* g_kc = nullptr;  // the K/V cache and logits the captured graph was made for
+  const void* g_vc = nullptr;
+  const void* g_logits = nullptr;
 };
 
 namespace {
@@ -136,6 +145,106 @@ int check_weights(const td_config* c, const td_weights* w) {
   return TD_OK;
 }
 
+// The per-op executor's parameters and fp32 activation buffers (one allocation).
+int setup_per_op(td_ctx* ctx, const td_kparams& kp) {
+  td_opparams& op = ctx->op;
+  op.L = kp.L;
+  op.H = kp.H;
+  op.nq = kp.nq;
+  op.nkv = kp.nkv;
+  op.d = kp.d;
+  op.I = kp.I;
+  op.V = kp.V;
+  op.max_ctx = kp.max_ctx;
+  op.wf = kp.wf;
+  op.has_bias = kp.has_bias;
+  op.qd = kp.qd;
+  op.kvd = kp.kvd;
+  op.qkv_rows = kp.qkv_rows;
+  op.group = kp.group;
+  op.eps = kp.eps;
+  op.attn_scale = kp.attn_scale;
+  op.chunk_len = kp.chunk_len;
+  op.n_chunks_max = kp.n_chunks_max;
+  op.layers = kp.layers;
+  op.embed = kp.embed;
+  op.head = kp.head;
+  op.final_norm = kp.final_norm;
+  op.rope_cs = kp.rope_cs;
+  op.token_out = kp.token_out;
+  op.err = kp.err;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  const size_t o_pos = take(4), o_x = take((size_t)op.H * 4), o_q = take((size_t)op.qd * 4);
+  const size_t o_part = take((size_t)op.nkv * op.n_chunks_max * op.group * (op.d + 4) * 4);
+  const size_t o_o = take((size_t)op.qd * 4), o_act = take((size_t)op.I * 4);
+  const size_t o_cand = take((size_t)td_op_head_blocks(&op) * 16);
+  hipError_t e = hipMalloc(&ctx->opbuf, off);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of per-op buffers failed")
+                                                       : hip_fail(e, "hipMalloc");
+  e = hipMemset(ctx->opbuf, 0, off);
+  if (e != hipSuccess) {
+    (void)hipFree(ctx->opbuf);
+    ctx->opbuf = nullptr;
+    return hip_fail(e, "hipMemset");
+  }
+  uint8_t* b = (uint8_t*)ctx->opbuf;
+  op.pos_word = (int32_t*)(b + o_pos);
+  op.x = (float*)(b + o_x);
+  op.q = (float*)(b + o_q);
+  op.part = (float*)(b + o_part);
+  op.o = (float*)(b + o_o);
+  op.act = (float*)(b + o_act);
+  op.cand = (uint32_t*)(b + o_cand);
+  int le = td_op_set_lds_limits(&op);
+  if (le) {
+    (void)hipFree(ctx->opbuf);
+    ctx->opbuf = nullptr;
+    return hip_fail((hipError_t)le, "hipFuncSetAttribute");
+  }
+  return TD_OK;
+}
+
+void drop_graph(td_ctx* ctx) {
+  if (ctx->gexec) (void)hipGraphExecDestroy(ctx->gexec);
+  if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
+  ctx->gexec = nullptr;
+  ctx->graph = nullptr;
+}
+
+// Captures every launch after op_begin into a graph (once per K/V cache and
+// logits buffer) on a private stream; no memset node is ever recorded.
+int capture_graph(td_ctx* ctx) {
+  drop_graph(ctx);
+  hipError_t e = hipSuccess;
+  if (!ctx->cap_stream) e = hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  e = hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  const int le = td_launch_op_layers(&ctx->op, ctx->cap_stream);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(ctx->cap_stream, &g);
+  if (le) {
+    if (g) (void)hipGraphDestroy(g);
+    return hip_fail((hipError_t)le, "launch during capture");
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  ctx->graph = g;
+  e = hipGraphInstantiate(&ctx->gexec, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    drop_graph(ctx);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  ctx->g_kc = ctx->op.kc;
+  ctx->g_vc = ctx->op.vc;
+  ctx->g_logits = ctx->op.logits;
+  return TD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,7 +273,8 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   if (rc) return rc;
   rc = check_weights(cfg, w);
   if (rc) return rc;
-  if (executor != TD_EXEC_MEGAKERNEL) return fail(TD_E_UNSUPPORTED, "executor not available");
+  if (executor != TD_EXEC_MEGAKERNEL && executor != TD_EXEC_PER_OP && executor != TD_EXEC_GRAPH)
+    return fail(TD_E_INVALID_ARG, "unknown executor");
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -388,6 +498,18 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   kp.n_stages = 5 * L + 1;
   kp.ws = (const td_wstream*)(base + o_ws);
 
+  if (executor != TD_EXEC_MEGAKERNEL) {
+    int rc2 = setup_per_op(ctx, kp);
+    if (rc2) {
+      (void)hipFree(ctx->scratch);
+      delete ctx;
+      return rc2;
+    }
+    ctx->kp = kp;
+    *out = ctx;
+    return TD_OK;
+  }
+
   // pack the weights into the per-wave streams
   const size_t code_bytes = (size_t)stream_code_chunks * TD_CHUNK;
   ctx->wstream_bytes = code_bytes + (size_t)stream_scale_blocks * TD_SCHUNK + TD_CHUNK;
@@ -432,9 +554,28 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
   p.kc = (uint16_t*)kv->k;
   p.vc = (uint16_t*)kv->v;
   hipStream_t s = (hipStream_t)stream;
+  if (ctx->executor != TD_EXEC_MEGAKERNEL) {
+    ctx->op.kc = p.kc;
+    ctx->op.vc = p.vc;
+    ctx->op.logits = d_logits_out;
+    if (ctx->executor == TD_EXEC_GRAPH &&
+        (!ctx->gexec || ctx->g_kc != p.kc || ctx->g_vc != p.vc || ctx->g_logits != d_logits_out)) {
+      int rc = capture_graph(ctx);
+      if (rc) return rc;
+    }
+  }
   if (ctx->timing) (void)hipEventRecord(ctx->ev0, s);
-  int le = td_launch_megakernel(&p, ctx->ncu, ctx->ring, stream);
-  if (le != 0) return hip_fail((hipError_t)le, "megakernel launch");
+  int le = 0;
+  if (ctx->executor == TD_EXEC_MEGAKERNEL) {
+    le = td_launch_megakernel(&p, ctx->ncu, ctx->ring, stream);
+  } else {
+    le = td_launch_op_begin(&ctx->op, d_token, pos, stream);
+    if (le == 0) {
+      if (ctx->executor == TD_EXEC_PER_OP) le = td_launch_op_layers(&ctx->op, stream);
+      else le = (int)hipGraphLaunch(ctx->gexec, s);
+    }
+  }
+  if (le != 0) return hip_fail((hipError_t)le, "step launch");
   if (ctx->timing) {
     (void)hipEventRecord(ctx->ev1, s);
     ctx->timed = true;
@@ -469,8 +610,11 @@ void td_destroy(td_ctx* ctx) {
   if (ctx->launched) (void)hipStreamSynchronize(ctx->last_stream);
   if (ctx->ev0) (void)hipEventDestroy(ctx->ev0);
   if (ctx->ev1) (void)hipEventDestroy(ctx->ev1);
+  drop_graph(ctx);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   if (ctx->scratch) (void)hipFree(ctx->scratch);
   if (ctx->wstream) (void)hipFree(ctx->wstream);
+  if (ctx->opbuf) (void)hipFree(ctx->opbuf);
   delete ctx;
 }
 

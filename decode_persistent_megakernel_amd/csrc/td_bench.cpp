@@ -12,7 +12,9 @@
 // timed steps: a transfer of known size, against which hardware byte
 // counters read on the decode kernel can be scaled.
 //
-//   td_bench [--config NAME] [--steps K] [--warmup W] [--copy-calibration] [--print-config]
+// --executor megakernel|per_op|graph picks the executor behind td_decode_step.
+//
+//   td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--copy-calibration] [--print-config]
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -128,6 +130,8 @@ int main(int argc, char** argv) {
   std::string name = "llama1b";
   int steps = 128, warmup = 8;
   bool only_config = false, copy_cal = false;
+  int executor = TD_EXEC_MEGAKERNEL;
+  std::string ex_name = "megakernel";
   for (int i = 1; i < argc; ++i) {
     const std::string a = argv[i];
     if (a == "--config" && i + 1 < argc) name = argv[++i];
@@ -135,9 +139,19 @@ int main(int argc, char** argv) {
     else if (a == "--warmup" && i + 1 < argc) warmup = atoi(argv[++i]);
     else if (a == "--print-config") only_config = true;
     else if (a == "--copy-calibration") copy_cal = true;
+    else if (a == "--executor" && i + 1 < argc) {
+      ex_name = argv[++i];
+      if (ex_name == "megakernel") executor = TD_EXEC_MEGAKERNEL;
+      else if (ex_name == "per_op") executor = TD_EXEC_PER_OP;
+      else if (ex_name == "graph") executor = TD_EXEC_GRAPH;
+      else {
+        fprintf(stderr, "td_bench: unknown executor %s\n", ex_name.c_str());
+        return 2;
+      }
+    }
     else {
-      fprintf(stderr, "usage: td_bench [--config NAME] [--steps K] [--warmup W] [--copy-calibration] "
-                      "[--print-config]\n");
+      fprintf(stderr, "usage: td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] "
+                      "[--copy-calibration] [--print-config]\n");
       return 2;
     }
   }
@@ -219,7 +233,7 @@ int main(int argc, char** argv) {
   td_kv kv{kc, vc, w.max_ctx};
 
   td_ctx* ctx = nullptr;
-  TD(td_create(&cfg, &tw, TD_EXEC_MEGAKERNEL, &ctx));
+  TD(td_create(&cfg, &tw, executor, &ctx));
   hipStream_t stream;
   CK(hipStreamCreate(&stream));
   float* logits = nullptr;
@@ -270,9 +284,9 @@ int main(int argc, char** argv) {
     CK(hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]));
     total += ms;
   }
-  printf("{\"workload\": \"%s\", \"steps\": %d, \"warmup\": %d, \"positions\": [%d, %d], "
-         "\"ms_per_step\": %.4f, \"tokens_per_s\": %.2f}\n",
-         w.name, steps, warmup, start, start + steps - 1, total / steps, steps / (total / 1e3));
+  printf("{\"workload\": \"%s\", \"executor\": \"%s\", \"steps\": %d, \"warmup\": %d, "
+         "\"positions\": [%d, %d], \"ms_per_step\": %.4f, \"tokens_per_s\": %.2f}\n",
+         w.name, ex_name.c_str(), steps, warmup, start, start + steps - 1, total / steps, steps / (total / 1e3));
   fflush(stdout);
 
   if (copy_cal) {

@@ -1,0 +1,190 @@
+// td_device.h - device helpers shared by the persistent decode kernel
+// (td_kernels.hip) and the per-op kernels (td_ops.hip): number formats, wave
+// reductions, the chunk dot products and the attention tile update.  Both
+// paths compute a GEMV row or an attention tile with exactly these routines.
+#ifndef TD_DEVICE_H
+#define TD_DEVICE_H
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define DEV __device__ __forceinline__
+
+DEV int lane_id() { return (int)__lane_id(); }
+DEV int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ------------------------------------------------------------ memory helpers
+DEV uint32_t ld_u(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV float ld_f(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void st_u(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV void st_f(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV void st_u16_sc1(uint16_t* p, uint32_t v) {
+  asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// workgroup barrier that waits for LDS traffic only (never for the ring loads)
+DEV void wg_bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+DEV void vmcnt_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ------------------------------------------------------------ number formats
+DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+DEV float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+DEV uint32_t f2bf(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+DEV float f16f(uint32_t h) { return __half2float(__ushort_as_half((unsigned short)(h & 0xffffu))); }
+
+// ------------------------------------------------------------ wave reductions (DPP)
+template <int CTRL, int RM = 0xf>
+DEV float dpp(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, RM, 0xf, false));
+}
+DEV float wave_sum(float v) {
+  v += dpp<0x111>(0.f, v);  // row_shr:1
+  v += dpp<0x112>(0.f, v);  // row_shr:2
+  v += dpp<0x114>(0.f, v);  // row_shr:4
+  v += dpp<0x118>(0.f, v);  // row_shr:8  -> lane 15 of each row holds the row sum
+  v += dpp<0x142, 0xa>(0.f, v);  // row_bcast:15 -> rows 1, 3
+  v += dpp<0x143, 0xc>(0.f, v);  // row_bcast:31 -> rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+DEV float wave_max(float v) {
+  const float ninf = -__builtin_inff();
+  v = fmaxf(v, dpp<0x111>(ninf, v));
+  v = fmaxf(v, dpp<0x112>(ninf, v));
+  v = fmaxf(v, dpp<0x114>(ninf, v));
+  v = fmaxf(v, dpp<0x118>(ninf, v));
+  v = fmaxf(v, dpp<0x142, 0xa>(ninf, v));
+  v = fmaxf(v, dpp<0x143, 0xc>(ninf, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ------------------------------------------------------------ chunk arithmetic
+// bf16 chunk: lane holds 8 consecutive weights of the row, x holds the 8
+// matching activations.
+DEV float dot_bf16(u32x4 w, const float* x) {
+  f32x4 a = *(const f32x4*)x;
+  f32x4 b = *(const f32x4*)(x + 4);
+  float s = bf_lo(w.x) * a.x;
+  s = fmaf(bf_hi(w.x), a.y, s);
+  s = fmaf(bf_lo(w.y), a.z, s);
+  s = fmaf(bf_hi(w.y), a.w, s);
+  s = fmaf(bf_lo(w.z), b.x, s);
+  s = fmaf(bf_hi(w.z), b.y, s);
+  s = fmaf(bf_lo(w.w), b.z, s);
+  s = fmaf(bf_hi(w.w), b.w, s);
+  return s;
+}
+// int4 chunk: lane holds 32 consecutive 4-bit codes (element 2i in the low
+// nibble of byte i), all in one scale group; weight = scale * (code - 8).
+DEV float dot_int4_word(uint32_t q, const float* x) {
+  f32x4 a = *(const f32x4*)x;
+  f32x4 b = *(const f32x4*)(x + 4);
+  float s = ((float)(q & 15u) - 8.f) * a.x;
+  s = fmaf((float)((q >> 4) & 15u) - 8.f, a.y, s);
+  s = fmaf((float)((q >> 8) & 15u) - 8.f, a.z, s);
+  s = fmaf((float)((q >> 12) & 15u) - 8.f, a.w, s);
+  s = fmaf((float)((q >> 16) & 15u) - 8.f, b.x, s);
+  s = fmaf((float)((q >> 20) & 15u) - 8.f, b.y, s);
+  s = fmaf((float)((q >> 24) & 15u) - 8.f, b.z, s);
+  s = fmaf((float)(q >> 28) - 8.f, b.w, s);
+  return s;
+}
+DEV float dot_int4(u32x4 w, const float* x, float scale) {
+  float s = dot_int4_word(w.x, x);
+  s += dot_int4_word(w.y, x + 8);
+  s += dot_int4_word(w.z, x + 16);
+  s += dot_int4_word(w.w, x + 24);
+  return s * scale;
+}
+
+// ------------------------------------------------------------ attention tile
+// One query head against one 64-row K/V tile in LDS (K rows padded to D + 8
+// elements, V rows D elements, rows past nv zero), updating the online softmax
+// state (m, l) and the unnormalised output ("One launch per token", "The
+// attention trap"; "How I built an LLM inference engine", attention section).
+// Scores: lane tau takes position tau.  P.V: lane (cg, pg) owns columns
+// 4 cg .. 4 cg + 3 over the rows of position group pg; p is broadcast from LDS
+// (ps, 64 floats of this wave); attn_finish sums the groups.
+#define TD_TILE_ROWS 64
+template <int D>
+DEV void attn_tile(const float* qs, const uint16_t* kt, const uint16_t* vt, float* ps, int nv, float& m, float& l,
+                   f32x4& acc) {
+  constexpr int LPR = D / 4, NG = 64 / LPR, RPG = TD_TILE_ROWS / NG;
+  const int lane = lane_id();
+  const uint16_t* kr = kt + lane * (D + 8);
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < D; e += 8) {
+    const u32x4 kw = *(const u32x4*)(kr + e);
+    const f32x4 q0 = *(const f32x4*)(qs + e), q1 = *(const f32x4*)(qs + e + 4);
+    a = fmaf(bf_lo(kw.x), q0.x, a);
+    a = fmaf(bf_hi(kw.x), q0.y, a);
+    a = fmaf(bf_lo(kw.y), q0.z, a);
+    a = fmaf(bf_hi(kw.y), q0.w, a);
+    a = fmaf(bf_lo(kw.z), q1.x, a);
+    a = fmaf(bf_hi(kw.z), q1.y, a);
+    a = fmaf(bf_lo(kw.w), q1.z, a);
+    a = fmaf(bf_hi(kw.w), q1.w, a);
+  }
+  const float s = lane < nv ? a : -__builtin_inff();
+  const float mn = fmaxf(m, wave_max(s));  // finite: nv >= 1
+  const float p = __expf(s - mn);
+  const float corr = __expf(m - mn);
+  l = l * corr + wave_sum(p);
+  m = mn;
+  acc *= corr;
+  ps[lane] = p;
+  const int cg = lane % LPR, pg = lane / LPR;
+  const uint16_t* vrow = vt + pg * RPG * D + cg * 4;
+  const float* prow = ps + pg * RPG;
+#pragma unroll
+  for (int t = 0; t < RPG; t += 4) {
+    const f32x4 p4 = *(const f32x4*)(prow + t);
+    u32x2 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = *(const u32x2*)(vrow + (t + k) * D);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float pk = k == 0 ? p4.x : k == 1 ? p4.y : k == 2 ? p4.z : p4.w;
+      acc.x = fmaf(pk, bf_lo(v[k].x), acc.x);
+      acc.y = fmaf(pk, bf_hi(v[k].x), acc.y);
+      acc.z = fmaf(pk, bf_lo(v[k].y), acc.z);
+      acc.w = fmaf(pk, bf_hi(v[k].y), acc.w);
+    }
+  }
+}
+
+// Sums the position groups: afterwards lanes 0 .. D/4 - 1 hold the columns
+// 4 lane .. 4 lane + 3.
+template <int D>
+DEV f32x4 attn_finish(f32x4 acc) {
+#pragma unroll
+  for (int off = D / 4; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  return acc;
+}
+
+}  // namespace
+#endif

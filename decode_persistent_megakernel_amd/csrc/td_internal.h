@@ -88,6 +88,34 @@ struct td_kparams {
   int32_t off_wtrace;          // LDS: per compute wave 4 uint64 trace stamps
 };
 
+// Parameters of the per-op executor (td_ops.hip): the same weights, table and
+// shapes; activations in plain fp32 device buffers ordered by kernel
+// boundaries; the step's position in a device word so the launches after
+// op_begin can be captured once and replayed.
+struct td_opparams {
+  int32_t L, H, nq, nkv, d, I, V, max_ctx, wf, has_bias;
+  int32_t qd, kvd, qkv_rows, group;
+  float eps, attn_scale;
+  int32_t chunk_len, n_chunks_max;
+  int32_t* pos_word;
+  const td_layer_dev* layers;
+  const uint16_t* embed;
+  const uint16_t* head;
+  const uint16_t* final_norm;
+  const float* rope_cs;
+  uint16_t* kc;
+  uint16_t* vc;
+  float* logits;
+  float* x;          // [H] residual
+  float* q;          // [nq d] rotated queries times 1/sqrt(d)
+  float* part;       // [nkv][n_chunks_max][group][d + 4] attention partials: acc[d], m, l, pad
+  float* o;          // [nq d] attention output
+  float* act;        // [I] SiLU(gate) * up
+  uint32_t* cand;    // [head blocks][4]: value bits, index, nonfinite
+  int32_t* token_out;
+  int32_t* err;
+};
+
 // Per (CU, stage) trace record of TD_TRACE_STAMPS uint64 timestamps (100 MHz):
 // [0..4] sync wave: stage start, inputs staged, compute finished, epilogue
 // finished, next stage's prefetches issued; [8 + 3 w + k] compute wave w:
@@ -129,6 +157,12 @@ int td_launch_megakernel(const td_kparams* p, int ncu, int ring_slots, void* str
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
                      void* stream);
 int td_megakernel_occupancy(int ring_slots, int lds_bytes, int* blocks_per_cu);
+// per-op executor (td_ops.hip)
+int td_op_head_blocks(const td_opparams* p);
+size_t td_op_lds_bytes(const td_opparams* p);
+int td_op_set_lds_limits(const td_opparams* p);
+int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos, void* stream);
+int td_launch_op_layers(const td_opparams* p, void* stream);
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,
                         void* stream);
 int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, float* out,

@@ -1,0 +1,412 @@
+// td_ops.hip - the per-op executor: the decode step as one kernel launch per
+// fused op, the baseline the persistent kernel is measured against ("Decoding
+// in tiles", sec. 1 and 6: one kernel per step with launch gaps and tails;
+// "One launch per token": the same ops captured in a graph).  The arithmetic
+// is the persistent kernel's own: the same chunk dot products over the same
+// 1 KiB chunks in the same order, the same RMSNorm, RoPE, attention tile,
+// merge and argmax, so both executors give the same bits.  Activations live
+// in plain device buffers; kernel boundaries order the ops.
+//
+// Per layer: op_qkv (RMSNorm + QKV GEMV + bias + RoPE + K/V write), op_attn
+// (split-K partials), op_merge, op_o (+ residual), op_gu (RMSNorm + gate/up +
+// SwiGLU), op_down (+ residual); then op_head (final RMSNorm + logits + block
+// candidates) and op_argmax.  op_begin (token, range check, embedding row,
+// position word) runs first and is the only launch that carries the step's
+// arguments, so the rest can be captured once and replayed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "td_internal.h"
+#include "td_device.h"
+
+namespace {
+
+constexpr int OP_WAVES = 4;  // waves per workgroup of the GEMV ops
+
+// xs = RMSNorm(x) * gain over H floats, with the persistent kernel's order:
+// lane-partial sums of squares over 4-float groups strided by 256, one wave
+// sum, inv = 1 / sqrt(ss / H + eps).
+DEV void op_norm_to_lds(const float* x, const uint16_t* gain, int H, float eps, float* xs, float* red) {
+  const int t = threadIdx.x, lane = lane_id();
+  for (int i = t; i < H; i += blockDim.x) xs[i] = x[i];
+  __syncthreads();
+  if (t < 64) {
+    float ss = 0.f;
+    for (int i = lane * 4; i < H; i += 256) {
+      const f32x4 v = *(const f32x4*)(xs + i);
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[0] = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+  const float inv = red[0];
+  for (int i = t * 4; i < H; i += blockDim.x * 4) {
+    f32x4 v = *(const f32x4*)(xs + i);
+    const uint2 g = *(const uint2*)(gain + i);
+    v.x = v.x * inv * bf_lo(g.x);
+    v.y = v.y * inv * bf_hi(g.x);
+    v.z = v.z * inv * bf_lo(g.y);
+    v.w = v.w * inv * bf_hi(g.y);
+    *(f32x4*)(xs + i) = v;
+  }
+}
+
+// Copies n floats to LDS and zeroes the tail up to the chunk multiple.
+DEV void op_copy_to_lds(const float* src, int n, int npad, float* xs) {
+  for (int i = threadIdx.x; i < npad; i += blockDim.x) xs[i] = i < n ? src[i] : 0.f;
+}
+
+DEV void op_zero_tail(float* xs, int from, int to) {
+  for (int i = from + (int)threadIdx.x; i < to; i += blockDim.x) xs[i] = 0.f;
+}
+
+DEV int op_kpad(int K, int fmt) {
+  const int ce = fmt ? 2048 : 512;
+  return (K + ce - 1) / ce * ce;
+}
+
+// One row of a stored linear against xs (LDS): the chunk loop of the
+// persistent kernel, reading the row's chunks straight from the caller's
+// row-major weights (a chunk column past the row end reads as zero weights).
+DEV float op_row(int fmt, const uint8_t* w, const uint16_t* s, int row, int K, const float* xs) {
+  const int lane = lane_id();
+  const int row_bytes = fmt == 0 ? K * 2 : K / 2;
+  const int J = (row_bytes + TD_CHUNK - 1) / TD_CHUNK;
+  const uint8_t* rp = w + (size_t)row * row_bytes;
+  float acc = 0.f;
+  for (int j0 = 0; j0 < J; j0 += 4) {
+    u32x4 c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int boff = (j0 + u) * TD_CHUNK + lane * 16;
+      const uint32_t z = fmt ? 0x88888888u : 0u;
+      c[u] = (j0 + u < J && boff < row_bytes) ? __builtin_nontemporal_load((const u32x4*)(rp + boff))
+                                              : (u32x4){z, z, z, z};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u;
+      if (j >= J) break;
+      if (fmt == 0) {
+        acc += dot_bf16(c[u], xs + j * 512 + lane * 8);
+      } else {
+        const int si = j * 32 + (lane >> 1);
+        const float sc = si < K / 64 ? f16f(s[(size_t)row * (K / 64) + si]) : 0.f;
+        acc += dot_int4(c[u], xs + j * 2048 + lane * 32, sc);
+      }
+    }
+  }
+  return wave_sum(acc);
+}
+
+DEV int op_unit_row_qkv(const td_opparams& P, int u, int r) {
+  const int half = P.d >> 1;
+  const int head = u / half;
+  const int i = u - head * half;
+  return head * P.d + i + r * half;
+}
+
+// --------------------------------------------------------------- op_begin
+__global__ void __launch_bounds__(256) op_begin(td_opparams P, const int32_t* d_token, int32_t pos) {
+  __shared__ int tok_s;
+  if (threadIdx.x == 0) {
+    int tok = *d_token;
+    if (tok < 0 || tok >= P.V) {
+      atomicOr(P.err, TD_ERRBIT_RANGE);
+      tok = 0;
+    }
+    tok_s = tok;
+    *P.pos_word = pos;
+  }
+  __syncthreads();
+  const uint16_t* e = P.embed + (size_t)tok_s * P.H;
+  for (int i = threadIdx.x; i < P.H; i += blockDim.x) P.x[i] = bf16f(e[i]);
+}
+
+// --------------------------------------------------------------- op_qkv
+__global__ void __launch_bounds__(256) op_qkv(td_opparams P, int layer, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const td_layer_dev& Ld = P.layers[layer];
+  op_norm_to_lds(P.x, Ld.attn_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
+  op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int pos = *P.pos_word;
+  const int half = P.d >> 1;
+  const int U = P.qkv_rows / 2;
+  for (int k = 0; k < R; ++k) {
+    const int u = (blockIdx.x * OP_WAVES + wave) * R + k;
+    if (u >= U) break;
+    const int ra = op_unit_row_qkv(P, u, 0), rb = ra + half;
+    float a = op_row(P.wf, Ld.w[0], Ld.s[0], ra, P.H, xs);
+    float b = op_row(P.wf, Ld.w[0], Ld.s[0], rb, P.H, xs);
+    if (lane != 0) continue;
+    if (P.has_bias) {
+      a += bf16f(Ld.bias[ra]);
+      b += bf16f(Ld.bias[rb]);
+    }
+    const int i = ra % P.d;
+    if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
+      const float c = P.rope_cs[((size_t)pos * half + i) * 2], sn = P.rope_cs[((size_t)pos * half + i) * 2 + 1];
+      const float a2 = a * c - b * sn;
+      const float b2 = b * c + a * sn;
+      a = a2;
+      b = b2;
+    }
+    if (ra < P.qd) {
+      P.q[ra] = a * P.attn_scale;
+      P.q[rb] = b * P.attn_scale;
+    } else {
+      const bool isk = ra < P.qd + P.kvd;
+      const int g = (ra - P.qd - (isk ? 0 : P.kvd)) / P.d;
+      uint16_t* row = (isk ? P.kc : P.vc) + (((size_t)layer * P.nkv + g) * P.max_ctx + pos) * P.d;
+      row[i] = (uint16_t)f2bf(a);
+      row[i + half] = (uint16_t)f2bf(b);
+    }
+  }
+}
+
+// --------------------------------------------------------------- op_attn
+// Workgroup (g, c): kv head g, positions of chunk c; wave h < group runs query
+// head g * group + h; all 8 waves load the tiles.
+template <int D>
+__global__ void __launch_bounds__(512) op_attn(td_opparams P, int layer) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int pos = *P.pos_word;
+  const int G = P.group;
+  const int g = blockIdx.x / P.n_chunks_max, c = blockIdx.x - g * P.n_chunks_max;
+  const int n_used = (pos + P.chunk_len) / P.chunk_len;
+  if (c >= n_used) return;
+  const int t0 = c * P.chunk_len, t1 = min(t0 + P.chunk_len, pos + 1);
+  float* qs = (float*)lds;                                             // [G][D]
+  float* ps = qs + G * D;                                              // [G][64]
+  uint16_t* kt = (uint16_t*)(ps + G * TD_TILE_ROWS);                   // [64][D + 8]
+  uint16_t* vt = kt + TD_TILE_ROWS * (D + 8);                          // [64][D]
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = P.q[(size_t)g * G * D + i];
+  const size_t head_off = ((size_t)layer * P.nkv + g) * P.max_ctx;
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int Q16 = D / 8;  // 16-byte pieces per row
+  for (int tb = t0; tb < t1; tb += TD_TILE_ROWS) {
+    const int nv = min(TD_TILE_ROWS, t1 - tb);
+    __syncthreads();  // previous tile consumed
+    for (int i = threadIdx.x; i < TD_TILE_ROWS * Q16; i += blockDim.x) {
+      const int row = i / Q16, pc = i - row * Q16;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (row < nv) {
+        kv = *(const u32x4*)(P.kc + (head_off + tb + row) * D + pc * 8);
+        vv = *(const u32x4*)(P.vc + (head_off + tb + row) * D + pc * 8);
+      }
+      *(u32x4*)(kt + row * (D + 8) + pc * 8) = kv;
+      *(u32x4*)(vt + row * D + pc * 8) = vv;
+    }
+    __syncthreads();  // tile in LDS
+    if (wave < G) attn_tile<D>(qs + wave * D, kt, vt, ps + wave * TD_TILE_ROWS, nv, m, l, acc);
+  }
+  if (wave < G) {
+    acc = attn_finish<D>(acc);
+    float* pr = P.part + (((size_t)g * P.n_chunks_max + c) * G + wave) * (D + 4);
+    if (lane < D / 4) *(f32x4*)(pr + 4 * lane) = acc;
+    if (lane == 0) *(f32x4*)(pr + D) = f32x4{m, l, 0.f, 0.f};
+  }
+}
+
+// --------------------------------------------------------------- op_merge
+// Workgroup g, wave h: o = sum_c acc_c w_c with w_c = e^(m_c - M) / sum l e^(m - M),
+// chunk 0 first, the others fused in chunk order.
+template <int D>
+__global__ void __launch_bounds__(512) op_merge(td_opparams P) {
+  const int pos = *P.pos_word;
+  const int G = P.group, g = blockIdx.x, h = threadIdx.x >> 6, lane = lane_id();
+  if (h >= G) return;
+  const int n = (pos + P.chunk_len) / P.chunk_len;  // <= 64
+  const float* base = P.part + (size_t)g * P.n_chunks_max * G * (D + 4);
+  auto part = [&](int c) { return base + ((size_t)c * G + h) * (D + 4); };
+  const bool have = lane < n;
+  const float* own = part(have ? lane : 0);
+  const float mm = have ? own[D] : -__builtin_inff();
+  const float ll = have ? own[D + 1] : 0.f;
+  const float M = wave_max(mm);
+  const float w0 = have ? __expf(mm - M) : 0.f;
+  __shared__ float wl[8][64];  // the weights leave the lanes before the loop below diverges
+  wl[h][lane] = w0 / wave_sum(ll * w0);
+  for (int e = lane * 4; e < D; e += 256) {
+    const float wc0 = wl[h][0];
+    const f32x4 p0 = *(const f32x4*)(part(0) + e);
+    f32x4 o;
+    o.x = p0.x * wc0;
+    o.y = p0.y * wc0;
+    o.z = p0.z * wc0;
+    o.w = p0.w * wc0;
+    for (int c = 1; c < n; ++c) {
+      const float wc = wl[h][c];
+      const f32x4 v = *(const f32x4*)(part(c) + e);
+      o.x = fmaf(wc, v.x, o.x);
+      o.y = fmaf(wc, v.y, o.y);
+      o.z = fmaf(wc, v.z, o.z);
+      o.w = fmaf(wc, v.w, o.w);
+    }
+    *(f32x4*)(P.o + ((size_t)g * G + h) * D + e) = o;
+  }
+}
+
+// --------------------------------------------------------------- op_o / op_down
+// x[r] += W[r] . in (in = o for the output projection, act for the down projection)
+__global__ void __launch_bounds__(256) op_resid(td_opparams P, int layer, int which, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const td_layer_dev& Ld = P.layers[layer];
+  const int K = which == 1 ? P.qd : P.I;
+  op_copy_to_lds(which == 1 ? P.o : P.act, K, op_kpad(K, P.wf), xs);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int k = 0; k < R; ++k) {
+    const int r = (blockIdx.x * OP_WAVES + wave) * R + k;
+    if (r >= P.H) break;
+    const float y = op_row(P.wf, Ld.w[which], Ld.s[which], r, K, xs);
+    if (lane_id() == 0) P.x[r] = P.x[r] + y;
+  }
+}
+
+// --------------------------------------------------------------- op_gu
+__global__ void __launch_bounds__(256) op_gu(td_opparams P, int layer, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const td_layer_dev& Ld = P.layers[layer];
+  op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
+  op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int k = 0; k < R; ++k) {
+    const int u = (blockIdx.x * OP_WAVES + wave) * R + k;
+    if (u >= P.I) break;
+    const float gt = op_row(P.wf, Ld.w[2], Ld.s[2], u, P.H, xs);
+    const float up = op_row(P.wf, Ld.w[2], Ld.s[2], u + P.I, P.H, xs);
+    if (lane_id() == 0) P.act[u] = gt / (1.0f + expf(-gt)) * up;
+  }
+}
+
+// --------------------------------------------------------------- op_head / op_argmax
+__global__ void __launch_bounds__(256) op_head(td_opparams P, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  __shared__ float cv[OP_WAVES];
+  __shared__ int ci[OP_WAVES], cb[OP_WAVES];
+  op_norm_to_lds(P.x, P.final_norm, P.H, P.eps, xs, xs + op_kpad(P.H, 0));
+  op_zero_tail(xs, P.H, op_kpad(P.H, 0));
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff, bad = 0;
+  for (int k = 0; k < R; ++k) {
+    const int r = (blockIdx.x * OP_WAVES + wave) * R + k;
+    if (r >= P.V) break;
+    const float v = op_row(0, (const uint8_t*)P.head, nullptr, r, P.H, xs);
+    if (lane == 0) P.logits[r] = v;
+    if (!isfinite(v)) bad = 1;
+    else if (v > bv) { bv = v; bi = r; }
+  }
+  if (lane == 0) {
+    cv[wave] = bv;
+    ci[wave] = bi;
+    cb[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < OP_WAVES; ++w) {
+      if (cv[w] > bv || (cv[w] == bv && ci[w] < bi)) { bv = cv[w]; bi = ci[w]; }
+      bad |= cb[w];
+    }
+    P.cand[blockIdx.x * 4 + 0] = __float_as_uint(bv);
+    P.cand[blockIdx.x * 4 + 1] = (uint32_t)bi;
+    P.cand[blockIdx.x * 4 + 2] = (uint32_t)bad;
+  }
+}
+
+__global__ void __launch_bounds__(64) op_argmax(td_opparams P, int nblocks) {
+  const int lane = lane_id();
+  float fv = -__builtin_inff();
+  int fi = 0x7fffffff, fbad = 0;
+  for (int c = lane; c < nblocks; c += 64) {
+    const float v = __uint_as_float(P.cand[c * 4 + 0]);
+    const int i = (int)P.cand[c * 4 + 1];
+    fbad |= (int)P.cand[c * 4 + 2];
+    if (v > fv || (v == fv && i < fi)) { fv = v; fi = i; }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(fv, off);
+    const int oi = __shfl_xor(fi, off);
+    if (ov > fv || (ov == fv && oi < fi)) { fv = ov; fi = oi; }
+  }
+  fbad = __any(fbad);
+  if (lane == 0) {
+    *P.token_out = fi == 0x7fffffff ? 0 : fi;
+    if (fbad) atomicOr(P.err, TD_ERRBIT_NONFINITE);
+  }
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- launchers
+namespace {
+constexpr int R_QKV = 1, R_RESID = 1, R_GU = 4, R_HEAD = 16;
+int blocks_for(int units, int r) { return (units + OP_WAVES * r - 1) / (OP_WAVES * r); }
+}  // namespace
+
+int td_op_head_blocks(const td_opparams* p) { return blocks_for(p->V, R_HEAD); }
+
+size_t td_op_lds_bytes(const td_opparams* p) {
+  auto kp = [](int K, int f) { return (size_t)((K + (f ? 2047 : 511)) / (f ? 2048 : 512) * (f ? 2048 : 512)); };
+  size_t x = std::max({kp(p->H, p->wf), kp(p->qd, p->wf), kp(p->I, p->wf), kp(p->H, 0)}) * 4 + 16;
+  const size_t D = (size_t)p->d, G = (size_t)p->group;
+  const size_t a = G * D * 4 + G * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2;
+  return std::max(x, a);
+}
+
+int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos, void* stream) {
+  op_begin<<<1, 256, 0, (hipStream_t)stream>>>(*p, d_token, pos);
+  return (int)hipGetLastError();
+}
+
+// Every launch of the step after op_begin, in order.
+int td_launch_op_layers(const td_opparams* p, void* stream) {
+  const hipStream_t s = (hipStream_t)stream;
+  const td_opparams& P = *p;
+  const size_t lds = td_op_lds_bytes(p);
+  const int U = P.qkv_rows / 2;
+  for (int l = 0; l < P.L; ++l) {
+    op_qkv<<<blocks_for(U, R_QKV), 256, lds, s>>>(P, l, R_QKV);
+    if (P.d == 64) {
+      op_attn<64><<<P.nkv * P.n_chunks_max, 512, lds, s>>>(P, l);
+      op_merge<64><<<P.nkv, 512, 0, s>>>(P);
+    } else {
+      op_attn<128><<<P.nkv * P.n_chunks_max, 512, lds, s>>>(P, l);
+      op_merge<128><<<P.nkv, 512, 0, s>>>(P);
+    }
+    op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 1, R_RESID);
+    op_gu<<<blocks_for(P.I, R_GU), 256, lds, s>>>(P, l, R_GU);
+    op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 3, R_RESID);
+  }
+  const int hb = blocks_for(P.V, R_HEAD);
+  op_head<<<hb, 256, lds, s>>>(P, R_HEAD);
+  op_argmax<<<1, 64, 0, s>>>(P, hb);
+  return (int)hipGetLastError();
+}
+
+int td_op_set_lds_limits(const td_opparams* p) {
+  const int lds = (int)td_op_lds_bytes(p);
+  hipError_t e = hipSuccess;
+  const void* fns[] = {(const void*)op_qkv, (const void*)op_attn<64>, (const void*)op_attn<128>,
+                       (const void*)op_resid, (const void*)op_gu, (const void*)op_head};
+  for (const void* f : fns)
+    if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  return (int)e;
+}

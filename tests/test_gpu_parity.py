@@ -126,7 +126,7 @@ def test_attention_hook_matches_oracle(td, n, d):
 
 # ------------------------------------------------------------------ whole step (megakernel)
 
-def run_compare(td, cfg, model, kv_k, kv_v, first_token, start_pos, n_steps, tol, label):
+def run_compare(td, cfg, model, kv_k, kv_v, first_token, start_pos, n_steps, tol, label, executor=0):
     """Teacher-forced comparison: both sides start from the same K/V state; at
     every step both receive the same input token (the oracle's greedy choice)
     and their logits and greedy tokens are compared."""
@@ -134,7 +134,7 @@ def run_compare(td, cfg, model, kv_k, kv_v, first_token, start_pos, n_steps, tol
     o.set_kv(kv_k, kv_v)
     dm = td.DeviceModel(model)
     kv = td.KVCache(cfg, cfg.max_ctx, k=kv_k, v=kv_v)
-    dec = td.Decoder(dm, cfg.max_ctx)
+    dec = td.Decoder(dm, cfg.max_ctx, executor=executor)
     tok = torch.empty(1, dtype=torch.int32, device="cuda")
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
     t = int(first_token)
