@@ -17,6 +17,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
          # packed fp32 instructions stay off: ordinary float code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # no implicit a*b+c contraction: every fused multiply-add is an explicit
+         # fmaf, so the persistent kernel and the per-op kernels round alike
+         "-ffp-contract=off",
          "-Wall", "-Wno-unused-function"]
 
 

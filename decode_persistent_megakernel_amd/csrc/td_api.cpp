@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -67,24 +68,45 @@ struct td_ctx {
 
 namespace {
 
+// Builds the partition table: CU c owns units [part[s][c], part[s][c + 1]) of
+// unit space s, in proportion to the per-CU weights (all 1 unless a weighting
+// is given), so that every unit has exactly one owner.
+std::vector<int32_t> build_partition(const td_config& c, int ncu, const std::vector<double>& wt) {
+  const int64_t U[TD_NSPACES] = {(int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2, c.hidden,
+                                 c.intermediate, c.vocab};
+  std::vector<double> cum(ncu + 1, 0.0);
+  for (int i = 0; i < ncu; ++i) cum[i + 1] = cum[i] + wt[i];
+  std::vector<int32_t> part((size_t)TD_NSPACES * (ncu + 1));
+  for (int sp = 0; sp < TD_NSPACES; ++sp)
+    for (int i = 0; i <= ncu; ++i)
+      part[(size_t)sp * (ncu + 1) + i] =
+          i == ncu ? (int32_t)U[sp] : (int32_t)std::llround((double)U[sp] * cum[i] / cum[ncu]);
+  return part;
+}
+
 // Enumerates the row ownership of every GEMV stage exactly as the kernel
-// derives it and checks: every unit of every stage is owned by exactly one
-// (CU, wave); every row is produced once; all rows are inside the matrix;
-// per-CU outputs fit the LDS output area.
-int validate_plan(const td_config& c, int ncu, int out_floats, int own_floats) {
+// derives it from the partition table and checks: every unit of every stage is
+// owned by exactly one (CU, wave); every row is produced once; all rows are
+// inside the matrix; a CU's residual rows fit the LDS area; a wave's QKV units
+// fit one wavefront (their biases are held one per lane).
+int validate_plan(const td_config& c, int ncu, const std::vector<int32_t>& part, int own_floats) {
   const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab;
-  const int qd = c.n_q_heads * d, qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * d;
+  const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * d;
   struct St {
-    int U, rpu, rows, kind;
-  } st[] = {{qkv_rows / 2, 2, qkv_rows, TD_ST_QKV}, {H, 1, H, TD_ST_O}, {I, 2, 2 * I, TD_ST_GU},
-            {H, 1, H, TD_ST_DOWN}, {V, 1, V, TD_ST_HEAD}};
+    int U, rpu, rows, kind, space;
+  } st[] = {{qkv_rows / 2, 2, qkv_rows, TD_ST_QKV, TD_SP_QKV}, {H, 1, H, TD_ST_O, TD_SP_H},
+            {I, 2, 2 * I, TD_ST_GU, TD_SP_I}, {H, 1, H, TD_ST_DOWN, TD_SP_H}, {V, 1, V, TD_ST_HEAD, TD_SP_V}};
   for (const St& s : st) {
     std::vector<uint8_t> seen_row(s.rows, 0);
     std::vector<uint8_t> seen_unit(s.U, 0);
+    const int32_t* t = part.data() + (size_t)s.space * (ncu + 1);
+    if (t[0] != 0 || t[ncu] != s.U) return fail(TD_E_PLAN, "partition does not cover the unit space");
     for (int cu = 0; cu < ncu; ++cu) {
-      int u0 = (int)(((int64_t)s.U * cu) / ncu), u1 = (int)(((int64_t)s.U * (cu + 1)) / ncu);
+      const int u0 = t[cu], u1 = t[cu + 1];
       if (u0 < 0 || u1 > s.U || u1 < u0) return fail(TD_E_PLAN, "unit range out of bounds");
-      if ((u1 - u0) * s.rpu > out_floats) return fail(TD_E_PLAN, "per-CU outputs exceed the LDS output area");
+      if (s.space == TD_SP_H && u1 - u0 > own_floats) return fail(TD_E_PLAN, "residual rows exceed the LDS area");
+      if (s.space == TD_SP_QKV && (u1 - u0 + TD_NW - 1) / TD_NW > 64)
+        return fail(TD_E_UNSUPPORTED, "more than 64 QKV row pairs per compute wave");
       for (int wave = 0; wave < TD_NW; ++wave) {
         for (int u = u0 + wave; u < u1; u += TD_NW) {
           if (seen_unit[u]++) return fail(TD_E_PLAN, "unit owned twice");
@@ -107,9 +129,6 @@ int validate_plan(const td_config& c, int ncu, int out_floats, int own_floats) {
     for (int r = 0; r < s.rows; ++r)
       if (!seen_row[r]) return fail(TD_E_PLAN, "row without a writer");
   }
-  int own = (int)(((int64_t)H + ncu - 1) / ncu);
-  if (own > own_floats) return fail(TD_E_PLAN, "residual rows exceed the LDS area");
-  (void)qd;
   return TD_OK;
 }
 
@@ -302,78 +321,101 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     chunk_len += TD_TILE;
   const int n_chunks_max = n_chunks_of(chunk_len);
   if (n_chunks_max * nkv > ncu) return fail(TD_E_PLAN, "attention split exceeds the CU count");
-  if ((qkv_rows / 2 + ncu - 1) / ncu > 64) return fail(TD_E_UNSUPPORTED, "more than 64 QKV row pairs per CU");
 
-  // LDS layout
+  // partition of every GEMV stage's units over the CUs
+  const std::vector<double> cu_weight(ncu, 1.0);
+  const std::vector<int32_t> part = build_partition(c, ncu, cu_weight);
+  int own_floats = 0;
+  for (int i = 0; i < ncu; ++i)
+    own_floats = std::max(own_floats, part[(size_t)TD_SP_H * (ncu + 1) + i + 1] - part[(size_t)TD_SP_H * (ncu + 1) + i]);
+  own_floats = (int)round_up(std::max(own_floats, 1), 64);
+  // the LDS output area holds a CU's dot products of one stage (rpu per unit)
+  int out_floats = 0;
+  for (int i = 0; i < ncu; ++i) {
+    auto cnt = [&](int sp) { return part[(size_t)sp * (ncu + 1) + i + 1] - part[(size_t)sp * (ncu + 1) + i]; };
+    out_floats = std::max({out_floats, 2 * cnt(TD_SP_QKV), cnt(TD_SP_H), 2 * cnt(TD_SP_I), cnt(TD_SP_V)});
+  }
+  out_floats = (int)round_up(std::max(out_floats, 1), 64);
+
+  // LDS layout: the rings take what the rest leaves, up to TD_RING_MAX slots per wave
   const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
   const int64_t kpad = round_up(std::max({H, qd, I}), 2048);
   const int64_t xin_bytes = std::max<int64_t>(kpad * 4, A.bytes);
-  auto per_cu = [&](int64_t U) { return (int)((U + ncu - 1) / ncu); };
-  const int out_floats = (int)round_up(std::max({per_cu(qkv_rows / 2) * 2, per_cu(H), per_cu(I) * 2, per_cu(V)}), 64);
-  const int own_floats = (int)round_up(per_cu(H), 64);
-  const int64_t lds_cap = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
-  int ring = 0;
+  const int64_t lds_cap = std::min<int64_t>((int64_t)prop.maxSharedMemoryPerMultiProcessor, 160 * 1024);
   td_kparams kp{};
-  uint64_t stream_code_chunks = 0, stream_scale_blocks = 0;
-  for (int S : {16, 12, 8}) {
+  int64_t fixed = 0;
+  {
     int64_t off = 0;
-    kp.off_ring = (int32_t)off;
-    off += (int64_t)TD_NW * S * TD_CHUNK;
-    kp.off_sring = (int32_t)off;
-    if (c.weight_format == TD_WF_INT4_G64) off += (int64_t)TD_NW * S * TD_SCHUNK;
-    kp.off_xin = (int32_t)off;
-    kp.off_attn = (int32_t)off;
-    off += round_up(xin_bytes, 256);
+    kp.off_xin = kp.off_attn = (int32_t)off;
+    off += round_up(xin_bytes, 1024);
     kp.off_tile = (int32_t)off;
     off += round_up(td_tile_bytes(d), 256);
-    kp.off_out = (int32_t)off;
-    off += (int64_t)out_floats * 4;
     kp.off_own = (int32_t)off;
     off += (int64_t)own_floats * 4;
-    kp.off_gain = (int32_t)off;
-    off += round_up((int64_t)H * 2, 256);
+    kp.off_out = (int32_t)off;
+    off += (int64_t)out_floats * 4;
     kp.off_rope = (int32_t)off;
     off += round_up((int64_t)d * 4, 256);
-    kp.off_wtrace = (int32_t)off;
-    off += (TD_NW + 1) * 4 * 8;
-    if (off <= lds_cap && off <= 160 * 1024) {
-      int blocks = 0;
-      int oe = td_megakernel_occupancy(S, (int)off, &blocks);
-      if (oe == 0 && blocks >= 1) {
-        ring = S;
-        kp.lds_bytes = (int32_t)off;
-        break;
-      }
-    }
+    kp.off_ctl = (int32_t)off;
+    off += TD_CTL_WORDS * 4;
+    fixed = round_up(off, 1024);
   }
-  if (!ring) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
+  const int64_t per_slot = (int64_t)TD_NW * (TD_CHUNK + (c.weight_format == TD_WF_INT4_G64 ? TD_SCHUNK : 0));
+  const int64_t ring = std::min<int64_t>(TD_RING_MAX, (lds_cap - fixed) / per_slot);
+  if (ring < TD_RING_MIN) return fail(TD_E_UNSUPPORTED, "the LDS cannot hold the weight rings for this shape");
+  {
+    // rings first (1 KiB aligned), then the fixed areas shifted behind them
+    const int32_t ring_bytes = (int32_t)((int64_t)TD_NW * ring * TD_CHUNK);
+    const int32_t sring_bytes =
+        c.weight_format == TD_WF_INT4_G64 ? (int32_t)round_up((int64_t)TD_NW * ring * TD_SCHUNK, 1024) : 0;
+    kp.off_ring = 0;
+    kp.off_sring = ring_bytes;
+    const int32_t shift = ring_bytes + sring_bytes;
+    kp.off_xin += shift;
+    kp.off_attn += shift;
+    kp.off_tile += shift;
+    kp.off_own += shift;
+    kp.off_out += shift;
+    kp.off_rope += shift;
+    kp.off_ctl += shift;
+    kp.lds_bytes = (int32_t)(shift + fixed);
+  }
+  if (kp.lds_bytes > lds_cap) return fail(TD_E_UNSUPPORTED, "LDS layout exceeds the CU's LDS");
+  {
+    int blocks = 0;
+    const int oe = td_megakernel_occupancy(d, kp.lds_bytes, &blocks);
+    if (oe != 0 || blocks < 1) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
+  }
+  kp.ring_slots = (int32_t)ring;
 
-  rc = validate_plan(c, ncu, out_floats, own_floats);
+
+  rc = validate_plan(c, ncu, part, own_floats);
   if (rc) return rc;
 
+  uint64_t stream_code_chunks = 0, stream_scale_blocks = 0;
   // every compute wave's packed stream, counted exactly as the kernel walks it:
   // stages in order (attention has no weights), the wave's units, their rows,
   // the row's chunks
   std::vector<td_wstream> ws((size_t)ncu * TD_NW);
   {
     struct St {
-      int U, rpu, K, fmt;
+      int space, rpu, K, fmt;
     };
     std::vector<St> stages;
     for (int l = 0; l < L; ++l) {
-      stages.push_back({qkv_rows / 2, 2, H, c.weight_format});
-      stages.push_back({H, 1, qd, c.weight_format});
-      stages.push_back({I, 2, H, c.weight_format});
-      stages.push_back({H, 1, I, c.weight_format});
+      stages.push_back({TD_SP_QKV, 2, H, c.weight_format});
+      stages.push_back({TD_SP_H, 1, qd, c.weight_format});
+      stages.push_back({TD_SP_I, 2, H, c.weight_format});
+      stages.push_back({TD_SP_H, 1, I, c.weight_format});
     }
-    stages.push_back({V, 1, H, TD_WF_BF16});
+    stages.push_back({TD_SP_V, 1, H, TD_WF_BF16});
     uint64_t code = 0, scal = 0;
     for (int cu = 0; cu < ncu; ++cu)
       for (int wave = 0; wave < TD_NW; ++wave) {
         uint64_t nt = 0, n4 = 0;
         for (const St& st : stages) {
-          const int u0 = (int)(((int64_t)st.U * cu) / ncu), u1 = (int)(((int64_t)st.U * (cu + 1)) / ncu);
-          const int cnt = u1 - u0;
+          const int32_t* t = part.data() + (size_t)st.space * (ncu + 1);
+          const int cnt = t[cu + 1] - t[cu];
           const int n = cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0;
           const int row_bytes = st.fmt == TD_WF_BF16 ? st.K * 2 : st.K / 2;
           const uint64_t ch = (uint64_t)n * st.rpu * ((row_bytes + TD_CHUNK - 1) / TD_CHUNK);
@@ -394,7 +436,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   ctx->cfg = c;
   ctx->executor = executor;
   ctx->ncu = ncu;
-  ctx->ring = ring;
+  ctx->ring = kp.ring_slots;
 
   // scratch: one allocation, 256-byte aligned pieces
   const int sync_words = TD_SY_WORDS;
@@ -414,6 +456,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const size_t o_rope = take((size_t)c.max_ctx * (d / 2) * 2 * 4);
   const size_t o_layers = take(sizeof(td_layer_dev) * L);
   const size_t o_ws = take(sizeof(td_wstream) * ws.size());
+  const size_t o_ptab = take(sizeof(int32_t) * part.size());
+  const size_t o_gains = take((size_t)(2 * L + 1) * H * 2);
+  const size_t o_bias = c.qkv_bias ? take((size_t)L * qkv_rows * 2) : 0;
   const size_t o_bad = take(4);
   ctx->scratch_bytes = off;
   e = hipMalloc(&ctx->scratch, off);
@@ -456,6 +501,19 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   e = hipMemcpy(base + o_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_layers, layers.data(), sizeof(td_layer_dev) * L, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_ws, ws.data(), sizeof(td_wstream) * ws.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_ptab, part.data(), sizeof(int32_t) * part.size(), hipMemcpyHostToDevice);
+  // the RMSNorm gains and QKV biases, contiguous per layer: the kernel finds
+  // them by arithmetic instead of through the per-layer pointer table
+  for (int l = 0; l < L && e == hipSuccess; ++l) {
+    const td_layer_weights& Lw = w->layers[l];
+    e = hipMemcpy(base + o_gains + (size_t)(2 * l) * H * 2, Lw.attn_norm, (size_t)H * 2, hipMemcpyDeviceToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(base + o_gains + (size_t)(2 * l + 1) * H * 2, Lw.mlp_norm, (size_t)H * 2, hipMemcpyDeviceToDevice);
+    if (e == hipSuccess && c.qkv_bias)
+      e = hipMemcpy(base + o_bias + (size_t)l * qkv_rows * 2, Lw.b_qkv, (size_t)qkv_rows * 2, hipMemcpyDeviceToDevice);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpy(base + o_gains + (size_t)(2 * L) * H * 2, w->final_norm, (size_t)H * 2, hipMemcpyDeviceToDevice);
   if (e != hipSuccess) {
     (void)hipFree(ctx->scratch);
     delete ctx;
@@ -497,6 +555,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   kp.err = (int32_t*)(base + o_err);
   kp.n_stages = 5 * L + 1;
   kp.ws = (const td_wstream*)(base + o_ws);
+  kp.part = (const int32_t*)(base + o_ptab);
+  kp.gains = (const uint16_t*)(base + o_gains);
+  kp.biases = c.qkv_bias ? (const uint16_t*)(base + o_bias) : nullptr;
 
   if (executor != TD_EXEC_MEGAKERNEL) {
     int rc2 = setup_per_op(ctx, kp);
@@ -567,7 +628,7 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
   if (ctx->timing) (void)hipEventRecord(ctx->ev0, s);
   int le = 0;
   if (ctx->executor == TD_EXEC_MEGAKERNEL) {
-    le = td_launch_megakernel(&p, ctx->ncu, ctx->ring, stream);
+    le = td_launch_megakernel(&p, ctx->ncu, stream);
   } else {
     le = td_launch_op_begin(&ctx->op, d_token, pos, stream);
     if (le == 0) {

@@ -8,6 +8,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include "td_internal.h"
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -74,6 +76,29 @@ DEV float wave_max(float v) {
   v = fmaxf(v, dpp<0x142, 0xa>(ninf, v));
   v = fmaxf(v, dpp<0x143, 0xc>(ninf, v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ------------------------------------------------------------ RMSNorm pieces
+// RMSNorm is applied as y = inv * (W . (x * g)) with inv = 1 / sqrt(mean(x^2) +
+// eps): the gains multiply the input elementwise, and the scalar inv multiplies
+// each dot product.  mean(x^2) is summed in a fixed order: the input is cut
+// into TD_NW slices (td_slice); within a slice, lane l adds the squares of the
+// element pairs l, l + 64, ... in order and the lanes are summed by wave_sum;
+// the slice sums are then added in slice order (norm_inv).
+DEV float slice_ssq(const float* x, int lo, int hi) {
+  float ss = 0.f;
+  for (int u = (lo >> 1) + lane_id(); u < (hi >> 1); u += 64) {
+    const float a = x[2 * u], b = x[2 * u + 1];
+    ss = fmaf(a, a, ss);
+    ss = fmaf(b, b, ss);
+  }
+  return wave_sum(ss);
+}
+DEV float norm_inv(const float* ssq, int H, float eps) {
+  float s = ssq[0];
+#pragma unroll
+  for (int w = 1; w < TD_NW; ++w) s += ssq[w];
+  return 1.0f / sqrtf(s / (float)H + eps);
 }
 
 // ------------------------------------------------------------ chunk arithmetic

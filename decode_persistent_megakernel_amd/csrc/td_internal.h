@@ -1,19 +1,25 @@
 // td_internal.h - device-side parameter block and layout constants shared by
-// the host API (td_api.cpp) and the kernels (td_kernels.hip).
+// the host API (td_api.cpp) and the kernels (td_kernels.hip, td_ops.hip).
 #pragma once
 #include <stdint.h>
 
-#define TD_NW 8                       // compute waves per workgroup
+#define TD_NW 8                       // compute waves per workgroup (waves 0..7)
+#define TD_SYNC_WAVE 8                // attention tiles and the greedy-token reduction
 #define TD_WAVE 64
-#define TD_THREADS ((TD_NW + 1) * TD_WAVE)  // + one sync wave
+#define TD_THREADS (9 * TD_WAVE)
 #define TD_TILE 64                    // attention positions per LDS tile
 #define TD_CHUNK 1024                 // bytes per wave-wide weight chunk (64 lanes x 16 B)
 #define TD_SCHUNK 64                  // bytes of fp16 scales per int4 chunk (32 scales)
 #define TD_MAX_GROUP 8                // query heads per kv head handled by one task
-#define TD_SPIN_TICKS 100000000ull    // grid-wait limit in 100 MHz ticks (1 s)
+#define TD_SPIN_TICKS 100000000ull    // wait limit in 100 MHz ticks (1 s)
+#define TD_RING_MIN 4                 // fewest ring slots per compute wave the plan accepts
+#define TD_RING_MAX 24
 
 // stage kinds, in layer order; the head follows the last layer
 enum { TD_ST_QKV = 0, TD_ST_ATTN = 1, TD_ST_O = 2, TD_ST_GU = 3, TD_ST_DOWN = 4, TD_ST_HEAD = 5 };
+
+// unit spaces of the partition table: which units of a GEMV stage each CU owns
+enum { TD_SP_QKV = 0, TD_SP_H = 1, TD_SP_I = 2, TD_SP_V = 3, TD_NSPACES = 4 };
 
 // error bits of the device error word
 enum { TD_ERRBIT_NONFINITE = 1, TD_ERRBIT_RANGE = 2, TD_ERRBIT_TIMEOUT = 4 };
@@ -24,6 +30,17 @@ enum {
   TD_SY_ABORT = 64,   // set when a wait timed out
   TD_SY_FINAL = 128,  // arrivals at the greedy-token reduction
   TD_SY_WORDS = 192
+};
+
+// uint32 word offsets of the LDS control block (intra-workgroup hand-offs)
+enum {
+  TD_CTL_RV = 16,        // rendezvous arrivals of the compute waves (monotonic)
+  TD_CTL_TREADY = 17,    // attention tiles made ready (monotonic)
+  TD_CTL_TDONE = 18,     // attention tiles consumed, summed over the query-head waves
+  TD_CTL_HEADDONE = 19,  // compute waves finished with the head stage
+  TD_CTL_SSQ = 24,       // [8] fp32 partial sums of squares of the RMSNorm input slices
+  TD_CTL_CAND = 32,      // [8][4] per-wave greedy candidates: value bits, index, nonfinite, pad
+  TD_CTL_WORDS = 64
 };
 
 struct td_layer_dev {
@@ -70,22 +87,24 @@ struct td_kparams {
                    // position's K row (rotated) and V row (bf16 values)
   uint2* to;       // [nq d] attention output
   uint2* tact;     // [I] SiLU(gate) * up
-  uint2* tpart;    // [nkv][n_chunks_max][group][d + 4] attention partials: acc[d], m, l, pad
+  uint2* tpart;    // [nkv][group][n_chunks_max][d + 4] attention partials: acc[d], m, l, pad
   uint32_t* cand;  // [ncu][4]: value bits, index, nonfinite
   uint32_t* sync;
   int32_t* token_out;
   int32_t* err;
+  const int32_t* part;  // [TD_NSPACES][ncu + 1] first unit of each CU in each unit space
+  const uint16_t* gains;   // ctx copy of the RMSNorm gains, bf16 [L][2][H] (attention, MLP) then final [H]
+  const uint16_t* biases;  // ctx copy of the QKV biases, bf16 [L][qkv_rows], or null
   // LDS layout (byte offsets into dynamic shared memory)
-  int32_t off_ring, off_sring, off_xin, off_out, off_own, off_attn, off_tile;
+  int32_t off_ring, off_sring, off_xin, off_attn, off_tile, off_own, off_out, off_rope, off_ctl;
   int32_t lds_bytes;
   int32_t n_stages;   // 5 L + 1
+  int32_t ring_slots; // S: LDS ring slots per compute wave
   uint64_t* trace;    // optional: [ncu][n_stages][TD_TRACE_STAMPS] 100 MHz timestamps, or null
   // packed weight streams (built at create time)
   const uint8_t* wcode;
   const uint8_t* wscale;
   const td_wstream* ws;   // [ncu][TD_NW]
-  int32_t off_gain, off_rope;  // LDS: next norm's bf16 gains [H]; (cos, sin) of pos for the d/2 pairs
-  int32_t off_wtrace;          // LDS: per compute wave 4 uint64 trace stamps
 };
 
 // Parameters of the per-op executor (td_ops.hip): the same weights, table and
@@ -108,7 +127,7 @@ struct td_opparams {
   float* logits;
   float* x;          // [H] residual
   float* q;          // [nq d] rotated queries times 1/sqrt(d)
-  float* part;       // [nkv][n_chunks_max][group][d + 4] attention partials: acc[d], m, l, pad
+  float* part;       // [nkv][group][n_chunks_max][d + 4] attention partials: acc[d], m, l, pad
   float* o;          // [nq d] attention output
   float* act;        // [I] SiLU(gate) * up
   uint32_t* cand;    // [head blocks][4]: value bits, index, nonfinite
@@ -117,9 +136,9 @@ struct td_opparams {
 };
 
 // Per (CU, stage) trace record of TD_TRACE_STAMPS uint64 timestamps (100 MHz):
-// [0..4] sync wave: stage start, inputs staged, compute finished, epilogue
-// finished, next stage's prefetches issued; [8 + 3 w + k] compute wave w:
-// stage start, first chunk ready, last chunk done (0 when the wave has no chunk).
+// compute wave w writes [4 w + k]: k = 0 stage entered, 1 inputs staged (the
+// workgroup rendezvous passed), 2 first weight chunk in LDS (or first attention
+// tile done), 3 last output published; 0 where the wave had no part.
 #define TD_TRACE_STAMPS 32
 
 // LDS layout of the attention stage.  The K/V tile area is separate (it is
@@ -134,7 +153,7 @@ static inline int32_t td_tile_bytes(int d) {
 }
 
 struct td_attn_lds {
-  int32_t q, p, part, kvp, merge, bytes;
+  int32_t q, kvp, p, merge, bytes;
 };
 
 #ifdef __HIPCC__
@@ -144,19 +163,29 @@ static inline td_attn_lds td_attn_layout(int d, int group, int n_chunks_max) {
   td_attn_lds a;
   a.q = 0;                                          // group x d queries, then this
   a.kvp = a.q + group * d * 4;                      // position's K and V rows (2 d floats)
-  a.p = a.kvp + 2 * d * 4;                          // group x 64 probabilities
-  a.part = a.p + group * TD_TILE * 4;               // group x (d + 4) own partial
-  a.merge = a.part + group * (d + 4) * 4;           // other chunks' partials
-  a.bytes = a.merge + (n_chunks_max > 1 ? n_chunks_max - 1 : 1) * group * (d + 4) * 4;
+  a.p = a.kvp + 2 * d * 4;                          // group x 64 probabilities / merge weights
+  a.merge = a.p + group * TD_TILE * 4;              // group x (n_chunks_max - 1) x (d + 4) partials
+  a.bytes = a.merge + group * (n_chunks_max > 1 ? n_chunks_max - 1 : 1) * (d + 4) * 4;
   a.bytes = (a.bytes + 255) & ~255;
   return a;
 }
 
+// Input slice of compute wave w (of TD_NW) over a K-element vector, in whole
+// (value, tag) pair units of two elements: [lo, hi).
+#ifdef __HIPCC__
+__host__ __device__
+#endif
+static inline void td_slice(int K, int w, int* lo, int* hi) {
+  const int nu = K / 2;
+  *lo = 2 * (int)(((int64_t)nu * w) / TD_NW);
+  *hi = 2 * (int)(((int64_t)nu * (w + 1)) / TD_NW);
+}
+
 // launch entry points (td_kernels.hip)
-int td_launch_megakernel(const td_kparams* p, int ncu, int ring_slots, void* stream);
+int td_launch_megakernel(const td_kparams* p, int ncu, void* stream);
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
                      void* stream);
-int td_megakernel_occupancy(int ring_slots, int lds_bytes, int* blocks_per_cu);
+int td_megakernel_occupancy(int head_dim, int lds_bytes, int* blocks_per_cu);
 // per-op executor (td_ops.hip)
 int td_op_head_blocks(const td_opparams* p);
 size_t td_op_lds_bytes(const td_opparams* p);

@@ -14,17 +14,18 @@
 // then HEAD: final RMSNorm, logits GEMV, greedy argmax (lowest id on ties,
 // non-finite logit -> error word; "Decoding in tiles", sec. 5).
 //
-// Workgroup roles:
-//   8 compute waves stream weight chunks (1 KiB = 64 lanes x 16 B) from HBM
-//     straight into a per-wave LDS ring with global_load_lds_dwordx4.  Each
-//     wave's chunks are packed at create time in the order it consumes them,
-//     and the ring runs S chunks ahead across stage boundaries: weights never
-//     depend on the token, so the next stage's loads are in flight while the
-//     CU waits for that stage's inputs.  These waves issue no other global
-//     memory operation, so vmcnt counts only ring loads.
-//   1 sync wave does all activation traffic: it stages a stage's inputs in
-//     LDS (with the RMSNorm applied), runs the epilogues (bias, RoPE, K/V
-//     write, SiLU*up, residual, merge, argmax) and publishes the outputs.
+// Workgroup roles (9 waves; no s_barrier after the first instruction block:
+// waves hand work to each other through counters in LDS):
+//   8 compute waves  each streams its own weight chunks (1 KiB = 64 lanes x
+//                 16 B) from HBM into its LDS ring with global_load_lds, in
+//                 the order it consumes them, with a bounded number in flight
+//                 (see "compute waves" below); polls one slice of the stage's
+//                 input vector into LDS, meets the others at a rendezvous, then
+//                 runs its rows from the ring and publishes its own outputs
+//                 (bias, RoPE, K/V write, SiLU*up, residual, logits); in the
+//                 attention stage, wave h < group runs query head h of the
+//                 task and merges.
+//   sync wave     loads the attention K/V tiles and reduces the greedy token.
 // Cross-CU hand-off without grid barriers: every value handed to other CUs is
 // a (value, tag) pair written with one 8-byte agent-scope (sc1) store, and a
 // reader polls the pairs with sc1 loads until all carry the tag of the stage
@@ -41,15 +42,15 @@
 namespace {
 
 // ------------------------------------------------------------ the plan
-// A GEMV stage splits its "units" evenly over the CUs (equal bytes per CU up
-// to one unit) and round-robins a CU's units over its compute waves.  A unit
-// is the set of rows one epilogue needs together: the two rows of a RoPE pair
-// (i, i + d/2) of one head for QKV, the gate and up rows of one intermediate
-// index for GU, one row otherwise.
+// A GEMV stage splits its "units" over the CUs by the partition table (CU c
+// owns units [part[c], part[c+1]) of the stage's unit space) and round-robins
+// a CU's units over its compute waves.  A unit is the set of rows one epilogue
+// needs together: the two rows of a RoPE pair (i, i + d/2) of one head for QKV,
+// the gate and up rows of one intermediate index for GU, one row otherwise.
 struct Gemv {
   const uint8_t* w;
   const uint16_t* s;
-  int K, row_bytes, J, U, rpu, kind, fmt;
+  int K, row_bytes, J, U, rpu, kind, fmt, space;
 };
 
 DEV void stage_of(const td_kparams& P, int seq, int& kind, int& layer) {
@@ -72,20 +73,42 @@ DEV Gemv gemv_of(const td_kparams& P, int kind, int layer) {
     g.U = P.V;
     g.rpu = 1;
     g.fmt = 0;
+    g.space = TD_SP_V;
   } else {
     const td_layer_dev& Ld = P.layers[layer];
     int idx = kind == TD_ST_QKV ? 0 : kind == TD_ST_O ? 1 : kind == TD_ST_GU ? 2 : 3;
     g.w = Ld.w[idx];
     g.s = Ld.s[idx];
     g.fmt = P.wf;
-    if (kind == TD_ST_QKV) { g.K = P.H; g.U = P.qkv_rows / 2; g.rpu = 2; }
-    else if (kind == TD_ST_O) { g.K = P.qd; g.U = P.H; g.rpu = 1; }
-    else if (kind == TD_ST_GU) { g.K = P.H; g.U = P.I; g.rpu = 2; }
-    else { g.K = P.I; g.U = P.H; g.rpu = 1; }
+    if (kind == TD_ST_QKV) { g.K = P.H; g.U = P.qkv_rows / 2; g.rpu = 2; g.space = TD_SP_QKV; }
+    else if (kind == TD_ST_O) { g.K = P.qd; g.U = P.H; g.rpu = 1; g.space = TD_SP_H; }
+    else if (kind == TD_ST_GU) { g.K = P.H; g.U = P.I; g.rpu = 2; g.space = TD_SP_I; }
+    else { g.K = P.I; g.U = P.H; g.rpu = 1; g.space = TD_SP_H; }
   }
   g.row_bytes = g.fmt == 0 ? g.K * 2 : g.K / 2;
   g.J = (g.row_bytes + TD_CHUNK - 1) / TD_CHUNK;
   return g;
+}
+
+// The shape of a GEMV stage from the plan's scalars alone (no memory access):
+// what a compute wave needs to walk its rows.
+struct Shape {
+  int J, rpu, fmt, space;
+};
+DEV Shape shape_of(const td_kparams& P, int kind) {
+  Shape h;
+  int K;
+  if (kind == TD_ST_HEAD) { K = P.H; h.rpu = 1; h.fmt = 0; h.space = TD_SP_V; }
+  else {
+    h.fmt = P.wf;
+    if (kind == TD_ST_QKV) { K = P.H; h.rpu = 2; h.space = TD_SP_QKV; }
+    else if (kind == TD_ST_O) { K = P.qd; h.rpu = 1; h.space = TD_SP_H; }
+    else if (kind == TD_ST_GU) { K = P.H; h.rpu = 2; h.space = TD_SP_I; }
+    else { K = P.I; h.rpu = 1; h.space = TD_SP_H; }
+  }
+  const int row_bytes = h.fmt == 0 ? K * 2 : K / 2;
+  h.J = (row_bytes + TD_CHUNK - 1) / TD_CHUNK;
+  return h;
 }
 
 DEV int unit_row(const td_kparams& P, int kind, int u, int r) {
@@ -99,12 +122,15 @@ DEV int unit_row(const td_kparams& P, int kind, int u, int r) {
   return u;
 }
 
-DEV void cu_units(int U, int cu, int ncu, int& u0, int& u1) {
-  u0 = (int)(((int64_t)U * cu) / ncu);
-  u1 = (int)(((int64_t)U * (cu + 1)) / ncu);
+DEV void cu_units(const td_kparams& P, int space, int cu, int ncu, int& u0, int& u1) {
+  const int32_t* t = P.part + (size_t)space * (ncu + 1);
+  u0 = t[cu];
+  u1 = t[cu + 1];
 }
 
-// position in one compute wave's chunk sequence over the whole step
+DEV int wave_units(int cnt, int wave) { return cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0; }
+
+// position in one compute wave's chunk sequence over the whole step (weight packing)
 struct Cursor {
   int seq;  // stage sequence number; == n_stages when done
   Gemv g;
@@ -118,9 +144,8 @@ DEV void cur_enter(Cursor& c, const td_kparams& P, int wave, int cu, int ncu, in
     if (kind == TD_ST_ATTN) continue;
     Gemv g = gemv_of(P, kind, layer);
     int u0, u1;
-    cu_units(g.U, cu, ncu, u0, u1);
-    int cnt = u1 - u0;
-    int n = cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0;
+    cu_units(P, g.space, cu, ncu, u0, u1);
+    const int n = wave_units(u1 - u0, wave);
     if (n == 0) continue;
     c.seq = seq;
     c.g = g;
@@ -141,13 +166,56 @@ DEV void cur_next(Cursor& c, const td_kparams& P, int wave, int cu, int ncu) {
   cur_enter(c, P, wave, cu, ncu, c.seq + 1);
 }
 
-// ------------------------------------------------------------ hand-off of activations
-// A value handed to other CUs is a (value bits, tag) pair written with one
-// 8-byte agent-scope store; readers poll the pairs with agent-scope loads until
-// every one carries the tag they expect.  The data is its own ready signal, so
-// a stage waits exactly for the values it reads (no grid-wide barrier), and a
-// buffer is only rewritten after every reader of its previous contents has
-// provably moved on (each stage reads the complete output of the one before).
+// ------------------------------------------------------------ waits
+// LDS control words are read and written with inline assembly: the compiler
+// would otherwise make every such access wait for all of the wave's
+// outstanding LDS DMAs (it cannot tell that the control block and the rings
+// do not overlap), which would drain the weight stream at each hand-off.
+DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+DEV uint32_t lds_ld(const uint32_t* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+DEV void lds_st(uint32_t* p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory"); }
+DEV void lds_add(uint32_t* p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory"); }
+DEV void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+DEV bool wait_expired(const td_kparams& P, uint64_t t0) {
+  if (ld_u(P.sync + TD_SY_ABORT)) return true;
+  if (wall_clock64() - t0 > TD_SPIN_TICKS) {
+    st_u(P.sync + TD_SY_ABORT, 1u);
+    return true;
+  }
+  return false;
+}
+
+// Spins until the LDS word *p reaches at least `target`; returns the value
+// seen (or 0 with ok cleared when the wait timed out or another wait did).
+// (A compiler barrier follows every return, so that no LDS read of the data
+// the word guards is moved above the wait.)
+DEV uint32_t lds_wait_ge(const td_kparams& P, const uint32_t* p, uint32_t target, bool& ok) {
+  uint32_t v = lds_ld(p);
+  if (v < target) {
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t it = 1;; ++it) {
+      __builtin_amdgcn_s_sleep(1);
+      v = lds_ld(p);
+      if (v >= target) break;
+      if ((it & 1023u) == 0u && uni(wait_expired(P, t0) ? 1 : 0)) {
+        ok = false;
+        v = 0;
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  return v;
+}
+
+// ------------------------------------------------------------ cross-CU hand-off
 #define TD_CPOL_SC1 16  // buffer-load cache policy: agent scope
 
 DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -159,23 +227,22 @@ DEV void st_tag(uint2* p, float v, uint32_t tag) {
   asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(w) : "memory");
 }
 
-DEV bool wait_expired(const td_kparams& P, uint64_t t0) {
-  if (ld_u(P.sync + TD_SY_ABORT)) return true;
-  if (wall_clock64() - t0 > TD_SPIN_TICKS) {
-    st_u(P.sync + TD_SY_ABORT, 1u);
-    return true;
-  }
-  return false;
-}
+struct CState;
+DEV void topup(const td_kparams& P, CState& C);
 
-// Waits until the n pairs at src (n even) all carry `tag` and copies their
-// values to dst (LDS).  Each round loads W 16-byte units per lane and re-polls
-// the units still missing.  false: the wait timed out (or another wait did).
+// Waits until the pairs [lo, hi) of src (lo, hi even) all carry `tag` and
+// copies their values to dst[lo, hi) (LDS).  Each round loads up to W 16-byte
+// units (two pairs) per lane and re-polls the units still missing; before each
+// re-poll round the (compute) wave tops up its weight ring, since the round's
+// wait leaves none of its own loads in flight.  false: the wait timed out (or
+// another wait did).
 template <int W>
-DEV bool poll_vec_w(const td_kparams& P, const uint2* src, int n, uint32_t tag, float* dst) {
+DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CState& C) {
   const int lane = lane_id();
-  const int nu = n >> 1;  // 16-byte units of two pairs
-  const __amdgpu_buffer_rsrc_t R = rsrc(src, (uint32_t)nu * 16u);
+  const int nu = (hi - lo) >> 1;
+  if (nu <= 0) return true;
+  const __amdgpu_buffer_rsrc_t R = rsrc(src + lo, (uint32_t)nu * 16u);
+  float* d = dst + lo;
   const uint64_t t0 = wall_clock64();
   for (int b0 = 0; b0 < nu; b0 += W * 64) {
     uint32_t pend = 0;
@@ -183,6 +250,7 @@ DEV bool poll_vec_w(const td_kparams& P, const uint2* src, int n, uint32_t tag, 
     for (int k = 0; k < W; ++k)
       if (b0 + k * 64 + lane < nu) pend |= 1u << k;
     for (uint32_t it = 0;; ++it) {
+      if (it) topup(P, C);
       u32x4 r[W];
 #pragma unroll
       for (int k = 0; k < W; ++k)
@@ -191,8 +259,8 @@ DEV bool poll_vec_w(const td_kparams& P, const uint2* src, int n, uint32_t tag, 
       for (int k = 0; k < W; ++k) {
         if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
           const int u = b0 + k * 64 + lane;
-          dst[2 * u] = __uint_as_float(r[k].x);
-          dst[2 * u + 1] = __uint_as_float(r[k].z);
+          d[2 * u] = __uint_as_float(r[k].x);
+          d[2 * u + 1] = __uint_as_float(r[k].z);
           pend &= ~(1u << k);
         }
       }
@@ -203,15 +271,11 @@ DEV bool poll_vec_w(const td_kparams& P, const uint2* src, int n, uint32_t tag, 
   return true;
 }
 
-DEV bool poll_vec(const td_kparams& P, const uint2* src, int n, uint32_t tag, float* dst) {
-  return poll_vec_w<16>(P, src, n, tag, dst);
-}
-
 // ------------------------------------------------------------ attention task
 // Split-K decode attention: kv head g's positions 0..pos are cut into chunks of
-// chunk_len; one CU per (g, chunk) computes a partial (m, l, acc) for the g's
-// query heads; the CU of chunk 0 merges the partials ("One launch per token",
-// "The attention trap").
+// chunk_len; one CU per (g, chunk) computes a partial (m, l, acc) for each of
+// g's query heads; on the CU of chunk 0 each query-head wave merges its head
+// ("One launch per token", "The attention trap").
 struct AttnTask {
   int valid, g, c, t0, t1, ntiles, n_used;
 };
@@ -227,49 +291,9 @@ DEV AttnTask attn_task(const td_kparams& P, int cu) {
   return t;
 }
 
-// compute waves: wave h < group handles query head g * group + h, one 64-row
-// tile at a time (attn_tile).  Rows past the chunk end are zero in the tile
-// and get p = 0.  Returns the trace stamp taken after the first tile (0
-// without a trace).
-template <int D>
-DEV uint64_t attn_compute_d(const td_kparams& P, uint8_t* lds, int wave, const AttnTask& T) {
-  const int lane = lane_id();
-  const td_attn_lds A = td_attn_layout(D, P.group, P.n_chunks_max);
-  uint8_t* base = lds + P.off_attn;
-  const bool active = wave < P.group;
-  const float* qs = (const float*)(base + A.q) + (active ? wave : 0) * D;
-  const uint16_t* kt = (const uint16_t*)(lds + P.off_tile);
-  const uint16_t* vt = kt + TD_TILE * (D + 8);
-  float* ps = (float*)(base + A.p) + (active ? wave : 0) * TD_TILE;
-  const int ntiles = T.ntiles, t0 = T.t0, t1 = T.t1;
-  uint64_t stamp = 0;
-  float m = -__builtin_inff(), l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int tile = 0; tile < ntiles; ++tile) {
-    wg_bar();  // tile in LDS
-    if (active) {
-      attn_tile<D>(qs, kt, vt, ps, min(TD_TILE, t1 - (t0 + tile * TD_TILE)), m, l, acc);
-      if (P.trace && tile == 0) stamp = wall_clock64();
-    }
-    wg_bar();  // tile consumed
-  }
-  if (active) {
-    acc = attn_finish<D>(acc);
-    float* pr = (float*)(base + A.part) + wave * (D + 4);
-    if (lane < D / 4) *(f32x4*)(pr + 4 * lane) = acc;
-    if (lane == 0) *(f32x4*)(pr + D) = f32x4{m, l, 0.f, 0.f};
-  }
-  return stamp;
-}
-
-DEV uint64_t attn_compute(const td_kparams& P, uint8_t* lds, int wave) {
-  const AttnTask T = attn_task(P, blockIdx.x);
-  if (!T.valid) return 0;
-  return P.d == 64 ? attn_compute_d<64>(P, lds, wave, T) : attn_compute_d<128>(P, lds, wave, T);
-}
-
-// sync wave: K and V rows [tb, tb + nv) of the tile, except row pos (written
-// during this very step; it comes from the published copy), into the LDS tile
+// K and V rows [tb, tb + nv) of the tile, except row pos (written during this
+// very step; it comes from the published copy), into the LDS tile; rows past
+// the chunk end read as zero.
 DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask& T, int tile) {
   const int lane = lane_id();
   const int d = P.d;
@@ -281,21 +305,21 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
   uint16_t* kt = (uint16_t*)(lds + P.off_tile);
   uint16_t* vt = kt + TD_TILE * (d + 8);
   const int q16 = d / 8;  // 16-byte pieces per row
-  const int npiece = TD_TILE * q16;  // the whole tile: rows >= nv read as zero
-  for (int i0 = 0; i0 < npiece; i0 += 8 * 64) {
-    u32x4 kr[8], vr[8];
+  const int npiece = TD_TILE * q16;
+  for (int i0 = 0; i0 < npiece; i0 += 4 * 64) {
+    u32x4 kr[4], vr[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       const uint32_t off = (uint32_t)(i0 + k * 64 + lane) * 16u;  // out of range reads 0
       kr[k] = __builtin_amdgcn_raw_buffer_load_b128(RK, off, 0, 0);
       vr[k] = __builtin_amdgcn_raw_buffer_load_b128(RV, off, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       const int i = i0 + k * 64 + lane;
       if (i < npiece) {
         const int row = i / q16, pc = i - row * q16;
-        if (row >= nv || tb + row != P.pos) {  // row pos comes from the published copy
+        if (row >= nv || tb + row != P.pos) {
           *(u32x4*)(kt + row * (d + 8) + pc * 8) = kr[k];
           *(u32x4*)(vt + row * d + pc * 8) = vr[k];
         }
@@ -304,8 +328,8 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
   }
 }
 
-// writes this position's K and V rows (from LDS, fp32 holding bf16 values)
-// into the tile when the tile holds position pos
+// this position's K and V rows (LDS fp32 holding bf16 values) into the tile
+// when the tile holds position pos
 DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int tile) {
   const int tb = T.t0 + tile * TD_TILE;
   if (P.pos < tb || P.pos >= tb + TD_TILE || P.pos >= T.t1) return;
@@ -321,214 +345,361 @@ DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int
 }
 
 // ------------------------------------------------------------ compute waves
-// A compute wave walks its packed weight stream (one contiguous array per wave,
-// built at create time in exactly the order consumed here): chunk t lands in
-// ring slot t % S, and the DMA of chunk t + S is issued as soon as chunk t has
-// been read out of its slot.  The DMA never waits for a stage boundary, so the
-// next stage's weights stream in while this CU waits at the grid barrier.
-#define TD_DMA_NT 2  // cache policy of the weight stream: non-temporal
+// Each compute wave streams its own packed weight stream (one contiguous array
+// per wave, built at create time in exactly the order consumed here) into its
+// LDS ring of S slots with global_load_lds, keeping at most TD_FLIGHT chunks
+// in flight: a CU serves its memory requests roughly in order, so every byte
+// queued ahead of a hand-off (an epilogue store, an input poll) delays it,
+// while a wave's own streaming rate is its bytes in flight over the load
+// latency; 6 KiB per wave (48 KiB per CU) was the best of 3, 4 and 6 measured
+// on the Llama-3.2-1B shape.  While a wave waits for a stage's inputs it tops
+// the ring up toward its S slots, so the stream keeps going through the
+// hand-offs and the next stage starts from chunks that are already in LDS.  A
+// wave's loads complete in issue order, so "chunk t is in LDS" is "at most the
+// loads issued after chunk t are outstanding"; the chunk loop waits only when
+// the chunk is not already known to have landed.
 #define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
+#define TD_DMA_NT 2   // cache policy of the weight stream: non-temporal
+#ifndef TD_FLIGHT
+#define TD_FLIGHT 6   // chunks of its own stream a compute wave keeps in flight at most
+#endif
 
-template <int S>
-DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
-  const int lane = lane_id();
-  const int cu = blockIdx.x, ncu = gridDim.x;
-  uint8_t* ring = lds + P.off_ring + wave * S * TD_CHUNK;
-  uint8_t* sring = lds + P.off_sring + wave * S * TD_SCHUNK;
-  const float* xin = (const float*)(lds + P.off_xin);
-  float* out = (float*)(lds + P.off_out);
-  const td_wstream& W = P.ws[cu * TD_NW + wave];
-  const uint32_t n_tot = W.n_tot, n4 = W.n4;
-  const uint8_t* fptr = P.wcode + (size_t)W.code_off * TD_CHUNK + lane * 16;
-  const uint8_t* sptr = P.wscale + (size_t)W.scale_off * TD_SCHUNK + lane * 4;
-  uint32_t issued = 0;
-  auto issue = [&](int slot) {
-    __builtin_amdgcn_global_load_lds((const void*)fptr, LDSPTR(ring + slot * TD_CHUNK), 16, 0, TD_DMA_NT);
-    fptr += TD_CHUNK;
-    if (issued < n4) {  // the chunk's 32 fp16 scales: 16 lanes x 4 bytes
-      if (lane < 16)
-        __builtin_amdgcn_global_load_lds((const void*)sptr, LDSPTR(sring + slot * TD_SCHUNK), 4, 0, TD_DMA_NT);
-      sptr += TD_SCHUNK;
-    }
-    ++issued;
-  };
-#pragma unroll
-  for (int t = 0; t < S; ++t)
-    if (issued < n_tot) issue(t);
+struct CState {
+  uint8_t* lds;
+  uint32_t* ctl;
+  float* xin;
+  float* own;
+  float* out;
+  uint8_t* ring;
+  uint8_t* sring;
+  const uint8_t* fbase;  // the next chunk to issue (wave-uniform; a lane loads its 16 bytes)
+  const uint8_t* sbase;  // the next int4 chunk's 64-byte scale block
+  uint32_t issued, n_tot, n4;  // chunks issued, stream length, leading int4 chunks
+  uint32_t lk;                 // chunks [0, lk) are known to be in LDS
+  int islot;                   // ring slot of the next chunk to issue
+  uint32_t t;                  // chunks consumed
+  int slot;                    // ring slot of chunk t
+  uint32_t nrv;                // rendezvous passed
+  bool ok;
+  int ranges;                  // lane 2 s: this CU's first unit of unit space s; lane 2 s + 1: its count
+  DEV int unit_lo(int sp) const { return __builtin_amdgcn_readlane(ranges, 2 * sp); }
+  DEV int unit_n(int sp) const { return __builtin_amdgcn_readlane(ranges, 2 * sp + 1); }
+};
 
-  uint32_t t = 0;  // chunks consumed
-  int slot = 0;
-  wg_bar();  // stage 0 inputs staged
-  for (int seq = 0; seq < P.n_stages; ++seq) {
-    if (seq) wg_bar();  // stage seq inputs staged
-    int kind, layer;
-    stage_of(P, seq, kind, layer);
-    uint64_t w0 = 0, w1 = 0;
-    if (P.trace) w0 = wall_clock64();
-    if (kind == TD_ST_ATTN) {
-      w1 = attn_compute(P, lds, wave);
-    } else {
-      const Gemv g = gemv_of(P, kind, layer);
-      int u0, u1;
-      cu_units(g.U, cu, ncu, u0, u1);
-      const int cnt = u1 - u0;
-      const int n = cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0;
-      const int nrows = n * g.rpu;
-      for (int row = 0; row < nrows; ++row) {
-        float acc = 0.f;
-        for (int j = 0; j < g.J; ++j) {
-          // chunk t is complete once at most the ops issued after it are pending
-          const uint32_t after = issued - 1u - t;
-          if (after >= (uint32_t)(S - 1)) {
-            if (t < n4 && issued - 1u < n4) vmcnt_wait<2 * S - 2>();
-            else vmcnt_wait<S - 1>();
-          } else {
-            vmcnt_wait<0>();
-          }
-          if (P.trace && row == 0 && j == 0) w1 = wall_clock64();
-          const u32x4 w = *(const u32x4*)(ring + slot * TD_CHUNK + lane * 16);
-          if (g.fmt == 0) {
-            acc += dot_bf16(w, xin + j * 512 + lane * 8);
-          } else {
-            const float sc = f16f(*(const uint16_t*)(sring + slot * TD_SCHUNK + (lane >> 1) * 2));
-            acc += dot_int4(w, xin + j * 2048 + lane * 32, sc);
-          }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot read out: refill it
-          if (issued < n_tot) issue(slot);
-          slot = slot + 1 == S ? 0 : slot + 1;
-          ++t;
-        }
-        const float r = wave_sum(acc);
-        const int k = g.rpu == 2 ? row >> 1 : row, rr = g.rpu == 2 ? row & 1 : 0;
-        if (lane == 0) out[(wave + k * TD_NW) * g.rpu + rr] = r;
-      }
-    }
-    if (P.trace) {
-      uint64_t* wt = (uint64_t*)(lds + P.off_wtrace) + wave * 4;
-      const uint64_t w2 = wall_clock64();
-      if (lane == 0) {
-        wt[0] = w0;
-        wt[1] = w1;
-        wt[2] = (w1 || kind == TD_ST_ATTN) ? w2 : 0;
-      }
-    }
-    wg_bar();  // stage seq outputs in LDS
+// loads of chunks [a, b): an int4 chunk is two (its codes and its scales)
+DEV uint32_t ops_of(const CState& C, uint32_t a, uint32_t b) {
+  const uint32_t hi4 = min(b, C.n4);
+  return (b - a) + (hi4 > a ? hi4 - a : 0u);
+}
+// s_waitcnt vmcnt(n) for a run-time n < 2 TD_FLIGHT (larger values wait for
+// everything, which is only more conservative)
+DEV void vmcnt_rt(uint32_t n) {
+  switch (n) {
+    case 1: vmcnt_wait<1>(); break;
+    case 2: vmcnt_wait<2>(); break;
+    case 3: vmcnt_wait<3>(); break;
+    case 4: vmcnt_wait<4>(); break;
+    case 5: vmcnt_wait<5>(); break;
+    case 6: vmcnt_wait<6>(); break;
+    case 7: vmcnt_wait<7>(); break;
+    case 8: vmcnt_wait<8>(); break;
+    case 9: vmcnt_wait<9>(); break;
+    case 10: vmcnt_wait<10>(); break;
+    default: vmcnt_wait<0>(); break;
   }
 }
-
-// ------------------------------------------------------------ sync wave
-// zero LDS floats [from, to): the tail of the last chunk of a GEMV input
-DEV void zero_tail(float* x, int from, int to) {
-  for (int i = from + lane_id(); i < to; i += 64) x[i] = 0.f;
+static_assert(TD_FLIGHT >= 1 && 2 * TD_FLIGHT - 2 <= 10, "vmcnt_rt covers the waits of at most TD_FLIGHT chunks");
+// Waits until no load older than chunk a is outstanding (chunks [a, issued)
+// may still be in flight; issued - a < TD_FLIGHT).  The steady-state case, the
+// newest TD_FLIGHT - 1 chunks all of one format, is one compile-time wait.
+DEV void wait_older_than(const CState& C, uint32_t a) {
+  const uint32_t m = C.issued - a;
+  if (m == TD_FLIGHT - 1 && a >= C.n4) vmcnt_wait<TD_FLIGHT - 1>();
+  else if (m == TD_FLIGHT - 1 && C.issued <= C.n4) vmcnt_wait<2 * TD_FLIGHT - 2>();
+  else vmcnt_rt(ops_of(C, a, C.issued));
 }
 
-DEV int chunk_elems(int fmt) { return fmt ? 2048 : 512; }
-
-// RMSNorm of the residual stream into LDS: xin = x / sqrt(mean(x^2) + eps) * gain.
-// The source is the published residual (tagged), or the bf16 embedding row; the
-// bf16 gains were DMA'd into LDS when the previous stage ended.
-DEV bool norm_input(const td_kparams& P, uint8_t* lds, const uint2* xsrc, uint32_t tag, const uint16_t* esrc,
-                    int fmt) {
+DEV void issue_chunk(const td_kparams& P, CState& C) {
   const int lane = lane_id();
-  float* xin = (float*)(lds + P.off_xin);
-  const uint16_t* gain = (const uint16_t*)(lds + P.off_gain);
-  const int H = P.H;  // multiple of 256
-  bool ok = true;
-  if (esrc) {
-    for (int i = lane * 4; i < H; i += 256) {
-      uint2 e = *(const uint2*)(esrc + i);
-      f32x4 v = {bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
-      *(f32x4*)(xin + i) = v;
+  __builtin_amdgcn_global_load_lds((const void*)(C.fbase + lane * 16), LDSPTR(C.ring + C.islot * TD_CHUNK), 16, 0,
+                                   TD_DMA_NT);
+  C.fbase += TD_CHUNK;
+  if (C.issued < C.n4) {  // the chunk's 32 fp16 scales: 16 lanes x 4 bytes
+    if (lane < 16)
+      __builtin_amdgcn_global_load_lds((const void*)(C.sbase + lane * 4), LDSPTR(C.sring + C.islot * TD_SCHUNK), 4,
+                                       0, TD_DMA_NT);
+    C.sbase += TD_SCHUNK;
+  }
+  ++C.issued;
+  C.islot = C.islot + 1 == P.ring_slots ? 0 : C.islot + 1;
+}
+DEV bool ring_room(const td_kparams& P, const CState& C) {
+  return C.issued < C.n_tot && C.issued < C.t + (uint32_t)P.ring_slots;
+}
+// After a chunk is consumed: one more chunk in flight if its slot is free, first
+// waiting (only if needed) until at most TD_FLIGHT - 1 chunks are outstanding.
+DEV void refill(const td_kparams& P, CState& C) {
+  if (!ring_room(P, C)) return;
+  if (C.issued - C.lk >= TD_FLIGHT) {
+    wait_older_than(C, C.issued - (TD_FLIGHT - 1));
+    C.lk = C.issued - (TD_FLIGHT - 1);
+  }
+  issue_chunk(P, C);
+}
+// During a wait, with none of the wave's loads outstanding (all issued chunks
+// are in LDS): up to TD_FLIGHT more chunks.
+DEV void topup(const td_kparams& P, CState& C) {
+  C.lk = C.issued;
+#pragma unroll 1
+  for (int k = 0; k < TD_FLIGHT && ring_room(P, C); ++k) issue_chunk(P, C);
+}
+// The next chunk of the stream, once it is in LDS.
+DEV const uint8_t* chunk_wait(CState& C) {
+  if (C.t >= C.lk) {
+    wait_older_than(C, C.t + 1);
+    C.lk = C.t + 1;
+  }
+  return C.ring + C.slot * TD_CHUNK;
+}
+DEV void chunk_release(const td_kparams& P, CState& C) {
+  lds_fence();  // the slot has been read out
+  ++C.t;
+  C.slot = C.slot + 1 == P.ring_slots ? 0 : C.slot + 1;
+  refill(P, C);
+}
+
+DEV void rendezvous(const td_kparams& P, CState& C) {
+  ++C.nrv;
+  lds_fence();
+  if (lane_id() == 0) lds_add(C.ctl + TD_CTL_RV, 1u);
+  (void)lds_wait_ge(P, C.ctl + TD_CTL_RV, TD_NW * C.nrv, C.ok);
+}
+
+// One row of the current stage: J chunks of the stream against xin.
+DEV float gemv_row(const td_kparams& P, CState& C, const Shape& g, uint64_t& first) {
+  const int lane = lane_id();
+  float acc = 0.f;
+  for (int j = 0; j < g.J; ++j) {
+    const uint8_t* ch = chunk_wait(C);
+    if (P.trace && !first) first = wall_clock64();
+    const u32x4 w = *(const u32x4*)(ch + lane * 16);
+    if (g.fmt == 0) {
+      acc += dot_bf16(w, C.xin + j * 512 + lane * 8);
+    } else {
+      const float sc = f16f(*(const uint16_t*)(C.sring + C.slot * TD_SCHUNK + (lane >> 1) * 2));
+      acc += dot_int4(w, C.xin + j * 2048 + lane * 32, sc);
+    }
+    chunk_release(P, C);
+  }
+  return wave_sum(acc);
+}
+
+// Input slice of a GEMV stage into xin: the published vector (polled), or the
+// bf16 embedding row for the first layer.  With gains (the RMSNorm stages) the
+// slice's sum of squares goes to the control block and the slice is multiplied
+// by the gains.  The last wave zeroes the tail up to the chunk multiple.
+DEV void stage_gemv_input(const td_kparams& P, CState& C, int wave, int kind, int K, const uint2* src,
+                          const uint16_t* erow, uint32_t tag, uint32_t g0, uint32_t g1, uint32_t g2, uint32_t g3,
+                          const uint16_t* gain) {
+  int lo, hi;
+  td_slice(K, wave, &lo, &hi);
+  if (erow) {
+    for (int u = (lo >> 1) + lane_id(); u < (hi >> 1); u += 64) {
+      const uint32_t e = *(const uint32_t*)(erow + 2 * u);
+      C.xin[2 * u] = bf_lo(e);
+      C.xin[2 * u + 1] = bf_hi(e);
     }
   } else {
-    ok = poll_vec(P, xsrc, H, tag, xin);
+    C.ok &= poll_pairs<8>(P, src, lo, hi, tag, C.xin, C);
   }
-  vm_drain();  // the gains' DMA into LDS
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  float ss = 0.f;
-  for (int i = lane * 4; i < H; i += 256) {
-    f32x4 v = *(const f32x4*)(xin + i);
-    ss = fmaf(v.x, v.x, ss);
-    ss = fmaf(v.y, v.y, ss);
-    ss = fmaf(v.z, v.z, ss);
-    ss = fmaf(v.w, v.w, ss);
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)H + P.eps);
-  for (int i = lane * 4; i < H; i += 256) {
-    f32x4 v = *(const f32x4*)(xin + i);
-    uint2 g = *(const uint2*)(gain + i);
-    v.x = v.x * inv * bf_lo(g.x);
-    v.y = v.y * inv * bf_hi(g.x);
-    v.z = v.z * inv * bf_lo(g.y);
-    v.w = v.w * inv * bf_hi(g.y);
-    *(f32x4*)(xin + i) = v;
-  }
-  const int ce = chunk_elems(fmt);
-  zero_tail(xin, H, (H + ce - 1) / ce * ce);
-  return ok;
-}
-
-// Issued as soon as a stage's epilogue is out: the DMA of the next stage's
-// bf16 norm gains into LDS, and the QKV bias of this CU's units.
-DEV void preload(const td_kparams& P, uint8_t* lds, int kind, int layer, float& ba, float& bb) {
-  const int lane = lane_id();
-  const uint16_t* g = kind == TD_ST_QKV ? P.layers[layer].attn_norm
-                    : kind == TD_ST_GU ? P.layers[layer].mlp_norm
-                    : kind == TD_ST_HEAD ? P.final_norm : nullptr;
-  if (g) {
-    const int bytes = P.H * 2;
-    for (int off = 0; off < bytes; off += TD_CHUNK)
-      if (off + lane * 16 < bytes)
-        __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)g + off + lane * 16),
-                                         LDSPTR(lds + P.off_gain + off), 16, 0, 0);
-  }
-  if (kind == TD_ST_QKV && P.has_bias) {
-    int u0, u1;
-    cu_units(P.qkv_rows / 2, blockIdx.x, gridDim.x, u0, u1);
-    if (lane < u1 - u0) {
-      const int ra = unit_row(P, TD_ST_QKV, u0 + lane, 0);
-      ba = bf16f(P.layers[layer].bias[ra]);
-      bb = bf16f(P.layers[layer].bias[ra + (P.d >> 1)]);
+  if (gain) {
+    lds_fence();
+    const float ss = slice_ssq(C.xin, lo, hi);
+    if (lane_id() == 0) ((float*)C.ctl)[TD_CTL_SSQ + wave] = ss;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // the gains fetched ahead of the rendezvous
+      const int u = (lo >> 1) + lane_id() + 64 * k;
+      const uint32_t g = k == 0 ? g0 : k == 1 ? g1 : k == 2 ? g2 : g3;
+      if (u < (hi >> 1)) {
+        C.xin[2 * u] *= bf_lo(g);
+        C.xin[2 * u + 1] *= bf_hi(g);
+      }
+    }
+    for (int u = (lo >> 1) + lane_id() + 256; u < (hi >> 1); u += 64) {
+      const uint32_t g = *(const uint32_t*)(gain + 2 * u);
+      C.xin[2 * u] *= bf_lo(g);
+      C.xin[2 * u + 1] *= bf_hi(g);
     }
   }
+  if (wave == TD_NW - 1) {
+    const int ce = P.wf && kind != TD_ST_HEAD ? 2048 : 512;
+    const int kp = (K + ce - 1) / ce * ce;
+    for (int i = K + lane_id(); i < kp; i += 64) C.xin[i] = 0.f;
+  }
 }
 
-// The chunk-0 CU of kv head g: combine every chunk's partial,
-// o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M), and publish o.  The
-// weights w[h][c] go to LDS first; then lane i owns 4 consecutive outputs
-// (head i / (D/4)) and sums over the chunks in chunk order.
-template <int D>
-DEV void attn_merge_d(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint32_t tag) {
+// The GEMV part of a stage for one compute wave: the rows of its units (their
+// dot products to the LDS output area), then the units' epilogues, one unit per
+// lane, with every store of the stage issued after its last row: a store
+// counts among the wave's outstanding loads, so a store issued between rows
+// would make every following chunk wait for it.
+DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer, uint32_t tag, float inv,
+                   float bias_a, float bias_b, uint64_t& first) {
   const int lane = lane_id();
-  const int G = P.group, n = T.n_used;
-  constexpr int st = D + 4;
-  const td_attn_lds A = td_attn_layout(D, G, P.n_chunks_max);
-  const float* own = (const float*)(lds + P.off_attn + A.part);
-  const float* mb = (const float*)(lds + P.off_attn + A.merge);
-  float* wl = (float*)(lds + P.off_attn + A.p);  // [G][64]: free once the tiles are consumed
-  for (int h = 0; h < G; ++h) {
-    const bool have = lane < n;  // n <= 64
-    const float* pc = lane == 0 ? own + h * st : mb + ((have ? lane - 1 : 0) * G + h) * st;
-    const float m = have ? pc[D] : -__builtin_inff();
-    const float l = have ? pc[D + 1] : 0.f;
-    const float M = wave_max(m);
-    const float w0 = have ? __expf(m - M) : 0.f;
-    wl[h * 64 + lane] = w0 / wave_sum(l * w0);
+  const Shape g = shape_of(P, kind);
+  const int u0 = C.unit_lo(g.space), u1 = C.unit_lo(g.space) + C.unit_n(g.space);
+  const int n = wave_units(u1 - u0, wave);
+  for (int k = 0; k < n; ++k) {
+    const int idx = wave + k * TD_NW;  // u - u0
+    const float r0 = gemv_row(P, C, g, first);
+    const float r1 = g.rpu == 2 ? gemv_row(P, C, g, first) : 0.f;
+    if (lane == 0) {
+      C.out[idx * g.rpu] = r0;
+      if (g.rpu == 2) C.out[idx * 2 + 1] = r1;
+    }
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  for (int i = lane; i < G * (D / 4); i += 64) {
-    const int h = i / (D / 4), e = 4 * (i - h * (D / 4));
-    const float w00 = wl[h * 64];
-    f32x4 o = *(const f32x4*)(own + h * st + e);
-    o.x *= w00; o.y *= w00; o.z *= w00; o.w *= w00;
+  lds_fence();
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff, bad = 0;
+  for (int k = lane; k < n; k += 64) {
+    const int idx = wave + k * TD_NW;
+    const int u = u0 + idx;
+    if (kind == TD_ST_QKV) {
+      const int half = P.d >> 1;
+      const int ra = unit_row(P, TD_ST_QKV, u, 0);
+      const int i = ra % P.d;
+      float a = C.out[2 * idx] * inv, b = C.out[2 * idx + 1] * inv;
+      if (P.has_bias) {  // lane k fetched unit k's biases
+        a += bias_a;
+        b += bias_b;
+      }
+      if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
+        const float* cs = (const float*)(C.lds + P.off_rope);
+        const float c = cs[2 * i], sn = cs[2 * i + 1];
+        const float a2 = a * c - b * sn;
+        const float b2 = b * c + a * sn;
+        a = a2;
+        b = b2;
+      }
+      const int gw = (P.group + 2) * P.d;  // published block of one kv head
+      if (ra < P.qd) {
+        const int h = ra / P.d, gg = h / P.group;
+        uint2* pub = P.tq + (size_t)gg * gw + (h - gg * P.group) * P.d;
+        st_tag(pub + i, a, tag);
+        st_tag(pub + i + half, b, tag);
+      } else {
+        const bool isk = ra < P.qd + P.kvd;
+        const int gg = (ra - P.qd - (isk ? 0 : P.kvd)) / P.d;
+        const uint32_t ab = f2bf(a), bbits = f2bf(b);
+        uint16_t* row = (isk ? P.kc : P.vc) + (((size_t)layer * P.nkv + gg) * P.max_ctx + P.pos) * P.d;
+        row[i] = (uint16_t)ab;
+        row[i + half] = (uint16_t)bbits;
+        uint2* pub = P.tq + (size_t)gg * gw + (P.group + (isk ? 0 : 1)) * P.d;
+        st_tag(pub + i, __uint_as_float(ab << 16), tag);
+        st_tag(pub + i + half, __uint_as_float(bbits << 16), tag);
+      }
+    } else if (kind == TD_ST_O || kind == TD_ST_DOWN) {
+      const float v = C.own[idx] + C.out[idx];
+      C.own[idx] = v;
+      st_tag((kind == TD_ST_O ? P.tx_mid : P.tx_out) + u, v, tag);
+    } else if (kind == TD_ST_GU) {
+      const float gt = C.out[2 * idx] * inv, up = C.out[2 * idx + 1] * inv;
+      st_tag(P.tact + u, gt / (1.0f + expf(-gt)) * up, tag);
+    } else {  // HEAD
+      const float v = C.out[idx] * inv;
+      P.logits[u] = v;
+      if (!isfinite(v)) bad = 1;
+      else if (v > bv || (v == bv && u < bi)) { bv = v; bi = u; }
+    }
+  }
+  if (kind == TD_ST_HEAD) {
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    bad = __any(bad);
+    if (lane == 0) {
+      uint32_t* cd = C.ctl + TD_CTL_CAND + 4 * wave;
+      lds_st(cd + 0, __float_as_uint(bv));
+      lds_st(cd + 1, (uint32_t)bi);
+      lds_st(cd + 2, (uint32_t)bad);
+    }
+    lds_fence();
+    if (lane == 0) lds_add(C.ctl + TD_CTL_HEADDONE, 1u);
+  }
+}
+
+// Query-head wave h of an attention task: the tiles the sync wave makes ready,
+// then either its partial (chunk c > 0) or, on the chunk-0 CU, the merge of all
+// chunks' partials of its head, o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
+// (the chunks summed in chunk order), published.
+template <int D>
+DEV void attn_wave_d(const td_kparams& P, CState& C, uint8_t* lds, int h, const AttnTask& T, uint32_t tag,
+                     uint32_t& tiles_seen, uint64_t& first) {
+  const int lane = lane_id();
+  const int G = P.group;
+  const td_attn_lds A = td_attn_layout(D, G, P.n_chunks_max);
+  uint8_t* base = lds + P.off_attn;
+  const float* qs = (const float*)(base + A.q) + h * D;
+  const uint16_t* kt = (const uint16_t*)(lds + P.off_tile);
+  const uint16_t* vt = kt + TD_TILE * (D + 8);
+  float* ps = (float*)(base + A.p) + h * TD_TILE;
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int tile = 0; tile < T.ntiles; ++tile) {
+    (void)lds_wait_ge(P, C.ctl + TD_CTL_TREADY, ++tiles_seen, C.ok);
+    attn_tile<D>(qs, kt, vt, ps, min(TD_TILE, T.t1 - (T.t0 + tile * TD_TILE)), m, l, acc);
+    lds_fence();
+    if (lane == 0) lds_add(C.ctl + TD_CTL_TDONE, 1u);
+    if (P.trace && !first) first = wall_clock64();
+  }
+  acc = attn_finish<D>(acc);
+  constexpr int st = D + 4;
+  uint2* myparts = P.tpart + ((size_t)T.g * G + h) * P.n_chunks_max * st;
+  if (T.c > 0) {
+    uint2* dst = myparts + (size_t)T.c * st;
+    if (lane < D / 4) {
+      st_tag(dst + 4 * lane + 0, acc.x, tag);
+      st_tag(dst + 4 * lane + 1, acc.y, tag);
+      st_tag(dst + 4 * lane + 2, acc.z, tag);
+      st_tag(dst + 4 * lane + 3, acc.w, tag);
+    }
+    if (lane == 0) {
+      st_tag(dst + D, m, tag);
+      st_tag(dst + D + 1, l, tag);
+      st_tag(dst + D + 2, 0.f, tag);
+      st_tag(dst + D + 3, 0.f, tag);
+    }
+    return;
+  }
+  const int n = T.n_used;  // <= 64
+  float* mb = (float*)(base + A.merge) + (size_t)h * (P.n_chunks_max - 1) * st;  // chunks 1..n-1
+  if (n > 1) C.ok &= poll_pairs<8>(P, myparts + st, 0, (n - 1) * st, tag, mb, C);
+  lds_fence();
+  const bool have = lane < n;
+  const float* pc = mb + (have && lane > 0 ? lane - 1 : 0) * st;
+  const float mc = lane == 0 ? m : have ? pc[D] : -__builtin_inff();
+  const float lc = lane == 0 ? l : have ? pc[D + 1] : 0.f;
+  const float M = wave_max(mc);
+  const float w0 = have ? __expf(mc - M) : 0.f;
+  ps[lane] = w0 / wave_sum(lc * w0);  // the weights leave the lanes before the loop below
+  lds_fence();
+  if (lane < D / 4) {
+    const int e = 4 * lane;
+    const float wc0 = ps[0];
+    f32x4 o;
+    o.x = acc.x * wc0;
+    o.y = acc.y * wc0;
+    o.z = acc.z * wc0;
+    o.w = acc.w * wc0;
     for (int c = 1; c < n; ++c) {
-      const f32x4 v = *(const f32x4*)(mb + ((c - 1) * G + h) * st + e);
-      const float w = wl[h * 64 + c];
-      o.x = fmaf(w, v.x, o.x);
-      o.y = fmaf(w, v.y, o.y);
-      o.z = fmaf(w, v.z, o.z);
-      o.w = fmaf(w, v.w, o.w);
+      const float wc = ps[c];
+      const f32x4 v = *(const f32x4*)(mb + (c - 1) * st + e);
+      o.x = fmaf(wc, v.x, o.x);
+      o.y = fmaf(wc, v.y, o.y);
+      o.z = fmaf(wc, v.z, o.z);
+      o.w = fmaf(wc, v.w, o.w);
     }
     uint2* dst = P.to + ((size_t)T.g * G + h) * D + e;
     st_tag(dst + 0, o.x, tag);
@@ -538,245 +709,241 @@ DEV void attn_merge_d(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint
   }
 }
 
-DEV bool attn_merge(const td_kparams& P, uint8_t* lds, const AttnTask& T, uint32_t tag) {
-  const int d = P.d, G = P.group, st = d + 4;
-  const td_attn_lds A = td_attn_layout(d, G, P.n_chunks_max);
-  float* mb = (float*)(lds + P.off_attn + A.merge);
-  bool ok = true;
-  if (T.n_used > 1)
-    ok = poll_vec(P, P.tpart + ((size_t)T.g * P.n_chunks_max + 1) * G * st, (T.n_used - 1) * G * st, tag, mb);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (P.trace && lane_id() == 0) ((uint64_t*)(lds + P.off_wtrace))[TD_NW * 4] = wall_clock64();
-  if (d == 64) attn_merge_d<64>(P, lds, T, tag);
-  else attn_merge_d<128>(P, lds, T, tag);
-  return ok;
+DEV void trace_rec(const td_kparams& P, int wave, int seq, uint64_t t0, uint64_t t1, uint64_t t2, uint64_t t3) {
+  uint64_t* rec = P.trace + ((size_t)blockIdx.x * P.n_stages + seq) * TD_TRACE_STAMPS + 4 * wave;
+  const int lane = lane_id();
+  const uint64_t v = lane == 0 ? t0 : lane == 1 ? t1 : lane == 2 ? t2 : t3;
+  if (lane < 4) rec[lane] = v;
 }
 
-// stage outputs -> epilogue -> published values (tag: this stage's)
-DEV bool sync_epilogue(const td_kparams& P, uint8_t* lds, int kind, int layer, uint32_t tag, uint32_t epoch,
-                       const AttnTask& T, float ba, float bb) {
+template <int D>
+DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
-  const float* out = (const float*)(lds + P.off_out);
-  float* own = (float*)(lds + P.off_own);
-  bool ok = true;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (kind == TD_ST_QKV) {
-    int u0, u1;
-    cu_units(P.qkv_rows / 2, cu, ncu, u0, u1);
-    const int half = P.d >> 1;
-    const float* cs = (const float*)(lds + P.off_rope);
-    if (lane < u1 - u0) {  // at most 64 units per CU (checked at create)
-      const int u = u0 + lane;
-      const int ra = unit_row(P, TD_ST_QKV, u, 0), rb = ra + half;
-      float a = out[2 * lane], b = out[2 * lane + 1];
-      if (P.has_bias) {
-        a += ba;
-        b += bb;
-      }
-      const int i = ra % P.d;  // < d/2
-      if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
-        const float c = cs[2 * i], sn = cs[2 * i + 1];
-        const float a2 = a * c - b * sn;
-        const float b2 = b * c + a * sn;
-        a = a2;
-        b = b2;
-      }
-      const int gw = (P.group + 2) * P.d;  // published block of one kv head
-      if (ra < P.qd) {
-        const int h = ra / P.d, g = h / P.group;
-        uint2* pub = P.tq + (size_t)g * gw + (h - g * P.group) * P.d;
-        st_tag(pub + i, a, tag);
-        st_tag(pub + i + half, b, tag);
-      } else {
-        const bool isk = ra < P.qd + P.kvd;
-        const int g = (ra - P.qd - (isk ? 0 : P.kvd)) / P.d;
-        const uint32_t ab = f2bf(a), bbits = f2bf(b);
-        uint16_t* row = (isk ? P.kc : P.vc) + (((size_t)layer * P.nkv + g) * P.max_ctx + P.pos) * P.d;
-        row[i] = (uint16_t)ab;
-        row[i + half] = (uint16_t)bbits;
-        uint2* pub = P.tq + (size_t)g * gw + (P.group + (isk ? 0 : 1)) * P.d;
-        st_tag(pub + i, __uint_as_float(ab << 16), tag);
-        st_tag(pub + i + half, __uint_as_float(bbits << 16), tag);
-      }
-    }
-  } else if (kind == TD_ST_O || kind == TD_ST_DOWN) {
-    int r0, r1;
-    cu_units(P.H, cu, ncu, r0, r1);
-    uint2* dst = kind == TD_ST_O ? P.tx_mid : P.tx_out;
-    for (int k = lane; k < r1 - r0; k += 64) {
-      const float v = own[k] + out[k];
-      own[k] = v;
-      st_tag(dst + r0 + k, v, tag);
-    }
-  } else if (kind == TD_ST_GU) {
-    int u0, u1;
-    cu_units(P.I, cu, ncu, u0, u1);
-    for (int k = lane; k < u1 - u0; k += 64) {
-      const float gt = out[2 * k], up = out[2 * k + 1];
-      st_tag(P.tact + u0 + k, gt / (1.0f + expf(-gt)) * up, tag);
-    }
-  } else if (kind == TD_ST_ATTN) {
-    if (T.valid) {
-      if (T.c == 0) {
-        ok = attn_merge(P, lds, T, tag);
-      } else {
-        const int st = P.d + 4;
-        const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
-        const float* pr = (const float*)(lds + P.off_attn + A.part);
-        uint2* gp = P.tpart + ((size_t)T.g * P.n_chunks_max + T.c) * P.group * st;
-        for (int i = lane; i < P.group * st; i += 64) st_tag(gp + i, pr[i], tag);
-      }
-    }
-  } else {  // HEAD: logits, per-CU candidate, last arriver picks the token
-    int u0, u1;
-    cu_units(P.V, cu, ncu, u0, u1);
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
-    int bad = 0;
-    for (int k = lane; k < u1 - u0; k += 64) {
-      const float v = out[k];
-      P.logits[u0 + k] = v;
-      if (!isfinite(v)) bad = 1;
-      else if (v > bv) { bv = v; bi = u0 + k; }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    bad = __any(bad);
-    if (lane == 0) {
-      st_u(P.cand + cu * 4 + 0, __float_as_uint(bv));
-      st_u(P.cand + cu * 4 + 1, (uint32_t)bi);
-      st_u(P.cand + cu * 4 + 2, (uint32_t)bad);
-    }
-    vm_drain();
-    int last = 0;
-    if (lane == 0) last = atomicAdd(P.sync + TD_SY_FINAL, 1u) + 1u == (uint32_t)ncu;
-    if (uni(last)) {
-      float fv = -__builtin_inff();
-      int fi = 0x7fffffff, fbad = 0;
-      for (int c = lane; c < ncu; c += 64) {
-        const float v = __uint_as_float(ld_u(P.cand + c * 4 + 0));
-        const int i = (int)ld_u(P.cand + c * 4 + 1);
-        fbad |= (int)ld_u(P.cand + c * 4 + 2);
-        if (v > fv || (v == fv && i < fi)) { fv = v; fi = i; }
-      }
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(fv, off);
-        const int oi = __shfl_xor(fi, off);
-        if (ov > fv || (ov == fv && oi < fi)) { fv = ov; fi = oi; }
-      }
-      fbad = __any(fbad);
-      if (lane == 0) {
-        *P.token_out = fi == 0x7fffffff ? 0 : fi;
-        if (fbad) atomicOr(P.err, TD_ERRBIT_NONFINITE);
-        st_u(P.sync + TD_SY_FINAL, 0u);
-        st_u(P.sync + TD_SY_EPOCH, epoch + 1u);
-      }
+  CState C;
+  C.lds = lds;
+  C.ctl = (uint32_t*)(lds + P.off_ctl);
+  C.xin = (float*)(lds + P.off_xin);
+  C.own = (float*)(lds + P.off_own);
+  C.out = (float*)(lds + P.off_out);
+  C.ring = lds + P.off_ring + wave * P.ring_slots * TD_CHUNK;
+  C.sring = lds + P.off_sring + wave * P.ring_slots * TD_SCHUNK;
+  {
+    const td_wstream W = P.ws[cu * TD_NW + wave];
+    C.fbase = P.wcode + (size_t)W.code_off * TD_CHUNK;
+    C.sbase = P.wscale + (size_t)W.scale_off * TD_SCHUNK;
+    C.n_tot = W.n_tot;
+    C.n4 = W.n4;
+  }
+  C.issued = C.t = C.lk = 0;
+  C.islot = C.slot = 0;
+  C.nrv = 0;
+  C.ok = true;
+  topup(P, C);  // the stream starts right away
+  {
+    C.ranges = 0;
+    if (lane < 2 * TD_NSPACES) {
+      const int32_t* t = P.part + (size_t)(lane >> 1) * (ncu + 1) + cu;
+      C.ranges = (lane & 1) ? t[1] - t[0] : t[0];
     }
   }
-  return ok;
+  const uint32_t epoch = uni(ld_u(P.sync + TD_SY_EPOCH));
+  const uint32_t tag0 = epoch * (uint32_t)P.n_stages;  // stage seq publishes tag0 + seq + 1
+  if (ld_u(P.sync + TD_SY_ABORT)) C.ok = false;
+  int tok = uni(*P.token_in);
+  if (tok < 0 || tok >= P.V) tok = 0;  // the sync wave reports the range error
+  const uint16_t* erow = P.embed + (size_t)tok * P.H;
+  {  // this wave's residual rows start as the embedding row; wave 0 stages the RoPE row of pos
+    const int r0 = C.unit_lo(TD_SP_H), r1 = r0 + C.unit_n(TD_SP_H);
+    for (int r = r0 + wave + lane * TD_NW; r < r1; r += 64 * TD_NW) C.own[r - r0] = bf16f(erow[r]);
+    if (wave == 0) {
+      float* cs = (float*)(lds + P.off_rope);
+      for (int i = lane; i < P.d; i += 64) cs[i] = P.rope_cs[(size_t)P.pos * P.d + i];
+    }
+  }
+  const AttnTask T = attn_task(P, cu);
+  uint32_t tiles_seen = 0;
+  bool first_stage = true;
+  for (int seq = 0; seq < P.n_stages; ++seq) {
+    int kind, layer;
+    stage_of(P, seq, kind, layer);
+    if (kind == TD_ST_ATTN && !T.valid) continue;
+    const uint32_t tag_in = tag0 + (uint32_t)seq, tag = tag_in + 1u;
+    uint64_t ts0 = 0, ts1 = 0, ts2 = 0;
+    if (P.trace) ts0 = wall_clock64();
+    // operands fetched ahead of the rendezvous: this slice's gains, this wave's QKV biases
+    const uint16_t* gain = kind == TD_ST_QKV ? P.gains + (size_t)(2 * layer) * P.H
+                         : kind == TD_ST_GU ? P.gains + (size_t)(2 * layer + 1) * P.H
+                         : kind == TD_ST_HEAD ? P.gains + (size_t)(2 * P.L) * P.H : nullptr;
+    uint32_t g0 = 0u, g1 = 0u, g2 = 0u, g3 = 0u;
+    if (gain) {
+      int lo, hi;
+      td_slice(P.H, wave, &lo, &hi);
+      const int u = (lo >> 1) + lane;
+      if (u < (hi >> 1)) g0 = *(const uint32_t*)(gain + 2 * u);
+      if (u + 64 < (hi >> 1)) g1 = *(const uint32_t*)(gain + 2 * (u + 64));
+      if (u + 128 < (hi >> 1)) g2 = *(const uint32_t*)(gain + 2 * (u + 128));
+      if (u + 192 < (hi >> 1)) g3 = *(const uint32_t*)(gain + 2 * (u + 192));
+    }
+    float bias_a = 0.f, bias_b = 0.f;
+    if (kind == TD_ST_QKV && P.has_bias) {
+      const int u0 = C.unit_lo(TD_SP_QKV);
+      if (lane < wave_units(C.unit_n(TD_SP_QKV), wave)) {
+        const uint16_t* bl = P.biases + (size_t)layer * P.qkv_rows;
+        const int ra = unit_row(P, TD_ST_QKV, u0 + wave + lane * TD_NW, 0);
+        bias_a = bf16f(bl[ra]);
+        bias_b = bf16f(bl[ra + (P.d >> 1)]);
+      }
+    }
+    if (!first_stage) rendezvous(P, C);  // every wave is done reading the previous stage's inputs
+    first_stage = false;
+    if (kind == TD_ST_ATTN) {
+      // the kv head's block: its query heads (scaled by 1/sqrt(d)), then this position's K and V rows
+      const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
+      float* qs = (float*)(lds + P.off_attn + A.q);
+      const int nqv = P.group * P.d, nb = nqv + 2 * P.d;
+      int lo, hi;
+      td_slice(nb, wave, &lo, &hi);
+      C.ok &= poll_pairs<8>(P, P.tq + (size_t)T.g * nb, lo, hi, tag_in, qs, C);
+      lds_fence();
+      for (int i = lo + lane; i < min(hi, nqv); i += 64) qs[i] *= P.attn_scale;
+      rendezvous(P, C);
+      if (P.trace) ts1 = wall_clock64();
+      if (wave < P.group) attn_wave_d<D>(P, C, lds, wave, T, tag, tiles_seen, ts2);
+    } else {
+      const int K = kind == TD_ST_O ? P.qd : kind == TD_ST_DOWN ? P.I : P.H;
+      const uint2* src = kind == TD_ST_O ? P.to : kind == TD_ST_DOWN ? P.tact
+                       : kind == TD_ST_GU ? P.tx_mid : P.tx_out;
+      stage_gemv_input(P, C, wave, kind, K, src, kind == TD_ST_QKV && layer == 0 ? erow : nullptr, tag_in, g0, g1,
+                       g2, g3, gain);
+      rendezvous(P, C);
+      if (P.trace) ts1 = wall_clock64();
+      float inv = 1.0f;
+      if (gain) {  // norm_inv over the slices' sums of squares, in slice order
+        u32x4 a, b;
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(a), "=v"(b)
+                     : "v"(lds_addr(C.ctl + TD_CTL_SSQ))
+                     : "memory");
+        float ss = __uint_as_float(a.x);
+        ss += __uint_as_float(a.y);
+        ss += __uint_as_float(a.z);
+        ss += __uint_as_float(a.w);
+        ss += __uint_as_float(b.x);
+        ss += __uint_as_float(b.y);
+        ss += __uint_as_float(b.z);
+        ss += __uint_as_float(b.w);
+        inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
+      }
+      gemv_wave(P, C, wave, kind, layer, tag, inv, bias_a, bias_b, ts2);
+    }
+    if (P.trace) trace_rec(P, wave, seq, ts0, ts1, ts2, wall_clock64());
+  }
+  vm_drain();
+  if (!C.ok && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
 }
+
+// ------------------------------------------------------------ sync wave
+// Rendezvous count of the compute waves once they have staged the inputs of
+// the k-th stage they take part in (k from 0): one rendezvous per stage for the
+// staged inputs and, from the second stage on, one before staging.
+DEV uint32_t staged_target(int k) { return (uint32_t)TD_NW * (uint32_t)(2 * k + 1); }
 
 DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
-  const uint32_t epoch = uni(ld_u(P.sync + TD_SY_EPOCH));
-  const uint32_t tag0 = epoch * (uint32_t)P.n_stages;  // stage seq publishes tag0 + seq + 1
+  uint32_t* ctl = (uint32_t*)(lds + P.off_ctl);
   bool ok = true;
-  if (ld_u(P.sync + TD_SY_ABORT)) ok = false;
-  int tok = uni(*P.token_in);
-  if (tok < 0 || tok >= P.V) {
-    if (lane == 0 && cu == 0) atomicOr(P.err, TD_ERRBIT_RANGE);
-    tok = 0;
-  }
-  const uint16_t* erow = P.embed + (size_t)tok * P.H;
-  {  // this CU's residual rows start as the embedding row; the RoPE row of pos
-    int r0, r1;
-    cu_units(P.H, cu, ncu, r0, r1);
-    float* own = (float*)(lds + P.off_own);
-    for (int k = lane; k < r1 - r0; k += 64) own[k] = bf16f(erow[r0 + k]);
-    float* cs = (float*)(lds + P.off_rope);
-    for (int i = lane; i < P.d; i += 64) cs[i] = P.rope_cs[(size_t)P.pos * P.d + i];
+  const uint32_t epoch = uni(ld_u(P.sync + TD_SY_EPOCH));
+  {
+    const int tok = uni(*P.token_in);
+    if ((tok < 0 || tok >= P.V) && lane == 0 && cu == 0) atomicOr(P.err, TD_ERRBIT_RANGE);
   }
   const AttnTask T = attn_task(P, cu);
-  const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
-  float ba = 0.f, bb = 0.f;
-  preload(P, lds, TD_ST_QKV, 0, ba, bb);
-  uint64_t* tr = P.trace ? P.trace + (size_t)cu * P.n_stages * TD_TRACE_STAMPS : nullptr;
-  for (int seq = 0; seq < P.n_stages; ++seq) {
-    int kind, layer;
-    stage_of(P, seq, kind, layer);
-    const uint32_t tag_in = tag0 + (uint32_t)seq, tag = tag_in + 1u;
-    uint64_t ts[TD_TRACE_STAMPS > 5 ? 5 : TD_TRACE_STAMPS] = {0, 0, 0, 0, 0};
-    if (tr) ts[0] = wall_clock64();
-    if (kind == TD_ST_QKV) {
-      ok &= norm_input(P, lds, P.tx_out, tag_in, layer == 0 ? erow : nullptr, P.wf);
-    } else if (kind == TD_ST_GU) {
-      ok &= norm_input(P, lds, P.tx_mid, tag_in, nullptr, P.wf);
-    } else if (kind == TD_ST_HEAD) {
-      ok &= norm_input(P, lds, P.tx_out, tag_in, nullptr, 0);
-    } else if (kind == TD_ST_O || kind == TD_ST_DOWN) {
-      float* xin = (float*)(lds + P.off_xin);
-      const int K = kind == TD_ST_O ? P.qd : P.I;
-      ok &= poll_vec(P, kind == TD_ST_O ? P.to : P.tact, K, tag_in, xin);
-      const int ce = chunk_elems(P.wf);
-      zero_tail(xin, K, (K + ce - 1) / ce * ce);
-    } else if (T.valid) {  // ATTN: the task's query heads (pre-scaled by 1/sqrt(d)), and row pos
-      // the kv head's block: its query heads, then this position's K and V rows
-      float* qs = (float*)(lds + P.off_attn + A.q);
-      const int n = P.group * P.d;
-      ok &= poll_vec(P, P.tq + (size_t)T.g * (n + 2 * P.d), n + 2 * P.d, tag_in, qs);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      for (int i = lane; i < n; i += 64) qs[i] *= P.attn_scale;
-      if (T.t1 == P.pos + 1) patch_pos_row(P, lds, T, 0);
+  const int G = P.group;
+  uint32_t tiles_ready = 0;
+  if (T.valid) load_tile(P, lds, 0, T, 0);  // layer 0's first tile
+  for (int layer = 0; T.valid && layer < P.L; ++layer) {
+    // ATTN of this layer is the (5 layer + 1)-th stage the compute waves take part in
+    (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(5 * layer + 1), ok);
+    patch_pos_row(P, lds, T, 0);
+    lds_fence();
+    lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
+    for (int tile = 1; tile < T.ntiles; ++tile) {
+      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
+      load_tile(P, lds, layer, T, tile);
+      patch_pos_row(P, lds, T, tile);
+      lds_fence();
+      lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
     }
-    wg_bar();  // inputs ready
-    if (tr) ts[1] = wall_clock64();
-    if (kind == TD_ST_QKV && T.valid) {
-      load_tile(P, lds, layer, T, 0);  // this layer's first attention tile, ahead of time
-    } else if (kind == TD_ST_ATTN && T.valid) {
-      for (int tile = 0; tile < T.ntiles; ++tile) {
-        if (tile) {
-          load_tile(P, lds, layer, T, tile);
-          patch_pos_row(P, lds, T, tile);
-        }
-        wg_bar();  // tile in LDS
-        wg_bar();  // tile consumed
-      }
+    if (layer + 1 < P.L) {
+      // the next layer's first tile, once this layer's tiles are consumed and the
+      // GU stage (whose input poll is on the critical path) has its inputs
+      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
+      (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(5 * layer + 3), ok);
+      load_tile(P, lds, layer + 1, T, 0);
     }
-    wg_bar();  // outputs ready
-    if (tr) ts[2] = wall_clock64();
-    ok &= sync_epilogue(P, lds, kind, layer, tag, epoch, T, ba, bb);
-    if (tr) ts[3] = wall_clock64();
-    if (seq + 1 < P.n_stages) {
-      int nkind, nlayer;
-      stage_of(P, seq + 1, nkind, nlayer);
-      preload(P, lds, nkind, nlayer, ba, bb);
+  }
+  // HEAD: the compute waves' candidates -> this CU's candidate -> the last
+  // arriving CU picks the token
+  (void)lds_wait_ge(P, ctl + TD_CTL_HEADDONE, TD_NW, ok);
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff, bad = 0;
+  if (lane < TD_NW) {
+    bv = __uint_as_float(ctl[TD_CTL_CAND + 4 * lane]);
+    bi = (int)ctl[TD_CTL_CAND + 4 * lane + 1];
+    bad = (int)ctl[TD_CTL_CAND + 4 * lane + 2];
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  bad = __any(bad);
+  if (lane == 0) {
+    st_u(P.cand + cu * 4 + 0, __float_as_uint(bv));
+    st_u(P.cand + cu * 4 + 1, (uint32_t)bi);
+    st_u(P.cand + cu * 4 + 2, (uint32_t)bad);
+  }
+  vm_drain();
+  int last = 0;
+  if (lane == 0) last = atomicAdd(P.sync + TD_SY_FINAL, 1u) + 1u == (uint32_t)ncu;
+  if (uni(last)) {
+    float fv = -__builtin_inff();
+    int fi = 0x7fffffff, fbad = 0;
+    for (int c = lane; c < ncu; c += 64) {
+      const float v = __uint_as_float(ld_u(P.cand + c * 4 + 0));
+      const int i = (int)ld_u(P.cand + c * 4 + 1);
+      fbad |= (int)ld_u(P.cand + c * 4 + 2);
+      if (v > fv || (v == fv && i < fi)) { fv = v; fi = i; }
     }
-    if (tr) {
-      ts[4] = wall_clock64();
-      uint64_t* rec = tr + (size_t)seq * TD_TRACE_STAMPS;
-      if (lane < TD_TRACE_STAMPS) {
-        const uint64_t* wt = (const uint64_t*)(lds + P.off_wtrace);
-        uint64_t v = 0;
-        if (lane < 5) v = ts[lane];
-        else if (lane == 5) v = kind == TD_ST_ATTN && T.valid && T.c == 0 ? wt[TD_NW * 4] : 0;
-        else if (lane >= 8 && lane < 8 + 3 * TD_NW) v = wt[((lane - 8) / 3) * 4 + (lane - 8) % 3];
-        rec[lane] = v;
-      }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(fv, off);
+      const int oi = __shfl_xor(fi, off);
+      if (ov > fv || (ov == fv && oi < fi)) { fv = ov; fi = oi; }
+    }
+    fbad = __any(fbad);
+    if (lane == 0) {
+      *P.token_out = fi == 0x7fffffff ? 0 : fi;
+      if (fbad) atomicOr(P.err, TD_ERRBIT_NONFINITE);
+      st_u(P.sync + TD_SY_FINAL, 0u);
+      st_u(P.sync + TD_SY_EPOCH, epoch + 1u);
     }
   }
   if (!ok && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
 }
 
-template <int S>
+// ------------------------------------------------------------ the kernel
+// D: the head dimension (64 or 128), a template parameter so that only one
+// attention tile routine is compiled into each kernel.
+template <int D>
 __global__ void __launch_bounds__(TD_THREADS, 1) td_megakernel(td_kparams P) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  uint32_t* ctl = (uint32_t*)(lds + P.off_ctl);
+  if (threadIdx.x < TD_CTL_WORDS) ctl[threadIdx.x] = 0u;
+  __syncthreads();  // the only workgroup barrier: the control block is clear
   const int wave = uni((int)(threadIdx.x >> 6));
-  if (wave < TD_NW) compute_wave<S>(P, lds, wave);
+  if (wave < TD_NW) compute_wave<D>(P, lds, wave);
   else sync_wave(P, lds);
 }
 
@@ -878,32 +1045,20 @@ __global__ void __launch_bounds__(64) td_attention_kernel(const float* q, const 
 }  // namespace
 
 // ------------------------------------------------------------ launchers
-#define TD_RING_CASES(X) X(8) X(12) X(16)
-
-int td_megakernel_occupancy(int ring_slots, int lds_bytes, int* blocks) {
-  hipError_t e = hipErrorInvalidValue;
-#define OCC(S)                                                                                          \
-  if (ring_slots == S) {                                                                                \
-    e = hipFuncSetAttribute((const void*)td_megakernel<S>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                            lds_bytes);                                                                 \
-    if (e == hipSuccess)                                                                                \
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, td_megakernel<S>, TD_THREADS, lds_bytes); \
-  }
-  TD_RING_CASES(OCC)
-#undef OCC
+int td_megakernel_occupancy(int d, int lds_bytes, int* blocks) {
+  const void* f = d == 64 ? (const void*)td_megakernel<64> : (const void*)td_megakernel<128>;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e == hipSuccess)
+    e = d == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, td_megakernel<64>, TD_THREADS, lds_bytes)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, td_megakernel<128>, TD_THREADS, lds_bytes);
   return (int)e;
 }
 
-int td_launch_megakernel(const td_kparams* p, int ncu, int ring_slots, void* stream) {
+int td_launch_megakernel(const td_kparams* p, int ncu, void* stream) {
   void* args[] = {(void*)p};
-  hipError_t e = hipErrorInvalidValue;
-#define LAUNCH(S)                                                                                           \
-  if (ring_slots == S)                                                                                      \
-    e = hipLaunchCooperativeKernel((const void*)td_megakernel<S>, dim3(ncu), dim3(TD_THREADS), args,        \
-                                   (unsigned)p->lds_bytes, (hipStream_t)stream);
-  TD_RING_CASES(LAUNCH)
-#undef LAUNCH
-  return (int)e;
+  const void* f = p->d == 64 ? (const void*)td_megakernel<64> : (const void*)td_megakernel<128>;
+  return (int)hipLaunchCooperativeKernel(f, dim3(ncu), dim3(TD_THREADS), args, (unsigned)p->lds_bytes,
+                                         (hipStream_t)stream);
 }
 
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,

@@ -25,36 +25,29 @@ namespace {
 
 constexpr int OP_WAVES = 4;  // waves per workgroup of the GEMV ops
 
-// xs = RMSNorm(x) * gain over H floats, with the persistent kernel's order:
-// lane-partial sums of squares over 4-float groups strided by 256, one wave
-// sum, inv = 1 / sqrt(ss / H + eps).
-DEV void op_norm_to_lds(const float* x, const uint16_t* gain, int H, float eps, float* xs, float* red) {
-  const int t = threadIdx.x, lane = lane_id();
+// RMSNorm of x [H] in the persistent kernel's form: xs = x * gain in LDS, and
+// the returned inv = 1 / sqrt(mean(x^2) + eps) (the caller multiplies each dot
+// product by it), mean(x^2) summed over the same TD_NW slices in the same order
+// (slice_ssq, norm_inv).  Needs blockDim.x >= 64.
+DEV float op_norm_to_lds(const float* x, const uint16_t* gain, int H, float eps, float* xs, float* red) {
+  const int t = threadIdx.x, wave = t >> 6, nwaves = blockDim.x >> 6;
   for (int i = t; i < H; i += blockDim.x) xs[i] = x[i];
   __syncthreads();
-  if (t < 64) {
-    float ss = 0.f;
-    for (int i = lane * 4; i < H; i += 256) {
-      const f32x4 v = *(const f32x4*)(xs + i);
-      ss = fmaf(v.x, v.x, ss);
-      ss = fmaf(v.y, v.y, ss);
-      ss = fmaf(v.z, v.z, ss);
-      ss = fmaf(v.w, v.w, ss);
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) red[0] = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int w = wave; w < TD_NW; w += nwaves) {
+    int lo, hi;
+    td_slice(H, w, &lo, &hi);
+    const float ss = slice_ssq(xs, lo, hi);
+    if (lane_id() == 0) red[w] = ss;
   }
   __syncthreads();
-  const float inv = red[0];
-  for (int i = t * 4; i < H; i += blockDim.x * 4) {
-    f32x4 v = *(const f32x4*)(xs + i);
-    const uint2 g = *(const uint2*)(gain + i);
-    v.x = v.x * inv * bf_lo(g.x);
-    v.y = v.y * inv * bf_hi(g.x);
-    v.z = v.z * inv * bf_lo(g.y);
-    v.w = v.w * inv * bf_hi(g.y);
-    *(f32x4*)(xs + i) = v;
+  const float inv = norm_inv(red, H, eps);
+  __syncthreads();
+  for (int i = t * 2; i < H; i += blockDim.x * 2) {
+    const uint32_t g = *(const uint32_t*)(gain + i);
+    xs[i] *= bf_lo(g);
+    xs[i + 1] *= bf_hi(g);
   }
+  return inv;
 }
 
 // Copies n floats to LDS and zeroes the tail up to the chunk multiple.
@@ -134,7 +127,7 @@ __global__ void __launch_bounds__(256) op_qkv(td_opparams P, int layer, int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* xs = (float*)lds;
   const td_layer_dev& Ld = P.layers[layer];
-  op_norm_to_lds(P.x, Ld.attn_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
+  const float inv = op_norm_to_lds(P.x, Ld.attn_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
   op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -145,8 +138,8 @@ __global__ void __launch_bounds__(256) op_qkv(td_opparams P, int layer, int R) {
     const int u = (blockIdx.x * OP_WAVES + wave) * R + k;
     if (u >= U) break;
     const int ra = op_unit_row_qkv(P, u, 0), rb = ra + half;
-    float a = op_row(P.wf, Ld.w[0], Ld.s[0], ra, P.H, xs);
-    float b = op_row(P.wf, Ld.w[0], Ld.s[0], rb, P.H, xs);
+    float a = op_row(P.wf, Ld.w[0], Ld.s[0], ra, P.H, xs) * inv;
+    float b = op_row(P.wf, Ld.w[0], Ld.s[0], rb, P.H, xs) * inv;
     if (lane != 0) continue;
     if (P.has_bias) {
       a += bf16f(Ld.bias[ra]);
@@ -213,7 +206,7 @@ __global__ void __launch_bounds__(512) op_attn(td_opparams P, int layer) {
   }
   if (wave < G) {
     acc = attn_finish<D>(acc);
-    float* pr = P.part + (((size_t)g * P.n_chunks_max + c) * G + wave) * (D + 4);
+    float* pr = P.part + (((size_t)g * G + wave) * P.n_chunks_max + c) * (D + 4);
     if (lane < D / 4) *(f32x4*)(pr + 4 * lane) = acc;
     if (lane == 0) *(f32x4*)(pr + D) = f32x4{m, l, 0.f, 0.f};
   }
@@ -228,8 +221,8 @@ __global__ void __launch_bounds__(512) op_merge(td_opparams P) {
   const int G = P.group, g = blockIdx.x, h = threadIdx.x >> 6, lane = lane_id();
   if (h >= G) return;
   const int n = (pos + P.chunk_len) / P.chunk_len;  // <= 64
-  const float* base = P.part + (size_t)g * P.n_chunks_max * G * (D + 4);
-  auto part = [&](int c) { return base + ((size_t)c * G + h) * (D + 4); };
+  const float* base = P.part + ((size_t)g * G + h) * P.n_chunks_max * (D + 4);
+  auto part = [&](int c) { return base + (size_t)c * (D + 4); };
   const bool have = lane < n;
   const float* own = part(have ? lane : 0);
   const float mm = have ? own[D] : -__builtin_inff();
@@ -281,15 +274,15 @@ __global__ void __launch_bounds__(256) op_gu(td_opparams P, int layer, int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* xs = (float*)lds;
   const td_layer_dev& Ld = P.layers[layer];
-  op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
+  const float inv = op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
   op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
   __syncthreads();
   const int wave = threadIdx.x >> 6;
   for (int k = 0; k < R; ++k) {
     const int u = (blockIdx.x * OP_WAVES + wave) * R + k;
     if (u >= P.I) break;
-    const float gt = op_row(P.wf, Ld.w[2], Ld.s[2], u, P.H, xs);
-    const float up = op_row(P.wf, Ld.w[2], Ld.s[2], u + P.I, P.H, xs);
+    const float gt = op_row(P.wf, Ld.w[2], Ld.s[2], u, P.H, xs) * inv;
+    const float up = op_row(P.wf, Ld.w[2], Ld.s[2], u + P.I, P.H, xs) * inv;
     if (lane_id() == 0) P.act[u] = gt / (1.0f + expf(-gt)) * up;
   }
 }
@@ -300,7 +293,7 @@ __global__ void __launch_bounds__(256) op_head(td_opparams P, int R) {
   float* xs = (float*)lds;
   __shared__ float cv[OP_WAVES];
   __shared__ int ci[OP_WAVES], cb[OP_WAVES];
-  op_norm_to_lds(P.x, P.final_norm, P.H, P.eps, xs, xs + op_kpad(P.H, 0));
+  const float inv = op_norm_to_lds(P.x, P.final_norm, P.H, P.eps, xs, xs + op_kpad(P.H, 0));
   op_zero_tail(xs, P.H, op_kpad(P.H, 0));
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -309,7 +302,7 @@ __global__ void __launch_bounds__(256) op_head(td_opparams P, int R) {
   for (int k = 0; k < R; ++k) {
     const int r = (blockIdx.x * OP_WAVES + wave) * R + k;
     if (r >= P.V) break;
-    const float v = op_row(0, (const uint8_t*)P.head, nullptr, r, P.H, xs);
+    const float v = op_row(0, (const uint8_t*)P.head, nullptr, r, P.H, xs) * inv;
     if (lane == 0) P.logits[r] = v;
     if (!isfinite(v)) bad = 1;
     else if (v > bv) { bv = v; bi = r; }
@@ -365,7 +358,7 @@ int td_op_head_blocks(const td_opparams* p) { return blocks_for(p->V, R_HEAD); }
 
 size_t td_op_lds_bytes(const td_opparams* p) {
   auto kp = [](int K, int f) { return (size_t)((K + (f ? 2047 : 511)) / (f ? 2048 : 512) * (f ? 2048 : 512)); };
-  size_t x = std::max({kp(p->H, p->wf), kp(p->qd, p->wf), kp(p->I, p->wf), kp(p->H, 0)}) * 4 + 16;
+  size_t x = std::max({kp(p->H, p->wf), kp(p->qd, p->wf), kp(p->I, p->wf), kp(p->H, 0)}) * 4 + TD_NW * 4;
   const size_t D = (size_t)p->d, G = (size_t)p->group;
   const size_t a = G * D * 4 + G * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2;
   return std::max(x, a);
