@@ -227,50 +227,6 @@ DEV void st_tag(uint2* p, float v, uint32_t tag) {
   asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(w) : "memory");
 }
 
-struct CState;
-DEV void topup(const td_kparams& P, CState& C);
-
-// Waits until the pairs [lo, hi) of src (lo, hi even) all carry `tag` and
-// copies their values to dst[lo, hi) (LDS).  Each round loads up to W 16-byte
-// units (two pairs) per lane and re-polls the units still missing; before each
-// re-poll round the (compute) wave tops up its weight ring, since the round's
-// wait leaves none of its own loads in flight.  false: the wait timed out (or
-// another wait did).
-template <int W>
-DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CState& C) {
-  const int lane = lane_id();
-  const int nu = (hi - lo) >> 1;
-  if (nu <= 0) return true;
-  const __amdgpu_buffer_rsrc_t R = rsrc(src + lo, (uint32_t)nu * 16u);
-  float* d = dst + lo;
-  const uint64_t t0 = wall_clock64();
-  for (int b0 = 0; b0 < nu; b0 += W * 64) {
-    uint32_t pend = 0;
-#pragma unroll
-    for (int k = 0; k < W; ++k)
-      if (b0 + k * 64 + lane < nu) pend |= 1u << k;
-    for (uint32_t it = 0;; ++it) {
-      if (it) topup(P, C);
-      u32x4 r[W];
-#pragma unroll
-      for (int k = 0; k < W; ++k)
-        r[k] = __builtin_amdgcn_raw_buffer_load_b128(R, (uint32_t)(b0 + k * 64 + lane) * 16u, 0, TD_CPOL_SC1);
-#pragma unroll
-      for (int k = 0; k < W; ++k) {
-        if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
-          const int u = b0 + k * 64 + lane;
-          d[2 * u] = __uint_as_float(r[k].x);
-          d[2 * u + 1] = __uint_as_float(r[k].z);
-          pend &= ~(1u << k);
-        }
-      }
-      if (!__any(pend != 0u)) break;
-      if ((it & 3u) == 3u && uni(wait_expired(P, t0) ? 1 : 0)) return false;
-    }
-  }
-  return true;
-}
-
 // ------------------------------------------------------------ attention task
 // Split-K decode attention: kv head g's positions 0..pos are cut into chunks of
 // chunk_len; one CU per (g, chunk) computes a partial (m, l, acc) for each of
@@ -391,7 +347,7 @@ DEV uint32_t ops_of(const CState& C, uint32_t a, uint32_t b) {
   const uint32_t hi4 = min(b, C.n4);
   return (b - a) + (hi4 > a ? hi4 - a : 0u);
 }
-// s_waitcnt vmcnt(n) for a run-time n < 2 TD_FLIGHT (larger values wait for
+// s_waitcnt vmcnt(n) for a run-time n (values past the table wait for
 // everything, which is only more conservative)
 DEV void vmcnt_rt(uint32_t n) {
   switch (n) {
@@ -410,8 +366,8 @@ DEV void vmcnt_rt(uint32_t n) {
 }
 static_assert(TD_FLIGHT >= 1 && 2 * TD_FLIGHT - 2 <= 10, "vmcnt_rt covers the waits of at most TD_FLIGHT chunks");
 // Waits until no load older than chunk a is outstanding (chunks [a, issued)
-// may still be in flight; issued - a < TD_FLIGHT).  The steady-state case, the
-// newest TD_FLIGHT - 1 chunks all of one format, is one compile-time wait.
+// may still be in flight).  The steady-state case, the newest TD_FLIGHT - 1
+// chunks all of one format, is one compile-time wait.
 DEV void wait_older_than(const CState& C, uint32_t a) {
   const uint32_t m = C.issued - a;
   if (m == TD_FLIGHT - 1 && a >= C.n4) vmcnt_wait<TD_FLIGHT - 1>();
@@ -446,10 +402,10 @@ DEV void refill(const td_kparams& P, CState& C) {
   }
   issue_chunk(P, C);
 }
-// During a wait, with none of the wave's loads outstanding (all issued chunks
-// are in LDS): up to TD_FLIGHT more chunks.
+// During a wait: up to TD_FLIGHT more chunks into free slots, without waiting
+// (so up to 2 TD_FLIGHT chunks can be in flight for a while; the waits below
+// count loads, not an assumed depth).
 DEV void topup(const td_kparams& P, CState& C) {
-  C.lk = C.issued;
 #pragma unroll 1
   for (int k = 0; k < TD_FLIGHT && ring_room(P, C); ++k) issue_chunk(P, C);
 }
@@ -466,6 +422,54 @@ DEV void chunk_release(const td_kparams& P, CState& C) {
   ++C.t;
   C.slot = C.slot + 1 == P.ring_slots ? 0 : C.slot + 1;
   refill(P, C);
+}
+
+
+// Waits until the pairs [lo, hi) of src (lo, hi even) all carry `tag` and
+// copies their values to dst[lo, hi) (LDS).  Each round loads up to W 16-byte
+// units (two pairs) per lane and re-polls the units still missing.  After a
+// round's loads are issued, the (compute) wave tops its weight ring up: those
+// chunk loads are younger than the poll's, so waiting for the poll never waits
+// for them, and every chunk issued before the round has landed once the
+// round's results are in.  false: the wait timed out (or another wait did).
+template <int W>
+DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CState& C) {
+  const int lane = lane_id();
+  const int nu = (hi - lo) >> 1;
+  if (nu <= 0) return true;
+  const __amdgpu_buffer_rsrc_t R = rsrc(src + lo, (uint32_t)nu * 16u);
+  float* d = dst + lo;
+  const uint64_t t0 = wall_clock64();
+  for (int b0 = 0; b0 < nu; b0 += W * 64) {
+    uint32_t pend = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+      if (b0 + k * 64 + lane < nu) pend |= 1u << k;
+    for (uint32_t it = 0;; ++it) {
+      const uint32_t landed_before = C.issued;
+      u32x4 r[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k)
+        r[k] = __builtin_amdgcn_raw_buffer_load_b128(R, (uint32_t)(b0 + k * 64 + lane) * 16u, 0, TD_CPOL_SC1);
+      topup(P, C);
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
+          const int u = b0 + k * 64 + lane;
+          d[2 * u] = __uint_as_float(r[k].x);
+          d[2 * u + 1] = __uint_as_float(r[k].z);
+          pend &= ~(1u << k);
+        }
+      }
+      // only the top-up's loads may still be outstanding: the poll's, and every
+      // chunk issued before the round, are complete
+      vmcnt_rt(ops_of(C, landed_before, C.issued));
+      if (C.lk < landed_before) C.lk = landed_before;
+      if (!__any(pend != 0u)) break;
+      if ((it & 3u) == 3u && uni(wait_expired(P, t0) ? 1 : 0)) return false;
+    }
+  }
+  return true;
 }
 
 DEV void rendezvous(const td_kparams& P, CState& C) {
