@@ -170,11 +170,13 @@ int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_
 /* In-kernel stage trace (the per-worker timeline of one step).  td_trace_bytes
  * gives the size of the trace: for each CU and each stage of the step (5 per
  * layer plus the head), a record of 32 uint64 timestamps of the 100 MHz device
- * clock: [0..4] stage start, inputs staged, compute finished, epilogue finished,
- * grid barrier passed; [8 + 3w .. 10 + 3w] compute wave w's stage start, first
- * weight chunk ready and last chunk done (0 if the wave had no chunk).  td_set_trace(ctx, d_buf, bytes) makes every following step write it
- * to the device buffer d_buf (caller-owned, at least td_trace_bytes bytes);
- * d_buf = NULL turns it off.  TD_E_INVALID_ARG for a buffer that is too small. */
+ * clock, four per compute wave w at [4 w .. 4 w + 3]: stage entered, inputs
+ * staged (the workgroup rendezvous passed), first weight chunk in LDS (first
+ * attention tile done), last output published; 0 where the wave had no part
+ * in the stage.  td_set_trace(ctx, d_buf, bytes) makes every following step
+ * write it to the device buffer d_buf (caller-owned, at least td_trace_bytes
+ * bytes); d_buf = NULL turns it off.  TD_E_INVALID_ARG for a buffer that is
+ * too small. */
 int64_t td_trace_bytes(const td_ctx* ctx);
 int td_set_trace(td_ctx* ctx, void* d_buf, int64_t bytes);
 
