@@ -109,7 +109,8 @@ class KVCache:
 
 
 class Decoder:
-    """One td_ctx: td_create at construction, td_decode_step per step."""
+    """One td_ctx: td_create at construction, td_decode_step per step (or
+    td_decode_loop for several greedy steps in one launch)."""
 
     def __init__(self, dm: DeviceModel, max_ctx: int, executor: int = TD_EXEC_MEGAKERNEL):
         self.dm = dm
@@ -133,6 +134,15 @@ class Decoder:
         kvs = kv.td_kv()
         _lib.check(_lib.lib().td_decode_step(self._h, token_ptr, int(pos), ctypes.byref(kvs), _ptr(logits),
                                              _stream_handle(stream)), "td_decode_step")
+
+    def loop(self, token_ptr: int, pos: int, n_steps: int, kv: KVCache, logits, tokens=None, count=None,
+             eos: int = -1, stream=None) -> None:
+        """Up to n_steps greedy steps in one launch (td_decode_loop); `tokens` (int32 device
+        tensor [n_steps]) and `count` (int32 device tensor [1]) are optional outputs."""
+        kvs = kv.td_kv()
+        _lib.check(_lib.lib().td_decode_loop(self._h, token_ptr, int(pos), int(n_steps), int(eos), ctypes.byref(kvs),
+                                             _ptr(logits), _ptr(tokens), _ptr(count), _stream_handle(stream)),
+                   "td_decode_loop")
 
     def status(self) -> int:
         err = ctypes.c_int32(0)

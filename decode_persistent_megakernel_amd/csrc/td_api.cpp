@@ -381,9 +381,11 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     kp.lds_bytes = (int32_t)(shift + fixed);
   }
   if (kp.lds_bytes > lds_cap) return fail(TD_E_UNSUPPORTED, "LDS layout exceeds the CU's LDS");
+  // the greedy candidates of all CUs are gathered in the attention tile area
+  if ((int64_t)ncu * 16 > td_tile_bytes(d)) return fail(TD_E_UNSUPPORTED, "too many CUs for the candidate area");
   {
     int blocks = 0;
-    const int oe = td_megakernel_occupancy(d, kp.lds_bytes, &blocks);
+    const int oe = td_megakernel_occupancy(d, c.weight_format, kp.lds_bytes, &blocks);
     if (oe != 0 || blocks < 1) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
   }
   kp.ring_slots = (int32_t)ring;
@@ -450,7 +452,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const size_t o_q = take((size_t)(qd + 2 * kvd) * 8), o_o = take((size_t)qd * 8);
   const size_t o_act = take((size_t)I * 8);
   const size_t o_part = take((size_t)nkv * n_chunks_max * group * (d + 4) * 8);
-  const size_t o_cand = take((size_t)ncu * 4 * 4);
+  const size_t o_cand = take((size_t)ncu * 4 * 8);
   const size_t o_sync = take((size_t)sync_words * 4);
   const size_t o_tok = take(4), o_err = take(4);
   const size_t o_rope = take((size_t)c.max_ctx * (d / 2) * 2 * 4);
@@ -549,7 +551,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   kp.to = (uint2*)(base + o_o);
   kp.tact = (uint2*)(base + o_act);
   kp.tpart = (uint2*)(base + o_part);
-  kp.cand = (uint32_t*)(base + o_cand);
+  kp.cand = (uint2*)(base + o_cand);
   kp.sync = (uint32_t*)(base + o_sync);
   kp.token_out = (int32_t*)(base + o_tok);
   kp.err = (int32_t*)(base + o_err);
@@ -610,6 +612,10 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
   if (pos < 0 || pos >= ctx->cfg.max_ctx) return fail(TD_E_RANGE, "pos outside [0, max_ctx)");
   td_kparams p = ctx->kp;
   p.pos = pos;
+  p.n_steps = 1;
+  p.eos = -1;
+  p.tokens_out = nullptr;
+  p.count_out = nullptr;
   p.token_in = d_token;
   p.logits = d_logits_out;
   p.kc = (uint16_t*)kv->k;
@@ -637,6 +643,37 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
     }
   }
   if (le != 0) return hip_fail((hipError_t)le, "step launch");
+  if (ctx->timing) {
+    (void)hipEventRecord(ctx->ev1, s);
+    ctx->timed = true;
+  }
+  ctx->last_stream = s;
+  ctx->launched = true;
+  return TD_OK;
+}
+
+int td_decode_loop(td_ctx* ctx, const int32_t* d_token, int32_t pos, int32_t n_steps, int32_t eos_id,
+                   const td_kv* kv, float* d_logits_out, int32_t* d_tokens_out, int32_t* d_count_out, void* stream) {
+  if (!ctx || !d_token || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
+  if (ctx->executor != TD_EXEC_MEGAKERNEL) return fail(TD_E_UNSUPPORTED, "the step loop needs the megakernel executor");
+  if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (n_steps < 1 || n_steps > TD_MAX_LOOP_STEPS) return fail(TD_E_INVALID_ARG, "n_steps outside [1, TD_MAX_LOOP_STEPS]");
+  if (eos_id < -1 || eos_id >= ctx->cfg.vocab) return fail(TD_E_INVALID_ARG, "eos_id outside [-1, vocab)");
+  if (pos < 0 || (int64_t)pos + n_steps > ctx->cfg.max_ctx) return fail(TD_E_RANGE, "positions outside [0, max_ctx)");
+  td_kparams p = ctx->kp;
+  p.pos = pos;
+  p.n_steps = n_steps;
+  p.eos = eos_id;
+  p.tokens_out = d_tokens_out;
+  p.count_out = d_count_out;
+  p.token_in = d_token;
+  p.logits = d_logits_out;
+  p.kc = (uint16_t*)kv->k;
+  p.vc = (uint16_t*)kv->v;
+  hipStream_t s = (hipStream_t)stream;
+  if (ctx->timing) (void)hipEventRecord(ctx->ev0, s);
+  const int le = td_launch_megakernel(&p, ctx->ncu, stream);
+  if (le != 0) return hip_fail((hipError_t)le, "loop launch");
   if (ctx->timing) {
     (void)hipEventRecord(ctx->ev1, s);
     ctx->timed = true;

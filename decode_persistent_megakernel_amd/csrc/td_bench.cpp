@@ -14,9 +14,14 @@
 //
 // --executor megakernel|per_op|graph picks the executor behind td_decode_step.
 //
-//   td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--copy-calibration] [--print-config]
+// --loop N runs the steps through td_decode_loop, N greedy steps per launch
+// (the last launch takes the remainder), instead of one td_decode_step each.
+//
+//   td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--loop N] [--copy-calibration]
+//            [--print-config]
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -130,6 +135,7 @@ int main(int argc, char** argv) {
   std::string name = "llama1b";
   int steps = 128, warmup = 8;
   bool only_config = false, copy_cal = false;
+  int loop_n = 0;
   int executor = TD_EXEC_MEGAKERNEL;
   std::string ex_name = "megakernel";
   for (int i = 1; i < argc; ++i) {
@@ -139,6 +145,7 @@ int main(int argc, char** argv) {
     else if (a == "--warmup" && i + 1 < argc) warmup = atoi(argv[++i]);
     else if (a == "--print-config") only_config = true;
     else if (a == "--copy-calibration") copy_cal = true;
+    else if (a == "--loop" && i + 1 < argc) loop_n = atoi(argv[++i]);
     else if (a == "--executor" && i + 1 < argc) {
       ex_name = argv[++i];
       if (ex_name == "megakernel") executor = TD_EXEC_MEGAKERNEL;
@@ -150,7 +157,7 @@ int main(int argc, char** argv) {
       }
     }
     else {
-      fprintf(stderr, "usage: td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] "
+      fprintf(stderr, "usage: td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--loop N] "
                       "[--copy-calibration] [--print-config]\n");
       return 2;
     }
@@ -263,30 +270,39 @@ int main(int argc, char** argv) {
   CK(hipMemcpy(&first_tok, w.prompt ? td_token_ptr(ctx) : tok, 4, hipMemcpyDeviceToHost));
   CK(hipMemcpy(tok, &first_tok, 4, hipMemcpyHostToDevice));
 
+  // one launch per step, or loops of loop_n steps; events bracket every launch
+  auto launches_of = [&](int n) { return loop_n > 0 ? (n + loop_n - 1) / loop_n : n; };
   auto run = [&](int n, std::vector<hipEvent_t>* ev) {
-    for (int i = 0; i < n; ++i) {
-      if (ev) CK(hipEventRecord((*ev)[2 * i], stream));
-      TD(td_decode_step(ctx, i == 0 ? tok : td_token_ptr(ctx), start + i, &kv, logits, stream));
-      if (ev) CK(hipEventRecord((*ev)[2 * i + 1], stream));
+    int li = 0;
+    for (int i = 0; i < n; ++li) {
+      const int m = loop_n > 0 ? std::min(loop_n, n - i) : 1;
+      if (ev) CK(hipEventRecord((*ev)[2 * li], stream));
+      const int32_t* t = i == 0 ? tok : td_token_ptr(ctx);
+      if (loop_n > 0) TD(td_decode_loop(ctx, t, start + i, m, -1, &kv, logits, nullptr, nullptr, stream));
+      else TD(td_decode_step(ctx, t, start + i, &kv, logits, stream));
+      if (ev) CK(hipEventRecord((*ev)[2 * li + 1], stream));
+      i += m;
     }
   };
   run(warmup, nullptr);
   CK(hipStreamSynchronize(stream));
   TD(td_status(ctx, nullptr));
-  std::vector<hipEvent_t> ev(2 * steps);
+  const int nl = launches_of(steps);
+  std::vector<hipEvent_t> ev(2 * nl);
   for (auto& e : ev) CK(hipEventCreate(&e));
   run(steps, &ev);
   CK(hipStreamSynchronize(stream));
   TD(td_status(ctx, nullptr));
   double total = 0.0;
-  for (int i = 0; i < steps; ++i) {
+  for (int i = 0; i < nl; ++i) {
     float ms = 0.f;
     CK(hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]));
     total += ms;
   }
-  printf("{\"workload\": \"%s\", \"executor\": \"%s\", \"steps\": %d, \"warmup\": %d, "
+  printf("{\"workload\": \"%s\", \"executor\": \"%s\", \"steps\": %d, \"warmup\": %d, \"steps_per_launch\": %d, "
          "\"positions\": [%d, %d], \"ms_per_step\": %.4f, \"tokens_per_s\": %.2f}\n",
-         w.name, ex_name.c_str(), steps, warmup, start, start + steps - 1, total / steps, steps / (total / 1e3));
+         w.name, ex_name.c_str(), steps, warmup, loop_n > 0 ? loop_n : 1, start, start + steps - 1, total / steps,
+         steps / (total / 1e3));
   fflush(stdout);
 
   if (copy_cal) {

@@ -26,10 +26,9 @@ enum { TD_ERRBIT_NONFINITE = 1, TD_ERRBIT_RANGE = 2, TD_ERRBIT_TIMEOUT = 4 };
 
 // uint32 word offsets inside the sync area (each on its own 256-byte line)
 enum {
-  TD_SY_EPOCH = 0,    // launches completed (the tag base of the next launch)
+  TD_SY_EPOCH = 0,    // steps completed (the tag base of the next launch's first step)
   TD_SY_ABORT = 64,   // set when a wait timed out
-  TD_SY_FINAL = 128,  // arrivals at the greedy-token reduction
-  TD_SY_WORDS = 192
+  TD_SY_WORDS = 128
 };
 
 // uint32 word offsets of the LDS control block (intra-workgroup hand-offs)
@@ -37,7 +36,10 @@ enum {
   TD_CTL_RV = 16,        // rendezvous arrivals of the compute waves (monotonic)
   TD_CTL_TREADY = 17,    // attention tiles made ready (monotonic)
   TD_CTL_TDONE = 18,     // attention tiles consumed, summed over the query-head waves
-  TD_CTL_HEADDONE = 19,  // compute waves finished with the head stage
+  TD_CTL_HEADDONE = 19,  // compute waves finished with the head stage (monotonic over the steps)
+  TD_CTL_TOKEN = 20,     // the greedy token of the last step finished
+  TD_CTL_TOKREADY = 21,  // steps whose token has been decided (monotonic)
+  TD_CTL_STOP = 22,      // nonzero: the step just decided is the launch's last
   TD_CTL_SSQ = 24,       // [8] fp32 partial sums of squares of the RMSNorm input slices
   TD_CTL_CAND = 32,      // [8][4] per-wave greedy candidates: value bits, index, nonfinite, pad
   TD_CTL_WORDS = 64
@@ -65,8 +67,10 @@ struct td_kparams {
   float eps, attn_scale;
   // attention split
   int32_t chunk_len, n_chunks_max;
-  // step
-  int32_t pos;
+  // steps: n_steps greedy steps at positions pos, pos + 1, ... in one launch,
+  // stopping early after a step whose token is eos (eos < 0: none) or whose
+  // logits were not all finite
+  int32_t pos, n_steps, eos;
   // weights
   const td_layer_dev* layers;
   const uint16_t* embed;
@@ -77,6 +81,8 @@ struct td_kparams {
   uint16_t* vc;
   const int32_t* token_in;
   float* logits;
+  int32_t* tokens_out;  // [n_steps] the steps' tokens, -1 past the last step run; or null
+  int32_t* count_out;   // steps run; or null
   // scratch (ctx-owned).  Every value handed from one CU to another is
   // published as a (value bits, tag) pair written with one 8-byte agent-scope
   // store; tag = launch epoch * n_stages + stage + 1 names the producing stage,
@@ -88,7 +94,7 @@ struct td_kparams {
   uint2* to;       // [nq d] attention output
   uint2* tact;     // [I] SiLU(gate) * up
   uint2* tpart;    // [nkv][group][n_chunks_max][d + 4] attention partials: acc[d], m, l, pad
-  uint32_t* cand;  // [ncu][4]: value bits, index, nonfinite
+  uint2* cand;     // [ncu][4] pairs: a CU's greedy candidate (value bits, index, nonfinite, 0)
   uint32_t* sync;
   int32_t* token_out;
   int32_t* err;
@@ -185,7 +191,7 @@ static inline void td_slice(int K, int w, int* lo, int* hi) {
 int td_launch_megakernel(const td_kparams* p, int ncu, void* stream);
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
                      void* stream);
-int td_megakernel_occupancy(int head_dim, int lds_bytes, int* blocks_per_cu);
+int td_megakernel_occupancy(int head_dim, int weight_format, int lds_bytes, int* blocks_per_cu);
 // per-op executor (td_ops.hip)
 int td_op_head_blocks(const td_opparams* p);
 size_t td_op_lds_bytes(const td_opparams* p);

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "td.h"
 #include "td_internal.h"
 
 #include "td_device.h"
@@ -235,22 +236,23 @@ DEV void st_tag(uint2* p, float v, uint32_t tag) {
 struct AttnTask {
   int valid, g, c, t0, t1, ntiles, n_used;
 };
-DEV AttnTask attn_task(const td_kparams& P, int cu) {
+DEV AttnTask attn_task(const td_kparams& P, int cu, int pos) {
   AttnTask t;
-  t.n_used = (P.pos + P.chunk_len) / P.chunk_len;  // chunks covering positions 0..pos
+  t.n_used = (pos + P.chunk_len) / P.chunk_len;  // chunks covering positions 0..pos
   t.valid = cu < P.nkv * t.n_used;
   t.g = t.valid ? cu / t.n_used : 0;
   t.c = t.valid ? cu - t.g * t.n_used : 0;
   t.t0 = t.c * P.chunk_len;
-  t.t1 = min(t.t0 + P.chunk_len, P.pos + 1);
+  t.t1 = min(t.t0 + P.chunk_len, pos + 1);
   t.ntiles = t.valid ? (t.t1 - t.t0 + TD_TILE - 1) / TD_TILE : 0;
   return t;
 }
 
 // K and V rows [tb, tb + nv) of the tile, except row pos (written during this
 // very step; it comes from the published copy), into the LDS tile; rows past
-// the chunk end read as zero.
-DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask& T, int tile) {
+// the chunk end read as zero.  The loads are agent-scope: rows written by an
+// earlier step of the same launch come from other CUs.
+DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask& T, int tile, int pos) {
   const int lane = lane_id();
   const int d = P.d;
   const int tb = T.t0 + tile * TD_TILE;
@@ -267,15 +269,15 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t off = (uint32_t)(i0 + k * 64 + lane) * 16u;  // out of range reads 0
-      kr[k] = __builtin_amdgcn_raw_buffer_load_b128(RK, off, 0, 0);
-      vr[k] = __builtin_amdgcn_raw_buffer_load_b128(RV, off, 0, 0);
+      kr[k] = __builtin_amdgcn_raw_buffer_load_b128(RK, off, 0, TD_CPOL_SC1);
+      vr[k] = __builtin_amdgcn_raw_buffer_load_b128(RV, off, 0, TD_CPOL_SC1);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = i0 + k * 64 + lane;
       if (i < npiece) {
         const int row = i / q16, pc = i - row * q16;
-        if (row >= nv || tb + row != P.pos) {
+        if (row >= nv || tb + row != pos) {
           *(u32x4*)(kt + row * (d + 8) + pc * 8) = kr[k];
           *(u32x4*)(vt + row * d + pc * 8) = vr[k];
         }
@@ -286,10 +288,10 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
 
 // this position's K and V rows (LDS fp32 holding bf16 values) into the tile
 // when the tile holds position pos
-DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int tile) {
+DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int tile, int pos) {
   const int tb = T.t0 + tile * TD_TILE;
-  if (P.pos < tb || P.pos >= tb + TD_TILE || P.pos >= T.t1) return;
-  const int d = P.d, row = P.pos - tb;
+  if (pos < tb || pos >= tb + TD_TILE || pos >= T.t1) return;
+  const int d = P.d, row = pos - tb;
   const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max);
   const float* kvp = (const float*)(lds + P.off_attn + A.kvp);
   uint16_t* kt = (uint16_t*)(lds + P.off_tile);
@@ -313,7 +315,11 @@ DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int
 // hand-offs and the next stage starts from chunks that are already in LDS.  A
 // wave's loads complete in issue order, so "chunk t is in LDS" is "at most the
 // loads issued after chunk t are outstanding"; the chunk loop waits only when
-// the chunk is not already known to have landed.
+// the chunk is not already known to have landed.  A launch of several steps
+// runs the stream once per step: once a step's stream is consumed the counts
+// start over, and the next step's first chunks stream while its token is
+// decided.  (The per-chunk path is kept free of any step logic: each
+// instruction there is paid once per KiB streamed.)
 #define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
 #define TD_DMA_NT 2   // cache policy of the weight stream: non-temporal
 #ifndef TD_FLIGHT
@@ -479,15 +485,17 @@ DEV void rendezvous(const td_kparams& P, CState& C) {
   (void)lds_wait_ge(P, C.ctl + TD_CTL_RV, TD_NW * C.nrv, C.ok);
 }
 
-// One row of the current stage: J chunks of the stream against xin.
-DEV float gemv_row(const td_kparams& P, CState& C, const Shape& g, uint64_t& first) {
+// One row of the current stage: J chunks of the stream against xin.  The
+// format is a template parameter so that each chunk loop is compiled for one
+// format only: every instruction in it is paid once per KiB streamed.
+template <int FMT>
+DEV float gemv_row(const td_kparams& P, CState& C, int J) {
   const int lane = lane_id();
   float acc = 0.f;
-  for (int j = 0; j < g.J; ++j) {
+  for (int j = 0; j < J; ++j) {
     const uint8_t* ch = chunk_wait(C);
-    if (P.trace && !first) first = wall_clock64();
     const u32x4 w = *(const u32x4*)(ch + lane * 16);
-    if (g.fmt == 0) {
+    if (FMT == 0) {
       acc += dot_bf16(w, C.xin + j * 512 + lane * 8);
     } else {
       const float sc = f16f(*(const uint16_t*)(C.sring + C.slot * TD_SCHUNK + (lane >> 1) * 2));
@@ -496,6 +504,25 @@ DEV float gemv_row(const td_kparams& P, CState& C, const Shape& g, uint64_t& fir
     chunk_release(P, C);
   }
   return wave_sum(acc);
+}
+
+// The rows of a wave's n units (rpu rows each), their dot products to the LDS
+// output area; `first` gets the time the first chunk was in LDS (when tracing).
+template <int FMT>
+DEV void gemv_rows(const td_kparams& P, CState& C, const Shape& g, int n, int wave, uint64_t& first) {
+  if (P.trace && n > 0) {
+    (void)chunk_wait(C);
+    first = wall_clock64();
+  }
+  for (int k = 0; k < n; ++k) {
+    const int idx = wave + k * TD_NW;  // u - u0
+    const float r0 = gemv_row<FMT>(P, C, g.J);
+    const float r1 = g.rpu == 2 ? gemv_row<FMT>(P, C, g.J) : 0.f;
+    if (lane_id() == 0) {
+      C.out[idx * g.rpu] = r0;
+      if (g.rpu == 2) C.out[idx * 2 + 1] = r1;
+    }
+  }
 }
 
 // Input slice of a GEMV stage into xin: the published vector (polled), or the
@@ -547,21 +574,15 @@ DEV void stage_gemv_input(const td_kparams& P, CState& C, int wave, int kind, in
 // lane, with every store of the stage issued after its last row: a store
 // counts among the wave's outstanding loads, so a store issued between rows
 // would make every following chunk wait for it.
-DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer, uint32_t tag, float inv,
+template <int WF>
+DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer, int pos, uint32_t tag, float inv,
                    float bias_a, float bias_b, uint64_t& first) {
   const int lane = lane_id();
   const Shape g = shape_of(P, kind);
   const int u0 = C.unit_lo(g.space), u1 = C.unit_lo(g.space) + C.unit_n(g.space);
   const int n = wave_units(u1 - u0, wave);
-  for (int k = 0; k < n; ++k) {
-    const int idx = wave + k * TD_NW;  // u - u0
-    const float r0 = gemv_row(P, C, g, first);
-    const float r1 = g.rpu == 2 ? gemv_row(P, C, g, first) : 0.f;
-    if (lane == 0) {
-      C.out[idx * g.rpu] = r0;
-      if (g.rpu == 2) C.out[idx * 2 + 1] = r1;
-    }
-  }
+  if (WF == TD_WF_BF16 || kind == TD_ST_HEAD) gemv_rows<TD_WF_BF16>(P, C, g, n, wave, first);
+  else gemv_rows<TD_WF_INT4_G64>(P, C, g, n, wave, first);
   lds_fence();
   float bv = -__builtin_inff();
   int bi = 0x7fffffff, bad = 0;
@@ -595,9 +616,9 @@ DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer
         const bool isk = ra < P.qd + P.kvd;
         const int gg = (ra - P.qd - (isk ? 0 : P.kvd)) / P.d;
         const uint32_t ab = f2bf(a), bbits = f2bf(b);
-        uint16_t* row = (isk ? P.kc : P.vc) + (((size_t)layer * P.nkv + gg) * P.max_ctx + P.pos) * P.d;
-        row[i] = (uint16_t)ab;
-        row[i + half] = (uint16_t)bbits;
+        uint16_t* row = (isk ? P.kc : P.vc) + (((size_t)layer * P.nkv + gg) * P.max_ctx + pos) * P.d;
+        st_u16_sc1(row + i, ab);  // agent scope: a later step of the launch reads it on other CUs
+        st_u16_sc1(row + i + half, bbits);
         uint2* pub = P.tq + (size_t)gg * gw + (P.group + (isk ? 0 : 1)) * P.d;
         st_tag(pub + i, __uint_as_float(ab << 16), tag);
         st_tag(pub + i + half, __uint_as_float(bbits << 16), tag);
@@ -720,7 +741,39 @@ DEV void trace_rec(const td_kparams& P, int wave, int seq, uint64_t t0, uint64_t
   if (lane < 4) rec[lane] = v;
 }
 
-template <int D>
+// The wave's stream from its first chunk (ring slots and their order carry on).
+DEV void stream_start(const td_kparams& P, CState& C, int w) {
+  const td_wstream W = P.ws[w];
+  C.fbase = P.wcode + (size_t)W.code_off * TD_CHUNK;
+  C.sbase = P.wscale + (size_t)W.scale_off * TD_SCHUNK;
+  C.issued = C.t = C.lk = 0;
+}
+
+// Spins until the LDS word *p reaches `target`, topping the weight ring up
+// meanwhile (the next step's first chunks stream while its token is decided).
+// The word is read as a wave-uniform value: the loop must not look divergent
+// to the compiler, or the ring state it updates would leave scalar registers.
+DEV uint32_t lds_wait_ge_topup(const td_kparams& P, CState& C, const uint32_t* p, uint32_t target) {
+  uint32_t v = (uint32_t)uni((int)lds_ld(p));
+  if (v < target) {
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t it = 1;; ++it) {
+      topup(P, C);
+      __builtin_amdgcn_s_sleep(1);
+      v = (uint32_t)uni((int)lds_ld(p));
+      if (v >= target) break;
+      if ((it & 1023u) == 0u && uni(wait_expired(P, t0) ? 1 : 0)) {
+        C.ok = false;
+        v = 0;
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  return v;
+}
+
+template <int D, int WF>
 DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
@@ -732,14 +785,9 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   C.out = (float*)(lds + P.off_out);
   C.ring = lds + P.off_ring + wave * P.ring_slots * TD_CHUNK;
   C.sring = lds + P.off_sring + wave * P.ring_slots * TD_SCHUNK;
-  {
-    const td_wstream W = P.ws[cu * TD_NW + wave];
-    C.fbase = P.wcode + (size_t)W.code_off * TD_CHUNK;
-    C.sbase = P.wscale + (size_t)W.scale_off * TD_SCHUNK;
-    C.n_tot = W.n_tot;
-    C.n4 = W.n4;
-  }
-  C.issued = C.t = C.lk = 0;
+  stream_start(P, C, cu * TD_NW + wave);
+  C.n_tot = P.ws[cu * TD_NW + wave].n_tot;
+  C.n4 = WF == TD_WF_BF16 ? 0u : P.ws[cu * TD_NW + wave].n4;  // a constant 0 for bf16 models
   C.islot = C.slot = 0;
   C.nrv = 0;
   C.ok = true;
@@ -752,96 +800,106 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
     }
   }
   const uint32_t epoch = uni(ld_u(P.sync + TD_SY_EPOCH));
-  const uint32_t tag0 = epoch * (uint32_t)P.n_stages;  // stage seq publishes tag0 + seq + 1
   if (ld_u(P.sync + TD_SY_ABORT)) C.ok = false;
   int tok = uni(*P.token_in);
   if (tok < 0 || tok >= P.V) tok = 0;  // the sync wave reports the range error
-  const uint16_t* erow = P.embed + (size_t)tok * P.H;
-  {  // this wave's residual rows start as the embedding row; wave 0 stages the RoPE row of pos
-    const int r0 = C.unit_lo(TD_SP_H), r1 = r0 + C.unit_n(TD_SP_H);
-    for (int r = r0 + wave + lane * TD_NW; r < r1; r += 64 * TD_NW) C.own[r - r0] = bf16f(erow[r]);
-    if (wave == 0) {
-      float* cs = (float*)(lds + P.off_rope);
-      for (int i = lane; i < P.d; i += 64) cs[i] = P.rope_cs[(size_t)P.pos * P.d + i];
-    }
-  }
-  const AttnTask T = attn_task(P, cu);
   uint32_t tiles_seen = 0;
   bool first_stage = true;
-  for (int seq = 0; seq < P.n_stages; ++seq) {
-    int kind, layer;
-    stage_of(P, seq, kind, layer);
-    if (kind == TD_ST_ATTN && !T.valid) continue;
-    const uint32_t tag_in = tag0 + (uint32_t)seq, tag = tag_in + 1u;
-    uint64_t ts0 = 0, ts1 = 0, ts2 = 0;
-    if (P.trace) ts0 = wall_clock64();
-    // operands fetched ahead of the rendezvous: this slice's gains, this wave's QKV biases
-    const uint16_t* gain = kind == TD_ST_QKV ? P.gains + (size_t)(2 * layer) * P.H
-                         : kind == TD_ST_GU ? P.gains + (size_t)(2 * layer + 1) * P.H
-                         : kind == TD_ST_HEAD ? P.gains + (size_t)(2 * P.L) * P.H : nullptr;
-    uint32_t g0 = 0u, g1 = 0u, g2 = 0u, g3 = 0u;
-    if (gain) {
-      int lo, hi;
-      td_slice(P.H, wave, &lo, &hi);
-      const int u = (lo >> 1) + lane;
-      if (u < (hi >> 1)) g0 = *(const uint32_t*)(gain + 2 * u);
-      if (u + 64 < (hi >> 1)) g1 = *(const uint32_t*)(gain + 2 * (u + 64));
-      if (u + 128 < (hi >> 1)) g2 = *(const uint32_t*)(gain + 2 * (u + 128));
-      if (u + 192 < (hi >> 1)) g3 = *(const uint32_t*)(gain + 2 * (u + 192));
-    }
-    float bias_a = 0.f, bias_b = 0.f;
-    if (kind == TD_ST_QKV && P.has_bias) {
-      const int u0 = C.unit_lo(TD_SP_QKV);
-      if (lane < wave_units(C.unit_n(TD_SP_QKV), wave)) {
-        const uint16_t* bl = P.biases + (size_t)layer * P.qkv_rows;
-        const int ra = unit_row(P, TD_ST_QKV, u0 + wave + lane * TD_NW, 0);
-        bias_a = bf16f(bl[ra]);
-        bias_b = bf16f(bl[ra + (P.d >> 1)]);
+  for (int step = 0;; ++step) {
+    const int pos = P.pos + step;
+    const uint32_t tag0 = (epoch + (uint32_t)step) * (uint32_t)P.n_stages;  // stage seq publishes tag0 + seq + 1
+    const uint16_t* erow = P.embed + (size_t)tok * P.H;
+    {  // this wave's residual rows start as the embedding row; wave 0 stages the RoPE row of pos
+      const int r0 = C.unit_lo(TD_SP_H), r1 = r0 + C.unit_n(TD_SP_H);
+      for (int r = r0 + wave + lane * TD_NW; r < r1; r += 64 * TD_NW) C.own[r - r0] = bf16f(erow[r]);
+      if (wave == 0) {
+        float* cs = (float*)(lds + P.off_rope);
+        for (int i = lane; i < P.d; i += 64) cs[i] = P.rope_cs[(size_t)pos * P.d + i];
       }
     }
-    if (!first_stage) rendezvous(P, C);  // every wave is done reading the previous stage's inputs
-    first_stage = false;
-    if (kind == TD_ST_ATTN) {
-      // the kv head's block: its query heads (scaled by 1/sqrt(d)), then this position's K and V rows
-      const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
-      float* qs = (float*)(lds + P.off_attn + A.q);
-      const int nqv = P.group * P.d, nb = nqv + 2 * P.d;
-      int lo, hi;
-      td_slice(nb, wave, &lo, &hi);
-      C.ok &= poll_pairs<8>(P, P.tq + (size_t)T.g * nb, lo, hi, tag_in, qs, C);
-      lds_fence();
-      for (int i = lo + lane; i < min(hi, nqv); i += 64) qs[i] *= P.attn_scale;
-      rendezvous(P, C);
-      if (P.trace) ts1 = wall_clock64();
-      if (wave < P.group) attn_wave_d<D>(P, C, lds, wave, T, tag, tiles_seen, ts2);
-    } else {
-      const int K = kind == TD_ST_O ? P.qd : kind == TD_ST_DOWN ? P.I : P.H;
-      const uint2* src = kind == TD_ST_O ? P.to : kind == TD_ST_DOWN ? P.tact
-                       : kind == TD_ST_GU ? P.tx_mid : P.tx_out;
-      stage_gemv_input(P, C, wave, kind, K, src, kind == TD_ST_QKV && layer == 0 ? erow : nullptr, tag_in, g0, g1,
-                       g2, g3, gain);
-      rendezvous(P, C);
-      if (P.trace) ts1 = wall_clock64();
-      float inv = 1.0f;
-      if (gain) {  // norm_inv over the slices' sums of squares, in slice order
-        u32x4 a, b;
-        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-                     : "=v"(a), "=v"(b)
-                     : "v"(lds_addr(C.ctl + TD_CTL_SSQ))
-                     : "memory");
-        float ss = __uint_as_float(a.x);
-        ss += __uint_as_float(a.y);
-        ss += __uint_as_float(a.z);
-        ss += __uint_as_float(a.w);
-        ss += __uint_as_float(b.x);
-        ss += __uint_as_float(b.y);
-        ss += __uint_as_float(b.z);
-        ss += __uint_as_float(b.w);
-        inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
+    const AttnTask T = attn_task(P, cu, pos);
+    for (int seq = 0; seq < P.n_stages; ++seq) {
+      int kind, layer;
+      stage_of(P, seq, kind, layer);
+      if (kind == TD_ST_ATTN && !T.valid) continue;
+      const uint32_t tag_in = tag0 + (uint32_t)seq, tag = tag_in + 1u;
+      uint64_t ts0 = 0, ts1 = 0, ts2 = 0;
+      if (P.trace) ts0 = wall_clock64();
+      // operands fetched ahead of the rendezvous: this slice's gains, this wave's QKV biases
+      const uint16_t* gain = kind == TD_ST_QKV ? P.gains + (size_t)(2 * layer) * P.H
+                           : kind == TD_ST_GU ? P.gains + (size_t)(2 * layer + 1) * P.H
+                           : kind == TD_ST_HEAD ? P.gains + (size_t)(2 * P.L) * P.H : nullptr;
+      uint32_t g0 = 0u, g1 = 0u, g2 = 0u, g3 = 0u;
+      if (gain) {
+        int lo, hi;
+        td_slice(P.H, wave, &lo, &hi);
+        const int u = (lo >> 1) + lane;
+        if (u < (hi >> 1)) g0 = *(const uint32_t*)(gain + 2 * u);
+        if (u + 64 < (hi >> 1)) g1 = *(const uint32_t*)(gain + 2 * (u + 64));
+        if (u + 128 < (hi >> 1)) g2 = *(const uint32_t*)(gain + 2 * (u + 128));
+        if (u + 192 < (hi >> 1)) g3 = *(const uint32_t*)(gain + 2 * (u + 192));
       }
-      gemv_wave(P, C, wave, kind, layer, tag, inv, bias_a, bias_b, ts2);
+      float bias_a = 0.f, bias_b = 0.f;
+      if (kind == TD_ST_QKV && P.has_bias) {
+        const int u0 = C.unit_lo(TD_SP_QKV);
+        if (lane < wave_units(C.unit_n(TD_SP_QKV), wave)) {
+          const uint16_t* bl = P.biases + (size_t)layer * P.qkv_rows;
+          const int ra = unit_row(P, TD_ST_QKV, u0 + wave + lane * TD_NW, 0);
+          bias_a = bf16f(bl[ra]);
+          bias_b = bf16f(bl[ra + (P.d >> 1)]);
+        }
+      }
+      if (!first_stage) rendezvous(P, C);  // every wave is done reading the previous stage's inputs
+      first_stage = false;
+      if (kind == TD_ST_ATTN) {
+        // the kv head's block: its query heads (scaled by 1/sqrt(d)), then this position's K and V rows
+        const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
+        float* qs = (float*)(lds + P.off_attn + A.q);
+        const int nqv = P.group * P.d, nb = nqv + 2 * P.d;
+        int lo, hi;
+        td_slice(nb, wave, &lo, &hi);
+        C.ok &= poll_pairs<8>(P, P.tq + (size_t)T.g * nb, lo, hi, tag_in, qs, C);
+        lds_fence();
+        for (int i = lo + lane; i < min(hi, nqv); i += 64) qs[i] *= P.attn_scale;
+        rendezvous(P, C);
+        if (P.trace) ts1 = wall_clock64();
+        if (wave < P.group) attn_wave_d<D>(P, C, lds, wave, T, tag, tiles_seen, ts2);
+      } else {
+        const int K = kind == TD_ST_O ? P.qd : kind == TD_ST_DOWN ? P.I : P.H;
+        const uint2* src = kind == TD_ST_O ? P.to : kind == TD_ST_DOWN ? P.tact
+                         : kind == TD_ST_GU ? P.tx_mid : P.tx_out;
+        stage_gemv_input(P, C, wave, kind, K, src, kind == TD_ST_QKV && layer == 0 ? erow : nullptr, tag_in, g0, g1,
+                         g2, g3, gain);
+        rendezvous(P, C);
+        if (P.trace) ts1 = wall_clock64();
+        float inv = 1.0f;
+        if (gain) {  // norm_inv over the slices' sums of squares, in slice order
+          u32x4 a, b;
+          asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                       : "=v"(a), "=v"(b)
+                       : "v"(lds_addr(C.ctl + TD_CTL_SSQ))
+                       : "memory");
+          float ss = __uint_as_float(a.x);
+          ss += __uint_as_float(a.y);
+          ss += __uint_as_float(a.z);
+          ss += __uint_as_float(a.w);
+          ss += __uint_as_float(b.x);
+          ss += __uint_as_float(b.y);
+          ss += __uint_as_float(b.z);
+          ss += __uint_as_float(b.w);
+          inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
+        }
+        gemv_wave<WF>(P, C, wave, kind, layer, pos, tag, inv, bias_a, bias_b, ts2);
+      }
+      if (P.trace) trace_rec(P, wave, seq, ts0, ts1, ts2, wall_clock64());
     }
-    if (P.trace) trace_rec(P, wave, seq, ts0, ts1, ts2, wall_clock64());
+    // the step's stream is consumed (every chunk issued has been read): the
+    // next step's starts over and streams while the sync wave decides the
+    // token (and whether another step follows)
+    if (step + 1 < P.n_steps) stream_start(P, C, cu * TD_NW + wave);
+    (void)lds_wait_ge_topup(P, C, C.ctl + TD_CTL_TOKREADY, (uint32_t)step + 1u);
+    if (!C.ok || uni((int)lds_ld(C.ctl + TD_CTL_STOP))) break;
+    tok = (int)uni((int)lds_ld(C.ctl + TD_CTL_TOKEN));
   }
   vm_drain();
   if (!C.ok && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
@@ -849,9 +907,53 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
 
 // ------------------------------------------------------------ sync wave
 // Rendezvous count of the compute waves once they have staged the inputs of
-// the k-th stage they take part in (k from 0): one rendezvous per stage for the
-// staged inputs and, from the second stage on, one before staging.
-DEV uint32_t staged_target(int k) { return (uint32_t)TD_NW * (uint32_t)(2 * k + 1); }
+// the k-th stage of a step they take part in (k from 0), where `base` counts
+// the rendezvous of the earlier steps: one per stage for the staged inputs and
+// one before staging, except before the launch's very first stage.
+DEV uint32_t staged_target(uint32_t base, int k) { return (uint32_t)TD_NW * (base + (uint32_t)(2 * k + 1)); }
+
+// Waits until the pairs [0, n) of src (n even) all carry `tag` and copies their
+// values to dst[0, n) (LDS); the sync wave's form of the input poll (it has no
+// weight ring to top up).  false: the wait timed out (or another wait did).
+DEV bool poll_pairs_plain(const td_kparams& P, const uint2* src, int n, uint32_t tag, float* dst) {
+  const int lane = lane_id();
+  const int nu = n >> 1;
+  const __amdgpu_buffer_rsrc_t R = rsrc(src, (uint32_t)nu * 16u);
+  const uint64_t t0 = wall_clock64();
+  for (int b0 = 0; b0 < nu; b0 += 8 * 64) {
+    uint32_t pend = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (b0 + k * 64 + lane < nu) pend |= 1u << k;
+    for (uint32_t it = 0;; ++it) {
+      u32x4 r[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        r[k] = __builtin_amdgcn_raw_buffer_load_b128(R, (uint32_t)(b0 + k * 64 + lane) * 16u, 0, TD_CPOL_SC1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
+          const int u = b0 + k * 64 + lane;
+          dst[2 * u] = __uint_as_float(r[k].x);
+          dst[2 * u + 1] = __uint_as_float(r[k].z);
+          pend &= ~(1u << k);
+        }
+      }
+      if (!__any(pend != 0u)) break;
+      if ((it & 3u) == 3u && uni(wait_expired(P, t0) ? 1 : 0)) return false;
+    }
+  }
+  return true;
+}
+
+// (value, index) of the better greedy candidate: larger value, lower index on ties
+DEV void cand_max(float& bv, int& bi) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+}
 
 DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
   const int lane = lane_id();
@@ -863,75 +965,88 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
     const int tok = uni(*P.token_in);
     if ((tok < 0 || tok >= P.V) && lane == 0 && cu == 0) atomicOr(P.err, TD_ERRBIT_RANGE);
   }
-  const AttnTask T = attn_task(P, cu);
   const int G = P.group;
-  uint32_t tiles_ready = 0;
-  if (T.valid) load_tile(P, lds, 0, T, 0);  // layer 0's first tile
-  for (int layer = 0; T.valid && layer < P.L; ++layer) {
-    // ATTN of this layer is the (5 layer + 1)-th stage the compute waves take part in
-    (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(5 * layer + 1), ok);
-    patch_pos_row(P, lds, T, 0);
-    lds_fence();
-    lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
-    for (int tile = 1; tile < T.ntiles; ++tile) {
-      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
-      load_tile(P, lds, layer, T, tile);
-      patch_pos_row(P, lds, T, tile);
+  uint32_t tiles_ready = 0, rv_base = 0;
+  for (int step = 0;; ++step) {
+    const int pos = P.pos + step;
+    const AttnTask T = attn_task(P, cu, pos);
+    if (T.valid) load_tile(P, lds, 0, T, 0, pos);  // layer 0's first tile
+    for (int layer = 0; T.valid && layer < P.L; ++layer) {
+      // ATTN of this layer is the (5 layer + 1)-th stage the compute waves take part in
+      (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, 5 * layer + 1), ok);
+      patch_pos_row(P, lds, T, 0, pos);
       lds_fence();
       lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
-    }
-    if (layer + 1 < P.L) {
-      // the next layer's first tile, once this layer's tiles are consumed and the
-      // GU stage (whose input poll is on the critical path) has its inputs
+      for (int tile = 1; tile < T.ntiles; ++tile) {
+        (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
+        load_tile(P, lds, layer, T, tile, pos);
+        patch_pos_row(P, lds, T, tile, pos);
+        lds_fence();
+        lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
+      }
+      // the next layer's first tile (or, after the last layer, the area for the
+      // candidates), once this layer's tiles are consumed
       (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
-      (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(5 * layer + 3), ok);
-      load_tile(P, lds, layer + 1, T, 0);
+      if (layer + 1 < P.L) {
+        // ... and the GU stage (whose input poll is on the critical path) has its inputs
+        (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, 5 * layer + 3), ok);
+        load_tile(P, lds, layer + 1, T, 0, pos);
+      }
     }
-  }
-  // HEAD: the compute waves' candidates -> this CU's candidate -> the last
-  // arriving CU picks the token
-  (void)lds_wait_ge(P, ctl + TD_CTL_HEADDONE, TD_NW, ok);
-  float bv = -__builtin_inff();
-  int bi = 0x7fffffff, bad = 0;
-  if (lane < TD_NW) {
-    bv = __uint_as_float(ctl[TD_CTL_CAND + 4 * lane]);
-    bi = (int)ctl[TD_CTL_CAND + 4 * lane + 1];
-    bad = (int)ctl[TD_CTL_CAND + 4 * lane + 2];
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-  }
-  bad = __any(bad);
-  if (lane == 0) {
-    st_u(P.cand + cu * 4 + 0, __float_as_uint(bv));
-    st_u(P.cand + cu * 4 + 1, (uint32_t)bi);
-    st_u(P.cand + cu * 4 + 2, (uint32_t)bad);
-  }
-  vm_drain();
-  int last = 0;
-  if (lane == 0) last = atomicAdd(P.sync + TD_SY_FINAL, 1u) + 1u == (uint32_t)ncu;
-  if (uni(last)) {
+    rv_base += 2u * (uint32_t)(P.n_stages - (T.valid ? 0 : P.L));
+    // HEAD: the compute waves' candidates -> this CU's candidate, published;
+    // then every CU reads all CUs' candidates and takes the same token
+    (void)lds_wait_ge(P, ctl + TD_CTL_HEADDONE, (uint32_t)TD_NW * (uint32_t)(step + 1), ok);
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff, bad = 0;
+    if (lane < TD_NW) {
+      bv = __uint_as_float(ctl[TD_CTL_CAND + 4 * lane]);
+      bi = (int)ctl[TD_CTL_CAND + 4 * lane + 1];
+      bad = (int)ctl[TD_CTL_CAND + 4 * lane + 2];
+    }
+    cand_max(bv, bi);
+    bad = __any(bad);
+    const uint32_t tag = (epoch + (uint32_t)step) * (uint32_t)P.n_stages + (uint32_t)P.n_stages;
+    if (lane == 0) {
+      uint2* mine = P.cand + (size_t)cu * 4;
+      st_tag(mine + 0, __uint_as_float(__float_as_uint(bv)), tag);
+      st_tag(mine + 1, __uint_as_float((uint32_t)bi), tag);
+      st_tag(mine + 2, __uint_as_float((uint32_t)bad), tag);
+      st_tag(mine + 3, 0.f, tag);
+    }
+    float* cands = (float*)(lds + P.off_tile);  // the tiles are consumed
+    ok &= poll_pairs_plain(P, P.cand, 4 * ncu, tag, cands);
+    lds_fence();
     float fv = -__builtin_inff();
     int fi = 0x7fffffff, fbad = 0;
     for (int c = lane; c < ncu; c += 64) {
-      const float v = __uint_as_float(ld_u(P.cand + c * 4 + 0));
-      const int i = (int)ld_u(P.cand + c * 4 + 1);
-      fbad |= (int)ld_u(P.cand + c * 4 + 2);
+      const float v = cands[4 * c];
+      const int i = (int)__float_as_uint(cands[4 * c + 1]);
+      fbad |= (int)__float_as_uint(cands[4 * c + 2]);
       if (v > fv || (v == fv && i < fi)) { fv = v; fi = i; }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(fv, off);
-      const int oi = __shfl_xor(fi, off);
-      if (ov > fv || (ov == fv && oi < fi)) { fv = ov; fi = oi; }
-    }
+    cand_max(fv, fi);
     fbad = __any(fbad);
-    if (lane == 0) {
-      *P.token_out = fi == 0x7fffffff ? 0 : fi;
+    const int token = uni(fi == 0x7fffffff ? 0 : fi);
+    const bool stop = !ok || fbad || token == P.eos || step + 1 >= P.n_steps;
+    if (cu == 0 && lane == 0) {
+      *P.token_out = token;
+      if (P.tokens_out) P.tokens_out[step] = token;
       if (fbad) atomicOr(P.err, TD_ERRBIT_NONFINITE);
-      st_u(P.sync + TD_SY_FINAL, 0u);
-      st_u(P.sync + TD_SY_EPOCH, epoch + 1u);
+    }
+    lds_st(ctl + TD_CTL_TOKEN, (uint32_t)token);
+    lds_st(ctl + TD_CTL_STOP, stop ? 1u : 0u);
+    lds_fence();
+    lds_st(ctl + TD_CTL_TOKREADY, (uint32_t)step + 1u);
+    if (stop) {
+      // every CU has read the epoch: all candidates of this step carry its tag
+      if (cu == 0 && lane == 0) {
+        if (P.count_out) *P.count_out = step + 1;
+        st_u(P.sync + TD_SY_EPOCH, epoch + (uint32_t)step + 1u);
+      }
+      if (cu == 0 && P.tokens_out)
+        for (int s = step + 1 + lane; s < P.n_steps; s += 64) P.tokens_out[s] = -1;
+      break;
     }
   }
   if (!ok && lane == 0) atomicOr(P.err, TD_ERRBIT_TIMEOUT);
@@ -939,15 +1054,16 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
 
 // ------------------------------------------------------------ the kernel
 // D: the head dimension (64 or 128), a template parameter so that only one
-// attention tile routine is compiled into each kernel.
-template <int D>
+// attention tile routine is compiled into each kernel; WF: the format of the
+// layer linears (TD_WF_*), so that each chunk loop is compiled for one format.
+template <int D, int WF>
 __global__ void __launch_bounds__(TD_THREADS, 1) td_megakernel(td_kparams P) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint32_t* ctl = (uint32_t*)(lds + P.off_ctl);
   if (threadIdx.x < TD_CTL_WORDS) ctl[threadIdx.x] = 0u;
   __syncthreads();  // the only workgroup barrier: the control block is clear
   const int wave = uni((int)(threadIdx.x >> 6));
-  if (wave < TD_NW) compute_wave<D>(P, lds, wave);
+  if (wave < TD_NW) compute_wave<D, WF>(P, lds, wave);
   else sync_wave(P, lds);
 }
 
@@ -1049,18 +1165,23 @@ __global__ void __launch_bounds__(64) td_attention_kernel(const float* q, const 
 }  // namespace
 
 // ------------------------------------------------------------ launchers
-int td_megakernel_occupancy(int d, int lds_bytes, int* blocks) {
-  const void* f = d == 64 ? (const void*)td_megakernel<64> : (const void*)td_megakernel<128>;
+namespace {
+const void* megakernel_of(int d, int wf) {
+  if (d == 64) return wf ? (const void*)td_megakernel<64, 1> : (const void*)td_megakernel<64, 0>;
+  return wf ? (const void*)td_megakernel<128, 1> : (const void*)td_megakernel<128, 0>;
+}
+}  // namespace
+
+int td_megakernel_occupancy(int d, int wf, int lds_bytes, int* blocks) {
+  const void* f = megakernel_of(d, wf);
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (e == hipSuccess)
-    e = d == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, td_megakernel<64>, TD_THREADS, lds_bytes)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, td_megakernel<128>, TD_THREADS, lds_bytes);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, TD_THREADS, lds_bytes);
   return (int)e;
 }
 
 int td_launch_megakernel(const td_kparams* p, int ncu, void* stream) {
   void* args[] = {(void*)p};
-  const void* f = p->d == 64 ? (const void*)td_megakernel<64> : (const void*)td_megakernel<128>;
+  const void* f = megakernel_of(p->d, p->wf);
   return (int)hipLaunchCooperativeKernel(f, dim3(ncu), dim3(TD_THREADS), args, (unsigned)p->lds_bytes,
                                          (hipStream_t)stream);
 }

@@ -137,6 +137,33 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
 /* Device address of the context's int32 greedy-token word (valid for the ctx's life). */
 const int32_t* td_token_ptr(const td_ctx* ctx);
 
+/* Most steps one td_decode_loop call runs. */
+#define TD_MAX_LOOP_STEPS 256
+
+/*
+ * td_decode_loop: up to n_steps greedy decode steps in one launch ("Decoding in
+ * tiles", sec. 5 and Figure 10: the token loop runs inside the persistent
+ * kernel and the workers pick the token themselves).  Step s runs at position
+ * pos + s; step 0 takes the token at d_token, every later step the greedy token
+ * of the step before, decided on the device: every CU reads every CU's
+ * candidate and takes the same token, so the host never sees it.  The loop stops
+ * after n_steps steps, after a step whose token is eos_id (eos_id = -1: never),
+ * or after a step with a non-finite logit (reported by td_status as
+ * TD_E_NONFINITE).  Each step computes exactly what td_decode_step computes:
+ * the K/V rows of its position are written to `kv`, d_logits_out holds the last
+ * step's fp32 logits [vocab], td_token_ptr(ctx) its token.
+ * d_tokens_out (device int32 [n_steps], or NULL) receives the steps' tokens,
+ * -1 past the last step run; d_count_out (device int32, or NULL) the number of
+ * steps run.  Asynchronous on `stream`, no allocation.
+ * Errors (before launch): TD_E_INVALID_ARG (null ctx/kv/logits/token, kv max_ctx
+ * mismatch, n_steps outside [1, TD_MAX_LOOP_STEPS], eos_id outside [-1, vocab)),
+ * TD_E_UNSUPPORTED (the context's executor is not TD_EXEC_MEGAKERNEL),
+ * TD_E_RANGE (pos < 0 or pos + n_steps > max_ctx), TD_E_HIP.  Device-side
+ * errors as for td_decode_step, through td_status.
+ */
+int td_decode_loop(td_ctx* ctx, const int32_t* d_token, int32_t pos, int32_t n_steps, int32_t eos_id,
+                   const td_kv* kv, float* d_logits_out, int32_t* d_tokens_out, int32_t* d_count_out, void* stream);
+
 /*
  * td_status: synchronises the stream of the last td_decode_step, then returns
  * the device error word as a TD_* code (TD_OK, TD_E_NONFINITE, TD_E_RANGE,

@@ -106,5 +106,6 @@ def test_null_arguments_are_rejected():
     assert L.td_create(None, None, 0, None) == _lib.TD_E_INVALID_ARG
     kv = _lib.TdKV(k=None, v=None, max_ctx=64)
     assert L.td_decode_step(None, None, 0, ctypes.byref(kv), None, None) == _lib.TD_E_INVALID_ARG
+    assert L.td_decode_loop(None, None, 0, 4, -1, ctypes.byref(kv), None, None, None, None) == _lib.TD_E_INVALID_ARG
     assert L.td_status(None, None) == _lib.TD_E_INVALID_ARG
     L.td_destroy(None)  # a no-op
