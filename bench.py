@@ -45,8 +45,8 @@ def source_hash() -> str:
 
 
 def read_traffic(workload: str, kernel_hash: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    workload, if it was taken on the current kernel sources; else None."""
+    """HBM bytes per decode step from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"megakernel_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -58,7 +58,7 @@ def read_traffic(workload: str, kernel_hash: str):
     if vals.get("source_sha256_16") != kernel_hash:
         return None
     try:
-        return int(float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"]))
+        return int(float(vals["fetch_bytes_per_step"]) + float(vals["write_bytes_per_step"]))
     except (KeyError, ValueError):
         return None
 
@@ -100,7 +100,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (a known-size kernel for counter calibration)")
     ap.add_argument("--baseline-steps", type=int, default=32,
-                    help="timed steps of each baseline executor (per-op launches, graph replay); 0 = skip")
+                    help="timed steps of each baseline (one launch per step, per-op launches, graph replay); 0 = skip")
+    ap.add_argument("--steps-per-launch", type=int, default=64,
+                    help="greedy steps per td_decode_loop launch (1 = one td_decode_step launch per token)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -159,19 +161,29 @@ def main() -> int:
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
     tok_ptr = dec.token_ptr()
     stream = torch.cuda.current_stream()
+    spl = max(1, min(args.steps_per_launch, td._lib.TD_MAX_LOOP_STEPS))
 
-    def run(n, record):
+    def run(n, record, per_launch=spl):
+        """n greedy steps from `first` at positions start.., per_launch steps per
+        launch; with `record`, HIP events on the stream around every launch.
+        Returns [(event pair, steps in the launch, first position)]."""
         evs = []
-        for i in range(n):
+        i = 0
+        while i < n:
+            m = min(per_launch, n - i)
             src = first.data_ptr() if i == 0 else tok_ptr
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            dec.step(src, start + i, kv, logits, stream=stream)
+            if per_launch == 1:
+                dec.step(src, start + i, kv, logits, stream=stream)
+            else:
+                dec.loop(src, start + i, m, kv, logits, stream=stream)
             if record:
                 e1.record(stream)
-                evs.append((e0, e1))
+                evs.append(((e0, e1), m, start + i))
+            i += m
         return evs
 
     run(min(args.warmup, cfg.max_ctx - start), False)
@@ -196,12 +208,13 @@ def main() -> int:
     if st != 0:
         print(f"device status {st} during the timed steps", file=sys.stderr)
         return 1
-    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    total_ms = float(step_ms.sum())
+    launch_ms = np.array([a.elapsed_time(b) for (a, b), _, _ in evs])
+    total_ms = float(launch_ms.sum())
     tokens_s = n_steps / (total_ms / 1e3)
-    bytes_mean = accounting.mean_step_bytes(cfg, start, n_steps)
-    kern_ms = float(step_ms.mean())
-    achieved = bytes_mean / (kern_ms / 1e3) / 1e9
+    launch_bytes = [accounting.mean_step_bytes(cfg, p0, m) * m for _, m, p0 in evs]
+    bytes_launch = float(np.mean(launch_bytes))
+    kern_ms = float(launch_ms.mean())
+    achieved = float(np.sum(launch_bytes)) / (total_ms / 1e3) / 1e9
     if args.trace:
         from decode_persistent_megakernel_amd import trace as tdtrace
         tr = dec.enable_trace(True)
@@ -216,10 +229,21 @@ def main() -> int:
         print(tdtrace.format_summary(summ), file=sys.stderr, flush=True)
     baselines = None
     if args.baseline_steps > 0:
-        # the same fused ops launched one kernel each, and those launches captured
-        # once into a hipGraph and replayed: timed exactly like the persistent kernel
+        # the persistent kernel launched once per token (td_decode_step); the same
+        # fused ops launched one kernel each, and those launches captured once into
+        # a hipGraph and replayed: timed like the headline, per launch
         baselines = {}
         nb = min(args.baseline_steps, n_steps)
+        if spl > 1:
+            sev = run(nb, True, per_launch=1)
+            torch.cuda.synchronize()
+            if dec.status() != 0:
+                print("device status error in the single-step baseline", file=sys.stderr)
+                return 1
+            sms = np.array([a.elapsed_time(b) for (a, b), _, _ in sev])
+            baselines["single_step_launch"] = {"tokens_per_s": round(nb / (sms.sum() / 1e3), 2),
+                                               "ms_per_step": round(float(sms.mean()), 4), "steps": nb,
+                                               "launches_per_step": 1}
         for name, ex in (("per_op", td.TD_EXEC_PER_OP), ("graph", td.TD_EXEC_GRAPH)):
             bdec = td.Decoder(dm, cfg.max_ctx, executor=ex)
             bdec.step(first.data_ptr(), start, kv, logits, stream=stream)  # warm-up (and graph capture)
@@ -243,6 +267,8 @@ def main() -> int:
             del bdec
     khash = source_hash()
     traffic = read_traffic(args.config, khash)
+    if traffic is not None:
+        traffic = int(round(traffic * float(np.mean([m for _, m, _ in evs]))))  # per step -> per launch
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -268,7 +294,9 @@ def main() -> int:
                         f"{start}..{start + n_steps - 1}, batch 1",
             "weights": "int4-g64+fp16-scales" if cfg.weight_format else "bf16",
             "arithmetic": "fp32 accumulate, fp32 activations, bf16 K/V cache",
-            "executor": "persistent megakernel (one cooperative launch per token)",
+            "executor": (f"persistent megakernel, {spl} greedy steps per cooperative launch (in-kernel token loop)"
+                         if spl > 1 else "persistent megakernel (one cooperative launch per token)"),
+            "steps_per_launch": spl,
             "global_batch": 1,
             "parallelism": "single GPU",
         },
@@ -279,11 +307,12 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "td_megakernel (the whole step)",
-            "algorithmic_bytes_per_launch": int(round(bytes_mean)),
+            "kernel": f"td_megakernel ({spl} whole decode step{'s' if spl > 1 else ''} per launch)",
+            "launches": len(evs),
+            "algorithmic_bytes_per_launch": int(round(bytes_launch)),
             "kernel_ms_mean": round(kern_ms, 4),
-            "kernel_ms_p10": round(float(np.percentile(step_ms, 10)), 4),
-            "kernel_ms_p90": round(float(np.percentile(step_ms, 90)), 4),
+            "kernel_ms_p10": round(float(np.percentile(launch_ms, 10)), 4),
+            "kernel_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
             "source_sha256_16": khash,
         },
         "cpu_baseline": cpu,
