@@ -13,7 +13,9 @@
 #define TD_MAX_GROUP 8                // query heads per kv head handled by one task
 #define TD_SPIN_TICKS 100000000ull    // wait limit in 100 MHz ticks (1 s)
 #define TD_RING_MIN 4                 // fewest ring slots per compute wave the plan accepts
+#ifndef TD_RING_MAX
 #define TD_RING_MAX 24
+#endif
 
 // stage kinds, in layer order; the head follows the last layer
 enum { TD_ST_QKV = 0, TD_ST_ATTN = 1, TD_ST_O = 2, TD_ST_GU = 3, TD_ST_DOWN = 4, TD_ST_HEAD = 5 };

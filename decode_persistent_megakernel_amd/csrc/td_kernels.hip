@@ -367,10 +367,24 @@ DEV void vmcnt_rt(uint32_t n) {
     case 8: vmcnt_wait<8>(); break;
     case 9: vmcnt_wait<9>(); break;
     case 10: vmcnt_wait<10>(); break;
+    case 11: vmcnt_wait<11>(); break;
+    case 12: vmcnt_wait<12>(); break;
+    case 13: vmcnt_wait<13>(); break;
+    case 14: vmcnt_wait<14>(); break;
+    case 15: vmcnt_wait<15>(); break;
+    case 16: vmcnt_wait<16>(); break;
+    case 17: vmcnt_wait<17>(); break;
+    case 18: vmcnt_wait<18>(); break;
+    case 19: vmcnt_wait<19>(); break;
+    case 20: vmcnt_wait<20>(); break;
+    case 21: vmcnt_wait<21>(); break;
+    case 22: vmcnt_wait<22>(); break;
+    case 23: vmcnt_wait<23>(); break;
+    case 24: vmcnt_wait<24>(); break;
     default: vmcnt_wait<0>(); break;
   }
 }
-static_assert(TD_FLIGHT >= 1 && 2 * TD_FLIGHT - 2 <= 10, "vmcnt_rt covers the waits of at most TD_FLIGHT chunks");
+static_assert(TD_FLIGHT >= 1 && 4 * TD_FLIGHT <= 24, "vmcnt_rt covers the waits of up to 2 TD_FLIGHT int4 chunks");
 // Waits until no load older than chunk a is outstanding (chunks [a, issued)
 // may still be in flight).  The steady-state case, the newest TD_FLIGHT - 1
 // chunks all of one format, is one compile-time wait.
@@ -434,11 +448,14 @@ DEV void chunk_release(const td_kparams& P, CState& C) {
 // Waits until the pairs [lo, hi) of src (lo, hi even) all carry `tag` and
 // copies their values to dst[lo, hi) (LDS).  Each round loads up to W 16-byte
 // units (two pairs) per lane and re-polls the units still missing.  After a
-// round's loads are issued, the (compute) wave tops its weight ring up: those
-// chunk loads are younger than the poll's, so waiting for the poll never waits
-// for them, and every chunk issued before the round has landed once the
-// round's results are in.  false: the wait timed out (or another wait did).
-template <int W>
+// round's loads are issued, the (compute) wave tops its weight ring up (with
+// TOPUP): those chunk loads are younger than the poll's, so waiting for the
+// poll never waits for them, and every chunk issued before the round has
+// landed once the round's results are in.  Without TOPUP the CU's memory queue
+// stays short, so the next round's loads come back sooner: for a poll on the
+// critical path of only a few CUs, whose streaming is not worth the delay.
+// false: the wait timed out (or another wait did).
+template <int W, bool TOPUP = true>
 DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CState& C) {
   const int lane = lane_id();
   const int nu = (hi - lo) >> 1;
@@ -457,7 +474,7 @@ DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint3
 #pragma unroll
       for (int k = 0; k < W; ++k)
         r[k] = __builtin_amdgcn_raw_buffer_load_b128(R, (uint32_t)(b0 + k * 64 + lane) * 16u, 0, TD_CPOL_SC1);
-      topup(P, C);
+      if (TOPUP) topup(P, C);
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
@@ -700,7 +717,9 @@ DEV void attn_wave_d(const td_kparams& P, CState& C, uint8_t* lds, int h, const 
   }
   const int n = T.n_used;  // <= 64
   float* mb = (float*)(base + A.merge) + (size_t)h * (P.n_chunks_max - 1) * st;  // chunks 1..n-1
-  if (n > 1) C.ok &= poll_pairs<8>(P, myparts + st, 0, (n - 1) * st, tag, mb, C);
+  // the merging CUs (one per kv head) poll without topping up: every CU's
+  // O stage waits for their outputs
+  if (n > 1) C.ok &= poll_pairs<8, false>(P, myparts + st, 0, (n - 1) * st, tag, mb, C);
   lds_fence();
   const bool have = lane < n;
   const float* pc = mb + (have && lane > 0 ? lane - 1 : 0) * st;
