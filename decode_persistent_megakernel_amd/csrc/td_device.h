@@ -117,8 +117,9 @@ DEV float dot_bf16(u32x4 w, const float* x) {
   s = fmaf(bf_hi(w.w), b.w, s);
   return s;
 }
-// int4 chunk: lane holds 32 consecutive 4-bit codes (element 2i in the low
-// nibble of byte i), all in one scale group; weight = scale * (code - 8).
+// 8 codes of one 32-bit word (element 2i in the low nibble of byte i) against
+// the 8 matching activations; weight = scale * (code - 8), the scale applied by
+// the caller.
 DEV float dot_int4_word(uint32_t q, const float* x) {
   f32x4 a = *(const f32x4*)x;
   f32x4 b = *(const f32x4*)(x + 4);
@@ -132,12 +133,43 @@ DEV float dot_int4_word(uint32_t q, const float* x) {
   s = fmaf((float)(q >> 28) - 8.f, b.w, s);
   return s;
 }
-DEV float dot_int4(u32x4 w, const float* x, float scale) {
-  float s = dot_int4_word(w.x, x);
-  s += dot_int4_word(w.y, x + 8);
-  s += dot_int4_word(w.z, x + 16);
-  s += dot_int4_word(w.w, x + 24);
-  return s * scale;
+// int4 chunk (2048 elements of a row): lane l holds four 8-code words, word w
+// covering elements [512 w + 8 l, 512 w + 8 l + 8) (so the lanes of a wave read
+// consecutive activations, free of LDS bank conflicts), in scale group
+// 8 w + l / 8 of the chunk.  xc: the chunk's 2048 activations; sc: the lane's
+// four scales as fp16 pairs (word 0 | word 1, word 2 | word 3).
+DEV float dot_int4(u32x4 q, const float* xc, int lane, uint2 sc) {
+  const float* x = xc + lane * 8;
+  float s = f16f(sc.x) * dot_int4_word(q.x, x);
+  s = fmaf(f16f(sc.x >> 16), dot_int4_word(q.y, x + 512), s);
+  s = fmaf(f16f(sc.y), dot_int4_word(q.z, x + 1024), s);
+  s = fmaf(f16f(sc.y >> 16), dot_int4_word(q.w, x + 1536), s);
+  return s;
+}
+// Byte offset of word w of lane l inside an int4 chunk of a row-major row, and
+// the scale group (within the chunk) of that word.
+DEV int int4_word_off(int w, int lane) { return w * 256 + lane * 4; }
+DEV int int4_word_group(int w, int lane) { return w * 8 + (lane >> 3); }
+// A lane's four words of chunk j of a row-major int4 row of row_bytes bytes
+// (code 8, a zero weight, past the row's end), and their four scales from the
+// row's ngroups fp16 scales (0 past the end).
+DEV u32x4 int4_words(const uint8_t* row, int row_bytes, int j, int lane) {
+  uint32_t wd[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int off = j * 1024 + int4_word_off(w, lane);
+    wd[w] = off < row_bytes ? *(const uint32_t*)(row + off) : 0x88888888u;
+  }
+  return (u32x4){wd[0], wd[1], wd[2], wd[3]};
+}
+DEV uint2 int4_scales(const uint16_t* srow, int ngroups, int j, int lane) {
+  uint32_t h[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int g = j * 32 + int4_word_group(w, lane);
+    h[w] = g < ngroups ? srow[g] : 0u;
+  }
+  return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
 // ------------------------------------------------------------ attention tile

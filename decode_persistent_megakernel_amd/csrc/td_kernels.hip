@@ -515,8 +515,8 @@ DEV float gemv_row(const td_kparams& P, CState& C, int J) {
     if (FMT == 0) {
       acc += dot_bf16(w, C.xin + j * 512 + lane * 8);
     } else {
-      const float sc = f16f(*(const uint16_t*)(C.sring + C.slot * TD_SCHUNK + (lane >> 1) * 2));
-      acc += dot_int4(w, C.xin + j * 2048 + lane * 32, sc);
+      const uint2 sc = *(const uint2*)(C.sring + C.slot * TD_SCHUNK + (lane >> 3) * 8);
+      acc += dot_int4(w, C.xin + j * 2048, lane, sc);
     }
     chunk_release(P, C);
   }
@@ -1107,23 +1107,29 @@ __global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, u
   while (c.seq < P.n_stages && n < W.n_tot) {
     const int u = c.u_first + c.k * TD_NW;
     const int row = unit_row(P, c.g.kind, u, c.r);
-    const int boff = c.j * TD_CHUNK + lane * 16;
+    const uint8_t* rp = c.g.w + (size_t)row * c.g.row_bytes;
     u32x4 v;
-    if (boff < c.g.row_bytes) {
-      v = *(const u32x4*)(c.g.w + (size_t)row * c.g.row_bytes + boff);
-    } else {
-      const uint32_t z = c.g.fmt ? 0x88888888u : 0u;
-      v = (u32x4){z, z, z, z};
+    if (c.g.fmt == 0) {
+      const int boff = c.j * TD_CHUNK + lane * 16;
+      v = boff < c.g.row_bytes ? *(const u32x4*)(rp + boff) : (u32x4){0u, 0u, 0u, 0u};
+    } else {  // the lane's four words, from their places in the row (zero weights past its end)
+      uint32_t wd[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int boff = c.j * TD_CHUNK + int4_word_off(w, lane);
+        wd[w] = boff < c.g.row_bytes ? *(const uint32_t*)(rp + boff) : 0x88888888u;
+      }
+      v = (u32x4){wd[0], wd[1], wd[2], wd[3]};
     }
     *(u32x4*)(dst + lane * 16) = v;
     dst += TD_CHUNK;
     if (c.g.fmt == 1) {
       if (n4 >= W.n4) break;
-      if (lane < 16) {
-        const int si = c.j * 32 + lane * 2;
-        uint32_t sv = 0;
-        if (si < c.g.K / 64) sv = *(const uint32_t*)(c.g.s + (size_t)row * (c.g.K / 64) + si);
-        *(uint32_t*)(sdst + lane * 4) = sv;
+      if (lane < 32) {  // block position 4 (l / 8) + w holds the scale of word w of lanes l
+        const int g = c.j * 32 + int4_word_group(lane & 3, (lane >> 2) * 8);
+        uint16_t sv = 0;
+        if (g < c.g.K / 64) sv = c.g.s[(size_t)row * (c.g.K / 64) + g];
+        *(uint16_t*)(sdst + lane * 2) = sv;
       }
       sdst += TD_SCHUNK;
       ++n4;
@@ -1145,15 +1151,12 @@ __global__ void __launch_bounds__(256) td_gemv_kernel(int fmt, const uint8_t* w,
   const int J = (row_bytes + TD_CHUNK - 1) / TD_CHUNK;
   float acc = 0.f;
   for (int j = 0; j < J; ++j) {
-    const int boff = j * TD_CHUNK + lane * 16;
-    if (boff < row_bytes) {
-      const u32x4 wv = *(const u32x4*)(w + (size_t)row * row_bytes + boff);
-      if (fmt == 0) {
-        acc += dot_bf16(wv, x + j * 512 + lane * 8);
-      } else {
-        const int si = (j * 2048 + lane * 32) / 64;
-        acc += dot_int4(wv, x + j * 2048 + lane * 32, f16f(s[(size_t)row * (cols / 64) + si]));
-      }
+    if (fmt == 0) {
+      const int boff = j * TD_CHUNK + lane * 16;
+      if (boff < row_bytes) acc += dot_bf16(*(const u32x4*)(w + (size_t)row * row_bytes + boff), x + j * 512 + lane * 8);
+    } else {
+      acc += dot_int4(int4_words(w + (size_t)row * row_bytes, row_bytes, j, lane), x + j * 2048, lane,
+                      int4_scales(s + (size_t)row * (cols / 64), cols / 64, j, lane));
     }
   }
   const float r = wave_sum(acc);

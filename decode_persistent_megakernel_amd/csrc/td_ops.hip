@@ -77,22 +77,20 @@ DEV float op_row(int fmt, const uint8_t* w, const uint16_t* s, int row, int K, c
     u32x4 c[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int boff = (j0 + u) * TD_CHUNK + lane * 16;
-      const uint32_t z = fmt ? 0x88888888u : 0u;
-      c[u] = (j0 + u < J && boff < row_bytes) ? __builtin_nontemporal_load((const u32x4*)(rp + boff))
-                                              : (u32x4){z, z, z, z};
+      if (fmt == 0) {
+        const int boff = (j0 + u) * TD_CHUNK + lane * 16;
+        c[u] = (j0 + u < J && boff < row_bytes) ? __builtin_nontemporal_load((const u32x4*)(rp + boff))
+                                                : (u32x4){0u, 0u, 0u, 0u};
+      } else {
+        c[u] = int4_words(rp, row_bytes, j0 + u, lane);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + u;
       if (j >= J) break;
-      if (fmt == 0) {
-        acc += dot_bf16(c[u], xs + j * 512 + lane * 8);
-      } else {
-        const int si = j * 32 + (lane >> 1);
-        const float sc = si < K / 64 ? f16f(s[(size_t)row * (K / 64) + si]) : 0.f;
-        acc += dot_int4(c[u], xs + j * 2048 + lane * 32, sc);
-      }
+      if (fmt == 0) acc += dot_bf16(c[u], xs + j * 512 + lane * 8);
+      else acc += dot_int4(c[u], xs + j * 2048, lane, int4_scales(s + (size_t)row * (K / 64), K / 64, j, lane));
     }
   }
   return wave_sum(acc);
