@@ -313,11 +313,16 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const int qd = nq * d, kvd = nkv * d, qkv_rows = qd + 2 * kvd;
 
   // attention split: at most one task per CU, chunks a multiple of the tile,
-  // at most 64 chunks per kv head, and the merge staging within 24 KiB of LDS
+  // at most 64 chunks per kv head, and the merge staging within the LDS the
+  // GEMV input area already takes (the attention area aliases it), at least
+  // 24 KiB: more chunks mean fewer tiles per CU, which a CU runs one by one
   const int cmax_by_cu = ncu / nkv;
   int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
   auto n_chunks_of = [&](int cl) { return (c.max_ctx + cl - 1) / cl; };
-  while (n_chunks_of(chunk_len) > 64 || (int64_t)n_chunks_of(chunk_len) * group * (d + 4) * 4 > 24 * 1024)
+  const int64_t kpad_in = round_up(std::max({H, qd, I}), 2048);
+  const int64_t merge_budget =
+      std::max<int64_t>(24 * 1024, kpad_in * 4 - ((int64_t)group * d * 4 + 2 * d * 4 + (int64_t)group * TD_TILE * 4));
+  while (n_chunks_of(chunk_len) > 64 || (int64_t)n_chunks_of(chunk_len) * group * (d + 4) * 4 > merge_budget)
     chunk_len += TD_TILE;
   const int n_chunks_max = n_chunks_of(chunk_len);
   if (n_chunks_max * nkv > ncu) return fail(TD_E_PLAN, "attention split exceeds the CU count");
@@ -344,12 +349,17 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const int64_t lds_cap = std::min<int64_t>((int64_t)prop.maxSharedMemoryPerMultiProcessor, 160 * 1024);
   td_kparams kp{};
   int64_t fixed = 0;
-  {
+  const int64_t per_slot = (int64_t)TD_NW * (TD_CHUNK + (c.weight_format == TD_WF_INT4_G64 ? TD_SCHUNK : 0));
+  // a second K/V tile buffer (the next tile loads while one is consumed) when a
+  // chunk spans several tiles and the rings keep at least TD_RING_MIN2 slots
+  kp.tile_stride = (int32_t)round_up(td_tile_bytes(d), 256);
+  kp.tile_bufs = 1;
+  for (int nb = 2; nb >= 1; --nb) {
     int64_t off = 0;
     kp.off_xin = kp.off_attn = (int32_t)off;
     off += round_up(xin_bytes, 1024);
     kp.off_tile = (int32_t)off;
-    off += round_up(td_tile_bytes(d), 256);
+    off += (int64_t)nb * kp.tile_stride;
     kp.off_own = (int32_t)off;
     off += (int64_t)own_floats * 4;
     kp.off_out = (int32_t)off;
@@ -359,8 +369,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     kp.off_ctl = (int32_t)off;
     off += TD_CTL_WORDS * 4;
     fixed = round_up(off, 1024);
+    kp.tile_bufs = nb;
+    if (nb == 1 || (chunk_len > TD_TILE && (lds_cap - fixed) / per_slot >= TD_RING_MIN2)) break;
   }
-  const int64_t per_slot = (int64_t)TD_NW * (TD_CHUNK + (c.weight_format == TD_WF_INT4_G64 ? TD_SCHUNK : 0));
   const int64_t ring = std::min<int64_t>(TD_RING_MAX, (lds_cap - fixed) / per_slot);
   if (ring < TD_RING_MIN) return fail(TD_E_UNSUPPORTED, "the LDS cannot hold the weight rings for this shape");
   {

@@ -13,6 +13,7 @@
 #define TD_MAX_GROUP 8                // query heads per kv head handled by one task
 #define TD_SPIN_TICKS 100000000ull    // wait limit in 100 MHz ticks (1 s)
 #define TD_RING_MIN 4                 // fewest ring slots per compute wave the plan accepts
+#define TD_RING_MIN2 9                // fewest ring slots with which a second attention tile buffer is taken
 #ifndef TD_RING_MAX
 #define TD_RING_MAX 24
 #endif
@@ -105,6 +106,7 @@ struct td_kparams {
   const uint16_t* biases;  // ctx copy of the QKV biases, bf16 [L][qkv_rows], or null
   // LDS layout (byte offsets into dynamic shared memory)
   int32_t off_ring, off_sring, off_xin, off_attn, off_tile, off_own, off_out, off_rope, off_ctl;
+  int32_t tile_bufs, tile_stride;  // attention K/V tile buffers (1 or 2) and their spacing in bytes
   int32_t lds_bytes;
   int32_t n_stages;   // 5 L + 1
   int32_t ring_slots; // S: LDS ring slots per compute wave

@@ -248,11 +248,17 @@ DEV AttnTask attn_task(const td_kparams& P, int cu, int pos) {
   return t;
 }
 
+// LDS buffer of the k-th tile made ready (counted over the whole launch): with
+// two buffers the next tile loads while the current one is consumed.
+DEV uint8_t* tile_buf(const td_kparams& P, uint8_t* lds, uint32_t k) {
+  return lds + P.off_tile + (P.tile_bufs > 1 ? (int)(k & 1u) * P.tile_stride : 0);
+}
+
 // K and V rows [tb, tb + nv) of the tile, except row pos (written during this
 // very step; it comes from the published copy), into the LDS tile; rows past
 // the chunk end read as zero.  The loads are agent-scope: rows written by an
 // earlier step of the same launch come from other CUs.
-DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask& T, int tile, int pos) {
+DEV void load_tile(const td_kparams& P, uint8_t* buf, int layer, const AttnTask& T, int tile, int pos) {
   const int lane = lane_id();
   const int d = P.d;
   const int tb = T.t0 + tile * TD_TILE;
@@ -260,20 +266,20 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
   const size_t head_off = ((size_t)layer * P.nkv + T.g) * P.max_ctx;
   const __amdgpu_buffer_rsrc_t RK = rsrc(P.kc + (head_off + tb) * d, (uint32_t)(nv * d * 2));
   const __amdgpu_buffer_rsrc_t RV = rsrc(P.vc + (head_off + tb) * d, (uint32_t)(nv * d * 2));
-  uint16_t* kt = (uint16_t*)(lds + P.off_tile);
+  uint16_t* kt = (uint16_t*)buf;
   uint16_t* vt = kt + TD_TILE * (d + 8);
   const int q16 = d / 8;  // 16-byte pieces per row
   const int npiece = TD_TILE * q16;
-  for (int i0 = 0; i0 < npiece; i0 += 4 * 64) {
-    u32x4 kr[4], vr[4];
+  for (int i0 = 0; i0 < npiece; i0 += 8 * 64) {  // 8 K and 8 V loads in flight per lane (d = 64: one round)
+    u32x4 kr[8], vr[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       const uint32_t off = (uint32_t)(i0 + k * 64 + lane) * 16u;  // out of range reads 0
       kr[k] = __builtin_amdgcn_raw_buffer_load_b128(RK, off, 0, TD_CPOL_SC1);
       vr[k] = __builtin_amdgcn_raw_buffer_load_b128(RV, off, 0, TD_CPOL_SC1);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       const int i = i0 + k * 64 + lane;
       if (i < npiece) {
         const int row = i / q16, pc = i - row * q16;
@@ -288,13 +294,13 @@ DEV void load_tile(const td_kparams& P, uint8_t* lds, int layer, const AttnTask&
 
 // this position's K and V rows (LDS fp32 holding bf16 values) into the tile
 // when the tile holds position pos
-DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, const AttnTask& T, int tile, int pos) {
+DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, uint8_t* buf, const AttnTask& T, int tile, int pos) {
   const int tb = T.t0 + tile * TD_TILE;
   if (pos < tb || pos >= tb + TD_TILE || pos >= T.t1) return;
   const int d = P.d, row = pos - tb;
   const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max);
   const float* kvp = (const float*)(lds + P.off_attn + A.kvp);
-  uint16_t* kt = (uint16_t*)(lds + P.off_tile);
+  uint16_t* kt = (uint16_t*)buf;
   uint16_t* vt = kt + TD_TILE * (d + 8);
   for (int e = lane_id(); e < d; e += 64) {
     kt[row * (d + 8) + e] = (uint16_t)(__float_as_uint(kvp[e]) >> 16);
@@ -684,12 +690,12 @@ DEV void attn_wave_d(const td_kparams& P, CState& C, uint8_t* lds, int h, const 
   const td_attn_lds A = td_attn_layout(D, G, P.n_chunks_max);
   uint8_t* base = lds + P.off_attn;
   const float* qs = (const float*)(base + A.q) + h * D;
-  const uint16_t* kt = (const uint16_t*)(lds + P.off_tile);
-  const uint16_t* vt = kt + TD_TILE * (D + 8);
   float* ps = (float*)(base + A.p) + h * TD_TILE;
   float m = -__builtin_inff(), l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int tile = 0; tile < T.ntiles; ++tile) {
+    const uint16_t* kt = (const uint16_t*)tile_buf(P, lds, tiles_seen);
+    const uint16_t* vt = kt + TD_TILE * (D + 8);
     (void)lds_wait_ge(P, C.ctl + TD_CTL_TREADY, ++tiles_seen, C.ok);
     attn_tile<D>(qs, kt, vt, ps, min(TD_TILE, T.t1 - (T.t0 + tile * TD_TILE)), m, l, acc);
     lds_fence();
@@ -989,29 +995,37 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
   for (int step = 0;; ++step) {
     const int pos = P.pos + step;
     const AttnTask T = attn_task(P, cu, pos);
-    if (T.valid) load_tile(P, lds, 0, T, 0, pos);  // layer 0's first tile
+    // a tile's buffer is free once the tile tile_bufs places earlier is consumed
+    const uint32_t nb = (uint32_t)P.tile_bufs;
+    auto buf_free = [&](uint32_t k) { return (uint32_t)G * (k + 1u > nb ? k + 1u - nb : 0u); };
+    if (T.valid) {  // layer 0's first tile
+      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
+      load_tile(P, tile_buf(P, lds, tiles_ready), 0, T, 0, pos);
+    }
     for (int layer = 0; T.valid && layer < P.L; ++layer) {
       // ATTN of this layer is the (5 layer + 1)-th stage the compute waves take part in
       (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, 5 * layer + 1), ok);
-      patch_pos_row(P, lds, T, 0, pos);
+      patch_pos_row(P, lds, tile_buf(P, lds, tiles_ready), T, 0, pos);
       lds_fence();
       lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
       for (int tile = 1; tile < T.ntiles; ++tile) {
-        (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
-        load_tile(P, lds, layer, T, tile, pos);
-        patch_pos_row(P, lds, T, tile, pos);
+        (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
+        uint8_t* b = tile_buf(P, lds, tiles_ready);
+        load_tile(P, b, layer, T, tile, pos);
+        patch_pos_row(P, lds, b, T, tile, pos);
         lds_fence();
         lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
       }
-      // the next layer's first tile (or, after the last layer, the area for the
-      // candidates), once this layer's tiles are consumed
-      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
       if (layer + 1 < P.L) {
-        // ... and the GU stage (whose input poll is on the critical path) has its inputs
+        // the next layer's first tile once its buffer is free and the GU stage
+        // (whose input poll is on the critical path) has its inputs
+        (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
         (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, 5 * layer + 3), ok);
-        load_tile(P, lds, layer + 1, T, 0, pos);
+        load_tile(P, tile_buf(P, lds, tiles_ready), layer + 1, T, 0, pos);
       }
     }
+    // every tile consumed: the tile area takes the candidates below
+    (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, (uint32_t)G * tiles_ready, ok);
     rv_base += 2u * (uint32_t)(P.n_stages - (T.valid ? 0 : P.L));
     // HEAD: the compute waves' candidates -> this CU's candidate, published;
     // then every CU reads all CUs' candidates and takes the same token
