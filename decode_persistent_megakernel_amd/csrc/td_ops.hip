@@ -67,7 +67,8 @@ DEV int op_kpad(int K, int fmt) {
 // One row of a stored linear against xs (LDS): the chunk loop of the
 // persistent kernel, reading the row's chunks straight from the caller's
 // row-major weights (a chunk column past the row end reads as zero weights).
-DEV float op_row(int fmt, const uint8_t* w, const uint16_t* s, int row, int K, const float* xs) {
+template <int fmt>
+DEV float op_row_f(const uint8_t* w, const uint16_t* s, int row, int K, const float* xs) {
   const int lane = lane_id();
   const int row_bytes = fmt == 0 ? K * 2 : K / 2;
   const int J = (row_bytes + TD_CHUNK - 1) / TD_CHUNK;
@@ -94,6 +95,11 @@ DEV float op_row(int fmt, const uint8_t* w, const uint16_t* s, int row, int K, c
     }
   }
   return wave_sum(acc);
+}
+
+// the format as a template parameter: each chunk loop is compiled for one format
+DEV float op_row(int fmt, const uint8_t* w, const uint16_t* s, int row, int K, const float* xs) {
+  return fmt ? op_row_f<1>(w, s, row, K, xs) : op_row_f<0>(w, s, row, K, xs);
 }
 
 DEV int op_unit_row_qkv(const td_opparams& P, int u, int r) {
