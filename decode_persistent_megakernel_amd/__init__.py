@@ -144,6 +144,16 @@ class Decoder:
                                              _ptr(logits), _ptr(tokens), _ptr(count), _stream_handle(stream)),
                    "td_decode_loop")
 
+    def forward_block(self, tokens, pos0: int, kv: KVCache, logits, all_logits: bool = False, argmax=None,
+                      stream=None) -> None:
+        """len(tokens) consecutive tokens at positions pos0.. in one pass (td_forward_block);
+        `tokens` is an int32 device tensor, `logits` float32 [vocab] (or [n][vocab] with
+        all_logits), `argmax` an optional int32 device tensor ([n] with all_logits, else [1])."""
+        kvs = kv.td_kv()
+        _lib.check(_lib.lib().td_forward_block(self._h, _ptr(tokens), int(tokens.numel()), int(pos0),
+                                               ctypes.byref(kvs), _ptr(logits), int(bool(all_logits)), _ptr(argmax),
+                                               _stream_handle(stream)), "td_forward_block")
+
     def status(self) -> int:
         err = ctypes.c_int32(0)
         return int(_lib.lib().td_status(self._h, ctypes.byref(err)))

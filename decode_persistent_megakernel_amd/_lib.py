@@ -25,9 +25,10 @@ TD_EXEC_PER_OP = 1
 TD_EXEC_GRAPH = 2
 
 TD_MAX_LOOP_STEPS = 256
+TD_MAX_BLOCK = 64
 
 EXPORTED = [
-    "td_create", "td_decode_step", "td_decode_loop", "td_token_ptr", "td_status", "td_destroy", "td_strerror", "td_last_error",
+    "td_create", "td_decode_step", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_status", "td_destroy", "td_strerror", "td_last_error",
     "td_test_gemv", "td_test_attention", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
 ]
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.td_decode_step.argtypes = [vp, vp, i32, ctypes.POINTER(TdKV), vp, vp]
         L.td_decode_loop.restype = i32
         L.td_decode_loop.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(TdKV), vp, vp, vp, vp]
+        L.td_forward_block.restype = i32
+        L.td_forward_block.argtypes = [vp, vp, i32, i32, ctypes.POINTER(TdKV), vp, i32, vp, vp]
         L.td_token_ptr.restype = vp
         L.td_token_ptr.argtypes = [vp]
         L.td_status.restype = i32

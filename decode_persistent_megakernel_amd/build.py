@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 SO = os.path.join(PKG, "libtd.so")
 BENCH = os.path.join(PKG, "td_bench")
 SYNTH_DIR = os.path.join(ROOT, "synth")
-SOURCES = ["td_kernels.hip", "td_ops.hip", "td_api.cpp"]
+SOURCES = ["td_kernels.hip", "td_ops.hip", "td_block.hip", "td_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
          # packed fp32 instructions stay off: ordinary float code only

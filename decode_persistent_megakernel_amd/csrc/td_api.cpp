@@ -64,6 +64,10 @@ struct td_ctx {
   const void* g_kc = nullptr;  // the K/V cache and logits the captured graph was made for
   const void* g_vc = nullptr;
   const void* g_logits = nullptr;
+  // block forward (td_forward_block): workspace and the layer pointers on the host
+  void* blockbuf = nullptr;
+  td_blockparams blk{};
+  std::vector<td_layer_dev> layers_host;
 };
 
 namespace {
@@ -572,11 +576,50 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   kp.gains = (const uint16_t*)(base + o_gains);
   kp.biases = c.qkv_bias ? (const uint16_t*)(base + o_bias) : nullptr;
 
+  // block forward workspace: TD_MAX_BLOCK rows of every activation it keeps
+  {
+    const size_t R = TD_MAX_BLOCK, ymax = (size_t)std::max(qkv_rows, 2 * I);
+    // split-K slices: the O and down projections always write slices (one when unsplit), the
+    // others only when split
+    size_t part_floats = 0;
+    const int gem[5][3] = {{qkv_rows, H, 0}, {H, qd, 1}, {2 * I, H, 0}, {H, I, 1}, {V, H, 0}};
+    for (const auto& g : gem) {
+      int KS = 0;
+      const int S = td_block_split(g[0], g[1], ncu, &KS);
+      if (S > 1 || g[2]) part_floats = std::max(part_floats, (size_t)S * R * g[0]);
+    }
+    size_t bo = 0;
+    auto btake = [&](size_t bytes) {
+      size_t o = bo;
+      bo += (size_t)round_up((int64_t)bytes, 256);
+      return o;
+    };
+    const size_t b_x = btake(R * H * 4), b_xn = btake(R * H * 4), b_act = btake(R * I * 4);
+    const size_t b_part = btake(part_floats * 4);
+    const size_t b_y = btake(R * ymax * 4), b_q = btake(R * qd * 4), b_ao = btake(R * qd * 4);
+    e = hipMalloc(&ctx->blockbuf, bo);
+    if (e != hipSuccess) {
+      (void)hipFree(ctx->scratch);
+      delete ctx;
+      return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of the block workspace failed")
+                                      : hip_fail(e, "hipMalloc");
+    }
+    uint8_t* bb = (uint8_t*)ctx->blockbuf;
+    ctx->blk.ncu = ncu;
+    ctx->blk.x = (float*)(bb + b_x);
+    ctx->blk.xn = (float*)(bb + b_xn);
+    ctx->blk.act = (float*)(bb + b_act);
+    ctx->blk.part = (float*)(bb + b_part);
+    ctx->blk.y = (float*)(bb + b_y);
+    ctx->blk.q = (float*)(bb + b_q);
+    ctx->blk.ao = (float*)(bb + b_ao);
+    ctx->layers_host = layers;
+  }
+
   if (executor != TD_EXEC_MEGAKERNEL) {
     int rc2 = setup_per_op(ctx, kp);
     if (rc2) {
-      (void)hipFree(ctx->scratch);
-      delete ctx;
+      td_destroy(ctx);
       return rc2;
     }
     ctx->kp = kp;
@@ -589,8 +632,8 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   ctx->wstream_bytes = code_bytes + (size_t)stream_scale_blocks * TD_SCHUNK + TD_CHUNK;
   e = hipMalloc(&ctx->wstream, ctx->wstream_bytes);
   if (e != hipSuccess) {
-    (void)hipFree(ctx->scratch);
-    delete ctx;
+    ctx->wstream = nullptr;
+    td_destroy(ctx);
     return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of the weight streams failed")
                                     : hip_fail(e, "hipMalloc");
   }
@@ -602,9 +645,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   if (le == 0) e = hipDeviceSynchronize();
   if (le == 0 && e == hipSuccess) e = hipMemcpy(&bad, base + o_bad, 4, hipMemcpyDeviceToHost);
   if (le != 0 || e != hipSuccess || bad) {
-    (void)hipFree(ctx->wstream);
-    (void)hipFree(ctx->scratch);
-    delete ctx;
+    td_destroy(ctx);
     if (le) return hip_fail((hipError_t)le, "repack launch");
     if (e != hipSuccess) return hip_fail(e, "repack");
     return fail(TD_E_PLAN, "packed weight stream disagrees with the plan");
@@ -694,6 +735,31 @@ int td_decode_loop(td_ctx* ctx, const int32_t* d_token, int32_t pos, int32_t n_s
   return TD_OK;
 }
 
+int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t pos0, const td_kv* kv,
+                     float* d_logits_out, int32_t all_logits, int32_t* d_argmax_out, void* stream) {
+  if (!ctx || !d_tokens || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
+  if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (n < 1 || n > TD_MAX_BLOCK) return fail(TD_E_INVALID_ARG, "n outside [1, TD_MAX_BLOCK]");
+  if (pos0 < 0 || (int64_t)pos0 + n > ctx->cfg.max_ctx) return fail(TD_E_RANGE, "positions outside [0, max_ctx)");
+  td_kparams p = ctx->kp;
+  p.kc = (uint16_t*)kv->k;
+  p.vc = (uint16_t*)kv->v;
+  td_blockparams B = ctx->blk;
+  B.kp = &p;
+  B.layers_host = ctx->layers_host.data();
+  hipStream_t s = (hipStream_t)stream;
+  if (ctx->timing) (void)hipEventRecord(ctx->ev0, s);
+  const int le = td_launch_block(&B, d_tokens, n, pos0, all_logits ? 1 : 0, d_logits_out, d_argmax_out, stream);
+  if (le != 0) return hip_fail((hipError_t)le, "block launch");
+  if (ctx->timing) {
+    (void)hipEventRecord(ctx->ev1, s);
+    ctx->timed = true;
+  }
+  ctx->last_stream = s;
+  ctx->launched = true;
+  return TD_OK;
+}
+
 int td_status(td_ctx* ctx, int32_t* device_error) {
   if (!ctx) return fail(TD_E_INVALID_ARG, "null ctx");
   hipError_t e = hipStreamSynchronize(ctx->last_stream);
@@ -724,6 +790,7 @@ void td_destroy(td_ctx* ctx) {
   if (ctx->scratch) (void)hipFree(ctx->scratch);
   if (ctx->wstream) (void)hipFree(ctx->wstream);
   if (ctx->opbuf) (void)hipFree(ctx->opbuf);
+  if (ctx->blockbuf) (void)hipFree(ctx->blockbuf);
   delete ctx;
 }
 

@@ -17,8 +17,14 @@
 // --loop N runs the steps through td_decode_loop, N greedy steps per launch
 // (the last launch takes the remainder), instead of one td_decode_step each.
 //
-//   td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--loop N] [--copy-calibration]
-//            [--print-config]
+// --block N fills the prompt through td_forward_block, N tokens per call,
+// instead of one decode step per token, and times that prefill (one untimed
+// pass, then three timed passes over the same positions) on its own JSON line.
+// A workload with a random cache prefix and no prompt times one block of N
+// tokens at the first decode position instead (the shape of a draft verify).
+//
+//   td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--loop N] [--block N]
+//            [--copy-calibration] [--print-config]
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -135,7 +141,7 @@ int main(int argc, char** argv) {
   std::string name = "llama1b";
   int steps = 128, warmup = 8;
   bool only_config = false, copy_cal = false;
-  int loop_n = 0;
+  int loop_n = 0, block_n = 0;
   int executor = TD_EXEC_MEGAKERNEL;
   std::string ex_name = "megakernel";
   for (int i = 1; i < argc; ++i) {
@@ -146,6 +152,7 @@ int main(int argc, char** argv) {
     else if (a == "--print-config") only_config = true;
     else if (a == "--copy-calibration") copy_cal = true;
     else if (a == "--loop" && i + 1 < argc) loop_n = atoi(argv[++i]);
+    else if (a == "--block" && i + 1 < argc) block_n = atoi(argv[++i]);
     else if (a == "--executor" && i + 1 < argc) {
       ex_name = argv[++i];
       if (ex_name == "megakernel") executor = TD_EXEC_MEGAKERNEL;
@@ -158,7 +165,7 @@ int main(int argc, char** argv) {
     }
     else {
       fprintf(stderr, "usage: td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--loop N] "
-                      "[--copy-calibration] [--print-config]\n");
+                      "[--block N] [--copy-calibration] [--print-config]\n");
       return 2;
     }
   }
@@ -175,6 +182,10 @@ int main(int argc, char** argv) {
     return 0;
   }
   const int start = w.prompt + w.kv_prefix;
+  if (block_n < 0 || block_n > TD_MAX_BLOCK) {
+    fprintf(stderr, "td_bench: --block takes 1..%d\n", TD_MAX_BLOCK);
+    return 2;
+  }
   if (steps < 1 || warmup < 0 || start + steps > w.max_ctx || start + warmup > w.max_ctx) {
     fprintf(stderr, "td_bench: steps/warmup do not fit the cache (%d positions after the prefix)\n",
             w.max_ctx - start);
@@ -250,8 +261,52 @@ int main(int argc, char** argv) {
   g_allocs.push_back(logits);
   g_allocs.push_back(tok);
 
-  // the prompt through the decode step (or the first token after a random prefix)
-  if (w.prompt) {
+  // the prompt in blocks (timed), through the decode step, or the first token after a random prefix
+  if (block_n > 0) {
+    const int n_tok = w.prompt ? w.prompt : block_n;
+    const int p0 = w.prompt ? 0 : start;
+    if (p0 + n_tok > w.max_ctx) {
+      fprintf(stderr, "td_bench: the block does not fit the cache\n");
+      return 2;
+    }
+    std::vector<int32_t> toks(n_tok);
+    if (w.prompt) synth_fill_i32_uniform(toks.data(), n_tok, synth_key(w.seed, -1, "prompt"), w.vocab);
+    else synth_fill_i32_uniform(toks.data(), n_tok, synth_key(w.seed, -1, "block"), w.vocab);
+    int32_t* d_toks = nullptr;
+    CK(hipMalloc(&d_toks, (size_t)n_tok * 4));
+    g_allocs.push_back(d_toks);
+    CK(hipMemcpy(d_toks, toks.data(), (size_t)n_tok * 4, hipMemcpyHostToDevice));
+    auto pass = [&]() {
+      for (int i = 0; i < n_tok; i += block_n)
+        TD(td_forward_block(ctx, d_toks + i, std::min(block_n, n_tok - i), p0 + i, &kv, logits, 0, nullptr, stream));
+    };
+    pass();
+    CK(hipStreamSynchronize(stream));
+    TD(td_status(ctx, nullptr));
+    hipEvent_t b0, b1;
+    CK(hipEventCreate(&b0));
+    CK(hipEventCreate(&b1));
+    const int reps = 3;
+    CK(hipEventRecord(b0, stream));
+    for (int r = 0; r < reps; ++r) pass();
+    CK(hipEventRecord(b1, stream));
+    CK(hipStreamSynchronize(stream));
+    TD(td_status(ctx, nullptr));
+    float ms = 0.f;
+    CK(hipEventElapsedTime(&ms, b0, b1));
+    ms /= reps;
+    printf("{\"workload\": \"%s\", \"block_rows\": %d, \"tokens\": %d, \"positions\": [%d, %d], "
+           "\"ms_per_pass\": %.4f, \"tokens_per_s\": %.1f}\n",
+           w.name, block_n, n_tok, p0, p0 + n_tok - 1, ms, n_tok / (ms / 1e3));
+    fflush(stdout);
+    CK(hipEventDestroy(b0));
+    CK(hipEventDestroy(b1));
+    if (!w.prompt) {
+      int32_t first = 0;
+      synth_fill_i32_uniform(&first, 1, synth_key(w.seed, -1, "first_token"), w.vocab);
+      CK(hipMemcpy(tok, &first, 4, hipMemcpyHostToDevice));
+    }
+  } else if (w.prompt) {
     std::vector<int32_t> prompt(w.prompt);
     synth_fill_i32_uniform(prompt.data(), w.prompt, synth_key(w.seed, -1, "prompt"), w.vocab);
     for (int i = 0; i < w.prompt; ++i) {

@@ -1,0 +1,579 @@
+// td_block.hip - the block forward: n <= TD_MAX_BLOCK consecutive tokens of
+// one sequence through the decoder in one pass over the weights, for a prompt
+// (prefill) or for checking drafted tokens (the M = K + 1 verify of
+// speculative decoding).  With M tokens the weight-streaming GEMVs of the
+// decode step become GEMMs, Y[M][N] = X[M][K] W[N][K]^T, and run on the matrix
+// cores.  Token i sits at position pos0 + i and attends to positions
+// 0 .. pos0 + i; its K/V rows are written to the cache.
+//
+// Arithmetic: the GEMM inputs stay fp32.  When a workgroup stages a chunk of
+// them into LDS it splits every value into three bf16 parts, hi + mid + lo,
+// which hold its 24 significant bits (each part takes the rounding residue of
+// the one before), and multiplies all three with the bf16 weights by
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation: the products are those of
+// fp32 inputs with bf16 weights, as in the decode step, up to the order of the
+// sums.  int4 codes minus 8 are exact in bf16; the fp16 scale of a 64-column
+// group multiplies that group's partial.  The residual stream, RMSNorm, RoPE,
+// softmax and SiLU are fp32 as in the decode step.
+//
+// One kernel launch per op (the prompt path is not latency-bound like a decode
+// step).  Per layer: residual update + RMSNorm statistics, QKV GEMM (the norm
+// applied while staging), QKV epilogue (bias, RoPE, K/V write), attention, O
+// GEMM, residual update + statistics, gate/up GEMM, down GEMM (SiLU(gate) * up
+// formed while staging); then the final statistics, the logits GEMM (the last
+// row or every row) and the greedy token of each logits row.  GEMMs with fewer
+// 64-row weight tiles than CUs split K into slices whose partial sums are
+// added by their consumer in slice order (deterministic results).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "td.h"
+#include "td_internal.h"
+#include "td_device.h"
+
+namespace {
+
+typedef short s8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+// Sum over the workgroup of one value per thread, in a fixed order (the same
+// bits on every run): wave sums, then the waves' sums in wave order.
+DEV float block_sum(float v, float* red) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  if (lane_id() == 0) red[wave] = v;
+  __syncthreads();
+  float s = red[0];
+  for (int w = 1; w < nw; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// ------------------------------------------------------------ elementwise
+// x[i][:] = the bf16 embedding row of token i (fp32); an id outside [0, V)
+// raises the range bit and reads row 0.
+__global__ void __launch_bounds__(256) blk_embed(const uint16_t* embed, const int32_t* tokens, int H, int V, float* x,
+                                                 int32_t* err) {
+  const int i = blockIdx.x;
+  int t = tokens[i];
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0) atomicOr(err, TD_ERRBIT_RANGE);
+    t = 0;
+  }
+  const uint16_t* row = embed + (size_t)t * H;
+  float* xi = x + (size_t)i * H;
+  for (int e = threadIdx.x; e < H; e += blockDim.x) xi[e] = bf16f(row[e]);
+}
+
+// Row i of the residual stream: x += the S partial sums of the producing GEMM
+// (slice order; S = 0 adds nothing), then the RMSNorm of the updated row,
+// xn = x * gain / sqrt(mean(x^2) + eps), the next GEMM's input.
+__global__ void __launch_bounds__(256) blk_resid_norm(float* x, const float* part, int S, size_t sstride, int H,
+                                                      float eps, const uint16_t* gain, float* xn) {
+  __shared__ float red[8];
+  const int i = blockIdx.x;
+  float* xi = x + (size_t)i * H;
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < H; e += blockDim.x) {
+    float v = xi[e];
+    for (int s = 0; s < S; ++s) v += part[s * sstride + (size_t)i * H + e];
+    if (S) xi[e] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int e = threadIdx.x; e < H; e += blockDim.x) xn[(size_t)i * H + e] = xi[e] * bf16f(gain[e]) * inv;
+}
+
+// Row i: act = SiLU(gate) * up from the gate/up GEMM output [gate I | up I]
+// (the sum of its S slices in slice order when split).
+__global__ void __launch_bounds__(256) blk_swiglu(const float* src, int S, size_t sstride, int I, float* act) {
+  const float* yi = src + (size_t)blockIdx.x * 2 * I;
+  for (int e = threadIdx.x; e < I; e += blockDim.x) {
+    float g = yi[e], u = yi[I + e];
+    for (int s = 1; s < S; ++s) {
+      g += yi[s * sstride + e];
+      u += yi[s * sstride + I + e];
+    }
+    act[(size_t)blockIdx.x * I + e] = g / (1.0f + expf(-g)) * u;
+  }
+}
+
+// logits[r][:] = the sum of the S slices of a split logits GEMM (slice order).
+__global__ void __launch_bounds__(256) blk_sum_parts(const float* part, int S, size_t sstride, int N, float* y) {
+  const size_t base = (size_t)blockIdx.x * N;
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    float v = part[base + e];
+    for (int s = 1; s < S; ++s) v += part[s * sstride + base + e];
+    y[base + e] = v;
+  }
+}
+
+// ------------------------------------------------------------ GEMM
+// Y[M][N] = X[M][K] W[N][K]^T over the K slice [KS blockIdx.y, + KS) for
+// M <= 16 MT, X fp32 with row pitch ldx.  A workgroup of 4 waves takes 64
+// weight rows, 16 per wave; all waves share the X chunk (64 columns of every
+// token row) that the workgroup stages into LDS, split into three bf16 parts,
+// two chunks deep.  Each wave streams its rows' weights through a ring of D
+// chunks held in registers (D - 1 chunks in flight ahead of the one being
+// multiplied).  Every load is issued unconditionally (rows past M read row
+// M - 1, chunks past the slice re-read its last chunk, results unused), so
+// the number of loads between any two points is fixed and each wait for a
+// chunk leaves the later loads in flight.
+//
+// The split is exact: hi = v with the low 16 bits cleared, mid = the same of
+// v - hi, lo = v - hi - mid; each part carries 8 of v's 24 significant bits,
+// so hi + mid + lo = v and the three products with a bf16 weight sum to the
+// fp32 product.
+//
+// MFMA 16x16x32 bf16 operands: lane l holds row l % 16 of A (token rows) and
+// of B (weight rows) at 8 columns of the 32-column step selected by l / 16;
+// the result lane l holds token rows 4 (l / 16) + e, weight row l % 16.  For
+// bf16 weights lane l takes columns 32 j + 8 (l / 16) of the chunk at step j;
+// for int4 columns 16 (l / 16) + 8 j (the chunk is one scale group and a lane
+// reads its 16 codes as one 8-byte word).  A and B take the same columns, so
+// each step's products are a dot product over 32 distinct columns.
+constexpr int XP = 72;  // LDS row pitch of a staged part, bf16 elements (144 B: conflict-free 16-B reads)
+
+// Thread t stages groups g = t + 256 i (i < MT) of a chunk: 4 consecutive
+// columns 4 (g % 16) of token row g / 16.
+template <int MT>
+DEV void stage_load(float4 (&v)[MT], const float* X, int ldx, int M, int k0) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int g = threadIdx.x + 256 * i, m = min(g >> 4, M - 1), c = (g & 15) * 4;
+    v[i] = *(const float4*)(X + (size_t)m * ldx + k0 + c);
+  }
+}
+
+DEV uint32_t hi_pair(float a, float b) {  // the high halves of a and b, a in the low half
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+DEV float drop_hi(float a) { return a - __uint_as_float(__float_as_uint(a) & 0xffff0000u); }
+
+template <int MT>
+DEV void stage_store(uint16_t* xs, const float4 (&v)[MT]) {
+  constexpr int PART = MT * 16 * XP;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int g = threadIdx.x + 256 * i, m = g >> 4, c = (g & 15) * 4;
+    float a[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint16_t* dst = xs + m * XP + c;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      *(uint2*)(dst + p * PART) = make_uint2(hi_pair(a[0], a[1]), hi_pair(a[2], a[3]));
+      if (p < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = drop_hi(a[e]);
+      }
+    }
+  }
+}
+
+template <int FMT>
+struct WChunk;
+template <>
+struct WChunk<TD_WF_BF16> {
+  u32x4 w[2];
+};
+template <>
+struct WChunk<TD_WF_INT4_G64> {
+  u32x2 w;
+  uint32_t s;
+};
+
+template <int FMT>
+DEV void load_chunk(WChunk<FMT>& c, const uint8_t* wrow, const uint16_t* srow, int ch, int q) {
+  if constexpr (FMT == TD_WF_BF16) {
+    c.w[0] = *(const u32x4*)(wrow + ch * 128 + q * 16);
+    c.w[1] = *(const u32x4*)(wrow + ch * 128 + 64 + q * 16);
+  } else {
+    c.w = *(const u32x2*)(wrow + ch * 32 + q * 8);
+    c.s = srow[ch];
+  }
+}
+
+DEV s8v int4_bf16x8(uint32_t c) {
+  s8v b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = (short)(__float_as_uint((float)((c >> (4 * e)) & 15u) - 8.f) >> 16);  // exact
+  return b;
+}
+
+// One chunk: each 64-column chunk's products are summed by the MFMAs into a
+// fresh partial (parts lo, mid, hi in that order), which a VALU add (round to
+// nearest) then adds to the running sum; the running sum never passes through
+// the matrix unit's accumulator.
+template <int FMT, int MT>
+DEV void mul_chunk(f32x4 (&acc)[MT], const WChunk<FMT>& c, const uint16_t* xs, int r, int q) {
+  constexpr int PART = MT * 16 * XP;
+  f32x4 pr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) pr[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bf8v b;
+    if constexpr (FMT == TD_WF_BF16) b = __builtin_bit_cast(bf8v, c.w[j]);
+    else b = __builtin_bit_cast(bf8v, int4_bf16x8(j ? c.w.y : c.w.x));
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint16_t* a = xs + (16 * t + r) * XP + (FMT == TD_WF_BF16 ? 32 * j + 8 * q : 16 * q + 8 * j);
+#pragma unroll
+      for (int p = 2; p >= 0; --p)
+        pr[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf8v*)(a + p * PART), b, pr[t], 0, 0, 0);
+    }
+  }
+  if constexpr (FMT == TD_WF_BF16) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] += pr[t];
+  } else {
+    // result lane l is weight row l % 16, the row whose scale this lane loaded
+    const float sc = f16f(c.s);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      acc[t].x = fmaf(sc, pr[t].x, acc[t].x);
+      acc[t].y = fmaf(sc, pr[t].y, acc[t].y);
+      acc[t].z = fmaf(sc, pr[t].z, acc[t].z);
+      acc[t].w = fmaf(sc, pr[t].w, acc[t].w);
+    }
+  }
+}
+
+template <int FMT, int MT>
+__global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, int K, int KS, const uint8_t* W,
+                                                const uint16_t* Sc, int N, float* Y, int ldy, size_t sstride) {
+  constexpr int PART = MT * 16 * XP;
+  constexpr int D = FMT == TD_WF_BF16 ? 4 : 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][3 * PART];
+  const int wave = threadIdx.x >> 6, lane = lane_id(), r = lane & 15, q = lane >> 4;
+  const int n = blockIdx.x * 64 + wave * 16 + r;
+  const int nr = min(n, N - 1);  // rows past N read row N - 1 and are not stored
+  const int kb = blockIdx.y * KS, nch = (min(K, kb + KS) - kb) >> 6;
+  const uint8_t* wrow;
+  const uint16_t* srow = nullptr;
+  if constexpr (FMT == TD_WF_BF16) {
+    wrow = W + ((size_t)nr * K + kb) * 2;
+  } else {
+    wrow = W + (size_t)nr * (K >> 1) + (kb >> 1);
+    srow = Sc + (size_t)nr * (K >> 6) + (kb >> 6);
+  }
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  WChunk<FMT> ring[D];
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) load_chunk<FMT>(ring[i], wrow, srow, min(i, nch - 1), q);
+  float4 sv[MT];
+  stage_load<MT>(sv, X, ldx, M, kb);
+  stage_store<MT>(xs[0], sv);
+  wg_bar();
+  for (int c0 = 0; c0 < nch; c0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int c = c0 + i;
+      // X loads of the next chunk first, then the weight prefetch: waiting for
+      // the X loads then leaves the newest weight chunk in flight
+      stage_load<MT>(sv, X, ldx, M, kb + 64 * min(c + 1, nch - 1));
+      load_chunk<FMT>(ring[(i + D - 1) % D], wrow, srow, min(c + D - 1, nch - 1), q);
+      if (c < nch) mul_chunk<FMT, MT>(acc, ring[i], xs[c & 1], r, q);
+      stage_store<MT>(xs[(c + 1) & 1], sv);
+      wg_bar();
+    }
+  }
+  if (n >= N) return;
+  float* dst = Y + blockIdx.y * sstride + n;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const float rv[4] = {acc[t].x, acc[t].y, acc[t].z, acc[t].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * t + 4 * q + e;
+      if (m < M) dst[(size_t)m * ldy] = rv[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------ QKV epilogue
+// Token i: the sum of the S QKV partial slices, bias, RoPE of the q and k row
+// pairs at position pos0 + i, q (times 1/sqrt(d)) to qout [n][qd], k and v
+// rows to the cache as bf16.
+__global__ void __launch_bounds__(256) blk_qkv_post(const float* part, int S, size_t sstride, int qkv_rows, int qd,
+                                                    int kvd, int d, int nkv, int max_ctx, int layer, int pos0,
+                                                    const uint16_t* bias, const float* rope_cs, float attn_scale,
+                                                    float* qout, uint16_t* kc, uint16_t* vc) {
+  const int i = blockIdx.x;
+  const int pos = pos0 + i;
+  const int half = d >> 1;
+  const float* yi = part + (size_t)i * qkv_rows;
+  for (int u = threadIdx.x; u < qkv_rows / 2; u += blockDim.x) {
+    const int head = u / half, j = u - head * half;
+    const int ra = head * d + j, rb = ra + half;
+    float a = yi[ra], b = yi[rb];
+    for (int s = 1; s < S; ++s) {
+      a += yi[s * sstride + ra];
+      b += yi[s * sstride + rb];
+    }
+    if (bias) {
+      a += bf16f(bias[ra]);
+      b += bf16f(bias[rb]);
+    }
+    if (ra < qd + kvd) {
+      const float c = rope_cs[((size_t)pos * half + j) * 2], sn = rope_cs[((size_t)pos * half + j) * 2 + 1];
+      const float a2 = a * c - b * sn;
+      const float b2 = b * c + a * sn;
+      a = a2;
+      b = b2;
+    }
+    if (ra < qd) {
+      qout[(size_t)i * qd + ra] = a * attn_scale;
+      qout[(size_t)i * qd + rb] = b * attn_scale;
+    } else {
+      const bool isk = ra < qd + kvd;
+      const int g = (ra - qd - (isk ? 0 : kvd)) / d;
+      uint16_t* row = (isk ? kc : vc) + (((size_t)layer * nkv + g) * max_ctx + pos) * d;
+      row[j] = (uint16_t)f2bf(a);
+      row[j + half] = (uint16_t)f2bf(b);
+    }
+  }
+}
+
+// ------------------------------------------------------------ attention
+// One workgroup per (token i, kv head g): the group's query heads (at most
+// TD_MAX_GROUP) over keys 0 .. pos0 + i, which share every K and V row they
+// read.  The keys are cut into tiles of 64; wave w takes tiles w, w + 4, ...
+// and keeps, per query head, an online softmax (running max m, sum l and the
+// weighted V sum): lane t scores key t of the tile against every head, then
+// lane e accumulates output column e (and e + 64 when D = 128) over the
+// tile's keys.  The four waves' states are merged in wave order at the end
+// (deterministic).  Keys past pos0 + i get probability 0 (their loads read
+// row pos0 + i instead).
+template <int D>
+__global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* kc, const uint16_t* vc, int nq,
+                                                int group, int nkv, int max_ctx, int layer, int pos0, float* out) {
+  constexpr int G = TD_MAX_GROUP, C = D / 64;
+  __shared__ __attribute__((aligned(16))) float qs[G][D];
+  __shared__ __attribute__((aligned(16))) float ps[4][64][G];  // [wave][key][head]
+  __shared__ float mst[4][G], lst[4][G];
+  __shared__ float ost[4][G][D];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int i = blockIdx.x, g = blockIdx.y, h0 = g * group;
+  const int last = pos0 + i;
+  for (int e = threadIdx.x; e < G * D; e += 256) {
+    const int r = e / D;
+    qs[r][e % D] = r < group ? q[((size_t)i * nq + h0 + r) * D + e % D] : 0.f;
+  }
+  __syncthreads();
+  const uint16_t* K = kc + ((size_t)layer * nkv + g) * max_ctx * D;
+  const uint16_t* Vv = vc + ((size_t)layer * nkv + g) * max_ctx * D;
+  float m[G], l[G], acc[G][C];
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    m[r] = -__builtin_inff();
+    l[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[r][c] = 0.f;
+  }
+  const int ntiles = (last + 64) / 64;
+  for (int tile = wave; tile < ntiles; tile += 4) {
+    const int t0 = tile * 64, key = t0 + lane;
+    const bool valid = key <= last;
+    const uint16_t* kr = K + (size_t)min(key, last) * D;
+    u32x4 kw[D / 8];
+#pragma unroll
+    for (int e = 0; e < D / 8; ++e) kw[e] = *(const u32x4*)(kr + 8 * e);
+    // the query rows are read from LDS where they are used, not kept in registers
+    asm volatile("" ::: "memory");
+    float s[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      s[r] = 0.f;
+      if (r < group) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < D / 8; ++e) {
+          const f32x4 qa = *(const f32x4*)&qs[r][8 * e], qb = *(const f32x4*)&qs[r][8 * e + 4];
+          a = fmaf(bf_lo(kw[e].x), qa.x, a);
+          a = fmaf(bf_hi(kw[e].x), qa.y, a);
+          a = fmaf(bf_lo(kw[e].y), qa.z, a);
+          a = fmaf(bf_hi(kw[e].y), qa.w, a);
+          a = fmaf(bf_lo(kw[e].z), qb.x, a);
+          a = fmaf(bf_hi(kw[e].z), qb.y, a);
+          a = fmaf(bf_lo(kw[e].w), qb.z, a);
+          a = fmaf(bf_hi(kw[e].w), qb.w, a);
+        }
+        s[r] = a;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      if (r < group) {
+        const float sv = valid ? s[r] : -__builtin_inff();
+        const float mn = fmaxf(m[r], wave_max(sv));
+        const float p = valid ? expf(sv - mn) : 0.f;
+        const float corr = expf(m[r] - mn);
+        l[r] = l[r] * corr + wave_sum(p);
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[r][c] *= corr;
+        m[r] = mn;
+        ps[wave][lane][r] = p;
+      }
+    }
+    // (each wave reads only its own ps rows, written by itself above)
+    const int nk = min(64, last + 1 - t0);
+#pragma unroll 8
+    for (int t = 0; t < nk; ++t) {
+      const uint16_t* vr = Vv + (size_t)(t0 + t) * D + lane;
+      float vv[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) vv[c] = bf16f(vr[64 * c]);
+      const f32x4 pa = *(const f32x4*)&ps[wave][t][0], pb = *(const f32x4*)&ps[wave][t][4];
+      const float pr[G] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int r = 0; r < G; ++r)
+        if (r < group) {
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[r][c] = fmaf(pr[r], vv[c], acc[r][c]);
+        }
+    }
+  }
+  // merge the waves' states in wave order
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    if (lane == 0) {
+      mst[wave][r] = m[r];
+      lst[wave][r] = l[r];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) ost[wave][r][64 * c + lane] = acc[r][c];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < group * D; e += 256) {
+    const int r = e / D, col = e % D;
+    float M = mst[0][r];
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, mst[w][r]);
+    float L = 0.f, O = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = mst[w][r] == -__builtin_inff() ? 0.f : expf(mst[w][r] - M);
+      L = fmaf(lst[w][r], f, L);
+      O = fmaf(ost[w][r][col], f, O);
+    }
+    out[((size_t)i * nq + h0 + r) * D + col] = O / L;
+  }
+}
+
+// ------------------------------------------------------------ greedy token
+// Row r of logits [rows][V]: the largest value (lowest id among equals); a
+// non-finite value raises the error bit (the token is then 0).
+__global__ void __launch_bounds__(256) blk_argmax(const float* logits, int V, int32_t* tokens, int32_t* token_word,
+                                                  int rows, int32_t* err) {
+  __shared__ float bvs[4];
+  __shared__ int bis[4], bads[4];
+  const int r = blockIdx.x;
+  const float* x = logits + (size_t)r * V;
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff, bad = 0;
+  for (int e = threadIdx.x; e < V; e += blockDim.x) {
+    const float v = x[e];
+    if (!isfinite(v)) bad = 1;
+    else if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  bad = __any(bad);
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 0) {
+    bvs[wave] = bv;
+    bis[wave] = bi;
+    bads[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  for (int w = 1; w < 4; ++w) {
+    if (bvs[w] > bv || (bvs[w] == bv && bis[w] < bi)) { bv = bvs[w]; bi = bis[w]; }
+    bad |= bads[w];
+  }
+  const int tok = (bad || bi == 0x7fffffff) ? 0 : bi;
+  if (bad) atomicOr(err, TD_ERRBIT_NONFINITE);
+  if (tokens) tokens[r] = tok;
+  if (r == rows - 1) *token_word = tok;
+}
+
+template <int FMT>
+int launch_gemm_f(dim3 grid, hipStream_t st, const float* X, int ldx, int M, int K, int KS, const uint8_t* W,
+                  const uint16_t* S, int N, float* Y, int ldy, size_t sstride) {
+  const dim3 block(256);
+  switch ((M + 15) / 16) {
+    case 1: blk_gemm<FMT, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
+    case 2: blk_gemm<FMT, 2><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
+    case 3: blk_gemm<FMT, 3><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
+    default: blk_gemm<FMT, 4><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
+  }
+  return (int)hipGetLastError();
+}
+
+// X W^T, N columns with row pitch ldy.  With one K slice the result goes to Y;
+// with S > 1 slices, slice s goes to part + s M ldy and the consumer adds them
+// in slice order.  *S_out receives S.
+int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t* W, const uint16_t* Sc, int N,
+         float* Y, float* part, int ldy, int* S_out, hipStream_t st) {
+  int KS = 0;
+  const int S = td_block_split(N, K, ncu, &KS);
+  *S_out = S;
+  float* dst = S == 1 ? Y : part;
+  const size_t sstride = (size_t)M * ldy;
+  const dim3 grid((N + 63) / 64, S);
+  return fmt ? launch_gemm_f<TD_WF_INT4_G64>(grid, st, X, ldx, M, K, KS, W, Sc, N, dst, ldy, sstride)
+             : launch_gemm_f<TD_WF_BF16>(grid, st, X, ldx, M, K, KS, W, Sc, N, dst, ldy, sstride);
+}
+
+}  // namespace
+
+int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int pos0, int all_logits,
+                    float* logits, int32_t* argmax_out, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const td_kparams& P = *B->kp;
+  const int H = P.H, I = P.I, d = P.d, qd = P.qd, L = P.L, ncu = B->ncu;
+  float* part = B->part;
+  int e = 0, S = 0, S_prev = 0;
+#define TD_CK(x)                      \
+  do {                                \
+    x;                                \
+    e = (int)hipGetLastError();       \
+    if (e) return e;                  \
+  } while (0)
+  TD_CK((blk_embed<<<n, 256, 0, st>>>(P.embed, tokens, H, P.V, B->x, P.err)));
+  for (int l = 0; l < L; ++l) {
+    const td_layer_dev& Ld = B->layers_host[l];
+    // x += the previous layer's down-projection slices; attention RMSNorm
+    TD_CK((blk_resid_norm<<<n, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, P.eps, Ld.attn_norm, B->xn)));
+    if ((e = gemm(P.wf, ncu, B->xn, H, n, H, Ld.w[0], Ld.s[0], P.qkv_rows, B->y, part, P.qkv_rows, &S, st))) return e;
+    TD_CK((blk_qkv_post<<<n, 256, 0, st>>>(S == 1 ? B->y : part, S, (size_t)n * P.qkv_rows, P.qkv_rows, qd, P.kvd,
+                                           d, P.nkv, P.max_ctx, l, pos0, Ld.bias, P.rope_cs, P.attn_scale, B->q,
+                                           P.kc, P.vc)));
+    const dim3 agrid(n, P.nkv);
+    if (d == 64)
+      TD_CK((blk_attn<64><<<agrid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0,
+                                                 B->ao)));
+    else
+      TD_CK((blk_attn<128><<<agrid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0,
+                                                  B->ao)));
+    // the O and down projections always land in part (slice 0 when unsplit)
+    if ((e = gemm(P.wf, ncu, B->ao, qd, n, qd, Ld.w[1], Ld.s[1], H, part, part, H, &S, st))) return e;
+    TD_CK((blk_resid_norm<<<n, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, P.eps, Ld.mlp_norm, B->xn)));
+    if ((e = gemm(P.wf, ncu, B->xn, H, n, H, Ld.w[2], Ld.s[2], 2 * I, B->y, part, 2 * I, &S, st))) return e;
+    TD_CK((blk_swiglu<<<n, 256, 0, st>>>(S == 1 ? B->y : part, S, (size_t)n * 2 * I, I, B->act)));
+    if ((e = gemm(P.wf, ncu, B->act, I, n, I, Ld.w[3], Ld.s[3], H, part, part, H, &S_prev, st))) return e;
+  }
+  TD_CK((blk_resid_norm<<<n, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, P.eps, P.final_norm, B->xn)));
+  const int r0 = all_logits ? 0 : n - 1, rows = all_logits ? n : 1;
+  if ((e = gemm(TD_WF_BF16, ncu, B->xn + (size_t)r0 * H, H, rows, H, (const uint8_t*)P.head, nullptr, P.V, logits,
+                part, P.V, &S, st)))
+    return e;
+  if (S > 1) TD_CK((blk_sum_parts<<<rows, 256, 0, st>>>(part, S, (size_t)rows * P.V, P.V, logits)));
+  TD_CK((blk_argmax<<<rows, 256, 0, st>>>(logits, P.V, argmax_out, P.token_out, rows, P.err)));
+#undef TD_CK
+  return 0;
+}

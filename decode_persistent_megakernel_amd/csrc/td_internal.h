@@ -191,8 +191,40 @@ static inline void td_slice(int K, int w, int* lo, int* hi) {
   *hi = 2 * (int)(((int64_t)nu * (w + 1)) / TD_NW);
 }
 
+// Workspace and host-side views of the block forward (td_block.hip), for
+// up to TD_MAX_BLOCK token rows (TD_MAX_BLOCK, the most rows, is declared in
+// td.h).
+struct td_blockparams {
+  const td_kparams* kp;            // shapes, weights, cache, rope table, token and error words
+  const td_layer_dev* layers_host; // [L] the layer pointers, host copy
+  int ncu;                         // CUs of the device (split-K sizing)
+  float* x;                        // [n][H] residual stream
+  float* xn;                       // [n][H] RMSNorm of x (a GEMM input)
+  float* y;                        // [n][max(qkv_rows, 2 I)] QKV or gate/up output
+  float* act;                      // [n][I] SiLU(gate) * up (a GEMM input)
+  float* part;                     // split-K partial slices, td_block_part_floats() floats
+  float* q;                        // [n][qd] rotated, scaled queries
+  float* ao;                       // [n][qd] attention output
+};
+
+// Split-K plan of one block GEMM (N weight rows, K columns, 64-row tiles):
+// GEMMs with fewer tiles than CUs cut K into S slices of KS columns (a
+// multiple of 64) so that about two workgroups per CU run.  Returns S.
+static inline int td_block_split(int N, int K, int ncu, int* KS) {
+  const int tiles = (N + 63) / 64, chunks = K / 64;
+  int s = tiles >= ncu ? 1 : (2 * ncu + tiles - 1) / tiles;
+  if (s > chunks) s = chunks;
+  if (s < 1) s = 1;
+  const int per = (chunks + s - 1) / s;
+  *KS = per * 64;
+  return (chunks + per - 1) / per;
+}
+
 // launch entry points (td_kernels.hip)
 int td_launch_megakernel(const td_kparams* p, int ncu, void* stream);
+// block forward (td_block.hip): logits [n][V] (all_logits) or [V] of the last token
+int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int pos0, int all_logits, float* logits,
+                    int32_t* argmax_out, void* stream);
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
                      void* stream);
 int td_megakernel_occupancy(int head_dim, int weight_format, int lds_bytes, int* blocks_per_cu);

@@ -164,6 +164,42 @@ const int32_t* td_token_ptr(const td_ctx* ctx);
 int td_decode_loop(td_ctx* ctx, const int32_t* d_token, int32_t pos, int32_t n_steps, int32_t eos_id,
                    const td_kv* kv, float* d_logits_out, int32_t* d_tokens_out, int32_t* d_count_out, void* stream);
 
+/* Most tokens one td_forward_block call takes. */
+#define TD_MAX_BLOCK 64
+
+/*
+ * td_forward_block: n consecutive tokens of one sequence through the decoder in
+ * one pass over the weights, for a prompt (prefill) or to check drafted tokens
+ * (the M = K + 1 verify of speculative decoding).  (tinyinfer, "What I'd tell
+ * someone starting, and what's next": a prompt fed one token at a time costs a
+ * full weight read per token, and a batch of prompt tokens turns the
+ * matrix-vector products into matrix-matrix products on the matrix cores;
+ * "Llama 1B: optimizing kernels", "Decode vs Prefill": prefill needs GEMM
+ * kernels and its own attention; the flint page, past the MLP-path table: the
+ * K + 1 positions of a draft are verified in one launch that reads the weights
+ * once.)  Token i (the int32 at d_tokens[i], device) sits at
+ * position pos0 + i and attends to positions 0 .. pos0 + i; the K/V rows of
+ * positions pos0 .. pos0 + n - 1 of every layer are written to `kv` (rows
+ * before pos0 must hold earlier tokens').  Row i of the result equals what
+ * td_decode_step computes for token i at position pos0 + i, up to rounding:
+ * the linears run as matrix-core products of bf16 weights with each input row
+ * split into a bf16 high and low part, fp32 accumulation.
+ * all_logits = 0: d_logits_out (device fp32 [vocab]) receives the logits of
+ * the last token; nonzero: d_logits_out is [n][vocab], row i token i's.
+ * d_argmax_out (device int32 [n] when all_logits, else [1]; or NULL) receives
+ * the greedy token of each logits row (largest logit, lowest id among ties);
+ * td_token_ptr(ctx) receives the last token's greedy token, so a decode loop
+ * can follow without a host round trip.  Uses the context's own workspace:
+ * asynchronous on `stream`, no allocation, and not concurrent with another call
+ * on the same context.  Works with every executor.
+ * Errors (before launch): TD_E_INVALID_ARG (null ctx/tokens/kv/logits, kv
+ * max_ctx mismatch, n outside [1, TD_MAX_BLOCK]), TD_E_RANGE (pos0 < 0 or
+ * pos0 + n > max_ctx), TD_E_HIP.  A token id outside [0, vocab) or a
+ * non-finite logit is reported by td_status.
+ */
+int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t pos0, const td_kv* kv,
+                     float* d_logits_out, int32_t all_logits, int32_t* d_argmax_out, void* stream);
+
 /*
  * td_status: synchronises the stream of the last td_decode_step, then returns
  * the device error word as a TD_* code (TD_OK, TD_E_NONFINITE, TD_E_RANGE,

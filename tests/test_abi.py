@@ -107,5 +107,6 @@ def test_null_arguments_are_rejected():
     kv = _lib.TdKV(k=None, v=None, max_ctx=64)
     assert L.td_decode_step(None, None, 0, ctypes.byref(kv), None, None) == _lib.TD_E_INVALID_ARG
     assert L.td_decode_loop(None, None, 0, 4, -1, ctypes.byref(kv), None, None, None, None) == _lib.TD_E_INVALID_ARG
+    assert L.td_forward_block(None, None, 4, 0, ctypes.byref(kv), None, 0, None, None) == _lib.TD_E_INVALID_ARG
     assert L.td_status(None, None) == _lib.TD_E_INVALID_ARG
     L.td_destroy(None)  # a no-op
