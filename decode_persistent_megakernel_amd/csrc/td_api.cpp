@@ -595,7 +595,8 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
       return o;
     };
     const size_t b_x = btake(R * H * 4), b_xn = btake(R * H * 4), b_act = btake(R * I * 4);
-    const size_t b_part = btake(part_floats * 4);
+    const size_t b_part = btake(part_floats * 4), b_ssq = btake(R * (H / 256) * 4);
+    const size_t b_cand = btake(R * TD_BLOCK_ARGMAX_SLICES * 8);
     const size_t b_y = btake(R * ymax * 4), b_q = btake(R * qd * 4), b_ao = btake(R * qd * 4);
     e = hipMalloc(&ctx->blockbuf, bo);
     if (e != hipSuccess) {
@@ -609,6 +610,8 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     ctx->blk.x = (float*)(bb + b_x);
     ctx->blk.xn = (float*)(bb + b_xn);
     ctx->blk.act = (float*)(bb + b_act);
+    ctx->blk.ssq = (float*)(bb + b_ssq);
+    ctx->blk.cand = (uint2*)(bb + b_cand);
     ctx->blk.part = (float*)(bb + b_part);
     ctx->blk.y = (float*)(bb + b_y);
     ctx->blk.q = (float*)(bb + b_q);

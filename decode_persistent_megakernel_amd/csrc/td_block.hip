@@ -65,48 +65,60 @@ __global__ void __launch_bounds__(256) blk_embed(const uint16_t* embed, const in
   for (int e = threadIdx.x; e < H; e += blockDim.x) xi[e] = bf16f(row[e]);
 }
 
-// Row i of the residual stream: x += the S partial sums of the producing GEMM
-// (slice order; S = 0 adds nothing), then the RMSNorm of the updated row,
-// xn = x * gain / sqrt(mean(x^2) + eps), the next GEMM's input.
-__global__ void __launch_bounds__(256) blk_resid_norm(float* x, const float* part, int S, size_t sstride, int H,
-                                                      float eps, const uint16_t* gain, float* xn) {
-  __shared__ float red[8];
-  const int i = blockIdx.x;
-  float* xi = x + (size_t)i * H;
-  float ss = 0.f;
-  for (int e = threadIdx.x; e < H; e += blockDim.x) {
-    float v = xi[e];
-    for (int s = 0; s < S; ++s) v += part[s * sstride + (size_t)i * H + e];
-    if (S) xi[e] = v;
-    ss = fmaf(v, v, ss);
+// Columns 256 b .. + 256 of row i of the residual stream: x += the S partial
+// sums of the producing GEMM (slice order; S = 0 adds nothing); the block's
+// sum of squares of the updated values goes to ssq[i][b] (wave sums in wave
+// order), for blk_norm.
+__global__ void __launch_bounds__(256) blk_resid(float* x, const float* part, int S, size_t sstride, int H,
+                                                 float* ssq) {
+  __shared__ float red[4];
+  const int i = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  const size_t o = (size_t)i * H + e;
+  float v = x[o];
+  if (S) {
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) v += part[s * sstride + o];
+    x[o] = v;
   }
-  ss = block_sum(ss, red);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int e = threadIdx.x; e < H; e += blockDim.x) xn[(size_t)i * H + e] = xi[e] * bf16f(gain[e]) * inv;
+  const float ss = block_sum(v * v, red);
+  if (threadIdx.x == 0) ssq[i * gridDim.x + blockIdx.x] = ss;
 }
 
-// Row i: act = SiLU(gate) * up from the gate/up GEMM output [gate I | up I]
-// (the sum of its S slices in slice order when split).
+// xn = x * gain / sqrt(mean(x^2) + eps) for columns 256 b .. + 256 of row i,
+// the row's sum of squares being its nb block sums added in block order.
+__global__ void __launch_bounds__(256) blk_norm(const float* x, const float* ssq, int H, float eps,
+                                                const uint16_t* gain, float* xn) {
+  const int i = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x, nb = gridDim.x;
+  float ss = ssq[i * nb];
+  for (int b = 1; b < nb; ++b) ss += ssq[i * nb + b];
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  const size_t o = (size_t)i * H + e;
+  xn[o] = x[o] * bf16f(gain[e]) * inv;
+}
+
+// act = SiLU(gate) * up from the gate/up GEMM output [gate I | up I] (the sum
+// of its S slices in slice order when split), columns 256 b .. of row i.
 __global__ void __launch_bounds__(256) blk_swiglu(const float* src, int S, size_t sstride, int I, float* act) {
-  const float* yi = src + (size_t)blockIdx.x * 2 * I;
-  for (int e = threadIdx.x; e < I; e += blockDim.x) {
-    float g = yi[e], u = yi[I + e];
-    for (int s = 1; s < S; ++s) {
-      g += yi[s * sstride + e];
-      u += yi[s * sstride + I + e];
-    }
-    act[(size_t)blockIdx.x * I + e] = g / (1.0f + expf(-g)) * u;
+  const int i = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= I) return;
+  const float* yi = src + (size_t)i * 2 * I;
+  float g = yi[e], u = yi[I + e];
+#pragma unroll 4
+  for (int s = 1; s < S; ++s) {
+    g += yi[s * sstride + e];
+    u += yi[s * sstride + I + e];
   }
+  act[(size_t)i * I + e] = g / (1.0f + expf(-g)) * u;
 }
 
 // logits[r][:] = the sum of the S slices of a split logits GEMM (slice order).
 __global__ void __launch_bounds__(256) blk_sum_parts(const float* part, int S, size_t sstride, int N, float* y) {
-  const size_t base = (size_t)blockIdx.x * N;
-  for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    float v = part[base + e];
-    for (int s = 1; s < S; ++s) v += part[s * sstride + base + e];
-    y[base + e] = v;
-  }
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= N) return;
+  const size_t o = (size_t)blockIdx.y * N + e;
+  float v = part[o];
+  for (int s = 1; s < S; ++s) v += part[s * sstride + o];
+  y[o] = v;
 }
 
 // ------------------------------------------------------------ GEMM
@@ -239,11 +251,25 @@ DEV void mul_chunk(f32x4 (&acc)[MT], const WChunk<FMT>& c, const uint16_t* xs, i
   }
 }
 
+// Chunk c's loads, weights and X, go into ring slot c % D together, D - 1
+// chunks ahead of their use, X first: waiting for the X of chunk c + 1 (to
+// stage it) then leaves the weights of chunks c + 1 .. c + D - 1 in flight.
+template <int FMT, int MT>
+struct Slot {
+  WChunk<FMT> w;
+  float4 x[MT];
+};
+
+template <int FMT, int MT>
+constexpr int ring_depth() {
+  return FMT == TD_WF_BF16 ? (MT <= 2 ? 8 : 6) : (MT <= 2 ? 10 : 8);
+}
+
 template <int FMT, int MT>
 __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, int K, int KS, const uint8_t* W,
                                                 const uint16_t* Sc, int N, float* Y, int ldy, size_t sstride) {
   constexpr int PART = MT * 16 * XP;
-  constexpr int D = FMT == TD_WF_BF16 ? 4 : 8;
+  constexpr int D = ring_depth<FMT, MT>();
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][3 * PART];
   const int wave = threadIdx.x >> 6, lane = lane_id(), r = lane & 15, q = lane >> 4;
   const int n = blockIdx.x * 64 + wave * 16 + r;
@@ -257,26 +283,31 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
     wrow = W + (size_t)nr * (K >> 1) + (kb >> 1);
     srow = Sc + (size_t)nr * (K >> 6) + (kb >> 6);
   }
+  const float* xb = X + kb;
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  WChunk<FMT> ring[D];
+  Slot<FMT, MT> ring[D];
 #pragma unroll
-  for (int i = 0; i < D - 1; ++i) load_chunk<FMT>(ring[i], wrow, srow, min(i, nch - 1), q);
-  float4 sv[MT];
-  stage_load<MT>(sv, X, ldx, M, kb);
-  stage_store<MT>(xs[0], sv);
+  for (int i = 0; i < D - 1; ++i) {
+    const int ch = min(i, nch - 1);
+    stage_load<MT>(ring[i].x, xb, ldx, M, 64 * ch);
+    load_chunk<FMT>(ring[i].w, wrow, srow, ch, q);
+  }
+  stage_store<MT>(xs[0], ring[0].x);
   wg_bar();
   for (int c0 = 0; c0 < nch; c0 += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int c = c0 + i;
-      // X loads of the next chunk first, then the weight prefetch: waiting for
-      // the X loads then leaves the newest weight chunk in flight
-      stage_load<MT>(sv, X, ldx, M, kb + 64 * min(c + 1, nch - 1));
-      load_chunk<FMT>(ring[(i + D - 1) % D], wrow, srow, min(c + D - 1, nch - 1), q);
-      if (c < nch) mul_chunk<FMT, MT>(acc, ring[i], xs[c & 1], r, q);
-      stage_store<MT>(xs[(c + 1) & 1], sv);
+      {
+        Slot<FMT, MT>& sl = ring[(i + D - 1) % D];  // chunk c - 1's slot, consumed
+        const int ch = min(c + D - 1, nch - 1);
+        stage_load<MT>(sl.x, xb, ldx, M, 64 * ch);
+        load_chunk<FMT>(sl.w, wrow, srow, ch, q);
+      }
+      if (c < nch) mul_chunk<FMT, MT>(acc, ring[i].w, xs[c & 1], r, q);
+      stage_store<MT>(xs[(c + 1) & 1], ring[(i + 1) % D].x);
       wg_bar();
     }
   }
@@ -294,21 +325,23 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
 }
 
 // ------------------------------------------------------------ QKV epilogue
-// Token i: the sum of the S QKV partial slices, bias, RoPE of the q and k row
-// pairs at position pos0 + i, q (times 1/sqrt(d)) to qout [n][qd], k and v
-// rows to the cache as bf16.
+// Token i (blockIdx.y), row pair u (256 per block): the sum of the S QKV
+// partial slices, bias, RoPE of the q and k row pairs at position pos0 + i, q
+// (times 1/sqrt(d)) to qout [n][qd], k and v rows to the cache as bf16.
 __global__ void __launch_bounds__(256) blk_qkv_post(const float* part, int S, size_t sstride, int qkv_rows, int qd,
                                                     int kvd, int d, int nkv, int max_ctx, int layer, int pos0,
                                                     const uint16_t* bias, const float* rope_cs, float attn_scale,
                                                     float* qout, uint16_t* kc, uint16_t* vc) {
-  const int i = blockIdx.x;
+  const int i = blockIdx.y;
   const int pos = pos0 + i;
   const int half = d >> 1;
   const float* yi = part + (size_t)i * qkv_rows;
-  for (int u = threadIdx.x; u < qkv_rows / 2; u += blockDim.x) {
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u < qkv_rows / 2) {
     const int head = u / half, j = u - head * half;
     const int ra = head * d + j, rb = ra + half;
     float a = yi[ra], b = yi[rb];
+#pragma unroll 4
     for (int s = 1; s < S; ++s) {
       a += yi[s * sstride + ra];
       b += yi[s * sstride + rb];
@@ -462,17 +495,21 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
 }
 
 // ------------------------------------------------------------ greedy token
-// Row r of logits [rows][V]: the largest value (lowest id among equals); a
-// non-finite value raises the error bit (the token is then 0).
-__global__ void __launch_bounds__(256) blk_argmax(const float* logits, int V, int32_t* tokens, int32_t* token_word,
-                                                  int rows, int32_t* err) {
+// Phase 1, workgroup (b, r): the largest value of columns [CH b, CH (b + 1))
+// of logits row r (lowest id among equals) as (value bits, id) in
+// cand[r][b]; id TD_ARGMAX_NONE when the slice is empty, TD_ARGMAX_BAD (and
+// the error bit) when it holds a NaN or an infinity.
+constexpr uint32_t TD_ARGMAX_NONE = 0x7fffffffu, TD_ARGMAX_BAD = 0xfffffffeu;
+__global__ void __launch_bounds__(256) blk_argmax_part(const float* logits, int V, int CH, uint2* cand,
+                                                       int32_t* err) {
   __shared__ float bvs[4];
   __shared__ int bis[4], bads[4];
-  const int r = blockIdx.x;
+  const int r = blockIdx.y, b = blockIdx.x;
   const float* x = logits + (size_t)r * V;
+  const int e1 = min(V, CH * (b + 1));
   float bv = -__builtin_inff();
-  int bi = 0x7fffffff, bad = 0;
-  for (int e = threadIdx.x; e < V; e += blockDim.x) {
+  int bi = (int)TD_ARGMAX_NONE, bad = 0;
+  for (int e = CH * b + threadIdx.x; e < e1; e += 256) {
     const float v = x[e];
     if (!isfinite(v)) bad = 1;
     else if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
@@ -495,8 +532,30 @@ __global__ void __launch_bounds__(256) blk_argmax(const float* logits, int V, in
     if (bvs[w] > bv || (bvs[w] == bv && bis[w] < bi)) { bv = bvs[w]; bi = bis[w]; }
     bad |= bads[w];
   }
-  const int tok = (bad || bi == 0x7fffffff) ? 0 : bi;
   if (bad) atomicOr(err, TD_ERRBIT_NONFINITE);
+  cand[r * gridDim.x + b] = make_uint2(__float_as_uint(bv), bad ? TD_ARGMAX_BAD : (uint32_t)bi);
+}
+
+// Phase 2, one thread per row r: the slices' candidates in slice order (ids
+// ascend with the slice, so the first of equal values has the lowest id);
+// token 0 when the row held a non-finite value.  The last row's token also
+// goes to token_word.
+__global__ void __launch_bounds__(64) blk_argmax_final(const uint2* cand, int nb, int rows, int32_t* tokens,
+                                                       int32_t* token_word) {
+  const int r = blockIdx.x * 64 + threadIdx.x;
+  if (r >= rows) return;
+  float bv = -__builtin_inff();
+  uint32_t bi = TD_ARGMAX_NONE;
+  bool bad = false;
+  for (int b = 0; b < nb; ++b) {
+    const uint2 c = cand[r * nb + b];
+    if (c.y == TD_ARGMAX_BAD) bad = true;
+    else if (c.y != TD_ARGMAX_NONE && (__uint_as_float(c.x) > bv || bi == TD_ARGMAX_NONE)) {
+      bv = __uint_as_float(c.x);
+      bi = c.y;
+    }
+  }
+  const int tok = (bad || bi == TD_ARGMAX_NONE) ? 0 : (int)bi;
   if (tokens) tokens[r] = tok;
   if (r == rows - 1) *token_word = tok;
 }
@@ -544,15 +603,18 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
     e = (int)hipGetLastError();       \
     if (e) return e;                  \
   } while (0)
+  const int hb = H / 256;  // column blocks of the residual stream (H is a multiple of 256)
+  const dim3 rgrid(hb, n);
   TD_CK((blk_embed<<<n, 256, 0, st>>>(P.embed, tokens, H, P.V, B->x, P.err)));
   for (int l = 0; l < L; ++l) {
     const td_layer_dev& Ld = B->layers_host[l];
     // x += the previous layer's down-projection slices; attention RMSNorm
-    TD_CK((blk_resid_norm<<<n, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, P.eps, Ld.attn_norm, B->xn)));
+    TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, B->ssq)));
+    TD_CK((blk_norm<<<rgrid, 256, 0, st>>>(B->x, B->ssq, H, P.eps, Ld.attn_norm, B->xn)));
     if ((e = gemm(P.wf, ncu, B->xn, H, n, H, Ld.w[0], Ld.s[0], P.qkv_rows, B->y, part, P.qkv_rows, &S, st))) return e;
-    TD_CK((blk_qkv_post<<<n, 256, 0, st>>>(S == 1 ? B->y : part, S, (size_t)n * P.qkv_rows, P.qkv_rows, qd, P.kvd,
-                                           d, P.nkv, P.max_ctx, l, pos0, Ld.bias, P.rope_cs, P.attn_scale, B->q,
-                                           P.kc, P.vc)));
+    TD_CK((blk_qkv_post<<<dim3((P.qkv_rows / 2 + 255) / 256, n), 256, 0, st>>>(
+        S == 1 ? B->y : part, S, (size_t)n * P.qkv_rows, P.qkv_rows, qd, P.kvd, d, P.nkv, P.max_ctx, l, pos0, Ld.bias,
+        P.rope_cs, P.attn_scale, B->q, P.kc, P.vc)));
     const dim3 agrid(n, P.nkv);
     if (d == 64)
       TD_CK((blk_attn<64><<<agrid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0,
@@ -562,18 +624,25 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
                                                   B->ao)));
     // the O and down projections always land in part (slice 0 when unsplit)
     if ((e = gemm(P.wf, ncu, B->ao, qd, n, qd, Ld.w[1], Ld.s[1], H, part, part, H, &S, st))) return e;
-    TD_CK((blk_resid_norm<<<n, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, P.eps, Ld.mlp_norm, B->xn)));
+    TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, B->ssq)));
+    TD_CK((blk_norm<<<rgrid, 256, 0, st>>>(B->x, B->ssq, H, P.eps, Ld.mlp_norm, B->xn)));
     if ((e = gemm(P.wf, ncu, B->xn, H, n, H, Ld.w[2], Ld.s[2], 2 * I, B->y, part, 2 * I, &S, st))) return e;
-    TD_CK((blk_swiglu<<<n, 256, 0, st>>>(S == 1 ? B->y : part, S, (size_t)n * 2 * I, I, B->act)));
+    TD_CK((blk_swiglu<<<dim3((I + 255) / 256, n), 256, 0, st>>>(S == 1 ? B->y : part, S, (size_t)n * 2 * I, I,
+                                                               B->act)));
     if ((e = gemm(P.wf, ncu, B->act, I, n, I, Ld.w[3], Ld.s[3], H, part, part, H, &S_prev, st))) return e;
   }
-  TD_CK((blk_resid_norm<<<n, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, P.eps, P.final_norm, B->xn)));
+  TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, B->ssq)));
+  TD_CK((blk_norm<<<rgrid, 256, 0, st>>>(B->x, B->ssq, H, P.eps, P.final_norm, B->xn)));
   const int r0 = all_logits ? 0 : n - 1, rows = all_logits ? n : 1;
   if ((e = gemm(TD_WF_BF16, ncu, B->xn + (size_t)r0 * H, H, rows, H, (const uint8_t*)P.head, nullptr, P.V, logits,
                 part, P.V, &S, st)))
     return e;
-  if (S > 1) TD_CK((blk_sum_parts<<<rows, 256, 0, st>>>(part, S, (size_t)rows * P.V, P.V, logits)));
-  TD_CK((blk_argmax<<<rows, 256, 0, st>>>(logits, P.V, argmax_out, P.token_out, rows, P.err)));
+  if (S > 1) TD_CK((blk_sum_parts<<<dim3((P.V + 255) / 256, rows), 256, 0, st>>>(part, S, (size_t)rows * P.V, P.V,
+                                                                                 logits)));
+  const int ch = (P.V + TD_BLOCK_ARGMAX_SLICES - 1) / TD_BLOCK_ARGMAX_SLICES;
+  TD_CK((blk_argmax_part<<<dim3(TD_BLOCK_ARGMAX_SLICES, rows), 256, 0, st>>>(logits, P.V, ch, B->cand, P.err)));
+  TD_CK((blk_argmax_final<<<(rows + 63) / 64, 64, 0, st>>>(B->cand, TD_BLOCK_ARGMAX_SLICES, rows, argmax_out,
+                                                           P.token_out)));
 #undef TD_CK
   return 0;
 }

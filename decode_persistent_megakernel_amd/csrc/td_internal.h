@@ -202,17 +202,22 @@ struct td_blockparams {
   float* xn;                       // [n][H] RMSNorm of x (a GEMM input)
   float* y;                        // [n][max(qkv_rows, 2 I)] QKV or gate/up output
   float* act;                      // [n][I] SiLU(gate) * up (a GEMM input)
+  float* ssq;                      // [n][H / 256] block sums of squares of x (RMSNorm)
+  uint2* cand;                     // [n][TD_BLOCK_ARGMAX_SLICES] greedy-token candidates
   float* part;                     // split-K partial slices, td_block_part_floats() floats
   float* q;                        // [n][qd] rotated, scaled queries
   float* ao;                       // [n][qd] attention output
 };
 
+#define TD_BLOCK_ARGMAX_SLICES 64  // column slices of a logits row searched in parallel
+
 // Split-K plan of one block GEMM (N weight rows, K columns, 64-row tiles):
-// GEMMs with fewer tiles than CUs cut K into S slices of KS columns (a
-// multiple of 64) so that about two workgroups per CU run.  Returns S.
+// GEMMs with fewer tiles than two per CU cut K into S slices of KS columns (a
+// multiple of 64), as many as keep the grid within two workgroups per CU (the
+// most that are resident at once), so that every CU runs two.  Returns S.
 static inline int td_block_split(int N, int K, int ncu, int* KS) {
   const int tiles = (N + 63) / 64, chunks = K / 64;
-  int s = tiles >= ncu ? 1 : (2 * ncu + tiles - 1) / tiles;
+  int s = tiles >= 2 * ncu ? 1 : (2 * ncu) / tiles;
   if (s > chunks) s = chunks;
   if (s < 1) s = 1;
   const int per = (chunks + s - 1) / s;
