@@ -4,9 +4,10 @@
 Workload (default): the Llama-3.2-1B-shaped bf16 decoder (16 layers, hidden
 2048, 32 q / 8 kv heads of 64, intermediate 8192, vocab 128256, tied
 embeddings, RoPE theta 500000) with seeded random-init weights ~N(0, 0.02).
-A seeded random 512-token prompt is prefilled into the K/V cache by running it
-through the decode step itself; then greedy decode steps run at positions
-512, 513, ... with the token chained on the device.  A "step" is one decode
+A seeded random 512-token prompt is prefilled into the K/V cache by the block
+forward (td_forward_block, 64 tokens per call on the matrix cores; its rate is
+reported as "prefill"); then greedy decode steps run at positions 512, 513, ...
+with the token chained on the device.  A "step" is one decode
 step (one token).  W warmup steps run first (positions 512..), then the K timed
 steps restart at position 512 (each step rewrites its own cache row first).
 
@@ -103,6 +104,8 @@ def main() -> int:
                     help="timed steps of each baseline (one launch per step, per-op launches, graph replay); 0 = skip")
     ap.add_argument("--steps-per-launch", type=int, default=64,
                     help="greedy steps per td_decode_loop launch (1 = one td_decode_step launch per token)")
+    ap.add_argument("--prefill-block", type=int, default=64,
+                    help="prompt tokens per td_forward_block call (0 = prefill through the decode step)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -130,6 +133,7 @@ def main() -> int:
     dm = td.DeviceModel(model, device=dev)
     dec = td.Decoder(dm, cfg.max_ctx)
     start = cfg.start_pos
+    prefill = None
     if cfg.kv_prefix:
         k, v = synth.kv_cache(cfg)
         kv = td.KVCache(cfg, cfg.max_ctx, device=dev, k=k, v=v)
@@ -138,15 +142,36 @@ def main() -> int:
     else:
         kv = td.KVCache(cfg, cfg.max_ctx, device=dev)
         prompt = synth.prompt(cfg)
-        tok = torch.empty(1, dtype=torch.int32, device=dev)
         scratch_logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
         t_pf = time.perf_counter()
-        for i, t in enumerate(prompt):
-            tok.fill_(int(t))
-            dec.step(tok.data_ptr(), i, kv, scratch_logits)
-        torch.cuda.synchronize()
-        print(f"[bench] prefilled {len(prompt)} tokens through the decode step in "
-              f"{time.perf_counter() - t_pf:.2f}s", file=sys.stderr, flush=True)
+        if args.prefill_block > 0:
+            blk = max(1, min(args.prefill_block, td._lib.TD_MAX_BLOCK))
+            ptoks = torch.from_numpy(np.ascontiguousarray(prompt, dtype=np.int32)).to(dev)
+            pstream = torch.cuda.current_stream()
+
+            def prefill_pass():
+                for i in range(0, len(prompt), blk):
+                    dec.forward_block(ptoks[i:i + blk], i, kv, scratch_logits, stream=pstream)
+
+            prefill_pass()  # untimed (first-call setup)
+            torch.cuda.synchronize()
+            pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            pe0.record(pstream)
+            prefill_pass()  # the same positions again: the cache rows are rewritten with the same values
+            pe1.record(pstream)
+            torch.cuda.synchronize()
+            pms = pe0.elapsed_time(pe1)
+            prefill = {"tokens": len(prompt), "block_rows": blk, "calls": (len(prompt) + blk - 1) // blk,
+                       "ms": round(pms, 3), "tokens_per_s": round(len(prompt) / (pms / 1e3), 1),
+                       "path": "td_forward_block (MFMA GEMMs, fp32 inputs split into three bf16 parts)"}
+        else:
+            tok = torch.empty(1, dtype=torch.int32, device=dev)
+            for i, t in enumerate(prompt):
+                tok.fill_(int(t))
+                dec.step(tok.data_ptr(), i, kv, scratch_logits)
+            torch.cuda.synchronize()
+        print(f"[bench] prefilled {len(prompt)} tokens in {time.perf_counter() - t_pf:.2f}s", file=sys.stderr,
+              flush=True)
         first = torch.empty(1, dtype=torch.int32, device=dev)
         first.copy_(torch.tensor([td.read_device_i32(dec.token_ptr())], dtype=torch.int32))
     st = dec.status()
@@ -317,6 +342,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "baselines": baselines,
+        "prefill": prefill,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(out), flush=True)
