@@ -130,7 +130,7 @@ void print_config(const Workload& w) {
   printf("{\"name\": \"%s\", \"n_layers\": %d, \"hidden\": %d, \"n_q_heads\": %d, \"n_kv_heads\": %d, "
          "\"head_dim\": %d, \"intermediate\": %d, \"vocab\": %d, \"rope_theta\": %.17g, \"rms_eps\": %.17g, "
          "\"weight_format\": %d, \"qkv_bias\": %d, \"tied\": %d, \"prompt_len\": %d, \"kv_prefix\": %d, "
-         "\"decode_steps\": %d, \"max_ctx\": %d, \"seed\": %d}\n",
+         "\"decode_steps\": %d, \"max_ctx\": %d, \"seed\": %d, \"n_experts\": 0, \"top_k\": 0}\n",
          w.name, w.layers, w.hidden, w.nq, w.nkv, w.d, w.inter, w.vocab, w.theta, w.eps, w.wf, w.bias, w.tied,
          w.prompt, w.kv_prefix, w.steps, w.max_ctx, w.seed);
 }

@@ -38,12 +38,13 @@ class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
                                               "intermediate", "vocab", "max_ctx")] + \
                [("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
-                ("weight_format", ctypes.c_int32), ("qkv_bias", ctypes.c_int32)]
+                ("weight_format", ctypes.c_int32), ("qkv_bias", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
 
 class _Layer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "w_qkv", "s_qkv", "b_qkv", "w_o", "s_o", "mlp_norm",
-                                               "w_gu", "s_gu", "w_d", "s_d")]
+                                               "w_gu", "s_gu", "w_d", "s_d", "w_router")]
 
 
 class _Weights(ctypes.Structure):
@@ -52,7 +53,8 @@ class _Weights(ctypes.Structure):
 
 
 class _Trace(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("x_in", "qkv", "attn", "x_mid", "act", "x_out", "h_final")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x_in", "qkv", "attn", "x_mid", "act", "x_out", "h_final",
+                                               "expert_ids", "expert_w")]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -81,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.orc_silu.argtypes = [d]
         L.orc_argmax.restype = i32
         L.orc_argmax.argtypes = [vp, i32, vp]
+        L.orc_route.restype = i32
+        L.orc_route.argtypes = [vp, i32, i32, vp, vp]
         L.orc_step.restype = i32
         L.orc_step.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), i32, i32, vp, vp, vp, i32]
         L.orc_step_traced.restype = i32
@@ -165,6 +169,15 @@ def argmax(logits: np.ndarray):
     return int(i), bool(bad.value)
 
 
+def route(z: np.ndarray, k: int):
+    """MoE routing of router logits z[E]: (status, ids[k], weights[k])."""
+    x = np.ascontiguousarray(z, dtype=np.float64)
+    ids = np.zeros(max(k, 1), dtype=np.int32)
+    w = np.zeros(max(k, 1), dtype=np.float64)
+    r = lib().orc_route(_p(x), x.size, int(k), _p(ids), _p(w))
+    return int(r), ids[:k], w[:k]
+
+
 # --------------------------------------------------------------------------- whole step
 
 class Oracle:
@@ -178,13 +191,14 @@ class Oracle:
         self.c = _Config(n_layers=cfg.n_layers, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads,
                          n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, intermediate=cfg.intermediate,
                          vocab=cfg.vocab, max_ctx=max_ctx or cfg.max_ctx, rope_theta=cfg.rope_theta,
-                         rms_eps=cfg.rms_eps, weight_format=cfg.weight_format, qkv_bias=int(cfg.qkv_bias))
+                         rms_eps=cfg.rms_eps, weight_format=cfg.weight_format, qkv_bias=int(cfg.qkv_bias),
+                         n_experts=cfg.n_experts, top_k=cfg.top_k)
         self._layers = (_Layer * cfg.n_layers)()
         for i, L in enumerate(model.layers):
             self._layers[i] = _Layer(attn_norm=_p(L.attn_norm), w_qkv=_p(L.qkv.w), s_qkv=_p(L.qkv.s),
                                      b_qkv=_p(L.qkv_bias), w_o=_p(L.o.w), s_o=_p(L.o.s), mlp_norm=_p(L.mlp_norm),
                                      w_gu=_p(L.gate_up.w), s_gu=_p(L.gate_up.s), w_d=_p(L.down.w),
-                                     s_d=_p(L.down.s))
+                                     s_d=_p(L.down.s), w_router=_p(L.router))
         self.w = _Weights(embed=_p(model.embed), head=_p(model.head), final_norm=_p(model.final_norm),
                           layers=self._layers)
         ctx = self.c.max_ctx
@@ -211,6 +225,9 @@ class Oracle:
             "x_in": np.zeros(H), "qkv": np.zeros((L, cfg.qkv_rows)), "attn": np.zeros((L, cfg.q_dim)),
             "x_mid": np.zeros((L, H)), "act": np.zeros((L, I)), "x_out": np.zeros((L, H)), "h_final": np.zeros(H),
         }
+        if cfg.n_experts:
+            t["expert_ids"] = np.zeros((L, cfg.top_k), dtype=np.int32)
+            t["expert_w"] = np.zeros((L, cfg.top_k))
         tr = _Trace(**{k: _p(v) for k, v in t.items()})
         logits = np.empty(cfg.vocab, dtype=np.float64)
         r = lib().orc_step_traced(ctypes.byref(self.c), ctypes.byref(self.w), int(token), int(pos), _p(self.k),

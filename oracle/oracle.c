@@ -177,6 +177,53 @@ int32_t orc_argmax(const double* logits, int32_t n, int32_t* nonfinite) {
     return best;
 }
 
+/* ---------------------------------------------------------------- MoE routing */
+
+/* The router of a mixture-of-experts layer ("One launch per token", its 64-expert
+ * MoE section): each token goes to a fixed number k of the E experts, chosen at
+ * run time from the router's scores, and the experts' outputs are combined as a
+ * weighted sum.  The pages fix neither the scores' normalisation nor the
+ * weights; read plainly, as in the model they name, the weights are the softmax
+ * of all E router logits taken at the k chosen experts (not renormalised over
+ * the k), and the k chosen are those with the largest logits.  The choice is an
+ * integer decided on floating point, so it is made on logits rounded to fp32,
+ * the precision the GPU decides in; ties go to the lowest expert id. */
+int32_t orc_route(const double* z, int32_t E, int32_t k, int32_t* ids, double* weights) {
+    if (!z || !ids || !weights || E <= 0 || k <= 0 || k > E) return ORC_E_ARG;
+    double m = z[0];
+    for (int32_t e = 0; e < E; ++e) {
+        if (!isfinite(z[e])) return ORC_E_NONFINITE;
+        if (z[e] > m) m = z[e];
+    }
+    double sum = 0.0;
+    for (int32_t e = 0; e < E; ++e) sum += exp(z[e] - m);
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t best = -1;
+        float bv = 0.0f;
+        for (int32_t e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            float v = (float)z[e];
+            if (best < 0 || bv < v) { bv = v; best = e; }   /* strict: ties keep the lower id */
+        }
+        taken[best] = 1;
+        ids[j] = best;
+        weights[j] = exp(z[best] - m) / sum;
+    }
+    free(taken);
+    return ORC_OK;
+}
+
+/* Expert e's block of a stacked [E][rows][cols] linear and of its scales. */
+static const void* expert_w(const void* w, int32_t fmt, int32_t e, int32_t rows, int32_t cols) {
+    if (fmt == ORC_WF_INT4_G64) return (const uint8_t*)w + (int64_t)e * rows * (cols / 2);
+    return (const uint16_t*)w + (int64_t)e * rows * cols;
+}
+static const uint16_t* expert_s(const uint16_t* s, int32_t fmt, int32_t e, int32_t rows, int32_t cols) {
+    if (fmt != ORC_WF_INT4_G64 || !s) return NULL;
+    return s + (int64_t)e * rows * (cols / 64);
+}
+
 /* ---------------------------------------------------------------- the step */
 
 static int32_t check_cfg(const orc_config* c) {
@@ -188,6 +235,7 @@ static int32_t check_cfg(const orc_config* c) {
         ((c->hidden % 64) || (c->intermediate % 64) || ((c->n_q_heads * c->head_dim) % 64)))
         return ORC_E_ARG;
     if (c->weight_format != ORC_WF_BF16 && c->weight_format != ORC_WF_INT4_G64) return ORC_E_ARG;
+    if (c->n_experts < 0 || (c->n_experts > 0 && (c->top_k < 1 || c->top_k > c->n_experts))) return ORC_E_ARG;
     return ORC_OK;
 }
 
@@ -258,13 +306,49 @@ int32_t orc_step_traced(const orc_config* c, const orc_weights* w, int32_t token
 
         /* 7. RMSNorm, gate and up projections, SiLU(gate) * up ([tiles] sec. 4 "FFN"). */
         orc_rmsnorm(x, L->mlp_norm, H, c->rms_eps, h);
-        orc_linear(L->w_gu, L->s_gu, fmt, 2 * I, H, h, gu, nthreads);
-        for (int32_t r = 0; r < I; ++r) act[r] = orc_silu(gu[r]) * gu[I + r];
-        if (tr && tr->act) memcpy(tr->act + (int64_t)l * I, act, sizeof(double) * I);
+        if (c->n_experts == 0) {
+            orc_linear(L->w_gu, L->s_gu, fmt, 2 * I, H, h, gu, nthreads);
+            for (int32_t r = 0; r < I; ++r) act[r] = orc_silu(gu[r]) * gu[I + r];
+            if (tr && tr->act) memcpy(tr->act + (int64_t)l * I, act, sizeof(double) * I);
 
-        /* 8. down projection and residual add ([metal] "GEMV (Down) + Residual Add"). */
-        orc_linear(L->w_d, L->s_d, fmt, H, I, act, y, nthreads);
-        for (int32_t i = 0; i < H; ++i) x[i] += y[i];
+            /* 8. down projection and residual add ([metal] "GEMV (Down) + Residual Add"). */
+            orc_linear(L->w_d, L->s_d, fmt, H, I, act, y, nthreads);
+            for (int32_t i = 0; i < H; ++i) x[i] += y[i];
+        } else {
+            /* 7-8 (MoE, [launch] 64-expert section): the router scores the E experts,
+             * the k chosen run the same SiLU-gated MLP on h, and their down
+             * projections are added to the residual weighted by the router
+             * probabilities, in the order chosen. */
+            const int32_t E = c->n_experts, k = c->top_k;
+            double* z = (double*)calloc((size_t)E, sizeof(double));
+            double* ysum = (double*)calloc((size_t)H, sizeof(double));
+            int32_t* ids = (int32_t*)calloc((size_t)k, sizeof(int32_t));
+            double* wts = (double*)calloc((size_t)k, sizeof(double));
+            int32_t rr = L->w_router ? ORC_OK : ORC_E_ARG;
+            if (rr == ORC_OK) {
+                orc_linear(L->w_router, NULL, ORC_WF_BF16, E, H, h, z, nthreads);
+                rr = orc_route(z, E, k, ids, wts);
+            }
+            if (rr == ORC_OK) {
+                for (int32_t j = 0; j < k; ++j) {
+                    const int32_t e = ids[j];
+                    orc_linear(expert_w(L->w_gu, fmt, e, 2 * I, H), expert_s(L->s_gu, fmt, e, 2 * I, H), fmt,
+                               2 * I, H, h, gu, nthreads);
+                    for (int32_t r = 0; r < I; ++r) act[r] = gu[I + r] * orc_silu(gu[r]);
+                    orc_linear(expert_w(L->w_d, fmt, e, H, I), expert_s(L->s_d, fmt, e, H, I), fmt, H, I, act, y,
+                               nthreads);
+                    for (int32_t i = 0; i < H; ++i) ysum[i] += wts[j] * y[i];
+                }
+                for (int32_t i = 0; i < H; ++i) x[i] += ysum[i];
+                if (tr && tr->expert_ids) memcpy(tr->expert_ids + (int64_t)l * k, ids, sizeof(int32_t) * k);
+                if (tr && tr->expert_w) memcpy(tr->expert_w + (int64_t)l * k, wts, sizeof(double) * k);
+            }
+            free(z); free(ysum); free(ids); free(wts);
+            if (rr != ORC_OK) {
+                free(x); free(h); free(y); free(qkv); free(att); free(gu); free(act);
+                return rr;
+            }
+        }
         if (tr && tr->x_out) memcpy(tr->x_out + (int64_t)l * H, x, sizeof(double) * H);
     }
 

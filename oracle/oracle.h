@@ -33,6 +33,8 @@ typedef struct {
     double rope_theta, rms_eps;
     int32_t weight_format; /* ORC_WF_* for the layer linears; embedding and head are bf16 */
     int32_t qkv_bias;      /* nonzero: b_qkv is added after the QKV projection */
+    int32_t n_experts;     /* > 0: the MLP is a mixture of n_experts experts (0: dense) */
+    int32_t top_k;         /* experts each token is routed to (MoE only) */
 } orc_config;
 
 typedef struct {
@@ -43,6 +45,9 @@ typedef struct {
     const uint16_t* mlp_norm;                  /* bf16 [H] */
     const void* w_gu; const uint16_t* s_gu;    /* [2I, H]: gate rows then up rows */
     const void* w_d; const uint16_t* s_d;      /* [H, I] */
+    const uint16_t* w_router;                  /* MoE: bf16 [E, H]; w_gu is [E][2I][H] and
+                                                  w_d [E][H][I] (expert e's block at e * rows),
+                                                  their scales likewise */
 } orc_layer;
 
 typedef struct {
@@ -67,6 +72,11 @@ void orc_attention(const double* q, const uint16_t* K, const uint16_t* V, int32_
                    int32_t head_dim, double* out);
 double orc_silu(double z);
 int32_t orc_argmax(const double* logits, int32_t n, int32_t* nonfinite);
+/* MoE routing of one token: the k experts with the largest router logits z[E]
+ * (compared rounded to fp32; ties to the lowest id), in that order, into ids[k],
+ * and their softmax probabilities over all E experts into weights[k].  Returns
+ * ORC_OK, ORC_E_ARG, or ORC_E_NONFINITE when a logit is NaN or infinite. */
+int32_t orc_route(const double* z, int32_t E, int32_t k, int32_t* ids, double* weights);
 
 /* The whole step at position `pos` for input `token`: writes K/V row `pos` of
  * every layer into the caches, reads rows 0..pos, and (when logits != NULL)
@@ -78,7 +88,8 @@ int32_t orc_step(const orc_config* cfg, const orc_weights* w, int32_t token, int
 
 /* The same step with every intermediate vector written out (tests only):
  * x_in[H] (embedding), per layer: qkv[(nq+2nkv)d] after bias and RoPE,
- * attn[nq d], x_mid[H], act[I], x_out[H]; then h_final[H].  Any pointer may be NULL. */
+ * attn[nq d], x_mid[H], act[I] (dense MLP only), x_out[H]; then h_final[H]; for a
+ * MoE model each layer's routed expert ids and weights.  Any pointer may be NULL. */
 typedef struct {
     double* x_in;
     double* qkv;    /* [n_layers][(nq+2nkv)d] */
@@ -87,6 +98,8 @@ typedef struct {
     double* act;    /* [n_layers][I] */
     double* x_out;  /* [n_layers][H] */
     double* h_final;/* [H] */
+    int32_t* expert_ids; /* MoE: [n_layers][top_k] routed experts */
+    double* expert_w;    /* MoE: [n_layers][top_k] their weights */
 } orc_trace;
 int32_t orc_step_traced(const orc_config* cfg, const orc_weights* w, int32_t token, int32_t pos,
                         uint16_t* k_cache, uint16_t* v_cache, double* logits, int32_t nthreads,

@@ -48,6 +48,8 @@ class Config:
     decode_steps: int
     max_ctx: int
     seed: int
+    n_experts: int = 0          # mixture-of-experts MLP: experts per layer (0: dense MLP)
+    top_k: int = 0              # experts each token is routed to
 
     @property
     def qkv_rows(self) -> int:
@@ -90,7 +92,15 @@ CONFIGS: Dict[str, Config] = {
                               rope_theta=500000.0, rms_eps=1e-5, weight_format=WF_INT4_G64,
                               qkv_bias=False, tied=True, prompt_len=0, kv_prefix=8192,
                               decode_steps=64, max_ctx=8256, seed=1004),
+    # f3: a mixture-of-experts decoder of the OLMoE-1B-7B shape (64 experts of
+    # intermediate 1024, 8 routed per token; 16 query and 16 kv heads of 128;
+    # vocab 50304; untied), with a random K/V prefix of 512 positions.
+    "olmoe": _cfg(name="olmoe", n_layers=16, hidden=2048, n_q_heads=16, n_kv_heads=16, head_dim=128,
+                  intermediate=1024, vocab=50304, rope_theta=10000.0, rms_eps=1e-5, weight_format=WF_BF16,
+                  qkv_bias=False, tied=False, prompt_len=0, kv_prefix=512, decode_steps=64, max_ctx=576,
+                  seed=1005, n_experts=64, top_k=8),
 }
+# the workloads of the native driver (td_bench) and of the dense decode kernel
 CONFIG_ORDER: List[str] = ["tiny", "llama1b", "tinyllama_int4", "qwen1p5b", "llama1b_int4_long"]
 
 
@@ -200,8 +210,9 @@ class Layer:
     qkv_bias: Optional[np.ndarray]  # bf16 [(nq + 2 nkv) d]
     o: Linear                  # [H, nq d]
     mlp_norm: np.ndarray       # bf16 [H]
-    gate_up: Linear            # [2 I, H]: gate rows, then up rows
-    down: Linear               # [H, I]
+    gate_up: Linear            # [2 I, H]: gate rows, then up rows; MoE: [E][2 I][H], expert e's block at rows 2 I e
+    down: Linear               # [H, I]; MoE: [E][H][I], expert e's block at rows H e
+    router: Optional[np.ndarray] = None  # MoE only: bf16 [E, H]
 
 
 @dataclasses.dataclass
@@ -220,6 +231,21 @@ class Model:
                 tot += lin.w.nbytes + (lin.s.nbytes if lin.s is not None else 0)
             if L.qkv_bias is not None:
                 tot += L.qkv_bias.nbytes
+            if L.router is not None:
+                tot += L.router.nbytes
+        return tot
+
+    def active_nbytes(self) -> int:
+        """Bytes one decode step reads from the weights: a MoE layer reads the router
+        and the top_k routed experts only."""
+        c = self.cfg
+        if not c.n_experts:
+            return self.nbytes()
+        tot = self.nbytes()
+        for L in self.layers:
+            for lin in (L.gate_up, L.down):
+                per = (lin.w.nbytes + (lin.s.nbytes if lin.s is not None else 0)) // c.n_experts
+                tot -= per * (c.n_experts - c.top_k)
         return tot
 
 
@@ -244,14 +270,19 @@ def make_model(cfg: Config) -> Model:
         bias = None
         if cfg.qkv_bias:
             bias = bf16_normal(cfg.qkv_rows, key(seed, l, "qkv_bias"), WEIGHT_STD)
+        E = max(cfg.n_experts, 1)
+        router = None
+        if cfg.n_experts:
+            router = bf16_normal(E * H, key(seed, l, "router"), WEIGHT_STD).reshape(E, H)
         layers.append(Layer(
             attn_norm=bf16_const(H, 1.0),
             qkv=_linear(cfg, l, "qkv", cfg.qkv_rows, H),
             qkv_bias=bias,
             o=_linear(cfg, l, "o", H, cfg.q_dim),
             mlp_norm=bf16_const(H, 1.0),
-            gate_up=_linear(cfg, l, "gate_up", 2 * I, H),
-            down=_linear(cfg, l, "down", H, I),
+            gate_up=_linear(cfg, l, "gate_up", E * 2 * I, H),
+            down=_linear(cfg, l, "down", E * H, I),
+            router=router,
         ))
     return Model(cfg=cfg, embed=embed, head=head, final_norm=bf16_const(H, 1.0), layers=layers)
 

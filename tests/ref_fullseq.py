@@ -84,10 +84,34 @@ def forward(model, tokens):
         o = np.einsum("hts,shd->thd", p, vv).reshape(T, nq * d)
         x = x + o @ dequant(L.o).T
         h = rmsnorm(x, bf16_to_f64(L.mlp_norm), cfg.rms_eps)
-        gu = h @ dequant(L.gate_up).T
         I = cfg.intermediate
-        a = gu[:, :I] * scipy.special.expit(gu[:, :I]) * gu[:, I:]
-        x = x + a @ dequant(L.down).T
+        if not cfg.n_experts:
+            gu = h @ dequant(L.gate_up).T
+            a = gu[:, :I] * scipy.special.expit(gu[:, :I]) * gu[:, I:]
+            x = x + a @ dequant(L.down).T
+        else:
+            x = x + moe(cfg, L, h)
     h = rmsnorm(x, bf16_to_f64(model.final_norm), cfg.rms_eps)
     logits = h @ bf16_to_f64(model.head).T
     return logits, ks, vs
+
+
+def moe(cfg, L, h):
+    """Mixture-of-experts MLP of every row of h at once: the router's softmax
+    over all experts (torch), the top_k experts by torch.topk on the fp32-rounded
+    logits (the precision the decision is made in), every expert's SiLU-gated MLP
+    evaluated for all rows as one batched product, and the chosen ones gathered
+    and combined with their probabilities."""
+    E, k, I, H = cfg.n_experts, cfg.top_k, cfg.intermediate, cfg.hidden
+    z = torch.from_numpy(h @ bf16_to_f64(L.router).T)                  # [T, E]
+    prob = torch.softmax(z, dim=-1)
+    _, ids = torch.topk(z.to(torch.float32), k, dim=-1, sorted=True)   # [T, k]
+    wgu = torch.from_numpy(dequant(L.gate_up)).reshape(E, 2 * I, H)
+    wd = torch.from_numpy(dequant(L.down)).reshape(E, H, I)
+    ht = torch.from_numpy(h)
+    gu = torch.einsum("eoh,th->teo", wgu, ht)                           # [T, E, 2I]
+    a = torch.nn.functional.silu(gu[..., :I]) * gu[..., I:]
+    y = torch.einsum("ehi,tei->teh", wd, a)                             # [T, E, H]
+    ysel = torch.gather(y, 1, ids[..., None].expand(-1, -1, H))         # [T, k, H]
+    psel = torch.gather(prob, 1, ids)                                   # [T, k]
+    return (psel[..., None] * ysel).sum(dim=1).numpy()

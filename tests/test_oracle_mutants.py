@@ -34,6 +34,16 @@ MUTANTS = {
     "v_from_k": ("orc_round_bf16(qkv[qd + kvd + g * d + i]);", "orc_round_bf16(qkv[qd + g * d + i]);"),
     "argmax_last_tie": ("if (best < 0 || v > bv)", "if (best < 0 || v >= bv)"),
     "bf16_round_truncates": ("if (rest > 0x8000u || (rest == 0x8000u && (top & 1u))) top += 1u;", ""),
+    "route_last_tie": ("if (best < 0 || bv < v)", "if (best < 0 || bv <= v)"),
+    "route_unnormalised": ("weights[j] = exp(z[best] - m) / sum;", "weights[j] = exp(z[best] - m);"),
+    "route_smallest": ("if (best < 0 || bv < v)", "if (best < 0 || bv > v)"),
+    "moe_swiglu_swap": ("gu[I + r] * orc_silu(gu[r])", "gu[r] * orc_silu(gu[I + r])"),
+    "moe_unweighted": ("ysum[i] += wts[j] * y[i];", "ysum[i] += y[i];"),
+    "moe_residual_dropped": ("for (int32_t i = 0; i < H; ++i) x[i] += ysum[i];",
+                             "for (int32_t i = 0; i < H; ++i) x[i] = ysum[i];"),
+    "moe_expert_offset": ("return (const uint16_t*)w + (int64_t)e * rows * cols;",
+                          "return (const uint16_t*)w + (int64_t)e * cols;"),
+    "moe_scale_offset": ("return s + (int64_t)e * rows * (cols / 64);", "return s;"),
 }
 
 PINS = [
@@ -56,6 +66,12 @@ PINS = [
      {"name": "gqa4_bias_int4", "over": dict(n_q_heads=8, n_kv_heads=2, qkv_bias=True,
                                              weight_format=oracle.WF_INT4_G64, tied=False, hidden=128,
                                              intermediate=192, vocab=500, head_dim=32)}),
+    (P.test_route_closed_form_example, {}),
+    (P.test_moe_identical_experts_reduce_to_dense, {}),
+    (P.test_moe_decode_matches_full_sequence_reference, {"name": "moe_bf16", "over": dict(n_experts=8, top_k=2)}),
+    (P.test_moe_decode_matches_full_sequence_reference,
+     {"name": "moe_int4", "over": dict(n_experts=6, top_k=3, weight_format=oracle.WF_INT4_G64, hidden=128,
+                                       intermediate=192, tied=False)}),
 ]
 
 

@@ -358,3 +358,103 @@ def test_tiny_greedy_regression_file():
     got = make_golden.tiny_run()
     assert got["prompt"] == ref["prompt"] and got["greedy"] == ref["greedy"]
     np.testing.assert_allclose(got["max_logit"], ref["max_logit"], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- MoE routing and MLP
+
+def test_route_closed_form_example():
+    """Router logits ln 4, ln 2, 0, 0: the softmax is 1/2, 1/4, 1/8, 1/8 exactly in
+    closed form; the top 3 are experts 0, 1, then 2 (the tie of 2 and 3 goes to
+    the lower id)."""
+    z = np.array([math.log(4.0), math.log(2.0), 0.0, 0.0])
+    r, ids, w = oracle.route(z, 3)
+    assert r == 0
+    assert ids.tolist() == [0, 1, 2]
+    np.testing.assert_allclose(w, [0.5, 0.25, 0.125], rtol=1e-15)
+    # order follows the logits, not the ids
+    r, ids, w = oracle.route(np.array([0.0, 0.0, math.log(4.0), math.log(2.0)]), 2)
+    assert ids.tolist() == [2, 3]
+    np.testing.assert_allclose(w, [0.5, 0.25], rtol=1e-15)
+    # equal after rounding to fp32: a tie, the lower id first
+    r, ids, w = oracle.route(np.array([1.0 + 1e-12, 1.0, -5.0]), 1)
+    assert ids.tolist() == [0]
+    r, ids, w = oracle.route(np.array([1.0, 1.0 + 1e-12, -5.0]), 1)
+    assert ids.tolist() == [0]
+    # all experts: the weights are the whole softmax and sum to 1
+    zz = RNG.normal(size=16)
+    r, ids, w = oracle.route(zz, 16)
+    assert sorted(ids.tolist()) == list(range(16))
+    np.testing.assert_allclose(w.sum(), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(w, scipy.special.softmax(zz)[ids], rtol=1e-14)
+
+
+def test_route_errors():
+    assert oracle.route(np.array([0.0, np.nan]), 1)[0] == oracle.E_NONFINITE
+    assert oracle.route(np.array([0.0, np.inf]), 1)[0] == oracle.E_NONFINITE
+    assert oracle.route(np.array([0.0, 1.0]), 3)[0] == oracle.E_ARG
+    assert oracle.route(np.array([0.0, 1.0]), 0)[0] == oracle.E_ARG
+
+
+def _moe_from_dense(dense, n_experts, top_k, poison_from=None):
+    """A MoE copy of a dense model: every expert is the dense MLP, the router is
+    zero (all logits equal, so the uniform softmax and the lowest ids win);
+    experts from `poison_from` on have NaN weights."""
+    cfg = synth.shrink(dense.cfg, n_experts=n_experts, top_k=top_k)
+    m = synth.make_model(cfg)
+    m.embed, m.head, m.final_norm = dense.embed, dense.head, dense.final_norm
+    for Ld, Lm in zip(dense.layers, m.layers):
+        Lm.attn_norm, Lm.qkv, Lm.qkv_bias, Lm.o, Lm.mlp_norm = Ld.attn_norm, Ld.qkv, Ld.qkv_bias, Ld.o, Ld.mlp_norm
+        Lm.router = np.zeros_like(Lm.router)
+        Lm.gate_up.w = np.ascontiguousarray(np.concatenate([Ld.gate_up.w] * n_experts))
+        Lm.down.w = np.ascontiguousarray(np.concatenate([Ld.down.w] * n_experts))
+        if poison_from is not None:
+            I, H = cfg.intermediate, cfg.hidden
+            Lm.gate_up.w[poison_from * 2 * I:] = 0x7FC0
+            Lm.down.w[poison_from * H:] = 0x7FC0
+    return m
+
+
+def test_moe_identical_experts_reduce_to_dense():
+    """A zero router over E identical experts routes to experts 0..k-1 with
+    weight 1/E each, so the MLP is k/E times the dense one.  With k = E the step
+    is the dense step; with E = 2k (the unrouted half poisoned with NaN) it is
+    the dense step with W_d halved (exact in bf16)."""
+    dense = synth.make_model(tiny_cfg())
+    toks = synth.i32_uniform(6, synth.key(9, 0, "moe"), dense.cfg.vocab)
+    ref = oracle.Oracle(dense)
+    moe = oracle.Oracle(_moe_from_dense(dense, 4, 4))
+    for p, t in enumerate(toks):
+        r0, l0 = ref.step(int(t), p)
+        r1, l1 = moe.step(int(t), p)
+        assert r0 == r1
+        np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+    half = synth.make_model(tiny_cfg())
+    for L in half.layers:
+        L.down.w = bf16_bits(R.bf16_to_f64(L.down.w) * 0.5)
+    ref2 = oracle.Oracle(half)
+    moe2 = oracle.Oracle(_moe_from_dense(dense, 8, 4, poison_from=4))
+    for p, t in enumerate(toks):
+        r0, l0 = ref2.step(int(t), p)
+        r1, l1 = moe2.step(int(t), p)
+        assert r0 == r1 and np.isfinite(l1).all()
+        np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("moe_bf16", dict(n_experts=8, top_k=2)),
+    ("moe_int4", dict(n_experts=6, top_k=3, weight_format=synth.WF_INT4_G64, hidden=128, intermediate=192,
+                      tied=False)),
+])
+def test_moe_decode_matches_full_sequence_reference(name, over):
+    """Incremental MoE decode == the full-sequence forward with torch.topk routing,
+    and the routed experts the oracle reports are torch's."""
+    cfg = tiny_cfg(**over)
+    m = synth.make_model(cfg)
+    toks = synth.i32_uniform(12, synth.key(5, 1, name), cfg.vocab)
+    ref_logits, _, _ = R.forward(m, toks)
+    o = oracle.Oracle(m, max_ctx=16)
+    for p, t in enumerate(toks):
+        nxt, tr = o.step_traced(int(t), p)
+        np.testing.assert_allclose(tr["logits"], ref_logits[p], rtol=0, atol=1e-9)
+        assert nxt == oracle.argmax(ref_logits[p])[0]
+        assert len(set(tr["expert_ids"][0].tolist())) == cfg.top_k
