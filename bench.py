@@ -131,7 +131,10 @@ def main() -> int:
     print(f"[bench] generated {model.nbytes() / 1e9:.2f} GB of weights in {time.perf_counter() - t_gen:.1f}s",
           file=sys.stderr, flush=True)
     dm = td.DeviceModel(model, device=dev)
-    dec = td.Decoder(dm, cfg.max_ctx)
+    moe = cfg.n_experts > 0
+    # a mixture-of-experts model runs on the graph executor (the routing tensor lets one
+    # recording serve every token); the persistent kernel and its token loop are dense only
+    dec = td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_GRAPH if moe else td.TD_EXEC_MEGAKERNEL)
     start = cfg.start_pos
     prefill = None
     if cfg.kv_prefix:
@@ -186,7 +189,7 @@ def main() -> int:
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
     tok_ptr = dec.token_ptr()
     stream = torch.cuda.current_stream()
-    spl = max(1, min(args.steps_per_launch, td._lib.TD_MAX_LOOP_STEPS))
+    spl = 1 if moe else max(1, min(args.steps_per_launch, td._lib.TD_MAX_LOOP_STEPS))
 
     def run(n, record, per_launch=spl):
         """n greedy steps from `first` at positions start.., per_launch steps per
@@ -269,7 +272,8 @@ def main() -> int:
             baselines["single_step_launch"] = {"tokens_per_s": round(nb / (sms.sum() / 1e3), 2),
                                                "ms_per_step": round(float(sms.mean()), 4), "steps": nb,
                                                "launches_per_step": 1}
-        for name, ex in (("per_op", td.TD_EXEC_PER_OP), ("graph", td.TD_EXEC_GRAPH)):
+        for name, ex in ((("per_op", td.TD_EXEC_PER_OP),) if moe else
+                         (("per_op", td.TD_EXEC_PER_OP), ("graph", td.TD_EXEC_GRAPH))):
             bdec = td.Decoder(dm, cfg.max_ctx, executor=ex)
             bdec.step(first.data_ptr(), start, kv, logits, stream=stream)  # warm-up (and graph capture)
             torch.cuda.synchronize()
@@ -287,7 +291,9 @@ def main() -> int:
                 return 1
             bms = np.array([a.elapsed_time(b) for a, b in bev])
             baselines[name] = {"tokens_per_s": round(nb / (bms.sum() / 1e3), 2), "ms_per_step": round(float(bms.mean()), 4),
-                               "steps": nb, "launches_per_step": (6 * cfg.n_layers + 3) if name == "per_op" else 2}
+                               "steps": nb,
+                               "launches_per_step": (((8 if moe else 6) * cfg.n_layers + 3) if name == "per_op"
+                                                     else 2)}
             bdec.close()
             del bdec
     khash = source_hash()
@@ -315,11 +321,14 @@ def main() -> int:
             "workload": f"{cfg.name}: Llama-style decoder, {cfg.n_layers} layers, hidden {cfg.hidden}, "
                         f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv heads x {cfg.head_dim}, intermediate "
                         f"{cfg.intermediate}, vocab {cfg.vocab}, "
-                        f"{'int4 g64' if cfg.weight_format else 'bf16'} weights, greedy decode at positions "
+                        + (f"mixture of {cfg.n_experts} experts, top {cfg.top_k}, " if moe else "")
+                        + f"{'int4 g64' if cfg.weight_format else 'bf16'} weights, greedy decode at positions "
                         f"{start}..{start + n_steps - 1}, batch 1",
             "weights": "int4-g64+fp16-scales" if cfg.weight_format else "bf16",
             "arithmetic": "fp32 accumulate, fp32 activations, bf16 K/V cache",
-            "executor": (f"persistent megakernel, {spl} greedy steps per cooperative launch (in-kernel token loop)"
+            "executor": ("hipGraph replay of the per-op launches (router ids in a device tensor), one per token"
+                         if moe else
+                         f"persistent megakernel, {spl} greedy steps per cooperative launch (in-kernel token loop)"
                          if spl > 1 else "persistent megakernel (one cooperative launch per token)"),
             "steps_per_launch": spl,
             "global_batch": 1,
@@ -332,7 +341,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": f"td_megakernel ({spl} whole decode step{'s' if spl > 1 else ''} per launch)",
+            "kernel": (f"graph of {8 * cfg.n_layers + 3} per-op kernels (one decode step per replay)" if moe else
+                       f"td_megakernel ({spl} whole decode step{'s' if spl > 1 else ''} per launch)"),
             "launches": len(evs),
             "algorithmic_bytes_per_launch": int(round(bytes_launch)),
             "kernel_ms_mean": round(kern_ms, 4),

@@ -70,6 +70,7 @@ class DeviceModel:
                 "w_o": _dev(L.o.w, device), "s_o": _dev(L.o.s, device),
                 "w_gu": _dev(L.gate_up.w, device), "s_gu": _dev(L.gate_up.s, device),
                 "w_d": _dev(L.down.w, device), "s_d": _dev(L.down.s, device),
+                "w_router": _dev(getattr(L, "router", None), device),
             })
 
     def td_config(self, max_ctx: int) -> _lib.TdConfig:
@@ -77,7 +78,8 @@ class DeviceModel:
         return _lib.TdConfig(n_layers=c.n_layers, hidden=c.hidden, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
                              head_dim=c.head_dim, intermediate=c.intermediate, vocab=c.vocab, max_ctx=max_ctx,
                              rope_theta=c.rope_theta, rms_eps=c.rms_eps, weight_format=c.weight_format,
-                             qkv_bias=int(c.qkv_bias))
+                             qkv_bias=int(c.qkv_bias), n_experts=getattr(c, "n_experts", 0),
+                             top_k=getattr(c, "top_k", 0))
 
     def td_weights(self):
         n = len(self.layers)
@@ -128,6 +130,21 @@ class Decoder:
 
     def token_ptr(self) -> int:
         return _lib.lib().td_token_ptr(self._h)
+
+    def routing(self):
+        """The last step's MoE routing as host arrays (ids [L][top_k] int32, weights
+        [L][top_k] float32), or None for a dense model (synchronous copy)."""
+        c = self.dm.cfg
+        if not getattr(c, "n_experts", 0):
+            return None
+        n = c.n_layers * c.top_k
+        ids = np.empty(n, dtype=np.int32)
+        w = np.empty(n, dtype=np.float32)
+        for dst, src in ((ids, _lib.lib().td_expert_ids(self._h)), (w, _lib.lib().td_expert_weights(self._h))):
+            e = _hip_rt().hipMemcpy(dst.ctypes.data, src, dst.nbytes, 2)
+            if e != 0:
+                raise RuntimeError(f"hipMemcpy failed: {e}")
+        return ids.reshape(c.n_layers, c.top_k), w.reshape(c.n_layers, c.top_k)
 
     def step(self, token_ptr: int, pos: int, kv: KVCache, logits, stream=None) -> None:
         """One decode step; `token_ptr` is a device int32 address, `logits` a float32 device tensor [vocab]."""

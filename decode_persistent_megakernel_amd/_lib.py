@@ -26,9 +26,11 @@ TD_EXEC_GRAPH = 2
 
 TD_MAX_LOOP_STEPS = 256
 TD_MAX_BLOCK = 64
+TD_MAX_EXPERTS = 256
+TD_MAX_TOPK = 16
 
 EXPORTED = [
-    "td_create", "td_decode_step", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_status", "td_destroy", "td_strerror", "td_last_error",
+    "td_create", "td_decode_step", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_expert_ids", "td_expert_weights", "td_status", "td_destroy", "td_strerror", "td_last_error",
     "td_test_gemv", "td_test_attention", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
 ]
 
@@ -37,12 +39,13 @@ class TdConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
                                               "intermediate", "vocab", "max_ctx")] + \
                [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("weight_format", ctypes.c_int32), ("qkv_bias", ctypes.c_int32)]
+                ("weight_format", ctypes.c_int32), ("qkv_bias", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
 
 class TdLayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "w_qkv", "s_qkv", "b_qkv", "w_o", "s_o", "mlp_norm",
-                                               "w_gu", "s_gu", "w_d", "s_d")]
+                                               "w_gu", "s_gu", "w_d", "s_d", "w_router")]
 
 
 class TdWeights(ctypes.Structure):
@@ -82,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.td_forward_block.restype = i32
         L.td_forward_block.argtypes = [vp, vp, i32, i32, ctypes.POINTER(TdKV), vp, i32, vp, vp]
         L.td_token_ptr.restype = vp
+        L.td_expert_ids.restype = vp
+        L.td_expert_ids.argtypes = [vp]
+        L.td_expert_weights.restype = vp
+        L.td_expert_weights.argtypes = [vp]
         L.td_token_ptr.argtypes = [vp]
         L.td_status.restype = i32
         L.td_status.argtypes = [vp, ctypes.POINTER(i32)]

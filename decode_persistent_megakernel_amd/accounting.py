@@ -25,8 +25,13 @@ def layer_weight_bytes(cfg) -> int:
     qkv_rows = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d
     b = linear_bytes(qkv_rows, H, cfg.weight_format)
     b += linear_bytes(H, cfg.n_q_heads * d, cfg.weight_format)
-    b += linear_bytes(2 * cfg.intermediate, H, cfg.weight_format)
-    b += linear_bytes(H, cfg.intermediate, cfg.weight_format)
+    # a mixture-of-experts layer streams its router and the top_k routed experts only
+    # ("One launch per token", 64-expert section: the floor is set by the active weights)
+    n_mlp = cfg.top_k if getattr(cfg, "n_experts", 0) else 1
+    b += n_mlp * linear_bytes(2 * cfg.intermediate, H, cfg.weight_format)
+    b += n_mlp * linear_bytes(H, cfg.intermediate, cfg.weight_format)
+    if getattr(cfg, "n_experts", 0):
+        b += cfg.n_experts * H * 2          # bf16 router
     b += 2 * H * 2                      # two bf16 norm gains
     if cfg.qkv_bias:
         b += qkv_rows * 2

@@ -152,6 +152,9 @@ int check_config(const td_config* c) {
       ((c->hidden % 128) || (c->intermediate % 128) || ((c->n_q_heads * c->head_dim) % 128)))
     return fail(TD_E_INVALID_ARG, "int4 needs every K to be a multiple of 128");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(TD_E_INVALID_ARG, "bad rope_theta or rms_eps");
+  if (c->n_experts < 0 || c->n_experts > TD_MAX_EXPERTS) return fail(TD_E_INVALID_ARG, "n_experts out of range");
+  if (c->n_experts > 0 && (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > TD_MAX_TOPK))
+    return fail(TD_E_INVALID_ARG, "top_k out of range");
   return TD_OK;
 }
 
@@ -164,6 +167,7 @@ int check_weights(const td_config* c, const td_weights* w) {
       return fail(TD_E_INVALID_ARG, "null layer weight pointer");
     if (q4 && (!L.s_qkv || !L.s_o || !L.s_gu || !L.s_d)) return fail(TD_E_INVALID_ARG, "int4 layer without scales");
     if (c->qkv_bias && !L.b_qkv) return fail(TD_E_INVALID_ARG, "qkv_bias set but b_qkv is null");
+    if (c->n_experts > 0 && !L.w_router) return fail(TD_E_INVALID_ARG, "MoE layer without router weights");
   }
   return TD_OK;
 }
@@ -189,6 +193,8 @@ int setup_per_op(td_ctx* ctx, const td_kparams& kp) {
   op.attn_scale = kp.attn_scale;
   op.chunk_len = kp.chunk_len;
   op.n_chunks_max = kp.n_chunks_max;
+  op.E = ctx->cfg.n_experts;
+  op.topk = op.E > 0 ? ctx->cfg.top_k : 0;
   op.layers = kp.layers;
   op.embed = kp.embed;
   op.head = kp.head;
@@ -204,8 +210,10 @@ int setup_per_op(td_ctx* ctx, const td_kparams& kp) {
   };
   const size_t o_pos = take(4), o_x = take((size_t)op.H * 4), o_q = take((size_t)op.qd * 4);
   const size_t o_part = take((size_t)op.nkv * op.n_chunks_max * op.group * (op.d + 4) * 4);
-  const size_t o_o = take((size_t)op.qd * 4), o_act = take((size_t)op.I * 4);
+  const size_t o_o = take((size_t)op.qd * 4), o_act = take((size_t)op.I * std::max(1, op.topk) * 4);
   const size_t o_cand = take((size_t)td_op_head_blocks(&op) * 16);
+  const size_t o_rl = take((size_t)std::max(1, op.E) * 4), o_eid = take((size_t)op.L * std::max(1, op.topk) * 4);
+  const size_t o_ew = take((size_t)op.L * std::max(1, op.topk) * 4);
   hipError_t e = hipMalloc(&ctx->opbuf, off);
   if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of per-op buffers failed")
                                                        : hip_fail(e, "hipMalloc");
@@ -223,6 +231,9 @@ int setup_per_op(td_ctx* ctx, const td_kparams& kp) {
   op.o = (float*)(b + o_o);
   op.act = (float*)(b + o_act);
   op.cand = (uint32_t*)(b + o_cand);
+  op.rlogits = (float*)(b + o_rl);
+  op.expert_ids = op.E > 0 ? (int32_t*)(b + o_eid) : nullptr;
+  op.expert_w = op.E > 0 ? (float*)(b + o_ew) : nullptr;
   int le = td_op_set_lds_limits(&op);
   if (le) {
     (void)hipFree(ctx->opbuf);
@@ -298,6 +309,8 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   if (rc) return rc;
   if (executor != TD_EXEC_MEGAKERNEL && executor != TD_EXEC_PER_OP && executor != TD_EXEC_GRAPH)
     return fail(TD_E_INVALID_ARG, "unknown executor");
+  if (cfg->n_experts > 0 && executor == TD_EXEC_MEGAKERNEL)
+    return fail(TD_E_UNSUPPORTED, "a mixture-of-experts config runs on the per-op or graph executor");
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -514,6 +527,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     Ld.bias = c.qkv_bias ? (const uint16_t*)Lw.b_qkv : nullptr;
     Ld.attn_norm = (const uint16_t*)Lw.attn_norm;
     Ld.mlp_norm = (const uint16_t*)Lw.mlp_norm;
+    Ld.router = c.n_experts > 0 ? (const uint16_t*)Lw.w_router : nullptr;
   }
   e = hipMemcpy(base + o_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_layers, layers.data(), sizeof(td_layer_dev) * L, hipMemcpyHostToDevice);
@@ -660,6 +674,10 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
 
 const int32_t* td_token_ptr(const td_ctx* ctx) { return ctx ? ctx->kp.token_out : nullptr; }
 
+const int32_t* td_expert_ids(const td_ctx* ctx) { return ctx ? ctx->op.expert_ids : nullptr; }
+
+const float* td_expert_weights(const td_ctx* ctx) { return ctx ? ctx->op.expert_w : nullptr; }
+
 int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv* kv, float* d_logits_out,
                    void* stream) {
   if (!ctx || !d_token || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
@@ -743,6 +761,7 @@ int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t po
   if (!ctx || !d_tokens || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
   if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
   if (n < 1 || n > TD_MAX_BLOCK) return fail(TD_E_INVALID_ARG, "n outside [1, TD_MAX_BLOCK]");
+  if (ctx->cfg.n_experts > 0) return fail(TD_E_UNSUPPORTED, "the block forward runs dense MLPs only");
   if (pos0 < 0 || (int64_t)pos0 + n > ctx->cfg.max_ctx) return fail(TD_E_RANGE, "positions outside [0, max_ctx)");
   td_kparams p = ctx->kp;
   p.kc = (uint16_t*)kv->k;

@@ -14,6 +14,9 @@
 //
 // --executor megakernel|per_op|graph picks the executor behind td_decode_step.
 //
+// A mixture-of-experts workload runs on the graph executor unless --executor
+// per_op is given.
+//
 // --loop N runs the steps through td_decode_loop, N greedy steps per launch
 // (the last launch takes the remainder), instead of one td_decode_step each.
 //
@@ -54,6 +57,7 @@ struct Workload {
   int layers, hidden, nq, nkv, d, inter, vocab;
   double theta, eps;
   int wf, bias, tied, prompt, kv_prefix, steps, max_ctx, seed;
+  int n_experts = 0, top_k = 0;  // mixture of experts (0: dense MLP)
 };
 
 // The workloads (same shapes, formats and seeds as the Python definitions).
@@ -65,6 +69,7 @@ const Workload kWorkloads[] = {
     {"qwen1p5b", 28, 1536, 12, 2, 128, 8960, 151936, 1e6, 1e-6, TD_WF_BF16, 1, 1, 1024, 0, 64, 1088, 1003},
     {"llama1b_int4_long", 16, 2048, 32, 8, 64, 8192, 128256, 500000.0, 1e-5, TD_WF_INT4_G64, 0, 1, 0, 8192, 64,
      8256, 1004},
+    {"olmoe", 16, 2048, 16, 16, 128, 1024, 50304, 10000.0, 1e-5, TD_WF_BF16, 0, 0, 0, 512, 64, 576, 1005, 64, 8},
 };
 
 constexpr double kWeightStd = 0.02, kScaleStd = 0.003, kKvStd = 1.0;
@@ -130,9 +135,9 @@ void print_config(const Workload& w) {
   printf("{\"name\": \"%s\", \"n_layers\": %d, \"hidden\": %d, \"n_q_heads\": %d, \"n_kv_heads\": %d, "
          "\"head_dim\": %d, \"intermediate\": %d, \"vocab\": %d, \"rope_theta\": %.17g, \"rms_eps\": %.17g, "
          "\"weight_format\": %d, \"qkv_bias\": %d, \"tied\": %d, \"prompt_len\": %d, \"kv_prefix\": %d, "
-         "\"decode_steps\": %d, \"max_ctx\": %d, \"seed\": %d, \"n_experts\": 0, \"top_k\": 0}\n",
+         "\"decode_steps\": %d, \"max_ctx\": %d, \"seed\": %d, \"n_experts\": %d, \"top_k\": %d}\n",
          w.name, w.layers, w.hidden, w.nq, w.nkv, w.d, w.inter, w.vocab, w.theta, w.eps, w.wf, w.bias, w.tied,
-         w.prompt, w.kv_prefix, w.steps, w.max_ctx, w.seed);
+         w.prompt, w.kv_prefix, w.steps, w.max_ctx, w.seed, w.n_experts, w.top_k);
 }
 
 }  // namespace
@@ -177,6 +182,14 @@ int main(int argc, char** argv) {
     return 2;
   }
   const Workload& w = *wp;
+  if (w.n_experts > 0 && executor == TD_EXEC_MEGAKERNEL) {
+    executor = TD_EXEC_GRAPH;  // a mixture of experts runs on the per-op launches (replayed as a graph)
+    ex_name = "graph";
+  }
+  if (w.n_experts > 0 && (loop_n > 0 || block_n > 0)) {
+    fprintf(stderr, "td_bench: --loop and --block run dense models only\n");
+    return 2;
+  }
   if (only_config) {
     print_config(w);
     return 0;
@@ -208,6 +221,9 @@ int main(int argc, char** argv) {
   cfg.rms_eps = (float)w.eps;
   cfg.weight_format = w.wf;
   cfg.qkv_bias = w.bias;
+  cfg.n_experts = w.n_experts;
+  cfg.top_k = w.top_k;
+  const int64_t E = std::max(1, w.n_experts);
   td_weights tw{};
   tw.embed = bf16_normal_dev(V * H, synth_key(w.seed, -1, "embed"), kWeightStd);
   tw.head = w.tied ? tw.embed : bf16_normal_dev(V * H, synth_key(w.seed, -1, "head"), kWeightStd);
@@ -220,8 +236,9 @@ int main(int argc, char** argv) {
     L.b_qkv = w.bias ? bf16_normal_dev(qkv_rows, synth_key(w.seed, l, "qkv_bias"), kWeightStd) : nullptr;
     linear_dev(w, l, "qkv", qkv_rows, H, &L.w_qkv, &L.s_qkv);
     linear_dev(w, l, "o", H, qd, &L.w_o, &L.s_o);
-    linear_dev(w, l, "gate_up", 2 * I, H, &L.w_gu, &L.s_gu);
-    linear_dev(w, l, "down", H, I, &L.w_d, &L.s_d);
+    linear_dev(w, l, "gate_up", E * 2 * I, H, &L.w_gu, &L.s_gu);
+    linear_dev(w, l, "down", E * H, I, &L.w_d, &L.s_d);
+    L.w_router = w.n_experts ? bf16_normal_dev(E * H, synth_key(w.seed, l, "router"), kWeightStd) : nullptr;
   }
   tw.layers = layers.data();
 

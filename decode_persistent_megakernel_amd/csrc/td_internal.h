@@ -54,6 +54,7 @@ struct td_layer_dev {
   const uint16_t* bias;    // bf16 QKV bias or null
   const uint16_t* attn_norm;
   const uint16_t* mlp_norm;
+  const uint16_t* router;  // MoE: bf16 [E][H], else null (w[2], w[3] then hold all experts)
 };
 
 // One compute wave's weight stream: its chunks for the whole step, in the
@@ -126,6 +127,7 @@ struct td_opparams {
   int32_t qd, kvd, qkv_rows, group;
   float eps, attn_scale;
   int32_t chunk_len, n_chunks_max;
+  int32_t E, topk;   // MoE: experts and experts per token (E = 0: dense MLP)
   int32_t* pos_word;
   const td_layer_dev* layers;
   const uint16_t* embed;
@@ -139,7 +141,10 @@ struct td_opparams {
   float* q;          // [nq d] rotated queries times 1/sqrt(d)
   float* part;       // [nkv][group][n_chunks_max][d + 4] attention partials: acc[d], m, l, pad
   float* o;          // [nq d] attention output
-  float* act;        // [I] SiLU(gate) * up
+  float* act;        // [I] SiLU(gate) * up; MoE: [topk][I], slot j of the j-th chosen expert
+  float* rlogits;    // MoE: [E] router logits of the current layer
+  int32_t* expert_ids;  // MoE: [L][topk] chosen experts (the routing tensor the expert ops read)
+  float* expert_w;      // MoE: [L][topk] their router probabilities
   uint32_t* cand;    // [head blocks][4]: value bits, index, nonfinite
   int32_t* token_out;
   int32_t* err;

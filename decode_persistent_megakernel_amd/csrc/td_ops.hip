@@ -18,6 +18,7 @@
 
 #include <algorithm>
 
+#include "td.h"
 #include "td_internal.h"
 #include "td_device.h"
 
@@ -291,6 +292,152 @@ __global__ void __launch_bounds__(256) op_gu(td_opparams P, int layer, int R) {
   }
 }
 
+// --------------------------------------------------------------- MoE
+// A mixture-of-experts MLP ("One launch per token", its 64-expert section):
+// the router writes the chosen expert ids into a fixed device tensor and the
+// expert kernels read their weights through it, so the launches (and a graph
+// recorded from them) never change while the routing does.
+
+// op_router: z[e] = W_router[e] . RMSNorm(x) for every expert e (bf16 rows,
+// the chunk arithmetic of the other GEMVs), one expert per wave.
+__global__ void __launch_bounds__(256) op_router(td_opparams P, int layer) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const td_layer_dev& Ld = P.layers[layer];
+  const float inv = op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, 0));
+  op_zero_tail(xs, P.H, op_kpad(P.H, 0));
+  __syncthreads();
+  const int e = blockIdx.x * OP_WAVES + (threadIdx.x >> 6);
+  if (e >= P.E) return;
+  const float z = op_row(0, (const uint8_t*)Ld.router, nullptr, e, P.H, xs) * inv;
+  if (lane_id() == 0) P.rlogits[e] = z;
+}
+
+// op_topk (one wave): the topk largest router logits in decreasing order, the
+// lower id first among equals, into expert_ids[layer]; their softmax
+// probabilities over all E experts (max subtracted, the sum reduced in a fixed
+// lane order) into expert_w[layer].  A non-finite logit raises the error bit;
+// the ids are then 0 .. topk - 1 with weight 0 (every later read stays in
+// bounds).
+__global__ void __launch_bounds__(64) op_topk(td_opparams P, int layer) {
+  constexpr int PER = TD_MAX_EXPERTS / 64;
+  const int lane = lane_id();
+  float z[PER];
+  bool tk[PER];
+  float m = -__builtin_inff();
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    tk[i] = e >= P.E;
+    z[i] = e < P.E ? P.rlogits[e] : -__builtin_inff();
+    if (e < P.E && !isfinite(z[i])) bad = 1;
+    if (e < P.E) m = fmaxf(m, z[i]);
+  }
+  bad = __any(bad);
+  m = wave_max(m);
+  float ssum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < P.E) ssum += expf(z[i] - m);
+  ssum = wave_sum(ssum);
+  int32_t* ids = P.expert_ids + layer * P.topk;
+  float* wts = P.expert_w + layer * P.topk;
+  if (bad) {
+    if (lane < P.topk) {
+      ids[lane] = lane;
+      wts[lane] = 0.f;
+    }
+    if (lane == 0) atomicOr(P.err, TD_ERRBIT_NONFINITE);
+    return;
+  }
+  for (int j = 0; j < P.topk; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      if (!tk[i] && (bi == 0x7fffffff || z[i] > bv)) {  // e ascends with i: the first of equals stays
+        bv = z[i];
+        bi = e;
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i == bi) tk[i] = true;
+    if (lane == 0) {
+      ids[j] = bi;
+      wts[j] = expf(bv - m) / ssum;
+    }
+  }
+}
+
+// Expert e's block of a stacked [E][rows][K] linear (codes and scales).
+DEV const uint8_t* expert_w(const uint8_t* w, int fmt, int e, int rows, int K) {
+  return w + (size_t)e * rows * (fmt ? (size_t)(K / 2) : (size_t)K * 2);
+}
+DEV const uint16_t* expert_s(const uint16_t* s, int fmt, int e, int rows, int K) {
+  return fmt ? s + (size_t)e * rows * (K / 64) : nullptr;
+}
+
+// op_moe_gu: unit u = j I + r: row r of the j-th chosen expert's gate and up
+// projections of RMSNorm(x), act[j][r] = SiLU(gate) * up.
+__global__ void __launch_bounds__(256) op_moe_gu(td_opparams P, int layer, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const td_layer_dev& Ld = P.layers[layer];
+  const float inv = op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
+  op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  const int32_t* ids = P.expert_ids + layer * P.topk;
+  for (int k = 0; k < R; ++k) {
+    const int u = (blockIdx.x * OP_WAVES + wave) * R + k;
+    if (u >= P.topk * P.I) break;
+    const int j = u / P.I, r = u - j * P.I;
+    const int e = uni(ids[j]);
+    const uint8_t* w = expert_w(Ld.w[2], P.wf, e, 2 * P.I, P.H);
+    const uint16_t* sc = expert_s(Ld.s[2], P.wf, e, 2 * P.I, P.H);
+    const float gt = op_row(P.wf, w, sc, r, P.H, xs) * inv;
+    const float up = op_row(P.wf, w, sc, r + P.I, P.H, xs) * inv;
+    if (lane_id() == 0) P.act[u] = gt / (1.0f + expf(-gt)) * up;
+  }
+}
+
+// op_moe_down: x[r] += sum over the chosen experts j (in order) of
+// w_j (W_down of expert j, row r) . act[j].
+__global__ void __launch_bounds__(256) op_moe_down(td_opparams P, int layer, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const td_layer_dev& Ld = P.layers[layer];
+  const int kp = op_kpad(P.I, P.wf);
+  for (int j = 0; j < P.topk; ++j) op_copy_to_lds(P.act + (size_t)j * P.I, P.I, kp, xs + (size_t)j * kp);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  const int32_t* ids = P.expert_ids + layer * P.topk;
+  const float* wts = P.expert_w + layer * P.topk;
+  for (int k = 0; k < R; ++k) {
+    const int r = (blockIdx.x * OP_WAVES + wave) * R + k;
+    if (r >= P.H) break;
+    float y = 0.f;
+    for (int j = 0; j < P.topk; ++j) {
+      const int e = uni(ids[j]);
+      const float d = op_row(P.wf, expert_w(Ld.w[3], P.wf, e, P.H, P.I), expert_s(Ld.s[3], P.wf, e, P.H, P.I), r,
+                             P.I, xs + (size_t)j * kp);
+      y = fmaf(wts[j], d, y);
+    }
+    if (lane_id() == 0) P.x[r] = P.x[r] + y;
+  }
+}
+
 // --------------------------------------------------------------- op_head / op_argmax
 __global__ void __launch_bounds__(256) op_head(td_opparams P, int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -363,6 +510,7 @@ int td_op_head_blocks(const td_opparams* p) { return blocks_for(p->V, R_HEAD); }
 size_t td_op_lds_bytes(const td_opparams* p) {
   auto kp = [](int K, int f) { return (size_t)((K + (f ? 2047 : 511)) / (f ? 2048 : 512) * (f ? 2048 : 512)); };
   size_t x = std::max({kp(p->H, p->wf), kp(p->qd, p->wf), kp(p->I, p->wf), kp(p->H, 0)}) * 4 + TD_NW * 4;
+  if (p->topk > 0) x = std::max(x, (size_t)p->topk * kp(p->I, p->wf) * 4);
   const size_t D = (size_t)p->d, G = (size_t)p->group;
   const size_t a = G * D * 4 + G * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2;
   return std::max(x, a);
@@ -389,8 +537,15 @@ int td_launch_op_layers(const td_opparams* p, void* stream) {
       op_merge<128><<<P.nkv, 512, 0, s>>>(P);
     }
     op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 1, R_RESID);
-    op_gu<<<blocks_for(P.I, R_GU), 256, lds, s>>>(P, l, R_GU);
-    op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 3, R_RESID);
+    if (P.E > 0) {
+      op_router<<<blocks_for(P.E, 1), 256, lds, s>>>(P, l);
+      op_topk<<<1, 64, 0, s>>>(P, l);
+      op_moe_gu<<<blocks_for(P.topk * P.I, R_GU), 256, lds, s>>>(P, l, R_GU);
+      op_moe_down<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, R_RESID);
+    } else {
+      op_gu<<<blocks_for(P.I, R_GU), 256, lds, s>>>(P, l, R_GU);
+      op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 3, R_RESID);
+    }
   }
   const int hb = blocks_for(P.V, R_HEAD);
   op_head<<<hb, 256, lds, s>>>(P, R_HEAD);
@@ -402,7 +557,8 @@ int td_op_set_lds_limits(const td_opparams* p) {
   const int lds = (int)td_op_lds_bytes(p);
   hipError_t e = hipSuccess;
   const void* fns[] = {(const void*)op_qkv, (const void*)op_attn<64>, (const void*)op_attn<128>,
-                       (const void*)op_resid, (const void*)op_gu, (const void*)op_head};
+                       (const void*)op_resid, (const void*)op_gu, (const void*)op_head,
+                       (const void*)op_router, (const void*)op_moe_gu, (const void*)op_moe_down};
   for (const void* f : fns)
     if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   return (int)e;

@@ -70,7 +70,17 @@ typedef struct td_config {
     float rms_eps;         /* RMSNorm: x / sqrt(mean(x^2) + eps) * gain */
     int32_t weight_format; /* TD_WF_* (layer linears) */
     int32_t qkv_bias;      /* nonzero: b_qkv is added after the QKV projection, before RoPE */
+    int32_t n_experts;     /* 0: dense MLP.  > 0: the MLP is a mixture of n_experts experts of
+                              intermediate size I ("One launch per token", its 64-expert MoE
+                              section): a router scores the experts, the token goes to the top_k
+                              best, and their outputs are added weighted by the router's softmax
+                              probabilities (not renormalised over the top_k) */
+    int32_t top_k;         /* experts per token (MoE only): 1 .. min(n_experts, TD_MAX_TOPK) */
 } td_config;
+
+/* Largest MoE shapes the kernels handle. */
+#define TD_MAX_EXPERTS 256
+#define TD_MAX_TOPK 16
 
 /* Device pointers of one layer.  Shapes are [rows][cols], row = output. */
 typedef struct td_layer_weights {
@@ -85,6 +95,9 @@ typedef struct td_layer_weights {
     const void* s_gu;
     const void* w_d;        /* [H][I] */
     const void* s_d;
+    const void* w_router;   /* MoE: bf16 [n_experts][H], else NULL.  With experts, w_gu is
+                               [n_experts][2 I][H] and w_d [n_experts][H][I] (expert e's block at
+                               row 2 I e, resp. H e) and their int4 scales follow the same rows */
 } td_layer_weights;
 
 typedef struct td_weights {
@@ -114,6 +127,12 @@ typedef struct td_ctx td_ctx;
  * more than 8 query heads per kv head, missing scales or bias), TD_E_UNSUPPORTED
  * (device is not gfx950, or its CU count is not a multiple of 8), TD_E_PLAN,
  * TD_E_NOMEM, TD_E_HIP.  On error *out is set to NULL.
+ * A mixture-of-experts config runs on TD_EXEC_PER_OP and TD_EXEC_GRAPH only: the
+ * router writes the chosen expert ids to a device tensor (td_expert_ids) and the
+ * expert kernels read their weights through it, so the recorded graph replays
+ * whatever the routing (TD_E_UNSUPPORTED with TD_EXEC_MEGAKERNEL; TD_E_INVALID_ARG
+ * for top_k outside [1, min(n_experts, TD_MAX_TOPK)], n_experts above
+ * TD_MAX_EXPERTS, or a null w_router).
  */
 int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ctx** out);
 
@@ -136,6 +155,13 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
 
 /* Device address of the context's int32 greedy-token word (valid for the ctx's life). */
 const int32_t* td_token_ptr(const td_ctx* ctx);
+
+/* MoE routing of the last step (device memory owned by the context, valid for
+ * its life; NULL for a dense config): int32 ids [n_layers][top_k], each layer's
+ * chosen experts in order of decreasing router logit (ties to the lower id), and
+ * float weights [n_layers][top_k], their softmax probabilities over all experts. */
+const int32_t* td_expert_ids(const td_ctx* ctx);
+const float* td_expert_weights(const td_ctx* ctx);
 
 /* Most steps one td_decode_loop call runs. */
 #define TD_MAX_LOOP_STEPS 256
@@ -193,8 +219,9 @@ int td_decode_loop(td_ctx* ctx, const int32_t* d_token, int32_t pos, int32_t n_s
  * asynchronous on `stream`, no allocation, and not concurrent with another call
  * on the same context.  Works with every executor.
  * Errors (before launch): TD_E_INVALID_ARG (null ctx/tokens/kv/logits, kv
- * max_ctx mismatch, n outside [1, TD_MAX_BLOCK]), TD_E_RANGE (pos0 < 0 or
- * pos0 + n > max_ctx), TD_E_HIP.  A token id outside [0, vocab) or a
+ * max_ctx mismatch, n outside [1, TD_MAX_BLOCK]), TD_E_UNSUPPORTED (a
+ * mixture-of-experts config), TD_E_RANGE (pos0 < 0 or pos0 + n > max_ctx),
+ * TD_E_HIP.  A token id outside [0, vocab) or a
  * non-finite logit is reported by td_status.
  */
 int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t pos0, const td_kv* kv,

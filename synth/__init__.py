@@ -100,8 +100,8 @@ CONFIGS: Dict[str, Config] = {
                   qkv_bias=False, tied=False, prompt_len=0, kv_prefix=512, decode_steps=64, max_ctx=576,
                   seed=1005, n_experts=64, top_k=8),
 }
-# the workloads of the native driver (td_bench) and of the dense decode kernel
-CONFIG_ORDER: List[str] = ["tiny", "llama1b", "tinyllama_int4", "qwen1p5b", "llama1b_int4_long"]
+# the workloads of the native driver (td_bench)
+CONFIG_ORDER: List[str] = ["tiny", "llama1b", "tinyllama_int4", "qwen1p5b", "llama1b_int4_long", "olmoe"]
 
 
 def shrink(cfg: Config, **over) -> Config:

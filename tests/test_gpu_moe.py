@@ -1,0 +1,153 @@
+"""Mixture-of-experts decode on the per-op and graph executors.
+
+The router writes each layer's chosen experts into a device tensor
+(td_expert_ids) and the expert kernels read their weights through it, so one
+recorded graph serves every routing.  Every step is compared with the
+oracle's teacher-forced step from the same K/V state: the V logits within the
+decode-step tolerance (2e-2 for bf16 weights, 5e-2 for int4), the greedy token
+(a flip only at a near-tie), and the routing itself: the same experts in the
+same order and their probabilities within 1e-3 (relative; a probability's
+relative error is its router logit's absolute error, which carries the
+residual stream's fp32 error through the layers: observed 1.4e-5 at 16 layers,
+while a wrong normalisation or a dropped weight is off by a factor).  The routing is an
+integer decided on floating point; both sides decide on fp32 router logits,
+and with these seeded models no two candidates come within the fp32 error of
+each other, so the choices must be identical.
+
+Shapes: bf16 with 16 experts / top 4 and GQA; int4 with 8 / top 2; the OLMoE
+head layout (query heads = kv heads, d = 128) with 64 experts / top 8; and the
+full OLMoE-1B-7B shape (16 layers, hidden 2048, 64 experts of 1024, top 8,
+vocab 50304) from a random K/V prefix of 512 positions.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.test_gpu_parity import td, torch, _say  # noqa: F401  (fixture)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {synth.WF_BF16: 2e-2, synth.WF_INT4_G64: 5e-2}
+BASE = dict(n_layers=2, vocab=1000, prompt_len=0, kv_prefix=0, decode_steps=0, max_ctx=96, tied=False)
+MOE_BF16 = synth.shrink(synth.CONFIGS["llama1b"], name="moe_bf16", hidden=256, n_q_heads=8, n_kv_heads=2,
+                        head_dim=64, intermediate=256, n_experts=16, top_k=4, seed=3001, **BASE)
+MOE_INT4 = synth.shrink(synth.CONFIGS["tinyllama_int4"], name="moe_int4", hidden=256, n_q_heads=4, n_kv_heads=2,
+                        head_dim=64, intermediate=384, n_experts=8, top_k=2, seed=3002, **BASE)
+MOE_D128 = synth.shrink(synth.CONFIGS["olmoe"], name="moe_d128", hidden=256, n_q_heads=2, n_kv_heads=2,
+                        head_dim=128, intermediate=128, n_experts=64, top_k=8, seed=3003, **BASE)
+
+
+def _run(td, cfg, m, k, v, first, start, n, executor, label):
+    o = oracle.Oracle(m)
+    o.set_kv(k, v)
+    dm = td.DeviceModel(m)
+    kv = td.KVCache(cfg, cfg.max_ctx, k=k, v=v)
+    dec = td.Decoder(dm, cfg.max_ctx, executor=executor)
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    t = int(first)
+    worst = 0.0
+    outs = []
+    for i in range(n):
+        pos = start + i
+        tok.fill_(t)
+        dec.step(tok.data_ptr(), pos, kv, logits)
+        torch.cuda.synchronize()
+        assert dec.status() == 0, (label, i)
+        g = td.read_device_i32(dec.token_ptr())
+        ids, wts = dec.routing()
+        r, tr = o.step_traced(t, pos)
+        assert r >= 0
+        ref = tr["logits"]
+        got = logits.cpu().numpy().astype(np.float64)
+        outs.append(logits.cpu().numpy().view(np.uint32).copy())
+        assert np.array_equal(ids, tr["expert_ids"]), (label, i, ids, tr["expert_ids"])
+        np.testing.assert_allclose(wts, tr["expert_w"], rtol=1e-3, atol=0, err_msg=label)
+        diff = float(np.max(np.abs(got - ref)))
+        worst = max(worst, diff)
+        assert diff <= TOL[cfg.weight_format], (label, i, diff)
+        if g != r:
+            top2 = np.sort(ref)[-2:]
+            assert top2[1] - top2[0] <= 2 * diff, (label, i, g, r)
+        t = r
+    dec.close()
+    _say(f"{label}: {n} steps, max|dlogit| = {worst:.3g}")
+    return outs
+
+
+@pytest.mark.parametrize("cfg,start", [(MOE_BF16, 30), (MOE_INT4, 10), (MOE_D128, 60)],
+                         ids=["bf16_e16k4", "int4_e8k2", "d128_e64k8"])
+@pytest.mark.parametrize("executor", ["per_op", "graph"])
+def test_moe_matches_oracle(td, cfg, start, executor):
+    ex = {"per_op": td.TD_EXEC_PER_OP, "graph": td.TD_EXEC_GRAPH}[executor]
+    m = synth.make_model(cfg)
+    k, v = synth.random_kv_prefix(cfg, start, seed_tag="moe")
+    _run(td, cfg, m, k, v, synth.first_token(cfg), start, 12, ex, f"{cfg.name}/{executor}")
+
+
+def test_graph_replays_follow_the_routing(td):
+    """The graph executor replays one recording; its logits equal the per-op
+    executor's bit for bit over steps whose routing differs."""
+    cfg = MOE_D128
+    m = synth.make_model(cfg)
+    k, v = synth.random_kv_prefix(cfg, 20, seed_tag="moe")
+    dm = td.DeviceModel(m)
+    res = {}
+    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH):
+        kv = td.KVCache(cfg, cfg.max_ctx, k=k, v=v)
+        dec = td.Decoder(dm, cfg.max_ctx, executor=ex)
+        tok = torch.tensor([synth.first_token(cfg)], dtype=torch.int32, device="cuda")
+        logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+        bits, routes = [], []
+        for i in range(8):
+            dec.step(tok.data_ptr() if i == 0 else dec.token_ptr(), 20 + i, kv, logits)
+            torch.cuda.synchronize()
+            assert dec.status() == 0
+            bits.append(logits.cpu().numpy().view(np.uint32).copy())
+            routes.append(dec.routing()[0].copy())
+        res[ex] = (bits, routes)
+        dec.close()
+    (b0, r0), (b1, r1) = res[td.TD_EXEC_PER_OP], res[td.TD_EXEC_GRAPH]
+    assert all(np.array_equal(a, b) for a, b in zip(b0, b1))
+    assert all(np.array_equal(a, b) for a, b in zip(r0, r1))
+    assert len({x.tobytes() for x in r0}) > 1  # the routing changed between steps
+    for ids in r0:
+        for row in ids:
+            assert len(set(row.tolist())) == cfg.top_k and row.min() >= 0 and row.max() < cfg.n_experts
+
+
+def test_moe_errors(td):
+    from decode_persistent_megakernel_amd import _lib
+    cfg = MOE_BF16
+    m = synth.make_model(cfg)
+    dm = td.DeviceModel(m)
+    with pytest.raises(td.TdError) as ei:
+        td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_MEGAKERNEL)
+    assert ei.value.code == _lib.TD_E_UNSUPPORTED
+    dec = td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_PER_OP)
+    kv = td.KVCache(cfg, cfg.max_ctx)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    toks = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(td.TdError) as ei:
+        dec.forward_block(toks, 0, kv, logits)
+    assert ei.value.code == _lib.TD_E_UNSUPPORTED
+    dec.close()
+    # a NaN router row: a non-finite router logit is reported, and the step stays in bounds
+    m.layers[1].router = m.layers[1].router.copy()
+    m.layers[1].router[3, :] = 0x7FC0
+    dec = td.Decoder(td.DeviceModel(m), cfg.max_ctx, executor=td.TD_EXEC_PER_OP)
+    tok = torch.tensor([5], dtype=torch.int32, device="cuda")
+    dec.step(tok.data_ptr(), 0, kv, logits)
+    torch.cuda.synchronize()
+    assert dec.status() == _lib.TD_E_NONFINITE
+    dec.close()
+
+
+def test_fullsize_olmoe_matches_oracle(td):
+    cfg = synth.CONFIGS["olmoe"]
+    _say("olmoe: generating the model")
+    m = synth.make_model(cfg)
+    k, v = synth.random_kv_prefix(cfg, cfg.start_pos)
+    _say(f"olmoe: 8 teacher-forced steps from position {cfg.start_pos} (graph executor)")
+    _run(td, cfg, m, k, v, synth.first_token(cfg), cfg.start_pos, 8, td.TD_EXEC_GRAPH, "olmoe")
