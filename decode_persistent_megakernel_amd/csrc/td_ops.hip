@@ -103,6 +103,59 @@ DEV float op_row(int fmt, const uint8_t* w, const uint16_t* s, int row, int K, c
   return fmt ? op_row_f<1>(w, s, row, K, xs) : op_row_f<0>(w, s, row, K, xs);
 }
 
+// Row `row` of nr <= NR different matrices w[i] (scales s[i]) against nr
+// different LDS vectors xs + i xs_stride, their chunks loaded together (two
+// chunks of every row per round) so that one wave keeps NR rows in flight;
+// each dot product adds its chunks in the order op_row_f does (same bits).
+// Every w[i] must point at a valid matrix (callers repeat a valid one past nr):
+// the bf16 loads are unconditional from clamped addresses and the unused
+// values are zeroed afterwards, so the compiler's wait counts stay exact and
+// all loads of a round are in flight together.
+template <int fmt, int NR>
+DEV void op_rows_multi(const uint8_t* const (&w)[NR], const uint16_t* const (&s)[NR], int nr, int row, int K,
+                       const float* xs, int xs_stride, float (&out)[NR]) {
+  const int lane = lane_id();
+  const int row_bytes = fmt == 0 ? K * 2 : K / 2;
+  const int J = (row_bytes + TD_CHUNK - 1) / TD_CHUNK;
+  float acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+  for (int j0 = 0; j0 < J; j0 += 2) {
+    u32x4 c[NR][2];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const uint8_t* rp = w[i] + (size_t)row * row_bytes;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        const bool ok = i < nr && j < J;
+        if (fmt == 0) {
+          const int boff = j * TD_CHUNK + lane * 16;
+          const u32x4 v = __builtin_nontemporal_load((const u32x4*)(rp + min(boff, row_bytes - 16)));
+          const bool use = ok && boff < row_bytes;
+          c[i][u] = (u32x4){use ? v.x : 0u, use ? v.y : 0u, use ? v.z : 0u, use ? v.w : 0u};
+        } else {
+          c[i][u] = ok ? int4_words(rp, row_bytes, j, lane) : (u32x4){0x88888888u, 0x88888888u, 0x88888888u,
+                                                                      0x88888888u};
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        if (i >= nr || j >= J) continue;
+        const float* x = xs + (size_t)i * xs_stride;
+        if (fmt == 0) acc[i] += dot_bf16(c[i][u], x + j * 512 + lane * 8);
+        else acc[i] += dot_int4(c[i][u], x + j * 2048, lane, int4_scales(s[i] + (size_t)row * (K / 64), K / 64, j, lane));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) out[i] = wave_sum(acc[i]);
+}
+
 DEV int op_unit_row_qkv(const td_opparams& P, int u, int r) {
   const int half = P.d >> 1;
   const int head = u / half;
@@ -428,11 +481,22 @@ __global__ void __launch_bounds__(256) op_moe_down(td_opparams P, int layer, int
     const int r = (blockIdx.x * OP_WAVES + wave) * R + k;
     if (r >= P.H) break;
     float y = 0.f;
-    for (int j = 0; j < P.topk; ++j) {
-      const int e = uni(ids[j]);
-      const float d = op_row(P.wf, expert_w(Ld.w[3], P.wf, e, P.H, P.I), expert_s(Ld.s[3], P.wf, e, P.H, P.I), r,
-                             P.I, xs + (size_t)j * kp);
-      y = fmaf(wts[j], d, y);
+    for (int g0 = 0; g0 < P.topk; g0 += 8) {  // eight experts' rows in flight at a time
+      const int nr = min(8, P.topk - g0);
+      const uint8_t* wp[8];
+      const uint16_t* sp[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = uni(ids[min(g0 + i, P.topk - 1)]);
+        wp[i] = expert_w(Ld.w[3], P.wf, e, P.H, P.I);
+        sp[i] = expert_s(Ld.s[3], P.wf, e, P.H, P.I);
+      }
+      float d[8];
+      if (P.wf) op_rows_multi<1, 8>(wp, sp, nr, r, P.I, xs + (size_t)g0 * kp, kp, d);
+      else op_rows_multi<0, 8>(wp, sp, nr, r, P.I, xs + (size_t)g0 * kp, kp, d);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < nr) y = fmaf(wts[g0 + i], d[i], y);
     }
     if (lane_id() == 0) P.x[r] = P.x[r] + y;
   }
