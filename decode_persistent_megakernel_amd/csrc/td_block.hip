@@ -212,41 +212,54 @@ DEV s8v int4_bf16x8(uint32_t c) {
   return b;
 }
 
-// One chunk: each 64-column chunk's products are summed by the MFMAs into a
-// fresh partial (parts lo, mid, hi in that order), which a VALU add (round to
-// nearest) then adds to the running sum; the running sum never passes through
-// the matrix unit's accumulator.
-template <int FMT, int MT>
-DEV void mul_chunk(f32x4 (&acc)[MT], const WChunk<FMT>& c, const uint16_t* xs, int r, int q) {
+// One chunk for NB weight tiles: each 64-column chunk's products are summed by
+// the MFMAs into a fresh partial (parts lo, mid, hi in that order), which a
+// VALU add (round to nearest) then adds to the running sum; the running sum
+// never passes through the matrix unit's accumulator.  Each A fragment read
+// from LDS serves all NB weight tiles.
+template <int FMT, int MT, int NB>
+DEV void mul_chunk(f32x4 (&acc)[MT][NB], const WChunk<FMT> (&c)[NB], const uint16_t* xs, int r, int q) {
   constexpr int PART = MT * 16 * XP;
-  f32x4 pr[MT];
+  f32x4 pr[MT][NB];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) pr[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pr[t][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    bf8v b;
-    if constexpr (FMT == TD_WF_BF16) b = __builtin_bit_cast(bf8v, c.w[j]);
-    else b = __builtin_bit_cast(bf8v, int4_bf16x8(j ? c.w.y : c.w.x));
+    bf8v b[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (FMT == TD_WF_BF16) b[nb] = __builtin_bit_cast(bf8v, c[nb].w[j]);
+      else b[nb] = __builtin_bit_cast(bf8v, int4_bf16x8(j ? c[nb].w.y : c[nb].w.x));
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const uint16_t* a = xs + (16 * t + r) * XP + (FMT == TD_WF_BF16 ? 32 * j + 8 * q : 16 * q + 8 * j);
 #pragma unroll
-      for (int p = 2; p >= 0; --p)
-        pr[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf8v*)(a + p * PART), b, pr[t], 0, 0, 0);
+      for (int p = 2; p >= 0; --p) {
+        const bf8v av = *(const bf8v*)(a + p * PART);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          pr[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nb], pr[t][nb], 0, 0, 0);
+      }
     }
   }
-  if constexpr (FMT == TD_WF_BF16) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] += pr[t];
-  } else {
-    // result lane l is weight row l % 16, the row whose scale this lane loaded
-    const float sc = f16f(c.s);
+  for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (FMT == TD_WF_BF16) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      acc[t].x = fmaf(sc, pr[t].x, acc[t].x);
-      acc[t].y = fmaf(sc, pr[t].y, acc[t].y);
-      acc[t].z = fmaf(sc, pr[t].z, acc[t].z);
-      acc[t].w = fmaf(sc, pr[t].w, acc[t].w);
+      for (int t = 0; t < MT; ++t) acc[t][nb] += pr[t][nb];
+    } else {
+      // result lane l is weight row l % 16 of tile nb, the row whose scale this lane loaded
+      const float sc = f16f(c[nb].s);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        acc[t][nb].x = fmaf(sc, pr[t][nb].x, acc[t][nb].x);
+        acc[t][nb].y = fmaf(sc, pr[t][nb].y, acc[t][nb].y);
+        acc[t][nb].z = fmaf(sc, pr[t][nb].z, acc[t][nb].z);
+        acc[t][nb].w = fmaf(sc, pr[t][nb].w, acc[t][nb].w);
+      }
     }
   }
 }
@@ -254,45 +267,59 @@ DEV void mul_chunk(f32x4 (&acc)[MT], const WChunk<FMT>& c, const uint16_t* xs, i
 // Chunk c's loads, weights and X, go into ring slot c % D together, D - 1
 // chunks ahead of their use, X first: waiting for the X of chunk c + 1 (to
 // stage it) then leaves the weights of chunks c + 1 .. c + D - 1 in flight.
-template <int FMT, int MT>
+template <int FMT, int MT, int NB>
 struct Slot {
-  WChunk<FMT> w;
+  WChunk<FMT> w[NB];
   float4 x[MT];
 };
 
-template <int FMT, int MT>
+template <int FMT, int MT, int NB>
 constexpr int ring_depth() {
+  if (NB > 1) return FMT == TD_WF_BF16 ? 4 : 6;
   return FMT == TD_WF_BF16 ? (MT <= 2 ? 8 : 6) : (MT <= 2 ? 10 : 8);
 }
 
-template <int FMT, int MT>
+// Weight tiles per wave: two (a workgroup covers 128 weight rows, halving the
+// input reads per weight byte) when the token rows make the staged input as
+// large as the weights it multiplies and the matrix still has a 64-row tile per
+// CU; otherwise one, which keeps the split-K slices of short matrices long.
+inline int nb_of(int mt, int N, int ncu) { return (mt >= 3 && N >= 64 * ncu) ? 2 : 1; }
+
+template <int FMT, int MT, int NB>
 __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, int K, int KS, const uint8_t* W,
                                                 const uint16_t* Sc, int N, float* Y, int ldy, size_t sstride) {
   constexpr int PART = MT * 16 * XP;
-  constexpr int D = ring_depth<FMT, MT>();
+  constexpr int D = ring_depth<FMT, MT, NB>();
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][3 * PART];
   const int wave = threadIdx.x >> 6, lane = lane_id(), r = lane & 15, q = lane >> 4;
-  const int n = blockIdx.x * 64 + wave * 16 + r;
-  const int nr = min(n, N - 1);  // rows past N read row N - 1 and are not stored
+  const int n0 = blockIdx.x * 64 * NB + wave * 16 * NB + r;  // tile nb: row n0 + 16 nb
   const int kb = blockIdx.y * KS, nch = (min(K, kb + KS) - kb) >> 6;
-  const uint8_t* wrow;
-  const uint16_t* srow = nullptr;
-  if constexpr (FMT == TD_WF_BF16) {
-    wrow = W + ((size_t)nr * K + kb) * 2;
-  } else {
-    wrow = W + (size_t)nr * (K >> 1) + (kb >> 1);
-    srow = Sc + (size_t)nr * (K >> 6) + (kb >> 6);
+  const uint8_t* wrow[NB];
+  const uint16_t* srow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int nr = min(n0 + 16 * nb, N - 1);  // rows past N read row N - 1 and are not stored
+    if constexpr (FMT == TD_WF_BF16) {
+      wrow[nb] = W + ((size_t)nr * K + kb) * 2;
+      srow[nb] = nullptr;
+    } else {
+      wrow[nb] = W + (size_t)nr * (K >> 1) + (kb >> 1);
+      srow[nb] = Sc + (size_t)nr * (K >> 6) + (kb >> 6);
+    }
   }
   const float* xb = X + kb;
-  f32x4 acc[MT];
+  f32x4 acc[MT][NB];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  Slot<FMT, MT> ring[D];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[t][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  Slot<FMT, MT, NB> ring[D];
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) {
     const int ch = min(i, nch - 1);
     stage_load<MT>(ring[i].x, xb, ldx, M, 64 * ch);
-    load_chunk<FMT>(ring[i].w, wrow, srow, ch, q);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) load_chunk<FMT>(ring[i].w[nb], wrow[nb], srow[nb], ch, q);
   }
   stage_store<MT>(xs[0], ring[0].x);
   wg_bar();
@@ -301,25 +328,30 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
     for (int i = 0; i < D; ++i) {
       const int c = c0 + i;
       {
-        Slot<FMT, MT>& sl = ring[(i + D - 1) % D];  // chunk c - 1's slot, consumed
+        Slot<FMT, MT, NB>& sl = ring[(i + D - 1) % D];  // chunk c - 1's slot, consumed
         const int ch = min(c + D - 1, nch - 1);
         stage_load<MT>(sl.x, xb, ldx, M, 64 * ch);
-        load_chunk<FMT>(sl.w, wrow, srow, ch, q);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) load_chunk<FMT>(sl.w[nb], wrow[nb], srow[nb], ch, q);
       }
-      if (c < nch) mul_chunk<FMT, MT>(acc, ring[i].w, xs[c & 1], r, q);
+      if (c < nch) mul_chunk<FMT, MT, NB>(acc, ring[i].w, xs[c & 1], r, q);
       stage_store<MT>(xs[(c + 1) & 1], ring[(i + 1) % D].x);
       wg_bar();
     }
   }
-  if (n >= N) return;
-  float* dst = Y + blockIdx.y * sstride + n;
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const float rv[4] = {acc[t].x, acc[t].y, acc[t].z, acc[t].w};
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + 16 * nb;
+    if (n >= N) continue;
+    float* dst = Y + blockIdx.y * sstride + n;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = 16 * t + 4 * q + e;
-      if (m < M) dst[(size_t)m * ldy] = rv[e];
+    for (int t = 0; t < MT; ++t) {
+      const float rv[4] = {acc[t][nb].x, acc[t][nb].y, acc[t][nb].z, acc[t][nb].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * t + 4 * q + e;
+        if (m < M) dst[(size_t)m * ldy] = rv[e];
+      }
     }
   }
 }
@@ -561,15 +593,16 @@ __global__ void __launch_bounds__(64) blk_argmax_final(const uint2* cand, int nb
 }
 
 template <int FMT>
-int launch_gemm_f(dim3 grid, hipStream_t st, const float* X, int ldx, int M, int K, int KS, const uint8_t* W,
-                  const uint16_t* S, int N, float* Y, int ldy, size_t sstride) {
-  const dim3 block(256);
-  switch ((M + 15) / 16) {
-    case 1: blk_gemm<FMT, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
-    case 2: blk_gemm<FMT, 2><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
-    case 3: blk_gemm<FMT, 3><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
-    default: blk_gemm<FMT, 4><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, S, N, Y, ldy, sstride); break;
-  }
+int launch_gemm_f(int S, int NB, int N, hipStream_t st, const float* X, int ldx, int M, int K, int KS,
+                  const uint8_t* W, const uint16_t* Sc, float* Y, int ldy, size_t sstride) {
+  const dim3 block(256), grid((N + 64 * NB - 1) / (64 * NB), S);
+  const int mt = (M + 15) / 16;
+  if (mt == 1) blk_gemm<FMT, 1, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
+  else if (mt == 2) blk_gemm<FMT, 2, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
+  else if (mt == 3 && NB == 1) blk_gemm<FMT, 3, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
+  else if (mt == 3) blk_gemm<FMT, 3, 2><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
+  else if (NB == 1) blk_gemm<FMT, 4, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
+  else blk_gemm<FMT, 4, 2><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
   return (int)hipGetLastError();
 }
 
@@ -579,13 +612,13 @@ int launch_gemm_f(dim3 grid, hipStream_t st, const float* X, int ldx, int M, int
 int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t* W, const uint16_t* Sc, int N,
          float* Y, float* part, int ldy, int* S_out, hipStream_t st) {
   int KS = 0;
-  const int S = td_block_split(N, K, ncu, &KS);
+  const int NB = nb_of((M + 15) / 16, N, ncu);
+  const int S = td_block_split(N, K, ncu, 64 * NB, &KS);
   *S_out = S;
   float* dst = S == 1 ? Y : part;
   const size_t sstride = (size_t)M * ldy;
-  const dim3 grid((N + 63) / 64, S);
-  return fmt ? launch_gemm_f<TD_WF_INT4_G64>(grid, st, X, ldx, M, K, KS, W, Sc, N, dst, ldy, sstride)
-             : launch_gemm_f<TD_WF_BF16>(grid, st, X, ldx, M, K, KS, W, Sc, N, dst, ldy, sstride);
+  return fmt ? launch_gemm_f<TD_WF_INT4_G64>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride)
+             : launch_gemm_f<TD_WF_BF16>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride);
 }
 
 }  // namespace

@@ -216,12 +216,13 @@ struct td_blockparams {
 
 #define TD_BLOCK_ARGMAX_SLICES 64  // column slices of a logits row searched in parallel
 
-// Split-K plan of one block GEMM (N weight rows, K columns, 64-row tiles):
-// GEMMs with fewer tiles than two per CU cut K into S slices of KS columns (a
-// multiple of 64), as many as keep the grid within two workgroups per CU (the
-// most that are resident at once), so that every CU runs two.  Returns S.
-static inline int td_block_split(int N, int K, int ncu, int* KS) {
-  const int tiles = (N + 63) / 64, chunks = K / 64;
+// Split-K plan of one block GEMM (N weight rows, K columns, tiles of
+// tile_rows weight rows): GEMMs with fewer tiles than two per CU cut K into S
+// slices of KS columns (a multiple of 64), as many as keep the grid within two
+// workgroups per CU (the most that are resident at once), so that every CU
+// runs two.  Returns S.
+static inline int td_block_split(int N, int K, int ncu, int tile_rows, int* KS) {
+  const int tiles = (N + tile_rows - 1) / tile_rows, chunks = K / 64;
   int s = tiles >= 2 * ncu ? 1 : (2 * ncu) / tiles;
   if (s > chunks) s = chunks;
   if (s < 1) s = 1;
