@@ -15,9 +15,11 @@ Shapes: the tiny model's whole prompt from position 0; the split-K model across
 the 63/64 chunk edge; head dim 128 with a QKV bias and 40 rows (three 16-row
 MFMA tiles, a ragged last one); int4 with a ragged K (intermediate 640) and 33
 rows; the largest block (64 rows) over 2000 cached positions; a single row.
-At full size (Llama-3.2-1B shape, bf16, and TinyLlama shape, int4) 16 rows
-against the oracle, and 64 rows against 64 greedy decode steps of the
-megakernel (a verify of the megakernel's own draft accepts every token).
+At full size against the oracle: Llama-3.2-1B (bf16) and TinyLlama (int4), 16
+rows at position 100; Qwen2.5-1.5B (d = 128, bias), 24 rows at 1000; the
+long-context int4 Llama shape, 33 rows at 8192; and 64 rows against 64 greedy
+decode steps of the megakernel (a verify of the megakernel's own draft accepts
+every token).
 """
 import math
 
@@ -56,7 +58,7 @@ def _block(td, cfg, m, k, v, toks, pos0, all_logits=True):
     return out
 
 
-def _kv_close(a2, b2, label):
+def _kv_close(a2, b2, label, atol_rel=2 ** -12):
     """Block K/V rows against reference rows, both bf16 (as float64).
 
     The block's pre-rounding values carry fp32-level errors that the matrix
@@ -67,23 +69,23 @@ def _kv_close(a2, b2, label):
     of 2^-12 of the tensor's largest value where the projection cancels to
     near zero (still far below a wrong term, head or position, which moves
     values by O(0.1)); and at most 5% of the entries one ulp apart at all."""
-    np.testing.assert_allclose(a2, b2, rtol=2 ** -7, atol=2 ** -12 * np.abs(b2).max(), err_msg=label)
+    np.testing.assert_allclose(a2, b2, rtol=2 ** -7, atol=atol_rel * np.abs(b2).max(), err_msg=label)
     frac = float(np.mean(a2 != b2))
     assert frac < 0.05, (label, frac)
     return frac
 
 
-def _check_kv(gk, gv, ok, ov, k0, v0, pos0, n, label):
+def _check_kv(gk, gv, ok, ov, k0, v0, pos0, n, label, atol_rel=2 ** -12):
     lo, hi = pos0, pos0 + n
     for a, b in ((gk, ok), (gv, ov)):
-        frac = _kv_close(bf16_to_f64(a[:, :, lo:hi]), bf16_to_f64(b[:, :, lo:hi]), label)
+        frac = _kv_close(bf16_to_f64(a[:, :, lo:hi]), bf16_to_f64(b[:, :, lo:hi]), label, atol_rel)
         _say(f"{label}: K/V entries one bf16 ulp from the oracle's: {100 * frac:.2f}%")
     for a, b in ((gk, k0), (gv, v0)):
         assert np.array_equal(a[:, :, :lo], b[:, :, :lo]), (label, "rows before pos0 changed")
         assert np.array_equal(a[:, :, hi:], b[:, :, hi:]), (label, "rows after the block changed")
 
 
-def _compare(td, cfg, m, k, v, toks, pos0, label):
+def _compare(td, cfg, m, k, v, toks, pos0, label, kv_atol_rel=2 ** -12):
     n = len(toks)
     _say(f"{label}: block of {n} rows at position {pos0}")
     got, am, word, st, gk, gv = _block(td, cfg, m, k, v, toks, pos0)
@@ -105,7 +107,7 @@ def _compare(td, cfg, m, k, v, toks, pos0, label):
             assert gap <= 2 * diff, (label, i, am[i], r, gap, diff)
         assert am[i] == int(np.argmax(got[i])), (label, i)  # lowest id among equal values
     assert word == am[-1]
-    _check_kv(gk, gv, o.k, o.v, k, v, pos0, n, label)
+    _check_kv(gk, gv, o.k, o.v, k, v, pos0, n, label, kv_atol_rel)
     _say(f"{label}: max|dlogit| = {worst:.3g}, min top-2 gap = {min_gap:.3g}")
 
 
@@ -236,14 +238,24 @@ def test_argument_checks(td):
     dec.close()
 
 
-@pytest.mark.parametrize("name", ["llama1b", "tinyllama_int4"])
-def test_fullsize_block_matches_oracle(td, name):
+@pytest.mark.parametrize("name,pos0,n,kv_atol_rel", [
+    ("llama1b", 100, 16, 2 ** -12),
+    ("tinyllama_int4", 100, 16, 2 ** -12),
+    ("qwen1p5b", 1000, 24, 2 ** -12),  # d = 128, QKV bias, 28 layers, two 16-row tiles
+    # int4, 33 rows over an 8192-position random N(0, 1) prefix.  Attention over
+    # 8192 random rows cancels heavily, and fp32 arithmetic (the decode kernel's
+    # as much as the block's) then differs from the fp64 oracle by up to one bf16
+    # ulp of the largest K/V values on entries near zero: measured max |d| 3.1e-2
+    # (|v| ~ 5) for both paths, while their logits agree with the oracle to 1e-4.
+    # Near zero the allowance is therefore one bf16 ulp of the tensor's largest value.
+    ("llama1b_int4_long", 8192, 33, 2 ** -7),
+])
+def test_fullsize_block_matches_oracle(td, name, pos0, n, kv_atol_rel):
     cfg = synth.CONFIGS[name]
     _say(f"{name}: generating the model")
     m = synth.make_model(cfg)
-    pos0 = 100
     k, v = synth.random_kv_prefix(cfg, pos0, seed_tag="block")
-    _compare(td, cfg, m, k, v, _tokens(cfg, 16), pos0, name)
+    _compare(td, cfg, m, k, v, _tokens(cfg, n), pos0, name, kv_atol_rel)
 
 
 def test_fullsize_verify_accepts_own_draft(td):
