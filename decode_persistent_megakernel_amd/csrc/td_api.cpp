@@ -168,7 +168,12 @@ int check_weights(const td_config* c, const td_weights* w) {
     if (q4 && (!L.s_qkv || !L.s_o || !L.s_gu || !L.s_d)) return fail(TD_E_INVALID_ARG, "int4 layer without scales");
     if (c->qkv_bias && !L.b_qkv) return fail(TD_E_INVALID_ARG, "qkv_bias set but b_qkv is null");
     if (c->n_experts > 0 && !L.w_router) return fail(TD_E_INVALID_ARG, "MoE layer without router weights");
+    for (const void* p : {L.attn_norm, L.w_qkv, L.s_qkv, L.b_qkv, L.w_o, L.s_o, L.mlp_norm, L.w_gu, L.s_gu, L.w_d,
+                          L.s_d, L.w_router})
+      if ((uintptr_t)p & 15) return fail(TD_E_INVALID_ARG, "layer weight pointer not 16-byte aligned");
   }
+  for (const void* p : {w->embed, w->final_norm, w->head})
+    if ((uintptr_t)p & 15) return fail(TD_E_INVALID_ARG, "weight pointer not 16-byte aligned");
   return TD_OK;
 }
 

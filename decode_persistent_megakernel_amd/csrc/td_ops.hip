@@ -10,7 +10,10 @@
 // Per layer: op_qkv (RMSNorm + QKV GEMV + bias + RoPE + K/V write), op_attn
 // (split-K partials), op_merge, op_o (+ residual), op_gu (RMSNorm + gate/up +
 // SwiGLU), op_down (+ residual); then op_head (final RMSNorm + logits + block
-// candidates) and op_argmax.  op_begin (token, range check, embedding row,
+// candidates) and op_argmax.  A mixture-of-experts layer replaces op_gu and
+// op_down with op_router (RMSNorm + router logits), op_moe_gu (top-k choice +
+// the chosen experts' gate/up + SwiGLU) and op_moe_down (the chosen experts'
+// down rows, weighted, + residual).  op_begin (token, range check, embedding row,
 // position word) runs first and is the only launch that carries the step's
 // arguments, so the rest can be captured once and replayed.
 #include <hip/hip_runtime.h>
@@ -26,13 +29,48 @@ namespace {
 
 constexpr int OP_WAVES = 4;  // waves per workgroup of the GEMV ops
 
+// Staging into LDS.  A thread's share of a vector is the 4-float groups
+// t, t + T, ... (T threads); all of a thread's loads of a batch of NV groups
+// are issued before its first LDS store, from clamped addresses so every load
+// is unconditional, and a block pays one load round trip per batch instead of
+// one per element.  Lengths are multiples of 4 floats and buffers 16-byte
+// aligned (the config and weight checks enforce both).
+
 // RMSNorm of x [H] in the persistent kernel's form: xs = x * gain in LDS, and
 // the returned inv = 1 / sqrt(mean(x^2) + eps) (the caller multiplies each dot
 // product by it), mean(x^2) summed over the same TD_NW slices in the same order
-// (slice_ssq, norm_inv).  Needs blockDim.x >= 64.
-DEV float op_norm_to_lds(const float* x, const uint16_t* gain, int H, float eps, float* xs, float* red) {
-  const int t = threadIdx.x, wave = t >> 6, nwaves = blockDim.x >> 6;
-  for (int i = t; i < H; i += blockDim.x) xs[i] = x[i];
+// (slice_ssq, norm_inv).  With H <= 4 NV T the gains are loaded with x and
+// held in registers across the sum of squares.  With zsrc, wave 0 also copies
+// the zn router logits zsrc to zs [TD_MAX_EXPERTS], padded with -inf, their
+// loads in flight with its share of x.  Needs blockDim.x >= 64.
+template <int NV>
+DEV float op_norm_to_lds_n(const float* x, const uint16_t* gain, int H, float eps, float* xs, float* red,
+                           const float* zsrc, int zn, float* zs) {
+  constexpr int ZPER = TD_MAX_EXPERTS / 64;
+  const int t = threadIdx.x, T = blockDim.x, wave = t >> 6, nwaves = T >> 6;
+  const int n4 = H >> 2;
+  f32x4 v[NV];
+  uint2 g[NV];
+  float z[ZPER];
+  for (int b = 0; b < n4; b += NV * T) {
+    if (b == 0 && zsrc && wave == 0) {
+#pragma unroll
+      for (int i = 0; i < ZPER; ++i) z[i] = zsrc[min(t + 64 * i, zn - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = min(b + u * T + t, n4 - 1);
+      v[u] = *(const f32x4*)(x + 4 * i);
+      g[u] = *(const uint2*)(gain + 4 * i);
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      if (b + u * T + t < n4) *(f32x4*)(xs + 4 * (b + u * T + t)) = v[u];
+    if (b == 0 && zsrc && wave == 0) {
+#pragma unroll
+      for (int i = 0; i < ZPER; ++i) zs[t + 64 * i] = t + 64 * i < zn ? z[i] : -__builtin_inff();
+    }
+  }
   __syncthreads();
   for (int w = wave; w < TD_NW; w += nwaves) {
     int lo, hi;
@@ -40,20 +78,69 @@ DEV float op_norm_to_lds(const float* x, const uint16_t* gain, int H, float eps,
     const float ss = slice_ssq(xs, lo, hi);
     if (lane_id() == 0) red[w] = ss;
   }
-  __syncthreads();
+  __syncthreads();  // every slice sum is in red and no wave reads xs again
   const float inv = norm_inv(red, H, eps);
-  __syncthreads();
-  for (int i = t * 2; i < H; i += blockDim.x * 2) {
-    const uint32_t g = *(const uint32_t*)(gain + i);
-    xs[i] *= bf_lo(g);
-    xs[i + 1] *= bf_hi(g);
+  for (int b = 0; b < n4; b += NV * T) {
+    if (n4 > NV * T) {  // several batches: the gains and x of this one again
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int i = min(b + u * T + t, n4 - 1);
+        v[u] = *(const f32x4*)(xs + 4 * i);
+        g[u] = *(const uint2*)(gain + 4 * i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = b + u * T + t;
+      if (i >= n4) continue;
+      f32x4 a = v[u];
+      a.x *= bf_lo(g[u].x);
+      a.y *= bf_hi(g[u].x);
+      a.z *= bf_lo(g[u].y);
+      a.w *= bf_hi(g[u].y);
+      *(f32x4*)(xs + 4 * i) = a;
+    }
   }
   return inv;
 }
 
-// Copies n floats to LDS and zeroes the tail up to the chunk multiple.
-DEV void op_copy_to_lds(const float* src, int n, int npad, float* xs) {
-  for (int i = threadIdx.x; i < npad; i += blockDim.x) xs[i] = i < n ? src[i] : 0.f;
+DEV float op_norm_to_lds(const float* x, const uint16_t* gain, int H, float eps, float* xs, float* red,
+                         const float* zsrc = nullptr, int zn = 0, float* zs = nullptr) {
+  const int per = (H / 4 + (int)blockDim.x - 1) / (int)blockDim.x;
+  if (per <= 2) return op_norm_to_lds_n<2>(x, gain, H, eps, xs, red, zsrc, zn, zs);
+  if (per <= 4) return op_norm_to_lds_n<4>(x, gain, H, eps, xs, red, zsrc, zn, zs);
+  return op_norm_to_lds_n<8>(x, gain, H, eps, xs, red, zsrc, zn, zs);
+}
+
+// Copies `rows` vectors of n floats (row j at src + j n) to LDS at xs + j kp,
+// each zero-filled from n up to kp.
+template <int NV>
+DEV void op_stage_rows_n(const float* src, int rows, int n, int kp, float* xs) {
+  const int t = threadIdx.x, T = blockDim.x;
+  const int n4 = n >> 2, k4 = kp >> 2, tot = rows * k4;
+  for (int b = 0; b < tot; b += NV * T) {
+    f32x4 v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = min(b + u * T + t, tot - 1);
+      const int r = i / k4, c = i - r * k4;
+      v[u] = *(const f32x4*)(src + (size_t)r * n + 4 * min(c, n4 - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = b + u * T + t;
+      if (i >= tot) continue;
+      const int r = i / k4, c = i - r * k4;
+      *(f32x4*)(xs + 4 * i) = c < n4 ? v[u] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+DEV void op_stage_rows(const float* src, int rows, int n, int kp, float* xs) {
+  const int per = (rows * (kp >> 2) + (int)blockDim.x - 1) / (int)blockDim.x;
+  if (per <= 2) op_stage_rows_n<2>(src, rows, n, kp, xs);
+  else if (per <= 4) op_stage_rows_n<4>(src, rows, n, kp, xs);
+  else op_stage_rows_n<8>(src, rows, n, kp, xs);
 }
 
 DEV void op_zero_tail(float* xs, int from, int to) {
@@ -316,7 +403,7 @@ __global__ void __launch_bounds__(256) op_resid(td_opparams P, int layer, int wh
   float* xs = (float*)lds;
   const td_layer_dev& Ld = P.layers[layer];
   const int K = which == 1 ? P.qd : P.I;
-  op_copy_to_lds(which == 1 ? P.o : P.act, K, op_kpad(K, P.wf), xs);
+  op_stage_rows(which == 1 ? P.o : P.act, 1, K, op_kpad(K, P.wf), xs);
   __syncthreads();
   const int wave = threadIdx.x >> 6;
   for (int k = 0; k < R; ++k) {
@@ -366,24 +453,25 @@ __global__ void __launch_bounds__(256) op_router(td_opparams P, int layer) {
   if (lane_id() == 0) P.rlogits[e] = z;
 }
 
-// op_topk (one wave): the topk largest router logits in decreasing order, the
-// lower id first among equals, into expert_ids[layer]; their softmax
-// probabilities over all E experts (max subtracted, the sum reduced in a fixed
-// lane order) into expert_w[layer].  A non-finite logit raises the error bit;
-// the ids are then 0 .. topk - 1 with weight 0 (every later read stays in
-// bounds).
-__global__ void __launch_bounds__(64) op_topk(td_opparams P, int layer) {
+// moe_select (one wave): the router's choice from the E logits zs (LDS,
+// padded with -inf to a multiple of 4).  The topk largest logits in decreasing
+// order, the lower id first among equals: expert e takes slot rank(e), the
+// number of experts with a larger logit or an equal one and a lower id, if that
+// is below topk.  Their softmax probabilities over all E experts (max
+// subtracted, the sum reduced in a fixed lane order) go to wts.  A non-finite
+// logit gives ids 0 .. topk - 1 with weight 0 (every later read stays in
+// bounds) and returns true.  Every caller computes the same bits from the same
+// logits.
+DEV bool moe_select(const td_opparams& P, const float* zs, int32_t* ids, float* wts) {
   constexpr int PER = TD_MAX_EXPERTS / 64;
   const int lane = lane_id();
   float z[PER];
-  bool tk[PER];
   float m = -__builtin_inff();
   int bad = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    tk[i] = e >= P.E;
-    z[i] = e < P.E ? P.rlogits[e] : -__builtin_inff();
+    z[i] = zs[e];
     if (e < P.E && !isfinite(z[i])) bad = 1;
     if (e < P.E) m = fmaxf(m, z[i]);
   }
@@ -394,43 +482,30 @@ __global__ void __launch_bounds__(64) op_topk(td_opparams P, int layer) {
   for (int i = 0; i < PER; ++i)
     if (lane + 64 * i < P.E) ssum += expf(z[i] - m);
   ssum = wave_sum(ssum);
-  int32_t* ids = P.expert_ids + layer * P.topk;
-  float* wts = P.expert_w + layer * P.topk;
   if (bad) {
     if (lane < P.topk) {
       ids[lane] = lane;
       wts[lane] = 0.f;
     }
-    if (lane == 0) atomicOr(P.err, TD_ERRBIT_NONFINITE);
-    return;
+    return true;
   }
-  for (int j = 0; j < P.topk; ++j) {
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
+  const int E4 = (P.E + 3) & ~3;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      if (!tk[i] && (bi == 0x7fffffff || z[i] > bv)) {  // e ascends with i: the first of equals stays
-        bv = z[i];
-        bi = e;
-      }
+  for (int i = 0; i < PER; ++i) {
+    if (64 * i >= P.E) break;
+    const int e = lane + 64 * i;
+    int rank = 0;
+    for (int c = 0; c < E4; c += 4) {  // the same address in every lane: a broadcast read
+      const f32x4 q = *(const f32x4*)(zs + c);
+      rank += (q.x > z[i] || (q.x == z[i] && c < e)) + (q.y > z[i] || (q.y == z[i] && c + 1 < e)) +
+              (q.z > z[i] || (q.z == z[i] && c + 2 < e)) + (q.w > z[i] || (q.w == z[i] && c + 3 < e));
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i == bi) tk[i] = true;
-    if (lane == 0) {
-      ids[j] = bi;
-      wts[j] = expf(bv - m) / ssum;
+    if (e < P.E && rank < P.topk) {
+      ids[rank] = e;
+      wts[rank] = expf(z[i] - m) / ssum;
     }
   }
+  return false;
 }
 
 // Expert e's block of a stacked [E][rows][K] linear (codes and scales).
@@ -442,21 +517,37 @@ DEV const uint16_t* expert_s(const uint16_t* s, int fmt, int e, int rows, int K)
 }
 
 // op_moe_gu: unit u = j I + r: row r of the j-th chosen expert's gate and up
-// projections of RMSNorm(x), act[j][r] = SiLU(gate) * up.
+// projections of RMSNorm(x), act[j][r] = SiLU(gate) * up.  Wave 0 of every
+// block stages the router logits with x and makes the router's choice
+// (moe_select) while the other waves finish the norm;
+// block 0 publishes it in expert_ids[layer] and expert_w[layer] for op_moe_down
+// and the caller, and raises the error bit on a non-finite router logit.
 __global__ void __launch_bounds__(256) op_moe_gu(td_opparams P, int layer, int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) float zs[TD_MAX_EXPERTS];
+  __shared__ int32_t sid[TD_MAX_TOPK];
+  __shared__ float swt[TD_MAX_TOPK];
   float* xs = (float*)lds;
   const td_layer_dev& Ld = P.layers[layer];
-  const float inv = op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf));
+  const int wave = threadIdx.x >> 6;
+  const float inv = op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf), P.rlogits, P.E, zs);
+  bool bad = false;
+  if (wave == 0) bad = moe_select(P, zs, sid, swt);
   op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
-  const int32_t* ids = P.expert_ids + layer * P.topk;
+  if (blockIdx.x == 0 && wave == 0) {
+    const int lane = lane_id();
+    if (lane < P.topk) {
+      P.expert_ids[layer * P.topk + lane] = sid[lane];
+      P.expert_w[layer * P.topk + lane] = swt[lane];
+    }
+    if (bad && lane == 0) atomicOr(P.err, TD_ERRBIT_NONFINITE);
+  }
   for (int k = 0; k < R; ++k) {
     const int u = (blockIdx.x * OP_WAVES + wave) * R + k;
     if (u >= P.topk * P.I) break;
     const int j = u / P.I, r = u - j * P.I;
-    const int e = uni(ids[j]);
+    const int e = uni(sid[j]);
     const uint8_t* w = expert_w(Ld.w[2], P.wf, e, 2 * P.I, P.H);
     const uint16_t* sc = expert_s(Ld.s[2], P.wf, e, 2 * P.I, P.H);
     const float gt = op_row(P.wf, w, sc, r, P.H, xs) * inv;
@@ -472,7 +563,7 @@ __global__ void __launch_bounds__(256) op_moe_down(td_opparams P, int layer, int
   float* xs = (float*)lds;
   const td_layer_dev& Ld = P.layers[layer];
   const int kp = op_kpad(P.I, P.wf);
-  for (int j = 0; j < P.topk; ++j) op_copy_to_lds(P.act + (size_t)j * P.I, P.I, kp, xs + (size_t)j * kp);
+  op_stage_rows(P.act, P.topk, P.I, kp, xs);
   __syncthreads();
   const int wave = threadIdx.x >> 6;
   const int32_t* ids = P.expert_ids + layer * P.topk;
@@ -565,7 +656,7 @@ __global__ void __launch_bounds__(64) op_argmax(td_opparams P, int nblocks) {
 
 // --------------------------------------------------------------- launchers
 namespace {
-constexpr int R_QKV = 1, R_RESID = 1, R_GU = 4, R_HEAD = 16;
+constexpr int R_QKV = 1, R_RESID = 1, R_GU = 4, R_HEAD = 16, R_MOE_GU = 2, R_MOE_DOWN = 1;
 int blocks_for(int units, int r) { return (units + OP_WAVES * r - 1) / (OP_WAVES * r); }
 }  // namespace
 
@@ -603,9 +694,8 @@ int td_launch_op_layers(const td_opparams* p, void* stream) {
     op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 1, R_RESID);
     if (P.E > 0) {
       op_router<<<blocks_for(P.E, 1), 256, lds, s>>>(P, l);
-      op_topk<<<1, 64, 0, s>>>(P, l);
-      op_moe_gu<<<blocks_for(P.topk * P.I, R_GU), 256, lds, s>>>(P, l, R_GU);
-      op_moe_down<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, R_RESID);
+      op_moe_gu<<<blocks_for(P.topk * P.I, R_MOE_GU), 256, lds, s>>>(P, l, R_MOE_GU);
+      op_moe_down<<<blocks_for(P.H, R_MOE_DOWN), 256, lds, s>>>(P, l, R_MOE_DOWN);
     } else {
       op_gu<<<blocks_for(P.I, R_GU), 256, lds, s>>>(P, l, R_GU);
       op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 3, R_RESID);

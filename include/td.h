@@ -82,7 +82,10 @@ typedef struct td_config {
 #define TD_MAX_EXPERTS 256
 #define TD_MAX_TOPK 16
 
-/* Device pointers of one layer.  Shapes are [rows][cols], row = output. */
+/* Device pointers of one layer.  Shapes are [rows][cols], row = output.  Every
+ * weight pointer (these and those of td_weights) must be 16-byte aligned: the
+ * kernels read rows in 16-byte pieces (td_create returns TD_E_INVALID_ARG
+ * otherwise; hipMalloc and torch allocations satisfy it). */
 typedef struct td_layer_weights {
     const void* attn_norm;  /* bf16 [H] */
     const void* w_qkv;      /* [(nq + 2 nkv) d][H]: q rows, then k rows, then v rows */
@@ -124,7 +127,8 @@ typedef struct td_ctx td_ctx;
  * must stay valid and unchanged for the life of the context.
  * Errors: TD_E_INVALID_ARG (null pointer, shape not positive, n_kv_heads not
  * dividing n_q_heads, head_dim not 64 or 128, a dimension not a multiple of 64,
- * more than 8 query heads per kv head, missing scales or bias), TD_E_UNSUPPORTED
+ * more than 8 query heads per kv head, missing scales or bias, a weight pointer
+ * not 16-byte aligned), TD_E_UNSUPPORTED
  * (device is not gfx950, or its CU count is not a multiple of 8), TD_E_PLAN,
  * TD_E_NOMEM, TD_E_HIP.  On error *out is set to NULL.
  * A mixture-of-experts config runs on TD_EXEC_PER_OP and TD_EXEC_GRAPH only: the

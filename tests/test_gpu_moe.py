@@ -151,3 +151,29 @@ def test_fullsize_olmoe_matches_oracle(td):
     k, v = synth.random_kv_prefix(cfg, cfg.start_pos)
     _say(f"olmoe: 8 teacher-forced steps from position {cfg.start_pos} (graph executor)")
     _run(td, cfg, m, k, v, synth.first_token(cfg), cfg.start_pos, 8, td.TD_EXEC_GRAPH, "olmoe")
+
+
+def test_tied_router_logits_take_the_lower_id_first(td):
+    """Equal router logits: the lower expert id takes the earlier slot.  The top
+    expert's router row is copied to two other experts of layer 0, so from the
+    first step on three experts share the largest logit bit for bit (the rows are
+    identical, so both sides compute identical logits for them); the kernel must
+    then order them by id, as the oracle does, on every step."""
+    cfg = MOE_BF16
+    m = synth.make_model(cfg)
+    k, v = synth.random_kv_prefix(cfg, 30, seed_tag="moe")
+    o = oracle.Oracle(m)
+    o.set_kv(k, v)
+    _, tr = o.step_traced(synth.first_token(cfg), 30)
+    top = int(tr["expert_ids"][0][0])
+    twins = sorted({(top + 3) % cfg.n_experts, (top + cfg.n_experts - 5) % cfg.n_experts})
+    m.layers[0].router = m.layers[0].router.copy()
+    for e in twins:
+        m.layers[0].router[e, :] = m.layers[0].router[top, :]
+    o = oracle.Oracle(m)
+    o.set_kv(k, v)
+    _, tr = o.step_traced(synth.first_token(cfg), 30)
+    assert sorted(tr["expert_ids"][0][:3].tolist()) == sorted([top] + twins)
+    assert tr["expert_ids"][0][:3].tolist() == sorted([top] + twins)  # the oracle's own tie order
+    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH):
+        _run(td, cfg, m, k, v, synth.first_token(cfg), 30, 4, ex, f"ties/{ex}")
