@@ -292,7 +292,7 @@ def main() -> int:
             bms = np.array([a.elapsed_time(b) for a, b in bev])
             baselines[name] = {"tokens_per_s": round(nb / (bms.sum() / 1e3), 2), "ms_per_step": round(float(bms.mean()), 4),
                                "steps": nb,
-                               "launches_per_step": (((8 if moe else 6) * cfg.n_layers + 3) if name == "per_op"
+                               "launches_per_step": (((7 if moe else 6) * cfg.n_layers + 3) if name == "per_op"
                                                      else 2)}
             bdec.close()
             del bdec
