@@ -614,7 +614,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
       bo += (size_t)round_up((int64_t)bytes, 256);
       return o;
     };
-    const size_t b_x = btake(R * H * 4), b_xn = btake(R * H * 4), b_act = btake(R * I * 4);
+    const size_t b_x = btake(R * H * 4), b_xg = btake(R * H * 4), b_act = btake(R * I * 4);
     const size_t b_part = btake(part_floats * 4), b_ssq = btake(R * (H / 256) * 4);
     const size_t b_cand = btake(R * TD_BLOCK_ARGMAX_SLICES * 8);
     const size_t b_y = btake(R * ymax * 4), b_q = btake(R * qd * 4), b_ao = btake(R * qd * 4);
@@ -628,7 +628,7 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     uint8_t* bb = (uint8_t*)ctx->blockbuf;
     ctx->blk.ncu = ncu;
     ctx->blk.x = (float*)(bb + b_x);
-    ctx->blk.xn = (float*)(bb + b_xn);
+    ctx->blk.xg = (float*)(bb + b_xg);
     ctx->blk.act = (float*)(bb + b_act);
     ctx->blk.ssq = (float*)(bb + b_ssq);
     ctx->blk.cand = (uint2*)(bb + b_cand);

@@ -19,9 +19,10 @@
 // One kernel launch per op (the prompt path is not latency-bound like a decode
 // step).  Per layer: residual update + RMSNorm statistics, QKV GEMM (the norm
 // applied while staging), QKV epilogue (bias, RoPE, K/V write), attention, O
-// GEMM, residual update + statistics, gate/up GEMM, down GEMM (SiLU(gate) * up
-// formed while staging); then the final statistics, the logits GEMM (the last
-// row or every row) and the greedy token of each logits row.  GEMMs with fewer
+// GEMM, residual update + statistics, gate/up GEMM (the norm applied while
+// staging), SwiGLU, down GEMM; then the final residual update + statistics, the
+// logits GEMM (normalised while staging; the last row or every row) and the
+// greedy token of each logits row.  GEMMs with fewer
 // 64-row weight tiles than CUs split K into slices whose partial sums are
 // added by their consumer in slice order (deterministic results).
 #include <hip/hip_runtime.h>
@@ -66,11 +67,12 @@ __global__ void __launch_bounds__(256) blk_embed(const uint16_t* embed, const in
 }
 
 // Columns 256 b .. + 256 of row i of the residual stream: x += the S partial
-// sums of the producing GEMM (slice order; S = 0 adds nothing); the block's
-// sum of squares of the updated values goes to ssq[i][b] (wave sums in wave
-// order), for blk_norm.
+// sums of the producing GEMM (slice order; S = 0 adds nothing); xg = x * gain,
+// the input of the GEMM that consumes RMSNorm(x); the block's sum of squares
+// of the updated values goes to ssq[i][b] (wave sums in wave order), from
+// which that GEMM forms the row's 1 / rms.
 __global__ void __launch_bounds__(256) blk_resid(float* x, const float* part, int S, size_t sstride, int H,
-                                                 float* ssq) {
+                                                 const uint16_t* gain, float* xg, float* ssq) {
   __shared__ float red[4];
   const int i = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
   const size_t o = (size_t)i * H + e;
@@ -80,20 +82,9 @@ __global__ void __launch_bounds__(256) blk_resid(float* x, const float* part, in
     for (int s = 0; s < S; ++s) v += part[s * sstride + o];
     x[o] = v;
   }
+  xg[o] = v * bf16f(gain[e]);
   const float ss = block_sum(v * v, red);
   if (threadIdx.x == 0) ssq[i * gridDim.x + blockIdx.x] = ss;
-}
-
-// xn = x * gain / sqrt(mean(x^2) + eps) for columns 256 b .. + 256 of row i,
-// the row's sum of squares being its nb block sums added in block order.
-__global__ void __launch_bounds__(256) blk_norm(const float* x, const float* ssq, int H, float eps,
-                                                const uint16_t* gain, float* xn) {
-  const int i = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x, nb = gridDim.x;
-  float ss = ssq[i * nb];
-  for (int b = 1; b < nb; ++b) ss += ssq[i * nb + b];
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  const size_t o = (size_t)i * H + e;
-  xn[o] = x[o] * bf16f(gain[e]) * inv;
 }
 
 // act = SiLU(gate) * up from the gate/up GEMM output [gate I | up I] (the sum
@@ -285,9 +276,14 @@ constexpr int ring_depth() {
 // CU; otherwise one, which keeps the split-K slices of short matrices long.
 inline int nb_of(int mt, int N, int ncu) { return (mt >= 3 && N >= 64 * ncu) ? 2 : 1; }
 
-template <int FMT, int MT, int NB>
+// With NORM, X holds x * gain and the result is RMSNorm(x) W^T: row m of the
+// product is multiplied by row m's 1 / rms, its sum of squares being the nbs
+// block sums ssq[m nbs ..] of blk_resid added in block order (the decode step's
+// form: the gains scale the input, 1 / rms the finished dot products).
+template <int FMT, int MT, int NB, bool NORM>
 __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, int K, int KS, const uint8_t* W,
-                                                const uint16_t* Sc, int N, float* Y, int ldy, size_t sstride) {
+                                                const uint16_t* Sc, int N, float* Y, int ldy, size_t sstride,
+                                                const float* ssq, int nbs, float eps) {
   constexpr int PART = MT * 16 * XP;
   constexpr int D = ring_depth<FMT, MT, NB>();
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][3 * PART];
@@ -308,6 +304,17 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
     }
   }
   const float* xb = X + kb;
+  // NORM: thread t < M forms row t's 1 / rms.  Its first 8 block sums are
+  // loaded before the weights of the prologue, so that waiting for them leaves
+  // those in flight (every thread loads, from a clamped row, so that the wait
+  // counts stay exact).
+  __shared__ float invs[NORM ? 64 : 1];
+  float sv[8];
+  const int nrow = min((int)threadIdx.x, M - 1);
+  if constexpr (NORM) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sv[u] = ssq[nrow * nbs + min(u, nbs - 1)];
+  }
   f32x4 acc[MT][NB];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -321,8 +328,16 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) load_chunk<FMT>(ring[i].w[nb], wrow[nb], srow[nb], ch, q);
   }
+  if constexpr (NORM) {
+    float ss = sv[0];  // the block sums added in block order
+#pragma unroll
+    for (int u = 1; u < 8; ++u)
+      if (u < nbs) ss += sv[u];
+    for (int b = 8; b < nbs; ++b) ss += ssq[nrow * nbs + b];
+    if (threadIdx.x < 64) invs[threadIdx.x] = 1.0f / sqrtf(ss / (float)K + eps);
+  }
   stage_store<MT>(xs[0], ring[0].x);
-  wg_bar();
+  wg_bar();  // (also makes invs visible)
   for (int c0 = 0; c0 < nch; c0 += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -350,7 +365,7 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * t + 4 * q + e;
-        if (m < M) dst[(size_t)m * ldy] = rv[e];
+        if (m < M) dst[(size_t)m * ldy] = NORM ? rv[e] * invs[m] : rv[e];
       }
     }
   }
@@ -592,33 +607,52 @@ __global__ void __launch_bounds__(64) blk_argmax_final(const uint2* cand, int nb
   if (r == rows - 1) *token_word = tok;
 }
 
-template <int FMT>
-int launch_gemm_f(int S, int NB, int N, hipStream_t st, const float* X, int ldx, int M, int K, int KS,
-                  const uint8_t* W, const uint16_t* Sc, float* Y, int ldy, size_t sstride) {
+// RMSNorm by row scaling of the product (ssq non-null) or none.
+struct NormArgs {
+  const float* ssq;
+  int nbs;
+  float eps;
+};
+
+template <int FMT, bool NORM>
+int launch_gemm_n(int S, int NB, int N, hipStream_t st, const float* X, int ldx, int M, int K, int KS,
+                  const uint8_t* W, const uint16_t* Sc, float* Y, int ldy, size_t sstride, const NormArgs& a) {
   const dim3 block(256), grid((N + 64 * NB - 1) / (64 * NB), S);
   const int mt = (M + 15) / 16;
-  if (mt == 1) blk_gemm<FMT, 1, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
-  else if (mt == 2) blk_gemm<FMT, 2, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
-  else if (mt == 3 && NB == 1) blk_gemm<FMT, 3, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
-  else if (mt == 3) blk_gemm<FMT, 3, 2><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
-  else if (NB == 1) blk_gemm<FMT, 4, 1><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
-  else blk_gemm<FMT, 4, 2><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride);
+#define TD_GEMM(MT_, NB_)                                                                                      \
+  blk_gemm<FMT, MT_, NB_, NORM><<<grid, block, 0, st>>>(X, ldx, M, K, KS, W, Sc, N, Y, ldy, sstride, a.ssq, a.nbs, \
+                                                        a.eps)
+  if (mt == 1) TD_GEMM(1, 1);
+  else if (mt == 2) TD_GEMM(2, 1);
+  else if (mt == 3 && NB == 1) TD_GEMM(3, 1);
+  else if (mt == 3) TD_GEMM(3, 2);
+  else if (NB == 1) TD_GEMM(4, 1);
+  else TD_GEMM(4, 2);
+#undef TD_GEMM
   return (int)hipGetLastError();
 }
 
-// X W^T, N columns with row pitch ldy.  With one K slice the result goes to Y;
-// with S > 1 slices, slice s goes to part + s M ldy and the consumer adds them
-// in slice order.  *S_out receives S.
+template <int FMT>
+int launch_gemm_f(int S, int NB, int N, hipStream_t st, const float* X, int ldx, int M, int K, int KS,
+                  const uint8_t* W, const uint16_t* Sc, float* Y, int ldy, size_t sstride, const NormArgs& a) {
+  return a.ssq ? launch_gemm_n<FMT, true>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, Y, ldy, sstride, a)
+                : launch_gemm_n<FMT, false>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, Y, ldy, sstride, a);
+}
+
+// X W^T (with norm.ssq, X = x * gain and the rows scaled to RMSNorm(x) W^T),
+// N columns with row pitch ldy.  With
+// one K slice the result goes to Y; with S > 1 slices, slice s goes to
+// part + s M ldy and the consumer adds them in slice order.  *S_out receives S.
 int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t* W, const uint16_t* Sc, int N,
-         float* Y, float* part, int ldy, int* S_out, hipStream_t st) {
+         float* Y, float* part, int ldy, int* S_out, hipStream_t st, const NormArgs& norm) {
   int KS = 0;
   const int NB = nb_of((M + 15) / 16, N, ncu);
   const int S = td_block_split(N, K, ncu, 64 * NB, &KS);
   *S_out = S;
   float* dst = S == 1 ? Y : part;
   const size_t sstride = (size_t)M * ldy;
-  return fmt ? launch_gemm_f<TD_WF_INT4_G64>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride)
-             : launch_gemm_f<TD_WF_BF16>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride);
+  return fmt ? launch_gemm_f<TD_WF_INT4_G64>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride, norm)
+             : launch_gemm_f<TD_WF_BF16>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride, norm);
 }
 
 }  // namespace
@@ -638,13 +672,14 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
   } while (0)
   const int hb = H / 256;  // column blocks of the residual stream (H is a multiple of 256)
   const dim3 rgrid(hb, n);
+  const NormArgs no_norm{nullptr, 0, 0.f}, norm{B->ssq, hb, P.eps};
   TD_CK((blk_embed<<<n, 256, 0, st>>>(P.embed, tokens, H, P.V, B->x, P.err)));
   for (int l = 0; l < L; ++l) {
     const td_layer_dev& Ld = B->layers_host[l];
     // x += the previous layer's down-projection slices; attention RMSNorm
-    TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, B->ssq)));
-    TD_CK((blk_norm<<<rgrid, 256, 0, st>>>(B->x, B->ssq, H, P.eps, Ld.attn_norm, B->xn)));
-    if ((e = gemm(P.wf, ncu, B->xn, H, n, H, Ld.w[0], Ld.s[0], P.qkv_rows, B->y, part, P.qkv_rows, &S, st))) return e;
+    TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, Ld.attn_norm, B->xg, B->ssq)));
+    if ((e = gemm(P.wf, ncu, B->xg, H, n, H, Ld.w[0], Ld.s[0], P.qkv_rows, B->y, part, P.qkv_rows, &S, st, norm)))
+      return e;
     TD_CK((blk_qkv_post<<<dim3((P.qkv_rows / 2 + 255) / 256, n), 256, 0, st>>>(
         S == 1 ? B->y : part, S, (size_t)n * P.qkv_rows, P.qkv_rows, qd, P.kvd, d, P.nkv, P.max_ctx, l, pos0, Ld.bias,
         P.rope_cs, P.attn_scale, B->q, P.kc, P.vc)));
@@ -656,19 +691,17 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
       TD_CK((blk_attn<128><<<agrid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0,
                                                   B->ao)));
     // the O and down projections always land in part (slice 0 when unsplit)
-    if ((e = gemm(P.wf, ncu, B->ao, qd, n, qd, Ld.w[1], Ld.s[1], H, part, part, H, &S, st))) return e;
-    TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, B->ssq)));
-    TD_CK((blk_norm<<<rgrid, 256, 0, st>>>(B->x, B->ssq, H, P.eps, Ld.mlp_norm, B->xn)));
-    if ((e = gemm(P.wf, ncu, B->xn, H, n, H, Ld.w[2], Ld.s[2], 2 * I, B->y, part, 2 * I, &S, st))) return e;
+    if ((e = gemm(P.wf, ncu, B->ao, qd, n, qd, Ld.w[1], Ld.s[1], H, part, part, H, &S, st, no_norm))) return e;
+    TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, Ld.mlp_norm, B->xg, B->ssq)));
+    if ((e = gemm(P.wf, ncu, B->xg, H, n, H, Ld.w[2], Ld.s[2], 2 * I, B->y, part, 2 * I, &S, st, norm))) return e;
     TD_CK((blk_swiglu<<<dim3((I + 255) / 256, n), 256, 0, st>>>(S == 1 ? B->y : part, S, (size_t)n * 2 * I, I,
                                                                B->act)));
-    if ((e = gemm(P.wf, ncu, B->act, I, n, I, Ld.w[3], Ld.s[3], H, part, part, H, &S_prev, st))) return e;
+    if ((e = gemm(P.wf, ncu, B->act, I, n, I, Ld.w[3], Ld.s[3], H, part, part, H, &S_prev, st, no_norm))) return e;
   }
-  TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, B->ssq)));
-  TD_CK((blk_norm<<<rgrid, 256, 0, st>>>(B->x, B->ssq, H, P.eps, P.final_norm, B->xn)));
+  TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, P.final_norm, B->xg, B->ssq)));
   const int r0 = all_logits ? 0 : n - 1, rows = all_logits ? n : 1;
-  if ((e = gemm(TD_WF_BF16, ncu, B->xn + (size_t)r0 * H, H, rows, H, (const uint8_t*)P.head, nullptr, P.V, logits,
-                part, P.V, &S, st)))
+  if ((e = gemm(TD_WF_BF16, ncu, B->xg + (size_t)r0 * H, H, rows, H, (const uint8_t*)P.head, nullptr, P.V, logits,
+                part, P.V, &S, st, NormArgs{B->ssq + (size_t)r0 * hb, hb, P.eps})))
     return e;
   if (S > 1) TD_CK((blk_sum_parts<<<dim3((P.V + 255) / 256, rows), 256, 0, st>>>(part, S, (size_t)rows * P.V, P.V,
                                                                                  logits)));

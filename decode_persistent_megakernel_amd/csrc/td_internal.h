@@ -204,8 +204,8 @@ struct td_blockparams {
   const td_layer_dev* layers_host; // [L] the layer pointers, host copy
   int ncu;                         // CUs of the device (split-K sizing)
   float* x;                        // [n][H] residual stream
-  float* xn;                       // [n][H] RMSNorm of x (a GEMM input)
   float* y;                        // [n][max(qkv_rows, 2 I)] QKV or gate/up output
+  float* xg;                       // [n][H] x * gain of the next RMSNorm (a GEMM input)
   float* act;                      // [n][I] SiLU(gate) * up (a GEMM input)
   float* ssq;                      // [n][H / 256] block sums of squares of x (RMSNorm)
   uint2* cand;                     // [n][TD_BLOCK_ARGMAX_SLICES] greedy-token candidates
