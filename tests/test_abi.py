@@ -110,3 +110,24 @@ def test_null_arguments_are_rejected():
     assert L.td_forward_block(None, None, 4, 0, ctypes.byref(kv), None, 0, None, None) == _lib.TD_E_INVALID_ARG
     assert L.td_status(None, None) == _lib.TD_E_INVALID_ARG
     L.td_destroy(None)  # a no-op
+
+
+@pytest.mark.parametrize("field", ["attn_norm", "w_qkv", "s_o", "b_qkv", "w_gu", "embed", "head", "final_norm"])
+def test_create_rejects_weight_pointers_not_16_byte_aligned(field):
+    """The kernels read weight rows and norm gains in 16-byte pieces, so td_create
+    refuses a weight pointer that is not 16-byte aligned (8-byte aligned here),
+    before any device call; the same weights aligned get past this check (and
+    fail later, at the device query, on a host without a GPU)."""
+    L = _lib.lib()
+    cfg = _valid_config(weight_format=_lib.TD_WF_INT4_G64, qkv_bias=1)
+    w, arr = _fake_weights(cfg.n_layers, scales=True, bias=True)
+    h = ctypes.c_void_p()
+    rc_aligned = L.td_create(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.byref(h))
+    assert rc_aligned != _lib.TD_E_INVALID_ARG
+    if field in ("embed", "head", "final_norm"):
+        setattr(w, field, 0x10008)
+    else:
+        setattr(arr[1], field, 0x10008)
+    assert L.td_create(ctypes.byref(cfg), ctypes.byref(w), 0, ctypes.byref(h)) == _lib.TD_E_INVALID_ARG
+    assert b"16-byte aligned" in L.td_last_error()
+    assert not h.value
