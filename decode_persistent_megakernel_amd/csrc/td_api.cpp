@@ -688,6 +688,7 @@ int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv
                    void* stream) {
   if (!ctx || !d_token || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
   if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (((uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return fail(TD_E_INVALID_ARG, "K/V cache pointer not 16-byte aligned");
   if (pos < 0 || pos >= ctx->cfg.max_ctx) return fail(TD_E_RANGE, "pos outside [0, max_ctx)");
   td_kparams p = ctx->kp;
   p.pos = pos;
@@ -736,6 +737,7 @@ int td_decode_loop(td_ctx* ctx, const int32_t* d_token, int32_t pos, int32_t n_s
   if (!ctx || !d_token || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
   if (ctx->executor != TD_EXEC_MEGAKERNEL) return fail(TD_E_UNSUPPORTED, "the step loop needs the megakernel executor");
   if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (((uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return fail(TD_E_INVALID_ARG, "K/V cache pointer not 16-byte aligned");
   if (n_steps < 1 || n_steps > TD_MAX_LOOP_STEPS) return fail(TD_E_INVALID_ARG, "n_steps outside [1, TD_MAX_LOOP_STEPS]");
   if (eos_id < -1 || eos_id >= ctx->cfg.vocab) return fail(TD_E_INVALID_ARG, "eos_id outside [-1, vocab)");
   if (pos < 0 || (int64_t)pos + n_steps > ctx->cfg.max_ctx) return fail(TD_E_RANGE, "positions outside [0, max_ctx)");
@@ -766,6 +768,7 @@ int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t po
                      float* d_logits_out, int32_t all_logits, int32_t* d_argmax_out, void* stream) {
   if (!ctx || !d_tokens || !kv || !kv->k || !kv->v || !d_logits_out) return fail(TD_E_INVALID_ARG, "null argument");
   if (kv->max_ctx != ctx->cfg.max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (((uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return fail(TD_E_INVALID_ARG, "K/V cache pointer not 16-byte aligned");
   if (n < 1 || n > TD_MAX_BLOCK) return fail(TD_E_INVALID_ARG, "n outside [1, TD_MAX_BLOCK]");
   if (ctx->cfg.n_experts > 0) return fail(TD_E_UNSUPPORTED, "the block forward runs dense MLPs only");
   if (pos0 < 0 || (int64_t)pos0 + n > ctx->cfg.max_ctx) return fail(TD_E_RANGE, "positions outside [0, max_ctx)");

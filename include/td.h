@@ -110,7 +110,8 @@ typedef struct td_weights {
     const td_layer_weights* layers;   /* host array of n_layers entries */
 } td_weights;
 
-/* Caller-owned K/V cache: bf16 [n_layers][n_kv_heads][max_ctx][head_dim] each. */
+/* Caller-owned K/V cache: bf16 [n_layers][n_kv_heads][max_ctx][head_dim] each, 16-byte
+ * aligned (the kernels move its rows in 16-byte pieces; TD_E_INVALID_ARG otherwise). */
 typedef struct td_kv {
     void* k;
     void* v;

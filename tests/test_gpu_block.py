@@ -232,6 +232,16 @@ def test_argument_checks(td):
     assert call(4, 0, lp=None) == _lib.TD_E_INVALID_ARG
     bad = _lib.TdKV(k=kvs.k, v=kvs.v, max_ctx=cfg.max_ctx - 1)
     assert call(4, 0, kvp=ctypes.byref(bad)) == _lib.TD_E_INVALID_ARG
+    # a K or V cache pointer that is not 16-byte aligned is refused on the host by
+    # every entry point that takes the cache (no kernel is launched)
+    for mk in (dict(k=kvs.k + 8, v=kvs.v), dict(k=kvs.k, v=kvs.v + 2)):
+        mis = _lib.TdKV(max_ctx=cfg.max_ctx, **mk)
+        assert call(4, 0, kvp=ctypes.byref(mis)) == _lib.TD_E_INVALID_ARG
+        assert L.td_decode_step(dec.handle, t.data_ptr(), 0, ctypes.byref(mis), logits.data_ptr(),
+                                None) == _lib.TD_E_INVALID_ARG
+        assert L.td_decode_loop(dec.handle, t.data_ptr(), 0, 2, -1, ctypes.byref(mis), logits.data_ptr(), None, None,
+                                None) == _lib.TD_E_INVALID_ARG
+        assert b"16-byte aligned" in L.td_last_error()
     assert call(4, cfg.max_ctx - 4) == _lib.TD_OK
     torch.cuda.synchronize()
     assert dec.status() == 0
