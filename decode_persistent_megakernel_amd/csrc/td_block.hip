@@ -422,9 +422,10 @@ __global__ void __launch_bounds__(256) blk_qkv_post(const float* part, int S, si
 // TD_MAX_GROUP) over keys 0 .. pos0 + i, which share every K and V row they
 // read.  The keys are cut into tiles of 64; wave w takes tiles w, w + 4, ...
 // and keeps, per query head, an online softmax (running max m, sum l and the
-// weighted V sum): lane t scores key t of the tile against every head, then
-// lane e accumulates output column e (and e + 64 when D = 128) over the
-// tile's keys.  The four waves' states are merged in wave order at the end
+// weighted V sum): lane t loads the K and V rows of key t of the tile together
+// (16-byte pieces), scores the key against every head and puts the V row into
+// the wave's LDS tile; then lane e accumulates output column e (and e + 64
+// when D = 128) over the tile's keys from that tile.  The four waves' states are merged in wave order at the end
 // (deterministic).  Keys past pos0 + i get probability 0 (their loads read
 // row pos0 + i instead).
 template <int D>
@@ -435,6 +436,8 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
   __shared__ __attribute__((aligned(16))) float ps[4][64][G];  // [wave][key][head]
   __shared__ float mst[4][G], lst[4][G];
   __shared__ float ost[4][G][D];
+  constexpr int VP = D + 8;  // V tile row pitch, bf16 (16-byte row writes without bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint16_t vs[4][64][VP];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int i = blockIdx.x, g = blockIdx.y, h0 = g * group;
   const int last = pos0 + i;
@@ -458,9 +461,12 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
     const int t0 = tile * 64, key = t0 + lane;
     const bool valid = key <= last;
     const uint16_t* kr = K + (size_t)min(key, last) * D;
-    u32x4 kw[D / 8];
+    const uint16_t* vr = Vv + (size_t)min(key, last) * D;
+    u32x4 kw[D / 8], vw[D / 8];
 #pragma unroll
     for (int e = 0; e < D / 8; ++e) kw[e] = *(const u32x4*)(kr + 8 * e);
+#pragma unroll
+    for (int e = 0; e < D / 8; ++e) vw[e] = *(const u32x4*)(vr + 8 * e);
     // the query rows are read from LDS where they are used, not kept in registers
     asm volatile("" ::: "memory");
     float s[G];
@@ -485,6 +491,8 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
       }
     }
 #pragma unroll
+    for (int e = 0; e < D / 8; ++e) *(u32x4*)&vs[wave][lane][8 * e] = vw[e];
+#pragma unroll
     for (int r = 0; r < G; ++r) {
       if (r < group) {
         const float sv = valid ? s[r] : -__builtin_inff();
@@ -498,14 +506,13 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
         ps[wave][lane][r] = p;
       }
     }
-    // (each wave reads only its own ps rows, written by itself above)
+    // (each wave reads only its own ps rows and V tile, written by itself above)
     const int nk = min(64, last + 1 - t0);
 #pragma unroll 8
     for (int t = 0; t < nk; ++t) {
-      const uint16_t* vr = Vv + (size_t)(t0 + t) * D + lane;
       float vv[C];
 #pragma unroll
-      for (int c = 0; c < C; ++c) vv[c] = bf16f(vr[64 * c]);
+      for (int c = 0; c < C; ++c) vv[c] = bf16f(vs[wave][t][lane + 64 * c]);
       const f32x4 pa = *(const f32x4*)&ps[wave][t][0], pb = *(const f32x4*)&ps[wave][t][4];
       const float pr[G] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
