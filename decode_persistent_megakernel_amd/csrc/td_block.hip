@@ -428,10 +428,14 @@ __global__ void __launch_bounds__(256) blk_qkv_post(const float* part, int S, si
 // when D = 128) over the tile's keys from that tile.  The four waves' states are merged in wave order at the end
 // (deterministic).  Keys past pos0 + i get probability 0 (their loads read
 // row pos0 + i instead).
-template <int D>
+template <int D, int GRP>
 __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* kc, const uint16_t* vc, int nq,
                                                 int group, int nkv, int max_ctx, int layer, int pos0, float* out) {
-  constexpr int G = TD_MAX_GROUP, C = D / 64;
+  // GRP: the group size compiled for (1, 2, 4 or 8), so the per-head loops
+  // carry no branches; 0 takes any group up to TD_MAX_GROUP with the run-time
+  // count ng
+  constexpr int G = GRP ? GRP : TD_MAX_GROUP, C = D / 64;
+  const int ng = GRP ? GRP : group;
   __shared__ __attribute__((aligned(16))) float qs[G][D];
   __shared__ __attribute__((aligned(16))) float ps[4][64][G];  // [wave][key][head]
   __shared__ float mst[4][G], lst[4][G];
@@ -443,7 +447,7 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
   const int last = pos0 + i;
   for (int e = threadIdx.x; e < G * D; e += 256) {
     const int r = e / D;
-    qs[r][e % D] = r < group ? q[((size_t)i * nq + h0 + r) * D + e % D] : 0.f;
+    qs[r][e % D] = r < ng ? q[((size_t)i * nq + h0 + r) * D + e % D] : 0.f;
   }
   __syncthreads();
   const uint16_t* K = kc + ((size_t)layer * nkv + g) * max_ctx * D;
@@ -473,7 +477,7 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
 #pragma unroll
     for (int r = 0; r < G; ++r) {
       s[r] = 0.f;
-      if (r < group) {
+      if (r < ng) {
         float a = 0.f;
 #pragma unroll
         for (int e = 0; e < D / 8; ++e) {
@@ -494,7 +498,7 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
     for (int e = 0; e < D / 8; ++e) *(u32x4*)&vs[wave][lane][8 * e] = vw[e];
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      if (r < group) {
+      if (r < ng) {
         const float sv = valid ? s[r] : -__builtin_inff();
         const float mn = fmaxf(m[r], wave_max(sv));
         const float p = valid ? expf(sv - mn) : 0.f;
@@ -513,11 +517,23 @@ __global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* 
       float vv[C];
 #pragma unroll
       for (int c = 0; c < C; ++c) vv[c] = bf16f(vs[wave][t][lane + 64 * c]);
-      const f32x4 pa = *(const f32x4*)&ps[wave][t][0], pb = *(const f32x4*)&ps[wave][t][4];
-      const float pr[G] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      float pr[G];
+      if constexpr (G % 4 == 0) {
+#pragma unroll
+        for (int r = 0; r < G; r += 4) {
+          const f32x4 pv = *(const f32x4*)&ps[wave][t][r];
+          pr[r] = pv.x;
+          pr[r + 1] = pv.y;
+          pr[r + 2] = pv.z;
+          pr[r + 3] = pv.w;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < G; ++r) pr[r] = ps[wave][t][r];
+      }
 #pragma unroll
       for (int r = 0; r < G; ++r)
-        if (r < group) {
+        if (r < ng) {
 #pragma unroll
           for (int c = 0; c < C; ++c) acc[r][c] = fmaf(pr[r], vv[c], acc[r][c]);
         }
@@ -662,6 +678,19 @@ int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t*
              : launch_gemm_f<TD_WF_BF16>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, dst, ldy, sstride, norm);
 }
 
+template <int D>
+void launch_attn(const td_kparams& P, const td_blockparams* B, int n, int l, int pos0, hipStream_t st) {
+  const dim3 grid(n, P.nkv);
+#define TD_ATTN(G_) \
+  blk_attn<D, G_><<<grid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0, B->ao)
+  if (P.group == 1) TD_ATTN(1);
+  else if (P.group == 2) TD_ATTN(2);
+  else if (P.group == 4) TD_ATTN(4);
+  else if (P.group == 8) TD_ATTN(8);
+  else TD_ATTN(0);
+#undef TD_ATTN
+}
+
 }  // namespace
 
 int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int pos0, int all_logits,
@@ -690,13 +719,7 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
     TD_CK((blk_qkv_post<<<dim3((P.qkv_rows / 2 + 255) / 256, n), 256, 0, st>>>(
         S == 1 ? B->y : part, S, (size_t)n * P.qkv_rows, P.qkv_rows, qd, P.kvd, d, P.nkv, P.max_ctx, l, pos0, Ld.bias,
         P.rope_cs, P.attn_scale, B->q, P.kc, P.vc)));
-    const dim3 agrid(n, P.nkv);
-    if (d == 64)
-      TD_CK((blk_attn<64><<<agrid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0,
-                                                 B->ao)));
-    else
-      TD_CK((blk_attn<128><<<agrid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0,
-                                                  B->ao)));
+    TD_CK(d == 64 ? launch_attn<64>(P, B, n, l, pos0, st) : launch_attn<128>(P, B, n, l, pos0, st));
     // the O and down projections always land in part (slice 0 when unsplit)
     if ((e = gemm(P.wf, ncu, B->ao, qd, n, qd, Ld.w[1], Ld.s[1], H, part, part, H, &S, st, no_norm))) return e;
     TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, Ld.mlp_norm, B->xg, B->ssq)));

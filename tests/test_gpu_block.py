@@ -111,6 +111,9 @@ def _compare(td, cfg, m, k, v, toks, pos0, label, kv_atol_rel=2 ** -12):
     _say(f"{label}: max|dlogit| = {worst:.3g}, min top-2 gap = {min_gap:.3g}")
 
 
+MHA1 = synth.shrink(SPLITK, name="mha_d64", n_q_heads=4, n_kv_heads=4, seed=2011)
+
+
 @pytest.mark.parametrize("cfg,pos0,n", [
     (SPLITK, 58, 20),        # positions 58..77 across the 63/64 edge, two 16-row tiles
     (SPLITK128, 100, 40),    # d = 128 + bias, three tiles (the last ragged), across 127/128
@@ -118,7 +121,8 @@ def _compare(td, cfg, m, k, v, toks, pos0, label, kv_atol_rel=2 ** -12):
     (MULTITILE, 2000, 64),   # the largest block over 2000 cached positions
     (SPLITK, 0, 1),          # a single row at position 0
     (SPLITK, 255 - 15, 16),  # ends at the last cache position
-], ids=["d64_edge", "d128_bias", "int4_ragged", "max_block", "single_row", "last_position"])
+    (MHA1, 70, 24),          # one query head per kv head (the attention's group-1 instance)
+], ids=["d64_edge", "d128_bias", "int4_ragged", "max_block", "single_row", "last_position", "group1"])
 def test_block_matches_oracle(td, cfg, pos0, n):
     m = synth.make_model(cfg)
     k, v = synth.random_kv_prefix(cfg, pos0, seed_tag="block")
