@@ -109,7 +109,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); the library runs on one GPU and has no multi-GPU path.",
               file=sys.stderr)
         return 2
 
