@@ -15,7 +15,8 @@ and with these seeded models no two candidates come within the fp32 error of
 each other, so the choices must be identical.
 
 Shapes: bf16 with 16 experts / top 4 and GQA; int4 with 8 / top 2; the OLMoE
-head layout (query heads = kv heads, d = 128) with 64 experts / top 8; and the
+head layout (query heads = kv heads, d = 128) with 64 experts / top 8; 10 / top 3,
+5 / top 1 and the largest, 256 / top 16; and the
 full OLMoE-1B-7B shape (16 layers, hidden 2048, 64 experts of 1024, top 8,
 vocab 50304) from a random K/V prefix of 512 positions.
 """
@@ -36,6 +37,15 @@ MOE_INT4 = synth.shrink(synth.CONFIGS["tinyllama_int4"], name="moe_int4", hidden
                         head_dim=64, intermediate=384, n_experts=8, top_k=2, seed=3002, **BASE)
 MOE_D128 = synth.shrink(synth.CONFIGS["olmoe"], name="moe_d128", hidden=256, n_q_heads=2, n_kv_heads=2,
                         head_dim=128, intermediate=128, n_experts=64, top_k=8, seed=3003, **BASE)
+# expert counts that are not a multiple of 4 (the padded tail of the staged router
+# logits), top-1, and the largest shapes the kernels take (TD_MAX_EXPERTS experts,
+# TD_MAX_TOPK chosen: two groups of eight rows in the down kernel)
+MOE_ODD = synth.shrink(synth.CONFIGS["llama1b"], name="moe_e10k3", hidden=256, n_q_heads=4, n_kv_heads=2,
+                       head_dim=64, intermediate=192, n_experts=10, top_k=3, seed=3004, **BASE)
+MOE_TOP1 = synth.shrink(synth.CONFIGS["llama1b"], name="moe_e5k1", hidden=256, n_q_heads=4, n_kv_heads=2,
+                        head_dim=64, intermediate=128, n_experts=5, top_k=1, seed=3005, **BASE)
+MOE_MAX = synth.shrink(synth.CONFIGS["llama1b"], name="moe_e256k16", hidden=256, n_q_heads=4, n_kv_heads=2,
+                       head_dim=64, intermediate=64, n_experts=256, top_k=16, seed=3006, **BASE)
 
 
 def _run(td, cfg, m, k, v, first, start, n, executor, label):
@@ -76,8 +86,9 @@ def _run(td, cfg, m, k, v, first, start, n, executor, label):
     return outs
 
 
-@pytest.mark.parametrize("cfg,start", [(MOE_BF16, 30), (MOE_INT4, 10), (MOE_D128, 60)],
-                         ids=["bf16_e16k4", "int4_e8k2", "d128_e64k8"])
+@pytest.mark.parametrize("cfg,start", [(MOE_BF16, 30), (MOE_INT4, 10), (MOE_D128, 60), (MOE_ODD, 20), (MOE_TOP1, 5),
+                                       (MOE_MAX, 40)],
+                         ids=["bf16_e16k4", "int4_e8k2", "d128_e64k8", "e10k3", "e5k1", "e256k16"])
 @pytest.mark.parametrize("executor", ["per_op", "graph"])
 def test_moe_matches_oracle(td, cfg, start, executor):
     ex = {"per_op": td.TD_EXEC_PER_OP, "graph": td.TD_EXEC_GRAPH}[executor]
