@@ -601,11 +601,12 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     // split-K slices: the O and down projections always write slices (one when unsplit), the
     // others only when split
     size_t part_floats = 0;
-    const int gem[5][3] = {{qkv_rows, H, 0}, {H, qd, 1}, {2 * I, H, 0}, {H, I, 1}, {V, H, 0}};
+    const int wf = c.weight_format;  // {rows, K, always sliced, format}: the logits GEMM is bf16
+    const int gem[5][4] = {{qkv_rows, H, 0, wf}, {H, qd, 1, wf}, {2 * I, H, 0, wf}, {H, I, 1, wf}, {V, H, 0, TD_WF_BF16}};
     for (const auto& g : gem)
       for (int tile_rows : {64, 128}) {  // the GEMM's tile height depends on the block's rows
         int KS = 0;
-        const int S = td_block_split(g[0], g[1], ncu, tile_rows, &KS);
+        const int S = td_block_split(g[0], g[1], ncu, tile_rows, g[3], &KS);
         if (S > 1 || g[2]) part_floats = std::max(part_floats, (size_t)S * R * g[0]);
       }
     size_t bo = 0;

@@ -670,7 +670,7 @@ int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t*
          float* Y, float* part, int ldy, int* S_out, hipStream_t st, const NormArgs& norm) {
   int KS = 0;
   const int NB = nb_of((M + 15) / 16, N, ncu);
-  const int S = td_block_split(N, K, ncu, 64 * NB, &KS);
+  const int S = td_block_split(N, K, ncu, 64 * NB, fmt, &KS);
   *S_out = S;
   float* dst = S == 1 ? Y : part;
   const size_t sstride = (size_t)M * ldy;

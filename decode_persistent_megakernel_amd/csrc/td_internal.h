@@ -217,14 +217,18 @@ struct td_blockparams {
 #define TD_BLOCK_ARGMAX_SLICES 64  // column slices of a logits row searched in parallel
 
 // Split-K plan of one block GEMM (N weight rows, K columns, tiles of
-// tile_rows weight rows): GEMMs with fewer tiles than two per CU cut K into S
-// slices of KS columns (a multiple of 64), as many as keep the grid within two
-// workgroups per CU (the most that are resident at once), so that every CU
-// runs two.  Returns S.
-static inline int td_block_split(int N, int K, int ncu, int tile_rows, int* KS) {
+// tile_rows weight rows, weight format fmt): GEMMs with fewer tiles than two
+// per CU cut K into S slices of KS columns (a multiple of 64), as many as keep
+// the grid within two workgroups per CU (the most that are resident at once),
+// but no more than leave every slice td_block_min_chunks(fmt) 64-column chunks:
+// a shorter slice spends its time filling and draining its pipeline (measured:
+// the 2048-column O projection took 14 us in 2-chunk slices, 10 us in 4).
+// Returns S.
+static inline int td_block_min_chunks(int fmt) { return fmt == TD_WF_INT4_G64 ? 6 : 4; }  // int4: 1/4 the bytes
+static inline int td_block_split(int N, int K, int ncu, int tile_rows, int fmt, int* KS) {
   const int tiles = (N + tile_rows - 1) / tile_rows, chunks = K / 64;
   int s = tiles >= 2 * ncu ? 1 : (2 * ncu) / tiles;
-  if (s > chunks) s = chunks;
+  if (s > chunks / td_block_min_chunks(fmt)) s = chunks / td_block_min_chunks(fmt);
   if (s < 1) s = 1;
   const int per = (chunks + s - 1) / s;
   *KS = per * 64;
