@@ -84,10 +84,23 @@ def cpu_baseline(model, cfg, pos0: int, budget_s: float):
         el = time.perf_counter() - t0
         if (n >= 2 and el >= budget_s) or pos0 + n >= cfg.max_ctx:
             break
+    # the same oracle on one thread, for two more steps: after the last position
+    # when the cache has room, else again at the first two (timing only)
+    o.nthreads = 1
+    p1 = pos0 + n if pos0 + n + 2 <= cfg.max_ctx else pos0
+    n1 = 0
+    t1 = time.perf_counter()
+    while n1 < 2 and p1 + n1 < cfg.max_ctx:
+        r, _ = o.step(t, p1 + n1)
+        t = r if r >= 0 else 0
+        n1 += 1
+    el1 = time.perf_counter() - t1
     return {"value": round(n / el, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n} decode steps of the same workload at positions {pos0}..{pos0 + n - 1}, "
                       f"fp64 scalar C oracle, {nthreads} OpenMP threads, K/V prefix random",
-            "ms_per_token": round(el / n * 1e3, 2)}
+            "ms_per_token": round(el / n * 1e3, 2),
+            "single_thread": ({"ms_per_token": round(el1 / n1 * 1e3, 2), "steps": n1,
+                               "positions": [p1, p1 + n1 - 1]} if n1 else None)}
 
 
 def main() -> int:
