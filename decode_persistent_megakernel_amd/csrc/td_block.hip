@@ -617,12 +617,19 @@ __global__ void __launch_bounds__(64) blk_argmax_final(const uint2* cand, int nb
   float bv = -__builtin_inff();
   uint32_t bi = TD_ARGMAX_NONE;
   bool bad = false;
-  for (int b = 0; b < nb; ++b) {
-    const uint2 c = cand[r * nb + b];
-    if (c.y == TD_ARGMAX_BAD) bad = true;
-    else if (c.y != TD_ARGMAX_NONE && (__uint_as_float(c.x) > bv || bi == TD_ARGMAX_NONE)) {
-      bv = __uint_as_float(c.x);
-      bi = c.y;
+  for (int b0 = 0; b0 < nb; b0 += 16) {  // 16 candidates loaded together, then taken in slice order
+    uint2 cs[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cs[u] = cand[r * nb + min(b0 + u, nb - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint2 c = cs[u];
+      if (b0 + u >= nb) continue;
+      if (c.y == TD_ARGMAX_BAD) bad = true;
+      else if (c.y != TD_ARGMAX_NONE && (__uint_as_float(c.x) > bv || bi == TD_ARGMAX_NONE)) {
+        bv = __uint_as_float(c.x);
+        bi = c.y;
+      }
     }
   }
   const int tok = (bad || bi == TD_ARGMAX_NONE) ? 0 : (int)bi;
