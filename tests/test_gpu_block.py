@@ -112,6 +112,7 @@ def _compare(td, cfg, m, k, v, toks, pos0, label, kv_atol_rel=2 ** -12):
 
 
 MHA1 = synth.shrink(SPLITK, name="mha_d64", n_q_heads=4, n_kv_heads=4, seed=2011)
+MHA1_LONG = synth.shrink(MHA1, name="mha_d64_long", max_ctx=2304, seed=2012)
 
 
 @pytest.mark.parametrize("cfg,pos0,n", [
@@ -122,7 +123,9 @@ MHA1 = synth.shrink(SPLITK, name="mha_d64", n_q_heads=4, n_kv_heads=4, seed=2011
     (SPLITK, 0, 1),          # a single row at position 0
     (SPLITK, 255 - 15, 16),  # ends at the last cache position
     (MHA1, 70, 24),          # one query head per kv head (the attention's group-1 instance)
-], ids=["d64_edge", "d128_bias", "int4_ragged", "max_block", "single_row", "last_position", "group1"])
+    (MHA1_LONG, 2100, 22),   # group 1 past 2048 cached keys (33 key tiles per token)
+], ids=["d64_edge", "d128_bias", "int4_ragged", "max_block", "single_row", "last_position", "group1",
+        "group1_long"])
 def test_block_matches_oracle(td, cfg, pos0, n):
     m = synth.make_model(cfg)
     k, v = synth.random_kv_prefix(cfg, pos0, seed_tag="block")
