@@ -119,18 +119,41 @@ DEV float dot_bf16(u32x4 w, const float* x) {
 }
 // 8 codes of one 32-bit word (element 2i in the low nibble of byte i) against
 // the 8 matching activations; weight = scale * (code - 8), the scale applied by
-// the caller.
+// the caller.  The unpack makes two codes at a time into half-precision values
+// without a conversion instruction: a code u placed in the low mantissa bits
+// of the half-precision number 1024 (bits 0x6400) gives exactly 1024 + u, and
+// one packed half-precision subtraction of 1032 leaves u - 8 exactly (the
+// exponent-bit trick of tinyinfer's "v0.1" section, here on a pair of 16-bit
+// halves).  Codes k and k + 4 of the word sit 16 bits apart, so one mask picks
+// both.  Each fused multiply-add then takes its half-precision operand as is
+// (v_fma_mix_f32: f32(u - 8) * x + s, one rounding).  Per word: 3 shifts, 4
+// and-or, 4 packed subtractions and 8 multiply-adds, 19 vector instructions for
+// 8 weights (2.4 per weight; a shift, a conversion, a subtraction and a
+// multiply-add per weight before).  The products are added in element order,
+// so the result is bit for bit the sum of fl((u_k - 8) x_k) in that order.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {  // (a & m) | c in one instruction
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
 DEV float dot_int4_word(uint32_t q, const float* x) {
   f32x4 a = *(const f32x4*)x;
   f32x4 b = *(const f32x4*)(x + 4);
-  float s = ((float)(q & 15u) - 8.f) * a.x;
-  s = fmaf((float)((q >> 4) & 15u) - 8.f, a.y, s);
-  s = fmaf((float)((q >> 8) & 15u) - 8.f, a.z, s);
-  s = fmaf((float)((q >> 12) & 15u) - 8.f, a.w, s);
-  s = fmaf((float)((q >> 16) & 15u) - 8.f, b.x, s);
-  s = fmaf((float)((q >> 20) & 15u) - 8.f, b.y, s);
-  s = fmaf((float)((q >> 24) & 15u) - 8.f, b.z, s);
-  s = fmaf((float)(q >> 28) - 8.f, b.w, s);
+  const uint32_t m = 0x000F000Fu, bias = 0x64006400u;
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 p0 = __builtin_bit_cast(f16x2, and_or(q, m, bias)) - off;        // codes 0, 4
+  const f16x2 p1 = __builtin_bit_cast(f16x2, and_or(q >> 4, m, bias)) - off;   // codes 1, 5
+  const f16x2 p2 = __builtin_bit_cast(f16x2, and_or(q >> 8, m, bias)) - off;   // codes 2, 6
+  const f16x2 p3 = __builtin_bit_cast(f16x2, and_or(q >> 12, m, bias)) - off;  // codes 3, 7
+  float s = (float)p0.x * a.x;
+  s = fmaf((float)p1.x, a.y, s);
+  s = fmaf((float)p2.x, a.z, s);
+  s = fmaf((float)p3.x, a.w, s);
+  s = fmaf((float)p0.y, b.x, s);
+  s = fmaf((float)p1.y, b.y, s);
+  s = fmaf((float)p2.y, b.z, s);
+  s = fmaf((float)p3.y, b.w, s);
   return s;
 }
 // int4 chunk (2048 elements of a row): lane l holds four 8-code words, word w

@@ -184,9 +184,18 @@ DEV void lds_st(uint32_t* p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::
 DEV void lds_add(uint32_t* p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory"); }
 DEV void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// A wait that began at t0 (100 MHz clock) gives up once another wait has set
+// the abort word or after TD_SPIN_TICKS.  The abort word is read only once the
+// wait has lasted TD_ABORT_CHECK_TICKS: a hand-off normally completes in a few
+// microseconds, and the read is a load the compiler tracks, whose wait (behind
+// every weight chunk in flight) would otherwise stall each poll round that
+// checks it.
+#define TD_ABORT_CHECK_TICKS 10000ull  // 100 us
 DEV bool wait_expired(const td_kparams& P, uint64_t t0) {
+  const uint64_t el = wall_clock64() - t0;
+  if (el < TD_ABORT_CHECK_TICKS) return false;
   if (ld_u(P.sync + TD_SY_ABORT)) return true;
-  if (wall_clock64() - t0 > TD_SPIN_TICKS) {
+  if (el > TD_SPIN_TICKS) {
     st_u(P.sync + TD_SY_ABORT, 1u);
     return true;
   }
@@ -221,6 +230,33 @@ DEV uint32_t lds_wait_ge(const td_kparams& P, const uint32_t* p, uint32_t target
 
 DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+// Loads whose completion the compiler does not track.  The compiler waits for
+// a tracked load before its result is used, and when LDS-DMA chunks of a
+// run-time count were issued after the load it can only wait for all of them
+// (vmcnt(0)), which would hold every hand-off poll and every prefetched operand
+// until the weight ring's newest chunks land.  With these, the kernel waits
+// itself (vmcnt of exactly the loads issued after) and then fences the
+// registers (reg_fence) so that no use is scheduled above that wait.
+DEV u32x4 ld16_sc1_untracked(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+DEV uint32_t ld4_untracked(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+DEV uint32_t ld2_untracked(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+template <class T>
+DEV void reg_fence(T& v) {
+  asm volatile("" : "+v"(v));
 }
 
 DEV void st_tag(uint2* p, float v, uint32_t tag) {
@@ -342,6 +378,8 @@ struct CState {
   uint8_t* sring;
   const uint8_t* fbase;  // the next chunk to issue (wave-uniform; a lane loads its 16 bytes)
   const uint8_t* sbase;  // the next int4 chunk's 64-byte scale block
+  const uint8_t* fbase0;  // the stream's first chunk and first scale block
+  const uint8_t* sbase0;
   uint32_t issued, n_tot, n4;  // chunks issued, stream length, leading int4 chunks
   uint32_t lk;                 // chunks [0, lk) are known to be in LDS
   int islot;                   // ring slot of the next chunk to issue
@@ -465,8 +503,11 @@ template <int W, bool TOPUP = true>
 DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CState& C) {
   const int lane = lane_id();
   const int nu = (hi - lo) >> 1;
-  if (nu <= 0) return true;
-  const __amdgpu_buffer_rsrc_t R = rsrc(src + lo, (uint32_t)nu * 16u);
+  if (nu <= 0) {
+    vm_drain();  // the operands prefetched ahead of the poll have landed
+    return true;
+  }
+  const uint8_t* base = (const uint8_t*)(src + lo);
   float* d = dst + lo;
   const uint64_t t0 = wall_clock64();
   for (int b0 = 0; b0 < nu; b0 += W * 64) {
@@ -478,9 +519,15 @@ DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint3
       const uint32_t landed_before = C.issued;
       u32x4 r[W];
 #pragma unroll
-      for (int k = 0; k < W; ++k)
-        r[k] = __builtin_amdgcn_raw_buffer_load_b128(R, (uint32_t)(b0 + k * 64 + lane) * 16u, 0, TD_CPOL_SC1);
+      for (int k = 0; k < W; ++k)  // past the slice: its last unit again (ignored)
+        r[k] = ld16_sc1_untracked(base + (size_t)min(b0 + k * 64 + lane, nu - 1) * 16u);
       if (TOPUP) topup(P, C);
+      // only the top-up's loads may still be outstanding: the poll's, and every
+      // load issued before the round, are complete
+      vmcnt_rt(ops_of(C, landed_before, C.issued));
+#pragma unroll
+      for (int k = 0; k < W; ++k) reg_fence(r[k]);
+      if (C.lk < landed_before) C.lk = landed_before;
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         if (((pend >> k) & 1u) && r[k].y == tag && r[k].w == tag) {
@@ -490,10 +537,6 @@ DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint3
           pend &= ~(1u << k);
         }
       }
-      // only the top-up's loads may still be outstanding: the poll's, and every
-      // chunk issued before the round, are complete
-      vmcnt_rt(ops_of(C, landed_before, C.issued));
-      if (C.lk < landed_before) C.lk = landed_before;
       if (!__any(pend != 0u)) break;
       if ((it & 3u) == 3u && uni(wait_expired(P, t0) ? 1 : 0)) return false;
     }
@@ -563,9 +606,14 @@ DEV void stage_gemv_input(const td_kparams& P, CState& C, int wave, int kind, in
       C.xin[2 * u] = bf_lo(e);
       C.xin[2 * u + 1] = bf_hi(e);
     }
+    vm_drain();  // the gains and biases loaded ahead (no input poll waits for them here)
   } else {
     C.ok &= poll_pairs<8>(P, src, lo, hi, tag, C.xin, C);
   }
+  reg_fence(g0);
+  reg_fence(g1);
+  reg_fence(g2);
+  reg_fence(g3);
   if (gain) {
     lds_fence();
     const float ss = slice_ssq(C.xin, lo, hi);
@@ -767,10 +815,9 @@ DEV void trace_rec(const td_kparams& P, int wave, int seq, uint64_t t0, uint64_t
 }
 
 // The wave's stream from its first chunk (ring slots and their order carry on).
-DEV void stream_start(const td_kparams& P, CState& C, int w) {
-  const td_wstream W = P.ws[w];
-  C.fbase = P.wcode + (size_t)W.code_off * TD_CHUNK;
-  C.sbase = P.wscale + (size_t)W.scale_off * TD_SCHUNK;
+DEV void stream_start(CState& C) {
+  C.fbase = C.fbase0;
+  C.sbase = C.sbase0;
   C.issued = C.t = C.lk = 0;
 }
 
@@ -810,9 +857,14 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   C.out = (float*)(lds + P.off_out);
   C.ring = lds + P.off_ring + wave * P.ring_slots * TD_CHUNK;
   C.sring = lds + P.off_sring + wave * P.ring_slots * TD_SCHUNK;
-  stream_start(P, C, cu * TD_NW + wave);
-  C.n_tot = P.ws[cu * TD_NW + wave].n_tot;
-  C.n4 = WF == TD_WF_BF16 ? 0u : P.ws[cu * TD_NW + wave].n4;  // a constant 0 for bf16 models
+  {
+    const td_wstream W = P.ws[cu * TD_NW + wave];
+    C.fbase0 = P.wcode + (size_t)W.code_off * TD_CHUNK;
+    C.sbase0 = P.wscale + (size_t)W.scale_off * TD_SCHUNK;
+    C.n_tot = W.n_tot;
+    C.n4 = WF == TD_WF_BF16 ? 0u : W.n4;  // a constant 0 for bf16 models
+  }
+  stream_start(C);
   C.islot = C.slot = 0;
   C.nrv = 0;
   C.ok = true;
@@ -859,19 +911,19 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
         int lo, hi;
         td_slice(P.H, wave, &lo, &hi);
         const int u = (lo >> 1) + lane;
-        if (u < (hi >> 1)) g0 = *(const uint32_t*)(gain + 2 * u);
-        if (u + 64 < (hi >> 1)) g1 = *(const uint32_t*)(gain + 2 * (u + 64));
-        if (u + 128 < (hi >> 1)) g2 = *(const uint32_t*)(gain + 2 * (u + 128));
-        if (u + 192 < (hi >> 1)) g3 = *(const uint32_t*)(gain + 2 * (u + 192));
+        if (u < (hi >> 1)) g0 = ld4_untracked(gain + 2 * u);
+        if (u + 64 < (hi >> 1)) g1 = ld4_untracked(gain + 2 * (u + 64));
+        if (u + 128 < (hi >> 1)) g2 = ld4_untracked(gain + 2 * (u + 128));
+        if (u + 192 < (hi >> 1)) g3 = ld4_untracked(gain + 2 * (u + 192));
       }
-      float bias_a = 0.f, bias_b = 0.f;
+      uint32_t bias_a = 0u, bias_b = 0u;  // bf16 bits
       if (kind == TD_ST_QKV && P.has_bias) {
         const int u0 = C.unit_lo(TD_SP_QKV);
         if (lane < wave_units(C.unit_n(TD_SP_QKV), wave)) {
           const uint16_t* bl = P.biases + (size_t)layer * P.qkv_rows;
           const int ra = unit_row(P, TD_ST_QKV, u0 + wave + lane * TD_NW, 0);
-          bias_a = bf16f(bl[ra]);
-          bias_b = bf16f(bl[ra + (P.d >> 1)]);
+          bias_a = ld2_untracked(bl + ra);
+          bias_b = ld2_untracked(bl + ra + (P.d >> 1));
         }
       }
       if (!first_stage) rendezvous(P, C);  // every wave is done reading the previous stage's inputs
@@ -895,6 +947,8 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
                          : kind == TD_ST_GU ? P.tx_mid : P.tx_out;
         stage_gemv_input(P, C, wave, kind, K, src, kind == TD_ST_QKV && layer == 0 ? erow : nullptr, tag_in, g0, g1,
                          g2, g3, gain);
+        reg_fence(bias_a);  // landed: loaded ahead of the input poll, whose wait covers them
+        reg_fence(bias_b);
         rendezvous(P, C);
         if (P.trace) ts1 = wall_clock64();
         float inv = 1.0f;
@@ -914,14 +968,14 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
           ss += __uint_as_float(b.w);
           inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
         }
-        gemv_wave<WF>(P, C, wave, kind, layer, pos, tag, inv, bias_a, bias_b, ts2);
+        gemv_wave<WF>(P, C, wave, kind, layer, pos, tag, inv, bf16f((uint16_t)bias_a), bf16f((uint16_t)bias_b), ts2);
       }
       if (P.trace) trace_rec(P, wave, seq, ts0, ts1, ts2, wall_clock64());
     }
     // the step's stream is consumed (every chunk issued has been read): the
     // next step's starts over and streams while the sync wave decides the
     // token (and whether another step follows)
-    if (step + 1 < P.n_steps) stream_start(P, C, cu * TD_NW + wave);
+    if (step + 1 < P.n_steps) stream_start(C);
     (void)lds_wait_ge_topup(P, C, C.ctl + TD_CTL_TOKREADY, (uint32_t)step + 1u);
     if (!C.ok || uni((int)lds_ld(C.ctl + TD_CTL_STOP))) break;
     tok = (int)uni((int)lds_ld(C.ctl + TD_CTL_TOKEN));
