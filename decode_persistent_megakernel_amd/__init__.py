@@ -212,9 +212,22 @@ def gemv(fmt: int, w, s, rows: int, cols: int, x, y, stream=None) -> None:
                "td_test_gemv")
 
 
-def attention(q, k, v, n_pos: int, head_dim: int, out, stream=None) -> None:
-    _lib.check(_lib.lib().td_test_attention(_ptr(q), _ptr(k), _ptr(v), n_pos, head_dim, _ptr(out),
+def attention(q, k, v, n_pos: int, head_dim: int, out, chunk_len: int = 0, stream=None) -> None:
+    """One query head over n_pos K/V rows through the step's tile and merge routines (test hook)."""
+    _lib.check(_lib.lib().td_test_attention(_ptr(q), _ptr(k), _ptr(v), n_pos, head_dim, int(chunk_len), _ptr(out),
                                             _stream_handle(stream)), "td_test_attention")
+
+
+def rope(x, n_heads: int, head_dim: int, pos: int, theta: float, out, stream=None) -> None:
+    """Half-split RoPE at one position through the step's rotation (test hook)."""
+    _lib.check(_lib.lib().td_test_rope(_ptr(x), n_heads, head_dim, int(pos), float(theta), _ptr(out),
+                                       _stream_handle(stream)), "td_test_rope")
+
+
+def argmax(logits, n: int, groups: int, work, token, nonfinite, stream=None) -> None:
+    """The step's greedy selection over n logits in `groups` workgroups (test hook)."""
+    _lib.check(_lib.lib().td_test_argmax(_ptr(logits), n, groups, _ptr(work), _ptr(token), _ptr(nonfinite),
+                                         _stream_handle(stream)), "td_test_argmax")
 
 
 _hip = None

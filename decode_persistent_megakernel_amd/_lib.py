@@ -31,7 +31,8 @@ TD_MAX_TOPK = 16
 
 EXPORTED = [
     "td_create", "td_decode_step", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_expert_ids", "td_expert_weights", "td_status", "td_destroy", "td_strerror", "td_last_error",
-    "td_test_gemv", "td_test_attention", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
+    "td_plan_partition", "td_plan_check",
+    "td_test_gemv", "td_test_attention", "td_test_rope", "td_test_argmax", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
 ]
 
 
@@ -98,10 +99,18 @@ def lib() -> ctypes.CDLL:
         L.td_strerror.argtypes = [i32]
         L.td_last_error.restype = ctypes.c_char_p
         L.td_last_error.argtypes = []
+        L.td_plan_partition.restype = i32
+        L.td_plan_partition.argtypes = [ctypes.POINTER(TdConfig), i32, vp, i32]
+        L.td_plan_check.restype = i32
+        L.td_plan_check.argtypes = [ctypes.POINTER(TdConfig), i32, vp, i32]
         L.td_test_gemv.restype = i32
         L.td_test_gemv.argtypes = [i32, vp, vp, i32, i32, vp, vp, vp]
         L.td_test_attention.restype = i32
-        L.td_test_attention.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+        L.td_test_attention.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+        L.td_test_rope.restype = i32
+        L.td_test_rope.argtypes = [vp, i32, i32, i32, f32, vp, vp]
+        L.td_test_argmax.restype = i32
+        L.td_test_argmax.argtypes = [vp, i32, i32, vp, vp, vp, vp]
         L.td_set_timing.restype = i32
         L.td_set_timing.argtypes = [vp, i32]
         L.td_last_step_ms.restype = f32

@@ -72,6 +72,17 @@ struct td_ctx {
 
 namespace {
 
+// One position's RoPE table row: pair i (i < d/2) turns by the angle
+// pos * theta^(-2i/d); the angle, its cosine and its sine are computed in
+// double and rounded to fp32 (cs[2 i] = cos, cs[2 i + 1] = sin).
+void rope_row(float theta, int d, int pos, float* cs) {
+  for (int i = 0; i < d / 2; ++i) {
+    const double ang = (double)pos * std::pow((double)theta, -2.0 * i / d);
+    cs[2 * i] = (float)std::cos(ang);
+    cs[2 * i + 1] = (float)std::sin(ang);
+  }
+}
+
 // Builds the partition table: CU c owns units [part[s][c], part[s][c + 1]) of
 // unit space s, in proportion to the per-CU weights (all 1 unless a weighting
 // is given), so that every unit has exactly one owner.
@@ -284,60 +295,34 @@ int capture_graph(td_ctx* ctx) {
   return TD_OK;
 }
 
-}  // namespace
+// The static plan of the persistent kernel for a device of ncu CUs with
+// lds_cap bytes of LDS per CU: the attention split, the partition of every
+// GEMV stage's units over the CUs (part_in: a caller's table to validate
+// instead, TD_NSPACES x (ncu + 1) entries), the LDS layout with the ring
+// depth, and every compute wave's packed stream.  Host arithmetic only: no
+// device call, so the plan and its validation can be tested without a GPU.
+struct Plan {
+  td_kparams kp{};
+  int chunk_len = 0, n_chunks_max = 0;
+  std::vector<int32_t> part;
+  std::vector<td_wstream> ws;
+  uint64_t stream_code_chunks = 0, stream_scale_blocks = 0;
+};
 
-extern "C" {
-
-const char* td_strerror(int code) {
-  switch (code) {
-    case TD_OK: return "ok";
-    case TD_E_INVALID_ARG: return "invalid argument";
-    case TD_E_UNSUPPORTED: return "unsupported device or config";
-    case TD_E_PLAN: return "work plan failed validation";
-    case TD_E_RANGE: return "position or token id out of range";
-    case TD_E_HIP: return "HIP runtime error";
-    case TD_E_NONFINITE: return "non-finite logit";
-    case TD_E_NOMEM: return "device allocation failed";
-    case TD_E_TIMEOUT: return "grid-wide wait timed out";
-    default: return "unknown error";
-  }
-}
-
-const char* td_last_error(void) { return g_last_error.c_str(); }
-
-int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ctx** out) {
-  if (!out) return fail(TD_E_INVALID_ARG, "null out pointer");
-  *out = nullptr;
+int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* part_in, Plan& out) {
   int rc = check_config(cfg);
   if (rc) return rc;
-  rc = check_weights(cfg, w);
-  if (rc) return rc;
-  if (executor != TD_EXEC_MEGAKERNEL && executor != TD_EXEC_PER_OP && executor != TD_EXEC_GRAPH)
-    return fail(TD_E_INVALID_ARG, "unknown executor");
-  if (cfg->n_experts > 0 && executor == TD_EXEC_MEGAKERNEL)
-    return fail(TD_E_UNSUPPORTED, "a mixture-of-experts config runs on the per-op or graph executor");
-
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  hipDeviceProp_t prop;
-  e = hipGetDeviceProperties(&prop, dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(TD_E_UNSUPPORTED, std::string("needs gfx950, found ") + prop.gcnArchName);
-  const int ncu = prop.multiProcessorCount;
   if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
-  if (!prop.cooperativeLaunch) return fail(TD_E_UNSUPPORTED, "device lacks cooperative launch");
-
   const td_config& c = *cfg;
-  const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab, L = c.n_layers;
+  const int d = c.head_dim, H = c.hidden, I = c.intermediate, L = c.n_layers;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
-  const int qd = nq * d, kvd = nkv * d, qkv_rows = qd + 2 * kvd;
+  const int qd = nq * d;
 
   // attention split: at most one task per CU, chunks a multiple of the tile,
   // at most 64 chunks per kv head, and the merge staging within the LDS the
   // GEMV input area already takes (the attention area aliases it), at least
   // 24 KiB: more chunks mean fewer tiles per CU, which a CU runs one by one
+  if (nkv > ncu) return fail(TD_E_UNSUPPORTED, "more kv heads than CUs: the attention split needs a CU per kv head");
   const int cmax_by_cu = ncu / nkv;
   int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
   auto n_chunks_of = [&](int cl) { return (c.max_ctx + cl - 1) / cl; };
@@ -349,9 +334,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const int n_chunks_max = n_chunks_of(chunk_len);
   if (n_chunks_max * nkv > ncu) return fail(TD_E_PLAN, "attention split exceeds the CU count");
 
-  // partition of every GEMV stage's units over the CUs
-  const std::vector<double> cu_weight(ncu, 1.0);
-  const std::vector<int32_t> part = build_partition(c, ncu, cu_weight);
+  // partition of every GEMV stage's units over the CUs (or the caller's, for the plan test)
+  std::vector<int32_t> part = build_partition(c, ncu, std::vector<double>(ncu, 1.0));
+  if (part_in) part.assign(part_in, part_in + part.size());
   int own_floats = 0;
   for (int i = 0; i < ncu; ++i)
     own_floats = std::max(own_floats, part[(size_t)TD_SP_H * (ncu + 1) + i + 1] - part[(size_t)TD_SP_H * (ncu + 1) + i]);
@@ -368,7 +353,6 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
   const int64_t kpad = round_up(std::max({H, qd, I}), 2048);
   const int64_t xin_bytes = std::max<int64_t>(kpad * 4, A.bytes);
-  const int64_t lds_cap = std::min<int64_t>((int64_t)prop.maxSharedMemoryPerMultiProcessor, 160 * 1024);
   td_kparams kp{};
   int64_t fixed = 0;
   const int64_t per_slot = (int64_t)TD_NW * (TD_CHUNK + (c.weight_format == TD_WF_INT4_G64 ? TD_SCHUNK : 0));
@@ -416,11 +400,6 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   if (kp.lds_bytes > lds_cap) return fail(TD_E_UNSUPPORTED, "LDS layout exceeds the CU's LDS");
   // the greedy candidates of all CUs are gathered in the attention tile area
   if ((int64_t)ncu * 16 > td_tile_bytes(d)) return fail(TD_E_UNSUPPORTED, "too many CUs for the candidate area");
-  {
-    int blocks = 0;
-    const int oe = td_megakernel_occupancy(d, c.weight_format, kp.lds_bytes, &blocks);
-    if (oe != 0 || blocks < 1) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
-  }
   kp.ring_slots = (int32_t)ring;
 
 
@@ -466,6 +445,80 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     stream_scale_blocks = scal;
   }
 
+  out.kp = kp;
+  out.chunk_len = chunk_len;
+  out.n_chunks_max = n_chunks_max;
+  out.part = part;
+  out.ws = ws;
+  out.stream_code_chunks = stream_code_chunks;
+  out.stream_scale_blocks = stream_scale_blocks;
+  return TD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* td_strerror(int code) {
+  switch (code) {
+    case TD_OK: return "ok";
+    case TD_E_INVALID_ARG: return "invalid argument";
+    case TD_E_UNSUPPORTED: return "unsupported device or config";
+    case TD_E_PLAN: return "work plan failed validation";
+    case TD_E_RANGE: return "position or token id out of range";
+    case TD_E_HIP: return "HIP runtime error";
+    case TD_E_NONFINITE: return "non-finite logit";
+    case TD_E_NOMEM: return "device allocation failed";
+    case TD_E_TIMEOUT: return "grid-wide wait timed out";
+    default: return "unknown error";
+  }
+}
+
+const char* td_last_error(void) { return g_last_error.c_str(); }
+
+int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ctx** out) {
+  if (!out) return fail(TD_E_INVALID_ARG, "null out pointer");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  rc = check_weights(cfg, w);
+  if (rc) return rc;
+  if (executor != TD_EXEC_MEGAKERNEL && executor != TD_EXEC_PER_OP && executor != TD_EXEC_GRAPH)
+    return fail(TD_E_INVALID_ARG, "unknown executor");
+  if (cfg->n_experts > 0 && executor == TD_EXEC_MEGAKERNEL)
+    return fail(TD_E_UNSUPPORTED, "a mixture-of-experts config runs on the per-op or graph executor");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(TD_E_UNSUPPORTED, std::string("needs gfx950, found ") + prop.gcnArchName);
+  const int ncu = prop.multiProcessorCount;
+  if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
+  if (!prop.cooperativeLaunch) return fail(TD_E_UNSUPPORTED, "device lacks cooperative launch");
+
+  Plan plan;
+  rc = build_plan(cfg, ncu, std::min<int64_t>((int64_t)prop.maxSharedMemoryPerMultiProcessor, 160 * 1024), nullptr,
+                  plan);
+  if (rc) return rc;
+  td_kparams kp = plan.kp;
+  {
+    int blocks = 0;
+    const int oe = td_megakernel_occupancy(cfg->head_dim, cfg->weight_format, kp.lds_bytes, &blocks);
+    if (oe != 0 || blocks < 1) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
+  }
+  const td_config& c = *cfg;
+  const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab, L = c.n_layers;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
+  const int qd = nq * d, kvd = nkv * d, qkv_rows = qd + 2 * kvd;
+  const int chunk_len = plan.chunk_len, n_chunks_max = plan.n_chunks_max;
+  const std::vector<int32_t>& part = plan.part;
+  const std::vector<td_wstream>& ws = plan.ws;
+  const uint64_t stream_code_chunks = plan.stream_code_chunks, stream_scale_blocks = plan.stream_scale_blocks;
+  (void)V;
   td_ctx* ctx = new (std::nothrow) td_ctx();
   if (!ctx) return fail(TD_E_NOMEM, "host allocation failed");
   ctx->cfg = c;
@@ -509,14 +562,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
     return hip_fail(e, "hipMemset");
   }
 
-  // RoPE table: angle pos * theta^(-2i/d) and its cos/sin in double, stored as fp32
+  // RoPE table: one row per position
   std::vector<float> rope((size_t)c.max_ctx * (d / 2) * 2);
-  for (int p = 0; p < c.max_ctx; ++p)
-    for (int i = 0; i < d / 2; ++i) {
-      double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / d);
-      rope[((size_t)p * (d / 2) + i) * 2 + 0] = (float)std::cos(ang);
-      rope[((size_t)p * (d / 2) + i) * 2 + 1] = (float)std::sin(ang);
-    }
+  for (int p = 0; p < c.max_ctx; ++p) rope_row(c.rope_theta, d, p, rope.data() + (size_t)p * d);
   std::vector<td_layer_dev> layers(L);
   for (int l = 0; l < L; ++l) {
     const td_layer_weights& Lw = w->layers[l];
@@ -858,9 +906,49 @@ int td_set_trace(td_ctx* ctx, void* d_buf, int64_t bytes) {
   return TD_OK;
 }
 
+int td_plan_partition(const td_config* cfg, int32_t ncu, int32_t* part_out, int32_t part_len) {
+  if (!cfg || !part_out) return fail(TD_E_INVALID_ARG, "null argument");
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
+  if (part_len != TD_NSPACES * (ncu + 1)) return fail(TD_E_INVALID_ARG, "part_len must be 4 (ncu + 1)");
+  const std::vector<int32_t> part = build_partition(*cfg, ncu, std::vector<double>(ncu, 1.0));
+  std::copy(part.begin(), part.end(), part_out);
+  return TD_OK;
+}
+
+int td_plan_check(const td_config* cfg, int32_t ncu, const int32_t* part, int32_t part_len) {
+  if (!cfg) return fail(TD_E_INVALID_ARG, "null config");
+  if (part && part_len != TD_NSPACES * (ncu + 1)) return fail(TD_E_INVALID_ARG, "part_len must be 4 (ncu + 1)");
+  Plan plan;
+  return build_plan(cfg, ncu, 160 * 1024, part, plan);
+}
+
+int td_test_rope(const float* d_x, int32_t n_heads, int32_t head_dim, int32_t pos, float rope_theta, float* d_out,
+                 void* stream) {
+  if (!d_x || !d_out || n_heads <= 0 || (head_dim != 64 && head_dim != 128) || pos < 0 || !(rope_theta > 0.f))
+    return fail(TD_E_INVALID_ARG, "bad rope arguments");
+  td_rope_row row{};
+  rope_row(rope_theta, head_dim, pos, row.cs);
+  int le = td_launch_test_rope(d_x, n_heads, head_dim, row, d_out, stream);
+  if (le) return hip_fail((hipError_t)le, "rope launch");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");
+}
+
+int td_test_argmax(const float* d_logits, int32_t n, int32_t groups, void* d_work, int32_t* d_token,
+                   int32_t* d_nonfinite, void* stream) {
+  if (!d_logits || !d_work || !d_token || !d_nonfinite || n <= 0 || groups <= 0 || groups > n)
+    return fail(TD_E_INVALID_ARG, "bad argmax arguments");
+  int le = td_launch_test_argmax(d_logits, n, groups, d_work, d_token, d_nonfinite, stream);
+  if (le) return hip_fail((hipError_t)le, "argmax launch");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");
+}
+
 int td_test_gemv(int32_t fmt, const void* w, const void* scales, int32_t rows, int32_t cols, const float* d_x,
                  float* d_y, void* stream) {
-  if (!w || !d_x || !d_y || rows <= 0 || cols <= 0) return fail(TD_E_INVALID_ARG, "bad gemv arguments");
+  if (!w || !d_x || !d_y || rows <= 0 || cols <= 0 || cols > 32768) return fail(TD_E_INVALID_ARG, "bad gemv arguments");
   if (fmt == TD_WF_BF16) {
     if (cols % 8) return fail(TD_E_INVALID_ARG, "bf16 cols must be a multiple of 8");
   } else if (fmt == TD_WF_INT4_G64) {
@@ -874,14 +962,19 @@ int td_test_gemv(int32_t fmt, const void* w, const void* scales, int32_t rows, i
   return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");
 }
 
-int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim, float* d_out,
-                      void* stream) {
+int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim,
+                      int32_t chunk_len, float* d_out, void* stream) {
   if (!d_q || !k || !v || !d_out || n_pos <= 0 || (head_dim != 64 && head_dim != 128))
     return fail(TD_E_INVALID_ARG, "bad attention arguments");
-  int le = td_launch_test_attention(d_q, k, v, n_pos, head_dim, d_out, stream);
+  if (chunk_len == 0) chunk_len = (int32_t)round_up(n_pos, TD_TILE);
+  if (chunk_len < 0 || chunk_len % TD_TILE) return fail(TD_E_INVALID_ARG, "chunk_len must be a multiple of 64");
+  if ((n_pos + chunk_len - 1) / chunk_len > 64) return fail(TD_E_INVALID_ARG, "more than 64 chunks");
+  const float scale = (float)(1.0 / std::sqrt((double)head_dim));  // the decode kernel's attention scale
+  int le = td_launch_test_attention(d_q, k, v, n_pos, head_dim, chunk_len, scale, d_out, stream);
   if (le) return hip_fail((hipError_t)le, "attention launch");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");
 }
+
 
 }  // extern "C"

@@ -101,6 +101,29 @@ DEV float norm_inv(const float* ssq, int H, float eps) {
   return 1.0f / sqrtf(s / (float)H + eps);
 }
 
+// ------------------------------------------------------------ RoPE and greedy candidates
+// Half-split rotary embedding of one pair (x_i, x_{i + d/2}) by the angle whose
+// cosine and sine are c and sn (fp32, from the host-built table): the flint
+// page's chat.py passage, out_i = x_i cos - x_{i + d/2} sin and
+// out_{i + d/2} = x_{i + d/2} cos + x_i sin; products and sums rounded apart.
+DEV void rope_pair(float& a, float& b, float c, float sn) {
+  const float a2 = a * c - b * sn;
+  const float b2 = b * c + a * sn;
+  a = a2;
+  b = b2;
+}
+// Greedy candidates ("Decoding in tiles", sec. 5: the largest logit, the lowest
+// id among equal ones): (v, i) replaces (bv, bi) when it is better.
+DEV bool cand_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+// The best candidate of the wave, on every lane.
+DEV void cand_wave_max(float& bv, int& bi) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (cand_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+}
+
 // ------------------------------------------------------------ chunk arithmetic
 // bf16 chunk: lane holds 8 consecutive weights of the row, x holds the 8
 // matching activations.
@@ -185,6 +208,16 @@ DEV u32x4 int4_words(const uint8_t* row, int row_bytes, int j, int lane) {
   }
   return (u32x4){wd[0], wd[1], wd[2], wd[3]};
 }
+// The packed stream keeps an int4 chunk's 32 scales in a 64-byte block ordered
+// for the consumer: position p (0..31) holds the scale of word p & 3 of lanes
+// 8 (p >> 2) .. 8 (p >> 2) + 7, so a lane's four scales are 8 consecutive bytes.
+// int4_block_scale is the packing side (one position), int4_lane_scales the
+// consuming side (word 0 | word 1 << 16, word 2 | word 3 << 16).
+DEV uint16_t int4_block_scale(const uint16_t* srow, int ngroups, int j, int p) {
+  const int g = j * 32 + int4_word_group(p & 3, (p >> 2) * 8);
+  return g < ngroups ? srow[g] : (uint16_t)0;
+}
+DEV uint2 int4_lane_scales(const uint8_t* block, int lane) { return *(const uint2*)(block + (lane >> 3) * 8); }
 DEV uint2 int4_scales(const uint16_t* srow, int ngroups, int j, int lane) {
   uint32_t h[4];
 #pragma unroll
@@ -264,6 +297,46 @@ DEV f32x4 attn_finish(f32x4 acc) {
     acc.w += __shfl_xor(acc.w, off);
   }
   return acc;
+}
+
+// Split-K merge of one query head's chunk partials ("One launch per token",
+// "The attention trap": each chunk's unnormalised output is rescaled by
+// e^(m_c - M), M the largest chunk maximum, and divided by the rescaled sum of
+// the l_c).  Chunk 0's state (acc, m, l) is the wave's own, after attn_finish;
+// chunks 1 .. n-1 (n <= 64) are at mb + (c - 1) * (D + 4) in LDS: D output
+// columns, then m and l.  ps (64 floats of LDS) takes the merge weights.
+// Returns, on lanes 0 .. D/4 - 1, the merged output columns 4 lane .. 4 lane + 3;
+// the chunks are added in chunk order.
+template <int D>
+DEV f32x4 attn_merge(f32x4 acc, float m, float l, const float* mb, int n, float* ps) {
+  constexpr int st = D + 4;
+  const int lane = lane_id();
+  const bool have = lane < n;
+  const float* pc = mb + (have && lane > 0 ? lane - 1 : 0) * st;
+  const float mc = lane == 0 ? m : have ? pc[D] : -__builtin_inff();
+  const float lc = lane == 0 ? l : have ? pc[D + 1] : 0.f;
+  const float M = wave_max(mc);
+  const float w0 = have ? __expf(mc - M) : 0.f;
+  ps[lane] = w0 / wave_sum(lc * w0);  // the weights leave the lanes before the loop below
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (lane < D / 4) {
+    const int e = 4 * lane;
+    const float wc0 = ps[0];
+    o.x = acc.x * wc0;
+    o.y = acc.y * wc0;
+    o.z = acc.z * wc0;
+    o.w = acc.w * wc0;
+    for (int c = 1; c < n; ++c) {
+      const float wc = ps[c];
+      const f32x4 v = *(const f32x4*)(mb + (c - 1) * st + e);
+      o.x = fmaf(wc, v.x, o.x);
+      o.y = fmaf(wc, v.y, o.y);
+      o.z = fmaf(wc, v.z, o.z);
+      o.w = fmaf(wc, v.w, o.w);
+    }
+  }
+  return o;
 }
 
 }  // namespace

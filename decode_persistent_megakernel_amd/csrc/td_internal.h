@@ -1,6 +1,7 @@
 // td_internal.h - device-side parameter block and layout constants shared by
 // the host API (td_api.cpp) and the kernels (td_kernels.hip, td_ops.hip).
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 #define TD_NW 8                       // compute waves per workgroup (waves 0..7)
@@ -251,5 +252,13 @@ int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos
 int td_launch_op_layers(const td_opparams* p, void* stream);
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,
                         void* stream);
-int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, float* out,
-                             void* stream);
+// one position's RoPE table row: (cos, sin) of pair i at [2 i], [2 i + 1], i < d/2 <= 64
+struct td_rope_row {
+  float cs[128];
+};
+int td_launch_test_rope(const float* x, int n_heads, int d, const td_rope_row& row, float* y, void* stream);
+int td_launch_test_argmax(const float* logits, int n, int groups, void* work, int* token, int* nonfinite,
+                          void* stream);
+size_t td_test_attention_lds(int d, int chunk_len, int n);
+int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, int chunk_len, float scale,
+                             float* out, void* stream);

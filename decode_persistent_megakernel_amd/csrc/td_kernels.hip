@@ -564,7 +564,7 @@ DEV float gemv_row(const td_kparams& P, CState& C, int J) {
     if (FMT == 0) {
       acc += dot_bf16(w, C.xin + j * 512 + lane * 8);
     } else {
-      const uint2 sc = *(const uint2*)(C.sring + C.slot * TD_SCHUNK + (lane >> 3) * 8);
+      const uint2 sc = int4_lane_scales(C.sring + C.slot * TD_SCHUNK, lane);
       acc += dot_int4(w, C.xin + j * 2048, lane, sc);
     }
     chunk_release(P, C);
@@ -671,11 +671,7 @@ DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer
       }
       if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
         const float* cs = (const float*)(C.lds + P.off_rope);
-        const float c = cs[2 * i], sn = cs[2 * i + 1];
-        const float a2 = a * c - b * sn;
-        const float b2 = b * c + a * sn;
-        a = a2;
-        b = b2;
+        rope_pair(a, b, cs[2 * i], cs[2 * i + 1]);
       }
       const int gw = (P.group + 2) * P.d;  // published block of one kv head
       if (ra < P.qd) {
@@ -705,15 +701,11 @@ DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer
       const float v = C.out[idx] * inv;
       P.logits[u] = v;
       if (!isfinite(v)) bad = 1;
-      else if (v > bv || (v == bv && u < bi)) { bv = v; bi = u; }
+      else if (cand_better(v, u, bv, bi)) { bv = v; bi = u; }
     }
   }
   if (kind == TD_ST_HEAD) {
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    cand_wave_max(bv, bi);
     bad = __any(bad);
     if (lane == 0) {
       uint32_t* cd = C.ctl + TD_CTL_CAND + 4 * wave;
@@ -775,31 +767,9 @@ DEV void attn_wave_d(const td_kparams& P, CState& C, uint8_t* lds, int h, const 
   // O stage waits for their outputs
   if (n > 1) C.ok &= poll_pairs<8, false>(P, myparts + st, 0, (n - 1) * st, tag, mb, C);
   lds_fence();
-  const bool have = lane < n;
-  const float* pc = mb + (have && lane > 0 ? lane - 1 : 0) * st;
-  const float mc = lane == 0 ? m : have ? pc[D] : -__builtin_inff();
-  const float lc = lane == 0 ? l : have ? pc[D + 1] : 0.f;
-  const float M = wave_max(mc);
-  const float w0 = have ? __expf(mc - M) : 0.f;
-  ps[lane] = w0 / wave_sum(lc * w0);  // the weights leave the lanes before the loop below
-  lds_fence();
+  const f32x4 o = attn_merge<D>(acc, m, l, mb, n, ps);
   if (lane < D / 4) {
-    const int e = 4 * lane;
-    const float wc0 = ps[0];
-    f32x4 o;
-    o.x = acc.x * wc0;
-    o.y = acc.y * wc0;
-    o.z = acc.z * wc0;
-    o.w = acc.w * wc0;
-    for (int c = 1; c < n; ++c) {
-      const float wc = ps[c];
-      const f32x4 v = *(const f32x4*)(mb + (c - 1) * st + e);
-      o.x = fmaf(wc, v.x, o.x);
-      o.y = fmaf(wc, v.y, o.y);
-      o.z = fmaf(wc, v.z, o.z);
-      o.w = fmaf(wc, v.w, o.w);
-    }
-    uint2* dst = P.to + ((size_t)T.g * G + h) * D + e;
+    uint2* dst = P.to + ((size_t)T.g * G + h) * D + 4 * lane;
     st_tag(dst + 0, o.x, tag);
     st_tag(dst + 1, o.y, tag);
     st_tag(dst + 2, o.z, tag);
@@ -1025,14 +995,7 @@ DEV bool poll_pairs_plain(const td_kparams& P, const uint2* src, int n, uint32_t
   return true;
 }
 
-// (value, index) of the better greedy candidate: larger value, lower index on ties
-DEV void cand_max(float& bv, int& bi) {
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-  }
-}
+DEV void cand_max(float& bv, int& bi) { cand_wave_max(bv, bi); }
 
 DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
   const int lane = lane_id();
@@ -1110,7 +1073,7 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
       const float v = cands[4 * c];
       const int i = (int)__float_as_uint(cands[4 * c + 1]);
       fbad |= (int)__float_as_uint(cands[4 * c + 2]);
-      if (v > fv || (v == fv && i < fi)) { fv = v; fi = i; }
+      if (cand_better(v, i, fv, fi)) { fv = v; fi = i; }
     }
     cand_max(fv, fi);
     fbad = __any(fbad);
@@ -1181,24 +1144,14 @@ __global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, u
       const int boff = c.j * TD_CHUNK + lane * 16;
       v = boff < c.g.row_bytes ? *(const u32x4*)(rp + boff) : (u32x4){0u, 0u, 0u, 0u};
     } else {  // the lane's four words, from their places in the row (zero weights past its end)
-      uint32_t wd[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int boff = c.j * TD_CHUNK + int4_word_off(w, lane);
-        wd[w] = boff < c.g.row_bytes ? *(const uint32_t*)(rp + boff) : 0x88888888u;
-      }
-      v = (u32x4){wd[0], wd[1], wd[2], wd[3]};
+      v = int4_words(rp, c.g.row_bytes, c.j, lane);
     }
     *(u32x4*)(dst + lane * 16) = v;
     dst += TD_CHUNK;
     if (c.g.fmt == 1) {
       if (n4 >= W.n4) break;
-      if (lane < 32) {  // block position 4 (l / 8) + w holds the scale of word w of lanes l
-        const int g = c.j * 32 + int4_word_group(lane & 3, (lane >> 2) * 8);
-        uint16_t sv = 0;
-        if (g < c.g.K / 64) sv = c.g.s[(size_t)row * (c.g.K / 64) + g];
-        *(uint16_t*)(sdst + lane * 2) = sv;
-      }
+      if (lane < 32)
+        *(uint16_t*)(sdst + lane * 2) = int4_block_scale(c.g.s + (size_t)row * (c.g.K / 64), c.g.K / 64, c.j, lane);
       sdst += TD_SCHUNK;
       ++n4;
     }
@@ -1209,47 +1162,179 @@ __global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, u
 }
 
 // ------------------------------------------------------------ test hooks
-// y = W x, one wave per row, same chunk arithmetic as the megakernel.
+// y = W x through the packed-stream layout and the step's chunk arithmetic:
+// x is staged into LDS zero-padded to whole chunks (as the step stages its
+// input), and each chunk of a row is first packed into an LDS chunk buffer by
+// the routines that build the packed streams (a lane's 16 bytes: its four
+// int4 words or its 8 bf16 weights, zero weights past the row's end; an int4
+// chunk's 64-byte scale block) and then consumed as the step consumes a ring
+// slot.  One wave per row, 4 rows per workgroup.
 __global__ void __launch_bounds__(256) td_gemv_kernel(int fmt, const uint8_t* w, const uint16_t* s, int rows,
-                                                      int cols, const float* x, float* y) {
-  const int lane = lane_id();
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                      int cols, int kpad, const float* x, float* y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* xs = (float*)lds;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  uint8_t* cbuf = lds + (size_t)kpad * 4 + wave * (TD_CHUNK + TD_SCHUNK);
+  uint8_t* sbuf = cbuf + TD_CHUNK;
+  for (int i = threadIdx.x; i < kpad; i += 256) xs[i] = i < cols ? x[i] : 0.f;
+  __syncthreads();
+  const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
   const int row_bytes = fmt == 0 ? cols * 2 : cols / 2;
   const int J = (row_bytes + TD_CHUNK - 1) / TD_CHUNK;
+  const uint8_t* rp = w + (size_t)row * row_bytes;
   float acc = 0.f;
   for (int j = 0; j < J; ++j) {
+    u32x4 v;
     if (fmt == 0) {
       const int boff = j * TD_CHUNK + lane * 16;
-      if (boff < row_bytes) acc += dot_bf16(*(const u32x4*)(w + (size_t)row * row_bytes + boff), x + j * 512 + lane * 8);
+      v = boff < row_bytes ? *(const u32x4*)(rp + boff) : (u32x4){0u, 0u, 0u, 0u};
     } else {
-      acc += dot_int4(int4_words(w + (size_t)row * row_bytes, row_bytes, j, lane), x + j * 2048, lane,
-                      int4_scales(s + (size_t)row * (cols / 64), cols / 64, j, lane));
+      v = int4_words(rp, row_bytes, j, lane);
+      if (lane < 32)
+        *(uint16_t*)(sbuf + lane * 2) = int4_block_scale(s + (size_t)row * (cols / 64), cols / 64, j, lane);
     }
+    *(u32x4*)(cbuf + lane * 16) = v;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const u32x4 wv = *(const u32x4*)(cbuf + lane * 16);
+    if (fmt == 0) acc += dot_bf16(wv, xs + j * 512 + lane * 8);
+    else acc += dot_int4(wv, xs + j * 2048, lane, int4_lane_scales(sbuf, lane));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   const float r = wave_sum(acc);
   if (lane == 0) y[row] = r;
 }
 
-// one query head over n bf16 K/V rows: scores, softmax, weighted V (one wave, lane = dim)
+// One query head over n bf16 K/V rows with the decode kernel's own attention
+// routines: the positions cut into chunks of chunk_len (a multiple of the
+// 64-row tile), each chunk's tiles staged into LDS in the kernel's tile layout
+// (K rows padded to D + 8, rows past the chunk's end zero) and taken by
+// attn_tile, the chunk's state finished by attn_finish, and the chunks merged
+// by attn_merge, chunk 0 holding its own state as on the merging CU.  q is
+// scaled by 1/sqrt(d) in fp32 first, as the kernel scales its staged queries.
+// One wave; LDS: q [D], p [64], the tile, the partials of chunks 1 .. n-1.
+template <int D>
 __global__ void __launch_bounds__(64) td_attention_kernel(const float* q, const uint16_t* k, const uint16_t* v,
-                                                          int n, int d, float* out) {
+                                                          int n, int chunk_len, float scale, float* out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int st = D + 4;
+  float* qs = (float*)lds;
+  float* ps = qs + D;
+  uint16_t* kt = (uint16_t*)(ps + TD_TILE);
+  uint16_t* vt = kt + TD_TILE * (D + 8);
+  float* mb = (float*)(vt + TD_TILE * D);
   const int lane = lane_id();
-  const float scale = 1.0f / sqrtf((float)d);
-  float m = -__builtin_inff(), l = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int t = 0; t < n; ++t) {
-    float part = 0.f;
-    for (int e = lane; e < d; e += 64) part = fmaf(q[e], bf16f(k[(size_t)t * d + e]), part);
-    const float s = wave_sum(part) * scale;
-    const float mn = fmaxf(m, s);
-    const float corr = expf(m - mn), p = expf(s - mn);
-    l = l * corr + p;
-    a0 = a0 * corr + p * bf16f(v[(size_t)t * d + lane]);
-    if (d > 64) a1 = a1 * corr + p * bf16f(v[(size_t)t * d + 64 + lane]);
-    m = mn;
+  for (int i = lane; i < D; i += 64) qs[i] = q[i] * scale;
+  const int nch = (n + chunk_len - 1) / chunk_len;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
+  float m0 = -__builtin_inff(), l0 = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * chunk_len, t1 = min(t0 + chunk_len, n);
+    float m = -__builtin_inff(), l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int tb = t0; tb < t1; tb += TD_TILE) {
+      const int nv = min(TD_TILE, t1 - tb);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      for (int i = lane; i < TD_TILE * (D / 8); i += 64) {
+        const int row = i / (D / 8), pc = i - row * (D / 8);
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (row < nv) {
+          kv = *(const u32x4*)(k + (size_t)(tb + row) * D + pc * 8);
+          vv = *(const u32x4*)(v + (size_t)(tb + row) * D + pc * 8);
+        }
+        *(u32x4*)(kt + row * (D + 8) + pc * 8) = kv;
+        *(u32x4*)(vt + row * D + pc * 8) = vv;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      attn_tile<D>(qs, kt, vt, ps, nv, m, l, acc);
+    }
+    acc = attn_finish<D>(acc);
+    if (c == 0) {
+      acc0 = acc;
+      m0 = m;
+      l0 = l;
+    } else {
+      float* dst = mb + (size_t)(c - 1) * st;
+      if (lane < D / 4) *(f32x4*)(dst + 4 * lane) = acc;
+      if (lane == 0) {
+        dst[D] = m;
+        dst[D + 1] = l;
+      }
+    }
   }
-  out[lane] = a0 / l;
-  if (d > 64) out[64 + lane] = a1 / l;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const f32x4 o = attn_merge<D>(acc0, m0, l0, mb, nch, ps);
+  if (lane < D / 4) *(f32x4*)(out + 4 * lane) = o;
+}
+
+// Half-split RoPE of n_heads vectors of d values at one position, with the
+// step's pair rotation and a table row built as the step's table is (cs: d/2
+// (cos, sin) pairs).  Thread (head, i) rotates pair (i, i + d/2) of its head.
+__global__ void __launch_bounds__(256) td_rope_kernel(const float* x, int n_heads, int d, td_rope_row row, float* y) {
+  const int t = blockIdx.x * 256 + threadIdx.x, half = d / 2;
+  if (t >= n_heads * half) return;
+  const int h = t / half, i = t - h * half;
+  float a = x[h * d + i], b = x[h * d + i + half];
+  rope_pair(a, b, row.cs[2 * i], row.cs[2 * i + 1]);
+  y[h * d + i] = a;
+  y[h * d + i + half] = b;
+}
+
+// The greedy token of n logits in the step's three levels: every one of the
+// `groups` workgroups (a CU's share of the vocabulary, split as the plan splits
+// it) runs its 8 waves over its rows round robin, lane k of a wave over its
+// rows k, k + 64, ...; each wave's candidate, then the workgroup's over its 8
+// waves, go to cand; the last kernel takes the best of all workgroups'.  A
+// non-finite logit is left out of the choice and raises the flag.
+__global__ void __launch_bounds__(512) td_argmax_groups(const float* logits, int n, int groups, uint2* cand,
+                                                        int* badw) {
+  __shared__ float wv[TD_NW];
+  __shared__ int wi[TD_NW], wb[TD_NW];
+  const int g = blockIdx.x, wave = threadIdx.x >> 6, lane = lane_id();
+  const int u0 = (int)((int64_t)n * g / groups), u1 = (int)((int64_t)n * (g + 1) / groups);
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff, bad = 0;
+  for (int u = u0 + wave + lane * TD_NW; u < u1; u += 64 * TD_NW) {
+    const float v = logits[u];
+    if (!isfinite(v)) bad = 1;
+    else if (cand_better(v, u, bv, bi)) { bv = v; bi = u; }
+  }
+  cand_wave_max(bv, bi);
+  bad = __any(bad);
+  if (lane == 0) {
+    wv[wave] = bv;
+    wi[wave] = bi;
+    wb[wave] = bad;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float v = lane < TD_NW ? wv[lane] : -__builtin_inff();
+    int i = lane < TD_NW ? wi[lane] : 0x7fffffff;
+    const int b = __any(lane < TD_NW && wb[lane]);
+    cand_wave_max(v, i);
+    if (lane == 0) {
+      cand[g] = make_uint2(__float_as_uint(v), (uint32_t)i);
+      badw[g] = b;
+    }
+  }
+}
+__global__ void __launch_bounds__(64) td_argmax_final(const uint2* cand, const int* badw, int groups, int* token,
+                                                      int* nonfinite) {
+  const int lane = lane_id();
+  float fv = -__builtin_inff();
+  int fi = 0x7fffffff, fbad = 0;
+  for (int c = lane; c < groups; c += 64) {
+    const float v = __uint_as_float(cand[c].x);
+    const int i = (int)cand[c].y;
+    fbad |= badw[c];
+    if (cand_better(v, i, fv, fi)) { fv = v; fi = i; }
+  }
+  cand_wave_max(fv, fi);
+  fbad = __any(fbad);
+  if (lane == 0) {
+    *token = fi == 0x7fffffff ? 0 : fi;
+    *nonfinite = fbad;
+  }
 }
 
 }  // namespace
@@ -1285,12 +1370,48 @@ int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale
 
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,
                         void* stream) {
-  td_gemv_kernel<<<(rows + 3) / 4, 256, 0, (hipStream_t)stream>>>(fmt, (const uint8_t*)w, (const uint16_t*)s, rows,
-                                                                   cols, x, y);
+  const int ce = fmt ? 2048 : 512;
+  const int kpad = (cols + ce - 1) / ce * ce;
+  const size_t lds = (size_t)kpad * 4 + 4 * (TD_CHUNK + TD_SCHUNK);
+  hipError_t e = hipFuncSetAttribute((const void*)td_gemv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return (int)e;
+  td_gemv_kernel<<<(rows + 3) / 4, 256, lds, (hipStream_t)stream>>>(fmt, (const uint8_t*)w, (const uint16_t*)s, rows,
+                                                                     cols, kpad, x, y);
   return (int)hipGetLastError();
 }
 
-int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, float* out, void* stream) {
-  td_attention_kernel<<<1, 64, 0, (hipStream_t)stream>>>(q, (const uint16_t*)k, (const uint16_t*)v, n, d, out);
+int td_launch_test_rope(const float* x, int n_heads, int d, const td_rope_row& row, float* y, void* stream) {
+  const int n = n_heads * (d / 2);
+  td_rope_kernel<<<(n + 255) / 256, 256, 0, (hipStream_t)stream>>>(x, n_heads, d, row, y);
+  return (int)hipGetLastError();
+}
+
+int td_launch_test_argmax(const float* logits, int n, int groups, void* work, int* token, int* nonfinite,
+                          void* stream) {
+  uint2* cand = (uint2*)work;
+  int* badw = (int*)(cand + groups);
+  td_argmax_groups<<<groups, 512, 0, (hipStream_t)stream>>>(logits, n, groups, cand, badw);
+  td_argmax_final<<<1, 64, 0, (hipStream_t)stream>>>(cand, badw, groups, token, nonfinite);
+  return (int)hipGetLastError();
+}
+
+size_t td_test_attention_lds(int d, int chunk_len, int n) {
+  const int nch = (n + chunk_len - 1) / chunk_len;
+  return (size_t)(d + TD_TILE) * 4 + (size_t)TD_TILE * (d + 8) * 2 + (size_t)TD_TILE * d * 2 +
+         (size_t)(nch > 1 ? nch - 1 : 1) * (d + 4) * 4;
+}
+
+int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, int chunk_len, float scale,
+                             float* out, void* stream) {
+  const size_t lds = td_test_attention_lds(d, chunk_len, n);
+  const void* f = d == 64 ? (const void*)td_attention_kernel<64> : (const void*)td_attention_kernel<128>;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return (int)e;
+  if (d == 64)
+    td_attention_kernel<64><<<1, 64, lds, (hipStream_t)stream>>>(q, (const uint16_t*)k, (const uint16_t*)v, n,
+                                                                  chunk_len, scale, out);
+  else
+    td_attention_kernel<128><<<1, 64, lds, (hipStream_t)stream>>>(q, (const uint16_t*)k, (const uint16_t*)v, n,
+                                                                   chunk_len, scale, out);
   return (int)hipGetLastError();
 }

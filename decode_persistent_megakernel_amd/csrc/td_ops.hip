@@ -292,11 +292,7 @@ __global__ void __launch_bounds__(256) op_qkv(td_opparams P, int layer, int R) {
     }
     const int i = ra % P.d;
     if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
-      const float c = P.rope_cs[((size_t)pos * half + i) * 2], sn = P.rope_cs[((size_t)pos * half + i) * 2 + 1];
-      const float a2 = a * c - b * sn;
-      const float b2 = b * c + a * sn;
-      a = a2;
-      b = b2;
+      rope_pair(a, b, P.rope_cs[((size_t)pos * half + i) * 2], P.rope_cs[((size_t)pos * half + i) * 2 + 1]);
     }
     if (ra < P.qd) {
       P.q[ra] = a * P.attn_scale;

@@ -254,13 +254,60 @@ const char* td_last_error(void);
  * synchronises; they exist so that tests can compare one routine with the
  * oracle.  Same error convention. */
 
-/* y[rows] = W x for a bf16 or int4 linear (the GEMV routine of the step). */
+/* The work plan without a device ("Decoding in tiles", sec. 4: the schedule is
+ * built and checked once, before any launch, and an invalid one is refused).
+ * td_plan_check builds the plan td_create would build on a gfx950 with ncu
+ * CUs and 160 KiB of LDS per CU (the attention split, every GEMV stage's units
+ * over the CUs, the LDS layout, the weight streams) and validates it: TD_OK,
+ * or the code td_create would return (TD_E_PLAN for a partition that leaves a
+ * unit or a row without an owner, gives one two owners, or leaves the
+ * matrix; TD_E_UNSUPPORTED for a config the kernels cannot split, such as
+ * more kv heads than CUs; TD_E_INVALID_ARG for a bad config).  With part
+ * non-NULL (host int32 [4][ncu + 1], part_len = 4 (ncu + 1): for each unit
+ * space -- QKV row pairs, hidden rows, intermediate rows, vocabulary rows --
+ * the first unit of every CU, then the unit count) the plan uses that
+ * partition instead of its own.  td_plan_partition writes the partition the
+ * plan builds into part_out (same layout).  Host code only: no HIP call. */
+int td_plan_partition(const td_config* cfg, int32_t ncu, int32_t* part_out, int32_t part_len);
+int td_plan_check(const td_config* cfg, int32_t ncu, const int32_t* part, int32_t part_len);
+
+/* y[rows] = W x for a bf16 or int4 linear (w, scales: device, row-major as in
+ * td_layer_weights; d_x [cols], d_y [rows]: device fp32) through the step's
+ * GEMV path: x zero-padded to whole chunks, each row chunk packed as the
+ * weight streams pack it (an int4 chunk's codes and its 64-byte scale block)
+ * and consumed by the step's chunk dot product.  cols <= 32768 (bf16: a
+ * multiple of 8; int4: a multiple of 64, scales non-NULL). */
 int td_test_gemv(int32_t weight_format, const void* w, const void* scales, int32_t rows, int32_t cols,
                  const float* d_x, float* d_y, void* stream);
 
-/* One query head's attention over n_pos bf16 K/V rows ([n_pos][d]), fp32 q and out [d]. */
+/* One query head's attention over n_pos bf16 K/V rows ([n_pos][head_dim], device), fp32 q and
+ * out [head_dim] (device): softmax(q . K^T / sqrt(d)) V with the decode step's own routines
+ * ("One launch per token", "The attention trap": split-K partials merged with the
+ * e^(m_c - M) rescale): the positions are cut into chunks of chunk_len (a multiple of 64; 0 =
+ * one chunk for all), each chunk runs the step's 64-row tile routine over its tiles, and the
+ * chunks' partials are merged by the step's merge routine in chunk order.  At most 64 chunks
+ * (TD_E_INVALID_ARG otherwise, or for head_dim not 64 or 128). */
 int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim,
-                      float* d_out, void* stream);
+                      int32_t chunk_len, float* d_out, void* stream);
+
+/* Half-split RoPE of n_heads vectors of head_dim fp32 values (d_x, d_out: device
+ * [n_heads][head_dim]) at position pos, with the step's rotation and a table row
+ * built as td_create builds its table (pair (i, i + d/2) turns by
+ * pos * rope_theta^(-2i/d); angle, cosine and sine in double, rounded to fp32;
+ * the flint page's chat.py passage on half-split RoPE). */
+int td_test_rope(const float* d_x, int32_t n_heads, int32_t head_dim, int32_t pos, float rope_theta, float* d_out,
+                 void* stream);
+
+/* The greedy token of n fp32 logits (d_logits, device) by the step's selection
+ * ("Decoding in tiles", sec. 5): `groups` workgroups (1 .. n) each take a
+ * contiguous share of the vocabulary as the plan splits it among the CUs, lanes
+ * of 8 waves run over their rows, and the candidates are reduced wave, then
+ * workgroup, then across workgroups; the largest finite logit wins, the lowest
+ * id among equal ones.  *d_token (device int32) receives it (0 if no logit is
+ * finite), *d_nonfinite (device int32) 1 if any logit is NaN or infinite, else 0.
+ * d_work: device scratch of at least 12 * groups bytes, caller-owned. */
+int td_test_argmax(const float* d_logits, int32_t n, int32_t groups, void* d_work, int32_t* d_token,
+                   int32_t* d_nonfinite, void* stream);
 
 /* In-kernel stage trace (the per-worker timeline of one step).  td_trace_bytes
  * gives the size of the trace: for each CU and each stage of the step (5 per

@@ -102,3 +102,28 @@ def test_nonfinite_logit_sets_error(td):
     got = logits.cpu().numpy()
     assert np.isnan(got[5]) and np.isfinite(np.delete(got, 5)).all()  # the logits are still written
     dec.close()
+
+
+def _random_gains(cfg, m, seed):
+    """Norm gains drawn from N(1, 0.25) (bf16) for every RMSNorm: the workloads'
+    gains are all 1.0, so these cases are the ones that check the gains are
+    applied where they belong (each element of the staged input)."""
+    rng = np.random.default_rng(seed)
+
+    def g():
+        return np.array([synth.lib().synth_f32_to_bf16(float(v)) for v in rng.normal(1.0, 0.25, size=cfg.hidden)],
+                        dtype=np.uint16)
+    for L in m.layers:
+        L.attn_norm = g()
+        L.mlp_norm = g()
+    m.final_norm = g()
+    return m
+
+
+@pytest.mark.parametrize("cfg", [SPLITK, SPLITK128, RAGGED4], ids=["d64", "d128_bias", "int4"])
+def test_random_norm_gains_match_oracle(td, cfg):
+    _say(f"random RMSNorm gains, {cfg.name}")
+    m = _random_gains(cfg, synth.make_model(cfg), seed=77)
+    k, v = synth.random_kv_prefix(cfg, 40, seed_tag="gains")
+    run_compare(td, cfg, m, k, v, synth.first_token(cfg), 40, 6, 2e-2 if cfg.weight_format == 0 else 5e-2,
+                cfg.name + "/gains")

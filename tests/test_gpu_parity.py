@@ -109,19 +109,57 @@ def test_gemv_int4_one_hot_is_bit_exact_dequant(td):
 
 # ------------------------------------------------------------------ attention hook
 
-@pytest.mark.parametrize("n,d", [(1, 64), (5, 64), (200, 64), (129, 128), (1, 128)])
-def test_attention_hook_matches_oracle(td, n, d):
-    _say(f"attention hook n={n} d={d}")
+# (positions, head dim, chunk length): one row, ragged single tiles, several tiles per
+# chunk, many chunks with a ragged last one, the largest chunk count (64), head dim 128
+ATTN_CASES = [(1, 64, 0), (5, 64, 0), (63, 64, 64), (64, 64, 64), (65, 64, 64), (200, 64, 0), (200, 64, 64),
+              (1000, 64, 128), (4095, 64, 64), (129, 128, 64), (1, 128, 0), (777, 128, 192), (513, 128, 0)]
+
+
+@pytest.mark.parametrize("n,d,chunk", ATTN_CASES, ids=[f"n{n}_d{d}_c{c}" for n, d, c in ATTN_CASES])
+def test_attention_hook_matches_oracle(td, n, d, chunk):
+    """The step's own tile routine and split-K merge (through td_test_attention)
+    against the oracle's two-pass softmax in fp64: within 2e-5 of the output's
+    scale (fp32 exponentials and sums over at most 4096 positions), and exactly
+    V when there is a single position."""
+    _say(f"attention hook n={n} d={d} chunk={chunk}")
     q = RNG.normal(size=d).astype(np.float32)
     K = bf16_from_f32(RNG.normal(size=(n, d)))
     V = bf16_from_f32(RNG.normal(size=(n, d)))
     out = torch.empty(d, dtype=torch.float32, device="cuda")
-    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out)
+    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out, chunk_len=chunk)
     ref = oracle.attention(q.astype(np.float64), K, V)
     got = out.cpu().numpy().astype(np.float64)
     if n == 1:
         assert np.array_equal(got, ref)
     np.testing.assert_allclose(got, ref, rtol=0, atol=2e-5 * max(1.0, np.abs(ref).max()))
+
+
+def test_attention_hook_one_dominant_key_and_equal_keys(td):
+    """Closed forms: with all keys equal the output is the mean of V; with one
+    key far ahead of the others it is that key's V row."""
+    d, n = 64, 300
+    q = np.ones(d, dtype=np.float32)
+    K = bf16_from_f32(np.full((n, d), 0.25))
+    V = bf16_from_f32(RNG.normal(size=(n, d)))
+    out = torch.empty(d, dtype=torch.float32, device="cuda")
+    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out, chunk_len=64)
+    np.testing.assert_allclose(out.cpu().numpy(), bf16_to_f64(V).mean(axis=0), rtol=0, atol=1e-5)
+    K2 = bf16_from_f32(np.zeros((n, d)))
+    K2[137] = bf16_from_f32(np.full(d, 8.0))  # score 8 * 64 / 8 = 64 above the rest: e^-64 weights
+    td.attention(torch.from_numpy(q).cuda(), dev(K2), dev(V), n, d, out, chunk_len=64)
+    np.testing.assert_allclose(out.cpu().numpy(), bf16_to_f64(V[137]), rtol=0, atol=1e-6)
+
+
+def test_attention_hook_argument_checks(td):
+    from decode_persistent_megakernel_amd import _lib
+    d = 64
+    q = torch.zeros(d, dtype=torch.float32, device="cuda")
+    kv = torch.zeros((5000, d), dtype=torch.int16, device="cuda")
+    out = torch.empty(d, dtype=torch.float32, device="cuda")
+    for n, dd, c in ((10, 64, 32), (10, 96, 0), (0, 64, 0), (4097, 64, 64)):
+        with pytest.raises(_lib.TdError) as ei:
+            td.attention(q, kv, kv, n, dd, out, chunk_len=c)
+        assert ei.value.code == _lib.TD_E_INVALID_ARG, (n, dd, c)
 
 
 # ------------------------------------------------------------------ whole step (megakernel)
