@@ -206,6 +206,19 @@ class Decoder:
             pass
 
 
+def decode_step_noalloc(dm: "DeviceModel", max_ctx: int, token_ptr: int, pos: int, kv: "KVCache", logits,
+                        token_out, error_out, stream=None) -> None:
+    """One decode step with no context and no device allocation (td_decode_step_noalloc):
+    the library's fixed scratch array holds every intermediate; token_out and error_out
+    are int32 device tensors [1]."""
+    cfg = dm.td_config(max_ctx)
+    w, _layers = dm.td_weights()
+    kvs = kv.td_kv()
+    _lib.check(_lib.lib().td_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(w), token_ptr, int(pos),
+                                                 ctypes.byref(kvs), _ptr(logits), _ptr(token_out), _ptr(error_out),
+                                                 _stream_handle(stream)), "td_decode_step_noalloc")
+
+
 def gemv(fmt: int, w, s, rows: int, cols: int, x, y, stream=None) -> None:
     """y = W x on device tensors through the test hook (same chunk arithmetic as the step)."""
     _lib.check(_lib.lib().td_test_gemv(fmt, _ptr(w), _ptr(s), rows, cols, _ptr(x), _ptr(y), _stream_handle(stream)),

@@ -28,9 +28,10 @@ TD_MAX_LOOP_STEPS = 256
 TD_MAX_BLOCK = 64
 TD_MAX_EXPERTS = 256
 TD_MAX_TOPK = 16
+TD_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTED = [
-    "td_create", "td_decode_step", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_expert_ids", "td_expert_weights", "td_status", "td_destroy", "td_strerror", "td_last_error",
+    "td_create", "td_decode_step", "td_decode_step_noalloc", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_expert_ids", "td_expert_weights", "td_status", "td_destroy", "td_strerror", "td_last_error",
     "td_plan_partition", "td_plan_check",
     "td_test_gemv", "td_test_attention", "td_test_rope", "td_test_argmax", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
 ]
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.td_create.argtypes = [ctypes.POINTER(TdConfig), ctypes.POINTER(TdWeights), i32, ctypes.POINTER(vp)]
         L.td_decode_step.restype = i32
         L.td_decode_step.argtypes = [vp, vp, i32, ctypes.POINTER(TdKV), vp, vp]
+        L.td_decode_step_noalloc.restype = i32
+        L.td_decode_step_noalloc.argtypes = [ctypes.POINTER(TdConfig), ctypes.POINTER(TdWeights), vp, i32,
+                                             ctypes.POINTER(TdKV), vp, vp, vp, vp]
         L.td_decode_loop.restype = i32
         L.td_decode_loop.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(TdKV), vp, vp, vp, vp]
         L.td_forward_block.restype = i32

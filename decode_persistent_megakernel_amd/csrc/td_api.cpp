@@ -309,19 +309,14 @@ struct Plan {
   uint64_t stream_code_chunks = 0, stream_scale_blocks = 0;
 };
 
-int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* part_in, Plan& out) {
-  int rc = check_config(cfg);
-  if (rc) return rc;
-  if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
-  const td_config& c = *cfg;
-  const int d = c.head_dim, H = c.hidden, I = c.intermediate, L = c.n_layers;
-  const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
-  const int qd = nq * d;
-
-  // attention split: at most one task per CU, chunks a multiple of the tile,
-  // at most 64 chunks per kv head, and the merge staging within the LDS the
-  // GEMV input area already takes (the attention area aliases it), at least
-  // 24 KiB: more chunks mean fewer tiles per CU, which a CU runs one by one
+// The attention split of a config on ncu CUs: at most one task per CU, chunks
+// a multiple of the tile, at most 64 chunks per kv head, and the merge staging
+// within the LDS the GEMV input area already takes (the attention area aliases
+// it), at least 24 KiB: more chunks mean fewer tiles per CU, which a CU runs
+// one by one.  No allocation.
+int attention_split(const td_config& c, int ncu, int* chunk_len_out, int* n_chunks_out) {
+  const int d = c.head_dim, H = c.hidden, I = c.intermediate;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv, qd = nq * d;
   if (nkv > ncu) return fail(TD_E_UNSUPPORTED, "more kv heads than CUs: the attention split needs a CU per kv head");
   const int cmax_by_cu = ncu / nkv;
   int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
@@ -333,6 +328,23 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
     chunk_len += TD_TILE;
   const int n_chunks_max = n_chunks_of(chunk_len);
   if (n_chunks_max * nkv > ncu) return fail(TD_E_PLAN, "attention split exceeds the CU count");
+  *chunk_len_out = chunk_len;
+  *n_chunks_out = n_chunks_max;
+  return TD_OK;
+}
+
+int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* part_in, Plan& out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
+  const td_config& c = *cfg;
+  const int d = c.head_dim, H = c.hidden, I = c.intermediate, L = c.n_layers;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
+  const int qd = nq * d;
+
+  int chunk_len = 0, n_chunks_max = 0;
+  rc = attention_split(c, ncu, &chunk_len, &n_chunks_max);
+  if (rc) return rc;
 
   // partition of every GEMV stage's units over the CUs (or the caller's, for the plan test)
   std::vector<int32_t> part = build_partition(c, ncu, std::vector<double>(ncu, 1.0));
@@ -837,6 +849,129 @@ int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t po
   }
   ctx->last_stream = s;
   ctx->launched = true;
+  return TD_OK;
+}
+
+int td_decode_step_noalloc(const td_config* cfg, const td_weights* w, const int32_t* d_token, int32_t pos,
+                           const td_kv* kv, float* d_logits_out, int32_t* d_token_out, int32_t* d_error_out,
+                           void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  rc = check_weights(cfg, w);
+  if (rc) return rc;
+  if (!d_token || !kv || !kv->k || !kv->v || !d_logits_out || !d_token_out || !d_error_out)
+    return fail(TD_E_INVALID_ARG, "null argument");
+  if (kv->max_ctx != cfg->max_ctx) return fail(TD_E_INVALID_ARG, "kv max_ctx differs from the config");
+  if (((uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return fail(TD_E_INVALID_ARG, "K/V cache pointer not 16-byte aligned");
+  if (pos < 0 || pos >= cfg->max_ctx) return fail(TD_E_RANGE, "pos outside [0, max_ctx)");
+  const td_config& c = *cfg;
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
+  int chunk_len = 0, n_chunks = 0;
+  rc = attention_split(c, ncu, &chunk_len, &n_chunks);
+  if (rc) return rc;
+  void* base = nullptr;
+  int se = td_noalloc_scratch(&base);
+  if (se) return hip_fail((hipError_t)se, "hipGetSymbolAddress");
+
+  // the per-op executor's parameters over the scratch array (no allocation)
+  td_opparams op{};
+  const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  op.L = c.n_layers;
+  op.H = c.hidden;
+  op.nq = nq;
+  op.nkv = nkv;
+  op.d = d;
+  op.I = c.intermediate;
+  op.V = c.vocab;
+  op.max_ctx = c.max_ctx;
+  op.wf = c.weight_format;
+  op.has_bias = c.qkv_bias ? 1 : 0;
+  op.qd = nq * d;
+  op.kvd = nkv * d;
+  op.qkv_rows = op.qd + 2 * op.kvd;
+  op.group = nq / nkv;
+  op.eps = c.rms_eps;
+  op.attn_scale = (float)(1.0 / std::sqrt((double)d));
+  op.chunk_len = chunk_len;
+  op.n_chunks_max = n_chunks;
+  op.E = c.n_experts;
+  op.topk = op.E > 0 ? c.top_k : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  const size_t o_layers = take(sizeof(td_layer_dev) * op.L), o_rope = take((size_t)d * 4), o_pos = take(4);
+  const size_t o_x = take((size_t)op.H * 4), o_q = take((size_t)op.qd * 4);
+  const size_t o_part = take((size_t)nkv * n_chunks * op.group * (d + 4) * 4);
+  const size_t o_o = take((size_t)op.qd * 4), o_act = take((size_t)op.I * std::max(1, op.topk) * 4);
+  const size_t o_cand = take((size_t)td_op_head_blocks(&op) * 16);
+  const size_t o_rl = take((size_t)std::max(1, op.E) * 4), o_eid = take((size_t)op.L * std::max(1, op.topk) * 4);
+  const size_t o_ew = take((size_t)op.L * std::max(1, op.topk) * 4);
+  if (off > TD_NOALLOC_SCRATCH_BYTES)
+    return fail(TD_E_UNSUPPORTED, "the config needs " + std::to_string(off) + " bytes of scratch, more than the " +
+                                      std::to_string(TD_NOALLOC_SCRATCH_BYTES) + " of the no-allocation step");
+  uint8_t* b = (uint8_t*)base;
+  td_layer_dev* table = (td_layer_dev*)(b + o_layers);
+  op.layers = table;
+  op.rope_cs = (const float*)(b + o_rope);
+  op.rope_pos0 = pos;
+  op.pos_word = (int32_t*)(b + o_pos);
+  op.x = (float*)(b + o_x);
+  op.q = (float*)(b + o_q);
+  op.part = (float*)(b + o_part);
+  op.o = (float*)(b + o_o);
+  op.act = (float*)(b + o_act);
+  op.cand = (uint32_t*)(b + o_cand);
+  op.rlogits = (float*)(b + o_rl);
+  op.expert_ids = op.E > 0 ? (int32_t*)(b + o_eid) : nullptr;
+  op.expert_w = op.E > 0 ? (float*)(b + o_ew) : nullptr;
+  op.embed = (const uint16_t*)w->embed;
+  op.head = (const uint16_t*)w->head;
+  op.final_norm = (const uint16_t*)w->final_norm;
+  op.kc = (uint16_t*)kv->k;
+  op.vc = (uint16_t*)kv->v;
+  op.logits = d_logits_out;
+  op.token_out = d_token_out;
+  op.err = d_error_out;
+  int le = td_op_set_lds_limits(&op);
+  if (le) return hip_fail((hipError_t)le, "hipFuncSetAttribute");
+  // the layer table, the RoPE row of pos and the cleared error word, written by
+  // kernels from their arguments (no copy from host memory)
+  for (int l0 = 0; l0 < op.L; l0 += TD_NOALLOC_LAYERS_PER_LAUNCH) {
+    td_noalloc_setup a{};
+    a.first = l0;
+    a.n = std::min(TD_NOALLOC_LAYERS_PER_LAUNCH, op.L - l0);
+    for (int i = 0; i < a.n; ++i) {
+      const td_layer_weights& Lw = w->layers[l0 + i];
+      td_layer_dev& Ld = a.layers[i];
+      Ld.w[0] = (const uint8_t*)Lw.w_qkv;
+      Ld.w[1] = (const uint8_t*)Lw.w_o;
+      Ld.w[2] = (const uint8_t*)Lw.w_gu;
+      Ld.w[3] = (const uint8_t*)Lw.w_d;
+      Ld.s[0] = (const uint16_t*)Lw.s_qkv;
+      Ld.s[1] = (const uint16_t*)Lw.s_o;
+      Ld.s[2] = (const uint16_t*)Lw.s_gu;
+      Ld.s[3] = (const uint16_t*)Lw.s_d;
+      Ld.bias = c.qkv_bias ? (const uint16_t*)Lw.b_qkv : nullptr;
+      Ld.attn_norm = (const uint16_t*)Lw.attn_norm;
+      Ld.mlp_norm = (const uint16_t*)Lw.mlp_norm;
+      Ld.router = c.n_experts > 0 ? (const uint16_t*)Lw.w_router : nullptr;
+    }
+    a.d = d;
+    a.write_rope = l0 == 0 ? 1 : 0;
+    if (a.write_rope) rope_row(c.rope_theta, d, pos, a.rope.cs);
+    le = td_launch_noalloc_setup(a, table, (float*)(b + o_rope), d_error_out, stream);
+    if (le) return hip_fail((hipError_t)le, "setup launch");
+  }
+  le = td_launch_op_begin(&op, d_token, pos, stream);
+  if (le == 0) le = td_launch_op_layers(&op, stream);
+  if (le) return hip_fail((hipError_t)le, "step launch");
   return TD_OK;
 }
 

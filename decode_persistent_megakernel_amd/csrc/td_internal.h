@@ -49,6 +49,11 @@ enum {
   TD_CTL_WORDS = 64
 };
 
+// one position's RoPE table row: (cos, sin) of pair i at [2 i], [2 i + 1], i < d/2 <= 64
+struct td_rope_row {
+  float cs[128];
+};
+
 struct td_layer_dev {
   const uint8_t* w[4];     // QKV, O, GU, DOWN
   const uint16_t* s[4];    // fp16 scales (int4) or null
@@ -130,6 +135,7 @@ struct td_opparams {
   int32_t chunk_len, n_chunks_max;
   int32_t E, topk;   // MoE: experts and experts per token (E = 0: dense MLP)
   int32_t* pos_word;
+  int32_t rope_pos0;  // position of rope_cs's first row (0: the full table; the no-allocation step keeps one row)
   const td_layer_dev* layers;
   const uint16_t* embed;
   const uint16_t* head;
@@ -246,16 +252,23 @@ int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale
 int td_megakernel_occupancy(int head_dim, int weight_format, int lds_bytes, int* blocks_per_cu);
 // per-op executor (td_ops.hip)
 int td_op_head_blocks(const td_opparams* p);
+// the no-allocation step (td_ops.hip): the device's copy of the file-scope
+// scratch array and its size; the setup launch (layer table, RoPE row, error word)
+#define TD_NOALLOC_LAYERS_PER_LAUNCH 16
+struct td_noalloc_setup {
+  td_layer_dev layers[TD_NOALLOC_LAYERS_PER_LAUNCH];
+  td_rope_row rope;
+  int32_t first, n, d, write_rope;
+};
+int td_noalloc_scratch(void** ptr);
+int td_launch_noalloc_setup(const td_noalloc_setup& a, td_layer_dev* table, float* rope_row, int32_t* err,
+                            void* stream);
 size_t td_op_lds_bytes(const td_opparams* p);
 int td_op_set_lds_limits(const td_opparams* p);
 int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos, void* stream);
 int td_launch_op_layers(const td_opparams* p, void* stream);
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,
                         void* stream);
-// one position's RoPE table row: (cos, sin) of pair i at [2 i], [2 i + 1], i < d/2 <= 64
-struct td_rope_row {
-  float cs[128];
-};
 int td_launch_test_rope(const float* x, int n_heads, int d, const td_rope_row& row, float* y, void* stream);
 int td_launch_test_argmax(const float* logits, int n, int groups, void* work, int* token, int* nonfinite,
                           void* stream);

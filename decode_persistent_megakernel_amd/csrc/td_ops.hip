@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "td.h"
 #include "td_internal.h"
@@ -292,7 +293,8 @@ __global__ void __launch_bounds__(256) op_qkv(td_opparams P, int layer, int R) {
     }
     const int i = ra % P.d;
     if (ra < P.qd + P.kvd) {  // q or k: rotate the pair by pos * theta_i
-      rope_pair(a, b, P.rope_cs[((size_t)pos * half + i) * 2], P.rope_cs[((size_t)pos * half + i) * 2 + 1]);
+      const size_t rr = (size_t)(pos - P.rope_pos0) * half + i;
+      rope_pair(a, b, P.rope_cs[rr * 2], P.rope_cs[rr * 2 + 1]);
     }
     if (ra < P.qd) {
       P.q[ra] = a * P.attn_scale;
@@ -648,7 +650,59 @@ __global__ void __launch_bounds__(64) op_argmax(td_opparams P, int nblocks) {
   }
 }
 
+// --------------------------------------------------------------- the no-allocation step
+// Writes one launch's share of the layer table (and, with write_rope, the
+// step's RoPE row and a cleared error word) into the scratch array.
+__global__ void __launch_bounds__(64) op_noalloc_setup(td_noalloc_setup a, td_layer_dev* table, float* rope_row,
+                                                       int32_t* err) {
+  const int t = threadIdx.x;
+  if (t < a.n) table[a.first + t] = a.layers[t];
+  if (a.write_rope) {
+    for (int i = t; i < a.d; i += 64) rope_row[i] = a.rope.cs[i];
+    if (t == 0) *err = 0;
+  }
+}
+
 }  // namespace
+
+// The scratch of td_decode_step_noalloc: activations, attention partials,
+// greedy candidates, the layer table and the step's RoPE row of the per-op
+// kernels, for callers that cannot allocate.  Each device holds its own copy
+// for the life of the process; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device (the array's name is a host-side
+// stand-in, not a device address).  Every call on a device shares the copy, so
+// calls that overlap on one device race.
+static __device__ __align__(256) uint8_t scratch[TD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int TD_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[TD_MAX_DEVICES] = {};
+}  // namespace
+
+// This device's copy of the scratch array (looked up once per device, with the
+// device current).
+int td_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= TD_MAX_DEVICES) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
+}
+
+int td_launch_noalloc_setup(const td_noalloc_setup& a, td_layer_dev* table, float* rope_row, int32_t* err,
+                            void* stream) {
+  op_noalloc_setup<<<1, 64, 0, (hipStream_t)stream>>>(a, table, rope_row, err);
+  return (int)hipGetLastError();
+}
 
 // --------------------------------------------------------------- launchers
 namespace {

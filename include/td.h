@@ -233,6 +233,34 @@ int td_forward_block(td_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t po
                      float* d_logits_out, int32_t all_logits, int32_t* d_argmax_out, void* stream);
 
 /*
+ * td_decode_step_noalloc: one decode step, as td_decode_step computes it on a
+ * TD_EXEC_PER_OP context (the same per-op kernels, the same bits), for callers
+ * that cannot allocate device memory: code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  There is no context: the config and
+ * the weights (as for td_create; device memory that must stay valid until the
+ * step has run) are passed each call, and every piece of device scratch the
+ * step uses (activations, attention partials, greedy candidates, the layer
+ * pointer table, the step's RoPE row) lives in the library's own fixed device
+ * array of TD_NOALLOC_SCRATCH_BYTES (4 MiB), one per GPU, held until the
+ * process ends.  The call allocates nothing: no hipMalloc, no hipFree, no
+ * pinned host memory.  The greedy token goes to d_token_out (device int32), the
+ * fp32 logits to d_logits_out (device [vocab]), and d_error_out (device int32)
+ * is cleared and then receives the device error bits of the step (1: a
+ * non-finite logit, 2: a token id outside [0, vocab)).  Every call on a GPU
+ * shares that GPU's array, which keeps the last call's contents: calls that
+ * overlap on one GPU (several streams or host threads) race, so serialise them.
+ * Asynchronous on `stream`.
+ * Errors (before any launch): as td_create for the config and weights,
+ * TD_E_INVALID_ARG (a null pointer, kv max_ctx mismatch, a cache pointer not
+ * 16-byte aligned), TD_E_RANGE (pos outside [0, max_ctx)), TD_E_UNSUPPORTED
+ * (the config needs more scratch than the array holds), TD_E_HIP.
+ */
+#define TD_NOALLOC_SCRATCH_BYTES (4u << 20)
+int td_decode_step_noalloc(const td_config* cfg, const td_weights* w, const int32_t* d_token, int32_t pos,
+                           const td_kv* kv, float* d_logits_out, int32_t* d_token_out, int32_t* d_error_out,
+                           void* stream);
+
+/*
  * td_status: synchronises the stream of the last td_decode_step, then returns
  * the device error word as a TD_* code (TD_OK, TD_E_NONFINITE, TD_E_RANGE,
  * TD_E_TIMEOUT) and clears it.  *device_error (optional) receives the same code.
