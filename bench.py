@@ -64,6 +64,17 @@ def read_traffic(workload: str, kernel_hash: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(model, cfg, pos0: int, budget_s: float):
     """The CPU oracle (fp64, all host threads) on decode steps of the same model
     at the same positions, for about `budget_s` seconds (at least 2 steps)."""
@@ -96,6 +107,7 @@ def cpu_baseline(model, cfg, pos0: int, budget_s: float):
         n1 += 1
     el1 = time.perf_counter() - t1
     return {"value": round(n / el, 4), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{n} decode steps of the same workload at positions {pos0}..{pos0 + n - 1}, "
                       f"fp64 scalar C oracle, {nthreads} OpenMP threads, K/V prefix random",
             "ms_per_token": round(el / n * 1e3, 2),
@@ -204,15 +216,18 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     spl = 1 if moe else max(1, min(args.steps_per_launch, td._lib.TD_MAX_LOOP_STEPS))
 
-    def run(n, record, per_launch=spl):
+    def run(n, record, per_launch=spl, clocks=None):
         """n greedy steps from `first` at positions start.., per_launch steps per
-        launch; with `record`, HIP events on the stream around every launch.
+        launch; with `record`, HIP events on the stream around every launch (and,
+        with `clocks`, a per-step device clock buffer for each launch).
         Returns [(event pair, steps in the launch, first position)]."""
         evs = []
         i = 0
         while i < n:
             m = min(per_launch, n - i)
             src = first.data_ptr() if i == 0 else tok_ptr
+            if clocks is not None:
+                dec.set_step_clock(clocks[len(evs)])
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -240,11 +255,21 @@ def main() -> int:
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    n_launch = (n_steps + spl - 1) // spl
+    clocks = None if moe else [torch.zeros(spl + 1, dtype=torch.int64, device=dev) for _ in range(n_launch)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    evs = run(n_steps, True)
+    evs = run(n_steps, True, clocks=clocks)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_us = None
+    if clocks is not None:
+        dec.set_step_clock(None)
+        d = []
+        for c, (_, m, _) in zip(clocks, evs):
+            t = c.cpu().numpy()[: m + 1].astype(np.int64)
+            d.extend(np.diff(t) * 10.0 / 1e3)  # 100 MHz ticks -> us
+        step_us = np.array(d)
     st = dec.status()
     if st != 0:
         print(f"device status {st} during the timed steps", file=sys.stderr)
@@ -309,6 +334,11 @@ def main() -> int:
                                                      else 2)}
             bdec.close()
             del bdec
+    # the stream-read yardstick: a plain read of 2 GiB, 5 timed passes
+    ybuf = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    ybuf.fill_(1.0)
+    yard = td.measure_stream(ybuf, reps=5, stream=stream)
+    del ybuf
     khash = source_hash()
     traffic = read_traffic(args.config, khash)
     if traffic is not None:
@@ -341,9 +371,9 @@ def main() -> int:
             "arithmetic": "fp32 accumulate, fp32 activations, bf16 K/V cache",
             "executor": ("hipGraph replay of the per-op launches (router ids in a device tensor), one per token"
                          if moe else
-                         f"persistent megakernel, {spl} greedy steps per cooperative launch (in-kernel token loop)"
+                         f"persistent megakernel, up to {spl} greedy steps per cooperative launch (in-kernel token loop)"
                          if spl > 1 else "persistent megakernel (one cooperative launch per token)"),
-            "steps_per_launch": spl,
+            "steps_per_launch": sorted({m for _, m, _ in evs}),
             "global_batch": 1,
             "parallelism": "single GPU",
         },
@@ -354,13 +384,21 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": (f"graph of {8 * cfg.n_layers + 3} per-op kernels (one decode step per replay)" if moe else
-                       f"td_megakernel ({spl} whole decode step{'s' if spl > 1 else ''} per launch)"),
+            "kernel": (f"graph of {7 * cfg.n_layers + 3} per-op kernels (one decode step per replay)" if moe else
+                       "td_megakernel (" + ", ".join(str(m) for m in sorted({m for _, m, _ in evs}))
+                       + " whole decode steps per launch)"),
             "launches": len(evs),
             "algorithmic_bytes_per_launch": int(round(bytes_launch)),
             "kernel_ms_mean": round(kern_ms, 4),
             "kernel_ms_p10": round(float(np.percentile(launch_ms, 10)), 4),
             "kernel_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
+            "step_ms_p10": None if step_us is None else round(float(np.percentile(step_us, 10)) / 1e3, 4),
+            "step_ms_p50": None if step_us is None else round(float(np.percentile(step_us, 50)) / 1e3, 4),
+            "step_ms_p90": None if step_us is None else round(float(np.percentile(step_us, 90)) / 1e3, 4),
+            "step_clock": "in-kernel 100 MHz clock at each step's token decision (first CU)",
+            "yardstick_gbps": round(yard, 1),
+            "frac_of_yardstick": round(achieved / yard, 4),
+            "yardstick": "td_measure_stream: 16-byte non-temporal reads of 2 GiB, one workgroup per CU, 32 KiB contiguous per pass, 5 passes",
             "source_sha256_16": khash,
         },
         "cpu_baseline": cpu,

@@ -175,6 +175,11 @@ class Decoder:
         err = ctypes.c_int32(0)
         return int(_lib.lib().td_status(self._h, ctypes.byref(err)))
 
+    def set_step_clock(self, buf) -> None:
+        """Following loop launches write their per-step clock into buf (uint64/int64 device tensor), or off."""
+        _lib.check(_lib.lib().td_set_step_clock(self._h, None if buf is None else buf.data_ptr(),
+                                                0 if buf is None else int(buf.numel())), "td_set_step_clock")
+
     def set_timing(self, enable: bool) -> None:
         _lib.check(_lib.lib().td_set_timing(self._h, int(enable)), "td_set_timing")
 
@@ -217,6 +222,15 @@ def decode_step_noalloc(dm: "DeviceModel", max_ctx: int, token_ptr: int, pos: in
     _lib.check(_lib.lib().td_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(w), token_ptr, int(pos),
                                                  ctypes.byref(kvs), _ptr(logits), _ptr(token_out), _ptr(error_out),
                                                  _stream_handle(stream)), "td_decode_step_noalloc")
+
+
+def measure_stream(buf, reps: int = 5, stream=None) -> float:
+    """The stream-read yardstick over a device tensor: GB/s of reps timed read passes."""
+    ms = ctypes.c_float(0.0)
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check(_lib.lib().td_measure_stream(buf.data_ptr(), nbytes, int(reps), ctypes.byref(ms),
+                                            _stream_handle(stream)), "td_measure_stream")
+    return nbytes * reps / (ms.value * 1e-3) / 1e9
 
 
 def gemv(fmt: int, w, s, rows: int, cols: int, x, y, stream=None) -> None:

@@ -33,7 +33,7 @@ TD_NOALLOC_SCRATCH_BYTES = 4 << 20
 EXPORTED = [
     "td_create", "td_decode_step", "td_decode_step_noalloc", "td_decode_loop", "td_forward_block", "td_token_ptr", "td_expert_ids", "td_expert_weights", "td_status", "td_destroy", "td_strerror", "td_last_error",
     "td_plan_partition", "td_plan_check",
-    "td_test_gemv", "td_test_attention", "td_test_rope", "td_test_argmax", "td_set_timing", "td_last_step_ms", "td_trace_bytes", "td_set_trace",
+    "td_test_gemv", "td_test_attention", "td_test_rope", "td_test_argmax", "td_set_timing", "td_last_step_ms", "td_set_step_clock", "td_measure_stream", "td_trace_bytes", "td_set_trace",
 ]
 
 
@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
         L.td_test_rope.argtypes = [vp, i32, i32, i32, f32, vp, vp]
         L.td_test_argmax.restype = i32
         L.td_test_argmax.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+        L.td_set_step_clock.restype = i32
+        L.td_set_step_clock.argtypes = [vp, vp, i32]
+        L.td_measure_stream.restype = i32
+        L.td_measure_stream.argtypes = [vp, ctypes.c_int64, i32, ctypes.POINTER(f32), vp]
         L.td_set_timing.restype = i32
         L.td_set_timing.argtypes = [vp, i32]
         L.td_last_step_ms.restype = f32

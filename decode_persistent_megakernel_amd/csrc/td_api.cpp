@@ -1009,6 +1009,39 @@ void td_destroy(td_ctx* ctx) {
   delete ctx;
 }
 
+int td_set_step_clock(td_ctx* ctx, uint64_t* d_buf, int32_t n) {
+  if (!ctx) return fail(TD_E_INVALID_ARG, "null ctx");
+  if (d_buf && n < 2) return fail(TD_E_INVALID_ARG, "the step clock needs at least 2 entries");
+  ctx->kp.step_clock = d_buf;
+  ctx->kp.step_clock_n = d_buf ? n : 0;
+  return TD_OK;
+}
+
+int td_measure_stream(const void* d_buf, int64_t bytes, int32_t reps, float* ms_out, void* stream) {
+  if (!d_buf || bytes < 16 || (bytes & 15) || ((uintptr_t)d_buf & 15) || reps < 1 || !ms_out)
+    return fail(TD_E_INVALID_ARG, "bad stream-read arguments");
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  int le = td_launch_stream_read(d_buf, bytes, ncu, stream);  // warm-up pass
+  if (le == 0) e = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && le == 0 && e == hipSuccess; ++r) le = td_launch_stream_read(d_buf, bytes, ncu, stream);
+  if (le == 0 && e == hipSuccess) e = hipEventRecord(e1, s);
+  if (le == 0 && e == hipSuccess) e = hipEventSynchronize(e1);
+  if (le == 0 && e == hipSuccess) e = hipEventElapsedTime(ms_out, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (le) return hip_fail((hipError_t)le, "stream-read launch");
+  if (e != hipSuccess) return hip_fail(e, "stream-read timing");
+  return TD_OK;
+}
+
 int td_set_timing(td_ctx* ctx, int32_t enable) {
   if (!ctx) return fail(TD_E_INVALID_ARG, "null ctx");
   if (enable && !ctx->ev0) {

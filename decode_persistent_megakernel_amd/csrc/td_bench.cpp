@@ -26,8 +26,12 @@
 // A workload with a random cache prefix and no prompt times one block of N
 // tokens at the first decode position instead (the shape of a draft verify).
 //
+// --maps FILE writes the process's memory map (/proc/self/maps) to FILE at the
+// end of main, so that addresses in a crash report from the exit-time
+// teardown can be matched to the library they fall in.
+//
 //   td_bench [--config NAME] [--steps K] [--warmup W] [--executor E] [--loop N] [--block N]
-//            [--copy-calibration] [--print-config]
+//            [--copy-calibration] [--print-config] [--maps FILE]
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -146,6 +150,7 @@ int main(int argc, char** argv) {
   std::string name = "llama1b";
   int steps = 128, warmup = 8;
   bool only_config = false, copy_cal = false;
+  std::string maps_path;
   int loop_n = 0, block_n = 0;
   int executor = TD_EXEC_MEGAKERNEL;
   std::string ex_name = "megakernel";
@@ -158,6 +163,7 @@ int main(int argc, char** argv) {
     else if (a == "--copy-calibration") copy_cal = true;
     else if (a == "--loop" && i + 1 < argc) loop_n = atoi(argv[++i]);
     else if (a == "--block" && i + 1 < argc) block_n = atoi(argv[++i]);
+    else if (a == "--maps" && i + 1 < argc) maps_path = argv[++i];
     else if (a == "--executor" && i + 1 < argc) {
       ex_name = argv[++i];
       if (ex_name == "megakernel") executor = TD_EXEC_MEGAKERNEL;
@@ -394,5 +400,15 @@ int main(int argc, char** argv) {
   td_destroy(ctx);
   CK(hipStreamDestroy(stream));
   for (void* p : g_allocs) CK(hipFree(p));
+  if (!maps_path.empty()) {  // the process's mappings at the end of main (which library sits where)
+    FILE* in = fopen("/proc/self/maps", "r");
+    FILE* out = fopen(maps_path.c_str(), "w");
+    if (in && out) {
+      char line[4096];
+      while (fgets(line, sizeof line, in)) fputs(line, out);
+    }
+    if (in) fclose(in);
+    if (out) fclose(out);
+  }
   return 0;
 }

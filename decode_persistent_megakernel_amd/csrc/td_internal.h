@@ -118,6 +118,8 @@ struct td_kparams {
   int32_t n_stages;   // 5 L + 1
   int32_t ring_slots; // S: LDS ring slots per compute wave
   uint64_t* trace;    // optional: [ncu][n_stages][TD_TRACE_STAMPS] 100 MHz timestamps, or null
+  uint64_t* step_clock;  // optional: [step_clock_n] 100 MHz clock: [0] launch start, [s + 1] step s's token decided
+  int32_t step_clock_n;
   // packed weight streams (built at create time)
   const uint8_t* wcode;
   const uint8_t* wscale;
@@ -269,6 +271,7 @@ int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos
 int td_launch_op_layers(const td_opparams* p, void* stream);
 int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int cols, const float* x, float* y,
                         void* stream);
+int td_launch_stream_read(const void* buf, int64_t bytes, int ncu, void* stream);
 int td_launch_test_rope(const float* x, int n_heads, int d, const td_rope_row& row, float* y, void* stream);
 int td_launch_test_argmax(const float* logits, int n, int groups, void* work, int* token, int* nonfinite,
                           void* stream);

@@ -1009,6 +1009,7 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
   }
   const int G = P.group;
   uint32_t tiles_ready = 0, rv_base = 0;
+  if (P.step_clock && cu == 0 && lane == 0) P.step_clock[0] = wall_clock64();
   for (int step = 0;; ++step) {
     const int pos = P.pos + step;
     const AttnTask T = attn_task(P, cu, pos);
@@ -1088,6 +1089,7 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
     lds_st(ctl + TD_CTL_STOP, stop ? 1u : 0u);
     lds_fence();
     lds_st(ctl + TD_CTL_TOKREADY, (uint32_t)step + 1u);
+    if (P.step_clock && cu == 0 && lane == 0 && step + 1 < P.step_clock_n) P.step_clock[step + 1] = wall_clock64();
     if (stop) {
       // every CU has read the epoch: all candidates of this step carry its tag
       if (cu == 0 && lane == 0) {
@@ -1159,6 +1161,37 @@ __global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, u
     ++n;
   }
   if (lane == 0 && (c.seq < P.n_stages || n != W.n_tot || n4 != W.n4)) atomicOr(bad, 1);
+}
+
+// ------------------------------------------------------------ stream-read yardstick
+// Reads `bytes` (a multiple of 16) once with 16-byte non-temporal loads, four
+// in flight per lane, over a grid of 8 workgroups of 512 threads per CU: the
+// HBM read rate the weight stream can hope for on this part ("Decoding in
+// tiles", sec. 2: the measured streaming rate, not the nominal one, is the
+// floor's denominator).  Each lane folds its loaded words into one value that
+// an empty asm statement consumes, so no load is dead.
+__global__ void __launch_bounds__(512) td_stream_read_kernel(const u32x4* p, int64_t n16) {
+  // a workgroup reads 32 KiB contiguous per pass (four 16-byte loads per lane in
+  // flight), the passes strided over the grid; the best of the layouts, grid
+  // sizes and cache policies measured on MI355X (1 workgroup per CU, non-temporal)
+  constexpr int U = 4;
+  const int64_t blk = (int64_t)U * 512;
+  const int64_t gstride = (int64_t)gridDim.x * blk;
+  uint32_t acc = 0;
+  int64_t b = (int64_t)blockIdx.x * blk;
+  for (; b + blk <= n16; b += gstride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(p + b + k * 512 + threadIdx.x);
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  if (b < n16)  // the ragged last block
+    for (int64_t i = b + threadIdx.x; i < n16; i += 512) {
+      const u32x4 a = __builtin_nontemporal_load(p + i);
+      acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+  asm volatile("" ::"v"(acc));  // every lane's folded value is kept, so none of its loads is dead
 }
 
 // ------------------------------------------------------------ test hooks
@@ -1377,6 +1410,11 @@ int td_launch_test_gemv(int fmt, const void* w, const void* s, int rows, int col
   if (e != hipSuccess) return (int)e;
   td_gemv_kernel<<<(rows + 3) / 4, 256, lds, (hipStream_t)stream>>>(fmt, (const uint8_t*)w, (const uint16_t*)s, rows,
                                                                      cols, kpad, x, y);
+  return (int)hipGetLastError();
+}
+
+int td_launch_stream_read(const void* buf, int64_t bytes, int ncu, void* stream) {
+  td_stream_read_kernel<<<ncu, 512, 0, (hipStream_t)stream>>>((const u32x4*)buf, bytes / 16);
   return (int)hipGetLastError();
 }
 

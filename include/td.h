@@ -350,6 +350,24 @@ int td_test_argmax(const float* d_logits, int32_t n, int32_t groups, void* d_wor
 int64_t td_trace_bytes(const td_ctx* ctx);
 int td_set_trace(td_ctx* ctx, void* d_buf, int64_t bytes);
 
+/* Per-step clock of the token loop.  td_set_step_clock(ctx, d_buf, n) makes
+ * every following td_decode_loop (and td_decode_step on the persistent
+ * kernel) write the device's 100 MHz clock into d_buf (device uint64 [n],
+ * caller-owned, n >= 2): [0] when the launch starts, [s + 1] when step s's
+ * greedy token has been decided (on the first CU; every CU decides it from
+ * the same candidates at the same moment), for s + 1 < n.  Step s took
+ * d_buf[s + 1] - d_buf[s] ticks.  d_buf = NULL turns it off. */
+int td_set_step_clock(td_ctx* ctx, uint64_t* d_buf, int32_t n);
+
+/* The stream-read yardstick ("Decoding in tiles", sec. 2: the measured rate
+ * of a plain streaming read, against which a weight-read floor is set): one
+ * warm-up pass and then `reps` timed passes of a kernel that reads `bytes`
+ * (a multiple of 16; d_buf device, 16-byte aligned) with 16-byte
+ * non-temporal loads, one workgroup per CU reading 32 KiB contiguous per
+ * pass.  *ms_out (host) receives the time of the
+ * `reps` passes; the rate is bytes * reps / time.  Synchronises `stream`. */
+int td_measure_stream(const void* d_buf, int64_t bytes, int32_t reps, float* ms_out, void* stream);
+
 /* Measured duration of the last megakernel step (HIP events on the step's own
  * stream), or a negative value when unavailable.  Timing is off unless enabled. */
 int td_set_timing(td_ctx* ctx, int32_t enable);

@@ -125,9 +125,9 @@ void orc_rope(double* v, int32_t d, int32_t pos, double base) {
 /* ---------------------------------------------------------------- attention */
 
 /* Decode attention of one query head over positions 0..n_pos-1 of its K/V head
- * ([tiles] sec. 2: attention is the only cost that grows with the position;
- * [metal] "Flash Attention": one query row attends to the whole cache, no
- * causal mask needed).  Scores q.k / sqrt(d), softmax, weighted sum of V.
+ * ([tiles] sec. 2: of the step's costs only attention depends on the
+ * position; [metal] "Flash Attention": at decode a single query row reads the
+ * whole cache, so no causal mask applies).  Scores q.k / sqrt(d), softmax, weighted sum of V.
  * Plain two-pass softmax: max, then exponentials and their sum. */
 void orc_attention(const double* q, const uint16_t* K, const uint16_t* V, int32_t n_pos,
                    int32_t d, double* out) {

@@ -109,6 +109,16 @@ def test_null_arguments_are_rejected():
     assert L.td_decode_loop(None, None, 0, 4, -1, ctypes.byref(kv), None, None, None, None) == _lib.TD_E_INVALID_ARG
     assert L.td_forward_block(None, None, 4, 0, ctypes.byref(kv), None, 0, None, None) == _lib.TD_E_INVALID_ARG
     assert L.td_status(None, None) == _lib.TD_E_INVALID_ARG
+    assert L.td_set_step_clock(None, None, 0) == _lib.TD_E_INVALID_ARG
+    ms = ctypes.c_float()
+    assert L.td_measure_stream(None, 1 << 20, 1, ctypes.byref(ms), None) == _lib.TD_E_INVALID_ARG
+    # sizes and alignment are checked before any device call (the pointer is never dereferenced)
+    fake = ctypes.c_void_p(1 << 40)
+    assert L.td_measure_stream(fake, 8, 1, ctypes.byref(ms), None) == _lib.TD_E_INVALID_ARG
+    assert L.td_measure_stream(fake, (1 << 20) + 4, 1, ctypes.byref(ms), None) == _lib.TD_E_INVALID_ARG
+    assert L.td_measure_stream(ctypes.c_void_p((1 << 40) + 8), 1 << 20, 1, ctypes.byref(ms), None) == _lib.TD_E_INVALID_ARG
+    assert L.td_measure_stream(fake, 1 << 20, 0, ctypes.byref(ms), None) == _lib.TD_E_INVALID_ARG
+    assert L.td_measure_stream(fake, 1 << 20, 1, None, None) == _lib.TD_E_INVALID_ARG
     L.td_destroy(None)  # a no-op
 
 

@@ -175,3 +175,38 @@ def test_loop_argument_checks(td):
         per_op.loop(tok.data_ptr(), 0, 2, kv, logits)
     assert ei.value.code == _lib.TD_E_UNSUPPORTED
     per_op.close()
+
+
+def test_step_clock_and_stream_yardstick(td):
+    """The measurement hooks: the in-kernel step clock of a loop (one stamp at
+    the launch's start, then one per step decided, none past the buffer), and
+    the stream-read yardstick's rate, between a plausible floor and the
+    device's published 8 TB/s."""
+    cfg, start = SPLITK, 20
+    _say("step clock of a loop launch, and the stream-read yardstick")
+    m, k, v = _setup(td, cfg, start)
+    dm = td.DeviceModel(m)
+    kv = td.KVCache(cfg, cfg.max_ctx, k=k, v=v)
+    dec = td.Decoder(dm, cfg.max_ctx)
+    tok = torch.tensor([int(synth.first_token(cfg))], dtype=torch.int32, device="cuda")
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    for n, slots in ((6, 7), (6, 4)):  # a buffer for every step, then one that holds only three
+        clk = torch.zeros(slots + 2, dtype=torch.int64, device="cuda")
+        dec.set_step_clock(clk[:slots])
+        dec.loop(tok.data_ptr(), start, n, kv, logits)
+        torch.cuda.synchronize()
+        assert dec.status() == 0
+        c = clk.cpu().numpy()
+        assert np.all(c[:slots] > 0) and np.all(np.diff(c[:slots]) > 0), c
+        assert np.all(c[slots:] == 0), c  # nothing past the buffer
+        assert np.all(np.diff(c[:slots]) < 100_000_000), c  # each step well under a second (100 MHz ticks)
+        start += n
+    dec.set_step_clock(None)
+    dec.loop(tok.data_ptr(), start, 2, kv, logits)
+    torch.cuda.synchronize()
+    assert dec.status() == 0 and np.all(clk.cpu().numpy()[:4] == c[:4])  # off: the old buffer is not written
+    dec.close()
+    buf = torch.ones(64 << 20, dtype=torch.int32, device="cuda")  # 256 MiB
+    gbps = td.measure_stream(buf, reps=3)
+    _say(f"stream-read yardstick over 256 MiB: {gbps:.0f} GB/s")
+    assert 500.0 < gbps < 8000.0 * 1.05
