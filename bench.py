@@ -18,7 +18,6 @@ kernel (algorithmic HBM bytes per step / measured kernel time, against the
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,19 +29,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 
 
-KERNEL_SOURCES = ("td_api.cpp", "td_internal.h", "td_kernels.hip")
-
-
 def source_hash() -> str:
     """sha256 (first 16 hex digits) of the sources that define the decode kernel
     and its launch plan; a counter summary taken on other sources is stale."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc")
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from decode_persistent_megakernel_amd.profile import sources_hash
+    return sources_hash()
 
 
 def read_traffic(workload: str, kernel_hash: str):

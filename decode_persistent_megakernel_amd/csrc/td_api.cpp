@@ -4,8 +4,9 @@
 // (which CU and wave owns which rows of every stage, how the attention context
 // is split, where everything sits in LDS), validates it, and allocates the
 // context's scratch.  td_decode_step fills the per-step fields and launches the
-// persistent kernel cooperatively (all workgroups resident at once, which the
-// grid barriers need).
+// persistent kernel cooperatively: every workgroup must be resident at once,
+// since each one spins on values that other workgroups publish (there is no
+// grid barrier; the hand-offs are tagged values in global memory).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
