@@ -148,9 +148,8 @@ def main() -> int:
           file=sys.stderr, flush=True)
     dm = td.DeviceModel(model, device=dev)
     moe = cfg.n_experts > 0
-    # a mixture-of-experts model runs on the graph executor (the routing tensor lets one
-    # recording serve every token); the persistent kernel and its token loop are dense only
-    dec = td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_GRAPH if moe else td.TD_EXEC_MEGAKERNEL)
+    # every model, dense or mixture-of-experts, runs on the persistent kernel and its token loop
+    dec = td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_MEGAKERNEL)
     start = cfg.start_pos
     prefill = None
     if cfg.kv_prefix:
@@ -205,7 +204,7 @@ def main() -> int:
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
     tok_ptr = dec.token_ptr()
     stream = torch.cuda.current_stream()
-    spl = 1 if moe else max(1, min(args.steps_per_launch, td._lib.TD_MAX_LOOP_STEPS))
+    spl = max(1, min(args.steps_per_launch, td._lib.TD_MAX_LOOP_STEPS))
 
     def run(n, record, per_launch=spl, clocks=None):
         """n greedy steps from `first` at positions start.., per_launch steps per
@@ -247,7 +246,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
     n_launch = (n_steps + spl - 1) // spl
-    clocks = None if moe else [torch.zeros(spl + 1, dtype=torch.int64, device=dev) for _ in range(n_launch)]
+    clocks = [torch.zeros(spl + 1, dtype=torch.int64, device=dev) for _ in range(n_launch)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs = run(n_steps, True, clocks=clocks)
@@ -279,7 +278,7 @@ def main() -> int:
         torch.cuda.synchronize()
         raw = tr.cpu().numpy()
         np.save(os.path.splitext(args.trace)[0] + "_raw.npy", raw)
-        summ = tdtrace.summarize(raw, cfg.n_layers)
+        summ = tdtrace.summarize(raw, cfg.n_layers, 6 if moe else 5)
         dec.enable_trace(False)
         with open(args.trace, "w") as f:
             json.dump(summ, f, indent=1)
@@ -301,8 +300,7 @@ def main() -> int:
             baselines["single_step_launch"] = {"tokens_per_s": round(nb / (sms.sum() / 1e3), 2),
                                                "ms_per_step": round(float(sms.mean()), 4), "steps": nb,
                                                "launches_per_step": 1}
-        for name, ex in ((("per_op", td.TD_EXEC_PER_OP),) if moe else
-                         (("per_op", td.TD_EXEC_PER_OP), ("graph", td.TD_EXEC_GRAPH))):
+        for name, ex in (("per_op", td.TD_EXEC_PER_OP), ("graph", td.TD_EXEC_GRAPH)):
             bdec = td.Decoder(dm, cfg.max_ctx, executor=ex)
             bdec.step(first.data_ptr(), start, kv, logits, stream=stream)  # warm-up (and graph capture)
             torch.cuda.synchronize()
@@ -360,10 +358,9 @@ def main() -> int:
                         f"{start}..{start + n_steps - 1}, batch 1",
             "weights": "int4-g64+fp16-scales" if cfg.weight_format else "bf16",
             "arithmetic": "fp32 accumulate, fp32 activations, bf16 K/V cache",
-            "executor": ("hipGraph replay of the per-op launches (router ids in a device tensor), one per token"
-                         if moe else
-                         f"persistent megakernel, up to {spl} greedy steps per cooperative launch (in-kernel token loop)"
-                         if spl > 1 else "persistent megakernel (one cooperative launch per token)"),
+            "executor": ((f"persistent megakernel, up to {spl} greedy steps per cooperative launch (in-kernel token loop)"
+                          if spl > 1 else "persistent megakernel (one cooperative launch per token)")
+                         + (": router, top-k and the chosen experts' rows inside the same launch" if moe else "")),
             "steps_per_launch": sorted({m for _, m, _ in evs}),
             "global_batch": 1,
             "parallelism": "single GPU",
@@ -375,8 +372,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": (f"graph of {7 * cfg.n_layers + 3} per-op kernels (one decode step per replay)" if moe else
-                       "td_megakernel (" + ", ".join(str(m) for m in sorted({m for _, m, _ in evs}))
+            "kernel": ("td_megakernel (" + ", ".join(str(m) for m in sorted({m for _, m, _ in evs}))
                        + " whole decode steps per launch)"),
             "launches": len(evs),
             "algorithmic_bytes_per_launch": int(round(bytes_launch)),

@@ -194,7 +194,8 @@ class Decoder:
             self._trace = None
             return None
         n = int(_lib.lib().td_trace_bytes(self._h))
-        stages = 5 * self.dm.cfg.n_layers + 1
+        c = self.dm.cfg
+        stages = (6 if getattr(c, "n_experts", 0) else 5) * c.n_layers + 1  # a MoE layer adds the router stage
         self._trace = torch.zeros(n // 8, dtype=torch.int64, device=self.dm.device)
         _lib.check(_lib.lib().td_set_trace(self._h, self._trace.data_ptr(), n), "td_set_trace")
         return self._trace.view(-1, stages, 32)

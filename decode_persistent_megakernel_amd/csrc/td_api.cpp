@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -88,15 +90,27 @@ void rope_row(float theta, int d, int pos, float* cs) {
 // unit space s, in proportion to the per-CU weights (all 1 unless a weighting
 // is given), so that every unit has exactly one owner.
 std::vector<int32_t> build_partition(const td_config& c, int ncu, const std::vector<double>& wt) {
+  const int64_t E = c.n_experts > 0 ? c.n_experts : 0, k = E ? c.top_k : 0, I = c.intermediate;
   const int64_t U[TD_NSPACES] = {(int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2, c.hidden,
-                                 c.intermediate, c.vocab};
+                                 I, c.vocab, E, k * I};
   std::vector<double> cum(ncu + 1, 0.0);
   for (int i = 0; i < ncu; ++i) cum[i + 1] = cum[i] + wt[i];
   std::vector<int32_t> part((size_t)TD_NSPACES * (ncu + 1));
-  for (int sp = 0; sp < TD_NSPACES; ++sp)
+  for (int sp = 0; sp < TD_NSPACES; ++sp) {
+    int32_t* t = part.data() + (size_t)sp * (ncu + 1);
+    if (sp == TD_SP_EI && k > 0) {
+      // slot j (the j-th chosen expert's I units) goes to CUs [j ncu / k, (j + 1) ncu / k):
+      // no CU's range crosses a slot, so each wave streams one expert's rows
+      for (int64_t j = 0; j < k; ++j) {
+        const int64_t c0 = j * ncu / k, c1 = (j + 1) * ncu / k;
+        for (int64_t i = c0; i < c1; ++i) t[i] = (int32_t)(j * I + (I * (i - c0)) / (c1 - c0));
+      }
+      t[ncu] = (int32_t)(k * I);
+      continue;
+    }
     for (int i = 0; i <= ncu; ++i)
-      part[(size_t)sp * (ncu + 1) + i] =
-          i == ncu ? (int32_t)U[sp] : (int32_t)std::llround((double)U[sp] * cum[i] / cum[ncu]);
+      t[i] = i == ncu ? (int32_t)U[sp] : (int32_t)std::llround((double)U[sp] * cum[i] / cum[ncu]);
+  }
   return part;
 }
 
@@ -108,10 +122,14 @@ std::vector<int32_t> build_partition(const td_config& c, int ncu, const std::vec
 int validate_plan(const td_config& c, int ncu, const std::vector<int32_t>& part, int own_floats) {
   const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab;
   const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * d;
+  const int E = c.n_experts > 0 ? c.n_experts : 0, k = E ? c.top_k : 0;
+  // the expert gate/up space (kind -1): unit u is slot u / I, rows (gate, up) of
+  // row u % I of the slot's expert, counted here as 2 u and 2 u + 1
   struct St {
     int U, rpu, rows, kind, space;
   } st[] = {{qkv_rows / 2, 2, qkv_rows, TD_ST_QKV, TD_SP_QKV}, {H, 1, H, TD_ST_O, TD_SP_H},
-            {I, 2, 2 * I, TD_ST_GU, TD_SP_I}, {H, 1, H, TD_ST_DOWN, TD_SP_H}, {V, 1, V, TD_ST_HEAD, TD_SP_V}};
+            {I, 2, 2 * I, TD_ST_GU, TD_SP_I}, {H, 1, H, TD_ST_DOWN, TD_SP_H}, {V, 1, V, TD_ST_HEAD, TD_SP_V},
+            {E, 1, E, TD_ST_ROUTER, TD_SP_E}, {k * I, 2, 2 * k * I, -1, TD_SP_EI}};
   for (const St& s : st) {
     std::vector<uint8_t> seen_row(s.rows, 0);
     std::vector<uint8_t> seen_unit(s.U, 0);
@@ -123,6 +141,8 @@ int validate_plan(const td_config& c, int ncu, const std::vector<int32_t>& part,
       if (s.space == TD_SP_H && u1 - u0 > own_floats) return fail(TD_E_PLAN, "residual rows exceed the LDS area");
       if (s.space == TD_SP_QKV && (u1 - u0 + TD_NW - 1) / TD_NW > 64)
         return fail(TD_E_UNSUPPORTED, "more than 64 QKV row pairs per compute wave");
+      if (s.space == TD_SP_EI && u1 > u0 && u0 / I != (u1 - 1) / I)
+        return fail(TD_E_PLAN, "a CU's expert units cross a slot");
       for (int wave = 0; wave < TD_NW; ++wave) {
         for (int u = u0 + wave; u < u1; u += TD_NW) {
           if (seen_unit[u]++) return fail(TD_E_PLAN, "unit owned twice");
@@ -133,6 +153,8 @@ int validate_plan(const td_config& c, int ncu, const std::vector<int32_t>& part,
               row = head * d + i + r * half;
             } else if (s.kind == TD_ST_GU) {
               row = u + r * I;
+            } else if (s.kind == -1) {
+              row = 2 * u + r;
             } else {
               row = u;
             }
@@ -334,7 +356,9 @@ int attention_split(const td_config& c, int ncu, int* chunk_len_out, int* n_chun
   return TD_OK;
 }
 
-int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* part_in, Plan& out) {
+// persistent: the plan is for the persistent kernel (which refuses int4 expert
+// weights); the per-op executors build it for the shapes and the attention split.
+int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* part_in, bool persistent, Plan& out) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
@@ -342,6 +366,10 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
   const int d = c.head_dim, H = c.hidden, I = c.intermediate, L = c.n_layers;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
   const int qd = nq * d;
+  const int E = c.n_experts > 0 ? c.n_experts : 0, topk = E ? c.top_k : 0;
+  if (persistent && E && c.weight_format != TD_WF_BF16)
+    return fail(TD_E_UNSUPPORTED, "the persistent kernel runs mixture-of-experts layers on bf16 weights only");
+  if (E && ncu < topk) return fail(TD_E_UNSUPPORTED, "fewer CUs than experts per token");
 
   int chunk_len = 0, n_chunks_max = 0;
   rc = attention_split(c, ncu, &chunk_len, &n_chunks_max);
@@ -358,13 +386,15 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
   int out_floats = 0;
   for (int i = 0; i < ncu; ++i) {
     auto cnt = [&](int sp) { return part[(size_t)sp * (ncu + 1) + i + 1] - part[(size_t)sp * (ncu + 1) + i]; };
-    out_floats = std::max({out_floats, 2 * cnt(TD_SP_QKV), cnt(TD_SP_H), 2 * cnt(TD_SP_I), cnt(TD_SP_V)});
+    out_floats = std::max({out_floats, 2 * cnt(TD_SP_QKV), cnt(TD_SP_H), 2 * cnt(TD_SP_I), cnt(TD_SP_V), cnt(TD_SP_E),
+                           2 * cnt(TD_SP_EI)});
   }
   out_floats = (int)round_up(std::max(out_floats, 1), 64);
 
   // LDS layout: the rings take what the rest leaves, up to TD_RING_MAX slots per wave
   const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
-  const int64_t kpad = round_up(std::max({H, qd, I}), 2048);
+  // the GEMV input area holds the longest input: a MoE down stage's is top_k slots of I
+  const int64_t kpad = round_up(std::max({H, qd, I, topk * I}), 2048);
   const int64_t xin_bytes = std::max<int64_t>(kpad * 4, A.bytes);
   td_kparams kp{};
   int64_t fixed = 0;
@@ -387,6 +417,8 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
     off += round_up((int64_t)d * 4, 256);
     kp.off_ctl = (int32_t)off;
     off += TD_CTL_WORDS * 4;
+    kp.off_route = (int32_t)off;
+    if (E) off += (TD_MAX_EXPERTS + TD_NW * 2 * TD_MAX_TOPK) * 4;
     fixed = round_up(off, 1024);
     kp.tile_bufs = nb;
     if (nb == 1 || (chunk_len > TD_TILE && (lds_cap - fixed) / per_slot >= TD_RING_MIN2)) break;
@@ -408,6 +440,7 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
     kp.off_out += shift;
     kp.off_rope += shift;
     kp.off_ctl += shift;
+    kp.off_route += shift;
     kp.lds_bytes = (int32_t)(shift + fixed);
   }
   if (kp.lds_bytes > lds_cap) return fail(TD_E_UNSUPPORTED, "LDS layout exceeds the CU's LDS");
@@ -421,21 +454,27 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
 
   uint64_t stream_code_chunks = 0, stream_scale_blocks = 0;
   // every compute wave's packed stream, counted exactly as the kernel walks it:
-  // stages in order (attention has no weights), the wave's units, their rows,
-  // the row's chunks
+  // stages in order (attention has no weights), for a MoE gate/up or down stage
+  // every expert in turn (ne = E), the wave's units, their rows, the row's chunks
   std::vector<td_wstream> ws((size_t)ncu * TD_NW);
   {
     struct St {
-      int space, rpu, K, fmt;
+      int space, rpu, K, fmt, ne;
     };
     std::vector<St> stages;
     for (int l = 0; l < L; ++l) {
-      stages.push_back({TD_SP_QKV, 2, H, c.weight_format});
-      stages.push_back({TD_SP_H, 1, qd, c.weight_format});
-      stages.push_back({TD_SP_I, 2, H, c.weight_format});
-      stages.push_back({TD_SP_H, 1, I, c.weight_format});
+      stages.push_back({TD_SP_QKV, 2, H, c.weight_format, 1});
+      stages.push_back({TD_SP_H, 1, qd, c.weight_format, 1});
+      if (E) {
+        stages.push_back({TD_SP_E, 1, H, TD_WF_BF16, 1});
+        stages.push_back({TD_SP_EI, 2, H, c.weight_format, E});
+        stages.push_back({TD_SP_H, 1, I, c.weight_format, E});
+      } else {
+        stages.push_back({TD_SP_I, 2, H, c.weight_format, 1});
+        stages.push_back({TD_SP_H, 1, I, c.weight_format, 1});
+      }
     }
-    stages.push_back({TD_SP_V, 1, H, TD_WF_BF16});
+    stages.push_back({TD_SP_V, 1, H, TD_WF_BF16, 1});
     uint64_t code = 0, scal = 0;
     for (int cu = 0; cu < ncu; ++cu)
       for (int wave = 0; wave < TD_NW; ++wave) {
@@ -445,7 +484,7 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
           const int cnt = t[cu + 1] - t[cu];
           const int n = cnt > wave ? (cnt - wave + TD_NW - 1) / TD_NW : 0;
           const int row_bytes = st.fmt == TD_WF_BF16 ? st.K * 2 : st.K / 2;
-          const uint64_t ch = (uint64_t)n * st.rpu * ((row_bytes + TD_CHUNK - 1) / TD_CHUNK);
+          const uint64_t ch = (uint64_t)st.ne * n * st.rpu * ((row_bytes + TD_CHUNK - 1) / TD_CHUNK);
           nt += ch;
           if (st.fmt == TD_WF_INT4_G64) n4 += ch;
         }
@@ -498,8 +537,6 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   if (rc) return rc;
   if (executor != TD_EXEC_MEGAKERNEL && executor != TD_EXEC_PER_OP && executor != TD_EXEC_GRAPH)
     return fail(TD_E_INVALID_ARG, "unknown executor");
-  if (cfg->n_experts > 0 && executor == TD_EXEC_MEGAKERNEL)
-    return fail(TD_E_UNSUPPORTED, "a mixture-of-experts config runs on the per-op or graph executor");
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -515,18 +552,19 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
 
   Plan plan;
   rc = build_plan(cfg, ncu, std::min<int64_t>((int64_t)prop.maxSharedMemoryPerMultiProcessor, 160 * 1024), nullptr,
-                  plan);
+                  executor == TD_EXEC_MEGAKERNEL, plan);
   if (rc) return rc;
   td_kparams kp = plan.kp;
-  {
+  if (executor == TD_EXEC_MEGAKERNEL) {
     int blocks = 0;
-    const int oe = td_megakernel_occupancy(cfg->head_dim, cfg->weight_format, kp.lds_bytes, &blocks);
+    const int oe = td_megakernel_occupancy(cfg->head_dim, cfg->weight_format, cfg->n_experts > 0, kp.lds_bytes, &blocks);
     if (oe != 0 || blocks < 1) return fail(TD_E_UNSUPPORTED, "the kernel does not fit one workgroup per CU");
   }
   const td_config& c = *cfg;
   const int d = c.head_dim, H = c.hidden, I = c.intermediate, V = c.vocab, L = c.n_layers;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv;
   const int qd = nq * d, kvd = nkv * d, qkv_rows = qd + 2 * kvd;
+  const int E = c.n_experts > 0 ? c.n_experts : 0, topk = E ? c.top_k : 0;
   const int chunk_len = plan.chunk_len, n_chunks_max = plan.n_chunks_max;
   const std::vector<int32_t>& part = plan.part;
   const std::vector<td_wstream>& ws = plan.ws;
@@ -549,7 +587,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   };
   const size_t o_xmid = take((size_t)H * 8), o_xout = take((size_t)H * 8);
   const size_t o_q = take((size_t)(qd + 2 * kvd) * 8), o_o = take((size_t)qd * 8);
-  const size_t o_act = take((size_t)I * 8);
+  const size_t o_act = take((size_t)std::max(I, topk * I) * 8);
+  const size_t o_rl = take((size_t)(E + 2) * 8);  // pairs [0, E), padded to an even count
+  const size_t o_eid = take((size_t)std::max(L * topk, 1) * 4), o_ew = take((size_t)std::max(L * topk, 1) * 4);
   const size_t o_part = take((size_t)nkv * n_chunks_max * group * (d + 4) * 8);
   const size_t o_cand = take((size_t)ncu * 4 * 8);
   const size_t o_sync = take((size_t)sync_words * 4);
@@ -611,6 +651,20 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   }
   if (e == hipSuccess)
     e = hipMemcpy(base + o_gains + (size_t)(2 * L) * H * 2, w->final_norm, (size_t)H * 2, hipMemcpyDeviceToDevice);
+  if (e == hipSuccess) {
+    // The launch epoch starts at a value of this context's own.  A hand-off
+    // pair's tag is (epoch + step) n_stages + stage + 1, and this context's
+    // scratch may sit where another context's kernels published and polled: a
+    // copy of such a line left in some XCD's L2 must not carry a tag this
+    // context expects, which a common starting epoch of 0 would allow.
+    static std::atomic<uint32_t> n_created{0};
+    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                 ((uint64_t)n_created.fetch_add(1) << 32) ^ (uint64_t)(uintptr_t)ctx;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;  // SplitMix64's output mix
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    const uint32_t epoch0 = (uint32_t)(z ^ (z >> 31));
+    e = hipMemcpy(base + o_sync + (size_t)TD_SY_EPOCH * 4, &epoch0, 4, hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     (void)hipFree(ctx->scratch);
     delete ctx;
@@ -645,12 +699,18 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
   kp.tq = (uint2*)(base + o_q);
   kp.to = (uint2*)(base + o_o);
   kp.tact = (uint2*)(base + o_act);
+  kp.trl = (uint2*)(base + o_rl);
+  kp.expert_ids = E ? (int32_t*)(base + o_eid) : nullptr;
+  kp.expert_w = E ? (float*)(base + o_ew) : nullptr;
   kp.tpart = (uint2*)(base + o_part);
   kp.cand = (uint2*)(base + o_cand);
   kp.sync = (uint32_t*)(base + o_sync);
   kp.token_out = (int32_t*)(base + o_tok);
   kp.err = (int32_t*)(base + o_err);
-  kp.n_stages = 5 * L + 1;
+  kp.E = E;
+  kp.topk = topk;
+  kp.spl = E ? 6 : 5;
+  kp.n_stages = kp.spl * L + 1;
   kp.ws = (const td_wstream*)(base + o_ws);
   kp.part = (const int32_t*)(base + o_ptab);
   kp.gains = (const uint16_t*)(base + o_gains);
@@ -742,9 +802,15 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
 
 const int32_t* td_token_ptr(const td_ctx* ctx) { return ctx ? ctx->kp.token_out : nullptr; }
 
-const int32_t* td_expert_ids(const td_ctx* ctx) { return ctx ? ctx->op.expert_ids : nullptr; }
+const int32_t* td_expert_ids(const td_ctx* ctx) {
+  if (!ctx) return nullptr;
+  return ctx->executor == TD_EXEC_MEGAKERNEL ? ctx->kp.expert_ids : ctx->op.expert_ids;
+}
 
-const float* td_expert_weights(const td_ctx* ctx) { return ctx ? ctx->op.expert_w : nullptr; }
+const float* td_expert_weights(const td_ctx* ctx) {
+  if (!ctx) return nullptr;
+  return ctx->executor == TD_EXEC_MEGAKERNEL ? ctx->kp.expert_w : ctx->op.expert_w;
+}
 
 int td_decode_step(td_ctx* ctx, const int32_t* d_token, int32_t pos, const td_kv* kv, float* d_logits_out,
                    void* stream) {
@@ -1080,7 +1146,7 @@ int td_plan_partition(const td_config* cfg, int32_t ncu, int32_t* part_out, int3
   int rc = check_config(cfg);
   if (rc) return rc;
   if (ncu <= 0 || ncu % 8) return fail(TD_E_UNSUPPORTED, "CU count must be a positive multiple of 8");
-  if (part_len != TD_NSPACES * (ncu + 1)) return fail(TD_E_INVALID_ARG, "part_len must be 4 (ncu + 1)");
+  if (part_len != TD_NSPACES * (ncu + 1)) return fail(TD_E_INVALID_ARG, "part_len must be 6 (ncu + 1)");
   const std::vector<int32_t> part = build_partition(*cfg, ncu, std::vector<double>(ncu, 1.0));
   std::copy(part.begin(), part.end(), part_out);
   return TD_OK;
@@ -1088,9 +1154,9 @@ int td_plan_partition(const td_config* cfg, int32_t ncu, int32_t* part_out, int3
 
 int td_plan_check(const td_config* cfg, int32_t ncu, const int32_t* part, int32_t part_len) {
   if (!cfg) return fail(TD_E_INVALID_ARG, "null config");
-  if (part && part_len != TD_NSPACES * (ncu + 1)) return fail(TD_E_INVALID_ARG, "part_len must be 4 (ncu + 1)");
+  if (part && part_len != TD_NSPACES * (ncu + 1)) return fail(TD_E_INVALID_ARG, "part_len must be 6 (ncu + 1)");
   Plan plan;
-  return build_plan(cfg, ncu, 160 * 1024, part, plan);
+  return build_plan(cfg, ncu, 160 * 1024, part, true, plan);
 }
 
 int td_test_rope(const float* d_x, int32_t n_heads, int32_t head_dim, int32_t pos, float rope_theta, float* d_out,

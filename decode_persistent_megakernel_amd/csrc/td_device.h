@@ -8,6 +8,7 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include "td.h"
 #include "td_internal.h"
 
 namespace {
@@ -339,5 +340,63 @@ DEV f32x4 attn_merge(f32x4 acc, float m, float l, const float* mb, int n, float*
   return o;
 }
 
+// ------------------------------------------------------------ MoE routing
+// moe_select (one wave): the router's choice from the E logits zs (LDS,
+// padded with -inf to a multiple of 4).  The topk largest logits in decreasing
+// order, the lower id first among equals: expert e takes slot rank(e), the
+// number of experts with a larger logit or an equal one and a lower id, if that
+// is below topk.  Their softmax probabilities over all E experts (max
+// subtracted, the sum reduced in a fixed lane order) go to wts.  A non-finite
+// logit gives ids 0 .. topk - 1 with weight 0 (every later read stays in
+// bounds) and returns true.  Every caller computes the same bits from the same
+// logits.
+DEV bool moe_select(int E, int topk, const float* zs, int32_t* ids, float* wts) {
+  constexpr int PER = TD_MAX_EXPERTS / 64;
+  const int lane = lane_id();
+  float z[PER];
+  float m = -__builtin_inff();
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    z[i] = zs[e];
+    if (e < E && !isfinite(z[i])) bad = 1;
+    if (e < E) m = fmaxf(m, z[i]);
+  }
+  bad = __any(bad);
+  m = wave_max(m);
+  float ssum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < E) ssum += expf(z[i] - m);
+  ssum = wave_sum(ssum);
+  if (bad) {
+    if (lane < topk) {
+      ids[lane] = lane;
+      wts[lane] = 0.f;
+    }
+    return true;
+  }
+  const int E4 = (E + 3) & ~3;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (64 * i >= E) break;
+    const int e = lane + 64 * i;
+    int rank = 0;
+    for (int c = 0; c < E4; c += 4) {  // the same address in every lane: a broadcast read
+      const f32x4 q = *(const f32x4*)(zs + c);
+      rank += (q.x > z[i] || (q.x == z[i] && c < e)) + (q.y > z[i] || (q.y == z[i] && c + 1 < e)) +
+              (q.z > z[i] || (q.z == z[i] && c + 2 < e)) + (q.w > z[i] || (q.w == z[i] && c + 3 < e));
+    }
+    if (e < E && rank < topk) {
+      ids[rank] = e;
+      wts[rank] = expf(z[i] - m) / ssum;
+    }
+  }
+  return false;
+}
+
+
 }  // namespace
+
 #endif

@@ -19,11 +19,16 @@
 #define TD_RING_MAX 24
 #endif
 
-// stage kinds, in layer order; the head follows the last layer
-enum { TD_ST_QKV = 0, TD_ST_ATTN = 1, TD_ST_O = 2, TD_ST_GU = 3, TD_ST_DOWN = 4, TD_ST_HEAD = 5 };
+// stage kinds.  A dense layer runs QKV, ATTN, O, GU, DOWN; a mixture-of-experts
+// layer runs QKV, ATTN, O, ROUTER, GU, DOWN (GU and DOWN then on the experts the
+// router chose); the head follows the last layer
+enum { TD_ST_QKV = 0, TD_ST_ATTN = 1, TD_ST_O = 2, TD_ST_GU = 3, TD_ST_DOWN = 4, TD_ST_HEAD = 5, TD_ST_ROUTER = 6 };
 
-// unit spaces of the partition table: which units of a GEMV stage each CU owns
-enum { TD_SP_QKV = 0, TD_SP_H = 1, TD_SP_I = 2, TD_SP_V = 3, TD_NSPACES = 4 };
+// unit spaces of the partition table: which units of a GEMV stage each CU owns.
+// TD_SP_E: the router's rows (one per expert); TD_SP_EI: the expert gate/up
+// units, top_k slots of I, a CU's range inside one slot.  Both are empty for a
+// dense config.
+enum { TD_SP_QKV = 0, TD_SP_H = 1, TD_SP_I = 2, TD_SP_V = 3, TD_SP_E = 4, TD_SP_EI = 5, TD_NSPACES = 6 };
 
 // error bits of the device error word
 enum { TD_ERRBIT_NONFINITE = 1, TD_ERRBIT_RANGE = 2, TD_ERRBIT_TIMEOUT = 4 };
@@ -75,6 +80,8 @@ struct td_kparams {
   int32_t L, H, nq, nkv, d, I, V, max_ctx, wf, has_bias;
   int32_t qd, kvd, qkv_rows, group;
   float eps, attn_scale;
+  int32_t E, topk;  // MoE: experts and experts per token (E = 0: dense MLP)
+  int32_t spl;      // stages per layer: 5 (dense) or 6 (MoE: with ROUTER)
   // attention split
   int32_t chunk_len, n_chunks_max;
   // steps: n_steps greedy steps at positions pos, pos + 1, ... in one launch,
@@ -102,7 +109,10 @@ struct td_kparams {
   uint2* tq;       // [nkv][(group + 2) d]: per kv head its rotated queries, then this
                    // position's K row (rotated) and V row (bf16 values)
   uint2* to;       // [nq d] attention output
-  uint2* tact;     // [I] SiLU(gate) * up
+  uint2* tact;     // [I] SiLU(gate) * up; MoE: [topk][I], slot j from the j-th chosen expert
+  uint2* trl;      // MoE: [E] router logits (then -inf at [E] when E is odd: read in pairs)
+  int32_t* expert_ids;  // MoE: [L][topk] the chosen experts of the last step (written by CU 0)
+  float* expert_w;      // MoE: [L][topk] their router probabilities
   uint2* tpart;    // [nkv][group][n_chunks_max][d + 4] attention partials: acc[d], m, l, pad
   uint2* cand;     // [ncu][4] pairs: a CU's greedy candidate (value bits, index, nonfinite, 0)
   uint32_t* sync;
@@ -113,9 +123,11 @@ struct td_kparams {
   const uint16_t* biases;  // ctx copy of the QKV biases, bf16 [L][qkv_rows], or null
   // LDS layout (byte offsets into dynamic shared memory)
   int32_t off_ring, off_sring, off_xin, off_attn, off_tile, off_own, off_out, off_rope, off_ctl;
+  int32_t off_route;  // MoE: router logits [TD_MAX_EXPERTS] floats, then per compute wave its choice
+                      // (ids [TD_MAX_TOPK], weights [TD_MAX_TOPK]); 0 for a dense config
   int32_t tile_bufs, tile_stride;  // attention K/V tile buffers (1 or 2) and their spacing in bytes
   int32_t lds_bytes;
-  int32_t n_stages;   // 5 L + 1
+  int32_t n_stages;   // spl L + 1
   int32_t ring_slots; // S: LDS ring slots per compute wave
   uint64_t* trace;    // optional: [ncu][n_stages][TD_TRACE_STAMPS] 100 MHz timestamps, or null
   uint64_t* step_clock;  // optional: [step_clock_n] 100 MHz clock: [0] launch start, [s + 1] step s's token decided
@@ -251,7 +263,7 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
                     int32_t* argmax_out, void* stream);
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
                      void* stream);
-int td_megakernel_occupancy(int head_dim, int weight_format, int lds_bytes, int* blocks_per_cu);
+int td_megakernel_occupancy(int head_dim, int weight_format, int moe, int lds_bytes, int* blocks_per_cu);
 // per-op executor (td_ops.hip)
 int td_op_head_blocks(const td_opparams* p);
 // the no-allocation step (td_ops.hip): the device's copy of the file-scope

@@ -48,26 +48,42 @@ namespace {
 // a CU's units over its compute waves.  A unit is the set of rows one epilogue
 // needs together: the two rows of a RoPE pair (i, i + d/2) of one head for QKV,
 // the gate and up rows of one intermediate index for GU, one row otherwise.
+// In a mixture-of-experts layer the GU units are top_k slots of I (slot j runs
+// the j-th chosen expert), a DOWN unit's row is summed over the slots, and the
+// packed stream holds every expert's rows of the wave's units (ne = E blocks,
+// estride bytes apart in the stacked weights): the wave streams the blocks of
+// the experts the router chose ("One launch per token", its 64-expert MoE
+// section: the expert weights are gathered by id inside the same launch).
 struct Gemv {
   const uint8_t* w;
   const uint16_t* s;
-  int K, row_bytes, J, U, rpu, kind, fmt, space;
+  int K, row_bytes, J, U, rpu, kind, fmt, space, ne;
+  size_t estride;
 };
 
+template <bool MOE>
 DEV void stage_of(const td_kparams& P, int seq, int& kind, int& layer) {
-  if (seq >= 5 * P.L) {
+  constexpr int spl = MOE ? 6 : 5;
+  if (seq >= spl * P.L) {
     kind = TD_ST_HEAD;
     layer = P.L;
   } else {
-    layer = seq / 5;
-    kind = seq - layer * 5;
+    layer = seq / spl;
+    const int k = seq - layer * spl;
+    kind = !MOE || k < 3 ? k : k == 3 ? TD_ST_ROUTER : k - 1;  // MoE: 3 ROUTER, 4 GU, 5 DOWN
   }
+}
+DEV void stage_of_any(const td_kparams& P, int seq, int& kind, int& layer) {
+  if (P.E) stage_of<true>(P, seq, kind, layer);
+  else stage_of<false>(P, seq, kind, layer);
 }
 
 DEV Gemv gemv_of(const td_kparams& P, int kind, int layer) {
   Gemv g;
   g.kind = kind;
   g.s = nullptr;
+  g.ne = 1;
+  g.estride = 0;
   if (kind == TD_ST_HEAD) {
     g.w = (const uint8_t*)P.head;
     g.K = P.H;
@@ -75,6 +91,13 @@ DEV Gemv gemv_of(const td_kparams& P, int kind, int layer) {
     g.rpu = 1;
     g.fmt = 0;
     g.space = TD_SP_V;
+  } else if (kind == TD_ST_ROUTER) {  // bf16 [E][H]
+    g.w = (const uint8_t*)P.layers[layer].router;
+    g.K = P.H;
+    g.U = P.E;
+    g.rpu = 1;
+    g.fmt = 0;
+    g.space = TD_SP_E;
   } else {
     const td_layer_dev& Ld = P.layers[layer];
     int idx = kind == TD_ST_QKV ? 0 : kind == TD_ST_O ? 1 : kind == TD_ST_GU ? 2 : 3;
@@ -83,11 +106,15 @@ DEV Gemv gemv_of(const td_kparams& P, int kind, int layer) {
     g.fmt = P.wf;
     if (kind == TD_ST_QKV) { g.K = P.H; g.U = P.qkv_rows / 2; g.rpu = 2; g.space = TD_SP_QKV; }
     else if (kind == TD_ST_O) { g.K = P.qd; g.U = P.H; g.rpu = 1; g.space = TD_SP_H; }
-    else if (kind == TD_ST_GU) { g.K = P.H; g.U = P.I; g.rpu = 2; g.space = TD_SP_I; }
+    else if (kind == TD_ST_GU) { g.K = P.H; g.U = P.E ? P.topk * P.I : P.I; g.rpu = 2; g.space = P.E ? TD_SP_EI : TD_SP_I; }
     else { g.K = P.I; g.U = P.H; g.rpu = 1; g.space = TD_SP_H; }
   }
   g.row_bytes = g.fmt == 0 ? g.K * 2 : g.K / 2;
   g.J = (g.row_bytes + TD_CHUNK - 1) / TD_CHUNK;
+  if (P.E && (kind == TD_ST_GU || kind == TD_ST_DOWN)) {  // all experts, stacked [E][rows][K]
+    g.ne = P.E;
+    g.estride = (size_t)(kind == TD_ST_GU ? 2 * P.I : P.H) * g.row_bytes;
+  }
   return g;
 }
 
@@ -96,15 +123,17 @@ DEV Gemv gemv_of(const td_kparams& P, int kind, int layer) {
 struct Shape {
   int J, rpu, fmt, space;
 };
+template <bool MOE>
 DEV Shape shape_of(const td_kparams& P, int kind) {
   Shape h;
   int K;
   if (kind == TD_ST_HEAD) { K = P.H; h.rpu = 1; h.fmt = 0; h.space = TD_SP_V; }
+  else if (kind == TD_ST_ROUTER) { K = P.H; h.rpu = 1; h.fmt = 0; h.space = TD_SP_E; }
   else {
     h.fmt = P.wf;
     if (kind == TD_ST_QKV) { K = P.H; h.rpu = 2; h.space = TD_SP_QKV; }
     else if (kind == TD_ST_O) { K = P.qd; h.rpu = 1; h.space = TD_SP_H; }
-    else if (kind == TD_ST_GU) { K = P.H; h.rpu = 2; h.space = TD_SP_I; }
+    else if (kind == TD_ST_GU) { K = P.H; h.rpu = 2; h.space = MOE ? TD_SP_EI : TD_SP_I; }
     else { K = P.I; h.rpu = 1; h.space = TD_SP_H; }
   }
   const int row_bytes = h.fmt == 0 ? K * 2 : K / 2;
@@ -119,7 +148,7 @@ DEV int unit_row(const td_kparams& P, int kind, int u, int r) {
     int i = u - head * half;
     return head * P.d + i + r * half;
   }
-  if (kind == TD_ST_GU) return u + r * P.I;
+  if (kind == TD_ST_GU) return (P.E ? u % P.I : u) + r * P.I;  // MoE: row u % I of slot u / I's expert
   return u;
 }
 
@@ -135,13 +164,13 @@ DEV int wave_units(int cnt, int wave) { return cnt > wave ? (cnt - wave + TD_NW 
 struct Cursor {
   int seq;  // stage sequence number; == n_stages when done
   Gemv g;
-  int u_first, n, k, r, j;
+  int u_first, n, e, k, r, j;
 };
 
 DEV void cur_enter(Cursor& c, const td_kparams& P, int wave, int cu, int ncu, int seq) {
   for (; seq < P.n_stages; ++seq) {
     int kind, layer;
-    stage_of(P, seq, kind, layer);
+    stage_of_any(P, seq, kind, layer);
     if (kind == TD_ST_ATTN) continue;
     Gemv g = gemv_of(P, kind, layer);
     int u0, u1;
@@ -152,7 +181,7 @@ DEV void cur_enter(Cursor& c, const td_kparams& P, int wave, int cu, int ncu, in
     c.g = g;
     c.u_first = u0 + wave;
     c.n = n;
-    c.k = c.r = c.j = 0;
+    c.e = c.k = c.r = c.j = 0;
     return;
   }
   c.seq = P.n_stages;
@@ -164,6 +193,8 @@ DEV void cur_next(Cursor& c, const td_kparams& P, int wave, int cu, int ncu) {
   if (++c.r < c.g.rpu) return;
   c.r = 0;
   if (++c.k < c.n) return;
+  c.k = 0;
+  if (++c.e < c.g.ne) return;
   cur_enter(c, P, wave, cu, ncu, c.seq + 1);
 }
 
@@ -386,10 +417,29 @@ struct CState {
   uint32_t t;                  // chunks consumed
   int slot;                    // ring slot of chunk t
   uint32_t nrv;                // rendezvous passed
+  // The stream in consumption order is a sequence of runs of contiguous
+  // chunks; the chunk issued next belongs to the run that ends before chunk
+  // run_end.  A dense model's step is one run.  A MoE layer is three kinds of
+  // run: its fixed part (QKV, O, router rows), then the gate/up block of the
+  // expert in this CU's slot and the down blocks of the chosen experts in slot
+  // order, which can be issued only once the wave has that layer's routing.
+  uint32_t run_end;
+  int rl, rp;                  // MoE: layer and phase of the current run (0 fixed, 1 gate/up, 2 + j down slot j)
+  int route_layer;             // MoE: the layer whose routing this wave holds (-1: none yet in this step)
+  int ids_v;                   // MoE: lane j < top_k: the j-th chosen expert
+  float wts_v;                 //      and its router probability
+  uint32_t m_fixed, m_gu, m_down, m_head, m_stride, m_slot;  // MoE: run lengths (chunks), layer stride, GU slot
+  float inv_mlp;               // MoE: the MLP RMSNorm factor of the layer (the router stage computes it)
   bool ok;
   int ranges;                  // lane 2 s: this CU's first unit of unit space s; lane 2 s + 1: its count
   DEV int unit_lo(int sp) const { return __builtin_amdgcn_readlane(ranges, 2 * sp); }
   DEV int unit_n(int sp) const { return __builtin_amdgcn_readlane(ranges, 2 * sp + 1); }
+};
+// The state's type says whether the model has MoE layers, so that a dense
+// model's kernel is compiled without the routed-run logic on its chunk path.
+template <bool M>
+struct CStateT : CState {
+  static constexpr bool kMoe = M;
 };
 
 // loads of chunks [a, b): an int4 chunk is two (its codes and its scales)
@@ -453,12 +503,45 @@ DEV void issue_chunk(const td_kparams& P, CState& C) {
   ++C.issued;
   C.islot = C.islot + 1 == P.ring_slots ? 0 : C.islot + 1;
 }
-DEV bool ring_room(const td_kparams& P, const CState& C) {
-  return C.issued < C.n_tot && C.issued < C.t + (uint32_t)P.ring_slots;
+// MoE: moves the issue position to the next non-empty run; false (and no
+// change) if that run needs routing the wave does not have yet.
+DEV bool run_advance(const td_kparams& P, CState& C) {
+  if (!P.E) return false;
+#pragma unroll 1
+  for (;;) {
+    int l = C.rl, p = C.rp + 1;
+    if (p > 1 + P.topk) {
+      ++l;
+      p = 0;
+    }
+    if (l > P.L) return false;
+    size_t off = (size_t)l * C.m_stride;
+    uint32_t len;
+    if (p == 0) {
+      len = l < P.L ? C.m_fixed : C.m_head;
+    } else {
+      len = p == 1 ? C.m_gu : C.m_down;
+      if (len && C.route_layer != l) return false;
+      if (p == 1) off += C.m_fixed + (uint32_t)__builtin_amdgcn_readlane(C.ids_v, (int)C.m_slot) * C.m_gu;
+      else off += C.m_fixed + (size_t)P.E * C.m_gu + (uint32_t)__builtin_amdgcn_readlane(C.ids_v, p - 2) * C.m_down;
+    }
+    C.rl = l;
+    C.rp = p;
+    C.fbase = C.fbase0 + off * TD_CHUNK;
+    C.run_end = C.issued + len;
+    if (len) return true;
+  }
+}
+template <class CS>
+DEV bool ring_room(const td_kparams& P, CS& C) {
+  if (C.issued >= C.n_tot || C.issued >= C.t + (uint32_t)P.ring_slots) return false;
+  if constexpr (CS::kMoe) return C.issued < C.run_end || run_advance(P, C);
+  return true;
 }
 // After a chunk is consumed: one more chunk in flight if its slot is free, first
 // waiting (only if needed) until at most TD_FLIGHT - 1 chunks are outstanding.
-DEV void refill(const td_kparams& P, CState& C) {
+template <class CS>
+DEV void refill(const td_kparams& P, CS& C) {
   if (!ring_room(P, C)) return;
   if (C.issued - C.lk >= TD_FLIGHT) {
     wait_older_than(C, C.issued - (TD_FLIGHT - 1));
@@ -469,19 +552,22 @@ DEV void refill(const td_kparams& P, CState& C) {
 // During a wait: up to TD_FLIGHT more chunks into free slots, without waiting
 // (so up to 2 TD_FLIGHT chunks can be in flight for a while; the waits below
 // count loads, not an assumed depth).
-DEV void topup(const td_kparams& P, CState& C) {
+template <class CS>
+DEV void topup(const td_kparams& P, CS& C) {
 #pragma unroll 1
   for (int k = 0; k < TD_FLIGHT && ring_room(P, C); ++k) issue_chunk(P, C);
 }
 // The next chunk of the stream, once it is in LDS.
-DEV const uint8_t* chunk_wait(CState& C) {
+template <class CS>
+DEV const uint8_t* chunk_wait(CS& C) {
   if (C.t >= C.lk) {
     wait_older_than(C, C.t + 1);
     C.lk = C.t + 1;
   }
   return C.ring + C.slot * TD_CHUNK;
 }
-DEV void chunk_release(const td_kparams& P, CState& C) {
+template <class CS>
+DEV void chunk_release(const td_kparams& P, CS& C) {
   lds_fence();  // the slot has been read out
   ++C.t;
   C.slot = C.slot + 1 == P.ring_slots ? 0 : C.slot + 1;
@@ -499,8 +585,8 @@ DEV void chunk_release(const td_kparams& P, CState& C) {
 // stays short, so the next round's loads come back sooner: for a poll on the
 // critical path of only a few CUs, whose streaming is not worth the delay.
 // false: the wait timed out (or another wait did).
-template <int W, bool TOPUP = true>
-DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CState& C) {
+template <int W, bool TOPUP = true, class CS>
+DEV bool poll_pairs(const td_kparams& P, const uint2* src, int lo, int hi, uint32_t tag, float* dst, CS& C) {
   const int lane = lane_id();
   const int nu = (hi - lo) >> 1;
   if (nu <= 0) {
@@ -554,18 +640,18 @@ DEV void rendezvous(const td_kparams& P, CState& C) {
 // One row of the current stage: J chunks of the stream against xin.  The
 // format is a template parameter so that each chunk loop is compiled for one
 // format only: every instruction in it is paid once per KiB streamed.
-template <int FMT>
-DEV float gemv_row(const td_kparams& P, CState& C, int J) {
+template <int FMT, class CS>
+DEV float gemv_row(const td_kparams& P, CS& C, int J, const float* x) {
   const int lane = lane_id();
   float acc = 0.f;
   for (int j = 0; j < J; ++j) {
     const uint8_t* ch = chunk_wait(C);
     const u32x4 w = *(const u32x4*)(ch + lane * 16);
     if (FMT == 0) {
-      acc += dot_bf16(w, C.xin + j * 512 + lane * 8);
+      acc += dot_bf16(w, x + j * 512 + lane * 8);
     } else {
       const uint2 sc = int4_lane_scales(C.sring + C.slot * TD_SCHUNK, lane);
-      acc += dot_int4(w, C.xin + j * 2048, lane, sc);
+      acc += dot_int4(w, x + j * 2048, lane, sc);
     }
     chunk_release(P, C);
   }
@@ -574,16 +660,16 @@ DEV float gemv_row(const td_kparams& P, CState& C, int J) {
 
 // The rows of a wave's n units (rpu rows each), their dot products to the LDS
 // output area; `first` gets the time the first chunk was in LDS (when tracing).
-template <int FMT>
-DEV void gemv_rows(const td_kparams& P, CState& C, const Shape& g, int n, int wave, uint64_t& first) {
+template <int FMT, class CS>
+DEV void gemv_rows(const td_kparams& P, CS& C, const Shape& g, int n, int wave, uint64_t& first) {
   if (P.trace && n > 0) {
     (void)chunk_wait(C);
     first = wall_clock64();
   }
   for (int k = 0; k < n; ++k) {
     const int idx = wave + k * TD_NW;  // u - u0
-    const float r0 = gemv_row<FMT>(P, C, g.J);
-    const float r1 = g.rpu == 2 ? gemv_row<FMT>(P, C, g.J) : 0.f;
+    const float r0 = gemv_row<FMT>(P, C, g.J, C.xin);
+    const float r1 = g.rpu == 2 ? gemv_row<FMT>(P, C, g.J, C.xin) : 0.f;
     if (lane_id() == 0) {
       C.out[idx * g.rpu] = r0;
       if (g.rpu == 2) C.out[idx * 2 + 1] = r1;
@@ -591,11 +677,56 @@ DEV void gemv_rows(const td_kparams& P, CState& C, const Shape& g, int n, int wa
   }
 }
 
+// The MoE down stage of a wave's n units: for each slot j in order, the rows of
+// the j-th chosen expert against slot j's activations (xin + j I), the dot
+// products summed with the slot's router probability as y = fma(w_j, d_j, y)
+// from y = 0 (the per-op executor's order, so the bits agree).
+template <int FMT, class CS>
+DEV void moe_down_rows(const td_kparams& P, CS& C, const Shape& g, int n, int wave, uint64_t& first) {
+  if (P.trace && n > 0) {
+    (void)chunk_wait(C);
+    first = wall_clock64();
+  }
+  for (int j = 0; j < P.topk; ++j) {
+    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(C.wts_v), j));
+    const float* xj = C.xin + (size_t)j * P.I;
+    for (int k = 0; k < n; ++k) {
+      const int idx = wave + k * TD_NW;
+      const float dk = gemv_row<FMT>(P, C, g.J, xj);
+      if (lane_id() == 0) C.out[idx] = fmaf(wj, dk, j == 0 ? 0.f : C.out[idx]);
+    }
+  }
+}
+
+// The wave's routing of a MoE layer from the staged router logits: its own
+// moe_select (every wave computes the same bits), kept one expert per lane;
+// CU 0's wave 0 reports it (expert ids and weights of the layer) and raises the
+// error bit on a non-finite router logit.
+DEV void moe_route(const td_kparams& P, CState& C, uint8_t* lds, int wave, int layer) {
+  const float* zs = (const float*)(lds + P.off_route);
+  int32_t* ids = (int32_t*)(lds + P.off_route + TD_MAX_EXPERTS * 4) + wave * 2 * TD_MAX_TOPK;
+  float* wts = (float*)(ids + TD_MAX_TOPK);
+  const bool bad = moe_select(P.E, P.topk, zs, ids, wts);
+  lds_fence();
+  const int lane = lane_id();
+  C.ids_v = lane < P.topk ? ids[lane] : 0;
+  C.wts_v = lane < P.topk ? wts[lane] : 0.f;
+  C.route_layer = layer;
+  if (blockIdx.x == 0 && wave == 0) {
+    if (lane < P.topk) {
+      P.expert_ids[layer * P.topk + lane] = C.ids_v;
+      P.expert_w[layer * P.topk + lane] = C.wts_v;
+    }
+    if (bad && lane == 0) atomicOr(P.err, TD_ERRBIT_NONFINITE);
+  }
+}
+
 // Input slice of a GEMV stage into xin: the published vector (polled), or the
 // bf16 embedding row for the first layer.  With gains (the RMSNorm stages) the
 // slice's sum of squares goes to the control block and the slice is multiplied
 // by the gains.  The last wave zeroes the tail up to the chunk multiple.
-DEV void stage_gemv_input(const td_kparams& P, CState& C, int wave, int kind, int K, const uint2* src,
+template <class CS>
+DEV void stage_gemv_input(const td_kparams& P, CS& C, int wave, int kind, int K, const uint2* src,
                           const uint16_t* erow, uint32_t tag, uint32_t g0, uint32_t g1, uint32_t g2, uint32_t g3,
                           const uint16_t* gain) {
   int lo, hi;
@@ -645,15 +776,26 @@ DEV void stage_gemv_input(const td_kparams& P, CState& C, int wave, int kind, in
 // lane, with every store of the stage issued after its last row: a store
 // counts among the wave's outstanding loads, so a store issued between rows
 // would make every following chunk wait for it.
-template <int WF>
-DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer, int pos, uint32_t tag, float inv,
+template <int WF, class CS>
+DEV void gemv_wave(const td_kparams& P, CS& C, int wave, int kind, int layer, int pos, uint32_t tag, float inv,
                    float bias_a, float bias_b, uint64_t& first) {
   const int lane = lane_id();
-  const Shape g = shape_of(P, kind);
+  const Shape g = shape_of<CS::kMoe>(P, kind);
   const int u0 = C.unit_lo(g.space), u1 = C.unit_lo(g.space) + C.unit_n(g.space);
   const int n = wave_units(u1 - u0, wave);
-  if (WF == TD_WF_BF16 || kind == TD_ST_HEAD) gemv_rows<TD_WF_BF16>(P, C, g, n, wave, first);
-  else gemv_rows<TD_WF_INT4_G64>(P, C, g, n, wave, first);
+  bool routed = false;
+  if constexpr (CS::kMoe) {  // the MoE down stage sums over the slots (bf16 only)
+    if (kind == TD_ST_DOWN) {
+      moe_down_rows<TD_WF_BF16>(P, C, g, n, wave, first);
+      routed = true;
+    }
+  }
+  if (routed) {
+  } else if (WF == TD_WF_BF16 || kind == TD_ST_HEAD || kind == TD_ST_ROUTER) {
+    gemv_rows<TD_WF_BF16>(P, C, g, n, wave, first);
+  } else {
+    gemv_rows<TD_WF_INT4_G64>(P, C, g, n, wave, first);
+  }
   lds_fence();
   float bv = -__builtin_inff();
   int bi = 0x7fffffff, bad = 0;
@@ -694,9 +836,13 @@ DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer
       const float v = C.own[idx] + C.out[idx];
       C.own[idx] = v;
       st_tag((kind == TD_ST_O ? P.tx_mid : P.tx_out) + u, v, tag);
-    } else if (kind == TD_ST_GU) {
+    } else if (kind == TD_ST_GU) {  // MoE: u is slot u / I's unit
       const float gt = C.out[2 * idx] * inv, up = C.out[2 * idx + 1] * inv;
       st_tag(P.tact + u, gt / (1.0f + expf(-gt)) * up, tag);
+    } else if (kind == TD_ST_ROUTER) {
+      st_tag(P.trl + u, C.out[idx] * inv, tag);
+      // an odd expert count: the logits are read in pairs, the last one padded with -inf
+      if ((P.E & 1) && u == P.E - 1) st_tag(P.trl + P.E, -__builtin_inff(), tag);
     } else {  // HEAD
       const float v = C.out[idx] * inv;
       P.logits[u] = v;
@@ -722,8 +868,8 @@ DEV void gemv_wave(const td_kparams& P, CState& C, int wave, int kind, int layer
 // then either its partial (chunk c > 0) or, on the chunk-0 CU, the merge of all
 // chunks' partials of its head, o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
 // (the chunks summed in chunk order), published.
-template <int D>
-DEV void attn_wave_d(const td_kparams& P, CState& C, uint8_t* lds, int h, const AttnTask& T, uint32_t tag,
+template <int D, class CS>
+DEV void attn_wave_d(const td_kparams& P, CS& C, uint8_t* lds, int h, const AttnTask& T, uint32_t tag,
                      uint32_t& tiles_seen, uint64_t& first) {
   const int lane = lane_id();
   const int G = P.group;
@@ -785,17 +931,24 @@ DEV void trace_rec(const td_kparams& P, int wave, int seq, uint64_t t0, uint64_t
 }
 
 // The wave's stream from its first chunk (ring slots and their order carry on).
-DEV void stream_start(CState& C) {
+template <class CS>
+DEV void stream_start(const td_kparams& P, CS& C) {
   C.fbase = C.fbase0;
   C.sbase = C.sbase0;
   C.issued = C.t = C.lk = 0;
+  if constexpr (CS::kMoe) {  // the first layer's fixed run; routing comes with each layer
+    C.run_end = C.m_fixed;
+    C.rl = C.rp = 0;
+    C.route_layer = -1;
+  }
 }
 
 // Spins until the LDS word *p reaches `target`, topping the weight ring up
 // meanwhile (the next step's first chunks stream while its token is decided).
 // The word is read as a wave-uniform value: the loop must not look divergent
 // to the compiler, or the ring state it updates would leave scalar registers.
-DEV uint32_t lds_wait_ge_topup(const td_kparams& P, CState& C, const uint32_t* p, uint32_t target) {
+template <class CS>
+DEV uint32_t lds_wait_ge_topup(const td_kparams& P, CS& C, const uint32_t* p, uint32_t target) {
   uint32_t v = (uint32_t)uni((int)lds_ld(p));
   if (v < target) {
     const uint64_t t0 = wall_clock64();
@@ -815,11 +968,11 @@ DEV uint32_t lds_wait_ge_topup(const td_kparams& P, CState& C, const uint32_t* p
   return v;
 }
 
-template <int D, int WF>
+template <int D, int WF, bool MOE>
 DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
-  CState C;
+  CStateT<MOE> C;
   C.lds = lds;
   C.ctl = (uint32_t*)(lds + P.off_ctl);
   C.xin = (float*)(lds + P.off_xin);
@@ -834,11 +987,6 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
     C.n_tot = W.n_tot;
     C.n4 = WF == TD_WF_BF16 ? 0u : W.n4;  // a constant 0 for bf16 models
   }
-  stream_start(C);
-  C.islot = C.slot = 0;
-  C.nrv = 0;
-  C.ok = true;
-  topup(P, C);  // the stream starts right away
   {
     C.ranges = 0;
     if (lane < 2 * TD_NSPACES) {
@@ -846,6 +994,27 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
       C.ranges = (lane & 1) ? t[1] - t[0] : t[0];
     }
   }
+  C.ids_v = 0;
+  C.wts_v = 0.f;
+  C.inv_mlp = 1.f;
+  if constexpr (MOE) {  // the runs of a MoE step (bf16 rows of K elements take ceil(2 K / 1 KiB) chunks)
+    auto chunks = [](int K) { return (uint32_t)((2 * K + TD_CHUNK - 1) / TD_CHUNK); };
+    const uint32_t nqkv = wave_units(C.unit_n(TD_SP_QKV), wave), nh = wave_units(C.unit_n(TD_SP_H), wave);
+    const uint32_t nr = wave_units(C.unit_n(TD_SP_E), wave), ng = wave_units(C.unit_n(TD_SP_EI), wave);
+    const uint32_t nv = wave_units(C.unit_n(TD_SP_V), wave);
+    C.m_fixed = nqkv * 2 * chunks(P.H) + nh * chunks(P.qd) + nr * chunks(P.H);
+    C.m_gu = ng * 2 * chunks(P.H);
+    C.m_down = nh * chunks(P.I);
+    C.m_head = nv * chunks(P.H);
+    C.m_stride = C.m_fixed + (uint32_t)P.E * (C.m_gu + C.m_down);
+    C.m_slot = C.unit_n(TD_SP_EI) > 0 ? (uint32_t)(C.unit_lo(TD_SP_EI) / P.I) : 0u;
+    C.n_tot = (uint32_t)P.L * (C.m_fixed + C.m_gu + (uint32_t)P.topk * C.m_down) + C.m_head;  // consumed per step
+  }
+  stream_start(P, C);
+  C.islot = C.slot = 0;
+  C.nrv = 0;
+  C.ok = true;
+  topup(P, C);  // the stream starts right away
   const uint32_t epoch = uni(ld_u(P.sync + TD_SY_EPOCH));
   if (ld_u(P.sync + TD_SY_ABORT)) C.ok = false;
   int tok = uni(*P.token_in);
@@ -867,14 +1036,14 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
     const AttnTask T = attn_task(P, cu, pos);
     for (int seq = 0; seq < P.n_stages; ++seq) {
       int kind, layer;
-      stage_of(P, seq, kind, layer);
+      stage_of<MOE>(P, seq, kind, layer);
       if (kind == TD_ST_ATTN && !T.valid) continue;
       const uint32_t tag_in = tag0 + (uint32_t)seq, tag = tag_in + 1u;
       uint64_t ts0 = 0, ts1 = 0, ts2 = 0;
       if (P.trace) ts0 = wall_clock64();
       // operands fetched ahead of the rendezvous: this slice's gains, this wave's QKV biases
       const uint16_t* gain = kind == TD_ST_QKV ? P.gains + (size_t)(2 * layer) * P.H
-                           : kind == TD_ST_GU ? P.gains + (size_t)(2 * layer + 1) * P.H
+                           : (kind == TD_ST_GU && !MOE) || kind == TD_ST_ROUTER ? P.gains + (size_t)(2 * layer + 1) * P.H
                            : kind == TD_ST_HEAD ? P.gains + (size_t)(2 * P.L) * P.H : nullptr;
       uint32_t g0 = 0u, g1 = 0u, g2 = 0u, g3 = 0u;
       if (gain) {
@@ -911,10 +1080,23 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
         rendezvous(P, C);
         if (P.trace) ts1 = wall_clock64();
         if (wave < P.group) attn_wave_d<D>(P, C, lds, wave, T, tag, tiles_seen, ts2);
+      } else if (MOE && kind == TD_ST_GU) {
+        // MoE gate/up: the router logits (all E, from every CU) next to the
+        // input the router stage staged, the wave's routing, then its slot's
+        // expert rows, which can stream from here on
+        float* zs = (float*)(lds + P.off_route);
+        int lo, hi;
+        td_slice((P.E + 1) & ~1, wave, &lo, &hi);
+        C.ok &= poll_pairs<8>(P, P.trl, lo, hi, tag_in, zs, C);
+        rendezvous(P, C);
+        if (P.trace) ts1 = wall_clock64();
+        moe_route(P, C, lds, wave, layer);
+        topup(P, C);
+        gemv_wave<WF>(P, C, wave, kind, layer, pos, tag, C.inv_mlp, 0.f, 0.f, ts2);
       } else {
-        const int K = kind == TD_ST_O ? P.qd : kind == TD_ST_DOWN ? P.I : P.H;
+        const int K = kind == TD_ST_O ? P.qd : kind == TD_ST_DOWN ? (MOE ? P.topk * P.I : P.I) : P.H;
         const uint2* src = kind == TD_ST_O ? P.to : kind == TD_ST_DOWN ? P.tact
-                         : kind == TD_ST_GU ? P.tx_mid : P.tx_out;
+                         : kind == TD_ST_GU || kind == TD_ST_ROUTER ? P.tx_mid : P.tx_out;
         stage_gemv_input(P, C, wave, kind, K, src, kind == TD_ST_QKV && layer == 0 ? erow : nullptr, tag_in, g0, g1,
                          g2, g3, gain);
         reg_fence(bias_a);  // landed: loaded ahead of the input poll, whose wait covers them
@@ -938,6 +1120,7 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
           ss += __uint_as_float(b.w);
           inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
         }
+        if (kind == TD_ST_ROUTER) C.inv_mlp = inv;  // the MoE gate/up stage reuses the staged input
         gemv_wave<WF>(P, C, wave, kind, layer, pos, tag, inv, bf16f((uint16_t)bias_a), bf16f((uint16_t)bias_b), ts2);
       }
       if (P.trace) trace_rec(P, wave, seq, ts0, ts1, ts2, wall_clock64());
@@ -945,7 +1128,7 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
     // the step's stream is consumed (every chunk issued has been read): the
     // next step's starts over and streams while the sync wave decides the
     // token (and whether another step follows)
-    if (step + 1 < P.n_steps) stream_start(C);
+    if (step + 1 < P.n_steps) stream_start(P, C);
     (void)lds_wait_ge_topup(P, C, C.ctl + TD_CTL_TOKREADY, (uint32_t)step + 1u);
     if (!C.ok || uni((int)lds_ld(C.ctl + TD_CTL_STOP))) break;
     tok = (int)uni((int)lds_ld(C.ctl + TD_CTL_TOKEN));
@@ -997,7 +1180,9 @@ DEV bool poll_pairs_plain(const td_kparams& P, const uint2* src, int n, uint32_t
 
 DEV void cand_max(float& bv, int& bi) { cand_wave_max(bv, bi); }
 
+template <bool MOE>
 DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
+  constexpr int SPL = MOE ? 6 : 5;  // stages per layer
   const int lane = lane_id();
   const int cu = blockIdx.x, ncu = gridDim.x;
   uint32_t* ctl = (uint32_t*)(lds + P.off_ctl);
@@ -1021,8 +1206,8 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
       load_tile(P, tile_buf(P, lds, tiles_ready), 0, T, 0, pos);
     }
     for (int layer = 0; T.valid && layer < P.L; ++layer) {
-      // ATTN of this layer is the (5 layer + 1)-th stage the compute waves take part in
-      (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, 5 * layer + 1), ok);
+      // ATTN of this layer is the (spl layer + 1)-th stage the compute waves take part in
+      (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, SPL * layer + 1), ok);
       patch_pos_row(P, lds, tile_buf(P, lds, tiles_ready), T, 0, pos);
       lds_fence();
       lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
@@ -1035,10 +1220,11 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
         lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
       }
       if (layer + 1 < P.L) {
-        // the next layer's first tile once its buffer is free and the GU stage
-        // (whose input poll is on the critical path) has its inputs
+        // the next layer's first tile once its buffer is free and the stage
+        // after O (GU, or the router of a MoE layer), whose input poll is on
+        // the critical path, has its inputs
         (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
-        (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, 5 * layer + 3), ok);
+        (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, SPL * layer + 3), ok);
         load_tile(P, tile_buf(P, lds, tiles_ready), layer + 1, T, 0, pos);
       }
     }
@@ -1108,15 +1294,17 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
 // D: the head dimension (64 or 128), a template parameter so that only one
 // attention tile routine is compiled into each kernel; WF: the format of the
 // layer linears (TD_WF_*), so that each chunk loop is compiled for one format.
-template <int D, int WF>
+template <int D, int WF, bool MOE>
 __global__ void __launch_bounds__(TD_THREADS, 1) td_megakernel(td_kparams P) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint32_t* ctl = (uint32_t*)(lds + P.off_ctl);
   if (threadIdx.x < TD_CTL_WORDS) ctl[threadIdx.x] = 0u;
+  // MoE: the router logits area is padded with -inf past E (the choice reads it in fours)
+  if (MOE && threadIdx.x < TD_MAX_EXPERTS) ((float*)(lds + P.off_route))[threadIdx.x] = -__builtin_inff();
   __syncthreads();  // the only workgroup barrier: the control block is clear
   const int wave = uni((int)(threadIdx.x >> 6));
-  if (wave < TD_NW) compute_wave<D, WF>(P, lds, wave);
-  else sync_wave(P, lds);
+  if (wave < TD_NW) compute_wave<D, WF, MOE>(P, lds, wave);
+  else sync_wave<MOE>(P, lds);
 }
 
 // ------------------------------------------------------------ weight packing
@@ -1140,7 +1328,7 @@ __global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, u
   while (c.seq < P.n_stages && n < W.n_tot) {
     const int u = c.u_first + c.k * TD_NW;
     const int row = unit_row(P, c.g.kind, u, c.r);
-    const uint8_t* rp = c.g.w + (size_t)row * c.g.row_bytes;
+    const uint8_t* rp = c.g.w + (size_t)c.e * c.g.estride + (size_t)row * c.g.row_bytes;
     u32x4 v;
     if (c.g.fmt == 0) {
       const int boff = c.j * TD_CHUNK + lane * 16;
@@ -1165,7 +1353,7 @@ __global__ void __launch_bounds__(256) td_repack_kernel(td_kparams P, int ncu, u
 
 // ------------------------------------------------------------ stream-read yardstick
 // Reads `bytes` (a multiple of 16) once with 16-byte non-temporal loads, four
-// in flight per lane, over a grid of 8 workgroups of 512 threads per CU: the
+// in flight per lane, over a grid of one workgroup of 512 threads per CU: the
 // HBM read rate the weight stream can hope for on this part ("Decoding in
 // tiles", sec. 2: the measured streaming rate, not the nominal one, is the
 // floor's denominator).  Each lane folds its loaded words into one value that
@@ -1374,14 +1562,16 @@ __global__ void __launch_bounds__(64) td_argmax_final(const uint2* cand, const i
 
 // ------------------------------------------------------------ launchers
 namespace {
-const void* megakernel_of(int d, int wf) {
-  if (d == 64) return wf ? (const void*)td_megakernel<64, 1> : (const void*)td_megakernel<64, 0>;
-  return wf ? (const void*)td_megakernel<128, 1> : (const void*)td_megakernel<128, 0>;
+// MoE layers run on bf16 weights only (the plan refuses the others)
+const void* megakernel_of(int d, int wf, bool moe) {
+  if (moe) return d == 64 ? (const void*)td_megakernel<64, 0, true> : (const void*)td_megakernel<128, 0, true>;
+  if (d == 64) return wf ? (const void*)td_megakernel<64, 1, false> : (const void*)td_megakernel<64, 0, false>;
+  return wf ? (const void*)td_megakernel<128, 1, false> : (const void*)td_megakernel<128, 0, false>;
 }
 }  // namespace
 
-int td_megakernel_occupancy(int d, int wf, int lds_bytes, int* blocks) {
-  const void* f = megakernel_of(d, wf);
+int td_megakernel_occupancy(int d, int wf, int moe, int lds_bytes, int* blocks) {
+  const void* f = megakernel_of(d, wf, moe != 0);
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, TD_THREADS, lds_bytes);
   return (int)e;
@@ -1389,7 +1579,7 @@ int td_megakernel_occupancy(int d, int wf, int lds_bytes, int* blocks) {
 
 int td_launch_megakernel(const td_kparams* p, int ncu, void* stream) {
   void* args[] = {(void*)p};
-  const void* f = megakernel_of(p->d, p->wf);
+  const void* f = megakernel_of(p->d, p->wf, p->E > 0);
   return (int)hipLaunchCooperativeKernel(f, dim3(ncu), dim3(TD_THREADS), args, (unsigned)p->lds_bytes,
                                          (hipStream_t)stream);
 }

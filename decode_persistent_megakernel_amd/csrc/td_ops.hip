@@ -451,61 +451,6 @@ __global__ void __launch_bounds__(256) op_router(td_opparams P, int layer) {
   if (lane_id() == 0) P.rlogits[e] = z;
 }
 
-// moe_select (one wave): the router's choice from the E logits zs (LDS,
-// padded with -inf to a multiple of 4).  The topk largest logits in decreasing
-// order, the lower id first among equals: expert e takes slot rank(e), the
-// number of experts with a larger logit or an equal one and a lower id, if that
-// is below topk.  Their softmax probabilities over all E experts (max
-// subtracted, the sum reduced in a fixed lane order) go to wts.  A non-finite
-// logit gives ids 0 .. topk - 1 with weight 0 (every later read stays in
-// bounds) and returns true.  Every caller computes the same bits from the same
-// logits.
-DEV bool moe_select(const td_opparams& P, const float* zs, int32_t* ids, float* wts) {
-  constexpr int PER = TD_MAX_EXPERTS / 64;
-  const int lane = lane_id();
-  float z[PER];
-  float m = -__builtin_inff();
-  int bad = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    z[i] = zs[e];
-    if (e < P.E && !isfinite(z[i])) bad = 1;
-    if (e < P.E) m = fmaxf(m, z[i]);
-  }
-  bad = __any(bad);
-  m = wave_max(m);
-  float ssum = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (lane + 64 * i < P.E) ssum += expf(z[i] - m);
-  ssum = wave_sum(ssum);
-  if (bad) {
-    if (lane < P.topk) {
-      ids[lane] = lane;
-      wts[lane] = 0.f;
-    }
-    return true;
-  }
-  const int E4 = (P.E + 3) & ~3;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (64 * i >= P.E) break;
-    const int e = lane + 64 * i;
-    int rank = 0;
-    for (int c = 0; c < E4; c += 4) {  // the same address in every lane: a broadcast read
-      const f32x4 q = *(const f32x4*)(zs + c);
-      rank += (q.x > z[i] || (q.x == z[i] && c < e)) + (q.y > z[i] || (q.y == z[i] && c + 1 < e)) +
-              (q.z > z[i] || (q.z == z[i] && c + 2 < e)) + (q.w > z[i] || (q.w == z[i] && c + 3 < e));
-    }
-    if (e < P.E && rank < P.topk) {
-      ids[rank] = e;
-      wts[rank] = expf(z[i] - m) / ssum;
-    }
-  }
-  return false;
-}
-
 // Expert e's block of a stacked [E][rows][K] linear (codes and scales).
 DEV const uint8_t* expert_w(const uint8_t* w, int fmt, int e, int rows, int K) {
   return w + (size_t)e * rows * (fmt ? (size_t)(K / 2) : (size_t)K * 2);
@@ -530,7 +475,7 @@ __global__ void __launch_bounds__(256) op_moe_gu(td_opparams P, int layer, int R
   const int wave = threadIdx.x >> 6;
   const float inv = op_norm_to_lds(P.x, Ld.mlp_norm, P.H, P.eps, xs, xs + op_kpad(P.H, P.wf), P.rlogits, P.E, zs);
   bool bad = false;
-  if (wave == 0) bad = moe_select(P, zs, sid, swt);
+  if (wave == 0) bad = moe_select(P.E, P.topk, zs, sid, swt);
   op_zero_tail(xs, P.H, op_kpad(P.H, P.wf));
   __syncthreads();
   if (blockIdx.x == 0 && wave == 0) {

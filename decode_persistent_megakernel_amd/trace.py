@@ -17,14 +17,16 @@ from __future__ import annotations
 
 import numpy as np
 
-KINDS = ["qkv", "attn", "o", "gu", "down", "head"]
+KINDS = ["qkv", "attn", "o", "gu", "down", "head", "router"]
+LAYER_KINDS = {5: ["qkv", "attn", "o", "gu", "down"], 6: ["qkv", "attn", "o", "router", "gu", "down"]}
 TICK_US = 0.01  # 100 MHz
 
 
-def summarize(trace: np.ndarray, n_layers: int) -> dict:
+def summarize(trace: np.ndarray, n_layers: int, spl: int = 5) -> dict:
+    """spl: stages per layer, 5 for a dense layer, 6 for a mixture-of-experts one (with the router)."""
     raw = trace.astype(np.int64).reshape(trace.shape[0], trace.shape[1], 8, 4)  # [ncu, stages, wave, stamp]
     ns = raw.shape[1]
-    kinds = [KINDS[s % 5] if s < 5 * n_layers else "head" for s in range(ns)]
+    kinds = [LAYER_KINDS[spl][s % spl] if s < spl * n_layers else "head" for s in range(ns)]
     valid = raw > 0
     t0 = raw[..., 0][valid[..., 0]].min()
     t = (raw - t0) * TICK_US

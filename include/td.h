@@ -132,12 +132,17 @@ typedef struct td_ctx td_ctx;
  * not 16-byte aligned), TD_E_UNSUPPORTED
  * (device is not gfx950, or its CU count is not a multiple of 8), TD_E_PLAN,
  * TD_E_NOMEM, TD_E_HIP.  On error *out is set to NULL.
- * A mixture-of-experts config runs on TD_EXEC_PER_OP and TD_EXEC_GRAPH only: the
- * router writes the chosen expert ids to a device tensor (td_expert_ids) and the
- * expert kernels read their weights through it, so the recorded graph replays
- * whatever the routing (TD_E_UNSUPPORTED with TD_EXEC_MEGAKERNEL; TD_E_INVALID_ARG
+ * A mixture-of-experts config ("One launch per token", its 64-expert MoE
+ * section) runs on every executor.  On TD_EXEC_MEGAKERNEL the routing happens
+ * inside the launch: a router stage publishes the E logits, every CU makes the
+ * same top-k choice and streams the chosen experts' rows, gathered by id from
+ * a packed copy of all experts (bf16 weights only: TD_E_UNSUPPORTED for int4
+ * experts on this executor).  On TD_EXEC_PER_OP and TD_EXEC_GRAPH the router
+ * writes the chosen ids to a device tensor and the expert kernels read their
+ * weights through it, so one recorded graph replays whatever the routing.
+ * Either way td_expert_ids reports the last step's routing.  TD_E_INVALID_ARG
  * for top_k outside [1, min(n_experts, TD_MAX_TOPK)], n_experts above
- * TD_MAX_EXPERTS, or a null w_router).
+ * TD_MAX_EXPERTS, or a null w_router.
  */
 int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ctx** out);
 
@@ -290,11 +295,14 @@ const char* td_last_error(void);
  * or the code td_create would return (TD_E_PLAN for a partition that leaves a
  * unit or a row without an owner, gives one two owners, or leaves the
  * matrix; TD_E_UNSUPPORTED for a config the kernels cannot split, such as
- * more kv heads than CUs; TD_E_INVALID_ARG for a bad config).  With part
- * non-NULL (host int32 [4][ncu + 1], part_len = 4 (ncu + 1): for each unit
- * space -- QKV row pairs, hidden rows, intermediate rows, vocabulary rows --
- * the first unit of every CU, then the unit count) the plan uses that
- * partition instead of its own.  td_plan_partition writes the partition the
+ * more kv heads than CUs, or int4 expert weights; TD_E_INVALID_ARG for a bad
+ * config).  With part non-NULL (host int32 [6][ncu + 1], part_len =
+ * 6 (ncu + 1): for each unit space -- QKV row pairs, hidden rows,
+ * intermediate rows, vocabulary rows, router rows (one per expert), expert
+ * gate/up units (top_k slots of intermediate units; every CU's range inside
+ * one slot, else TD_E_PLAN) -- the first unit of every CU, then the unit
+ * count; the last two spaces are empty for a dense config) the plan uses
+ * that partition instead of its own.  td_plan_partition writes the partition the
  * plan builds into part_out (same layout).  Host code only: no HIP call. */
 int td_plan_partition(const td_config* cfg, int32_t ncu, int32_t* part_out, int32_t part_len);
 int td_plan_check(const td_config* cfg, int32_t ncu, const int32_t* part, int32_t part_len);

@@ -7,7 +7,8 @@ launch of 32 steps (the launch form the benchmark times), the oracle step by
 step on its own argmax.  Required: the 32 tokens identical, the last step's
 logits (all V of them) within the contract tolerance (2e-2 for bf16 weights,
 5e-2 for int4), and the K/V rows the 32 steps wrote within the same
-tolerance of the oracle's, at most 2 % of them differing at all.  No token flip
+tolerance of the oracle's, at |v| >= 1/4 at most one bf16 ulp apart, and
+fewer than 5 % of them differing at all.  No token flip
 is excused: the oracle's smallest top-2 gap over the chain is printed, and
 NEAR_TIES lists the (workload, step) pairs at which a flip was observed with a
 gap below the observed logit error, none so far.
@@ -20,7 +21,9 @@ chains are included as well: the TinyLlama-shaped int4 model (untied by its
 reading) and the Llama-3.2-1B shape with a separate head.
 The tiny model decodes from a cache the oracle prefilled with the prompt;
 the full-size workloads decode from a seeded random K/V prefix of the
-prompt's length (the oracle would take minutes to prefill them).
+prompt's length (the oracle would take minutes to prefill them).  The
+mixture-of-experts workload (OLMoE shape, 64 experts, top 8) runs the same
+loop with the router and the expert choice inside the launch.
 """
 import math
 import sys
@@ -84,6 +87,7 @@ WORKLOADS = [
     ("tinyllama_int4", {}),
     ("qwen1p5b", {}),
     ("llama1b_int4_long", {}),
+    ("olmoe", {}),  # mixture of experts: routing inside the launch
 ]
 
 
@@ -124,17 +128,29 @@ def test_loop_free_run_matches_oracle_chain(td, label, over):  # noqa: F811
     assert td.read_device_i32(dec.token_ptr()) == got[-1]
     # the K/V rows the chain wrote: bf16 roundings of fp32 sums (GPU) and of fp64
     # sums (oracle).  Most are identical; where the two sums straddle a rounding
-    # boundary they differ by a bf16 ulp, and near zero, where an ulp is smaller
-    # than the sums' difference, by that difference.  Bound: the logits contract
-    # (the same absolute tolerance), and at most 2 % of the entries differing.
+    # boundary the roundings are adjacent bf16 values (one ulp apart), and near
+    # zero, where an ulp is smaller than the sums' difference, they differ by
+    # about that difference.  Bound: the logits contract (the same absolute
+    # tolerance) on every entry; away from zero (|v| >= 1/4, where a bf16 ulp,
+    # 2^-9 or more, exceeds the sums' fp32 drift) no entry more than one ulp off
+    # (nearer zero two-ulp differences occur: 2^-14 at |v| ~ 2^-6); and a minority of entries
+    # differing at all (below 5 %: the share of straddled roundings grows with
+    # the sums' fp32 error relative to the ulp, 0.3 % to 2.3 % over these
+    # workloads; a row computed from wrong inputs differs almost everywhere).
     gk, gv = kv.host()
     for a, b in ((gk, ok), (gv, ov)):
+        a16 = a[:, :, pos0:pos0 + n].astype(np.int64)
+        b16 = b[:, :, pos0:pos0 + n].astype(np.int64)
         a = bf16_to_f64(a[:, :, pos0:pos0 + n])
         b = bf16_to_f64(b[:, :, pos0:pos0 + n])
         d = np.abs(a - b)
-        _say(f"{label}: K/V rows max|d| = {d.max():.3g}, differing {np.mean(a != b):.2%}")
+        far = (np.abs(b) >= 0.25) & (np.sign(a) == np.sign(b))
+        ulps = np.abs((a16 & 0x7FFF) - (b16 & 0x7FFF))[far]
+        _say(f"{label}: K/V rows max|d| = {d.max():.3g}, differing {np.mean(a != b):.2%}, "
+             f"max ulps away from zero {ulps.max() if ulps.size else 0}")
         assert d.max() <= TOL[cfg.weight_format]
-        assert np.mean(a != b) < 0.02
+        assert ulps.size == 0 or ulps.max() <= 1
+        assert np.mean(a != b) < 0.05
     # rows before the chain are untouched
     gk0, gv0 = kv.host()
     assert np.array_equal(gk0[:, :, :pos0], k[:, :, :pos0]) and np.array_equal(gv0[:, :, :pos0], v[:, :, :pos0])

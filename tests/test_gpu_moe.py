@@ -1,8 +1,12 @@
-"""Mixture-of-experts decode on the per-op and graph executors.
+"""Mixture-of-experts decode on the persistent kernel and on the per-op and
+graph executors.
 
-The router writes each layer's chosen experts into a device tensor
-(td_expert_ids) and the expert kernels read their weights through it, so one
-recorded graph serves every routing.  Every step is compared with the
+On the per-op and graph executors the router writes each layer's chosen
+experts into a device tensor (td_expert_ids) and the expert kernels read
+their weights through it, so one recorded graph serves every routing.  The
+persistent kernel routes inside the launch: a router stage publishes the
+logits, every CU makes the same choice and streams the chosen experts' rows
+("One launch per token", its 64-expert MoE section); it runs bf16 weights.  Every step is compared with the
 oracle's teacher-forced step from the same K/V state: the V logits within the
 decode-step tolerance (2e-2 for bf16 weights, 5e-2 for int4), the greedy token
 (a flip only at a near-tie), and the routing itself: the same experts in the
@@ -89,23 +93,30 @@ def _run(td, cfg, m, k, v, first, start, n, executor, label):
 @pytest.mark.parametrize("cfg,start", [(MOE_BF16, 30), (MOE_INT4, 10), (MOE_D128, 60), (MOE_ODD, 20), (MOE_TOP1, 5),
                                        (MOE_MAX, 40)],
                          ids=["bf16_e16k4", "int4_e8k2", "d128_e64k8", "e10k3", "e5k1", "e256k16"])
-@pytest.mark.parametrize("executor", ["per_op", "graph"])
+@pytest.mark.parametrize("executor", ["megakernel", "per_op", "graph"])
 def test_moe_matches_oracle(td, cfg, start, executor):
-    ex = {"per_op": td.TD_EXEC_PER_OP, "graph": td.TD_EXEC_GRAPH}[executor]
+    from decode_persistent_megakernel_amd import _lib
+    ex = {"per_op": td.TD_EXEC_PER_OP, "graph": td.TD_EXEC_GRAPH, "megakernel": td.TD_EXEC_MEGAKERNEL}[executor]
     m = synth.make_model(cfg)
+    if ex == td.TD_EXEC_MEGAKERNEL and cfg.weight_format != synth.WF_BF16:
+        with pytest.raises(td.TdError) as ei:  # the persistent kernel runs MoE layers on bf16 weights
+            td.Decoder(td.DeviceModel(m), cfg.max_ctx, executor=ex)
+        assert ei.value.code == _lib.TD_E_UNSUPPORTED
+        return
     k, v = synth.random_kv_prefix(cfg, start, seed_tag="moe")
     _run(td, cfg, m, k, v, synth.first_token(cfg), start, 12, ex, f"{cfg.name}/{executor}")
 
 
-def test_graph_replays_follow_the_routing(td):
-    """The graph executor replays one recording; its logits equal the per-op
-    executor's bit for bit over steps whose routing differs."""
-    cfg = MOE_D128
+@pytest.mark.parametrize("cfg", [MOE_D128, MOE_BF16, MOE_MAX], ids=["d128_e64k8", "bf16_e16k4", "e256k16"])
+def test_executors_agree_across_routings(td, cfg):
+    """The graph executor replays one recording and the persistent kernel routes
+    inside its launch; the logits of both equal the per-op executor's bit for
+    bit over steps whose routing differs, and so do the routings."""
     m = synth.make_model(cfg)
     k, v = synth.random_kv_prefix(cfg, 20, seed_tag="moe")
     dm = td.DeviceModel(m)
     res = {}
-    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH):
+    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH, td.TD_EXEC_MEGAKERNEL):
         kv = td.KVCache(cfg, cfg.max_ctx, k=k, v=v)
         dec = td.Decoder(dm, cfg.max_ctx, executor=ex)
         tok = torch.tensor([synth.first_token(cfg)], dtype=torch.int32, device="cuda")
@@ -119,9 +130,11 @@ def test_graph_replays_follow_the_routing(td):
             routes.append(dec.routing()[0].copy())
         res[ex] = (bits, routes)
         dec.close()
-    (b0, r0), (b1, r1) = res[td.TD_EXEC_PER_OP], res[td.TD_EXEC_GRAPH]
-    assert all(np.array_equal(a, b) for a, b in zip(b0, b1))
-    assert all(np.array_equal(a, b) for a, b in zip(r0, r1))
+    (b0, r0) = res[td.TD_EXEC_PER_OP]
+    for ex in (td.TD_EXEC_GRAPH, td.TD_EXEC_MEGAKERNEL):
+        b1, r1 = res[ex]
+        assert all(np.array_equal(a, b) for a, b in zip(r0, r1)), ex
+        assert all(np.array_equal(a, b) for a, b in zip(b0, b1)), ex
     assert len({x.tobytes() for x in r0}) > 1  # the routing changed between steps
     for ids in r0:
         for row in ids:
@@ -133,8 +146,9 @@ def test_moe_errors(td):
     cfg = MOE_BF16
     m = synth.make_model(cfg)
     dm = td.DeviceModel(m)
-    with pytest.raises(td.TdError) as ei:
-        td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_MEGAKERNEL)
+    m4 = synth.make_model(MOE_INT4)
+    with pytest.raises(td.TdError) as ei:  # int4 experts: per-op and graph executors only
+        td.Decoder(td.DeviceModel(m4), MOE_INT4.max_ctx, executor=td.TD_EXEC_MEGAKERNEL)
     assert ei.value.code == _lib.TD_E_UNSUPPORTED
     dec = td.Decoder(dm, cfg.max_ctx, executor=td.TD_EXEC_PER_OP)
     kv = td.KVCache(cfg, cfg.max_ctx)
@@ -147,21 +161,27 @@ def test_moe_errors(td):
     # a NaN router row: a non-finite router logit is reported, and the step stays in bounds
     m.layers[1].router = m.layers[1].router.copy()
     m.layers[1].router[3, :] = 0x7FC0
-    dec = td.Decoder(td.DeviceModel(m), cfg.max_ctx, executor=td.TD_EXEC_PER_OP)
-    tok = torch.tensor([5], dtype=torch.int32, device="cuda")
-    dec.step(tok.data_ptr(), 0, kv, logits)
-    torch.cuda.synchronize()
-    assert dec.status() == _lib.TD_E_NONFINITE
-    dec.close()
+    dmn = td.DeviceModel(m)
+    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_MEGAKERNEL):
+        dec = td.Decoder(dmn, cfg.max_ctx, executor=ex)
+        tok = torch.tensor([5], dtype=torch.int32, device="cuda")
+        dec.step(tok.data_ptr(), 0, kv, logits)
+        torch.cuda.synchronize()
+        assert dec.status() == _lib.TD_E_NONFINITE, ex
+        ids, wts = dec.routing()
+        assert ids[1].tolist() == list(range(cfg.top_k)) and not wts[1].any(), ex  # in-bounds fallback routing
+        dec.close()
 
 
-def test_fullsize_olmoe_matches_oracle(td):
+@pytest.mark.parametrize("executor", ["megakernel", "graph"])
+def test_fullsize_olmoe_matches_oracle(td, executor):
     cfg = synth.CONFIGS["olmoe"]
+    ex = {"graph": td.TD_EXEC_GRAPH, "megakernel": td.TD_EXEC_MEGAKERNEL}[executor]
     _say("olmoe: generating the model")
     m = synth.make_model(cfg)
     k, v = synth.random_kv_prefix(cfg, cfg.start_pos)
-    _say(f"olmoe: 8 teacher-forced steps from position {cfg.start_pos} (graph executor)")
-    _run(td, cfg, m, k, v, synth.first_token(cfg), cfg.start_pos, 8, td.TD_EXEC_GRAPH, "olmoe")
+    _say(f"olmoe: 8 teacher-forced steps from position {cfg.start_pos} ({executor})")
+    _run(td, cfg, m, k, v, synth.first_token(cfg), cfg.start_pos, 8, ex, f"olmoe/{executor}")
 
 
 def test_tied_router_logits_take_the_lower_id_first(td):
@@ -186,5 +206,5 @@ def test_tied_router_logits_take_the_lower_id_first(td):
     _, tr = o.step_traced(synth.first_token(cfg), 30)
     assert sorted(tr["expert_ids"][0][:3].tolist()) == sorted([top] + twins)
     assert tr["expert_ids"][0][:3].tolist() == sorted([top] + twins)  # the oracle's own tie order
-    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH):
+    for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH, td.TD_EXEC_MEGAKERNEL):
         _run(td, cfg, m, k, v, synth.first_token(cfg), 30, 4, ex, f"ties/{ex}")

@@ -16,14 +16,14 @@ import synth
 from decode_persistent_megakernel_amd import _lib
 
 NCU = 256
-NSP = 4  # unit spaces: QKV row pairs, hidden rows, intermediate rows, vocabulary rows
+NSP = 6  # unit spaces: QKV row pairs, hidden rows, intermediate rows, vocabulary rows, router rows, expert units
 
 
 def _cfg(c, **over):
     kw = dict(n_layers=c.n_layers, hidden=c.hidden, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
               head_dim=c.head_dim, intermediate=c.intermediate, vocab=c.vocab, max_ctx=c.max_ctx,
               rope_theta=c.rope_theta, rms_eps=c.rms_eps, weight_format=c.weight_format,
-              qkv_bias=int(c.qkv_bias), n_experts=0, top_k=0)
+              qkv_bias=int(c.qkv_bias), n_experts=c.n_experts, top_k=c.top_k)
     kw.update(over)
     return _lib.TdConfig(**kw)
 
@@ -42,16 +42,13 @@ def _check(cfg, part=None, ncu=NCU):
     return _lib.lib().td_plan_check(ctypes.byref(cfg), ncu, part.ctypes.data, part.size)
 
 
-DENSE = [n for n in synth.CONFIG_ORDER if synth.CONFIGS[n].n_experts == 0]
-
-
-@pytest.mark.parametrize("name", DENSE)
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
 def test_every_workload_plan_validates(name):
     cfg = _cfg(synth.CONFIGS[name])
     assert _check(cfg) == _lib.TD_OK, _lib.last_error()
     part = _partition(cfg).reshape(NSP, NCU + 1)
     c = synth.CONFIGS[name]
-    units = [c.qkv_rows // 2, c.hidden, c.intermediate, c.vocab]
+    units = [c.qkv_rows // 2, c.hidden, c.intermediate, c.vocab, c.n_experts, c.top_k * c.intermediate]
     for sp in range(NSP):
         assert part[sp, 0] == 0 and part[sp, -1] == units[sp]
         assert np.all(np.diff(part[sp]) >= 0)
@@ -91,10 +88,40 @@ def test_another_exact_tiling_is_accepted():
     moving one boundary by a unit still gives every unit one owner."""
     cfg = _cfg(synth.CONFIGS["llama1b"])
     p = _partition(cfg).reshape(NSP, NCU + 1).copy()
-    for sp in range(NSP):
+    for sp in range(4):  # the spaces a dense model uses
         assert p[sp, 101] > p[sp, 100]
         p[sp, 101] -= 1
     assert _check(cfg, p.ravel()) == _lib.TD_OK, _lib.last_error()
+
+
+def test_moe_plan_keeps_each_cu_in_one_expert_slot():
+    """The expert gate/up units are top_k slots of I; every CU's range lies in one
+    slot (its waves stream one chosen expert's rows), so a table in which a CU's
+    range crosses a slot boundary is refused with TD_E_PLAN.  The router's rows
+    are a unit space of their own; int4 experts are refused by the persistent
+    kernel (the per-op executors run them)."""
+    c = synth.CONFIGS["olmoe"]
+    cfg = _cfg(c)
+    part = _partition(cfg).reshape(NSP, NCU + 1)
+    ei = part[5]
+    per_slot = NCU // c.top_k
+    for j in range(c.top_k + 1):
+        assert ei[j * per_slot] == j * c.intermediate
+    for cu in range(NCU):
+        if ei[cu + 1] > ei[cu]:
+            assert ei[cu] // c.intermediate == (ei[cu + 1] - 1) // c.intermediate
+    bad = part.copy()
+    b = per_slot  # the first CU of slot 1 starts one unit early: the previous CU ends inside slot 0 ...
+    bad[5, b] -= 1  # ... and this CU's range now crosses from slot 0 into slot 1
+    assert _check(cfg, bad.ravel()) == _lib.TD_E_PLAN
+    assert "slot" in _lib.last_error()
+    for corrupt in ("overlap", "start_gap", "end_gap", "past_end", "negative"):
+        for sp in (4, 5):
+            assert _check(cfg, _corrupt(part, sp, corrupt).ravel()) == _lib.TD_E_PLAN, (sp, corrupt)
+    c4 = _cfg(c, weight_format=synth.WF_INT4_G64)
+    assert _check(c4) == _lib.TD_E_UNSUPPORTED
+    # odd expert counts and top-1 plan too (the logits hand-off pads to a pair)
+    assert _check(_cfg(c, n_experts=5, top_k=1)) == _lib.TD_OK, _lib.last_error()
 
 
 def test_more_kv_heads_than_cus_is_unsupported_not_a_crash():
