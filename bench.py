@@ -109,7 +109,8 @@ def cpu_baseline(model, cfg, pos0: int, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 128, or fewer where the workload's cache holds fewer)")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="llama1b")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
@@ -197,7 +198,7 @@ def main() -> int:
         print(f"device status {st} after prefill", file=sys.stderr)
         return 1
 
-    n_steps = args.steps
+    n_steps = args.steps if args.steps is not None else min(128, cfg.max_ctx - start)
     if start + n_steps > cfg.max_ctx:
         print(f"--steps {n_steps} exceeds the cache ({cfg.max_ctx - start} positions left)", file=sys.stderr)
         return 1

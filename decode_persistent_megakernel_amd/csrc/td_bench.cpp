@@ -14,11 +14,9 @@
 //
 // --executor megakernel|per_op|graph picks the executor behind td_decode_step.
 //
-// A mixture-of-experts workload runs on the graph executor unless --executor
-// per_op is given.
-//
 // --loop N runs the steps through td_decode_loop, N greedy steps per launch
-// (the last launch takes the remainder), instead of one td_decode_step each.
+// (the last launch takes the remainder), instead of one td_decode_step each
+// (persistent executor only).
 //
 // --block N fills the prompt through td_forward_block, N tokens per call,
 // instead of one decode step per token, and times that prefill (one untimed
@@ -188,12 +186,8 @@ int main(int argc, char** argv) {
     return 2;
   }
   const Workload& w = *wp;
-  if (w.n_experts > 0 && executor == TD_EXEC_MEGAKERNEL) {
-    executor = TD_EXEC_GRAPH;  // a mixture of experts runs on the per-op launches (replayed as a graph)
-    ex_name = "graph";
-  }
-  if (w.n_experts > 0 && (loop_n > 0 || block_n > 0)) {
-    fprintf(stderr, "td_bench: --loop and --block run dense models only\n");
+  if (w.n_experts > 0 && block_n > 0) {
+    fprintf(stderr, "td_bench: --block runs dense models only\n");
     return 2;
   }
   if (only_config) {

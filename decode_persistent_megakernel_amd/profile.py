@@ -6,9 +6,9 @@
 For each workload (td_bench and bench.py run as child processes; this process
 never touches the GPU):
 
-  trace   rocprofv3 --kernel-trace --stats of td_bench: per-kernel time; for a
-          dense model the timed td_decode_loop launches (64 steps each), for a
-          mixture-of-experts model the per-op kernels of the graph executor
+  trace   rocprofv3 --kernel-trace --stats of td_bench: per-kernel time of the
+          timed td_decode_loop launches (64 steps each); with --executor graph
+          the per-op kernels of the graph executor instead
   pmc     two counter runs, FETCH_SIZE then WRITE_SIZE, each followed in the
           same process by a 1 GiB device-to-device copy whose counter reading
           scales KiB-per-dispatch into bytes; HBM bytes per decode step against
@@ -111,9 +111,9 @@ def _cmd_text(prof: str, prog: str) -> str:
 
 
 # ---------------------------------------------------------------- kernel trace
-def trace(name: str, out: str, raw: str) -> str:
+def trace(name: str, out: str, raw: str, graph: bool = False) -> str:
     cfg = _cfg(name)
-    moe = bool(cfg.n_experts)
+    moe = graph  # the per-op kernels (replayed as a graph) instead of the persistent kernel
     if moe:
         steps, warmup, prog = 16, 2, f"--config {name} --executor graph --steps 16 --warmup 2"
     else:
@@ -127,6 +127,8 @@ def trace(name: str, out: str, raw: str) -> str:
     if moe:
         path = os.path.join(out, f"graph_{name}_kernel_trace.txt")
         ops = [(_short(n), du) for n, du in per if "op_" in n]
+        if not cfg.n_experts:
+            raise RuntimeError("the graph-executor trace summary is written for mixture-of-experts workloads")
         begins = [i for i, (n, _) in enumerate(ops) if n == "op_begin"]
         timed = ops[begins[-steps]:]
         agg = collections.OrderedDict()
@@ -183,9 +185,9 @@ def trace(name: str, out: str, raw: str) -> str:
 
 
 # ---------------------------------------------------------------- HBM counters
-def pmc(name: str, out: str, raw: str) -> str:
+def pmc(name: str, out: str, raw: str, graph: bool = False) -> str:
     cfg = _cfg(name)
-    moe = bool(cfg.n_experts)
+    moe = graph
     if moe:
         steps, prog = 16, f"--config {name} --executor graph --steps 16 --warmup 2 --copy-calibration"
     else:
@@ -256,7 +258,7 @@ def stages(name: str, out: str, raw: str) -> str:
              "CUs); work: a CU's inputs staged to its last output (median, max over CUs); averaged over the layers; "
              "us", "", tdtrace.format_summary(s)]
     per_layer = sum(v["span_us"] for k, v in s["stages"].items() if k != "head")
-    lines.append(f"per layer (sum of the five spans): {per_layer:.2f} us")
+    lines.append(f"per layer (sum of the layer's stage spans): {per_layer:.2f} us")
     path = os.path.join(out, f"megakernel_{name}_stage_trace.txt")
     open(path, "w").write("\n".join(lines) + "\n")
     return path
@@ -324,15 +326,19 @@ def main(argv=None) -> int:
     ap.add_argument("--what", default="trace,pmc,stages")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--raw", required=True, help="directory for the profiler's databases and logs")
+    ap.add_argument("--executor", default="megakernel", choices=["megakernel", "graph"],
+                    help="graph: a mixture-of-experts workload's per-op kernels replayed as a graph")
     a = ap.parse_args(argv)
     os.makedirs(a.out, exist_ok=True)
     os.makedirs(a.raw, exist_ok=True)
-    fns = {"trace": trace, "pmc": pmc, "stages": stages, "block": block}
+    graph = a.executor == "graph"
+    fns = {"trace": lambda n, o, r: trace(n, o, r, graph), "pmc": lambda n, o, r: pmc(n, o, r, graph),
+           "stages": stages, "block": block}
     for name in a.config:
         moe = bool(_cfg(name).n_experts)
         for w in a.what.split(","):
-            if moe and w in ("stages", "block"):
-                continue  # the MoE decode runs per-op kernels: no stage trace, no block path
+            if (moe and w == "block") or (graph and w in ("stages", "block")):
+                continue  # no block forward for MoE; no stage trace off the persistent kernel
             _say(f"{name}: {w}")
             path = fns[w](name, a.out, a.raw)
             _say(f"{name}: {w} -> {os.path.relpath(path, ROOT)}")
