@@ -334,9 +334,11 @@ struct Plan {
 
 // The attention split of a config on ncu CUs: at most one task per CU, chunks
 // a multiple of the tile, at most 64 chunks per kv head, and the merge staging
-// within the LDS the GEMV input area already takes (the attention area aliases
-// it), at least 24 KiB: more chunks mean fewer tiles per CU, which a CU runs
-// one by one.  No allocation.
+// within the LDS the GEMV input area and the first K/V tile buffer already take
+// (the attention area aliases the input area; the merge runs once the CU's own
+// tiles are consumed, so its staging may run on into the tile buffer), at
+// least 24 KiB: more chunks mean fewer tiles per CU, which a CU runs one by
+// one.  No allocation.
 int attention_split(const td_config& c, int ncu, int* chunk_len_out, int* n_chunks_out) {
   const int d = c.head_dim, H = c.hidden, I = c.intermediate;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, group = nq / nkv, qd = nq * d;
@@ -344,9 +346,10 @@ int attention_split(const td_config& c, int ncu, int* chunk_len_out, int* n_chun
   const int cmax_by_cu = ncu / nkv;
   int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
   auto n_chunks_of = [&](int cl) { return (c.max_ctx + cl - 1) / cl; };
-  const int64_t kpad_in = round_up(std::max({H, qd, I}), 2048);
-  const int64_t merge_budget =
-      std::max<int64_t>(24 * 1024, kpad_in * 4 - ((int64_t)group * d * 4 + 2 * d * 4 + (int64_t)group * TD_TILE * 4));
+  const int64_t topk_i = c.n_experts > 0 ? (int64_t)c.top_k * I : 0;
+  const int64_t kpad_in = round_up(std::max<int64_t>({H, qd, I, topk_i}), 2048);
+  const int64_t merge_budget = std::max<int64_t>(
+      24 * 1024, kpad_in * 4 + td_tile_bytes(d) - ((int64_t)group * d * 4 + 2 * d * 4 + (int64_t)group * TD_TILE * 4));
   while (n_chunks_of(chunk_len) > 64 || (int64_t)n_chunks_of(chunk_len) * group * (d + 4) * 4 > merge_budget)
     chunk_len += TD_TILE;
   const int n_chunks_max = n_chunks_of(chunk_len);
@@ -395,7 +398,9 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
   const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
   // the GEMV input area holds the longest input: a MoE down stage's is top_k slots of I
   const int64_t kpad = round_up(std::max({H, qd, I, topk * I}), 2048);
-  const int64_t xin_bytes = std::max<int64_t>(kpad * 4, A.bytes);
+  // the attention area aliases the input area; its merge staging (used after the
+  // CU's tiles) may run on into the first tile buffer, which follows
+  const int64_t xin_bytes = std::max<int64_t>({kpad * 4, (int64_t)A.merge, A.bytes - td_tile_bytes(d)});
   td_kparams kp{};
   int64_t fixed = 0;
   const int64_t per_slot = (int64_t)TD_NW * (TD_CHUNK + (c.weight_format == TD_WF_INT4_G64 ? TD_SCHUNK : 0));
@@ -408,6 +413,7 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
     kp.off_xin = kp.off_attn = (int32_t)off;
     off += round_up(xin_bytes, 1024);
     kp.off_tile = (int32_t)off;
+    kp.merge_in_tile = A.bytes > kp.off_tile - kp.off_attn ? 1 : 0;
     off += (int64_t)nb * kp.tile_stride;
     kp.off_own = (int32_t)off;
     off += (int64_t)own_floats * 4;

@@ -136,6 +136,7 @@ struct td_kparams {
   const uint8_t* wcode;
   const uint8_t* wscale;
   const td_wstream* ws;   // [ncu][TD_NW]
+  int32_t merge_in_tile;  // the attention merge staging runs on into the first tile buffer
 };
 
 // Parameters of the per-op executor (td_ops.hip): the same weights, table and

@@ -910,7 +910,9 @@ DEV void attn_wave_d(const td_kparams& P, CS& C, uint8_t* lds, int h, const Attn
   const int n = T.n_used;  // <= 64
   float* mb = (float*)(base + A.merge) + (size_t)h * (P.n_chunks_max - 1) * st;  // chunks 1..n-1
   // the merging CUs (one per kv head) poll without topping up: every CU's
-  // O stage waits for their outputs
+  // O stage waits for their outputs.  Where the staging runs on into the K/V
+  // tile buffer, it waits until every query-head wave is done with the tiles.
+  if (P.merge_in_tile) (void)lds_wait_ge(P, C.ctl + TD_CTL_TDONE, (uint32_t)G * tiles_seen, C.ok);
   if (n > 1) C.ok &= poll_pairs<8, false>(P, myparts + st, 0, (n - 1) * st, tag, mb, C);
   lds_fence();
   const f32x4 o = attn_merge<D>(acc, m, l, mb, n, ps);
