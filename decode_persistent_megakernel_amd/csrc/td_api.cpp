@@ -736,6 +736,13 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
         const int S = td_block_split(g[0], g[1], ncu, tile_rows, g[3], &KS);
         if (S > 1 || g[2]) part_floats = std::max(part_floats, (size_t)S * R * g[0]);
       }
+    for (int gi = 0; gi < 4; ++gi) {  // the streamed GEMM's slices (bf16, all but the logits GEMM)
+      const auto& g = gem[gi];
+      if (g[3] != TD_WF_BF16) continue;
+      int nt = 0, xc = 0;
+      const int S = td_block_stream_plan(g[0], g[1], ncu, &nt, &xc);
+      if (S > 1 || g[2]) part_floats = std::max(part_floats, (size_t)S * R * g[0]);
+    }
     size_t bo = 0;
     auto btake = [&](size_t bytes) {
       size_t o = bo;
@@ -752,6 +759,14 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
       delete ctx;
       return e == hipErrorOutOfMemory ? fail(TD_E_NOMEM, "hipMalloc of the block workspace failed")
                                       : hip_fail(e, "hipMalloc");
+    }
+    const int pe = td_block_prepare();
+    if (pe) {
+      (void)hipFree(ctx->blockbuf);
+      ctx->blockbuf = nullptr;
+      (void)hipFree(ctx->scratch);
+      delete ctx;
+      return hip_fail((hipError_t)pe, "hipFuncSetAttribute (block GEMM)");
     }
     uint8_t* bb = (uint8_t*)ctx->blockbuf;
     ctx->blk.ncu = ncu;

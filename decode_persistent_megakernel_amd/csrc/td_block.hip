@@ -371,6 +371,230 @@ __global__ void __launch_bounds__(256) blk_gemm(const float* X, int ldx, int M, 
   }
 }
 
+// ------------------------------------------------------------ streamed GEMM
+// Y[M][N] = X[M][K] W[N][K]^T for bf16 weights and 49 <= M <= 64 token rows,
+// over the K slice [KS blockIdx.y, + KS) of at most XC 64-column chunks.  A
+// workgroup of 8 waves takes NR = 16 NT weight rows; wave w multiplies token
+// rows 16 (w & 3) .. + 15 by weight tiles (w >> 2) NT / 2 .. + NT / 2 (two
+// waves per SIMD, so one wave's matrix work covers the other's waits).
+//
+// The weights stream through a ring of SR LDS slots, one 64-column chunk
+// (NR rows x 128 bytes) each: global_load_lds copies 8 whole 128-byte rows
+// per instruction, and each wave copies 1/8 of every chunk.  Each wave loads
+// its 16 token rows' 64 input columns of the chunk straight into registers and
+// splits them into the three bf16 parts there.  A chunk's copies and input
+// loads are issued together, SR - 1 chunks ahead of their use, so one counted
+// wait covers both; the waves meet once per chunk, when all copies of the
+// chunk have landed and the slot about to be refilled has been read out by
+// all of them.  Compared with blk_gemm (weights in registers, input split in
+// LDS) this reads every weight line whole and splits each input value once
+// per pair of waves instead of staging it through LDS.
+//
+// The 16-byte units of weight row n sit in the LDS slot in the order
+// u ^ (n & 7), so that a fragment read (16 rows at one column offset) spreads
+// over the banks.  The fragments of each group of 4 tiles are read one group
+// ahead with inline ds_reads and counted waits (the compiler would read each
+// just before its use and stall on every read).
+//
+// The input and norm loads are inline-asm loads the wave waits for with an
+// exact count: the compiler, unable to order them against the LDS copies,
+// would otherwise wait for every copy in flight.  Such a load's destination
+// must stay live until the load has been waited for (the compiler, which sees
+// the value written at issue, may otherwise give a dead destination to another
+// value while the load is still in flight): inputs are loaded only for
+// chunks below XC, and every loaded register is consumed in its own
+// iteration, after its wait, also past the end of the slice.
+//
+// The products, and the order in which each chunk's partial is formed (fresh
+// per chunk, parts lo, mid, hi) and added to the running sum, are those of
+// blk_gemm: the same bits.  Outputs are stored non-temporally (the partial
+// slices are read once, by the next kernel).
+template <int NT>
+constexpr int stream_slots() {
+  return (147456 / (NT * 2048)) < 5 ? 147456 / (NT * 2048) : 5;
+}
+template <int NT>
+constexpr int stream_lds() {
+  return stream_slots<NT>() * NT * 2048;
+}
+
+DEV u32x4 ld16_asm(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
+// s_waitcnt vmcnt(n) for an n that the unrolled caller makes a constant
+DEV void vm_wait_n(int n) {
+  switch (n) {
+#define TD_VW(k) \
+  case k: vmcnt_wait<k>(); break;
+    TD_VW(0) TD_VW(1) TD_VW(2) TD_VW(3) TD_VW(4) TD_VW(5) TD_VW(6) TD_VW(7) TD_VW(8) TD_VW(9) TD_VW(10) TD_VW(11)
+    TD_VW(12) TD_VW(13) TD_VW(14) TD_VW(15) TD_VW(16) TD_VW(17) TD_VW(18) TD_VW(19) TD_VW(20) TD_VW(21) TD_VW(22)
+    TD_VW(23) TD_VW(24) TD_VW(25) TD_VW(26) TD_VW(27) TD_VW(28) TD_VW(29) TD_VW(30) TD_VW(31) TD_VW(32)
+#undef TD_VW
+    default: vmcnt_wait<0>(); break;
+  }
+}
+
+#define TD_LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int NT, int XC, bool NORM>
+__global__ void __launch_bounds__(512) blk_gemm_stream(const float* X, int ldx, int M, int K, int KS,
+                                                       const uint16_t* W, int N, float* Y, int ldy, size_t sstride,
+                                                       const float* ssq, int nbs, float eps) {
+  constexpr int NR = 16 * NT, WB = NR * 128, SR = stream_slots<NT>(), WI = WB / 8192, NTW = NT / 2;
+  static_assert(SR >= 3 && NTW % 4 == 0, "the ring keeps two chunks in flight; tiles go in groups of 4");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t ring[];
+  __shared__ float invs[NORM ? 64 : 1];
+  const int wave = threadIdx.x >> 6, lane = lane_id(), r = lane & 15, q = lane >> 4;
+  const int tw = wave & 3, th = wave >> 2;
+  const int n0 = blockIdx.x * NR;
+  const int kb = blockIdx.y * KS, nch = (min(K, kb + KS) - kb) >> 6;
+  const float* xr = X + (size_t)min(16 * tw + r, M - 1) * ldx + kb + 8 * q;
+  // NORM: the first 8 block sums of row t's sum of squares, consumed in the first chunk's iteration
+  uint32_t sv[8];
+  const int nrow = min((int)threadIdx.x & 63, M - 1);
+  if constexpr (NORM) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      asm volatile("global_load_dword %0, %1, off" : "=v"(sv[u]) : "v"(ssq + nrow * nbs + min(u, nbs - 1)) : "memory");
+  }
+  // copy sources: instruction WI wave + e of a chunk covers rows 8 (WI wave + e) + lane / 8
+  const uint8_t* wsrc[WI];
+#pragma unroll
+  for (int e = 0; e < WI; ++e) {
+    const int n = 8 * (WI * wave + e) + (lane >> 3), u = (lane & 7) ^ (n & 7);
+    wsrc[e] = (const uint8_t*)(W + (size_t)min(n0 + n, N - 1) * K + kb) + 16 * u;
+  }
+  u32x4 xq[XC][2][2];  // chunk c's inputs: columns 32 j + 8 q + 4 h of token row 16 tw + r
+  auto issue = [&](int c) {
+    const int ch = min(c, nch - 1);  // past the slice: its last chunk again (results unused)
+    if (c < XC) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xq[c][j][h] = ld16_asm(xr + 64 * ch + 32 * j + 4 * h);
+    }
+    uint8_t* base = ring + (c % SR) * WB + 1024 * WI * wave;
+#pragma unroll
+    for (int e = 0; e < WI; ++e)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[e] + ch * 128), TD_LDSPTR(base + 1024 * e), 16, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < SR - 1; ++i) issue(i);
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < XC; ++c) {
+    if (c >= nch) {  // past the slice: everything lands, then this chunk's input registers are released
+      vm_drain();
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(xq[c][j][h]));
+      continue;
+    }
+    {  // this wave's loads of chunk c have landed: later ones are chunks c + 1 .. c + SR - 2's
+      int later = 0;
+#pragma unroll
+      for (int k = c + 1; k <= c + SR - 2; ++k) later += WI + (k < XC ? 4 : 0);
+      vm_wait_n(later);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(xq[c][j][h]));
+    if (NORM && c == 0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(sv[u]));
+      float ss = __uint_as_float(sv[0]);  // the block sums added in block order
+#pragma unroll
+      for (int u = 1; u < 8; ++u)
+        if (u < nbs) ss += __uint_as_float(sv[u]);
+      for (int b = 8; b < nbs; ++b) ss += ssq[nrow * nbs + b];
+      if (threadIdx.x < 64) invs[threadIdx.x] = 1.0f / sqrtf(ss / (float)K + eps);
+    }
+    wg_bar();  // every wave's copies of chunk c; and chunk c - 1's slot has been read out
+    issue(c + SR - 1);
+    // A fragments: step j, part p (hi, mid, lo)
+    bf8v xa[2][3];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = __uint_as_float(xq[c][j][0][e]);
+        a[4 + e] = __uint_as_float(xq[c][j][1][e]);
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        u32x4 hh;
+        hh.x = hi_pair(a[0], a[1]);
+        hh.y = hi_pair(a[2], a[3]);
+        hh.z = hi_pair(a[4], a[5]);
+        hh.w = hi_pair(a[6], a[7]);
+        xa[j][p] = __builtin_bit_cast(bf8v, hh);
+        if (p < 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = drop_hi(a[e]);
+        }
+      }
+    }
+    // B fragments: weight row 16 (NTW th + t) + r, columns 32 j + 8 q (unit 4 j + q); steps
+    // s = (j, group of 4 tiles), each read one step ahead
+    constexpr int GPJ = NTW / 4, NS = 2 * GPJ;
+    u32x4 bq[NS][4];
+    const uint32_t wsa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(ring + (c % SR) * WB) +
+                         r * 128 + 2048 * NTW * th;
+    auto rd = [&](int s) {
+      const int j = s / GPJ, g = s % GPJ;
+      const uint32_t a = wsa + 16 * ((4 * j + q) ^ (r & 7)) + 2048 * 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("ds_read_b128 %0, %1" : "=v"(bq[s][i]) : "v"(a + 2048 * i));
+    };
+    f32x4 pr[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) pr[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    rd(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + 1 < NS) {
+        rd(s + 1);
+        asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(bq[s][i]));
+      const int j = s / GPJ, g = s % GPJ;
+#pragma unroll
+      for (int p = 2; p >= 0; --p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pr[4 * g + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j][p], __builtin_bit_cast(bf8v, bq[s][i]),
+                                                                  pr[4 * g + i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[t] += pr[t];
+  }
+  vm_drain();  // the copies past the slice have landed before the workgroup ends
+  wg_bar();    // invs
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int n = n0 + 16 * (NTW * th + t) + r;
+    if (n >= N) continue;
+    float* dst = Y + blockIdx.y * sstride + n;
+    const float rv[4] = {acc[t].x, acc[t].y, acc[t].z, acc[t].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int mm = 16 * tw + 4 * q + e;
+      if (mm < M) __builtin_nontemporal_store(NORM ? rv[e] * invs[mm] : rv[e], dst + (size_t)mm * ldy);
+    }
+  }
+}
+
 // ------------------------------------------------------------ QKV epilogue
 // Token i (blockIdx.y), row pair u (256 per block): the sum of the S QKV
 // partial slices, bias, RoPE of the q and k row pairs at position pos0 + i, q
@@ -669,13 +893,52 @@ int launch_gemm_f(int S, int NB, int N, hipStream_t st, const float* X, int ldx,
                 : launch_gemm_n<FMT, false>(S, NB, N, st, X, ldx, M, K, KS, W, Sc, Y, ldy, sstride, a);
 }
 
+template <int NT, int XC>
+int launch_stream(dim3 grid, hipStream_t st, const float* X, int ldx, int M, int K, int KS, const uint8_t* W, int N,
+                  float* Y, int ldy, size_t sstride, const NormArgs& a) {
+  if (a.ssq)
+    blk_gemm_stream<NT, XC, true><<<grid, 512, stream_lds<NT>(), st>>>(X, ldx, M, K, KS, (const uint16_t*)W, N, Y,
+                                                                       ldy, sstride, a.ssq, a.nbs, a.eps);
+  else
+    blk_gemm_stream<NT, XC, false><<<grid, 512, stream_lds<NT>(), st>>>(X, ldx, M, K, KS, (const uint16_t*)W, N, Y,
+                                                                        ldy, sstride, nullptr, 0, 0.f);
+  return (int)hipGetLastError();
+}
+
+template <int NT, int XC>
+int prepare_stream() {
+  for (const void* f : {(const void*)blk_gemm_stream<NT, XC, true>, (const void*)blk_gemm_stream<NT, XC, false>}) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, stream_lds<NT>());
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
+}
+
 // X W^T (with norm.ssq, X = x * gain and the rows scaled to RMSNorm(x) W^T),
 // N columns with row pitch ldy.  With
 // one K slice the result goes to Y; with S > 1 slices, slice s goes to
 // part + s M ldy and the consumer adds them in slice order.  *S_out receives S.
+// stream: the streamed GEMM may serve (bf16, 49..64 rows); the logits GEMM
+// keeps blk_gemm, so that its last row's bits match the last-row-only call.
 int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t* W, const uint16_t* Sc, int N,
-         float* Y, float* part, int ldy, int* S_out, hipStream_t st, const NormArgs& norm) {
+         float* Y, float* part, int ldy, int* S_out, hipStream_t st, const NormArgs& norm, bool stream = true) {
   int KS = 0;
+  if (stream && td_block_stream_ok(fmt, M)) {
+    int nt = 0, xc = 0;
+    const int S = td_block_stream_plan(N, K, ncu, &nt, &xc);
+    KS = 64 * xc;
+    *S_out = S;
+    float* dst = S == 1 ? Y : part;
+    const size_t sstride = (size_t)M * ldy;
+    const dim3 grid((N + 16 * nt - 1) / (16 * nt), S);
+    if (nt == 16)
+      return xc == 8   ? launch_stream<16, 8>(grid, st, X, ldx, M, K, KS, W, N, dst, ldy, sstride, norm)
+             : xc == 4 ? launch_stream<16, 4>(grid, st, X, ldx, M, K, KS, W, N, dst, ldy, sstride, norm)
+                       : launch_stream<16, 2>(grid, st, X, ldx, M, K, KS, W, N, dst, ldy, sstride, norm);
+    return xc == 8   ? launch_stream<8, 8>(grid, st, X, ldx, M, K, KS, W, N, dst, ldy, sstride, norm)
+           : xc == 4 ? launch_stream<8, 4>(grid, st, X, ldx, M, K, KS, W, N, dst, ldy, sstride, norm)
+                     : launch_stream<8, 2>(grid, st, X, ldx, M, K, KS, W, N, dst, ldy, sstride, norm);
+  }
   const int NB = nb_of((M + 15) / 16, N, ncu);
   const int S = td_block_split(N, K, ncu, 64 * NB, fmt, &KS);
   *S_out = S;
@@ -699,6 +962,19 @@ void launch_attn(const td_kparams& P, const td_blockparams* B, int n, int l, int
 }
 
 }  // namespace
+
+int td_block_prepare() {
+  static int rc = -1;  // once per process (the attribute belongs to the function, on every device)
+  if (rc < 0) {
+    rc = prepare_stream<16, 8>();
+    if (!rc) rc = prepare_stream<16, 4>();
+    if (!rc) rc = prepare_stream<16, 2>();
+    if (!rc) rc = prepare_stream<8, 8>();
+    if (!rc) rc = prepare_stream<8, 4>();
+    if (!rc) rc = prepare_stream<8, 2>();
+  }
+  return rc;
+}
 
 int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int pos0, int all_logits,
                     float* logits, int32_t* argmax_out, void* stream) {
@@ -738,7 +1014,7 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
   TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S_prev, (size_t)n * H, H, P.final_norm, B->xg, B->ssq)));
   const int r0 = all_logits ? 0 : n - 1, rows = all_logits ? n : 1;
   if ((e = gemm(TD_WF_BF16, ncu, B->xg + (size_t)r0 * H, H, rows, H, (const uint8_t*)P.head, nullptr, P.V, logits,
-                part, P.V, &S, st, NormArgs{B->ssq + (size_t)r0 * hb, hb, P.eps})))
+                part, P.V, &S, st, NormArgs{B->ssq + (size_t)r0 * hb, hb, P.eps}, false)))
     return e;
   if (S > 1) TD_CK((blk_sum_parts<<<dim3((P.V + 255) / 256, rows), 256, 0, st>>>(part, S, (size_t)rows * P.V, P.V,
                                                                                  logits)));

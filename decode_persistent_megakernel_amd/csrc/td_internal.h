@@ -257,11 +257,44 @@ static inline int td_block_split(int N, int K, int ncu, int tile_rows, int fmt, 
   return (chunks + per - 1) / per;
 }
 
+// The streamed block GEMM (bf16 weights, 49 to 64 token rows): workgroups of
+// 16 nt weight rows (nt = 16 or 8) over K slices of 64 xc columns (xc = 8, 4
+// or 2).  Among the plans whose grid fits one workgroup per CU (or, failing
+// that, the fewest rounds), the one whose workgroup moves the fewest bytes: its
+// weights, half the bytes of 64 input rows (they come from L2), a fixed fill
+// cost and, when split, its partial output.  The plan does not depend on the
+// block's row count, so the partial buffer sized for it fits every block.
+// Measured on the Llama shapes: gate/up nt 16 xc 8, down nt 8 xc 8, QKV nt 8
+// xc 4, O nt 8 xc 2.  Returns S, the number of K slices.
+static inline int td_block_stream_plan(int N, int K, int ncu, int* nt, int* xc) {
+  constexpr int M = 64;
+  const int chunks = K / 64;
+  double best = 1e300;
+  int bs = 1;
+  for (int t : {8, 16})
+    for (int c : {8, 4, 2}) {
+      const int nr = 16 * t, tiles = (N + nr - 1) / nr, S = (chunks + c - 1) / c;
+      const long grid = (long)tiles * S, rounds = (grid + ncu - 1) / ncu;
+      const double per_wg = (double)c * (nr * 128.0 + M * 128.0) + 49152.0 + (S > 1 ? 4.0 * M * nr : 0.0);
+      const double sc = (double)rounds * per_wg;
+      if (sc < best) {
+        best = sc;
+        *nt = t;
+        *xc = c;
+        bs = S;
+      }
+    }
+  return bs;
+}
+static inline bool td_block_stream_ok(int fmt, int M) { return fmt == TD_WF_BF16 && M > 48 && M <= 64; }
+
 // launch entry points (td_kernels.hip)
 int td_launch_megakernel(const td_kparams* p, int ncu, void* stream);
 // block forward (td_block.hip): logits [n][V] (all_logits) or [V] of the last token
 int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int pos0, int all_logits, float* logits,
                     int32_t* argmax_out, void* stream);
+// sets the dynamic LDS limit of the streamed block GEMM's instances (once per process)
+int td_block_prepare();
 int td_launch_repack(const td_kparams* p, int ncu, uint8_t* code, uint8_t* scale, const td_wstream* ws, int* bad,
                      void* stream);
 int td_megakernel_occupancy(int head_dim, int weight_format, int moe, int lds_bytes, int* blocks_per_cu);

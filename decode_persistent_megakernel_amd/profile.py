@@ -265,17 +265,25 @@ def stages(name: str, out: str, raw: str) -> str:
 
 
 # ---------------------------------------------------------------- block forward
+def _gemm_tile_rows(kernel: str) -> int:
+    """Weight rows per workgroup of a block GEMM instance, from its template
+    arguments: blk_gemm<FMT, MT, NB, NORM> takes 64 NB, blk_gemm_stream<NT, XC,
+    NORM> 16 NT."""
+    args = [a.strip() for a in kernel.split("<", 1)[1].rstrip(">").split(",")]
+    return 16 * int(args[0]) if kernel.startswith("blk_gemm_stream") else 64 * int(args[2])
+
+
 def block(name: str, out: str, raw: str) -> str:
     cfg = _cfg(name)
     prog = f"--config {name} --block 64 --steps 4 --warmup 1"
     d = os.path.join(raw, f"blk_{name}")
     _rocprof(["--kernel-trace", "--stats"], prog.split(), d, d + ".log", 400, "ms_per_step")
-    rows = _db(d).execute("select name, grid_x, grid_y, duration from kernels order by start").fetchall()
+    rows = _db(d).execute("select name, grid_x, workgroup_x, grid_y, duration from kernels order by start").fetchall()
     blk = [r for r in rows if "blk_" in r[0]]
     nblocks = sum(1 for r in blk if "blk_embed" in r[0])
     agg = collections.OrderedDict()
-    for n, gx, gy, du in blk:
-        key = (_short(n), gx // 256 if gx >= 256 else gx, gy)  # grid_x in workgroups
+    for n, gx, wx, gy, du in blk:
+        key = (_short(n), gx // max(wx, 1), gy)  # grid_x in workgroups
         agg.setdefault(key, []).append(du)
     H, I, V, d_ = cfg.hidden, cfg.intermediate, cfg.vocab, cfg.head_dim
     qkv_rows = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d_
@@ -286,19 +294,18 @@ def block(name: str, out: str, raw: str) -> str:
     for (k, gx, gy) in agg:
         if "gemm" not in k:
             continue
-        for tile in (64, 128):
-            if gx * tile in shapes:
-                role[(k, gx, gy)] = shapes[gx * tile]
-                break
-            if gx * tile == H:  # O, then down, in a layer's launch order
-                seen_h.append((k, gx, gy))
-                role[(k, gx, gy)] = ("O", H * cfg.n_q_heads * d_) if len(seen_h) == 1 else ("down", H * I)
-                break
+        tile = _gemm_tile_rows(k)
+        hit = [n for n in shapes if -(-n // tile) == gx]
+        if hit:
+            role[(k, gx, gy)] = shapes[hit[0]]
+        elif -(-H // tile) == gx:  # O, then down, in a layer's launch order
+            seen_h.append((k, gx, gy))
+            role[(k, gx, gy)] = ("O", H * cfg.n_q_heads * d_) if len(seen_h) == 1 else ("down", H * I)
     lines = [f"# block forward (td_forward_block), workload {name}: rocprofv3 kernel trace",
              "command: " + _cmd_text("--kernel-trace --stats", prog),
              f"(the {cfg.prompt_len}-token prompt in 64-token blocks: one untimed and three timed passes = "
              f"{nblocks} block calls; the decode launches that follow are not listed)",
-             "per-dispatch query: select name, grid_x, grid_y, duration from kernels order by start",
+             "per-dispatch query: select name, grid_x, workgroup_x, grid_y, duration from kernels order by start",
              f"sources_sha256_16 ({', '.join(BLOCK_SOURCES)}): {sources_hash(BLOCK_SOURCES)}", "",
              f"{'kernel':26} {'grid (wg)':>12} {'calls':>6} {'avg_us':>9} {'us/block':>9}  role"]
     tot = 0.0
