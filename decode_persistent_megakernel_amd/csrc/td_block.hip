@@ -641,150 +641,202 @@ __global__ void __launch_bounds__(256) blk_qkv_post(const float* part, int S, si
   }
 }
 
-// ------------------------------------------------------------ attention
-// One workgroup per (token i, kv head g): the group's query heads (at most
-// TD_MAX_GROUP) over keys 0 .. pos0 + i, which share every K and V row they
-// read.  The keys are cut into tiles of 64; wave w takes tiles w, w + 4, ...
-// and keeps, per query head, an online softmax (running max m, sum l and the
-// weighted V sum): lane t loads the K and V rows of key t of the tile together
-// (16-byte pieces), scores the key against every head and puts the V row into
-// the wave's LDS tile; then lane e accumulates output column e (and e + 64
-// when D = 128) over the tile's keys from that tile.  The four waves' states are merged in wave order at the end
-// (deterministic).  Keys past pos0 + i get probability 0 (their loads read
-// row pos0 + i instead).
-template <int D, int GRP>
-__global__ void __launch_bounds__(256) blk_attn(const float* q, const uint16_t* kc, const uint16_t* vc, int nq,
-                                                int group, int nkv, int max_ctx, int layer, int pos0, float* out) {
-  // GRP: the group size compiled for (1, 2, 4 or 8), so the per-head loops
-  // carry no branches; 0 takes any group up to TD_MAX_GROUP with the run-time
-  // count ng
-  constexpr int G = GRP ? GRP : TD_MAX_GROUP, C = D / 64;
-  const int ng = GRP ? GRP : group;
-  __shared__ __attribute__((aligned(16))) float qs[G][D];
-  __shared__ __attribute__((aligned(16))) float ps[4][64][G];  // [wave][key][head]
-  __shared__ float mst[4][G], lst[4][G];
-  __shared__ float ost[4][G][D];
-  constexpr int VP = D + 8;  // V tile row pitch, bf16 (16-byte row writes without bank conflicts)
-  __shared__ __attribute__((aligned(16))) uint16_t vs[4][64][VP];
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int i = blockIdx.x, g = blockIdx.y, h0 = g * group;
-  const int last = pos0 + i;
-  for (int e = threadIdx.x; e < G * D; e += 256) {
-    const int r = e / D;
-    qs[r][e % D] = r < ng ? q[((size_t)i * nq + h0 + r) * D + e % D] : 0.f;
+// ------------------------------------------------------------ attention on the matrix cores
+// Workgroup (x, g): kv head g and 16 of its query rows, the (token, head)
+// pairs r0 .. r0 + 15 (r0 = 16 x) of the block's n tokens and the group's
+// heads, row = token * group + head.  The scores come out transposed, S^T =
+// K Q^T, so that each lane holds one query's scores for 8 keys:
+// v_mfma_f32_16x16x32_bf16 with the keys' K rows (bf16, straight from the
+// cache) as A and the queries (fp32, split into three bf16 parts as in the
+// GEMMs: exact products) as B; result lane l holds keys 4 (l / 16) + e of a
+// 16-key block for query l % 16.  The online softmax then needs only the
+// lane's own values and the 3 other lanes of its query (two shuffles), and
+// O^T += V^T P^T takes P^T straight from those registers (split into three
+// parts) as B; the A operand, V^T, gathers each lane's 8 keys for one
+// dimension from the wave's V tile in LDS.  The MFMA's K index of lane group
+// a is the key set {4 a + e, 16 + 4 a + e}, the same in both operands.
+// Keys come in tiles of 32; wave w takes tiles w, w + 8, ... (loads of its
+// next tile in flight during this one), keeps its running max m, sum l and
+// O^T, and the 8 waves' states merge in wave order at the end
+// (deterministic).  Keys after a query's position get probability 0; loads
+// past the workgroup's last key read that key instead.
+template <int D>
+__global__ void __launch_bounds__(512) blk_attn_mma(const float* q, const uint16_t* kc, const uint16_t* vc, int nq,
+                                                    int group, int nkv, int max_ctx, int layer, int pos0, int n,
+                                                    float* out) {
+  constexpr int NS = D / 32, DB = D / 16, VP = D + 8, SEG = D / 8, VL = 32 * SEG / 64;
+  // the V tiles, and after the key loop the waves' output states in the same bytes
+  constexpr int VT_BYTES = 8 * 32 * VP * 2, OST_BYTES = 8 * 16 * (D + 1) * 4;
+  static_assert(OST_BYTES <= VT_BYTES, "the output states fit the V tiles' bytes");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[VT_BYTES];
+  __shared__ float mst[8][16], lst[8][16];
+  uint16_t(*vt)[32][VP] = (uint16_t(*)[32][VP])lds_v;
+  float(*ost)[16][D + 1] = (float(*)[16][D + 1])lds_v;
+  const int wave = threadIdx.x >> 6, lane = lane_id(), r = lane & 15, a = lane >> 4;
+  // workgroup L of a 1-D grid: kv head L % nkv, rows 16 (L / nkv) ..; the
+  // dispatcher deals workgroups to the 8 XCDs in turn, so all workgroups of a
+  // head land on the same XCDs and share their L2's copy of its K/V rows
+  const int g = blockIdx.x % nkv, rows = n * group, r0 = (blockIdx.x / nkv) * 16;
+  const int qr = min(r0 + r, rows - 1), ti = qr / group, hh = qr - ti * group;
+  const int pos_q = pos0 + ti;
+  const int last = pos0 + min(r0 + 15, rows - 1) / group;  // the workgroup's last key
+  const int ntiles = last / 32 + 1;
+  // B fragments of Q^T: columns 32 s + 8 a .. + 8 of query qr, in three parts
+  bf8v qf[NS][3];
+  {
+    const float* qp = q + ((size_t)ti * nq + g * group + hh) * D + 8 * a;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 x0 = *(const f32x4*)(qp + 32 * s), x1 = *(const f32x4*)(qp + 32 * s + 4);
+      float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        u32x4 h;
+        h.x = hi_pair(v[0], v[1]);
+        h.y = hi_pair(v[2], v[3]);
+        h.z = hi_pair(v[4], v[5]);
+        h.w = hi_pair(v[6], v[7]);
+        qf[s][p] = __builtin_bit_cast(bf8v, h);
+        if (p < 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = drop_hi(v[e]);
+        }
+      }
+    }
   }
-  __syncthreads();
   const uint16_t* K = kc + ((size_t)layer * nkv + g) * max_ctx * D;
-  const uint16_t* Vv = vc + ((size_t)layer * nkv + g) * max_ctx * D;
-  float m[G], l[G], acc[G][C];
+  const uint16_t* V = vc + ((size_t)layer * nkv + g) * max_ctx * D;
+  // a tile's loads: K fragments (key k0 + 16 b + r, columns 32 s + 8 a) and
+  // this lane's pieces of the V rows (piece lane + 64 u of the tile)
+  auto load_k = [&](int t, u32x4 (&kf)[2][NS]) {
+    const int k0 = 32 * t;
 #pragma unroll
-  for (int r = 0; r < G; ++r) {
-    m[r] = -__builtin_inff();
-    l[r] = 0.f;
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[r][c] = 0.f;
-  }
-  const int ntiles = (last + 64) / 64;
-  for (int tile = wave; tile < ntiles; tile += 4) {
-    const int t0 = tile * 64, key = t0 + lane;
-    const bool valid = key <= last;
-    const uint16_t* kr = K + (size_t)min(key, last) * D;
-    const uint16_t* vr = Vv + (size_t)min(key, last) * D;
-    u32x4 kw[D / 8], vw[D / 8];
+      for (int s = 0; s < NS; ++s)
+        kf[b][s] = *(const u32x4*)(K + (size_t)min(k0 + 16 * b + r, last) * D + 32 * s + 8 * a);
+  };
+  auto load_v = [&](int t, u32x4 (&vr)[VL]) {
+    const int k0 = 32 * t;
 #pragma unroll
-    for (int e = 0; e < D / 8; ++e) kw[e] = *(const u32x4*)(kr + 8 * e);
+    for (int u = 0; u < VL; ++u) {
+      const int idx = lane + 64 * u;
+      vr[u] = *(const u32x4*)(V + (size_t)min(k0 + idx / SEG, last) * D + 8 * (idx % SEG));
+    }
+  };
+  f32x4 o[DB];
 #pragma unroll
-    for (int e = 0; e < D / 8; ++e) vw[e] = *(const u32x4*)(vr + 8 * e);
-    // the query rows are read from LDS where they are used, not kept in registers
-    asm volatile("" ::: "memory");
-    float s[G];
+  for (int db = 0; db < DB; ++db) o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), l = 0.f;
+  // each tile's loads are issued during the previous tile: V right after the
+  // previous V went to LDS, K right after the previous scores (past the last
+  // tile: the last one again, unused)
+  u32x4 kb[2][NS], vb[VL];
+  load_k(min(wave, ntiles - 1), kb);
+  load_v(min(wave, ntiles - 1), vb);
+  // one key tile t with its loads in kf, vr; then tile tn's loads into them
+  auto tile = [&](int t, u32x4 (&kf)[2][NS], u32x4 (&vr)[VL], int tn) {
+    const int k0 = 32 * t;
+    // the V tile into LDS (this wave's own area; its reads below follow in order)
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
-      s[r] = 0.f;
-      if (r < ng) {
-        float a = 0.f;
+    for (int u = 0; u < VL; ++u) {
+      const int idx = lane + 64 * u;
+      *(u32x4*)&vt[wave][idx / SEG][8 * (idx % SEG)] = vr[u];
+    }
+    load_v(tn, vr);
+    // S^T blocks: keys k0 + 16 b .. + 16 against the 16 queries
+    f32x4 sb[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int e = 0; e < D / 8; ++e) {
-          const f32x4 qa = *(const f32x4*)&qs[r][8 * e], qb = *(const f32x4*)&qs[r][8 * e + 4];
-          a = fmaf(bf_lo(kw[e].x), qa.x, a);
-          a = fmaf(bf_hi(kw[e].x), qa.y, a);
-          a = fmaf(bf_lo(kw[e].y), qa.z, a);
-          a = fmaf(bf_hi(kw[e].y), qa.w, a);
-          a = fmaf(bf_lo(kw[e].z), qb.x, a);
-          a = fmaf(bf_hi(kw[e].z), qb.y, a);
-          a = fmaf(bf_lo(kw[e].w), qb.z, a);
-          a = fmaf(bf_hi(kw[e].w), qb.w, a);
-        }
-        s[r] = a;
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int p = 2; p >= 0; --p)
+          sb[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, kf[b][s]), qf[s][p], sb[b], 0, 0, 0);
+    load_k(tn, kf);
+    // causal mask and the tile's max over the query's 32 keys
+    float sv[8], mt = -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = k0 + 16 * b + 4 * a + e;
+        sv[4 * b + e] = key <= pos_q ? sb[b][e] : -__builtin_inff();
+        mt = fmaxf(mt, sv[4 * b + e]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float corr = m == -__builtin_inff() ? 0.f : expf(m - mn);
+    float pv[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = sv[e] == -__builtin_inff() ? 0.f : expf(sv[e] - mn);
+      ps += pv[e];
+    }
+    l = l * corr + ps;
+    m = mn;
+    // P^T in three parts; K index 8 a + e' is key 4 a + e' (e' < 4) or 16 + 4 a + e' - 4
+    bf8v pp[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      u32x4 h;
+      h.x = hi_pair(pv[0], pv[1]);
+      h.y = hi_pair(pv[2], pv[3]);
+      h.z = hi_pair(pv[4], pv[5]);
+      h.w = hi_pair(pv[6], pv[7]);
+      pp[p] = __builtin_bit_cast(bf8v, h);
+      if (p < 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = drop_hi(pv[e]);
       }
     }
 #pragma unroll
-    for (int e = 0; e < D / 8; ++e) *(u32x4*)&vs[wave][lane][8 * e] = vw[e];
+    for (int db = 0; db < DB; ++db) {
+      o[db] *= corr;
+      // A fragment of V^T: dimension 16 db + r at the lane group's 8 keys
+      const int d = 16 * db + r;
+      u32x4 w;
+      w.x = (uint32_t)vt[wave][4 * a][d] | ((uint32_t)vt[wave][4 * a + 1][d] << 16);
+      w.y = (uint32_t)vt[wave][4 * a + 2][d] | ((uint32_t)vt[wave][4 * a + 3][d] << 16);
+      w.z = (uint32_t)vt[wave][16 + 4 * a][d] | ((uint32_t)vt[wave][16 + 4 * a + 1][d] << 16);
+      w.w = (uint32_t)vt[wave][16 + 4 * a + 2][d] | ((uint32_t)vt[wave][16 + 4 * a + 3][d] << 16);
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
-      if (r < ng) {
-        const float sv = valid ? s[r] : -__builtin_inff();
-        const float mn = fmaxf(m[r], wave_max(sv));
-        const float p = valid ? expf(sv - mn) : 0.f;
-        const float corr = expf(m[r] - mn);
-        l[r] = l[r] * corr + wave_sum(p);
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc[r][c] *= corr;
-        m[r] = mn;
-        ps[wave][lane][r] = p;
-      }
+      for (int p = 2; p >= 0; --p)
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, w), pp[p], o[db], 0, 0, 0);
     }
-    // (each wave reads only its own ps rows and V tile, written by itself above)
-    const int nk = min(64, last + 1 - t0);
-#pragma unroll 8
-    for (int t = 0; t < nk; ++t) {
-      float vv[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) vv[c] = bf16f(vs[wave][t][lane + 64 * c]);
-      float pr[G];
-      if constexpr (G % 4 == 0) {
-#pragma unroll
-        for (int r = 0; r < G; r += 4) {
-          const f32x4 pv = *(const f32x4*)&ps[wave][t][r];
-          pr[r] = pv.x;
-          pr[r + 1] = pv.y;
-          pr[r + 2] = pv.z;
-          pr[r + 3] = pv.w;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < G; ++r) pr[r] = ps[wave][t][r];
-      }
-#pragma unroll
-      for (int r = 0; r < G; ++r)
-        if (r < ng) {
-#pragma unroll
-          for (int c = 0; c < C; ++c) acc[r][c] = fmaf(pr[r], vv[c], acc[r][c]);
-        }
-    }
+  };
+  for (int t = wave; t < ntiles; t += 8) tile(t, kb, vb, min(t + 8, ntiles - 1));
+  // the query's sum over its 4 lanes; the wave's state to LDS
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (a == 0) {
+    mst[wave][r] = m;
+    lst[wave][r] = l;
   }
-  // merge the waves' states in wave order
+  __syncthreads();  // every wave is done with its V tile: the bytes now hold the output states
 #pragma unroll
-  for (int r = 0; r < G; ++r) {
-    if (lane == 0) {
-      mst[wave][r] = m[r];
-      lst[wave][r] = l[r];
-    }
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int c = 0; c < C; ++c) ost[wave][r][64 * c + lane] = acc[r][c];
-  }
+    for (int e = 0; e < 4; ++e) ost[wave][r][16 * db + 4 * a + e] = o[db][e];
   __syncthreads();
-  for (int e = threadIdx.x; e < group * D; e += 256) {
-    const int r = e / D, col = e % D;
-    float M = mst[0][r];
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mst[w][r]);
+  // merge in wave order; output (row r0 + qq, dimension d)
+  for (int idx = threadIdx.x; idx < 16 * D; idx += 512) {
+    const int qq = idx / D, d = idx - qq * D, row = r0 + qq;
+    if (row >= rows) continue;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < 8; ++w) M = fmaxf(M, mst[w][qq]);
     float L = 0.f, O = 0.f;
-    for (int w = 0; w < 4; ++w) {
-      const float f = mst[w][r] == -__builtin_inff() ? 0.f : expf(mst[w][r] - M);
-      L = fmaf(lst[w][r], f, L);
-      O = fmaf(ost[w][r][col], f, O);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      if (mst[w][qq] == -__builtin_inff()) continue;
+      const float f = expf(mst[w][qq] - M);
+      L = fmaf(lst[w][qq], f, L);
+      O = fmaf(ost[w][qq][d], f, O);
     }
-    out[((size_t)i * nq + h0 + r) * D + col] = O / L;
+    const int i = row / group, h = row - i * group;
+    out[((size_t)i * nq + g * group + h) * D + d] = O / L;
   }
 }
 
@@ -950,15 +1002,8 @@ int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t*
 
 template <int D>
 void launch_attn(const td_kparams& P, const td_blockparams* B, int n, int l, int pos0, hipStream_t st) {
-  const dim3 grid(n, P.nkv);
-#define TD_ATTN(G_) \
-  blk_attn<D, G_><<<grid, 256, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0, B->ao)
-  if (P.group == 1) TD_ATTN(1);
-  else if (P.group == 2) TD_ATTN(2);
-  else if (P.group == 4) TD_ATTN(4);
-  else if (P.group == 8) TD_ATTN(8);
-  else TD_ATTN(0);
-#undef TD_ATTN
+  const dim3 grid((n * P.group + 15) / 16 * P.nkv);
+  blk_attn_mma<D><<<grid, 512, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0, n, B->ao);
 }
 
 }  // namespace
