@@ -404,11 +404,14 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
   td_kparams kp{};
   int64_t fixed = 0;
   const int64_t per_slot = (int64_t)TD_NW * (TD_CHUNK + (c.weight_format == TD_WF_INT4_G64 ? TD_SCHUNK : 0));
-  // a second K/V tile buffer (the next tile loads while one is consumed) when a
-  // chunk spans several tiles and the rings keep at least TD_RING_MIN2 slots
+  // more K/V tile buffers (nb - 1 tiles in flight while one is consumed) when a
+  // chunk spans at least nb tiles and the rings keep at least TD_RING_MIN2
+  // (two buffers) or TD_RING_MIN3 (three) slots; three only at d = 64, where a
+  // tile is 17 copy instructions and two tiles in flight stay within the wait
+  // counts the sync wave uses (34)
   kp.tile_stride = (int32_t)round_up(td_tile_bytes(d), 256);
   kp.tile_bufs = 1;
-  for (int nb = 2; nb >= 1; --nb) {
+  for (int nb = d == 64 ? 3 : 2; nb >= 1; --nb) {
     int64_t off = 0;
     kp.off_xin = kp.off_attn = (int32_t)off;
     off += round_up(xin_bytes, 1024);
@@ -427,7 +430,8 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
     if (E) off += (TD_MAX_EXPERTS + TD_NW * 2 * TD_MAX_TOPK) * 4;
     fixed = round_up(off, 1024);
     kp.tile_bufs = nb;
-    if (nb == 1 || (chunk_len > TD_TILE && (lds_cap - fixed) / per_slot >= TD_RING_MIN2)) break;
+    if (nb == 1 || (chunk_len > (nb - 1) * TD_TILE && (lds_cap - fixed) / per_slot >= (nb == 3 ? TD_RING_MIN3 : TD_RING_MIN2)))
+      break;
   }
   const int64_t ring = std::min<int64_t>(TD_RING_MAX, (lds_cap - fixed) / per_slot);
   if (ring < TD_RING_MIN) return fail(TD_E_UNSUPPORTED, "the LDS cannot hold the weight rings for this shape");

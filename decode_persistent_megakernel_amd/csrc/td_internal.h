@@ -15,6 +15,7 @@
 #define TD_SPIN_TICKS 100000000ull    // wait limit in 100 MHz ticks (1 s)
 #define TD_RING_MIN 4                 // fewest ring slots per compute wave the plan accepts
 #define TD_RING_MIN2 9                // fewest ring slots with which a second attention tile buffer is taken
+#define TD_RING_MIN3 7                // fewest ring slots with which a third attention tile buffer is taken
 #ifndef TD_RING_MAX
 #define TD_RING_MAX 24
 #endif

@@ -315,10 +315,11 @@ DEV AttnTask attn_task(const td_kparams& P, int cu, int pos) {
   return t;
 }
 
-// LDS buffer of the k-th tile made ready (counted over the whole launch): with
-// two buffers the next tile loads while the current one is consumed.
+// LDS buffer of the k-th tile (counted over the whole launch): with nb
+// buffers, nb - 1 tiles are in flight while one is consumed.
 DEV uint8_t* tile_buf(const td_kparams& P, uint8_t* lds, uint32_t k) {
-  return lds + P.off_tile + (P.tile_bufs > 1 ? (int)(k & 1u) * P.tile_stride : 0);
+  const uint32_t b = P.tile_bufs == 3 ? k % 3u : k & (uint32_t)(P.tile_bufs - 1);  // 1, 2 or 3 buffers
+  return lds + P.off_tile + (int)b * P.tile_stride;
 }
 
 // K and V rows [tb, tb + nv) of the tile, except row pos (written during this
@@ -359,6 +360,38 @@ DEV void load_tile(const td_kparams& P, uint8_t* buf, int layer, const AttnTask&
   }
 }
 
+// The same rows by LDS DMA (buffer_load ... lds, 16 bytes per lane, one KiB
+// per instruction), so that the sync wave can keep several tiles in flight
+// (three tile buffers; with fewer, load_tile's register path is as fast and
+// does not share the LDS-DMA path with the weight streams): K rows
+// at a pitch of 2 d + 16 bytes (a lane whose 16 bytes fall in a row's padding
+// reads that row's first bytes again), then V rows unpadded.  Rows past the
+// chunk end read as zero (the buffer's range ends there).  The loads are
+// agent-scope: rows written by an earlier step of the same launch come from
+// other CUs.  Row pos (written during this very step) arrives stale and is
+// replaced from the published copy once the tile has landed (patch_pos_row).
+// 17 instructions per tile at d = 64.
+#define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
+DEV void issue_tile(const td_kparams& P, uint8_t* buf, int layer, const AttnTask& T, int tile) {
+  const int lane = lane_id();
+  const int d = P.d;
+  const int tb = T.t0 + tile * TD_TILE;
+  const int nv = min(TD_TILE, T.t1 - tb);
+  const size_t head_off = ((size_t)layer * P.nkv + T.g) * P.max_ctx;
+  const __amdgpu_buffer_rsrc_t RK = rsrc(P.kc + (head_off + tb) * d, (uint32_t)(nv * d * 2));
+  const __amdgpu_buffer_rsrc_t RV = rsrc(P.vc + (head_off + tb) * d, (uint32_t)(nv * d * 2));
+  const int kpitch = 2 * d + 16, kw = TD_TILE * kpitch / 1024, vw = TD_TILE * 2 * d / 1024;
+  for (int w = 0; w < kw; ++w) {
+    const int off = 1024 * w + 16 * lane, row = off / kpitch, in = off - row * kpitch;
+    const uint32_t src = (uint32_t)(row * 2 * d + (in < 2 * d ? in : 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(RK, LDSPTR(buf + 1024 * w), 16, src, 0, 0, TD_CPOL_SC1);
+  }
+  uint8_t* vb = buf + TD_TILE * kpitch;
+  for (int w = 0; w < vw; ++w)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(RV, LDSPTR(vb + 1024 * w), 16, (uint32_t)(1024 * w + 16 * lane), 0, 0,
+                                             TD_CPOL_SC1);
+}
+
 // this position's K and V rows (LDS fp32 holding bf16 values) into the tile
 // when the tile holds position pos
 DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, uint8_t* buf, const AttnTask& T, int tile, int pos) {
@@ -393,7 +426,6 @@ DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, uint8_t* buf, const At
 // start over, and the next step's first chunks stream while its token is
 // decided.  (The per-chunk path is kept free of any step logic: each
 // instruction there is paid once per KiB streamed.)
-#define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
 #define TD_DMA_NT 2   // cache policy of the weight stream: non-temporal
 #ifndef TD_FLIGHT
 #define TD_FLIGHT 6   // chunks of its own stream a compute wave keeps in flight at most
@@ -1197,39 +1229,58 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
     if ((tok < 0 || tok >= P.V) && lane == 0 && cu == 0) atomicOr(P.err, TD_ERRBIT_RANGE);
   }
   const int G = P.group;
-  uint32_t tiles_ready = 0, rv_base = 0;
+  uint32_t tiles_ready = 0, tiles_issued = 0, rv_base = 0;
   if (P.step_clock && cu == 0 && lane == 0) P.step_clock[0] = wall_clock64();
   for (int step = 0;; ++step) {
     const int pos = P.pos + step;
     const AttnTask T = attn_task(P, cu, pos);
-    // a tile's buffer is free once the tile tile_bufs places earlier is consumed
+    // a tile's buffer is free once the tile tile_bufs places earlier is
+    // consumed; tiles [tiles_ready, tiles_issued) have their copies in flight
     const uint32_t nb = (uint32_t)P.tile_bufs;
     auto buf_free = [&](uint32_t k) { return (uint32_t)G * (k + 1u > nb ? k + 1u - nb : 0u); };
-    if (T.valid) {  // layer 0's first tile
-      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
-      load_tile(P, tile_buf(P, lds, tiles_ready), 0, T, 0, pos);
-    }
-    for (int layer = 0; T.valid && layer < P.L; ++layer) {
-      // ATTN of this layer is the (spl layer + 1)-th stage the compute waves take part in
-      (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, SPL * layer + 1), ok);
-      patch_pos_row(P, lds, tile_buf(P, lds, tiles_ready), T, 0, pos);
+    const bool dma = nb >= 3 && P.d == 64;  // (the waits below count 17 copies a tile)
+    auto issue = [&](int layer, int tile) {
+      (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_issued), ok);
+      if (dma) issue_tile(P, tile_buf(P, lds, tiles_issued), layer, T, tile);
+      else load_tile(P, tile_buf(P, lds, tiles_issued), layer, T, tile, pos);  // (in LDS on return)
+      ++tiles_issued;
+    };
+    // the oldest tile in flight: landed (only the copies issued after it may
+    // be outstanding), its position row replaced, published to the compute waves
+    auto ready = [&](int tile) {
+      if (dma) {  // three buffers (d = 64, 17 copies a tile): at most two later tiles in flight
+        const uint32_t later = tiles_issued - tiles_ready - 1u;
+        if (later >= 2u) vmcnt_wait<34>();
+        else if (later == 1u) vmcnt_wait<17>();
+        else vmcnt_wait<0>();
+      }
+      patch_pos_row(P, lds, tile_buf(P, lds, tiles_ready), T, tile, pos);
       lds_fence();
       lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
-      for (int tile = 1; tile < T.ntiles; ++tile) {
-        (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
-        uint8_t* b = tile_buf(P, lds, tiles_ready);
-        load_tile(P, b, layer, T, tile, pos);
-        patch_pos_row(P, lds, b, T, tile, pos);
-        lds_fence();
-        lds_st(ctl + TD_CTL_TREADY, ++tiles_ready);
+    };
+    // A layer's first tiles (as many as there are buffers) are issued ahead:
+    // rows before pos are final, and row pos is patched when the tile is made
+    // ready.  Within the layer a tile is issued once tile r, the next to be
+    // made ready, needs it (one buffer) or while it is fewer than nb - 1 tiles
+    // ahead of r: its buffer's previous tile, two behind r, is consumed by then
+    // or soon, and the compute waves already hold tile r - 1.  (One issue site
+    // per phase keeps the loaders' code from being inlined more often.)
+    for (int layer = -1; T.valid && layer < P.L; ++layer) {
+      if (layer >= 0) {
+        // ATTN of this layer is the (spl layer + 1)-th stage the compute waves take part in
+        (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, SPL * layer + 1), ok);
+        int next = min(T.ntiles, (int)nb), r = 0;
+        while (r < T.ntiles) {
+          if (next < T.ntiles && (next <= r || next < r + (int)nb - 1)) issue(layer, next++);
+          else ready(r++);
+        }
       }
       if (layer + 1 < P.L) {
-        // the next layer's first tile once its buffer is free and the stage
-        // after O (GU, or the router of a MoE layer), whose input poll is on
-        // the critical path, has its inputs
-        (void)lds_wait_ge(P, ctl + TD_CTL_TDONE, buf_free(tiles_ready), ok);
-        (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, SPL * layer + 3), ok);
-        load_tile(P, tile_buf(P, lds, tiles_ready), layer + 1, T, 0, pos);
+        // the next layer's first tiles once the stage after O (GU, or the
+        // router of a MoE layer), whose input poll is on the critical path, has
+        // its inputs (every tile of this layer is consumed by then)
+        if (layer >= 0) (void)lds_wait_ge(P, ctl + TD_CTL_RV, staged_target(rv_base, SPL * layer + 3), ok);
+        for (int tile = 0; tile < T.ntiles && tile < (int)nb; ++tile) issue(layer + 1, tile);
       }
     }
     // every tile consumed: the tile area takes the candidates below
