@@ -319,7 +319,7 @@ def block(name: str, out: str, raw: str) -> str:
                   f"({64 / (tot / nblocks * 1e-6):.0f} tokens/s)"]
     for key, (rname, n_w) in role.items():
         us = sum(agg[key]) / len(agg[key]) / 1e3
-        b = n_w * eb
+        b = n_w * (2 if rname == "logits" else eb)  # the output head is bf16 in every format
         lines.append(f"{rname} GEMM: {b:.0f} weight bytes per call / {us:.2f} us = {b / us / 1e3:.0f} GB/s "
                      f"({b / us / 1e3 / PEAK_GBS:.3f} of 8000 GB/s)")
     path = os.path.join(out, f"block_{name}_kernel_trace.txt")

@@ -124,8 +124,11 @@ MHA1_LONG = synth.shrink(MHA1, name="mha_d64_long", max_ctx=2304, seed=2012)
     (SPLITK, 255 - 15, 16),  # ends at the last cache position
     (MHA1, 70, 24),          # one query head per kv head (the attention's group-1 instance)
     (MHA1_LONG, 2100, 22),   # group 1 past 2048 cached keys (33 key tiles per token)
+    (SPLITK, 100, 57),       # the streamed GEMM (49..64 rows) with a ragged last token tile
+    (RAGGED4, 40, 64),       # int4 weights at the largest block, K = 640 in the down projection
+    (RAGGED4, 10, 49),       # int4 weights, 49 rows (a ragged fourth token tile)
 ], ids=["d64_edge", "d128_bias", "int4_ragged", "max_block", "single_row", "last_position", "group1",
-        "group1_long"])
+        "group1_long", "stream_bf16_57", "int4_64", "int4_49"])
 def test_block_matches_oracle(td, cfg, pos0, n):
     m = synth.make_model(cfg)
     k, v = synth.random_kv_prefix(cfg, pos0, seed_tag="block")
@@ -259,6 +262,7 @@ def test_argument_checks(td):
     ("llama1b", 100, 16, 2 ** -12),
     ("tinyllama_int4", 100, 16, 2 ** -12),
     ("qwen1p5b", 1000, 24, 2 ** -12),  # d = 128, QKV bias, 28 layers, two 16-row tiles
+    ("tinyllama_int4", 60, 52, 2 ** -12),  # int4 weights at full size, 52 rows
     # int4, 33 rows over an 8192-position random N(0, 1) prefix.  Attention over
     # 8192 random rows cancels heavily, and fp32 arithmetic (the decode kernel's
     # as much as the block's) then differs from the fp64 oracle by up to one bf16
