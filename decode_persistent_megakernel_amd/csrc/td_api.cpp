@@ -740,6 +740,9 @@ int td_create(const td_config* cfg, const td_weights* w, int32_t executor, td_ct
         const int S = td_block_split(g[0], g[1], ncu, tile_rows, g[3], &KS);
         if (S > 1 || g[2]) part_floats = std::max(part_floats, (size_t)S * R * g[0]);
       }
+    // the block attention's key splits use the same buffer (between the QKV
+    // epilogue and the O GEMM, when it holds nothing)
+    part_floats = std::max(part_floats, td_block_attn_part_floats(nkv, group, d, c.max_ctx, ncu));
     for (int gi = 0; gi < 4; ++gi) {  // the streamed GEMM's slices (bf16, all but the logits GEMM)
       const auto& g = gem[gi];
       if (g[3] != TD_WF_BF16) continue;

@@ -660,10 +660,15 @@ __global__ void __launch_bounds__(256) blk_qkv_post(const float* part, int S, si
 // O^T, and the 8 waves' states merge in wave order at the end
 // (deterministic).  Keys after a query's position get probability 0; loads
 // past the workgroup's last key read that key instead.
+//
+// Long contexts split the key tiles over nsplit workgroups per (rows, head),
+// contiguous ranges in split order: each writes its merged (O, m, l) to
+// part[sp][g][row] (O unnormalised, relative to m) and blk_attn_merge combines
+// the splits in split order.  With nsplit = 1 the output is written here.
 template <int D>
 __global__ void __launch_bounds__(512) blk_attn_mma(const float* q, const uint16_t* kc, const uint16_t* vc, int nq,
                                                     int group, int nkv, int max_ctx, int layer, int pos0, int n,
-                                                    float* out) {
+                                                    int nsplit, float* part, float* out) {
   constexpr int NS = D / 32, DB = D / 16, VP = D + 8, SEG = D / 8, VL = 32 * SEG / 64;
   // the V tiles, and after the key loop the waves' output states in the same bytes
   constexpr int VT_BYTES = 8 * 32 * VP * 2, OST_BYTES = 8 * 16 * (D + 1) * 4;
@@ -673,14 +678,17 @@ __global__ void __launch_bounds__(512) blk_attn_mma(const float* q, const uint16
   uint16_t(*vt)[32][VP] = (uint16_t(*)[32][VP])lds_v;
   float(*ost)[16][D + 1] = (float(*)[16][D + 1])lds_v;
   const int wave = threadIdx.x >> 6, lane = lane_id(), r = lane & 15, a = lane >> 4;
-  // workgroup L of a 1-D grid: kv head L % nkv, rows 16 (L / nkv) ..; the
-  // dispatcher deals workgroups to the 8 XCDs in turn, so all workgroups of a
-  // head land on the same XCDs and share their L2's copy of its K/V rows
-  const int g = blockIdx.x % nkv, rows = n * group, r0 = (blockIdx.x / nkv) * 16;
+  // workgroup L of a 1-D grid: kv head L % nkv, rows 16 x, key split sp with
+  // x + nx sp = L / nkv; the dispatcher deals workgroups to the 8 XCDs in
+  // turn, so all workgroups of a head land on the same XCDs and share their
+  // L2's copy of its K/V rows
+  const int rows = n * group, nx = (rows + 15) / 16, g = blockIdx.x % nkv;
+  const int r0 = (blockIdx.x / nkv % nx) * 16, sp = blockIdx.x / nkv / nx;
   const int qr = min(r0 + r, rows - 1), ti = qr / group, hh = qr - ti * group;
   const int pos_q = pos0 + ti;
   const int last = pos0 + min(r0 + 15, rows - 1) / group;  // the workgroup's last key
-  const int ntiles = last / 32 + 1;
+  const int ntiles_all = last / 32 + 1;
+  const int t_lo = ntiles_all * sp / nsplit, ntiles = ntiles_all * (sp + 1) / nsplit;  // this split: [t_lo, ntiles)
   // B fragments of Q^T: columns 32 s + 8 a .. + 8 of query qr, in three parts
   bf8v qf[NS][3];
   {
@@ -732,8 +740,8 @@ __global__ void __launch_bounds__(512) blk_attn_mma(const float* q, const uint16
   // previous V went to LDS, K right after the previous scores (past the last
   // tile: the last one again, unused)
   u32x4 kb[2][NS], vb[VL];
-  load_k(min(wave, ntiles - 1), kb);
-  load_v(min(wave, ntiles - 1), vb);
+  load_k(max(min(t_lo + wave, ntiles - 1), 0), kb);
+  load_v(max(min(t_lo + wave, ntiles - 1), 0), vb);
   // one key tile t with its loads in kf, vr; then tile tn's loads into them
   auto tile = [&](int t, u32x4 (&kf)[2][NS], u32x4 (&vr)[VL], int tn) {
     const int k0 = 32 * t;
@@ -806,7 +814,7 @@ __global__ void __launch_bounds__(512) blk_attn_mma(const float* q, const uint16
         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, w), pp[p], o[db], 0, 0, 0);
     }
   };
-  for (int t = wave; t < ntiles; t += 8) tile(t, kb, vb, min(t + 8, ntiles - 1));
+  for (int t = t_lo + wave; t < ntiles; t += 8) tile(t, kb, vb, min(t + 8, ntiles - 1));
   // the query's sum over its 4 lanes; the wave's state to LDS
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -835,9 +843,41 @@ __global__ void __launch_bounds__(512) blk_attn_mma(const float* q, const uint16
       L = fmaf(lst[w][qq], f, L);
       O = fmaf(ost[w][qq][d], f, O);
     }
-    const int i = row / group, h = row - i * group;
-    out[((size_t)i * nq + g * group + h) * D + d] = O / L;
+    if (nsplit == 1) {
+      const int i = row / group, h = row - i * group;
+      out[((size_t)i * nq + g * group + h) * D + d] = O / L;
+    } else {
+      float* ps = part + (((size_t)sp * nkv + g) * rows + row) * (D + 2);
+      ps[d] = O;
+      if (d == 0) {
+        ps[D] = M;
+        ps[D + 1] = L;
+      }
+    }
   }
+}
+
+// The key splits of blk_attn_mma combined in split order: thread (row, d) of
+// kv head g (blockIdx.y) over rows 512 / D blockIdx.x ...
+template <int D>
+__global__ void __launch_bounds__(512) blk_attn_merge(const float* part, int nsplit, int nq, int group, int nkv, int n,
+                                                      float* out) {
+  const int g = blockIdx.y, rows = n * group;
+  const int row = blockIdx.x * (512 / D) + (int)threadIdx.x / D, d = threadIdx.x % D;
+  if (row >= rows) return;
+  auto at = [&](int s) { return part + (((size_t)s * nkv + g) * rows + row) * (D + 2); };
+  float M = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, at(s)[D]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* ps = at(s);
+    if (ps[D] == -__builtin_inff()) continue;
+    const float f = expf(ps[D] - M);
+    L = fmaf(ps[D + 1], f, L);
+    O = fmaf(ps[d], f, O);
+  }
+  const int i = row / group, h = row - i * group;
+  out[((size_t)i * nq + g * group + h) * D + d] = O / L;
 }
 
 // ------------------------------------------------------------ greedy token
@@ -1001,9 +1041,15 @@ int gemm(int fmt, int ncu, const float* X, int ldx, int M, int K, const uint8_t*
 }
 
 template <int D>
-void launch_attn(const td_kparams& P, const td_blockparams* B, int n, int l, int pos0, hipStream_t st) {
-  const dim3 grid((n * P.group + 15) / 16 * P.nkv);
-  blk_attn_mma<D><<<grid, 512, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l, pos0, n, B->ao);
+int launch_attn(const td_kparams& P, const td_blockparams* B, int n, int l, int pos0, hipStream_t st) {
+  const int rows = n * P.group, nx = (rows + 15) / 16;
+  const int nsplit = td_block_attn_split(nx * P.nkv, (pos0 + n - 1) / 32 + 1, B->ncu);
+  blk_attn_mma<D><<<dim3(nx * P.nkv * nsplit), 512, 0, st>>>(B->q, P.kc, P.vc, P.nq, P.group, P.nkv, P.max_ctx, l,
+                                                             pos0, n, nsplit, B->part, B->ao);
+  if (nsplit > 1)
+    blk_attn_merge<D><<<dim3((rows + 512 / D - 1) / (512 / D), P.nkv), 512, 0, st>>>(B->part, nsplit, P.nq, P.group,
+                                                                                     P.nkv, n, B->ao);
+  return (int)hipGetLastError();
 }
 
 }  // namespace
@@ -1047,7 +1093,7 @@ int td_launch_block(const td_blockparams* B, const int32_t* tokens, int n, int p
     TD_CK((blk_qkv_post<<<dim3((P.qkv_rows / 2 + 255) / 256, n), 256, 0, st>>>(
         S == 1 ? B->y : part, S, (size_t)n * P.qkv_rows, P.qkv_rows, qd, P.kvd, d, P.nkv, P.max_ctx, l, pos0, Ld.bias,
         P.rope_cs, P.attn_scale, B->q, P.kc, P.vc)));
-    TD_CK(d == 64 ? launch_attn<64>(P, B, n, l, pos0, st) : launch_attn<128>(P, B, n, l, pos0, st));
+    if ((e = d == 64 ? launch_attn<64>(P, B, n, l, pos0, st) : launch_attn<128>(P, B, n, l, pos0, st))) return e;
     // the O and down projections always land in part (slice 0 when unsplit)
     if ((e = gemm(P.wf, ncu, B->ao, qd, n, qd, Ld.w[1], Ld.s[1], H, part, part, H, &S, st, no_norm))) return e;
     TD_CK((blk_resid<<<rgrid, 256, 0, st>>>(B->x, part, S, (size_t)n * H, H, Ld.mlp_norm, B->xg, B->ssq)));

@@ -289,6 +289,29 @@ static inline int td_block_stream_plan(int N, int K, int ncu, int* nt, int* xc) 
 }
 static inline bool td_block_stream_ok(int fmt, int M) { return fmt == TD_WF_BF16 && M > 48 && M <= 64; }
 
+// Key splits of the block attention: the workgroups of one split (base of
+// them) use fewer than half the CUs and the keys span at least 64 tiles of 32
+// (2048 positions), so more workgroups share the K/V reads; at most 4, and
+// every split keeps 8 tiles (one per wave) or more.  Short prompts keep one
+// launch (a split costs a merge launch).
+static inline int td_block_attn_split(int base, int ntiles, int ncu) {
+  if (ntiles < 64 || 2 * base > ncu) return 1;
+  int s = ncu / base;
+  if (s > 4) s = 4;
+  if (s > ntiles / 8) s = ntiles / 8;
+  return s < 1 ? 1 : s;
+}
+// scratch floats the block attention's splits need, the most over blocks of
+// 1..TD_MAX_BLOCK rows: nsplit x nkv x rows x (D + 2)
+static inline size_t td_block_attn_part_floats(int nkv, int group, int d, int max_ctx, int ncu) {
+  size_t most = 0;
+  for (int n = 1; n <= TD_MAX_BLOCK; ++n) {
+    const int rows = n * group, nx = (rows + 15) / 16, s = td_block_attn_split(nx * nkv, max_ctx / 32 + 1, ncu);
+    if (s > 1 && (size_t)s * nkv * rows * (d + 2) > most) most = (size_t)s * nkv * rows * (d + 2);
+  }
+  return most;
+}
+
 // launch entry points (td_kernels.hip)
 int td_launch_megakernel(const td_kparams* p, int ncu, void* stream);
 // block forward (td_block.hip): logits [n][V] (all_logits) or [V] of the last token
