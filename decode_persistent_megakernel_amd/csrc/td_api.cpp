@@ -346,7 +346,7 @@ int attention_split(const td_config& c, int ncu, int* chunk_len_out, int* n_chun
   const int cmax_by_cu = ncu / nkv;
   int chunk_len = (int)round_up(std::max<int64_t>(1, ((int64_t)c.max_ctx + cmax_by_cu - 1) / cmax_by_cu), TD_TILE);
   auto n_chunks_of = [&](int cl) { return (c.max_ctx + cl - 1) / cl; };
-  const int64_t topk_i = c.n_experts > 0 ? (int64_t)c.top_k * I : 0;
+  const int64_t topk_i = c.n_experts > 0 ? (int64_t)td_moe_down_reach(c.top_k, I) : 0;
   const int64_t kpad_in = round_up(std::max<int64_t>({H, qd, I, topk_i}), 2048);
   const int64_t merge_budget = std::max<int64_t>(
       24 * 1024, kpad_in * 4 + td_tile_bytes(d) - ((int64_t)group * d * 4 + 2 * d * 4 + (int64_t)group * TD_TILE * 4));
@@ -397,7 +397,8 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
   // LDS layout: the rings take what the rest leaves, up to TD_RING_MAX slots per wave
   const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
   // the GEMV input area holds the longest input: a MoE down stage's is top_k slots of I
-  const int64_t kpad = round_up(std::max({H, qd, I, topk * I}), 2048);
+  // (a MoE down stage reads its last slot's whole chunks: td_moe_down_reach)
+  const int64_t kpad = round_up(std::max({H, qd, I, E ? td_moe_down_reach(topk, I) : 0}), 2048);
   // the attention area aliases the input area; its merge staging (used after the
   // CU's tiles) may run on into the first tile buffer, which follows
   const int64_t xin_bytes = std::max<int64_t>({kpad * 4, (int64_t)A.merge, A.bytes - td_tile_bytes(d)});

@@ -208,6 +208,16 @@ static inline td_attn_lds td_attn_layout(int d, int group, int n_chunks_max) {
   return a;
 }
 
+// How far into the LDS input area a mixture-of-experts down stage reads: slot j's
+// activations start at j I, and a down row's whole chunks (512 bf16 weights
+// each, zero weights past I) read 512 ceil(I / 512) activations from there, so
+// the last slot reads up to (top_k - 1) I + 512 ceil(I / 512); the stage zeroes
+// the input area from top_k I up to that point (0 x a stale NaN would be NaN).
+#ifdef __HIPCC__
+__host__ __device__
+#endif
+static inline int td_moe_down_reach(int top_k, int I) { return (top_k - 1) * I + (I + 511) / 512 * 512; }
+
 // Input slice of compute wave w (of TD_NW) over a K-element vector, in whole
 // (value, tag) pair units of two elements: [lo, hi).
 #ifdef __HIPCC__

@@ -816,9 +816,11 @@ DEV void stage_gemv_input(const td_kparams& P, CS& C, int wave, int kind, int K,
       C.xin[2 * u + 1] *= bf_hi(g);
     }
   }
-  if (wave == TD_NW - 1) {
+  if (wave == TD_NW - 1) {  // the zero activations the padded tail of a row's last chunk meets
     const int ce = P.wf && kind != TD_ST_HEAD ? 2048 : 512;
-    const int kp = (K + ce - 1) / ce * ce;
+    int kp = (K + ce - 1) / ce * ce;
+    if constexpr (CS::kMoe)
+      if (kind == TD_ST_DOWN) kp = max(kp, td_moe_down_reach(P.topk, P.I));  // bf16 expert rows
     for (int i = K + lane_id(); i < kp; i += 64) C.xin[i] = 0.f;
   }
 }

@@ -208,3 +208,29 @@ def test_tied_router_logits_take_the_lower_id_first(td):
     assert tr["expert_ids"][0][:3].tolist() == sorted([top] + twins)  # the oracle's own tie order
     for ex in (td.TD_EXEC_PER_OP, td.TD_EXEC_GRAPH, td.TD_EXEC_MEGAKERNEL):
         _run(td, cfg, m, k, v, synth.first_token(cfg), 30, 4, ex, f"ties/{ex}")
+
+
+@pytest.mark.parametrize("cfg,start", [(MOE_MAX, 40), (MOE_BF16, 30), (MOE_D128, 60)],
+                         ids=["e256k16", "bf16_e16k4", "d128_e64k8"])
+def test_moe_down_reads_no_stale_input(td, cfg, start):
+    """Regression: a MoE down row shorter than its whole chunks meets zero
+    weights in its padded lanes, against the activations after its slot, and
+    the last slot's reach runs past top_k I.  The persistent kernel zeroes its
+    input area out to that reach; before, the stage read whatever an earlier
+    kernel had left in LDS there, and a stale NaN made the router logits of the
+    next layer NaN (0 x NaN).  Here an earlier kernel leaves NaN in every CU's
+    LDS on purpose: the GEMV hook stages a NaN input of 32768 values (128 KiB)
+    on a grid of one workgroup per CU, then the MoE step must still match the
+    oracle.  These shapes have top_k I a multiple of 512 (no zero padding past
+    top_k I without the reach) and down rows of 64 to 256 values."""
+    rows, cols = 2048, 32768
+    w = torch.zeros((rows, cols), dtype=torch.int16, device="cuda")
+    x = torch.full((cols,), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    m = synth.make_model(cfg)
+    k, v = synth.random_kv_prefix(cfg, start, seed_tag="moe")
+    for rep in range(2):
+        td.gemv(synth.WF_BF16, w, None, rows, cols, x, y)
+        torch.cuda.synchronize()
+        assert torch.isnan(y).all()  # the hook ran on the NaN input
+        _run(td, cfg, m, k, v, synth.first_token(cfg), start, 2, td.TD_EXEC_MEGAKERNEL, f"{cfg.name}/stale-lds{rep}")
