@@ -240,10 +240,12 @@ def gemv(fmt: int, w, s, rows: int, cols: int, x, y, stream=None) -> None:
                "td_test_gemv")
 
 
-def attention(q, k, v, n_pos: int, head_dim: int, out, chunk_len: int = 0, stream=None) -> None:
-    """One query head over n_pos K/V rows through the step's tile and merge routines (test hook)."""
-    _lib.check(_lib.lib().td_test_attention(_ptr(q), _ptr(k), _ptr(v), n_pos, head_dim, int(chunk_len), _ptr(out),
-                                            _stream_handle(stream)), "td_test_attention")
+def attention(q, k, v, n_pos: int, head_dim: int, out, chunk_len: int = 0, waves: int = 1, stream=None) -> None:
+    """One query head over n_pos K/V rows through the step's tile, wave-fold and merge
+    routines, as `waves` waves of the head run them in the step (test hook)."""
+    _lib.check(_lib.lib().td_test_attention(_ptr(q), _ptr(k), _ptr(v), n_pos, head_dim, int(chunk_len), int(waves),
+                                            _ptr(out), _stream_handle(stream)), "td_test_attention")
+
 
 
 def rope(x, n_heads: int, head_dim: int, pos: int, theta: float, out, stream=None) -> None:

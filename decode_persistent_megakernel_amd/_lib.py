@@ -110,7 +110,7 @@ def lib() -> ctypes.CDLL:
         L.td_test_gemv.restype = i32
         L.td_test_gemv.argtypes = [i32, vp, vp, i32, i32, vp, vp, vp]
         L.td_test_attention.restype = i32
-        L.td_test_attention.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+        L.td_test_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
         L.td_test_rope.restype = i32
         L.td_test_rope.argtypes = [vp, i32, i32, i32, f32, vp, vp]
         L.td_test_argmax.restype = i32

@@ -349,7 +349,7 @@ int attention_split(const td_config& c, int ncu, int* chunk_len_out, int* n_chun
   const int64_t topk_i = c.n_experts > 0 ? (int64_t)td_moe_down_reach(c.top_k, I) : 0;
   const int64_t kpad_in = round_up(std::max<int64_t>({H, qd, I, topk_i}), 2048);
   const int64_t merge_budget = std::max<int64_t>(
-      24 * 1024, kpad_in * 4 + td_tile_bytes(d) - ((int64_t)group * d * 4 + 2 * d * 4 + (int64_t)group * TD_TILE * 4));
+      24 * 1024, kpad_in * 4 + td_tile_bytes(d) - (int64_t)td_attn_layout(d, group, 1, c.n_experts > 0).merge);
   while (n_chunks_of(chunk_len) > 64 || (int64_t)n_chunks_of(chunk_len) * group * (d + 4) * 4 > merge_budget)
     chunk_len += TD_TILE;
   const int n_chunks_max = n_chunks_of(chunk_len);
@@ -395,7 +395,7 @@ int build_plan(const td_config* cfg, int ncu, int64_t lds_cap, const int32_t* pa
   out_floats = (int)round_up(std::max(out_floats, 1), 64);
 
   // LDS layout: the rings take what the rest leaves, up to TD_RING_MAX slots per wave
-  const td_attn_lds A = td_attn_layout(d, group, n_chunks_max);
+  const td_attn_lds A = td_attn_layout(d, group, n_chunks_max, E > 0);
   // the GEMV input area holds the longest input: a MoE down stage's is top_k slots of I
   // (a MoE down stage reads its last slot's whole chunks: td_moe_down_reach)
   const int64_t kpad = round_up(std::max({H, qd, I, E ? td_moe_down_reach(topk, I) : 0}), 2048);
@@ -1227,14 +1227,16 @@ int td_test_gemv(int32_t fmt, const void* w, const void* scales, int32_t rows, i
 }
 
 int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim,
-                      int32_t chunk_len, float* d_out, void* stream) {
+                      int32_t chunk_len, int32_t waves_per_head, float* d_out, void* stream) {
   if (!d_q || !k || !v || !d_out || n_pos <= 0 || (head_dim != 64 && head_dim != 128))
     return fail(TD_E_INVALID_ARG, "bad attention arguments");
+  if (waves_per_head != 1 && waves_per_head != 2 && waves_per_head != 4 && !(waves_per_head == 8 && head_dim == 128))
+    return fail(TD_E_INVALID_ARG, "waves_per_head must be 1, 2 or 4 (or 8 at head_dim 128)");
   if (chunk_len == 0) chunk_len = (int32_t)round_up(n_pos, TD_TILE);
   if (chunk_len < 0 || chunk_len % TD_TILE) return fail(TD_E_INVALID_ARG, "chunk_len must be a multiple of 64");
   if ((n_pos + chunk_len - 1) / chunk_len > 64) return fail(TD_E_INVALID_ARG, "more than 64 chunks");
   const float scale = (float)(1.0 / std::sqrt((double)head_dim));  // the decode kernel's attention scale
-  int le = td_launch_test_attention(d_q, k, v, n_pos, head_dim, chunk_len, scale, d_out, stream);
+  int le = td_launch_test_attention(d_q, k, v, n_pos, head_dim, chunk_len, waves_per_head, scale, d_out, stream);
   if (le) return hip_fail((hipError_t)le, "attention launch");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   return e == hipSuccess ? TD_OK : hip_fail(e, "hipStreamSynchronize");

@@ -286,6 +286,79 @@ DEV void attn_tile(const float* qs, const uint16_t* kt, const uint16_t* vt, floa
   }
 }
 
+// The same update by one of W waves sharing a query head: this wave takes the
+// tile's rows [s R, (s + 1) R), R = 64 / W, of which the first min(R, nv - s R)
+// are positions (the caller skips a tile with none).  Scores: lane (r, part)
+// with r = lane % R sums the dimensions [part D / W, (part + 1) D / W) of row
+// s R + r, the W parts then added by butterfly shuffles; P.V as attn_tile over
+// the wave's R rows (lane groups of RPG = R / (64 / (D / 4)) rows).
+template <int D, int W>
+DEV void attn_tile_w(const float* qs, const uint16_t* kt, const uint16_t* vt, float* ps, int nv, int s, float& m,
+                     float& l, f32x4& acc) {
+  constexpr int R = TD_TILE_ROWS / W, DPL = D / W, LPR = D / 4, NG = 64 / LPR, RPG = R / NG;
+  static_assert(DPL % 8 == 0 && RPG % 4 == 0, "a wave's rows and dimensions come in whole loop steps");
+  const int lane = lane_id();
+  const int r0 = s * R, nr = min(R, nv - r0);
+  const int r = lane % R, part = lane / R;
+  const uint16_t* kr = kt + (r0 + r) * (D + 8) + part * DPL;
+  const float* qp = qs + part * DPL;
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; e += 8) {
+    const u32x4 kw = *(const u32x4*)(kr + e);
+    const f32x4 q0 = *(const f32x4*)(qp + e), q1 = *(const f32x4*)(qp + e + 4);
+    a = fmaf(bf_lo(kw.x), q0.x, a);
+    a = fmaf(bf_hi(kw.x), q0.y, a);
+    a = fmaf(bf_lo(kw.y), q0.z, a);
+    a = fmaf(bf_hi(kw.y), q0.w, a);
+    a = fmaf(bf_lo(kw.z), q1.x, a);
+    a = fmaf(bf_hi(kw.z), q1.y, a);
+    a = fmaf(bf_lo(kw.w), q1.z, a);
+    a = fmaf(bf_hi(kw.w), q1.w, a);
+  }
+#pragma unroll
+  for (int off = R; off < 64; off <<= 1) a += __shfl_xor(a, off);
+  const float sc = r < nr ? a : -__builtin_inff();
+  const float mn = fmaxf(m, wave_max(sc));  // finite: nr >= 1
+  const float p = __expf(sc - mn);
+  const float corr = __expf(m - mn);
+  l = l * corr + wave_sum(part == 0 ? p : 0.f);
+  m = mn;
+  acc *= corr;
+  if (part == 0) ps[r] = p;
+  const int cg = lane % LPR, pg = lane / LPR;
+  const uint16_t* vrow = vt + (r0 + pg * RPG) * D + cg * 4;
+  const float* prow = ps + pg * RPG;
+#pragma unroll
+  for (int t = 0; t < RPG; t += 4) {
+    const f32x4 p4 = *(const f32x4*)(prow + t);
+    u32x2 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = *(const u32x2*)(vrow + (t + k) * D);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float pk = k == 0 ? p4.x : k == 1 ? p4.y : k == 2 ? p4.z : p4.w;
+      acc.x = fmaf(pk, bf_lo(v[k].x), acc.x);
+      acc.y = fmaf(pk, bf_hi(v[k].x), acc.y);
+      acc.z = fmaf(pk, bf_lo(v[k].y), acc.z);
+      acc.w = fmaf(pk, bf_hi(v[k].y), acc.w);
+    }
+  }
+}
+// One tile by wave s of W (W = 1: attn_tile itself); a wave whose share of the
+// tile holds no position leaves its state as it is.
+template <int D>
+DEV void attn_tile_part(const float* qs, const uint16_t* kt, const uint16_t* vt, float* ps, int nv, int W, int s,
+                        float& m, float& l, f32x4& acc) {
+  if (W == 1) {
+    attn_tile<D>(qs, kt, vt, ps, nv, m, l, acc);
+  } else if (s * (TD_TILE_ROWS / W) < nv) {
+    if (W == 2) attn_tile_w<D, 2>(qs, kt, vt, ps, nv, s, m, l, acc);
+    else if (W == 4) attn_tile_w<D, 4>(qs, kt, vt, ps, nv, s, m, l, acc);
+    else if constexpr (D >= 128) attn_tile_w<D, 8>(qs, kt, vt, ps, nv, s, m, l, acc);
+  }
+}
+
 // Sums the position groups: afterwards lanes 0 .. D/4 - 1 hold the columns
 // 4 lane .. 4 lane + 3.
 template <int D>
@@ -298,6 +371,46 @@ DEV f32x4 attn_finish(f32x4 acc) {
     acc.w += __shfl_xor(acc.w, off);
   }
   return acc;
+}
+
+// A wave's finished state (after attn_finish) for the head's first wave: D
+// columns, then m and l, at st (LDS, D + 4 floats).
+template <int D>
+DEV void attn_sub_store(float* st, f32x4 acc, float m, float l) {
+  const int lane = lane_id();
+  if (lane < D / 4) *(f32x4*)(st + 4 * lane) = acc;
+  if (lane == 0) {
+    st[D] = m;
+    st[D + 1] = l;
+  }
+}
+// The head's first wave folds the states of waves 1 .. W - 1 (at sub, D + 4
+// floats apart) into its own, in wave order, as one chunk's unnormalised state:
+// M the largest m, acc = sum_s acc_s e^(m_s - M), l = sum_s l_s e^(m_s - M) (a
+// wave without positions has m = -inf and adds nothing; the first wave always
+// has some, so M is finite).  Lanes 0 .. D/4 - 1 carry acc.
+template <int D>
+DEV void attn_combine(f32x4& acc, float& m, float& l, const float* sub, int W) {
+  const int lane = lane_id();
+  float M = m;
+  for (int k = 1; k < W; ++k) M = fmaxf(M, sub[(k - 1) * (D + 4) + D]);
+  const float c0 = __expf(m - M);
+  acc *= c0;
+  float ls = l * c0;
+  for (int k = 1; k < W; ++k) {
+    const float* st = sub + (k - 1) * (D + 4);
+    const float ck = __expf(st[D] - M);
+    ls = fmaf(st[D + 1], ck, ls);
+    if (lane < D / 4) {
+      const f32x4 v = *(const f32x4*)(st + 4 * lane);
+      acc.x = fmaf(ck, v.x, acc.x);
+      acc.y = fmaf(ck, v.y, acc.y);
+      acc.z = fmaf(ck, v.z, acc.z);
+      acc.w = fmaf(ck, v.w, acc.w);
+    }
+  }
+  m = M;
+  l = ls;
 }
 
 // Split-K merge of one query head's chunk partials ("One launch per token",

@@ -43,6 +43,7 @@ enum {
 
 // uint32 word offsets of the LDS control block (intra-workgroup hand-offs)
 enum {
+  TD_CTL_SUB = 0,        // [8] per query head: partial attention states its other waves have left (monotonic)
   TD_CTL_RV = 16,        // rendezvous arrivals of the compute waves (monotonic)
   TD_CTL_TREADY = 17,    // attention tiles made ready (monotonic)
   TD_CTL_TDONE = 18,     // attention tiles consumed, summed over the query-head waves
@@ -191,18 +192,36 @@ static inline int32_t td_tile_bytes(int d) {
 }
 
 struct td_attn_lds {
-  int32_t q, kvp, p, merge, bytes;
+  int32_t q, kvp, p, sub, merge, bytes;
 };
+
+// Compute waves per query head in the decode step's attention.  With one
+// query head per kv head (group 1, the OLMoE layout) a CU's attention would run
+// on one of its eight compute waves, so in a mixture-of-experts model W = 8
+// waves share it (4 at head dim 64, where a wave's share of a tile, 64 / W
+// rows, stays a multiple of 16): wave w takes query head w % group and rows
+// [s 64 / W, (s + 1) 64 / W) of every tile, s = w / group, and the W partial
+// states of a head are combined in wave order.  Measured on the OLMoE shape:
+// 0.966 -> 0.951 ms per step.  Every other model keeps one wave per head, and
+// the dense kernels are compiled without the split: two waves per head measured
+// slower on the Llama-3.2-1B shapes (0.664 -> 0.682 ms per step), and the split's
+// code alone, unused, cost the dense kernels 2 % in their GEMV loops.
+#ifdef __HIPCC__
+__host__ __device__
+#endif
+static inline int td_attn_waves(int d, int group, bool moe) { return moe && group == 1 ? (d == 64 ? 4 : 8) : 1; }
 
 #ifdef __HIPCC__
 __host__ __device__
 #endif
-static inline td_attn_lds td_attn_layout(int d, int group, int n_chunks_max) {
+static inline td_attn_lds td_attn_layout(int d, int group, int n_chunks_max, bool moe = false) {
   td_attn_lds a;
+  const int W = td_attn_waves(d, group, moe);
   a.q = 0;                                          // group x d queries, then this
   a.kvp = a.q + group * d * 4;                      // position's K and V rows (2 d floats)
-  a.p = a.kvp + 2 * d * 4;                          // group x 64 probabilities / merge weights
-  a.merge = a.p + group * TD_TILE * 4;              // group x (n_chunks_max - 1) x (d + 4) partials
+  a.p = a.kvp + 2 * d * 4;                          // group W x 64 probabilities / merge weights (one row a wave)
+  a.sub = a.p + group * W * TD_TILE * 4;            // group x (W - 1) x (d + 4) partial states of a head's waves
+  a.merge = a.sub + group * (W - 1) * (d + 4) * 4;  // group x (n_chunks_max - 1) x (d + 4) partials
   a.bytes = a.merge + group * (n_chunks_max > 1 ? n_chunks_max - 1 : 1) * (d + 4) * 4;
   a.bytes = (a.bytes + 255) & ~255;
   return a;
@@ -356,5 +375,5 @@ int td_launch_test_rope(const float* x, int n_heads, int d, const td_rope_row& r
 int td_launch_test_argmax(const float* logits, int n, int groups, void* work, int* token, int* nonfinite,
                           void* stream);
 size_t td_test_attention_lds(int d, int chunk_len, int n);
-int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, int chunk_len, float scale,
-                             float* out, void* stream);
+int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, int chunk_len, int waves,
+                             float scale, float* out, void* stream);

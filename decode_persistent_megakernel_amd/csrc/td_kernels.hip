@@ -404,7 +404,7 @@ DEV void patch_pos_row(const td_kparams& P, uint8_t* lds, uint8_t* buf, const At
   const int tb = T.t0 + tile * TD_TILE;
   if (pos < tb || pos >= tb + TD_TILE || pos >= T.t1) return;
   const int d = P.d, row = pos - tb;
-  const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max);
+  const td_attn_lds A = td_attn_layout(d, P.group, P.n_chunks_max, false);  // (kvp: the same in every layout)
   const float* kvp = (const float*)(lds + P.off_attn + A.kvp);
   uint16_t* kt = (uint16_t*)buf;
   uint16_t* vt = kt + TD_TILE * (d + 8);
@@ -982,6 +982,89 @@ DEV void attn_wave_d(const td_kparams& P, CS& C, uint8_t* lds, int h, const Attn
   }
 }
 
+// The same for a MoE kernel, whose attention may spread a head over W waves
+// (td_attn_waves): attention wave w of a task takes query head h = w % group
+// and rows [s 64 / W,
+// (s + 1) 64 / W) of every tile the sync wave makes ready (s = w / group, W
+// waves a head).  A head's waves 1 .. W - 1 leave their states in LDS and are
+// done; its first wave folds them in, in wave order, and publishes the chunk's
+// partial (chunk c > 0) or, on the chunk-0 CU, merges all chunks' partials of
+// its head, o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M) (the chunks
+// summed in chunk order), and publishes o.  nattn counts the attention stages
+// this wave has taken part in (the partial-state counters are monotonic).
+template <int D, class CS>
+DEV void attn_wave_split(const td_kparams& P, CS& C, uint8_t* lds, int w, const AttnTask& T, uint32_t tag,
+                         uint32_t& tiles_seen, uint32_t& nattn, uint64_t& first) {
+  const int lane = lane_id();
+  const int G = P.group, W = td_attn_waves(D, G, true);
+  const int h = w % G, s = w / G;
+  const td_attn_lds A = td_attn_layout(D, G, P.n_chunks_max, true);
+  uint8_t* base = lds + P.off_attn;
+  const float* qs = (const float*)(base + A.q) + h * D;
+  float* ps = (float*)(base + A.p) + w * TD_TILE;
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  ++nattn;
+  for (int tile = 0; tile < T.ntiles; ++tile) {
+    const uint16_t* kt = (const uint16_t*)tile_buf(P, lds, tiles_seen);
+    const uint16_t* vt = kt + TD_TILE * (D + 8);
+    (void)lds_wait_ge(P, C.ctl + TD_CTL_TREADY, ++tiles_seen, C.ok);
+    const int nv = min(TD_TILE, T.t1 - (T.t0 + tile * TD_TILE));
+    attn_tile_part<D>(qs, kt, vt, ps, nv, W, s, m, l, acc);
+    lds_fence();
+    if (lane == 0) lds_add(C.ctl + TD_CTL_TDONE, 1u);
+    if (P.trace && !first) first = wall_clock64();
+  }
+  acc = attn_finish<D>(acc);
+  constexpr int st = D + 4;
+  if (W > 1) {
+    float* sub = (float*)(base + A.sub) + (size_t)h * (W - 1) * st;
+    if (s > 0) {  // this wave's state for the head's first wave
+      attn_sub_store<D>(sub + (s - 1) * st, acc, m, l);
+      lds_fence();
+      if (lane == 0) lds_add(C.ctl + TD_CTL_SUB + h, 1u);
+      return;
+    }
+    (void)lds_wait_ge(P, C.ctl + TD_CTL_SUB + h, (uint32_t)(W - 1) * nattn, C.ok);
+    attn_combine<D>(acc, m, l, sub, W);
+  }
+  uint2* myparts = P.tpart + ((size_t)T.g * G + h) * P.n_chunks_max * st;
+  if (T.c > 0) {
+    uint2* dst = myparts + (size_t)T.c * st;
+    if (lane < D / 4) {
+      st_tag(dst + 4 * lane + 0, acc.x, tag);
+      st_tag(dst + 4 * lane + 1, acc.y, tag);
+      st_tag(dst + 4 * lane + 2, acc.z, tag);
+      st_tag(dst + 4 * lane + 3, acc.w, tag);
+    }
+    if (lane == 0) {
+      st_tag(dst + D, m, tag);
+      st_tag(dst + D + 1, l, tag);
+      st_tag(dst + D + 2, 0.f, tag);
+      st_tag(dst + D + 3, 0.f, tag);
+    }
+    return;
+  }
+  const int n = T.n_used;  // <= 64
+  float* mb = (float*)(base + A.merge) + (size_t)h * (P.n_chunks_max - 1) * st;  // chunks 1..n-1
+  // the merging CUs (one per kv head) poll without topping up: every CU's
+  // O stage waits for their outputs.  Where the staging runs on into the K/V
+  // tile buffer, it waits until every query-head wave is done with the tiles.
+  if (P.merge_in_tile) (void)lds_wait_ge(P, C.ctl + TD_CTL_TDONE, (uint32_t)(G * W) * tiles_seen, C.ok);
+  // (d = 128: 9 loads per lane, so that the nine chunks of a 576-position
+  // context are polled in one round; measured faster than 8 or 12)
+  if (n > 1) C.ok &= poll_pairs<D == 128 ? 9 : 8, false>(P, myparts + st, 0, (n - 1) * st, tag, mb, C);
+  lds_fence();
+  const f32x4 o = attn_merge<D>(acc, m, l, mb, n, ps);
+  if (lane < D / 4) {
+    uint2* dst = P.to + ((size_t)T.g * G + h) * D + 4 * lane;
+    st_tag(dst + 0, o.x, tag);
+    st_tag(dst + 1, o.y, tag);
+    st_tag(dst + 2, o.z, tag);
+    st_tag(dst + 3, o.w, tag);
+  }
+}
+
 DEV void trace_rec(const td_kparams& P, int wave, int seq, uint64_t t0, uint64_t t1, uint64_t t2, uint64_t t3) {
   uint64_t* rec = P.trace + ((size_t)blockIdx.x * P.n_stages + seq) * TD_TRACE_STAMPS + 4 * wave;
   const int lane = lane_id();
@@ -1078,7 +1161,8 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
   if (ld_u(P.sync + TD_SY_ABORT)) C.ok = false;
   int tok = uni(*P.token_in);
   if (tok < 0 || tok >= P.V) tok = 0;  // the sync wave reports the range error
-  uint32_t tiles_seen = 0;
+  uint32_t tiles_seen = 0, nattn = 0;
+  const int attn_waves = P.group * (MOE ? td_attn_waves(D, P.group, true) : 1);  // waves taking part in attention
   bool first_stage = true;
   for (int step = 0;; ++step) {
     const int pos = P.pos + step;
@@ -1128,7 +1212,7 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
       first_stage = false;
       if (kind == TD_ST_ATTN) {
         // the kv head's block: its query heads (scaled by 1/sqrt(d)), then this position's K and V rows
-        const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max);
+        const td_attn_lds A = td_attn_layout(P.d, P.group, P.n_chunks_max, MOE);
         float* qs = (float*)(lds + P.off_attn + A.q);
         const int nqv = P.group * P.d, nb = nqv + 2 * P.d;
         int lo, hi;
@@ -1141,7 +1225,11 @@ DEV void compute_wave(const td_kparams& P, uint8_t* lds, int wave) {
         for (int i = lo + lane; i < min(hi, nqv); i += 64) qs[i] *= P.attn_scale;
         rendezvous(P, C);
         if (P.trace) ts1 = wall_clock64();
-        if (wave < P.group) attn_wave_d<D>(P, C, lds, wave, T, tag, tiles_seen, ts2);
+        if constexpr (MOE) {
+          if (wave < attn_waves) attn_wave_split<D>(P, C, lds, wave, T, tag, tiles_seen, nattn, ts2);
+        } else {
+          if (wave < P.group) attn_wave_d<D>(P, C, lds, wave, T, tag, tiles_seen, ts2);
+        }
       } else if (MOE && kind == TD_ST_GU) {
         // MoE gate/up: the router logits (all E, from every CU) next to the
         // input the router stage staged, the wave's routing, then its slot's
@@ -1254,7 +1342,7 @@ DEV void sync_wave(const td_kparams& P, uint8_t* lds) {
     const int tok = uni(*P.token_in);
     if ((tok < 0 || tok >= P.V) && lane == 0 && cu == 0) atomicOr(P.err, TD_ERRBIT_RANGE);
   }
-  const int G = P.group;
+  const int G = P.group * (MOE ? td_attn_waves(P.d, P.group, true) : 1);  // the attention waves, each consuming every tile
   uint32_t tiles_ready = 0, tiles_issued = 0, rv_base = 0;
   if (P.step_clock && cu == 0 && lane == 0) P.step_clock[0] = wall_clock64();
   for (int step = 0;; ++step) {
@@ -1517,14 +1605,15 @@ __global__ void __launch_bounds__(256) td_gemv_kernel(int fmt, const uint8_t* w,
 // One wave; LDS: q [D], p [64], the tile, the partials of chunks 1 .. n-1.
 template <int D>
 __global__ void __launch_bounds__(64) td_attention_kernel(const float* q, const uint16_t* k, const uint16_t* v,
-                                                          int n, int chunk_len, float scale, float* out) {
+                                                          int n, int chunk_len, int W, float scale, float* out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int st = D + 4;
   float* qs = (float*)lds;
   float* ps = qs + D;
   uint16_t* kt = (uint16_t*)(ps + TD_TILE);
   uint16_t* vt = kt + TD_TILE * (D + 8);
-  float* mb = (float*)(vt + TD_TILE * D);
+  float* sub = (float*)(vt + TD_TILE * D);  // the states of waves 1 .. W - 1 of the head
+  float* mb = sub + 7 * st;
   const int lane = lane_id();
   for (int i = lane; i < D; i += 64) qs[i] = q[i] * scale;
   const int nch = (n + chunk_len - 1) / chunk_len;
@@ -1532,8 +1621,14 @@ __global__ void __launch_bounds__(64) td_attention_kernel(const float* q, const 
   float m0 = -__builtin_inff(), l0 = 0.f;
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * chunk_len, t1 = min(t0 + chunk_len, n);
-    float m = -__builtin_inff(), l = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float m[8], l[8];
+    f32x4 acc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      m[s] = -__builtin_inff();
+      l[s] = 0.f;
+      acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
     for (int tb = t0; tb < t1; tb += TD_TILE) {
       const int nv = min(TD_TILE, t1 - tb);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1548,20 +1643,28 @@ __global__ void __launch_bounds__(64) td_attention_kernel(const float* q, const 
         *(u32x4*)(vt + row * D + pc * 8) = vv;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      attn_tile<D>(qs, kt, vt, ps, nv, m, l, acc);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)  // the head's W waves, one after another
+        if (s < W) {
+          attn_tile_part<D>(qs, kt, vt, ps, nv, W, s, m[s], l[s], acc[s]);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
     }
-    acc = attn_finish<D>(acc);
-    if (c == 0) {
-      acc0 = acc;
-      m0 = m;
-      l0 = l;
-    } else {
-      float* dst = mb + (size_t)(c - 1) * st;
-      if (lane < D / 4) *(f32x4*)(dst + 4 * lane) = acc;
-      if (lane == 0) {
-        dst[D] = m;
-        dst[D + 1] = l;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < W) {
+        acc[s] = attn_finish<D>(acc[s]);
+        if (s > 0) attn_sub_store<D>(sub + (s - 1) * st, acc[s], m[s], l[s]);
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (W > 1) attn_combine<D>(acc[0], m[0], l[0], sub, W);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (c == 0) {
+      acc0 = acc[0];
+      m0 = m[0];
+      l0 = l[0];
+    } else {
+      attn_sub_store<D>(mb + (size_t)(c - 1) * st, acc[0], m[0], l[0]);
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1706,21 +1809,21 @@ int td_launch_test_argmax(const float* logits, int n, int groups, void* work, in
 
 size_t td_test_attention_lds(int d, int chunk_len, int n) {
   const int nch = (n + chunk_len - 1) / chunk_len;
-  return (size_t)(d + TD_TILE) * 4 + (size_t)TD_TILE * (d + 8) * 2 + (size_t)TD_TILE * d * 2 +
+  return (size_t)(d + TD_TILE) * 4 + (size_t)TD_TILE * (d + 8) * 2 + (size_t)TD_TILE * d * 2 + (size_t)7 * (d + 4) * 4 +
          (size_t)(nch > 1 ? nch - 1 : 1) * (d + 4) * 4;
 }
 
-int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, int chunk_len, float scale,
-                             float* out, void* stream) {
+int td_launch_test_attention(const float* q, const void* k, const void* v, int n, int d, int chunk_len, int waves,
+                             float scale, float* out, void* stream) {
   const size_t lds = td_test_attention_lds(d, chunk_len, n);
   const void* f = d == 64 ? (const void*)td_attention_kernel<64> : (const void*)td_attention_kernel<128>;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return (int)e;
   if (d == 64)
     td_attention_kernel<64><<<1, 64, lds, (hipStream_t)stream>>>(q, (const uint16_t*)k, (const uint16_t*)v, n,
-                                                                  chunk_len, scale, out);
+                                                                  chunk_len, waves, scale, out);
   else
     td_attention_kernel<128><<<1, 64, lds, (hipStream_t)stream>>>(q, (const uint16_t*)k, (const uint16_t*)v, n,
-                                                                   chunk_len, scale, out);
+                                                                   chunk_len, waves, scale, out);
   return (int)hipGetLastError();
 }

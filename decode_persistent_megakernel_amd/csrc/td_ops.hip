@@ -310,8 +310,12 @@ __global__ void __launch_bounds__(256) op_qkv(td_opparams P, int layer, int R) {
 }
 
 // --------------------------------------------------------------- op_attn
-// Workgroup (g, c): kv head g, positions of chunk c; wave h < group runs query
-// head g * group + h; all 8 waves load the tiles.
+// Workgroup (g, c): kv head g, positions of chunk c; all 8 waves load the
+// tiles, and wave w < group W runs rows [s 64 / W, (s + 1) 64 / W) of every
+// tile for query head g * group + w % group (s = w / group; W = td_attn_waves,
+// as in the persistent kernel: 1 but for a MoE model with one query head per kv
+// head), the head's W states then folded in wave order by its first wave: the
+// persistent kernel's routines in its order.
 template <int D>
 __global__ void __launch_bounds__(512) op_attn(td_opparams P, int layer) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -321,11 +325,14 @@ __global__ void __launch_bounds__(512) op_attn(td_opparams P, int layer) {
   const int n_used = (pos + P.chunk_len) / P.chunk_len;
   if (c >= n_used) return;
   const int t0 = c * P.chunk_len, t1 = min(t0 + P.chunk_len, pos + 1);
+  const int W = td_attn_waves(D, G, P.E > 0);
   float* qs = (float*)lds;                                             // [G][D]
-  float* ps = qs + G * D;                                              // [G][64]
-  uint16_t* kt = (uint16_t*)(ps + G * TD_TILE_ROWS);                   // [64][D + 8]
+  float* ps = qs + G * D;                                              // [G W][64]
+  uint16_t* kt = (uint16_t*)(ps + G * W * TD_TILE_ROWS);               // [64][D + 8]
   uint16_t* vt = kt + TD_TILE_ROWS * (D + 8);                          // [64][D]
+  float* sub = (float*)(vt + TD_TILE_ROWS * D);                        // [G][W - 1][D + 4]
   const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int h = wave % G, s = wave / G;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = P.q[(size_t)g * G * D + i];
   const size_t head_off = ((size_t)layer * P.nkv + g) * P.max_ctx;
   float m = -__builtin_inff(), l = 0.f;
@@ -345,10 +352,15 @@ __global__ void __launch_bounds__(512) op_attn(td_opparams P, int layer) {
       *(u32x4*)(vt + row * D + pc * 8) = vv;
     }
     __syncthreads();  // tile in LDS
-    if (wave < G) attn_tile<D>(qs + wave * D, kt, vt, ps + wave * TD_TILE_ROWS, nv, m, l, acc);
+    if (wave < G * W) attn_tile_part<D>(qs + h * D, kt, vt, ps + wave * TD_TILE_ROWS, nv, W, s, m, l, acc);
+  }
+  if (wave < G * W) acc = attn_finish<D>(acc);
+  if (W > 1) {
+    if (wave < G * W && s > 0) attn_sub_store<D>(sub + ((size_t)h * (W - 1) + s - 1) * (D + 4), acc, m, l);
+    __syncthreads();
+    if (wave < G) attn_combine<D>(acc, m, l, sub + (size_t)h * (W - 1) * (D + 4), W);
   }
   if (wave < G) {
-    acc = attn_finish<D>(acc);
     float* pr = P.part + (((size_t)g * G + wave) * P.n_chunks_max + c) * (D + 4);
     if (lane < D / 4) *(f32x4*)(pr + 4 * lane) = acc;
     if (lane == 0) *(f32x4*)(pr + D) = f32x4{m, l, 0.f, 0.f};
@@ -662,7 +674,9 @@ size_t td_op_lds_bytes(const td_opparams* p) {
   size_t x = std::max({kp(p->H, p->wf), kp(p->qd, p->wf), kp(p->I, p->wf), kp(p->H, 0)}) * 4 + TD_NW * 4;
   if (p->topk > 0) x = std::max(x, (size_t)p->topk * kp(p->I, p->wf) * 4);
   const size_t D = (size_t)p->d, G = (size_t)p->group;
-  const size_t a = G * D * 4 + G * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2;
+  const size_t W = (size_t)td_attn_waves(p->d, p->group, p->E > 0);
+  const size_t a = G * D * 4 + G * W * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2 +
+                   G * (W - 1) * (D + 4) * 4;
   return std::max(x, a);
 }
 

@@ -320,11 +320,15 @@ int td_test_gemv(int32_t weight_format, const void* w, const void* scales, int32
  * out [head_dim] (device): softmax(q . K^T / sqrt(d)) V with the decode step's own routines
  * ("One launch per token", "The attention trap": split-K partials merged with the
  * e^(m_c - M) rescale): the positions are cut into chunks of chunk_len (a multiple of 64; 0 =
- * one chunk for all), each chunk runs the step's 64-row tile routine over its tiles, and the
- * chunks' partials are merged by the step's merge routine in chunk order.  At most 64 chunks
- * (TD_E_INVALID_ARG otherwise, or for head_dim not 64 or 128). */
+ * one chunk for all), each chunk runs the step's 64-row tile routine over its tiles as
+ * waves_per_head waves of one head do in the step (wave s takes rows [s 64 / W, (s + 1) 64 / W)
+ * of every tile; the W states are then folded in wave order by the step's routine), and the
+ * chunks' partials are merged by the step's merge routine in chunk order.  waves_per_head: 1, 2
+ * or 4, or 8 at head_dim 128 (the step uses 8, or 4 at head_dim 64, for a model with one query
+ * head per kv head, else 1).  At most 64 chunks (TD_E_INVALID_ARG otherwise, or for head_dim not
+ * 64 or 128). */
 int td_test_attention(const float* d_q, const void* k, const void* v, int32_t n_pos, int32_t head_dim,
-                      int32_t chunk_len, float* d_out, void* stream);
+                      int32_t chunk_len, int32_t waves_per_head, float* d_out, void* stream);
 
 /* Half-split RoPE of n_heads vectors of head_dim fp32 values (d_x, d_out: device
  * [n_heads][head_dim]) at position pos, with the step's rotation and a table row

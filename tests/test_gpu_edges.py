@@ -25,6 +25,12 @@ SPLITK128 = synth.shrink(synth.CONFIGS["qwen1p5b"], name="splitk_d128", n_q_head
                          intermediate=512, max_ctx=256, seed=2002, **BASE)
 RAGGED4 = synth.shrink(synth.CONFIGS["tinyllama_int4"], name="ragged_int4", n_q_heads=4, n_kv_heads=2, head_dim=64,
                        intermediate=640, max_ctx=128, seed=2003, **BASE)
+# one query head per kv head (a dense model keeps one wave per head; the MoE kernels
+# spread it over 4 or 8 waves, covered in the MoE tests)
+MHA64 = synth.shrink(synth.CONFIGS["llama1b"], name="mha_d64_split", n_q_heads=4, n_kv_heads=4, head_dim=64,
+                     intermediate=512, max_ctx=256, seed=2005, **BASE)
+MHA128 = synth.shrink(synth.CONFIGS["olmoe"], name="mha_d128_split", n_q_heads=2, n_kv_heads=2, head_dim=128,
+                      intermediate=512, max_ctx=256, seed=2006, n_experts=0, top_k=0, **BASE)
 
 
 def _case(td, cfg, start, n, tol):
@@ -53,6 +59,13 @@ def test_last_position_and_beyond(td):
             dec.step(tok.data_ptr(), bad, kv, logits)
         assert ei.value.code == _lib.TD_E_RANGE
     dec.close()
+
+
+@pytest.mark.parametrize("cfg", [MHA64, MHA128], ids=["d64", "d128"])
+def test_one_query_head_per_kv_head(td, cfg):
+    """Positions 5..69: single-row and ragged tiles and the chunk edge at 64."""
+    _say(f"one query head per kv head, {cfg.name}, positions 5..69")
+    _case(td, cfg, 5, 65, 2e-2)
 
 
 def test_splitk_head_dim_128_with_bias(td):

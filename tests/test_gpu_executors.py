@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from tests.test_gpu_parity import run_compare, td, torch, _say  # noqa: F401  (fixture)
-from tests.test_gpu_edges import SPLITK, SPLITK128, RAGGED4
+from tests.test_gpu_edges import SPLITK, SPLITK128, RAGGED4, MHA64, MHA128
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +44,8 @@ MULTITILE = synth.shrink(SPLITK, name="multitile", n_q_heads=16, n_kv_heads=8, m
 
 
 @pytest.mark.parametrize("cfg,start,n", [(SPLITK, 60, 12), (SPLITK128, 120, 12), (RAGGED4, 40, 8),
-                                         (MULTITILE, 2100, 6)],
-                         ids=["d64", "d128_bias", "int4", "multitile"])
+                                         (MULTITILE, 2100, 6), (MHA64, 20, 8), (MHA128, 120, 8)],
+                         ids=["d64", "d128_bias", "int4", "multitile", "mha_d64", "mha_d128"])
 def test_executors_agree_bit_for_bit(td, cfg, start, n):
     _say(f"executors on {cfg.name}")
     m = synth.make_model(cfg)

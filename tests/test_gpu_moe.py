@@ -50,6 +50,11 @@ MOE_TOP1 = synth.shrink(synth.CONFIGS["llama1b"], name="moe_e5k1", hidden=256, n
                         head_dim=64, intermediate=128, n_experts=5, top_k=1, seed=3005, **BASE)
 MOE_MAX = synth.shrink(synth.CONFIGS["llama1b"], name="moe_e256k16", hidden=256, n_q_heads=4, n_kv_heads=2,
                        head_dim=64, intermediate=64, n_experts=256, top_k=16, seed=3006, **BASE)
+# one query head per kv head at d = 64: the persistent kernel spreads each head's
+# attention over 4 waves (8 at d = 128, MOE_D128), each taking a slice of every
+# tile's rows, the states folded in wave order
+MOE_MHA64 = synth.shrink(synth.CONFIGS["llama1b"], name="moe_mha64", hidden=256, n_q_heads=4, n_kv_heads=4,
+                         head_dim=64, intermediate=192, n_experts=8, top_k=2, seed=3007, **BASE)
 
 
 def _run(td, cfg, m, k, v, first, start, n, executor, label):
@@ -91,8 +96,8 @@ def _run(td, cfg, m, k, v, first, start, n, executor, label):
 
 
 @pytest.mark.parametrize("cfg,start", [(MOE_BF16, 30), (MOE_INT4, 10), (MOE_D128, 60), (MOE_ODD, 20), (MOE_TOP1, 5),
-                                       (MOE_MAX, 40)],
-                         ids=["bf16_e16k4", "int4_e8k2", "d128_e64k8", "e10k3", "e5k1", "e256k16"])
+                                       (MOE_MAX, 40), (MOE_MHA64, 58)],
+                         ids=["bf16_e16k4", "int4_e8k2", "d128_e64k8", "e10k3", "e5k1", "e256k16", "mha64_e8k2"])
 @pytest.mark.parametrize("executor", ["megakernel", "per_op", "graph"])
 def test_moe_matches_oracle(td, cfg, start, executor):
     from decode_persistent_megakernel_amd import _lib
@@ -107,7 +112,8 @@ def test_moe_matches_oracle(td, cfg, start, executor):
     _run(td, cfg, m, k, v, synth.first_token(cfg), start, 12, ex, f"{cfg.name}/{executor}")
 
 
-@pytest.mark.parametrize("cfg", [MOE_D128, MOE_BF16, MOE_MAX], ids=["d128_e64k8", "bf16_e16k4", "e256k16"])
+@pytest.mark.parametrize("cfg", [MOE_D128, MOE_BF16, MOE_MAX, MOE_MHA64],
+                         ids=["d128_e64k8", "bf16_e16k4", "e256k16", "mha64_e8k2"])
 def test_executors_agree_across_routings(td, cfg):
     """The graph executor replays one recording and the persistent kernel routes
     inside its launch; the logits of both equal the per-op executor's bit for

@@ -115,18 +115,25 @@ ATTN_CASES = [(1, 64, 0), (5, 64, 0), (63, 64, 64), (64, 64, 64), (65, 64, 64), 
               (1000, 64, 128), (4095, 64, 64), (129, 128, 64), (1, 128, 0), (777, 128, 192), (513, 128, 0)]
 
 
-@pytest.mark.parametrize("n,d,chunk", ATTN_CASES, ids=[f"n{n}_d{d}_c{c}" for n, d, c in ATTN_CASES])
-def test_attention_hook_matches_oracle(td, n, d, chunk):
-    """The step's own tile routine and split-K merge (through td_test_attention)
-    against the oracle's two-pass softmax in fp64: within 2e-5 of the output's
-    scale (fp32 exponentials and sums over at most 4096 positions), and exactly
-    V when there is a single position."""
-    _say(f"attention hook n={n} d={d} chunk={chunk}")
+# waves per query head: the forms the step takes (1; 4 for group 1 at head dim 64, 8 at
+# head dim 128) and 2, which the routine supports as well
+ATTN_WAVE_CASES = [(n, d, c, w) for n, d, c in ATTN_CASES for w in ((1, 2, 4) if d == 64 else (1, 2, 4, 8))]
+
+
+@pytest.mark.parametrize("n,d,chunk,waves", ATTN_WAVE_CASES,
+                         ids=[f"n{n}_d{d}_c{c}_w{w}" for n, d, c, w in ATTN_WAVE_CASES])
+def test_attention_hook_matches_oracle(td, n, d, chunk, waves):
+    """The step's own tile routine, its fold of a head's wave states and its
+    split-K merge (through td_test_attention) against the oracle's two-pass
+    softmax in fp64: within 2e-5 of the output's scale (fp32 exponentials and
+    sums over at most 4096 positions), and exactly V when there is a single
+    position (the head's other waves then hold no position and add nothing)."""
+    _say(f"attention hook n={n} d={d} chunk={chunk} waves={waves}")
     q = RNG.normal(size=d).astype(np.float32)
     K = bf16_from_f32(RNG.normal(size=(n, d)))
     V = bf16_from_f32(RNG.normal(size=(n, d)))
     out = torch.empty(d, dtype=torch.float32, device="cuda")
-    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out, chunk_len=chunk)
+    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out, chunk_len=chunk, waves=waves)
     ref = oracle.attention(q.astype(np.float64), K, V)
     got = out.cpu().numpy().astype(np.float64)
     if n == 1:
@@ -134,19 +141,22 @@ def test_attention_hook_matches_oracle(td, n, d, chunk):
     np.testing.assert_allclose(got, ref, rtol=0, atol=2e-5 * max(1.0, np.abs(ref).max()))
 
 
-def test_attention_hook_one_dominant_key_and_equal_keys(td):
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_attention_hook_one_dominant_key_and_equal_keys(td, waves):
     """Closed forms: with all keys equal the output is the mean of V; with one
-    key far ahead of the others it is that key's V row."""
+    key far ahead of the others it is that key's V row (for each wave split:
+    the dominant key sits in one wave's rows, the other waves' states fold in
+    with weight e^-64)."""
     d, n = 64, 300
     q = np.ones(d, dtype=np.float32)
     K = bf16_from_f32(np.full((n, d), 0.25))
     V = bf16_from_f32(RNG.normal(size=(n, d)))
     out = torch.empty(d, dtype=torch.float32, device="cuda")
-    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out, chunk_len=64)
+    td.attention(torch.from_numpy(q).cuda(), dev(K), dev(V), n, d, out, chunk_len=64, waves=waves)
     np.testing.assert_allclose(out.cpu().numpy(), bf16_to_f64(V).mean(axis=0), rtol=0, atol=1e-5)
     K2 = bf16_from_f32(np.zeros((n, d)))
     K2[137] = bf16_from_f32(np.full(d, 8.0))  # score 8 * 64 / 8 = 64 above the rest: e^-64 weights
-    td.attention(torch.from_numpy(q).cuda(), dev(K2), dev(V), n, d, out, chunk_len=64)
+    td.attention(torch.from_numpy(q).cuda(), dev(K2), dev(V), n, d, out, chunk_len=64, waves=waves)
     np.testing.assert_allclose(out.cpu().numpy(), bf16_to_f64(V[137]), rtol=0, atol=1e-6)
 
 
@@ -156,10 +166,11 @@ def test_attention_hook_argument_checks(td):
     q = torch.zeros(d, dtype=torch.float32, device="cuda")
     kv = torch.zeros((5000, d), dtype=torch.int16, device="cuda")
     out = torch.empty(d, dtype=torch.float32, device="cuda")
-    for n, dd, c in ((10, 64, 32), (10, 96, 0), (0, 64, 0), (4097, 64, 64)):
+    for n, dd, c, w in ((10, 64, 32, 1), (10, 96, 0, 1), (0, 64, 0, 1), (4097, 64, 64, 1), (10, 64, 0, 3),
+                        (10, 64, 0, 8), (10, 64, 0, 0)):
         with pytest.raises(_lib.TdError) as ei:
-            td.attention(q, kv, kv, n, dd, out, chunk_len=c)
-        assert ei.value.code == _lib.TD_E_INVALID_ARG, (n, dd, c)
+            td.attention(q, kv, kv, n, dd, out, chunk_len=c, waves=w)
+        assert ei.value.code == _lib.TD_E_INVALID_ARG, (n, dd, c, w)
 
 
 # ------------------------------------------------------------------ whole step (megakernel)
