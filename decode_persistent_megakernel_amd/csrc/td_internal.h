@@ -202,7 +202,7 @@ struct td_attn_lds {
 // rows, stays a multiple of 16): wave w takes query head w % group and rows
 // [s 64 / W, (s + 1) 64 / W) of every tile, s = w / group, and the W partial
 // states of a head are combined in wave order.  Measured on the OLMoE shape:
-// 0.966 -> 0.951 ms per step.  Every other model keeps one wave per head, and
+// 0.967 -> 0.954 ms per step.  Every other model keeps one wave per head, and
 // the dense kernels are compiled without the split: two waves per head measured
 // slower on the Llama-3.2-1B shapes (0.664 -> 0.682 ms per step), and the split's
 // code alone, unused, cost the dense kernels 2 % in their GEMV loops.
