@@ -669,15 +669,23 @@ int blocks_for(int units, int r) { return (units + OP_WAVES * r - 1) / (OP_WAVES
 
 int td_op_head_blocks(const td_opparams* p) { return blocks_for(p->V, R_HEAD); }
 
+// op_attn's LDS: queries, one probability row a wave, the tile, the head's wave
+// states (td_attn_waves).  It has its own size, so that the other kernels' LDS
+// (and their workgroups per CU) does not grow with the wave split.
+static size_t op_attn_lds_bytes(const td_opparams* p, size_t W) {
+  const size_t D = (size_t)p->d, G = (size_t)p->group;
+  return G * D * 4 + G * W * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2 +
+         G * (W - 1) * (D + 4) * 4;
+}
+static size_t op_attn_lds_bytes(const td_opparams* p) {
+  return op_attn_lds_bytes(p, (size_t)td_attn_waves(p->d, p->group, p->E > 0));
+}
+
 size_t td_op_lds_bytes(const td_opparams* p) {
   auto kp = [](int K, int f) { return (size_t)((K + (f ? 2047 : 511)) / (f ? 2048 : 512) * (f ? 2048 : 512)); };
   size_t x = std::max({kp(p->H, p->wf), kp(p->qd, p->wf), kp(p->I, p->wf), kp(p->H, 0)}) * 4 + TD_NW * 4;
   if (p->topk > 0) x = std::max(x, (size_t)p->topk * kp(p->I, p->wf) * 4);
-  const size_t D = (size_t)p->d, G = (size_t)p->group;
-  const size_t W = (size_t)td_attn_waves(p->d, p->group, p->E > 0);
-  const size_t a = G * D * 4 + G * W * TD_TILE_ROWS * 4 + TD_TILE_ROWS * (D + 8) * 2 + TD_TILE_ROWS * D * 2 +
-                   G * (W - 1) * (D + 4) * 4;
-  return std::max(x, a);
+  return std::max(x, op_attn_lds_bytes(p, 1));  // (the one-wave attention layout, as before the split)
 }
 
 int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos, void* stream) {
@@ -689,15 +697,15 @@ int td_launch_op_begin(const td_opparams* p, const int32_t* d_token, int32_t pos
 int td_launch_op_layers(const td_opparams* p, void* stream) {
   const hipStream_t s = (hipStream_t)stream;
   const td_opparams& P = *p;
-  const size_t lds = td_op_lds_bytes(p);
+  const size_t lds = td_op_lds_bytes(p), alds = op_attn_lds_bytes(p);
   const int U = P.qkv_rows / 2;
   for (int l = 0; l < P.L; ++l) {
     op_qkv<<<blocks_for(U, R_QKV), 256, lds, s>>>(P, l, R_QKV);
     if (P.d == 64) {
-      op_attn<64><<<P.nkv * P.n_chunks_max, 512, lds, s>>>(P, l);
+      op_attn<64><<<P.nkv * P.n_chunks_max, 512, alds, s>>>(P, l);
       op_merge<64><<<P.nkv, 512, 0, s>>>(P);
     } else {
-      op_attn<128><<<P.nkv * P.n_chunks_max, 512, lds, s>>>(P, l);
+      op_attn<128><<<P.nkv * P.n_chunks_max, 512, alds, s>>>(P, l);
       op_merge<128><<<P.nkv, 512, 0, s>>>(P);
     }
     op_resid<<<blocks_for(P.H, R_RESID), 256, lds, s>>>(P, l, 1, R_RESID);
@@ -717,12 +725,13 @@ int td_launch_op_layers(const td_opparams* p, void* stream) {
 }
 
 int td_op_set_lds_limits(const td_opparams* p) {
-  const int lds = (int)td_op_lds_bytes(p);
+  const int lds = (int)td_op_lds_bytes(p), alds = (int)op_attn_lds_bytes(p);
   hipError_t e = hipSuccess;
-  const void* fns[] = {(const void*)op_qkv, (const void*)op_attn<64>, (const void*)op_attn<128>,
-                       (const void*)op_resid, (const void*)op_gu, (const void*)op_head,
+  const void* fns[] = {(const void*)op_qkv, (const void*)op_resid, (const void*)op_gu, (const void*)op_head,
                        (const void*)op_router, (const void*)op_moe_gu, (const void*)op_moe_down};
   for (const void* f : fns)
     if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  for (const void* f : {(const void*)op_attn<64>, (const void*)op_attn<128>})
+    if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, alds);
   return (int)e;
 }
