@@ -5,7 +5,9 @@ may hand those registers to another value while the load is still in flight,
 and the late data then corrupts that value (an address, say).  This test builds
 the device code to assembly and checks, within each basic block, that no
 register an asm load writes is overwritten before it is read or before a
-vmcnt(0) wait.  CPU only: hipcc cross-compiles for gfx950."""
+vmcnt(0) wait, and that none is read (a copy the compiler makes of the value,
+say) before any counted wait.  Dword loads and the 16-bit loads of the QKV
+biases are covered.  CPU only: hipcc cross-compiles for gfx950."""
 import os
 import re
 import shutil
@@ -52,19 +54,24 @@ def check_asm(text):
                 continue
             ins.append((line, in_asm))
         for i, (line, from_asm) in enumerate(ins):
-            if not from_asm or not re.match(r"global_load_dword(x2|x3|x4)?\s", line):
+            if not from_asm or not re.match(r"(global|buffer)_load_(dword(x2|x3|x4)?|ushort|ubyte|sshort|sbyte)\s", line):
                 continue
             seen += 1
             dest = _regs(line.split(None, 1)[1].split(",")[0].strip())
+            waited = False  # a counted wait (any vmcnt) seen since the load
             for later, _ in ins[i + 1:]:
                 if later == "<block>" or later.startswith("s_waitcnt vmcnt(0)"):
                     break
+                if later.startswith("s_waitcnt") and "vmcnt" in later:
+                    waited = True
                 parts = later.split(None, 1)
                 if len(parts) < 2:
                     continue
                 op, ops = parts[0], [o.strip() for o in parts[1].split(",")]
                 srcs = ops if op.startswith(NO_VGPR_DEST) else ops[1:]
                 if set().union(*[_regs(o) for o in srcs]) & dest:
+                    if not waited:  # e.g. a copy the compiler made of the not yet loaded value
+                        findings.append(f"{name[:80]}: '{line}' read by '{later}' before any wait")
                     break
                 if not op.startswith(NO_VGPR_DEST) and _regs(ops[0]) & dest:
                     findings.append(f"{name[:80]}: '{line}' overwritten by '{later}' before it is read")
@@ -72,7 +79,7 @@ def check_asm(text):
     return seen, findings
 
 
-def test_checker_flags_a_dead_in_flight_destination():
+def test_checker_flags_a_dead_or_early_read_destination():
     bad = """_Zk:
 \t;;#ASMSTART
 \tglobal_load_dwordx4 v[0:3], v[4:5], off
@@ -88,8 +95,16 @@ def test_checker_flags_a_dead_in_flight_destination():
 \tv_add_f32_e32 v6, v0, v1
 \tv_lshl_add_u64 v[0:1], v[8:9], 0, s[4:5]
 """
+    copied = """_Zk:
+\t;;#ASMSTART
+\tglobal_load_ushort v2, v[4:5], off
+\t;;#ASMEND
+\tv_mov_b32_e32 v7, v2
+\ts_waitcnt vmcnt(0)
+"""
     assert check_asm(bad)[1] and check_asm(bad)[0] == 1
     assert check_asm(good) == (1, [])
+    assert check_asm(copied)[0] == 1 and "before any wait" in check_asm(copied)[1][0]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
