@@ -225,12 +225,14 @@ def test_moe_down_reads_no_stale_input(td, cfg, start):
     input area out to that reach; before, the stage read whatever an earlier
     kernel had left in LDS there, and a stale NaN made the router logits of the
     next layer NaN (0 x NaN).  Here an earlier kernel leaves NaN in every CU's
-    LDS on purpose: the GEMV hook stages a NaN input of 32768 values (128 KiB)
-    on a grid of one workgroup per CU, then the MoE step must still match the
-    oracle.  These shapes have top_k I a multiple of 512 (no zero padding past
-    top_k I without the reach) and down rows of 64 to 256 values."""
+    LDS on purpose: the GEMV hook, on a grid of one workgroup per CU, stages a
+    NaN input of 32768 values (LDS bytes 0 to 128 Ki) and packs NaN weight
+    chunks just above it (where the d = 64 shapes keep their input area); then
+    the MoE step must still match the oracle.  These shapes have top_k I a
+    multiple of 512 (no zero padding past top_k I without the reach) and down
+    rows of 64 to 256 values."""
     rows, cols = 2048, 32768
-    w = torch.zeros((rows, cols), dtype=torch.int16, device="cuda")
+    w = torch.full((rows, cols), -1, dtype=torch.int16, device="cuda")  # 0xFFFF: a bf16 NaN
     x = torch.full((cols,), float("nan"), dtype=torch.float32, device="cuda")
     y = torch.empty(rows, dtype=torch.float32, device="cuda")
     m = synth.make_model(cfg)
