@@ -140,3 +140,28 @@ def test_random_norm_gains_match_oracle(td, cfg):
     k, v = synth.random_kv_prefix(cfg, 40, seed_tag="gains")
     run_compare(td, cfg, m, k, v, synth.first_token(cfg), 40, 6, 2e-2 if cfg.weight_format == 0 else 5e-2,
                 cfg.name + "/gains")
+
+
+def _poison_lds(td):
+    """Leaves NaN in most of every CU's LDS: the GEMV hook, one workgroup per CU,
+    stages a NaN input of 32768 values (the first 128 KiB) and packs NaN weight
+    chunks above it."""
+    rows, cols = 2048, 32768
+    w = torch.full((rows, cols), -1, dtype=torch.int16, device="cuda")  # 0xFFFF: a bf16 NaN
+    x = torch.full((cols,), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    td.gemv(synth.WF_BF16, w, None, rows, cols, x, y)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+
+
+@pytest.mark.parametrize("cfg,start", [(SPLITK, 60), (SPLITK128, 120), (RAGGED4, 40), (MHA64, 5)],
+                         ids=["d64", "d128_bias", "int4", "mha_d64"])
+def test_dense_steps_read_no_stale_lds(td, cfg, start):
+    """The persistent kernel reads only LDS it has written in the launch: with
+    NaN left in the LDS by an earlier kernel, steps still match the oracle (a
+    read of stale LDS against a zero weight or input would give 0 x NaN = NaN;
+    the MoE down stage had such a read)."""
+    _say(f"stale-LDS check, {cfg.name}")
+    _poison_lds(td)
+    _case(td, cfg, start, 6, 2e-2)

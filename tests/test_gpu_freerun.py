@@ -156,3 +156,13 @@ def test_loop_free_run_matches_oracle_chain(td, label, over):  # noqa: F811
     assert np.array_equal(gk0[:, :, :pos0], k[:, :, :pos0]) and np.array_equal(gv0[:, :, :pos0], v[:, :, :pos0])
     dec.close()
     assert math.isfinite(min(gaps))
+
+
+@pytest.mark.parametrize("label", ["llama1b", "qwen1p5b", "tinyllama_int4"])
+def test_free_run_after_stale_lds(td, label):  # noqa: F811
+    """The same free-running chain with NaN left in every CU's LDS by an earlier
+    kernel (the GEMV hook, as in the stale-LDS edge tests): the full-size
+    layouts read no LDS they have not written in the launch."""
+    from tests.test_gpu_edges import _poison_lds
+    _poison_lds(td)
+    test_loop_free_run_matches_oracle_chain(td, label, {})
